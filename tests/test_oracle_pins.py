@@ -1,0 +1,326 @@
+"""Pins of the fp64 oracle to things other than itself (CPU only).
+
+Each test names the passage or the mathematics it rests on.  Together they are
+chosen so that a plausible slip in the oracle (a dropped rope score term, a
+flipped RoPE sign, a wrong K/V slice of kv_b_proj, a missing gain, an
+off-by-one in the causal mask, a transposed operand) fails at least one.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import mla as O
+from mla_latent_kv_decode_amd import synth
+from tests.bruteforce import mla_brute
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def shape_of(d: synth.LayerDims, **kw) -> O.MLAShape:
+    return O.MLAShape(hidden=d.hidden, n_heads=d.n_heads, qk_nope=d.qk_nope,
+                      qk_rope=d.qk_rope, v_head=d.v_head, kv_lora=d.kv_lora,
+                      q_lora=d.q_lora, **kw)
+
+
+def rel_err(a, b):
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300))
+
+
+def _lists(w):
+    return {k: v.astype(np.float64).tolist() for k, v in w.items()}
+
+
+def _prior_rows(x_prior, w, shp):
+    n = x_prior.shape[0]
+    if n == 0:
+        return np.zeros((0, shp.row))
+    return O.latent_rows(x_prior, np.arange(n), w["w_kva"], w["kv_norm_g"], shp)
+
+
+# --------------------------------------------------------------------------
+# 1. brute force (pure Python loops) on tiny inputs
+# --------------------------------------------------------------------------
+
+BRUTE_CASES = [
+    # tiny fp32 layer of the parity suite: 8 cached tokens + decode at pos 8
+    (synth.TINY, 8, 1),
+    # same layer, chunked prefill: 3 cached + 5 new tokens
+    (synth.TINY, 3, 5),
+    # query LoRA path (the DeepSeek-V3 form) at tiny size
+    (synth.LayerDims(hidden=32, n_heads=3, qk_nope=8, qk_rope=4, v_head=6, kv_lora=10,
+                     q_lora=12), 4, 3),
+    # no rope part at all (the plain MLA of the post's section 3.2)
+    (synth.LayerDims(hidden=24, n_heads=2, qk_nope=6, qk_rope=0, v_head=5, kv_lora=8),
+     2, 3),
+]
+
+
+@pytest.mark.parametrize("dims,n_prior,n_new", BRUTE_CASES)
+def test_oracle_matches_bruteforce(dims, n_prior, n_new):
+    w = synth.make_weights(dims, 0.05, "f32", random_gains=True)
+    shp = shape_of(dims)
+    x = synth.hidden_states(0, n_prior + n_new, dims.hidden, "f32")
+    pos_new = np.arange(n_prior, n_prior + n_new)
+    r = O.mla_step(x[n_prior:], pos_new, _prior_rows(x[:n_prior], w, shp), w, shp)
+    ref = mla_brute([list(map(float, v)) for v in x], list(pos_new), n_prior, _lists(w),
+                    dims.__dict__)
+    assert rel_err(r["y"], ref) < 1e-12
+
+
+def test_oracle_matches_bruteforce_toy_mla_post():
+    """The MLA post's section 3.2 example layer: 8 heads of 64, latent 128,
+    hidden 512 (a few tokens, to keep the pure-Python loops fast)."""
+    dims = synth.LayerDims(hidden=512, n_heads=8, qk_nope=64, qk_rope=0, v_head=64,
+                           kv_lora=128)
+    w = synth.make_weights(dims, 0.05, "f32")
+    shp = shape_of(dims)
+    x = synth.hidden_states(1, 4, 512, "f32")
+    r = O.mla_step(x[2:], np.array([2, 3]), _prior_rows(x[:2], w, shp), w, shp)
+    ref = mla_brute([list(map(float, v)) for v in x], [2, 3], 2, _lists(w), dims.__dict__)
+    assert rel_err(r["y"], ref) < 1e-12
+
+
+# --------------------------------------------------------------------------
+# 2. absorbed form == non-absorbed form (MLA post, section 3.3 eq. 3.3.3 and
+#    section 3.6: the rope score adds to the absorbed latent score)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dims,S,T", [
+    (synth.TINY, 9, 1),
+    (synth.TINY, 9, 4),
+    (synth.V2_LITE, 40, 1),
+    (synth.V2_LITE, 33, 3),
+    (synth.V3, 24, 1),
+])
+def test_absorbed_equals_non_absorbed(dims, S, T):
+    w = synth.make_weights(dims, 0.02, "bf16", random_gains=True)
+    shp = shape_of(dims)
+    x = synth.hidden_states(2, S, dims.hidden, "bf16")
+    prior = _prior_rows(x[:S - T], w, shp)
+    pos = np.arange(S - T, S)
+    r = O.mla_step(x[S - T:], pos, prior, w, shp)
+    rows = np.concatenate([prior, r["rows_new"]])
+    a = O.absorbed_step(x[S - T:], pos, rows, w, shp)
+    assert rel_err(a["y"], r["y"]) < 1e-10
+    assert rel_err(a["o"], r["o"]) < 1e-10
+
+
+# --------------------------------------------------------------------------
+# 3. cached == uncached (MLA post section 2.1; KV-cache page: prefill and decode
+#    are treated the same way)
+# --------------------------------------------------------------------------
+
+def test_cached_equals_uncached():
+    dims = synth.LayerDims(hidden=48, n_heads=4, qk_nope=8, qk_rope=6, v_head=8,
+                           kv_lora=12, q_lora=10)
+    w = synth.make_weights(dims, 0.1, "f32", random_gains=True)
+    shp = shape_of(dims)
+    n = 11
+    x = synth.hidden_states(3, n, dims.hidden, "f32")
+    full = O.mla_step(x, np.arange(n), np.zeros((0, shp.row)), w, shp)
+    rows = np.zeros((0, shp.row))
+    for t in range(n):
+        r = O.mla_step(x[t:t + 1], np.array([t]), rows, w, shp)
+        assert rel_err(r["y"][0], full["y"][t]) < 1e-12
+        rows = np.concatenate([rows, r["rows_new"]])
+    assert rel_err(rows, full["rows_new"]) < 1e-15
+    # chunked: 4 + 7
+    r1 = O.mla_step(x[:4], np.arange(4), np.zeros((0, shp.row)), w, shp)
+    r2 = O.mla_step(x[4:], np.arange(4, n), r1["rows_new"], w, shp)
+    assert rel_err(np.concatenate([r1["y"], r2["y"]]), full["y"]) < 1e-12
+
+
+# --------------------------------------------------------------------------
+# 4. softmax rows sum to one; the offset causal mask
+# --------------------------------------------------------------------------
+
+def test_softmax_rows_and_offset_mask():
+    dims = synth.TINY
+    w = synth.make_weights(dims, 0.05, "f32")
+    shp = shape_of(dims)
+    P, n = 5, 6
+    x = synth.hidden_states(4, P + n, dims.hidden, "f32")
+    r = O.mla_step(x[P:], np.arange(P, P + n), _prior_rows(x[:P], w, shp), w, shp,
+                   return_probs=True)
+    p = r["p"]  # (H, n, P + n)
+    assert np.allclose(p.sum(-1), 1.0, rtol=0, atol=1e-12)
+    for i in range(n):
+        assert np.all(p[:, i, P + i + 1:] == 0.0)      # future keys masked
+        assert np.all(p[:, i, :P + i + 1] > 0.0)       # own and earlier keys seen
+
+
+# --------------------------------------------------------------------------
+# 5. special cases with closed forms
+# --------------------------------------------------------------------------
+
+def test_single_row_closed_form():
+    """S = 1: the only key gets probability 1, so y = W_o [W_UV_h c_0]_h."""
+    dims = synth.V2_LITE
+    w = synth.make_weights(dims, 0.02, "bf16", random_gains=True)
+    shp = shape_of(dims)
+    x = synth.hidden_states(5, 1, dims.hidden, "bf16")
+    r = O.mla_step(x, np.array([0]), np.zeros((0, shp.row)), w, shp)
+    c0 = r["rows_new"][0, :dims.kv_lora]
+    kvb = w["w_kvb"].astype(np.float64)
+    o = []
+    for h in range(dims.n_heads):
+        r0 = h * (dims.qk_nope + dims.v_head) + dims.qk_nope
+        o.append(kvb[r0:r0 + dims.v_head] @ c0)
+    y = w["w_o"].astype(np.float64) @ np.concatenate(o)
+    assert rel_err(r["y"][0], y) < 1e-12
+
+
+def test_zero_query_gives_uniform_attention():
+    """A zero query scores every visible key 0, so each head averages V:
+    o_h = W_UV_h mean_t(c_t) and the probabilities are 1/S."""
+    dims = synth.TINY
+    w = synth.make_weights(dims, 0.05, "f32", random_gains=True)
+    w["w_q"] = np.zeros_like(w["w_q"])
+    shp = shape_of(dims)
+    S = 9
+    x = synth.hidden_states(6, S, dims.hidden, "f32")
+    r = O.mla_step(x[S - 1:], np.array([S - 1]), _prior_rows(x[:S - 1], w, shp), w, shp,
+                   return_probs=True)
+    assert np.allclose(r["p"], 1.0 / S, rtol=0, atol=1e-15)
+    rows = np.concatenate([_prior_rows(x[:S - 1], w, shp), r["rows_new"]])
+    cbar = rows[:, :dims.kv_lora].mean(0)
+    kvb = w["w_kvb"].astype(np.float64)
+    o = []
+    for h in range(dims.n_heads):
+        r0 = h * (dims.qk_nope + dims.v_head) + dims.qk_nope
+        o.append(kvb[r0:r0 + dims.v_head] @ cbar)
+    assert rel_err(r["o"][0].reshape(-1), np.concatenate(o)) < 1e-13
+
+
+def test_reduces_to_standard_mha():
+    """dc = D with W_DKV = I, no rope and unit gains: MLA is standard MHA on the
+    RMS-normalised input with W^K = W_UK and W^V = W_UV (MLA post section 3.1).
+    The reference is the batched MHA of "Transformer and KV Cache Basics"
+    (reshape to heads, Q K^T / sqrt(d_k / H), future mask, softmax, @ V)."""
+    D, H, dh = 12, 3, 4
+    dims = synth.LayerDims(hidden=D, n_heads=H, qk_nope=dh, qk_rope=0, v_head=dh,
+                           kv_lora=D)
+    w = synth.make_weights(dims, 0.3, "f32")
+    w["w_kva"] = np.eye(D, dtype=np.float32)
+    shp = shape_of(dims)
+    n = 7
+    x = synth.hidden_states(7, n, D, "f32").astype(np.float64)
+    r = O.mla_step(x, np.arange(n), np.zeros((0, D)), w, shp)
+    xn = x / np.sqrt(np.mean(x * x, axis=1, keepdims=True) + 1e-6)
+    wk = np.concatenate([w["w_kvb"][h * 2 * dh:h * 2 * dh + dh] for h in range(H)])
+    wv = np.concatenate([w["w_kvb"][h * 2 * dh + dh:(h + 1) * 2 * dh] for h in range(H)])
+    Q = (x @ w["w_q"].T).reshape(n, H, dh).transpose(1, 0, 2)
+    K = (xn @ wk.T).reshape(n, H, dh).transpose(1, 0, 2)
+    V = (xn @ wv.T).reshape(n, H, dh).transpose(1, 0, 2)
+    mask = np.triu(np.full((n, n), -np.inf), k=1)
+    s = Q @ K.transpose(0, 2, 1) / math.sqrt(H * dh / H) + mask
+    s = np.exp(s - s.max(-1, keepdims=True))
+    ratio = (s / s.sum(-1, keepdims=True)) @ V
+    y = ratio.transpose(1, 0, 2).reshape(n, H * dh) @ w["w_o"].T
+    assert rel_err(r["y"], y) < 1e-12
+
+
+# --------------------------------------------------------------------------
+# 6. RoPE and RMSNorm properties
+# --------------------------------------------------------------------------
+
+def test_rope_properties():
+    rng = np.random.default_rng(0)
+    d = 64
+    x = rng.standard_normal((5, d))
+    # position 0 is the identity
+    assert np.array_equal(O.rope(x, np.zeros(5), 10000.0), x)
+    # each pair keeps its norm
+    y = O.rope(x, np.arange(5) * 37, 10000.0)
+    assert np.allclose(np.hypot(y[:, 0::2], y[:, 1::2]), np.hypot(x[:, 0::2], x[:, 1::2]),
+                       rtol=1e-14)
+    # rotations compose: RoPE(RoPE(x, a), b) = RoPE(x, a + b)
+    assert np.allclose(O.rope(O.rope(x, np.full(5, 11), 1e4), np.full(5, 30), 1e4),
+                       O.rope(x, np.full(5, 41), 1e4), atol=1e-12)
+    # scores depend only on the position difference (MLA post eq. 3.4.2)
+    q, k = rng.standard_normal(d), rng.standard_normal(d)
+    s1 = O.rope(q, 100, 1e4) @ O.rope(k, 93, 1e4)
+    s2 = O.rope(q, 7, 1e4) @ O.rope(k, 0, 1e4)
+    assert abs(s1 - s2) < 1e-12
+    # closed form at d = 2 (theta_0 = 1): [1, 0] at position p -> [cos p, sin p];
+    # rotation direction is counter-clockwise (positive imaginary part)
+    assert np.allclose(O.rope(np.array([1.0, 0.0]), 1, 1e4), [0.5403023058681398,
+                                                            0.8414709848078965])
+    # the last pair turns slowest: theta_{d/2-1} = base^(-(d-2)/d)
+    e = np.zeros(d)
+    e[-2] = 1.0
+    r = O.rope(e, 1, 1e4)
+    assert abs(math.atan2(r[-1], r[-2]) - 1e4 ** (-(d - 2) / d)) < 1e-15
+    with pytest.raises(ValueError):
+        O.rope(np.zeros(3), 1, 1e4)
+
+
+def test_rmsnorm_properties():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((4, 32))
+    g = 1 + 0.1 * rng.standard_normal(32)
+    y = O.rms_norm(x, np.ones(32), 0.0)
+    assert np.allclose(np.sqrt(np.mean(y * y, axis=1)), 1.0, rtol=1e-14)
+    assert np.allclose(O.rms_norm(7.5 * x, g, 0.0), O.rms_norm(x, g, 0.0), rtol=1e-13)
+    assert np.allclose(O.rms_norm(x, g, 0.0), y * g, rtol=1e-14)
+    # constant vector c: c / sqrt(c^2 + eps)
+    assert np.allclose(O.rms_norm(np.full(8, 0.5), np.ones(8), 1e-6),
+                       0.5 / math.sqrt(0.25 + 1e-6), rtol=1e-15)
+
+
+# --------------------------------------------------------------------------
+# 7. shapes printed by the MLA post's section 3.2 example
+# --------------------------------------------------------------------------
+
+def test_mla_post_example_shapes():
+    g = json.load(open(os.path.join(GOLDEN, "mla_post_example_shapes.json")))
+    e = g["example"]
+    dims = synth.LayerDims(hidden=e["dim_model"], n_heads=e["nhead"],
+                           qk_nope=e["dim_head"], qk_rope=0, v_head=e["dim_head"],
+                           kv_lora=e["dim_lora"])
+    w = synth.make_weights(dims, 0.05, "f32")
+    shp = shape_of(dims)
+    N, B = e["N"], 2  # two of the example's batch of 8 suffice for shapes
+    for b in range(B):
+        x = synth.hidden_states(b, N + 1, dims.hidden, "f32")
+        r = O.mla_step(x[:N], np.arange(N), np.zeros((0, shp.row)), w, shp,
+                       return_probs=True)
+        # Julia is column-major: size(A) == (dim_out, N, B) <-> our (N, dim_out)
+        assert list(r["y"].shape[::-1]) == g["A"][:2]
+        # size(scores) == (N keys, N queries, nhead, B) <-> our p (H, N q, N k)
+        assert [r["p"].shape[2], r["p"].shape[1], r["p"].shape[0]] == g["scores"][:3]
+        rx = O.mla_step(x[N:], np.array([N]), r["rows_new"], w, shp, return_probs=True)
+        assert list(rx["y"].shape[::-1]) == g["Ax"][:2]
+        assert [rx["p"].shape[2], rx["p"].shape[1], rx["p"].shape[0]] == g["scoresx"][:3]
+
+
+# --------------------------------------------------------------------------
+# 8. the input generator (no method arithmetic, but both sides rely on it)
+# --------------------------------------------------------------------------
+
+def test_bf16_round_ties_to_even():
+    one = np.float32(1.0)
+    ulp = 2.0 ** -7
+    vals = np.array([1.0, 1 + ulp / 2, 1 + 1.5 * ulp, 1 + ulp / 4, -1 - 0.75 * ulp, 3.0e38],
+                    dtype=np.float32)
+    out = synth.bf16_round(vals)
+    assert out[0] == one
+    assert out[1] == one                        # tie -> even (1.0)
+    assert out[2] == np.float32(1 + 2 * ulp)    # tie -> even (1 + 2ulp)
+    assert out[3] == one
+    assert out[4] == np.float32(-1 - ulp)
+    assert np.all((out.view(np.uint32) & 0xFFFF) == 0)
+
+
+def test_hidden_state_stream_is_positional():
+    full = synth.hidden_states(9, 10, 16, "bf16")
+    tail = synth.hidden_states(9, 4, 16, "bf16", start=6)
+    assert np.array_equal(full[6:], tail)
+    w = synth.WORKLOADS["v2lite_decode_b64"]
+    L = synth.lengths(w)
+    assert L.shape == (64,) and L.min() >= 512 and L.max() <= 8192
