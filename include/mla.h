@@ -1,0 +1,211 @@
+/*
+ * mla.h -- C ABI of the MI355X (gfx950) Multi-Head Latent Attention library.
+ *
+ * One attention layer in the weight-absorbed form over a latent KV cache:
+ * each cached token is ONE row [c_kv (kv_lora) | k_rope (qk_rope)], the
+ * RMS-normalised latent followed by the RoPE-rotated key shared by all heads
+ * ("Multi-Head Latent Attention" post, sections 3.1 C cache and 3.6
+ * Decoupled RoPE).  Decode folds W_UK into the query so scores are taken
+ * against the latent rows directly and applies W_UV after the
+ * probability-weighted latent sum (same post, section 3.3 Absorption,
+ * eq. 3.3.3).  Prefill is causal and chunked (the "Transformer and KV Cache
+ * Basics" page, KV Cache / mask design: query positions are offset by the
+ * cached length).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Pointers.  Tensors (weights, hidden states, the cache, outputs, workspace)
+ *   are DEVICE pointers.  The small ragged metadata arrays (pos, slot,
+ *   seq_off, seq_len, cu_new, prior_len) are HOST arrays: the library
+ *   validates them on the host before any launch and copies what the kernels
+ *   need into the caller's workspace, asynchronously, through pinned staging
+ *   memory it owns.
+ * Element type.  Every tensor argument holds elements of the handle's dtype
+ *   (bf16 for MLA_BF16, float for MLA_F32), row-major, densely packed.
+ * Layouts.  Weight matrices are (out, in) row-major, like a linear layer's
+ *   weight (y = x W^T).  Per head h, q_proj rows [h*(dn+dr), (h+1)*(dn+dr))
+ *   are [q_nope_h | q_rope_h]; kv_b_proj rows [h*(dn+dv), (h+1)*(dn+dv)) are
+ *   [K_nope_h ; V_h] ("Deepseek V2 Lite Inference Engine in C", MLA notes:
+ *   the K and V values of each head are interleaved).  kv_a_proj rows are
+ *   [latent (kv_lora) ; rope key (qk_rope)].  The cache is (cache_rows, R)
+ *   with R = kv_lora + qk_rope.
+ * Ownership.  The caller owns every tensor, cache, output and workspace
+ *   buffer.  The library owns only the handle, its repacked weight copies and
+ *   its pinned staging memory.
+ * Streams.  All calls are asynchronous on the handle's HIP stream (the one
+ *   given to mla_create / mla_set_stream; NULL = the null stream).  Nothing
+ *   synchronises implicitly except mla_absorb_weights and mla_destroy.
+ * Errors.  Every call returns an mla_status.  Argument, shape and capacity
+ *   errors are detected on the host before anything is launched and leave all
+ *   device memory untouched.  MLA_ERR_HIP reports a failed HIP runtime call;
+ *   mla_last_error(h) returns a description of the last failure on h.
+ * Threads.  A handle may be used by one host thread at a time.
+ */
+#ifndef MLA_H
+#define MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_ABI_VERSION 1
+
+typedef enum mla_status {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = -1, /* null pointer, count <= 0, pos != len-1, duplicate slot ... */
+  MLA_ERR_SHAPE = -2,       /* unsupported dimensions (e.g. odd qk_rope) */
+  MLA_ERR_CAPACITY = -3,    /* a slot or a sequence's rows fall outside the cache */
+  MLA_ERR_STATE = -4,       /* call out of order (e.g. decode before absorb) */
+  MLA_ERR_HIP = -5,         /* a HIP runtime call failed */
+  MLA_ERR_WORKSPACE = -6    /* workspace missing, too small or misaligned */
+} mla_status;
+
+typedef enum mla_dtype { MLA_BF16 = 0, MLA_F32 = 1 } mla_dtype;
+
+/* Layer dimensions (MLA post, section 3.2 constructor; section 3.6 widths).
+ * qk_rope must be even (RoPE rotates pairs; MLA post section 3.7).  q_lora = 0
+ * means the query is projected straight from the hidden state (w_q); > 0
+ * means q = W_qb RMSNorm(W_qa x) (MLA post section 3.1, query compression). */
+typedef struct mla_config {
+  int32_t hidden;    /* D */
+  int32_t n_heads;   /* H */
+  int32_t qk_nope;   /* dn */
+  int32_t qk_rope;   /* dr, even; 0 allowed (no decoupled RoPE) */
+  int32_t v_head;    /* dv */
+  int32_t kv_lora;   /* dc */
+  int32_t q_lora;    /* dq, 0 = none */
+  float rope_base;   /* RoPE base, e.g. 10000 */
+  float rms_eps;     /* RMSNorm epsilon, e.g. 1e-6 */
+  float softmax_scale; /* 0 -> 1/sqrt(dn + dr) */
+  int32_t dtype;     /* mla_dtype: storage type of every tensor */
+} mla_config;
+
+typedef struct mla_ctx* mla_handle;
+
+/* Host-only check of a configuration: MLA_OK, MLA_ERR_INVALID_ARG (cfg NULL,
+ * a dimension <= 0 other than qk_rope/q_lora, a negative one, unknown dtype,
+ * non-finite or non-positive base/eps) or MLA_ERR_SHAPE (odd qk_rope).  Makes
+ * no HIP call; mla_create runs it first. */
+int mla_config_check(const mla_config* cfg);
+
+/* Host-only argument checks, run first by the corresponding calls and exported
+ * so callers (and tests without a GPU) can validate before enqueuing.  They
+ * make no HIP call and return the status the call itself would return for
+ * these arguments (weights/workspace state aside). */
+int mla_append_check(const mla_config* cfg, const int32_t* pos, const int64_t* slot, int32_t T,
+                     int64_t cache_rows);
+int mla_decode_check(const mla_config* cfg, const int32_t* pos, const int64_t* seq_off,
+                     const int32_t* seq_len, int32_t B, int64_t cache_rows);
+int mla_prefill_check(const mla_config* cfg, const int32_t* cu_new, const int32_t* prior_len,
+                      const int64_t* seq_off, int32_t B, int64_t cache_rows);
+
+/* Create a handle on the current HIP device.  stream: a hipStream_t or NULL.
+ * *out receives the handle (NULL on failure). */
+int mla_create(const mla_config* cfg, void* stream, mla_handle* out);
+
+/* Synchronise the handle's stream and free everything the library owns. */
+int mla_destroy(mla_handle h);
+
+/* Change the stream later calls are issued on. */
+int mla_set_stream(mla_handle h, void* stream);
+
+/* A1 -- copy and repack the layer weights (MLA post section 3.5: W_UK and W_UV
+ * are split out of kv_b_proj per head and kept separate, NOT multiplied into
+ * W^KQ / W^OV).  Pass w_q (H*(dn+dr), D) when q_lora == 0, else w_qa (dq, D),
+ * q_norm_g (dq) and w_qb (H*(dn+dr), dq); the unused ones must be NULL.
+ * w_kva (dc+dr, D); kv_norm_g (dc) or NULL for ones; w_kvb (H*(dn+dv), dc);
+ * w_o (D, H*dv).  All device pointers; the caller may free them on return
+ * (this call synchronises the stream).  May be called again to replace the
+ * weights. */
+int mla_absorb_weights(mla_handle h, const void* w_q, const void* w_qa,
+                       const void* q_norm_g, const void* w_qb, const void* w_kva,
+                       const void* kv_norm_g, const void* w_kvb, const void* w_o);
+
+/* Workspace bytes mla_append_latent needs for T tokens (256-byte aligned
+ * base required). */
+size_t mla_append_workspace_bytes(mla_handle h, int32_t T);
+
+/* A2 -- append T tokens to the latent cache: a = W_kva x;
+ * cache[slot[t]] = [RMSNorm(a[:dc]) * kv_norm_g | RoPE(a[dc:], pos[t])],
+ * rounded to the storage type ("Deepseek V2 Lite Inference Engine in C", MLA
+ * notes: kv_a_proj fuses the down-projection and the shared rope key; MLA post
+ * sections 3.5 and 3.7).  hidden: device (T, D).  pos, slot: HOST arrays of T
+ * entries; pos >= 0; slots must be distinct and in [0, cache_rows)
+ * (MLA_ERR_CAPACITY otherwise, the KV-cache page's overflow condition).
+ * Rows not named in slot are not touched. */
+int mla_append_latent(mla_handle h, const void* hidden, const int32_t* pos,
+                      const int64_t* slot, int32_t T, void* cache, int64_t cache_rows,
+                      void* ws, size_t ws_bytes);
+
+/* Raw scatter of T ready-made rows (T, R) into cache[slot[t]] -- the indexing
+ * half of mla_append_latent on its own (bit-exact copy).  Same slot rules. */
+size_t mla_cache_write_workspace_bytes(mla_handle h, int32_t T);
+int mla_cache_write(mla_handle h, const void* rows, const int64_t* slot, int32_t T,
+                    void* cache, int64_t cache_rows, void* ws, size_t ws_bytes);
+
+/* Workspace bytes mla_decode needs for B sequences holding total_rows cache
+ * rows in all (sum of seq_len). */
+size_t mla_decode_workspace_bytes(mla_handle h, int32_t B, int64_t total_rows);
+
+/* A3..A8 -- decode one new token per sequence over a ragged batch, absorbed
+ * form.  The caller has already appended each sequence's new row (write, then
+ * read through the new position: MLA post section 3.2), so sequence b owns
+ * cache rows [seq_off[b], seq_off[b] + seq_len[b]) holding positions
+ * 0 .. seq_len[b]-1 and its query is at pos[b] == seq_len[b] - 1.
+ *   hidden: device (B, D) -- the new tokens' hidden states.
+ *   pos, seq_off, seq_len: HOST arrays of B entries.
+ *   out: device (B, D) -- y = W_o [W_UV_h o_lat_h]_h.
+ * Errors: B <= 0 or NULL -> INVALID_ARG; seq_len[b] < 1 or pos[b] !=
+ * seq_len[b]-1 -> INVALID_ARG; seq_off[b] < 0 or seq_off[b]+seq_len[b] >
+ * cache_rows -> CAPACITY; weights not absorbed -> STATE; workspace too small
+ * -> WORKSPACE. */
+int mla_decode(mla_handle h, const void* hidden, const int32_t* pos,
+               const int64_t* seq_off, const int32_t* seq_len, int32_t B,
+               const void* cache, int64_t cache_rows, void* out, void* ws,
+               size_t ws_bytes);
+
+/* Where the staged intermediates of the last mla_decode with these (B,
+ * total_rows) live inside its workspace, as byte offsets from ws:
+ *   q_cat (B, H, R) storage type: [W_UK_h^T q_nope_h | RoPE(q_rope_h)] * scale
+ *   o_lat (B, H, dc) storage type: the probability-weighted latent sum.
+ * For staged parity tests; valid until the workspace is reused. */
+int mla_decode_stage_offsets(mla_handle h, int32_t B, int64_t total_rows,
+                             size_t* q_cat_off, size_t* o_lat_off);
+
+/* Workspace bytes mla_prefill needs for T new tokens in B sequences whose
+ * caches hold total_key_rows rows in all after the append. */
+size_t mla_prefill_workspace_bytes(mla_handle h, int32_t T, int32_t B,
+                                   int64_t total_key_rows);
+
+/* P1 -- causal chunked prefill.  Sequence b has prior_len[b] cached rows and
+ * new tokens hidden[cu_new[b] .. cu_new[b+1]) at positions prior_len[b],
+ * prior_len[b]+1, ...; the caller has already appended the new rows, so the
+ * sequence owns cache rows [seq_off[b], seq_off[b] + prior_len[b] + n_b).
+ * Each new token attends to rows 0..its position (KV-cache page: the
+ * position-offset causal mask).
+ *   hidden: device (T, D), T = cu_new[B]; out: device (T, D).
+ *   cu_new: HOST (B+1), cu_new[0] = 0, non-decreasing; prior_len, seq_off:
+ *   HOST (B).
+ * Errors as for mla_decode (CAPACITY if a sequence's rows leave the cache). */
+int mla_prefill(mla_handle h, const void* hidden, const int32_t* cu_new,
+                const int32_t* prior_len, const int64_t* seq_off, int32_t B,
+                const void* cache, int64_t cache_rows, void* out, void* ws,
+                size_t ws_bytes);
+
+/* Static text for a status code. */
+const char* mla_status_string(int status);
+
+/* Description of the last failure on h (empty string if none). */
+const char* mla_last_error(mla_handle h);
+
+/* ABI version the library was built with (MLA_ABI_VERSION). */
+int mla_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H */

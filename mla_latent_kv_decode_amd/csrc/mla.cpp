@@ -1,0 +1,805 @@
+// Host layer of the MLA library: the C ABI of include/mla.h.
+//
+// Validation of every argument happens here, on the host, before anything is
+// launched.  Ragged metadata arrive as host arrays; the decode work list is
+// built here and copied into the caller's workspace from pinned staging
+// memory the handle owns (a small ring, so a call never overwrites staging
+// data an earlier asynchronous copy may still be reading).
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+#include <unordered_set>
+#include <vector>
+
+#include "../../include/mla.h"
+#include "kernels.h"
+
+using mla::bf16;
+using mla::DecodeMeta;
+using mla::DecodeSeg;
+using mla::Dims;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kRing = 4;
+
+size_t align_up(size_t v, size_t a = kAlign) { return (v + a - 1) / a * a; }
+
+struct Staging {
+  void* host = nullptr;
+  size_t cap = 0;
+  hipEvent_t ev = nullptr;
+  bool pending = false;
+};
+
+}  // namespace
+
+struct mla_ctx {
+  mla_config cfg{};
+  Dims d{};
+  hipStream_t stream = nullptr;
+  int device = 0;
+  int n_cu = 256;
+  size_t esz = 2;
+  bool absorbed = false;
+  bool mfma = false;  // bf16 MFMA kernels apply to these shapes
+  // owned device weights
+  void* w_q = nullptr;
+  void* w_qa = nullptr;
+  void* q_norm_g = nullptr;
+  void* w_qb = nullptr;
+  void* w_kva = nullptr;
+  void* kv_norm_g = nullptr;
+  void* w_kvb = nullptr;
+  void* w_ukT = nullptr;  // (H, dc, dn): q_abs = q_nope . W_ukT^T per head
+  void* w_uv = nullptr;   // (H, dv, dc)
+  void* w_o = nullptr;
+  Staging ring[kRing];
+  int ring_next = 0;
+  std::string err;
+};
+
+namespace {
+
+int fail(mla_ctx* h, int code, const char* fmt, ...) {
+  if (h) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    h->err = buf;
+  }
+  return code;
+}
+
+#define HIP_TRY(h, call)                                                              \
+  do {                                                                                \
+    hipError_t e_ = (call);                                                           \
+    if (e_ != hipSuccess)                                                             \
+      return fail((h), MLA_ERR_HIP, "%s failed: %s", #call, hipGetErrorString(e_));  \
+  } while (0)
+
+// Makes the handle's device current for the duration of a call.
+struct DeviceGuard {
+  int prev = -1;
+  bool ok = true;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) { ok = false; return; }
+    if (prev != dev && hipSetDevice(dev) != hipSuccess) ok = false;
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+  }
+};
+
+int check_launch(mla_ctx* h, const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(h, MLA_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
+  return MLA_OK;
+}
+
+// Copy `bytes` of host data to device `dst` on the handle's stream through the
+// pinned staging ring.
+int stage_upload(mla_ctx* h, void* dst, const void* src, size_t bytes) {
+  if (bytes == 0) return MLA_OK;
+  Staging& s = h->ring[h->ring_next];
+  h->ring_next = (h->ring_next + 1) % kRing;
+  if (s.pending) {
+    HIP_TRY(h, hipEventSynchronize(s.ev));
+    s.pending = false;
+  }
+  if (s.cap < bytes) {
+    if (s.host) HIP_TRY(h, hipHostFree(s.host));
+    s.host = nullptr;
+    s.cap = 0;
+    const size_t cap = std::max(align_up(bytes, 1 << 16), (size_t)1 << 16);
+    HIP_TRY(h, hipHostMalloc(&s.host, cap, hipHostMallocDefault));
+    s.cap = cap;
+  }
+  if (!s.ev) HIP_TRY(h, hipEventCreateWithFlags(&s.ev, hipEventDisableTiming));
+  memcpy(s.host, src, bytes);
+  HIP_TRY(h, hipMemcpyAsync(dst, s.host, bytes, hipMemcpyHostToDevice, h->stream));
+  HIP_TRY(h, hipEventRecord(s.ev, h->stream));
+  s.pending = true;
+  return MLA_OK;
+}
+
+// Workspace carving: regions are 256-byte aligned offsets from the base.
+struct Carve {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  }
+};
+
+bool is_f32(const mla_ctx* h) { return h->cfg.dtype == MLA_F32; }
+
+// split-K factor for a GEMM of M x N x K over `batch` problems: aims at >= ~2
+// blocks per CU for the MFMA kernel; K chunks stay whole multiples of 32.
+int choose_ksplit(const mla_ctx* h, int M, int N, int K, int batch) {
+  if (!h->mfma) return 1;
+  const long blocks = (long)((N + 63) / 64) * ((M + 63) / 64) * batch;
+  int ks = 1;
+  while (ks < 16 && blocks * ks < 2L * h->n_cu && (K / 32) % (ks * 2) == 0) ks *= 2;
+  return ks;
+}
+
+template <typename T>
+void gemm_t(const mla_ctx* h, const T* A, int64_t lda, int64_t sA, const T* W, int64_t ldw,
+            int64_t sW, float* C, int M, int N, int K, int batch, int ksplit);
+
+template <>
+void gemm_t<float>(const mla_ctx* h, const float* A, int64_t lda, int64_t sA, const float* W,
+                   int64_t ldw, int64_t sW, float* C, int M, int N, int K, int batch,
+                   int ksplit) {
+  mla::gemm_generic<float>(A, lda, sA, W, ldw, sW, C, M, N, K, batch, ksplit, h->stream);
+}
+
+template <>
+void gemm_t<bf16>(const mla_ctx* h, const bf16* A, int64_t lda, int64_t sA, const bf16* W,
+                  int64_t ldw, int64_t sW, float* C, int M, int N, int K, int batch,
+                  int ksplit) {
+  if (h->mfma && K % (32 * ksplit) == 0 && N % 16 == 0)
+    mla::gemm_bf16_mfma(A, lda, sA, W, ldw, sW, C, M, N, K, batch, ksplit, h->stream);
+  else
+    mla::gemm_generic<bf16>(A, lda, sA, W, ldw, sW, C, M, N, K, batch, ksplit, h->stream);
+}
+
+// ------------------------------------------------------------------------
+// decode plan
+// ------------------------------------------------------------------------
+struct DecodeLayout {
+  int ks_qa = 1, ks_q = 1, ks_abs = 1, ks_uv = 1, ks_o = 1;
+  int max_segs = 0;
+  size_t meta, cq_part, cq, q_part, q_nope, q_cat, abs_part, acc, ml, o_lat, uv_part, o, y_part;
+  size_t total = 0;
+};
+
+int max_parts(const mla_ctx* h, int64_t total_rows) {
+  int64_t p = (total_rows + 63) / 64;
+  if (p > h->n_cu) p = h->n_cu;
+  if (p < 1) p = 1;
+  return (int)p;
+}
+
+size_t meta_bytes(int B, int parts, int max_segs) {
+  return align_up((size_t)B * 8) + 4 * align_up((size_t)B * 4) + align_up((size_t)(parts + 1) * 4) +
+         align_up((size_t)max_segs * sizeof(DecodeSeg));
+}
+
+DecodeLayout decode_layout(const mla_ctx* h, int B, int64_t total_rows) {
+  const Dims& d = h->d;
+  DecodeLayout L;
+  const int parts = max_parts(h, total_rows);
+  L.max_segs = parts + B;
+  if (d.dq) {
+    L.ks_qa = choose_ksplit(h, B, d.dq, d.D, 1);
+    L.ks_q = choose_ksplit(h, B, d.H * (d.dn + d.dr), d.dq, 1);
+  } else {
+    L.ks_q = choose_ksplit(h, B, d.H * (d.dn + d.dr), d.D, 1);
+  }
+  L.ks_abs = choose_ksplit(h, B, d.dc, d.dn, d.H);
+  L.ks_uv = choose_ksplit(h, B, d.dv, d.dc, d.H);
+  L.ks_o = choose_ksplit(h, B, d.D, d.H * d.dv, 1);
+  const size_t e = h->esz;
+  Carve c;
+  L.meta = c.take(meta_bytes(B, parts, L.max_segs));
+  L.cq_part = c.take(d.dq ? (size_t)L.ks_qa * B * d.dq * 4 : 0);
+  L.cq = c.take(d.dq ? (size_t)B * d.dq * e : 0);
+  L.q_part = c.take((size_t)L.ks_q * B * d.H * (d.dn + d.dr) * 4);
+  L.q_nope = c.take((size_t)B * d.H * d.dn * e);
+  L.q_cat = c.take((size_t)B * d.H * d.R * e);
+  L.abs_part = c.take((size_t)L.ks_abs * d.H * B * d.dc * 4);
+  L.acc = c.take((size_t)L.max_segs * d.H * d.dc * 4);
+  L.ml = c.take((size_t)L.max_segs * d.H * 2 * 4);
+  L.o_lat = c.take((size_t)B * d.H * d.dc * e);
+  L.uv_part = c.take((size_t)L.ks_uv * d.H * B * d.dv * 4);
+  L.o = c.take((size_t)B * d.H * d.dv * e);
+  L.y_part = c.take((size_t)L.ks_o * B * d.D * 4);
+  L.total = c.off;
+  return L;
+}
+
+// Host-side work list: equal spans of the concatenated rows, cut at sequence
+// boundaries.  Returns parts and fills the packed metadata blob.
+int build_decode_meta(const mla_ctx* h, int B, const int64_t* seq_off, const int32_t* seq_len,
+                      const int32_t* pos, int64_t total, std::vector<char>& blob,
+                      size_t* o_seq_off, size_t* o_seq_len, size_t* o_pos, size_t* o_pstart,
+                      size_t* o_nseg, size_t* o_part, size_t* o_segs, int* nseg_total) {
+  int parts = max_parts(h, total);
+  const int64_t per = (total + parts - 1) / parts;
+  parts = (int)((total + per - 1) / per);
+  std::vector<DecodeSeg> segs;
+  std::vector<int32_t> part_begin(1, 0), pstart(B, 0), nseg(B, 0);
+  int b = 0;
+  int32_t in_b = 0;
+  int64_t cur = 0;
+  for (int p = 0; p < parts; ++p) {
+    const int64_t hi = std::min(total, (int64_t)(p + 1) * per);
+    while (cur < hi) {
+      const int32_t take = (int32_t)std::min<int64_t>(hi - cur, (int64_t)seq_len[b] - in_b);
+      if (in_b == 0) pstart[b] = (int32_t)segs.size();
+      segs.push_back(DecodeSeg{b, in_b, in_b + take, (int32_t)segs.size()});
+      nseg[b]++;
+      cur += take;
+      in_b += take;
+      if (in_b == seq_len[b]) {
+        ++b;
+        in_b = 0;
+      }
+    }
+    part_begin.push_back((int32_t)segs.size());
+  }
+  Carve c;
+  *o_seq_off = c.take((size_t)B * 8);
+  *o_seq_len = c.take((size_t)B * 4);
+  *o_pos = c.take((size_t)B * 4);
+  *o_pstart = c.take((size_t)B * 4);
+  *o_nseg = c.take((size_t)B * 4);
+  *o_part = c.take((size_t)(parts + 1) * 4);
+  *o_segs = c.take(segs.size() * sizeof(DecodeSeg));
+  blob.assign(c.off, 0);
+  memcpy(blob.data() + *o_seq_off, seq_off, (size_t)B * 8);
+  memcpy(blob.data() + *o_seq_len, seq_len, (size_t)B * 4);
+  memcpy(blob.data() + *o_pos, pos, (size_t)B * 4);
+  memcpy(blob.data() + *o_pstart, pstart.data(), (size_t)B * 4);
+  memcpy(blob.data() + *o_nseg, nseg.data(), (size_t)B * 4);
+  memcpy(blob.data() + *o_part, part_begin.data(), part_begin.size() * 4);
+  memcpy(blob.data() + *o_segs, segs.data(), segs.size() * sizeof(DecodeSeg));
+  *nseg_total = (int)segs.size();
+  return parts;
+}
+
+int check_ws(mla_ctx* h, void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return MLA_OK;
+  if (!ws) return fail(h, MLA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if (((uintptr_t)ws) % kAlign)
+    return fail(h, MLA_ERR_WORKSPACE, "workspace must be %zu-byte aligned", kAlign);
+  if (ws_bytes < need)
+    return fail(h, MLA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, need);
+  return MLA_OK;
+}
+
+template <typename T>
+T* at(void* base, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(base) + off);
+}
+
+}  // namespace
+
+// ==========================================================================
+// C ABI (linkage comes from the extern "C" declarations in mla.h)
+// ==========================================================================
+
+int mla_abi_version(void) { return MLA_ABI_VERSION; }
+
+const char* mla_status_string(int s) {
+  switch (s) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_INVALID_ARG: return "invalid argument";
+    case MLA_ERR_SHAPE: return "unsupported shape";
+    case MLA_ERR_CAPACITY: return "cache capacity exceeded";
+    case MLA_ERR_STATE: return "call out of order";
+    case MLA_ERR_HIP: return "HIP runtime error";
+    case MLA_ERR_WORKSPACE: return "workspace too small or misaligned";
+    default: return "unknown status";
+  }
+}
+
+const char* mla_last_error(mla_handle h) { return h ? h->err.c_str() : "null handle"; }
+
+int mla_config_check(const mla_config* c) {
+  if (!c) return MLA_ERR_INVALID_ARG;
+  if (c->hidden <= 0 || c->n_heads <= 0 || c->qk_nope <= 0 || c->v_head <= 0 || c->kv_lora <= 0)
+    return MLA_ERR_INVALID_ARG;
+  if (c->qk_rope < 0 || c->q_lora < 0) return MLA_ERR_INVALID_ARG;
+  if (c->dtype != MLA_BF16 && c->dtype != MLA_F32) return MLA_ERR_INVALID_ARG;
+  if (!(c->rope_base > 0.f) || !isfinite(c->rope_base)) return MLA_ERR_INVALID_ARG;
+  if (!(c->rms_eps > 0.f) || !isfinite(c->rms_eps)) return MLA_ERR_INVALID_ARG;
+  if (!(c->softmax_scale >= 0.f) || !isfinite(c->softmax_scale)) return MLA_ERR_INVALID_ARG;
+  if (c->qk_rope % 2) return MLA_ERR_SHAPE;  // RoPE rotates pairs
+  // kernel limits of the VALU paths: latent width and v_head per thread block
+  if (c->kv_lora > 1024 || c->v_head > 256) return MLA_ERR_SHAPE;
+  return MLA_OK;
+}
+
+static int check_slots_pure(const int64_t* slot, int32_t T, int64_t cache_rows, int32_t* bad) {
+  std::unordered_set<int64_t> seen;
+  seen.reserve((size_t)T * 2);
+  for (int32_t t = 0; t < T; ++t) {
+    *bad = t;
+    if (slot[t] < 0 || slot[t] >= cache_rows) return MLA_ERR_CAPACITY;
+    if (!seen.insert(slot[t]).second) return MLA_ERR_INVALID_ARG;
+  }
+  return MLA_OK;
+}
+
+int mla_append_check(const mla_config* cfg, const int32_t* pos, const int64_t* slot, int32_t T,
+                     int64_t cache_rows) {
+  int rc = mla_config_check(cfg);
+  if (rc) return rc;
+  if (T <= 0 || !pos || !slot || cache_rows <= 0) return MLA_ERR_INVALID_ARG;
+  for (int32_t t = 0; t < T; ++t)
+    if (pos[t] < 0) return MLA_ERR_INVALID_ARG;
+  int32_t bad = 0;
+  return check_slots_pure(slot, T, cache_rows, &bad);
+}
+
+int mla_decode_check(const mla_config* cfg, const int32_t* pos, const int64_t* seq_off,
+                     const int32_t* seq_len, int32_t B, int64_t cache_rows) {
+  int rc = mla_config_check(cfg);
+  if (rc) return rc;
+  if (B <= 0 || !pos || !seq_off || !seq_len || cache_rows <= 0) return MLA_ERR_INVALID_ARG;
+  for (int32_t b = 0; b < B; ++b) {
+    if (seq_len[b] < 1 || pos[b] != seq_len[b] - 1) return MLA_ERR_INVALID_ARG;
+    if (seq_off[b] < 0 || seq_off[b] > cache_rows - seq_len[b]) return MLA_ERR_CAPACITY;
+  }
+  return MLA_OK;
+}
+
+int mla_prefill_check(const mla_config* cfg, const int32_t* cu_new, const int32_t* prior_len,
+                      const int64_t* seq_off, int32_t B, int64_t cache_rows) {
+  int rc = mla_config_check(cfg);
+  if (rc) return rc;
+  if (B <= 0 || !cu_new || !prior_len || !seq_off || cache_rows <= 0) return MLA_ERR_INVALID_ARG;
+  if (cu_new[0] != 0) return MLA_ERR_INVALID_ARG;
+  for (int32_t b = 0; b < B; ++b) {
+    if (cu_new[b + 1] < cu_new[b] || prior_len[b] < 0) return MLA_ERR_INVALID_ARG;
+    const int64_t len = (int64_t)prior_len[b] + (cu_new[b + 1] - cu_new[b]);
+    if (seq_off[b] < 0 || seq_off[b] > cache_rows - len) return MLA_ERR_CAPACITY;
+  }
+  if (cu_new[B] <= 0) return MLA_ERR_INVALID_ARG;
+  return MLA_OK;
+}
+
+int mla_create(const mla_config* cfg, void* stream, mla_handle* out) {
+  if (!out) return MLA_ERR_INVALID_ARG;
+  *out = nullptr;
+  int rc = mla_config_check(cfg);
+  if (rc != MLA_OK) return rc;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_HIP;
+  mla_ctx* h = new mla_ctx();
+  h->cfg = *cfg;
+  h->device = dev;
+  h->stream = (hipStream_t)stream;
+  h->esz = cfg->dtype == MLA_F32 ? 4 : 2;
+  Dims& d = h->d;
+  d.D = cfg->hidden; d.H = cfg->n_heads; d.dn = cfg->qk_nope; d.dr = cfg->qk_rope;
+  d.dv = cfg->v_head; d.dc = cfg->kv_lora; d.dq = cfg->q_lora; d.R = d.dc + d.dr;
+  d.rope_base = cfg->rope_base; d.eps = cfg->rms_eps;
+  d.scale = cfg->softmax_scale > 0.f ? cfg->softmax_scale : 1.0f / sqrtf((float)(d.dn + d.dr));
+  int ncu = 0;
+  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+      ncu > 0)
+    h->n_cu = ncu;
+  h->mfma = cfg->dtype == MLA_BF16 && d.dc == 512 && d.dr == 64 && d.H % 16 == 0;
+  *out = h;
+  return MLA_OK;
+}
+
+static void free_weights(mla_ctx* h) {
+  void** ws[] = {&h->w_q, &h->w_qa, &h->q_norm_g, &h->w_qb, &h->w_kva,
+                 &h->kv_norm_g, &h->w_kvb, &h->w_ukT, &h->w_uv, &h->w_o};
+  for (void** p : ws) {
+    if (*p) (void)hipFree(*p);
+    *p = nullptr;
+  }
+  h->absorbed = false;
+}
+
+int mla_destroy(mla_handle h) {
+  if (!h) return MLA_ERR_INVALID_ARG;
+  DeviceGuard g(h->device);
+  (void)hipStreamSynchronize(h->stream);
+  free_weights(h);
+  for (auto& s : h->ring) {
+    if (s.ev) (void)hipEventDestroy(s.ev);
+    if (s.host) (void)hipHostFree(s.host);
+  }
+  delete h;
+  return MLA_OK;
+}
+
+int mla_set_stream(mla_handle h, void* stream) {
+  if (!h) return MLA_ERR_INVALID_ARG;
+  h->stream = (hipStream_t)stream;
+  return MLA_OK;
+}
+
+int mla_absorb_weights(mla_handle h, const void* w_q, const void* w_qa, const void* q_norm_g,
+                       const void* w_qb, const void* w_kva, const void* kv_norm_g,
+                       const void* w_kvb, const void* w_o) {
+  if (!h) return MLA_ERR_INVALID_ARG;
+  const Dims& d = h->d;
+  if (d.dq) {
+    if (!w_qa || !q_norm_g || !w_qb || w_q)
+      return fail(h, MLA_ERR_INVALID_ARG, "q_lora > 0 needs w_qa, q_norm_g, w_qb and no w_q");
+  } else if (!w_q || w_qa || q_norm_g || w_qb) {
+    return fail(h, MLA_ERR_INVALID_ARG, "q_lora == 0 needs w_q and no w_qa/q_norm_g/w_qb");
+  }
+  if (!w_kva || !w_kvb || !w_o) return fail(h, MLA_ERR_INVALID_ARG, "missing weight pointer");
+  DeviceGuard g(h->device);
+  if (!g.ok) return fail(h, MLA_ERR_HIP, "cannot select device %d", h->device);
+  free_weights(h);
+  const size_t e = h->esz;
+  auto dup = [&](void** dst, const void* src, size_t n) -> int {
+    HIP_TRY(h, hipMalloc(dst, n * e));
+    HIP_TRY(h, hipMemcpyAsync(*dst, src, n * e, hipMemcpyDeviceToDevice, h->stream));
+    return MLA_OK;
+  };
+  int rc;
+  const size_t qw = (size_t)d.H * (d.dn + d.dr);
+  if (d.dq) {
+    if ((rc = dup(&h->w_qa, w_qa, (size_t)d.dq * d.D))) return rc;
+    if ((rc = dup(&h->q_norm_g, q_norm_g, (size_t)d.dq))) return rc;
+    if ((rc = dup(&h->w_qb, w_qb, qw * d.dq))) return rc;
+  } else if ((rc = dup(&h->w_q, w_q, qw * d.D))) {
+    return rc;
+  }
+  if ((rc = dup(&h->w_kva, w_kva, (size_t)d.R * d.D))) return rc;
+  if (kv_norm_g) {
+    if ((rc = dup(&h->kv_norm_g, kv_norm_g, (size_t)d.dc))) return rc;
+  }
+  if ((rc = dup(&h->w_kvb, w_kvb, (size_t)d.H * (d.dn + d.dv) * d.dc))) return rc;
+  if ((rc = dup(&h->w_o, w_o, (size_t)d.D * d.H * d.dv))) return rc;
+  // W_UV per head: rows dn .. dn+dv of each head's kv_b block, packed (H, dv, dc)
+  HIP_TRY(h, hipMalloc(&h->w_uv, (size_t)d.H * d.dv * d.dc * e));
+  HIP_TRY(h, hipMemcpy2DAsync(h->w_uv, (size_t)d.dv * d.dc * e,
+                              static_cast<const char*>(w_kvb) + (size_t)d.dn * d.dc * e,
+                              (size_t)(d.dn + d.dv) * d.dc * e, (size_t)d.dv * d.dc * e, d.H,
+                              hipMemcpyDeviceToDevice, h->stream));
+  // W_UK^T per head (H, dc, dn) through a transposing copy
+  HIP_TRY(h, hipMalloc(&h->w_ukT, (size_t)d.H * d.dc * d.dn * e));
+  if (is_f32(h))
+    mla::transpose_heads<float>((const float*)w_kvb, (float*)h->w_ukT, d.H, d.dn, d.dc,
+                                (int64_t)(d.dn + d.dv) * d.dc, h->stream);
+  else
+    mla::transpose_heads<bf16>((const bf16*)w_kvb, (bf16*)h->w_ukT, d.H, d.dn, d.dc,
+                               (int64_t)(d.dn + d.dv) * d.dc, h->stream);
+  if ((rc = check_launch(h, "transpose_heads"))) return rc;
+  HIP_TRY(h, hipStreamSynchronize(h->stream));
+  h->absorbed = true;
+  return MLA_OK;
+}
+
+size_t mla_append_workspace_bytes(mla_handle h, int32_t T) {
+  if (!h || T <= 0) return 0;
+  Carve c;
+  c.take((size_t)T * 4);
+  c.take((size_t)T * 8);
+  const int ks = choose_ksplit(h, T, h->d.R, h->d.D, 1);
+  c.take((size_t)ks * T * h->d.R * 4);
+  return c.off;
+}
+
+int mla_append_latent(mla_handle h, const void* hidden, const int32_t* pos, const int64_t* slot,
+                      int32_t T, void* cache, int64_t cache_rows, void* ws, size_t ws_bytes) {
+  if (!h) return MLA_ERR_INVALID_ARG;
+  if (!hidden || !cache) return fail(h, MLA_ERR_INVALID_ARG, "append: NULL tensor");
+  int rc = mla_append_check(&h->cfg, pos, slot, T, cache_rows);
+  if (rc) return fail(h, rc, "append: %s (T=%d, cache_rows=%lld)", mla_status_string(rc), T,
+                      (long long)cache_rows);
+  if (!h->absorbed) return fail(h, MLA_ERR_STATE, "append before mla_absorb_weights");
+  const size_t need = mla_append_workspace_bytes(h, T);
+  if ((rc = check_ws(h, ws, ws_bytes, need))) return rc;
+  DeviceGuard g(h->device);
+  if (!g.ok) return fail(h, MLA_ERR_HIP, "cannot select device %d", h->device);
+  Carve c;
+  const size_t o_pos = c.take((size_t)T * 4), o_slot = c.take((size_t)T * 8);
+  const int ks = choose_ksplit(h, T, h->d.R, h->d.D, 1);
+  const size_t o_part = c.take((size_t)ks * T * h->d.R * 4);
+  std::vector<char> blob(o_part, 0);
+  memcpy(blob.data() + o_pos, pos, (size_t)T * 4);
+  memcpy(blob.data() + o_slot, slot, (size_t)T * 8);
+  if ((rc = stage_upload(h, ws, blob.data(), blob.size()))) return rc;
+  const Dims& d = h->d;
+  float* part = at<float>(ws, o_part);
+  if (is_f32(h)) {
+    gemm_t<float>(h, (const float*)hidden, d.D, 0, (const float*)h->w_kva, d.D, 0, part, T, d.R,
+                  d.D, 1, ks);
+    mla::append_rows<float>(part, ks, T, at<int32_t>(ws, o_pos), at<int64_t>(ws, o_slot),
+                            (const float*)h->kv_norm_g, (float*)cache, d, h->stream);
+  } else {
+    gemm_t<bf16>(h, (const bf16*)hidden, d.D, 0, (const bf16*)h->w_kva, d.D, 0, part, T, d.R, d.D,
+                 1, ks);
+    mla::append_rows<bf16>(part, ks, T, at<int32_t>(ws, o_pos), at<int64_t>(ws, o_slot),
+                           (const bf16*)h->kv_norm_g, (bf16*)cache, d, h->stream);
+  }
+  return check_launch(h, "append");
+}
+
+size_t mla_cache_write_workspace_bytes(mla_handle h, int32_t T) {
+  if (!h || T <= 0) return 0;
+  return align_up((size_t)T * 8);
+}
+
+int mla_cache_write(mla_handle h, const void* rows, const int64_t* slot, int32_t T, void* cache,
+                    int64_t cache_rows, void* ws, size_t ws_bytes) {
+  if (!h) return MLA_ERR_INVALID_ARG;
+  if (T <= 0 || !rows || !slot || !cache || cache_rows <= 0)
+    return fail(h, MLA_ERR_INVALID_ARG, "cache_write: bad argument (T=%d)", T);
+  int32_t bad = 0;
+  int rc = check_slots_pure(slot, T, cache_rows, &bad);
+  if (rc) return fail(h, rc, "cache_write: slot[%d] = %lld is out of range or repeated", bad,
+                      (long long)slot[bad]);
+  if ((rc = check_ws(h, ws, ws_bytes, mla_cache_write_workspace_bytes(h, T)))) return rc;
+  DeviceGuard g(h->device);
+  if (!g.ok) return fail(h, MLA_ERR_HIP, "cannot select device %d", h->device);
+  if ((rc = stage_upload(h, ws, slot, (size_t)T * 8))) return rc;
+  if (is_f32(h))
+    mla::cache_write<float>((const float*)rows, (const int64_t*)ws, T, h->d.R, (float*)cache,
+                            h->stream);
+  else
+    mla::cache_write<bf16>((const bf16*)rows, (const int64_t*)ws, T, h->d.R, (bf16*)cache,
+                           h->stream);
+  return check_launch(h, "cache_write");
+}
+
+size_t mla_decode_workspace_bytes(mla_handle h, int32_t B, int64_t total_rows) {
+  if (!h || B <= 0 || total_rows <= 0) return 0;
+  return decode_layout(h, B, total_rows).total;
+}
+
+int mla_decode_stage_offsets(mla_handle h, int32_t B, int64_t total_rows, size_t* q_cat_off,
+                             size_t* o_lat_off) {
+  if (!h || B <= 0 || total_rows <= 0 || !q_cat_off || !o_lat_off) return MLA_ERR_INVALID_ARG;
+  const DecodeLayout L = decode_layout(h, B, total_rows);
+  *q_cat_off = L.q_cat;
+  *o_lat_off = L.o_lat;
+  return MLA_OK;
+}
+
+template <typename T>
+static void run_q_path(mla_ctx* h, const T* x, int ntok, const DecodeLayout* L, void* ws,
+                       float* cq_part, T* cq, float* q_part, int ks_qa, int ks_q, T* q_nope,
+                       T* rope_out, int64_t tok_stride, int64_t head_stride, float scale,
+                       const int32_t* pos_dev) {
+  (void)L;
+  (void)ws;
+  const Dims& d = h->d;
+  const int qw = d.H * (d.dn + d.dr);
+  if (d.dq) {
+    gemm_t<T>(h, x, d.D, 0, (const T*)h->w_qa, d.D, 0, cq_part, ntok, d.dq, d.D, 1, ks_qa);
+    mla::rmsnorm_rows<T>(cq_part, ks_qa, ntok, d.dq, (const T*)h->q_norm_g, d.eps, cq, h->stream);
+    gemm_t<T>(h, cq, d.dq, 0, (const T*)h->w_qb, d.dq, 0, q_part, ntok, qw, d.dq, 1, ks_q);
+  } else {
+    gemm_t<T>(h, x, d.D, 0, (const T*)h->w_q, d.D, 0, q_part, ntok, qw, d.D, 1, ks_q);
+  }
+  mla::q_finish<T>(q_part, ks_q, ntok, pos_dev, q_nope, rope_out, tok_stride, head_stride, scale,
+                   d, h->stream);
+}
+
+template <typename T>
+static int run_decode(mla_ctx* h, const T* hidden, int B, const T* cache, T* out, void* ws,
+                      const DecodeLayout& L, const DecodeMeta& mt, int parts, int nseg_total,
+                      const int32_t* pos_dev) {
+  const Dims& d = h->d;
+  T* q_nope = at<T>(ws, L.q_nope);
+  T* q_cat = at<T>(ws, L.q_cat);
+  // A3: query projection + RoPE of the rope part (scaled, into q_cat)
+  run_q_path<T>(h, hidden, B, &L, ws, at<float>(ws, L.cq_part), at<T>(ws, L.cq),
+                at<float>(ws, L.q_part), L.ks_qa, L.ks_q, q_nope, q_cat + d.dc,
+                (int64_t)d.H * d.R, d.R, d.scale, pos_dev);
+  // A4: absorbed query q_abs_h = W_UK_h^T q_nope_h, scaled into q_cat[:, :, :dc]
+  float* abs_part = at<float>(ws, L.abs_part);
+  gemm_t<T>(h, q_nope, (int64_t)d.H * d.dn, d.dn, (const T*)h->w_ukT, d.dn, (int64_t)d.dc * d.dn,
+            abs_part, B, d.dc, d.dn, d.H, L.ks_abs);
+  mla::sum_store<T>(abs_part, L.ks_abs, B, d.dc, d.H, q_cat, (int64_t)d.H * d.R, d.R, d.scale,
+                    h->stream);
+  // A5: split-S latent attention core
+  float* acc = at<float>(ws, L.acc);
+  float* ml = at<float>(ws, L.ml);
+  if constexpr (sizeof(T) == 2) {
+    if (h->mfma)
+      mla::decode_core_mfma(q_cat, cache, mt, parts, B, acc, ml, d, h->stream);
+    else
+      mla::decode_core_generic<T>(q_cat, cache, mt, nseg_total, acc, ml, d, h->stream);
+  } else {
+    mla::decode_core_generic<T>(q_cat, cache, mt, nseg_total, acc, ml, d, h->stream);
+  }
+  // A6: combine the partials of each sequence
+  T* o_lat = at<T>(ws, L.o_lat);
+  mla::decode_combine<T>(acc, ml, mt, B, o_lat, d, h->stream);
+  // A7: o_h = W_UV_h o_lat_h
+  float* uv_part = at<float>(ws, L.uv_part);
+  T* o = at<T>(ws, L.o);
+  gemm_t<T>(h, o_lat, (int64_t)d.H * d.dc, d.dc, (const T*)h->w_uv, d.dc, (int64_t)d.dv * d.dc,
+            uv_part, B, d.dv, d.dc, d.H, L.ks_uv);
+  mla::sum_store<T>(uv_part, L.ks_uv, B, d.dv, d.H, o, (int64_t)d.H * d.dv, d.dv, 1.f, h->stream);
+  // A8: y = W_o o
+  float* y_part = at<float>(ws, L.y_part);
+  gemm_t<T>(h, o, (int64_t)d.H * d.dv, 0, (const T*)h->w_o, (int64_t)d.H * d.dv, 0, y_part, B, d.D,
+            d.H * d.dv, 1, L.ks_o);
+  mla::sum_store<T>(y_part, L.ks_o, B, d.D, 1, out, d.D, 0, 1.f, h->stream);
+  return check_launch(h, "decode");
+}
+
+int mla_decode(mla_handle h, const void* hidden, const int32_t* pos, const int64_t* seq_off,
+               const int32_t* seq_len, int32_t B, const void* cache, int64_t cache_rows, void* out,
+               void* ws, size_t ws_bytes) {
+  if (!h) return MLA_ERR_INVALID_ARG;
+  if (!hidden || !cache || !out) return fail(h, MLA_ERR_INVALID_ARG, "decode: NULL tensor");
+  int rc0 = mla_decode_check(&h->cfg, pos, seq_off, seq_len, B, cache_rows);
+  if (rc0) return fail(h, rc0, "decode: %s (B=%d, cache_rows=%lld)", mla_status_string(rc0), B,
+                       (long long)cache_rows);
+  if (!h->absorbed) return fail(h, MLA_ERR_STATE, "decode before mla_absorb_weights");
+  int64_t total = 0;
+  for (int32_t b = 0; b < B; ++b) total += seq_len[b];
+  const DecodeLayout L = decode_layout(h, B, total);
+  int rc = check_ws(h, ws, ws_bytes, L.total);
+  if (rc) return rc;
+  DeviceGuard g(h->device);
+  if (!g.ok) return fail(h, MLA_ERR_HIP, "cannot select device %d", h->device);
+  std::vector<char> blob;
+  size_t o_so, o_sl, o_pos, o_ps, o_ns, o_pb, o_sg;
+  int nseg_total = 0;
+  const int parts = build_decode_meta(h, B, seq_off, seq_len, pos, total, blob, &o_so, &o_sl,
+                                      &o_pos, &o_ps, &o_ns, &o_pb, &o_sg, &nseg_total);
+  if (blob.size() > meta_bytes(B, max_parts(h, total), L.max_segs))
+    return fail(h, MLA_ERR_WORKSPACE, "internal: decode metadata larger than planned");
+  void* meta = at<char>(ws, L.meta);
+  if ((rc = stage_upload(h, meta, blob.data(), blob.size()))) return rc;
+  DecodeMeta mt;
+  mt.seq_off = at<int64_t>(meta, o_so);
+  mt.seq_len = at<int32_t>(meta, o_sl);
+  mt.pos = at<int32_t>(meta, o_pos);
+  mt.pstart = at<int32_t>(meta, o_ps);
+  mt.nseg = at<int32_t>(meta, o_ns);
+  mt.part_begin = at<int32_t>(meta, o_pb);
+  mt.segs = at<DecodeSeg>(meta, o_sg);
+  if (is_f32(h))
+    return run_decode<float>(h, (const float*)hidden, B, (const float*)cache, (float*)out, ws, L,
+                             mt, parts, nseg_total, mt.pos);
+  return run_decode<bf16>(h, (const bf16*)hidden, B, (const bf16*)cache, (bf16*)out, ws, L, mt,
+                          parts, nseg_total, mt.pos);
+}
+
+// ------------------------------------------------------------------------
+// prefill
+// ------------------------------------------------------------------------
+namespace {
+struct PrefillLayout {
+  int ks_qa = 1, ks_q = 1, ks_o = 1;
+  size_t meta, cq_part, cq, q_part, q_nope, q_rope, kv, o, y_part, total;
+};
+
+PrefillLayout prefill_layout(const mla_ctx* h, int T, int B, int64_t rows) {
+  const Dims& d = h->d;
+  PrefillLayout L;
+  if (d.dq) {
+    L.ks_qa = choose_ksplit(h, T, d.dq, d.D, 1);
+    L.ks_q = choose_ksplit(h, T, d.H * (d.dn + d.dr), d.dq, 1);
+  } else {
+    L.ks_q = choose_ksplit(h, T, d.H * (d.dn + d.dr), d.D, 1);
+  }
+  L.ks_o = choose_ksplit(h, T, d.D, d.H * d.dv, 1);
+  const size_t e = h->esz;
+  Carve c;
+  L.meta = c.take(align_up((size_t)T * 4) * 2 + align_up((size_t)B * 8) * 2);
+  L.cq_part = c.take(d.dq ? (size_t)L.ks_qa * T * d.dq * 4 : 0);
+  L.cq = c.take(d.dq ? (size_t)T * d.dq * e : 0);
+  L.q_part = c.take((size_t)L.ks_q * T * d.H * (d.dn + d.dr) * 4);
+  L.q_nope = c.take((size_t)T * d.H * d.dn * e);
+  L.q_rope = c.take((size_t)T * d.H * std::max(d.dr, 1) * e);
+  L.kv = c.take((size_t)rows * d.H * (d.dn + d.dv) * 4);
+  L.o = c.take((size_t)T * d.H * d.dv * e);
+  L.y_part = c.take((size_t)L.ks_o * T * d.D * 4);
+  L.total = c.off;
+  return L;
+}
+}  // namespace
+
+size_t mla_prefill_workspace_bytes(mla_handle h, int32_t T, int32_t B, int64_t total_key_rows) {
+  if (!h || T <= 0 || B <= 0 || total_key_rows <= 0) return 0;
+  return prefill_layout(h, T, B, total_key_rows).total;
+}
+
+template <typename T>
+static int run_prefill(mla_ctx* h, const T* hidden, int ntok, int B, const int32_t* cu_new,
+                       const int32_t* prior, const int64_t* seq_off, const T* cache, T* out,
+                       void* ws, const PrefillLayout& L, const int64_t* kv_off_h) {
+  const Dims& d = h->d;
+  char* meta = at<char>(ws, L.meta);
+  const int32_t* tok_seq = reinterpret_cast<const int32_t*>(meta);
+  const int32_t* tok_pos = reinterpret_cast<const int32_t*>(meta + align_up((size_t)ntok * 4));
+  const int64_t* kv_off =
+      reinterpret_cast<const int64_t*>(meta + 2 * align_up((size_t)ntok * 4));
+  const int64_t* seq_off_d = kv_off + align_up((size_t)B * 8) / 8;
+  T* q_nope = at<T>(ws, L.q_nope);
+  T* q_rope = at<T>(ws, L.q_rope);
+  run_q_path<T>(h, hidden, ntok, nullptr, ws, at<float>(ws, L.cq_part), at<T>(ws, L.cq),
+                at<float>(ws, L.q_part), L.ks_qa, L.ks_q, q_nope, q_rope,
+                (int64_t)d.H * d.dr, d.dr, 1.f, tok_pos);
+  // expansion of every key row: [K_nope_h | V_h] = W_kvb c_t
+  float* kv = at<float>(ws, L.kv);
+  for (int b = 0; b < B; ++b) {
+    const int rows = prior[b] + (cu_new[b + 1] - cu_new[b]);
+    if (rows == 0) continue;
+    gemm_t<T>(h, cache + seq_off[b] * d.R, d.R, 0, (const T*)h->w_kvb, d.dc, 0,
+              kv + kv_off_h[b] * (int64_t)d.H * (d.dn + d.dv), rows, d.H * (d.dn + d.dv), d.dc, 1,
+              1);
+  }
+  T* o = at<T>(ws, L.o);
+  mla::prefill_attn_generic<T>(q_nope, q_rope, kv, cache, tok_seq, tok_pos, kv_off, seq_off_d,
+                               ntok, o, d, h->stream);
+  float* y_part = at<float>(ws, L.y_part);
+  gemm_t<T>(h, o, (int64_t)d.H * d.dv, 0, (const T*)h->w_o, (int64_t)d.H * d.dv, 0, y_part, ntok,
+            d.D, d.H * d.dv, 1, L.ks_o);
+  mla::sum_store<T>(y_part, L.ks_o, ntok, d.D, 1, out, d.D, 0, 1.f, h->stream);
+  return check_launch(h, "prefill");
+}
+
+int mla_prefill(mla_handle h, const void* hidden, const int32_t* cu_new, const int32_t* prior_len,
+                const int64_t* seq_off, int32_t B, const void* cache, int64_t cache_rows,
+                void* out, void* ws, size_t ws_bytes) {
+  if (!h) return MLA_ERR_INVALID_ARG;
+  if (!hidden || !cache || !out) return fail(h, MLA_ERR_INVALID_ARG, "prefill: NULL tensor");
+  int rc0 = mla_prefill_check(&h->cfg, cu_new, prior_len, seq_off, B, cache_rows);
+  if (rc0) return fail(h, rc0, "prefill: %s (B=%d, cache_rows=%lld)", mla_status_string(rc0), B,
+                       (long long)cache_rows);
+  if (!h->absorbed) return fail(h, MLA_ERR_STATE, "prefill before mla_absorb_weights");
+  int64_t rows = 0;
+  std::vector<int64_t> kv_off(B);
+  for (int32_t b = 0; b < B; ++b) {
+    kv_off[b] = rows;
+    rows += (int64_t)prior_len[b] + (cu_new[b + 1] - cu_new[b]);
+  }
+  const int32_t T = cu_new[B];
+  const PrefillLayout L = prefill_layout(h, T, B, rows);
+  int rc = check_ws(h, ws, ws_bytes, L.total);
+  if (rc) return rc;
+  DeviceGuard g(h->device);
+  if (!g.ok) return fail(h, MLA_ERR_HIP, "cannot select device %d", h->device);
+  std::vector<char> blob(align_up((size_t)T * 4) * 2 + align_up((size_t)B * 8) * 2, 0);
+  int32_t* tok_seq = reinterpret_cast<int32_t*>(blob.data());
+  int32_t* tok_pos = reinterpret_cast<int32_t*>(blob.data() + align_up((size_t)T * 4));
+  int64_t* kvo = reinterpret_cast<int64_t*>(blob.data() + 2 * align_up((size_t)T * 4));
+  int64_t* so = kvo + align_up((size_t)B * 8) / 8;
+  for (int32_t b = 0; b < B; ++b) {
+    for (int32_t i = cu_new[b]; i < cu_new[b + 1]; ++i) {
+      tok_seq[i] = b;
+      tok_pos[i] = prior_len[b] + (i - cu_new[b]);
+    }
+    kvo[b] = kv_off[b];
+    so[b] = seq_off[b];
+  }
+  if ((rc = stage_upload(h, at<char>(ws, L.meta), blob.data(), blob.size()))) return rc;
+  if (is_f32(h))
+    return run_prefill<float>(h, (const float*)hidden, T, B, cu_new, prior_len, seq_off,
+                              (const float*)cache, (float*)out, ws, L, kv_off.data());
+  return run_prefill<bf16>(h, (const bf16*)hidden, T, B, cu_new, prior_len, seq_off,
+                           (const bf16*)cache, (bf16*)out, ws, L, kv_off.data());
+}
+

@@ -1,0 +1,268 @@
+"""Thin ctypes binding over the MLA C ABI (``include/mla.h``).
+
+Argument marshalling only: tensors are passed as device pointers
+(``tensor.data_ptr()``), ragged metadata as host arrays, streams as the raw
+``hipStream_t`` of torch's current stream.  Every step of the computation runs
+in the HIP library; this module raises if the library is missing.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmla.so")
+
+MLA_OK = 0
+MLA_ERR_INVALID_ARG = -1
+MLA_ERR_SHAPE = -2
+MLA_ERR_CAPACITY = -3
+MLA_ERR_STATE = -4
+MLA_ERR_HIP = -5
+MLA_ERR_WORKSPACE = -6
+MLA_BF16 = 0
+MLA_F32 = 1
+
+_P = ctypes.c_void_p
+_I32P = ctypes.POINTER(ctypes.c_int32)
+_I64P = ctypes.POINTER(ctypes.c_int64)
+
+
+class MLAConfig(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+                ("qk_nope", ctypes.c_int32), ("qk_rope", ctypes.c_int32),
+                ("v_head", ctypes.c_int32), ("kv_lora", ctypes.c_int32),
+                ("q_lora", ctypes.c_int32), ("rope_base", ctypes.c_float),
+                ("rms_eps", ctypes.c_float), ("softmax_scale", ctypes.c_float),
+                ("dtype", ctypes.c_int32)]
+
+
+# name -> (restype, argtypes)
+_SIGS = {
+    "mla_abi_version": (ctypes.c_int, []),
+    "mla_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "mla_last_error": (ctypes.c_char_p, [_P]),
+    "mla_config_check": (ctypes.c_int, [ctypes.POINTER(MLAConfig)]),
+    "mla_append_check": (ctypes.c_int, [ctypes.POINTER(MLAConfig), _I32P, _I64P, ctypes.c_int32,
+                                        ctypes.c_int64]),
+    "mla_decode_check": (ctypes.c_int, [ctypes.POINTER(MLAConfig), _I32P, _I64P, _I32P,
+                                        ctypes.c_int32, ctypes.c_int64]),
+    "mla_prefill_check": (ctypes.c_int, [ctypes.POINTER(MLAConfig), _I32P, _I32P, _I64P,
+                                         ctypes.c_int32, ctypes.c_int64]),
+    "mla_create": (ctypes.c_int, [ctypes.POINTER(MLAConfig), _P, ctypes.POINTER(_P)]),
+    "mla_destroy": (ctypes.c_int, [_P]),
+    "mla_set_stream": (ctypes.c_int, [_P, _P]),
+    "mla_absorb_weights": (ctypes.c_int, [_P] * 9),
+    "mla_append_workspace_bytes": (ctypes.c_size_t, [_P, ctypes.c_int32]),
+    "mla_append_latent": (ctypes.c_int, [_P, _P, _I32P, _I64P, ctypes.c_int32, _P,
+                                         ctypes.c_int64, _P, ctypes.c_size_t]),
+    "mla_cache_write_workspace_bytes": (ctypes.c_size_t, [_P, ctypes.c_int32]),
+    "mla_cache_write": (ctypes.c_int, [_P, _P, _I64P, ctypes.c_int32, _P, ctypes.c_int64, _P,
+                                       ctypes.c_size_t]),
+    "mla_decode_workspace_bytes": (ctypes.c_size_t, [_P, ctypes.c_int32, ctypes.c_int64]),
+    "mla_decode": (ctypes.c_int, [_P, _P, _I32P, _I64P, _I32P, ctypes.c_int32, _P,
+                                  ctypes.c_int64, _P, _P, ctypes.c_size_t]),
+    "mla_decode_stage_offsets": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.c_int64,
+                                                ctypes.POINTER(ctypes.c_size_t),
+                                                ctypes.POINTER(ctypes.c_size_t)]),
+    "mla_prefill_workspace_bytes": (ctypes.c_size_t, [_P, ctypes.c_int32, ctypes.c_int32,
+                                                      ctypes.c_int64]),
+    "mla_prefill": (ctypes.c_int, [_P, _P, _I32P, _I32P, _I64P, ctypes.c_int32, _P,
+                                   ctypes.c_int64, _P, _P, ctypes.c_size_t]),
+}
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"MLA HIP library not found at {path}; build it with "
+                           "`python -m mla_latent_kv_decode_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+class MLAError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{msg} (status {status})")
+        self.status = status
+
+
+def make_config(dims, dtype: str, softmax_scale: float = 0.0) -> MLAConfig:
+    return MLAConfig(dims.hidden, dims.n_heads, dims.qk_nope, dims.qk_rope, dims.v_head,
+                     dims.kv_lora, dims.q_lora, float(dims.rope_base), float(dims.rms_eps),
+                     float(softmax_scale), MLA_BF16 if dtype == "bf16" else MLA_F32)
+
+
+def _i32(a):
+    a = np.ascontiguousarray(a, dtype=np.int32)
+    return a, a.ctypes.data_as(_I32P)
+
+
+def _i64(a):
+    a = np.ascontiguousarray(a, dtype=np.int64)
+    return a, a.ctypes.data_as(_I64P)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream_ptr():
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+class Workspace:
+    """Grow-only device scratch buffer (256-byte aligned view of a torch tensor)."""
+
+    def __init__(self, device):
+        self.device = device
+        self.buf = None
+
+    def get(self, nbytes: int):
+        import torch
+        if nbytes == 0:
+            return None, 0
+        if self.buf is None or self.buf.numel() < nbytes + 256:
+            self.buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=self.device)
+        addr = self.buf.data_ptr()
+        pad = (-addr) % 256
+        return ctypes.c_void_p(addr + pad), self.buf.numel() - pad
+
+
+class MLALayer:
+    """One MLA layer bound to a library handle on the current device/stream."""
+
+    def __init__(self, dims, dtype: str = "bf16", softmax_scale: float = 0.0, device="cuda"):
+        import torch
+        self.lib = load()
+        self.dims = dims
+        self.dtype = dtype
+        self.torch_dtype = torch.bfloat16 if dtype == "bf16" else torch.float32
+        self.cfg = make_config(dims, dtype, softmax_scale)
+        self.device = torch.device(device)
+        h = ctypes.c_void_p()
+        self._check(self.lib.mla_create(ctypes.byref(self.cfg), _stream_ptr(), ctypes.byref(h)),
+                    None, "mla_create")
+        self.h = h
+        self.ws = Workspace(self.device)
+
+    # -- helpers
+    def _check(self, rc, h, what):
+        if rc != MLA_OK:
+            detail = self.lib.mla_last_error(h).decode() if h else ""
+            raise MLAError(rc, f"{what}: {self.lib.mla_status_string(rc).decode()} {detail}")
+
+    def _sync_stream(self):
+        self.lib.mla_set_stream(self.h, _stream_ptr())
+
+    def close(self):
+        if getattr(self, "h", None):
+            self.lib.mla_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # -- A1
+    def absorb_weights(self, w: dict):
+        """w: dict of device tensors in the layer dtype (keys as synth.make_weights)."""
+        self._sync_stream()
+        rc = self.lib.mla_absorb_weights(
+            self.h, _ptr(w.get("w_q")), _ptr(w.get("w_qa")), _ptr(w.get("q_norm_g")),
+            _ptr(w.get("w_qb")), _ptr(w["w_kva"]), _ptr(w.get("kv_norm_g")), _ptr(w["w_kvb"]),
+            _ptr(w["w_o"]))
+        self._check(rc, self.h, "mla_absorb_weights")
+
+    # -- A2
+    def append(self, hidden, pos, slot, cache, check_only=False):
+        self._sync_stream()
+        T = int(hidden.shape[0])
+        pos_a, pos_p = _i32(pos)
+        slot_a, slot_p = _i64(slot)
+        wsp, wsn = self.ws.get(self.lib.mla_append_workspace_bytes(self.h, T))
+        rc = self.lib.mla_append_latent(self.h, _ptr(hidden), pos_p, slot_p, T, _ptr(cache),
+                                        int(cache.shape[0]), wsp, wsn)
+        self._check(rc, self.h, "mla_append_latent")
+
+    def cache_write(self, rows, slot, cache):
+        self._sync_stream()
+        T = int(rows.shape[0])
+        slot_a, slot_p = _i64(slot)
+        wsp, wsn = self.ws.get(self.lib.mla_cache_write_workspace_bytes(self.h, T))
+        rc = self.lib.mla_cache_write(self.h, _ptr(rows), slot_p, T, _ptr(cache),
+                                      int(cache.shape[0]), wsp, wsn)
+        self._check(rc, self.h, "mla_cache_write")
+
+    # -- A3..A8
+    def decode(self, hidden, pos, seq_off, seq_len, cache, out=None, stages=False):
+        import torch
+        self._sync_stream()
+        B = int(hidden.shape[0])
+        pos_a, pos_p = _i32(pos)
+        so_a, so_p = _i64(seq_off)
+        sl_a, sl_p = _i32(seq_len)
+        total = int(sl_a.astype(np.int64).sum())
+        if out is None:
+            out = torch.empty((B, self.dims.hidden), dtype=self.torch_dtype, device=self.device)
+        wsp, wsn = self.ws.get(self.lib.mla_decode_workspace_bytes(self.h, B, max(total, 1)))
+        rc = self.lib.mla_decode(self.h, _ptr(hidden), pos_p, so_p, sl_p, B, _ptr(cache),
+                                 int(cache.shape[0]), _ptr(out), wsp, wsn)
+        self._check(rc, self.h, "mla_decode")
+        if not stages:
+            return out
+        qo, oo = ctypes.c_size_t(), ctypes.c_size_t()
+        self._check(self.lib.mla_decode_stage_offsets(self.h, B, total, ctypes.byref(qo),
+                                                      ctypes.byref(oo)), self.h, "stages")
+        d = self.dims
+        es = 2 if self.dtype == "bf16" else 4
+        base = wsp.value - self.ws.buf.data_ptr()
+        raw = self.ws.buf
+        q_cat = raw[base + qo.value: base + qo.value + B * d.n_heads * d.row * es]
+        o_lat = raw[base + oo.value: base + oo.value + B * d.n_heads * d.kv_lora * es]
+        q_cat = q_cat.view(self.torch_dtype).reshape(B, d.n_heads, d.row).clone()
+        o_lat = o_lat.view(self.torch_dtype).reshape(B, d.n_heads, d.kv_lora).clone()
+        return out, q_cat, o_lat
+
+    # -- P1
+    def prefill(self, hidden, cu_new, prior_len, seq_off, cache, out=None):
+        import torch
+        self._sync_stream()
+        cu_a, cu_p = _i32(cu_new)
+        pr_a, pr_p = _i32(prior_len)
+        so_a, so_p = _i64(seq_off)
+        B = len(pr_a)
+        T = int(cu_a[-1])
+        rows = int((pr_a.astype(np.int64) + np.diff(cu_a)).sum())
+        if out is None:
+            out = torch.empty((T, self.dims.hidden), dtype=self.torch_dtype, device=self.device)
+        wsp, wsn = self.ws.get(self.lib.mla_prefill_workspace_bytes(self.h, T, B, max(rows, 1)))
+        rc = self.lib.mla_prefill(self.h, _ptr(hidden), cu_p, pr_p, so_p, B, _ptr(cache),
+                                  int(cache.shape[0]), _ptr(out), wsp, wsn)
+        self._check(rc, self.h, "mla_prefill")
+        return out
+
+
+def header_functions(header: str = None) -> list:
+    """Names of the functions include/mla.h declares."""
+    import re
+    header = header or os.path.join(os.path.dirname(_PKG), "include", "mla.h")
+    text = open(header).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z0-9_]+)\s*\(", text)))

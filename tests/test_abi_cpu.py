@@ -1,0 +1,147 @@
+"""The C-ABI library without a GPU: it loads, exports every function the
+header declares, and its host-side validation returns the documented status
+codes (no compute call is made here)."""
+
+import ctypes
+import os
+
+import numpy as np
+import pytest
+
+from mla_latent_kv_decode_amd import lib as L
+from mla_latent_kv_decode_amd import synth
+
+
+@pytest.fixture(scope="module")
+def mla():
+    if not os.path.exists(L.LIB_PATH):
+        from mla_latent_kv_decode_amd import build
+        build.build()
+    return L.load()
+
+
+def cfg(dims=synth.V2_LITE, dtype="bf16", **over):
+    c = L.make_config(dims, dtype)
+    for k, v in over.items():
+        setattr(c, k, v)
+    return c
+
+
+def test_exports_every_declared_symbol(mla):
+    names = L.header_functions()
+    assert len(names) >= 20
+    missing = [n for n in names if not hasattr(mla, n)]
+    assert not missing, missing
+    assert set(names) == set(L._SIGS), set(names) ^ set(L._SIGS)
+    assert mla.mla_abi_version() == 1
+
+
+def test_status_strings(mla):
+    for code in range(0, -7, -1):
+        assert mla.mla_status_string(code).decode()
+    assert mla.mla_status_string(-99).decode() == "unknown status"
+
+
+def test_config_check(mla):
+    ok = lambda c: mla.mla_config_check(ctypes.byref(c))
+    assert ok(cfg()) == L.MLA_OK
+    assert ok(cfg(synth.V3)) == L.MLA_OK
+    assert ok(cfg(synth.TINY, "f32")) == L.MLA_OK
+    assert ok(cfg(qk_rope=7)) == L.MLA_ERR_SHAPE           # RoPE rotates pairs
+    assert ok(cfg(qk_rope=0)) == L.MLA_OK                  # no decoupled rope part
+    assert ok(cfg(hidden=0)) == L.MLA_ERR_INVALID_ARG
+    assert ok(cfg(n_heads=-1)) == L.MLA_ERR_INVALID_ARG
+    assert ok(cfg(q_lora=-1)) == L.MLA_ERR_INVALID_ARG
+    c7 = cfg()
+    c7.dtype = 7
+    assert ok(c7) == L.MLA_ERR_INVALID_ARG
+    assert ok(cfg(rope_base=0.0)) == L.MLA_ERR_INVALID_ARG
+    assert ok(cfg(rms_eps=float("nan"))) == L.MLA_ERR_INVALID_ARG
+    assert ok(cfg(softmax_scale=-1.0)) == L.MLA_ERR_INVALID_ARG
+    assert mla.mla_config_check(None) == L.MLA_ERR_INVALID_ARG
+
+
+def _i32(a):
+    a = np.ascontiguousarray(a, np.int32)
+    return a, a.ctypes.data_as(L._I32P)
+
+
+def _i64(a):
+    a = np.ascontiguousarray(a, np.int64)
+    return a, a.ctypes.data_as(L._I64P)
+
+
+def test_append_check(mla):
+    c = cfg()
+
+    def chk(pos, slot, rows, T=None):
+        pa, pp = _i32(pos)
+        sa, sp = _i64(slot)
+        return mla.mla_append_check(ctypes.byref(c), pp, sp, len(pa) if T is None else T, rows)
+
+    assert chk([0, 1, 2], [5, 6, 7], 8) == L.MLA_OK
+    assert chk([0, 1, 2], [5, 6, 8], 8) == L.MLA_ERR_CAPACITY      # slot == cache_rows
+    assert chk([0, 1, 2], [-1, 6, 7], 8) == L.MLA_ERR_CAPACITY
+    assert chk([0, 1, 2], [5, 6, 5], 8) == L.MLA_ERR_INVALID_ARG   # duplicate slot
+    assert chk([0, -1, 2], [5, 6, 7], 8) == L.MLA_ERR_INVALID_ARG  # negative position
+    assert chk([0], [0], 8, T=0) == L.MLA_ERR_INVALID_ARG
+    assert chk([0], [0], 0) == L.MLA_ERR_INVALID_ARG
+    bad = cfg(qk_rope=3)
+    pa, pp = _i32([0])
+    sa, sp = _i64([0])
+    assert mla.mla_append_check(ctypes.byref(bad), pp, sp, 1, 4) == L.MLA_ERR_SHAPE
+
+
+def test_decode_check(mla):
+    c = cfg()
+
+    def chk(pos, off, ln, rows):
+        pa, pp = _i32(pos)
+        oa, op = _i64(off)
+        la, lp = _i32(ln)
+        return mla.mla_decode_check(ctypes.byref(c), pp, op, lp, len(pa), rows)
+
+    assert chk([4, 0], [0, 5], [5, 1], 6) == L.MLA_OK
+    assert chk([4, 0], [0, 5], [5, 1], 5) == L.MLA_ERR_CAPACITY    # last row past the end
+    assert chk([4, 0], [-1, 5], [5, 1], 6) == L.MLA_ERR_CAPACITY
+    assert chk([3, 0], [0, 5], [5, 1], 6) == L.MLA_ERR_INVALID_ARG  # pos != len - 1
+    assert chk([4, -1], [0, 5], [5, 0], 6) == L.MLA_ERR_INVALID_ARG  # empty sequence
+    assert chk([], [], [], 6) == L.MLA_ERR_INVALID_ARG              # B = 0
+    # int64 offsets near the top of the range must not overflow into "fits"
+    assert chk([4], [2 ** 62], [5], 2 ** 62) == L.MLA_ERR_CAPACITY
+
+
+def test_prefill_check(mla):
+    c = cfg()
+
+    def chk(cu, prior, off, rows):
+        ca, cp = _i32(cu)
+        pa, pp = _i32(prior)
+        oa, op = _i64(off)
+        return mla.mla_prefill_check(ctypes.byref(c), cp, pp, op, len(pa), rows)
+
+    assert chk([0, 4, 7], [0, 2], [0, 4], 9) == L.MLA_OK
+    assert chk([0, 4, 7], [0, 2], [0, 4], 8) == L.MLA_ERR_CAPACITY
+    assert chk([1, 4, 7], [0, 2], [0, 4], 9) == L.MLA_ERR_INVALID_ARG   # cu_new[0] != 0
+    assert chk([0, 4, 3], [0, 2], [0, 4], 9) == L.MLA_ERR_INVALID_ARG   # decreasing
+    assert chk([0, 4, 7], [0, -2], [0, 4], 9) == L.MLA_ERR_INVALID_ARG
+    assert chk([0, 0, 0], [3, 2], [0, 4], 9) == L.MLA_ERR_INVALID_ARG   # no new tokens
+
+
+def test_product_path_has_no_oracle_dependency():
+    """The package never imports or loads the oracle (test infrastructure
+    only), and the binding fails loudly when the library is missing."""
+    import re
+    pat = re.compile(r"^\s*(from\s+oracle|import\s+oracle)|oracle/", re.M)
+    for dirpath, _, files in os.walk(L._PKG):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not pat.search(text), f
+    old = L._lib
+    L._lib = None
+    try:
+        with pytest.raises(RuntimeError):
+            L.load(os.path.join(os.path.dirname(L._PKG), "no_such_lib.so"))
+    finally:
+        L._lib = old
