@@ -35,6 +35,11 @@
  * Streams.  All calls are asynchronous on the handle's HIP stream (the one
  *   given to mla_create / mla_set_stream; NULL = the null stream).  Nothing
  *   synchronises implicitly except mla_absorb_weights and mla_destroy.
+ * Graph capture.  mla_append_latent, mla_cache_write, mla_decode and
+ *   mla_prefill may be captured into a HIP graph: while the stream is
+ *   capturing, the metadata a call uploads are staged in pinned memory kept
+ *   for the life of the handle (the graph's copy node reads it at every
+ *   replay), so a replay re-runs the call with the metadata of capture time.
  * Errors.  Every call returns an mla_status.  Argument, shape and capacity
  *   errors are detected on the host before anything is launched and leave all
  *   device memory untouched.  MLA_ERR_HIP reports a failed HIP runtime call;
@@ -73,7 +78,7 @@ typedef struct mla_config {
   int32_t hidden;    /* D */
   int32_t n_heads;   /* H */
   int32_t qk_nope;   /* dn */
-  int32_t qk_rope;   /* dr, even; 0 allowed (no decoupled RoPE) */
+  int32_t qk_rope;   /* dr, even, <= 128; 0 allowed (no decoupled RoPE) */
   int32_t v_head;    /* dv */
   int32_t kv_lora;   /* dc */
   int32_t q_lora;    /* dq, 0 = none */
@@ -87,8 +92,9 @@ typedef struct mla_ctx* mla_handle;
 
 /* Host-only check of a configuration: MLA_OK, MLA_ERR_INVALID_ARG (cfg NULL,
  * a dimension <= 0 other than qk_rope/q_lora, a negative one, unknown dtype,
- * non-finite or non-positive base/eps) or MLA_ERR_SHAPE (odd qk_rope).  Makes
- * no HIP call; mla_create runs it first. */
+ * non-finite or non-positive base/eps) or MLA_ERR_SHAPE (odd qk_rope,
+ * qk_rope > 128, kv_lora > 1024, v_head > 256).  Makes no HIP call;
+ * mla_create runs it first. */
 int mla_config_check(const mla_config* cfg);
 
 /* Host-only argument checks, run first by the corresponding calls and exported
@@ -167,6 +173,21 @@ int mla_decode(mla_handle h, const void* hidden, const int32_t* pos,
                const void* cache, int64_t cache_rows, void* out, void* ws,
                size_t ws_bytes);
 
+/* Workspace bytes mla_decode_step needs (same arguments as for mla_decode). */
+size_t mla_decode_step_workspace_bytes(mla_handle h, int32_t B, int64_t total_rows);
+
+/* A2..A8 in one call -- append each sequence's new token, then decode it
+ * (write, then read through the new position: MLA post section 3.2).  The
+ * same arguments as mla_decode, but the caller has NOT appended the new rows:
+ * this call writes row seq_off[b] + seq_len[b] - 1 of the cache (position
+ * pos[b] = seq_len[b] - 1) from hidden[b] exactly as mla_append_latent would,
+ * then decodes.  The latent down-projection and the query projection read the
+ * same hidden states, so they run as one GEMM over [W_kva ; W_q] (or
+ * [W_kva ; W_qa]).  Same errors as mla_decode. */
+int mla_decode_step(mla_handle h, const void* hidden, const int32_t* pos,
+                    const int64_t* seq_off, const int32_t* seq_len, int32_t B, void* cache,
+                    int64_t cache_rows, void* out, void* ws, size_t ws_bytes);
+
 /* Where the staged intermediates of the last mla_decode with these (B,
  * total_rows) live inside its workspace, as byte offsets from ws:
  *   q_cat (B, H, R) storage type: [W_UK_h^T q_nope_h | RoPE(q_rope_h)] * scale
@@ -194,6 +215,13 @@ int mla_prefill(mla_handle h, const void* hidden, const int32_t* cu_new,
                 const int32_t* prior_len, const int64_t* seq_off, int32_t B,
                 const void* cache, int64_t cache_rows, void* out, void* ws,
                 size_t ws_bytes);
+
+/* Measurement hook: when both are non-NULL hipEvent_t handles, later calls
+ * record `start` on the handle's stream right before the split-S core kernel
+ * of mla_decode (the attention kernel of mla_prefill) and `stop` right after
+ * it, so the caller can time that kernel alone with hipEventElapsedTime.
+ * NULL, NULL turns it off.  The events stay owned by the caller. */
+int mla_set_timing_events(mla_handle h, void* start, void* stop);
 
 /* Static text for a status code. */
 const char* mla_status_string(int status);

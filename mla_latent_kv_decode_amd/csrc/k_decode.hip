@@ -14,8 +14,8 @@
 // softmax state and a private double-buffered LDS stage filled by
 // global_load_lds_dwordx4 (no VGPRs held by loads in flight).  At the end of a
 // segment the 4 wave states are merged through LDS and one partial
-// (max, sum, unnormalised acc) is written; the combine kernel merges partials
-// of a sequence in a fixed order.
+// (max, sum, unnormalised acc) is written; a separate combine kernel merges
+// the partials of each sequence in a fixed order.
 //
 // Per 16-row sub-tile and wave:
 //   S^T (16 rows x 16 heads) = K (16 x 576) . Q^T   -- 18 x mfma 16x16x32,
@@ -24,9 +24,13 @@
 //   softmax: per head = per lane column; max/sum across the 4 lane groups by
 //       two xor-shuffles.
 //   O^T (512 cols x 16 heads) += C^T (512 x 16 rows) . P^T (16 rows x 16 heads)
-//       -- 32 x mfma 16x16x16; B = P exactly as S^T left it; A = C^T built from
-//       4 x 16-byte LDS reads (4 rows x 8 columns) and a 4x8 bf16 transpose
-//       in registers, giving fragments for 8 MFMAs (column 8c + j of chunk c).
+//       -- 32 x mfma 16x16x16; B = P exactly as S^T left it; A = C^T read
+//       straight into operand layout by ds_read_b64_tr_b16 (gfx950 transposing
+//       LDS read: inside each 16-lane group, output lane i element k is element
+//       i % 4 of source lane 4k + i/4; source lane s of group g addresses row
+//       4g + s/4, columns c0 + 4(s % 4), so lane i receives rows 4g..4g+3 of
+//       column c0 + i).  Lane l accumulates columns c0 + 4(l/16) .. +3 of head
+//       l % 16 for every 16-column block c0.
 #include "kernels.h"
 
 namespace mla {
@@ -39,6 +43,7 @@ constexpr int SUB_BYTES = SUB * RW * 2;      // 18432
 constexpr int LOADS = SUB + 2;               // 18 wave-wide 16-byte loads per sub-tile
 constexpr int NWAVE = 4;
 constexpr int NSTAGE = 2;
+constexpr float kRescale = 8.0f;             // lazy-rescale threshold, log2 units
 constexpr int LDS_BYTES = NWAVE * NSTAGE * SUB_BYTES;  // 147456
 static_assert(NWAVE * 16 * DC * 4 + NWAVE * 16 * 2 * 4 <= LDS_BYTES, "merge space");
 
@@ -115,12 +120,17 @@ decode_core_mfma_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
   const int qk_base1 = lr * 1024 + 64 * (qk_b ^ 1) + qk_lo;    // odd s
   const int qk_rope0 = ROPE_OFF + lr * 128 + 64 * qk_b + qk_lo;        // s = 16
   const int qk_rope1 = ROPE_OFF + lr * 128 + 64 * (qk_b ^ 1) + qk_lo;  // s = 17
-  // PV operand: row r = 4lg + i, latent chunk 16cb + lr at r*1024 + 256cb + 16(lr ^ (r & 7))
-  int pv_base[4];
+  // PV operand (transposing read): lane = (group g = lg, s = lr) addresses row
+  // r = 4g + s/4, column 16cb + 4(s % 4), i.e. latent chunk 2cb + h (h = (s%4)/2)
+  // at byte 8(s & 1).  With x = r & 7, y = x >> 1: the physical chunk is
+  // 2(cb ^ y) + (h ^ (x & 1)), so for cb = 4q + t the byte offset is
+  // pv_off[t] + 128q.
+  int pv_off[4];
+  {
+    const int r = 4 * lg + (lr >> 2);
+    const int x = r & 7, y = x >> 1, hh = ((lr & 3) >> 1) ^ (x & 1);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 4 * lg + i;
-    pv_base[i] = r * 1024 + 16 * (lr ^ (r & 7));
+    for (int t = 0; t < 4; ++t) pv_off[t] = r * 1024 + 8 * (lr & 1) + 16 * hh + 32 * (t ^ y);
   }
 
   const int sbeg = mt.part_begin[part], send = mt.part_begin[part + 1];
@@ -149,11 +159,9 @@ decode_core_mfma_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
     }
 
     float m_run = -INFINITY, l_run = 0.f;
-    f32x4_t o[4][8];
+    f32x4_t o[32];  // o[cb][i]: head lr, column 16 cb + 4 lg + i
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) o[cb][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    for (int cb = 0; cb < 32; ++cb) o[cb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 
     for (int it = 0; it < my_n; ++it) {
       char* stage = my + (it & 1) * SUB_BYTES;
@@ -177,35 +185,41 @@ decode_core_mfma_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
         sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s + 1], qf[s + 1], sb, 0, 0, 0);
       }
       const f32x4_t sacc = sa + sb;
+      // schedule: all 18 LDS reads first, then the 18 MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, 18, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 18, 0);
 
-      // ---- online softmax (log2 units); lane owns rows row0 + 4 lg + i of head lr
+      // ---- online softmax (log2 units); lane owns rows row0 + 4 lg + i of head lr.
+      // No cross-lane work in the common case: the reference max m_run only
+      // moves when some score exceeds it by more than kRescale (a wave vote),
+      // so p stays <= 2^kRescale; the running sum is kept per lane and reduced
+      // over the 4 lane groups once per segment.  On a (rare) move, the head's
+      // tile max is formed with two xor-shuffles and O and the sums rescaled.
+      // The same reference enters l and acc, so their ratio is exact math.
       float sv[4];
-      float mx = -INFINITY;
+      bool grow = false;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const bool valid = row0 + 4 * lg + i < n;
         sv[i] = valid ? sacc[i] * kLog2e : -INFINITY;
-        mx = fmaxf(mx, sv[i]);
+        grow |= sv[i] > m_run + kRescale;
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      float pv[4], rs = 0.f;
+      if (__any(grow)) {
+        float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+        m_run = m_new;
+#pragma unroll
+        for (int cb = 0; cb < 32; ++cb) o[cb] *= alpha;
+      }
+      float pv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        pv[i] = __builtin_amdgcn_exp2f(sv[i] - m_new);
-        rs += pv[i];
-      }
-      rs += __shfl_xor(rs, 16, 64);
-      rs += __shfl_xor(rs, 32, 64);
-      l_run = l_run * alpha + rs;
-      m_run = m_new;
-      if (!__all(alpha == 1.0f)) {
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) o[cb][j] *= alpha;
+        pv[i] = __builtin_amdgcn_exp2f(sv[i] - m_run);
+        l_run += pv[i];
       }
       s16x4_t pf;
       {
@@ -219,25 +233,13 @@ decode_core_mfma_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
 
       // ---- O^T += C^T . P^T
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        uint32_t d[4][4];
+      for (int q = 0; q < 8; ++q)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint4 v = *reinterpret_cast<const uint4*>(stage + pv_base[i] + 256 * cb);
-          d[i][0] = v.x; d[i][1] = v.y; d[i][2] = v.z; d[i][3] = v.w;
+        for (int t = 0; t < 4; ++t) {
+          const s16x4_t cf = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4_t*)(stage + pv_off[t] + 128 * q));
+          o[4 * q + t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(cf, pf, o[4 * q + t], 0, 0, 0);
         }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          s16x4_t a0, a1;  // column 2q and 2q + 1 of this lane's chunk, rows 4lg..4lg+3
-          a0[0] = (short)(d[0][q] & 0xffff); a0[1] = (short)(d[1][q] & 0xffff);
-          a0[2] = (short)(d[2][q] & 0xffff); a0[3] = (short)(d[3][q] & 0xffff);
-          a1[0] = (short)(d[0][q] >> 16);    a1[1] = (short)(d[1][q] >> 16);
-          a1[2] = (short)(d[2][q] >> 16);    a1[3] = (short)(d[3][q] >> 16);
-          o[cb][2 * q] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a0, pf, o[cb][2 * q], 0, 0, 0);
-          o[cb][2 * q + 1] =
-              __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a1, pf, o[cb][2 * q + 1], 0, 0, 0);
-        }
-      }
 
       // refill this stage with the sub-tile two steps ahead
       if (it + 2 < my_n) {
@@ -252,63 +254,117 @@ decode_core_mfma_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
     float* om = reinterpret_cast<float*>(lds);             // [wave][16 heads][512]
     float* mlm = om + NWAVE * 16 * DC;                      // [wave][16][2]
     {
-      float* ow = om + (wave * 16 + lr) * DC;
+      float* ow = om + (wave * 16 + lr) * DC + 4 * lg;
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int col = 8 * (16 * cb + 4 * lg + i);
-          float4 lo = make_float4(o[cb][0][i], o[cb][1][i], o[cb][2][i], o[cb][3][i]);
-          float4 hi = make_float4(o[cb][4][i], o[cb][5][i], o[cb][6][i], o[cb][7][i]);
-          *reinterpret_cast<float4*>(ow + col) = lo;
-          *reinterpret_cast<float4*>(ow + col + 4) = hi;
-        }
+      for (int cb = 0; cb < 32; ++cb)
+        *reinterpret_cast<float4*>(ow + 16 * cb) =
+            make_float4(o[cb][0], o[cb][1], o[cb][2], o[cb][3]);
+      // per-lane partial sums -> per-head sum over the 4 lane groups
+      l_run += __shfl_xor(l_run, 16, 64);
+      l_run += __shfl_xor(l_run, 32, 64);
       if (lg == 0) {
         mlm[(wave * 16 + lr) * 2] = m_run;
         mlm[(wave * 16 + lr) * 2 + 1] = l_run;
       }
     }
     __syncthreads();
+    // thread t: head t / 16, columns (t % 16) * 32 .. + 31
+    const int h = threadIdx.x >> 4;
+    const int c0 = (threadIdx.x & 15) * 32;
+    const int gh = hg * 16 + h;  // global head index
+    float r[32];
+    float M = -INFINITY, L = 0.f;
     {
-      // thread t: head t / 16, columns (t % 16) * 32 .. + 31
-      const int h = threadIdx.x >> 4;
-      const int c0 = (threadIdx.x & 15) * 32;
-      float mw[NWAVE], M = -INFINITY;
+      float mw[NWAVE], sc[NWAVE];
 #pragma unroll
       for (int w = 0; w < NWAVE; ++w) {
         mw[w] = mlm[(w * 16 + h) * 2];
         M = fmaxf(M, mw[w]);
       }
-      float L = 0.f, sc[NWAVE];
 #pragma unroll
       for (int w = 0; w < NWAVE; ++w) {
         sc[w] = exp2f(mw[w] - M);
         L += sc[w] * mlm[(w * 16 + h) * 2 + 1];
       }
-      float* dst = acc_out + ((int64_t)sg.pidx * H + hg * 16 + h) * DC + c0;
 #pragma unroll
       for (int c = 0; c < 32; c += 4) {
-        float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
+        float4 acc4 = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
         for (int w = 0; w < NWAVE; ++w) {
           const float4 v = *reinterpret_cast<const float4*>(om + (w * 16 + h) * DC + c0 + c);
-          r.x = fmaf(sc[w], v.x, r.x);
-          r.y = fmaf(sc[w], v.y, r.y);
-          r.z = fmaf(sc[w], v.z, r.z);
-          r.w = fmaf(sc[w], v.w, r.w);
+          acc4.x = fmaf(sc[w], v.x, acc4.x);
+          acc4.y = fmaf(sc[w], v.y, acc4.y);
+          acc4.z = fmaf(sc[w], v.z, acc4.z);
+          acc4.w = fmaf(sc[w], v.w, acc4.w);
         }
-        *reinterpret_cast<float4*>(dst + c) = r;
+        r[c] = acc4.x; r[c + 1] = acc4.y; r[c + 2] = acc4.z; r[c + 3] = acc4.w;
       }
-      if ((threadIdx.x & 15) == 0) {
-        ml_out[((int64_t)sg.pidx * H + hg * 16 + h) * 2] = M;
-        ml_out[((int64_t)sg.pidx * H + hg * 16 + h) * 2 + 1] = L;
-      }
+    }
+    float* pacc = acc_out + ((int64_t)sg.pidx * H + gh) * DC + c0;
+#pragma unroll
+    for (int c = 0; c < 32; c += 4)
+      *reinterpret_cast<float4*>(pacc + c) = make_float4(r[c], r[c + 1], r[c + 2], r[c + 3]);
+    if ((threadIdx.x & 15) == 0) {
+      ml_out[((int64_t)sg.pidx * H + gh) * 2] = M;
+      ml_out[((int64_t)sg.pidx * H + gh) * 2 + 1] = L;
     }
     __syncthreads();
   }
 }
 
+// Split combine for a 512-wide latent: block = (sequence b, 4 heads); thread t
+// owns head 4*blockIdx.y + t/64, columns 8*(t%64) .. +7.
+//   o_lat = sum_j e^(m_j - M) acc_j / sum_j e^(m_j - M) l_j,
+// summed in slot order j (deterministic); partial loads are issued 4 slots at
+// a time before any add.
+__global__ void __launch_bounds__(256)
+decode_combine_512_k(const float* __restrict__ acc, const float* __restrict__ ml, DecodeMeta mt,
+                     int H, bf16* __restrict__ o_lat) {
+  const int b = blockIdx.x;
+  const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
+  const int c = (threadIdx.x & 63) * 8;
+  const int j0 = mt.pstart[b], nj = mt.nseg[b];
+  float M = -INFINITY;
+  for (int j = 0; j < nj; ++j) M = fmaxf(M, ml[((int64_t)(j0 + j) * H + h) * 2]);
+  float L = 0.f;
+  float r[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < nj; j += 4) {
+    float4 v[4][2];
+    float w[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int jj = min(j + u, nj - 1);
+      const int64_t idx = (int64_t)(j0 + jj) * H + h;
+      const float* p = acc + idx * DC + c;
+      v[u][0] = *reinterpret_cast<const float4*>(p);
+      v[u][1] = *reinterpret_cast<const float4*>(p + 4);
+      w[u] = (j + u < nj) ? exp2f(ml[idx * 2] - M) : 0.f;
+      L = fmaf(w[u], (j + u < nj) ? ml[idx * 2 + 1] : 0.f, L);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      r[0] = fmaf(w[u], v[u][0].x, r[0]); r[1] = fmaf(w[u], v[u][0].y, r[1]);
+      r[2] = fmaf(w[u], v[u][0].z, r[2]); r[3] = fmaf(w[u], v[u][0].w, r[3]);
+      r[4] = fmaf(w[u], v[u][1].x, r[4]); r[5] = fmaf(w[u], v[u][1].y, r[5]);
+      r[6] = fmaf(w[u], v[u][1].z, r[6]); r[7] = fmaf(w[u], v[u][1].w, r[7]);
+    }
+  }
+  const float inv = 1.f / L;
+  uint4 pk;
+  pk.x = pack_bf16x2(r[0] * inv, r[1] * inv);
+  pk.y = pack_bf16x2(r[2] * inv, r[3] * inv);
+  pk.z = pack_bf16x2(r[4] * inv, r[5] * inv);
+  pk.w = pack_bf16x2(r[6] * inv, r[7] * inv);
+  *reinterpret_cast<uint4*>(o_lat + ((int64_t)b * H + h) * DC + c) = pk;
+}
+
 }  // namespace dec
+
+void decode_combine_512(const float* acc, const float* ml, const DecodeMeta& m, int B, int H,
+                        bf16* o_lat, hipStream_t st) {
+  dim3 grid(B, H / 4);
+  dec::decode_combine_512_k<<<grid, 256, 0, st>>>(acc, ml, m, H, o_lat);
+}
 
 void decode_core_mfma(const bf16* q_cat, const bf16* cache, const DecodeMeta& m, int parts,
                       int B, float* acc, float* ml, const Dims& d, hipStream_t st) {

@@ -47,33 +47,50 @@ void gemm_generic(const T* A, int64_t lda, int64_t sA, const T* W, int64_t ldw, 
 }
 
 // ---------------------------------------------------------------------------
-// split-K epilogues
+// epilogues over split-K partials (summed in split order z = 0..ks-1)
 // ---------------------------------------------------------------------------
-template <typename T>
-__global__ void sum_store_k(const float* __restrict__ part, int ksplit, int M, int N, int batch,
-                            T* __restrict__ out, int64_t ldo, int64_t so, float alpha) {
+// Sum over the ks split slices; the loads of 4 slices are independent (issued
+// together), the adds follow a fixed order (deterministic).
+__device__ __forceinline__ float part_at(const Part& a, int64_t row, int col) {
+  const float* p = a.p + row * a.ld + col;
+  if (a.ks == 1) return p[0];
+  float s = 0.f;
+  int z = 0;
+  for (; z + 4 <= a.ks; z += 4) {
+    const float v0 = p[(int64_t)z * a.zs], v1 = p[(int64_t)(z + 1) * a.zs];
+    const float v2 = p[(int64_t)(z + 2) * a.zs], v3 = p[(int64_t)(z + 3) * a.zs];
+    s += (v0 + v1) + (v2 + v3);
+  }
+  for (; z < a.ks; ++z) s += p[(int64_t)z * a.zs];
+  return s;
+}
+
+__global__ void gemm_store_k(const float* __restrict__ C, int ks, int M, int N, int batch,
+                             GemmOut out) {
   const int64_t total = (int64_t)batch * M * N;
-  const int64_t zs = total;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
        i += (int64_t)gridDim.x * blockDim.x) {
-    float s = 0.f;
-    for (int z = 0; z < ksplit; ++z) s += part[z * zs + i];
+    float v = C[i];
+    for (int z = 1; z < ks; ++z) v += C[z * total + i];
     const int n = (int)(i % N);
     const int64_t r = i / N;
     const int m = (int)(r % M);
     const int bt = (int)(r / M);
-    stf(out + bt * so + (int64_t)m * ldo + n, alpha * s);
+    const int64_t o = bt * out.so + (int64_t)m * out.ldo + n;
+    if (out.f32)
+      out.f32[o] = out.alpha * v;
+    else
+      out.b16[o] = f32_to_bf16(out.alpha * v);
   }
 }
 
-template <typename T>
-void sum_store(const float* part, int ksplit, int M, int N, int batch, T* out, int64_t ldo,
-               int64_t so, float alpha, hipStream_t st) {
+void gemm_store(const float* C, int ks, int M, int N, int batch, const GemmOut& out,
+                hipStream_t st) {
   const int64_t total = (int64_t)batch * M * N;
   int blocks = (int)((total + 255) / 256);
   if (blocks > 8192) blocks = 8192;
   if (blocks < 1) blocks = 1;
-  sum_store_k<T><<<blocks, 256, 0, st>>>(part, ksplit, M, N, batch, out, ldo, so, alpha);
+  gemm_store_k<<<blocks, 256, 0, st>>>(C, ks, M, N, batch, out);
 }
 
 __device__ __forceinline__ float block_sum_256(float v, float* red) {
@@ -89,132 +106,170 @@ __device__ __forceinline__ float block_sum_256(float v, float* red) {
 
 template <typename T>
 __global__ void __launch_bounds__(256)
-rmsnorm_rows_k(const float* __restrict__ part, int ksplit, int rows, int n,
-               const T* __restrict__ gamma, float eps, T* __restrict__ out) {
+rmsnorm_rows_k(Part x, int n, const T* __restrict__ gamma, float eps, T* __restrict__ out) {
   __shared__ float red[4];
   const int r = blockIdx.x;
-  const int64_t zs = (int64_t)rows * n;
   float ss = 0.f;
   for (int j = threadIdx.x; j < n; j += blockDim.x) {
-    float a = 0.f;
-    for (int z = 0; z < ksplit; ++z) a += part[z * zs + (int64_t)r * n + j];
+    const float a = part_at(x, r, j);
     ss += a * a;
   }
   const float inv = rsqrtf(block_sum_256(ss, red) / (float)n + eps);
-  for (int j = threadIdx.x; j < n; j += blockDim.x) {
-    float a = 0.f;
-    for (int z = 0; z < ksplit; ++z) a += part[z * zs + (int64_t)r * n + j];
-    stf(out + (int64_t)r * n + j, a * inv * ldf(gamma + j));
-  }
+  for (int j = threadIdx.x; j < n; j += blockDim.x)
+    stf(out + (int64_t)r * n + j, part_at(x, r, j) * inv * ldf(gamma + j));
 }
 
 template <typename T>
-void rmsnorm_rows(const float* part, int ksplit, int rows, int n, const T* gamma, float eps,
-                  T* out, hipStream_t st) {
-  rmsnorm_rows_k<T><<<rows, 256, 0, st>>>(part, ksplit, rows, n, gamma, eps, out);
+void rmsnorm_rows(const Part& x, int rows, int n, const T* gamma, float eps, T* out,
+                  hipStream_t st) {
+  rmsnorm_rows_k<T><<<rows, 256, 0, st>>>(x, n, gamma, eps, out);
 }
 
-// RoPE of one pair (u, v) at position pos, pair index i of a d-wide rope vector:
-// angle pos * base^(-2i/d) evaluated in double so long positions keep full
-// accuracy ("Multi-Head Latent Attention" post, section 3.7: adjacent pairs as
-// complex numbers times cos + i sin).
-__device__ __forceinline__ void rope_pair(float u, float v, int pos, int i, int d, float base,
-                                          float* ou, float* ov) {
-  const double theta = pow((double)base, -2.0 * (double)i / (double)d);
-  double s, c;
-  sincos((double)pos * theta, &s, &c);
-  const float cf = (float)c, sf = (float)s;
+// RoPE of one pair (u, v) at position pos with frequency theta ("Multi-Head
+// Latent Attention" post, section 3.7: adjacent pairs as complex numbers times
+// cos + i sin of pos * theta).  The angle is formed and reduced to [-pi, pi]
+// in double precision (positions reach 10^4..10^5 radians), then sin/cos are
+// taken in fp32.
+__device__ __forceinline__ void rope_pair(float u, float v, int pos, double theta, float* ou,
+                                          float* ov) {
+  const double ang = (double)pos * theta;
+  const double k = rint(ang * 0.15915494309189535);       // 1 / (2 pi)
+  double r = fma(-k, 6.283185307179586, ang);             // 2 pi, high part
+  r = fma(-k, 2.4492935982947064e-16, r);                 // 2 pi, low part
+  float sf, cf;
+  sincosf((float)r, &sf, &cf);
   *ou = u * cf - v * sf;
   *ov = u * sf + v * cf;
 }
 
-// One block per appended token ("Deepseek V2 Lite Inference Engine in C", MLA
-// notes: kv_a_proj gives [latent | rope key]; the latent is RMS-normalised and
-// the key rotated; then the row is written to its cache slot).
+// Latent row of token t ("Deepseek V2 Lite Inference Engine in C", MLA notes:
+// kv_a_proj gives [latent | rope key]; the latent is RMS-normalised and the key
+// rotated; then the row is written to its cache slot).  One block per token.
 template <typename T>
-__global__ void __launch_bounds__(256)
-append_rows_k(const float* __restrict__ apart, int ksplit, int ntok,
-              const int32_t* __restrict__ pos, const int64_t* __restrict__ slot,
-              const T* __restrict__ gamma, T* __restrict__ cache, Dims d) {
-  __shared__ float red[4];
-  const int t = blockIdx.x;
-  const int R = d.R;
-  const int64_t zs = (int64_t)ntok * R;
-  const float* a = apart + (int64_t)t * R;
+__device__ __forceinline__ void append_row_block(const Part& a, int t, int p, int64_t slot,
+                                                 const T* __restrict__ gamma,
+                                                 T* __restrict__ cache, const Dims& d,
+                                                 const RopeTab& rt, float* red) {
   float ss = 0.f;
   for (int j = threadIdx.x; j < d.dc; j += blockDim.x) {
-    float v = 0.f;
-    for (int z = 0; z < ksplit; ++z) v += a[z * zs + j];
+    const float v = part_at(a, t, j);
     ss += v * v;
   }
   const float inv = rsqrtf(block_sum_256(ss, red) / (float)d.dc + d.eps);
-  T* row = cache + slot[t] * (int64_t)R;
-  for (int j = threadIdx.x; j < d.dc; j += blockDim.x) {
-    float v = 0.f;
-    for (int z = 0; z < ksplit; ++z) v += a[z * zs + j];
-    stf(row + j, v * inv * (gamma ? ldf(gamma + j) : 1.f));
-  }
-  const int p = pos[t];
+  T* row = cache + slot * (int64_t)d.R;
+  for (int j = threadIdx.x; j < d.dc; j += blockDim.x)
+    stf(row + j, part_at(a, t, j) * inv * (gamma ? ldf(gamma + j) : 1.f));
   for (int i = threadIdx.x; i < d.dr / 2; i += blockDim.x) {
-    float u = 0.f, v = 0.f;
-    for (int z = 0; z < ksplit; ++z) {
-      u += a[z * zs + d.dc + 2 * i];
-      v += a[z * zs + d.dc + 2 * i + 1];
-    }
     float ou, ov;
-    rope_pair(u, v, p, i, d.dr, d.rope_base, &ou, &ov);
+    rope_pair(part_at(a, t, d.dc + 2 * i), part_at(a, t, d.dc + 2 * i + 1), p, rt.theta[i], &ou,
+              &ov);
     stf(row + d.dc + 2 * i, ou);
     stf(row + d.dc + 2 * i + 1, ov);
   }
 }
 
-template <typename T>
-void append_rows(const float* apart, int ksplit, int ntok, const int32_t* pos,
-                 const int64_t* slot, const T* gamma, T* cache, const Dims& d, hipStream_t st) {
-  append_rows_k<T><<<ntok, 256, 0, st>>>(apart, ksplit, ntok, pos, slot, gamma, cache, d);
-}
-
-// One block per token: per head, the nope part is stored for the absorb GEMM
-// and the rope part rotated per head ("Multi-Head Latent Attention" post,
+// Query heads of token t: the nope part of each head is stored for the absorb
+// GEMM and the rope part rotated per head ("Multi-Head Latent Attention" post,
 // section 3.7: embedding is done per head) and scaled into its destination.
+// Query heads [h0, h1) of token t: the nope part of each head is stored for
+// the absorb GEMM and the rope part rotated per head ("Multi-Head Latent
+// Attention" post, section 3.7: embedding is done per head) and scaled into
+// its destination.
 template <typename T>
-__global__ void __launch_bounds__(256)
-q_finish_k(const float* __restrict__ qpart, int ksplit, int ntok, const int32_t* __restrict__ pos,
-           T* __restrict__ q_nope, T* __restrict__ rope_out, int64_t tok_stride,
-           int64_t head_stride, float scale, Dims d) {
-  const int t = blockIdx.x;
+__device__ __forceinline__ void q_finish_block(const Part& q, int t, int p, int h0, int h1,
+                                               T* __restrict__ q_nope, T* __restrict__ rope_out,
+                                               int64_t tok_stride, int64_t head_stride,
+                                               float scale, const Dims& d, const RopeTab& rt) {
   const int w = d.dn + d.dr;
-  const int64_t zs = (int64_t)ntok * d.H * w;
-  const float* q = qpart + (int64_t)t * d.H * w;
-  for (int i = threadIdx.x; i < d.H * d.dn; i += blockDim.x) {
-    const int h = i / d.dn, j = i % d.dn;
-    float v = 0.f;
-    for (int z = 0; z < ksplit; ++z) v += q[z * zs + h * w + j];
-    stf(q_nope + ((int64_t)t * d.H + h) * d.dn + j, v);
+  for (int i = threadIdx.x; i < (h1 - h0) * d.dn; i += blockDim.x) {
+    const int h = h0 + i / d.dn, j = i % d.dn;
+    stf(q_nope + ((int64_t)t * d.H + h) * d.dn + j, part_at(q, t, h * w + j));
   }
   const int hp = d.dr / 2;
-  const int p = pos[t];
-  for (int i = threadIdx.x; i < d.H * hp; i += blockDim.x) {
-    const int h = i / hp, k = i % hp;
-    float u = 0.f, v = 0.f;
-    for (int z = 0; z < ksplit; ++z) {
-      u += q[z * zs + h * w + d.dn + 2 * k];
-      v += q[z * zs + h * w + d.dn + 2 * k + 1];
-    }
+  for (int i = threadIdx.x; i < (h1 - h0) * hp; i += blockDim.x) {
+    const int h = h0 + i / hp, k = i % hp;
     float ou, ov;
-    rope_pair(u, v, p, k, d.dr, d.rope_base, &ou, &ov);
+    rope_pair(part_at(q, t, h * w + d.dn + 2 * k), part_at(q, t, h * w + d.dn + 2 * k + 1), p,
+              rt.theta[k], &ou, &ov);
     T* o = rope_out + t * tok_stride + h * head_stride;
     stf(o + 2 * k, ou * scale);
     stf(o + 2 * k + 1, ov * scale);
   }
 }
 
+// heads per q_finish block: ~4 KB of partial columns per block
+__host__ __device__ inline int q_heads_per_block(const Dims& d) {
+  int g = 1024 / (d.dn + d.dr);
+  return g < 1 ? 1 : g;
+}
+
 template <typename T>
-void q_finish(const float* qpart, int ksplit, int ntok, const int32_t* pos, T* q_nope,
-              T* rope_out, int64_t tok_stride, int64_t head_stride, float scale,
-              const Dims& d, hipStream_t st) {
-  q_finish_k<T><<<ntok, 256, 0, st>>>(qpart, ksplit, ntok, pos, q_nope, rope_out, tok_stride,
-                                       head_stride, scale, d);
+__global__ void __launch_bounds__(256)
+append_rows_k(Part a, const int32_t* __restrict__ pos, const int64_t* __restrict__ slot,
+              const T* __restrict__ gamma, T* __restrict__ cache, Dims d, RopeTab rt) {
+  __shared__ float red[4];
+  const int t = blockIdx.x;
+  append_row_block<T>(a, t, pos[t], slot[t], gamma, cache, d, rt, red);
+}
+
+template <typename T>
+void append_rows(const Part& a, int ntok, const int32_t* pos, const int64_t* slot,
+                 const T* gamma, T* cache, const Dims& d, const RopeTab& rt, hipStream_t st) {
+  append_rows_k<T><<<ntok, 256, 0, st>>>(a, pos, slot, gamma, cache, d, rt);
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256)
+q_finish_k(Part q, const int32_t* __restrict__ pos, T* __restrict__ q_nope,
+           T* __restrict__ rope_out, int64_t tok_stride, int64_t head_stride, float scale, Dims d,
+           RopeTab rt) {
+  const int t = blockIdx.x, g = q_heads_per_block(d);
+  const int h0 = blockIdx.y * g, h1 = min(d.H, h0 + g);
+  q_finish_block<T>(q, t, pos[t], h0, h1, q_nope, rope_out, tok_stride, head_stride, scale, d,
+                    rt);
+}
+
+template <typename T>
+void q_finish(const Part& q, int ntok, const int32_t* pos, T* q_nope, T* rope_out,
+              int64_t tok_stride, int64_t head_stride, float scale, const Dims& d,
+              const RopeTab& rt, hipStream_t st) {
+  const int g = q_heads_per_block(d);
+  dim3 grid(ntok, (d.H + g - 1) / g);
+  q_finish_k<T><<<grid, 256, 0, st>>>(q, pos, q_nope, rope_out, tok_stride, head_stride, scale,
+                                       d, rt);
+}
+
+// blockIdx.y == 0: the token's latent row; blockIdx.y >= 1: a group of query
+// heads (one launch finishes the fused in-projection)
+template <typename T>
+__global__ void __launch_bounds__(256)
+step_finish_k(Part a, const int32_t* __restrict__ pos, const int64_t* __restrict__ slot,
+              const T* __restrict__ gamma, T* __restrict__ cache, T* __restrict__ q_nope,
+              T* __restrict__ rope_out, int64_t tok_stride, int64_t head_stride, float scale,
+              Dims d, RopeTab rt) {
+  __shared__ float red[4];
+  const int t = blockIdx.x;
+  if (blockIdx.y == 0) {
+    append_row_block<T>(a, t, pos[t], slot[t], gamma, cache, d, rt, red);
+    return;
+  }
+  Part q = a;
+  q.p += d.R;
+  const int g = q_heads_per_block(d);
+  const int h0 = (blockIdx.y - 1) * g, h1 = min(d.H, h0 + g);
+  q_finish_block<T>(q, t, pos[t], h0, h1, q_nope, rope_out, tok_stride, head_stride, scale, d,
+                    rt);
+}
+
+template <typename T>
+void step_finish(const Part& a, int ntok, const int32_t* pos, const int64_t* slot,
+                 const T* gamma, T* cache, T* q_nope, T* rope_out, int64_t tok_stride,
+                 int64_t head_stride, float scale, const Dims& d, const RopeTab& rt,
+                 hipStream_t st) {
+  const int g = q_heads_per_block(d);
+  dim3 grid(ntok, 1 + (d.H + g - 1) / g);
+  step_finish_k<T><<<grid, 256, 0, st>>>(a, pos, slot, gamma, cache, q_nope, rope_out,
+                                          tok_stride, head_stride, scale, d, rt);
 }
 
 template <typename T>
@@ -435,14 +490,14 @@ void prefill_attn_generic(const T* q_nope, const T* q_rope, const float* kv, con
 #define MLA_INST(T)                                                                          \
   template void gemm_generic<T>(const T*, int64_t, int64_t, const T*, int64_t, int64_t,     \
                                 float*, int, int, int, int, int, hipStream_t);              \
-  template void sum_store<T>(const float*, int, int, int, int, T*, int64_t, int64_t, float,  \
-                             hipStream_t);                                                   \
-  template void rmsnorm_rows<T>(const float*, int, int, int, const T*, float, T*,            \
-                                hipStream_t);                                                \
-  template void append_rows<T>(const float*, int, int, const int32_t*, const int64_t*,       \
-                               const T*, T*, const Dims&, hipStream_t);                      \
-  template void q_finish<T>(const float*, int, int, const int32_t*, T*, T*, int64_t, int64_t, \
-                            float, const Dims&, hipStream_t);                                \
+  template void rmsnorm_rows<T>(const Part&, int, int, const T*, float, T*, hipStream_t);    \
+  template void append_rows<T>(const Part&, int, const int32_t*, const int64_t*, const T*,   \
+                               T*, const Dims&, const RopeTab&, hipStream_t);                \
+  template void q_finish<T>(const Part&, int, const int32_t*, T*, T*, int64_t, int64_t,      \
+                            float, const Dims&, const RopeTab&, hipStream_t);                \
+  template void step_finish<T>(const Part&, int, const int32_t*, const int64_t*, const T*,   \
+                               T*, T*, T*, int64_t, int64_t, float, const Dims&,             \
+                               const RopeTab&, hipStream_t);                                 \
   template void cache_write<T>(const T*, const int64_t*, int, int, T*, hipStream_t);         \
   template void transpose_heads<T>(const T*, T*, int, int, int, int64_t, hipStream_t);        \
   template void decode_core_generic<T>(const T*, const T*, const DecodeMeta&, int, float*,   \

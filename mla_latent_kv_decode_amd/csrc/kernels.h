@@ -9,10 +9,18 @@
 
 namespace mla {
 
+// RoPE frequencies theta_i = base^(-2i/dr), computed once on the host in
+// double precision (dr <= 2 * kMaxRopePairs).
+constexpr int kMaxRopePairs = 64;
+
 // Shapes the kernels need, copied from the public config.
 struct Dims {
   int D, H, dn, dr, dv, dc, dq, R;
   float rope_base, eps, scale;
+};
+
+struct RopeTab {
+  double theta[kMaxRopePairs];
 };
 
 // One decode work segment: rows [r0, r1) of sequence b (row indices relative
@@ -38,30 +46,57 @@ struct DecodeMeta {
 template <typename T>
 void gemm_generic(const T* A, int64_t lda, int64_t sA, const T* W, int64_t ldw, int64_t sW,
                   float* C, int M, int N, int K, int batch, int ksplit, hipStream_t st);
-// MFMA bf16 version; needs K % (32*ksplit) == 0 and N % 16 == 0.
+// Fused GEMM epilogue: out[bt*so + m*ldo + n] = alpha * C (fp32 if f32 is set,
+// else rounded to bf16 into b16).
+struct GemmOut {
+  float* f32;
+  bf16* b16;
+  int64_t ldo, so;
+  float alpha;
+};
+// MFMA bf16 GEMM (decode shapes): needs N % 16 == 0, K % 128 == 0 and
+// (K/32) % (4*ksplit) == 0.  ksplit == 1: the result goes through `out`.
+// ksplit > 1: fp32 partials part[((z * batch + bt) * M + m) * N + n] are left
+// for the consumer to sum over z (the epilogue is not applied).
 void gemm_bf16_mfma(const bf16* A, int64_t lda, int64_t sA, const bf16* W, int64_t ldw,
-                    int64_t sW, float* C, int M, int N, int K, int batch, int ksplit,
-                    hipStream_t st);
+                    int64_t sW, int M, int N, int K, int batch, int ksplit, float* part,
+                    const GemmOut& out, hipStream_t st);
+int gemm_bf16_ksplit(int M, int N, int K, int batch, int n_cu);
+
+// Split-K partial sums as a consumer sees them: element (z, row, col) at
+// p[z * zs + row * ld + col], summed over z = 0..ks-1 in order.
+struct Part {
+  const float* p;
+  int ks;
+  int64_t ld, zs;
+};
+
+// out = alpha * sum_z C[z] (layout [z][bt][m][n]) with GemmOut's strides and type
+void gemm_store(const float* C, int ks, int M, int N, int batch, const GemmOut& out,
+                hipStream_t st);
 
 // ---- epilogues over split-K partials
-// out[bt*so + m*ldo + n] = T(alpha * sum_z part[z][bt][m][n])
+// out[row] = T(RMSNorm(sum_z x[z][row][0:n]) * gamma)
 template <typename T>
-void sum_store(const float* part, int ksplit, int M, int N, int batch, T* out, int64_t ldo,
-               int64_t so, float alpha, hipStream_t st);
-// out[row] = T(RMSNorm(sum_z part[z][row]) * gamma)   (row width n)
+void rmsnorm_rows(const Part& x, int rows, int n, const T* gamma, float eps, T* out,
+                  hipStream_t st);
+// latent rows: cache[slot[t]] = [RMSNorm(a[:dc])*gamma | RoPE(a[dc:R], pos[t])]
 template <typename T>
-void rmsnorm_rows(const float* part, int ksplit, int rows, int n, const T* gamma, float eps,
-                  T* out, hipStream_t st);
-// latent rows: cache[slot[t]] = [RMSNorm(a[:dc])*gamma | RoPE(a[dc:], pos[t])]
-template <typename T>
-void append_rows(const float* apart, int ksplit, int ntok, const int32_t* pos,
-                 const int64_t* slot, const T* gamma, T* cache, const Dims& d, hipStream_t st);
+void append_rows(const Part& a, int ntok, const int32_t* pos, const int64_t* slot,
+                 const T* gamma, T* cache, const Dims& d, const RopeTab& rt, hipStream_t st);
 // query heads: q_nope[t][h][:] = T(q_nope); rope_out[t*tok_stride + h*head_stride + i] =
 // T(scale * RoPE(q_rope)[i])
 template <typename T>
-void q_finish(const float* qpart, int ksplit, int ntok, const int32_t* pos, T* q_nope,
-              T* rope_out, int64_t tok_stride, int64_t head_stride, float scale,
-              const Dims& d, hipStream_t st);
+void q_finish(const Part& q, int ntok, const int32_t* pos, T* q_nope, T* rope_out,
+              int64_t tok_stride, int64_t head_stride, float scale, const Dims& d,
+              const RopeTab& rt, hipStream_t st);
+// append_rows on columns [0, R) and q_finish on columns [R, R + H(dn+dr)) of
+// one fused in-projection, one block per token
+template <typename T>
+void step_finish(const Part& a, int ntok, const int32_t* pos, const int64_t* slot,
+                 const T* gamma, T* cache, T* q_nope, T* rope_out, int64_t tok_stride,
+                 int64_t head_stride, float scale, const Dims& d, const RopeTab& rt,
+                 hipStream_t st);
 // per-head transpose: out[h][c][n] = in[h*stride + n*cols + c], n < rows, c < cols
 template <typename T>
 void transpose_heads(const T* in, T* out, int H, int rows, int cols, int64_t stride,
@@ -78,6 +113,9 @@ void decode_core_generic(const T* q_cat, const T* cache, const DecodeMeta& m, in
 // MFMA version: bf16, dc == 512, dr == 64, H % 16 == 0.  parts = persistent groups.
 void decode_core_mfma(const bf16* q_cat, const bf16* cache, const DecodeMeta& m, int parts,
                       int B, float* acc, float* ml, const Dims& d, hipStream_t st);
+// combine for dc == 512, bf16 output: all partial loads of a thread in flight at once
+void decode_combine_512(const float* acc, const float* ml, const DecodeMeta& m, int B, int H,
+                        bf16* o_lat, hipStream_t st);
 template <typename T>
 void decode_combine(const float* acc, const float* ml, const DecodeMeta& m, int B, T* o_lat,
                     const Dims& d, hipStream_t st);

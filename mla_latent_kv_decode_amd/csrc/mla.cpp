@@ -17,7 +17,7 @@
 #include <unordered_set>
 #include <vector>
 
-#include "../../include/mla.h"
+#include "mla.h"
 #include "kernels.h"
 
 using mla::bf16;
@@ -44,6 +44,7 @@ struct Staging {
 struct mla_ctx {
   mla_config cfg{};
   Dims d{};
+  mla::RopeTab rope{};
   hipStream_t stream = nullptr;
   int device = 0;
   int n_cu = 256;
@@ -61,8 +62,12 @@ struct mla_ctx {
   void* w_ukT = nullptr;  // (H, dc, dn): q_abs = q_nope . W_ukT^T per head
   void* w_uv = nullptr;   // (H, dv, dc)
   void* w_o = nullptr;
+  void* w_in = nullptr;   // [W_kva ; W_q] (or [W_kva ; W_qa]) rows: one in-projection GEMM
+  int n_in = 0;           // rows of w_in
   Staging ring[kRing];
   int ring_next = 0;
+  std::vector<void*> captured;  // pinned staging owned by captured graphs
+  hipEvent_t t_start = nullptr, t_stop = nullptr;  // caller's timing events
   std::string err;
 };
 
@@ -111,6 +116,18 @@ int check_launch(mla_ctx* h, const char* what) {
 // pinned staging ring.
 int stage_upload(mla_ctx* h, void* dst, const void* src, size_t bytes) {
   if (bytes == 0) return MLA_OK;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  HIP_TRY(h, hipStreamIsCapturing(h->stream, &cap));
+  if (cap == hipStreamCaptureStatusActive) {
+    // the graph's copy node reads this buffer at every replay: keep it for
+    // the life of the handle and never reuse it
+    void* p = nullptr;
+    HIP_TRY(h, hipHostMalloc(&p, bytes, hipHostMallocDefault));
+    h->captured.push_back(p);
+    memcpy(p, src, bytes);
+    HIP_TRY(h, hipMemcpyAsync(dst, p, bytes, hipMemcpyHostToDevice, h->stream));
+    return MLA_OK;
+  }
   Staging& s = h->ring[h->ring_next];
   h->ring_next = (h->ring_next + 1) % kRing;
   if (s.pending) {
@@ -145,44 +162,77 @@ struct Carve {
 
 bool is_f32(const mla_ctx* h) { return h->cfg.dtype == MLA_F32; }
 
-// split-K factor for a GEMM of M x N x K over `batch` problems: aims at >= ~2
-// blocks per CU for the MFMA kernel; K chunks stay whole multiples of 32.
-int choose_ksplit(const mla_ctx* h, int M, int N, int K, int batch) {
-  if (!h->mfma) return 1;
-  const long blocks = (long)((N + 63) / 64) * ((M + 63) / 64) * batch;
-  int ks = 1;
-  while (ks < 16 && blocks * ks < 2L * h->n_cu && (K / 32) % (ks * 2) == 0) ks *= 2;
-  return ks;
+bool mfma_gemm(const mla_ctx* h, int N, int K) {
+  // every one of the 4 K-slices of a block needs whole 32-wide k-steps
+  return h->cfg.dtype == MLA_BF16 && N % 16 == 0 && K % 128 == 0;
 }
 
+int gemm_ks(const mla_ctx* h, int M, int N, int K, int batch) {
+  return mfma_gemm(h, N, K) ? mla::gemm_bf16_ksplit(M, N, K, batch, h->n_cu) : 1;
+}
+
+// fp32 scratch floats of gemm_out (split-K partials, or the VALU path's C)
+size_t out_scratch(const mla_ctx* h, int M, int N, int K, int batch) {
+  const int ks = gemm_ks(h, M, N, K, batch);
+  if (mfma_gemm(h, N, K) && ks == 1) return 0;
+  return (size_t)ks * batch * M * N;
+}
+// fp32 floats of gemm_part's partial buffer
+size_t part_floats(const mla_ctx* h, int M, int N, int K) {
+  return (size_t)gemm_ks(h, M, N, K, 1) * M * N;
+}
+
+// out = alpha * A W^T (batched, strided).  MFMA path: epilogue fused when K is
+// not split, else partials in `scratch` and a store kernel sums them.
 template <typename T>
-void gemm_t(const mla_ctx* h, const T* A, int64_t lda, int64_t sA, const T* W, int64_t ldw,
-            int64_t sW, float* C, int M, int N, int K, int batch, int ksplit);
-
-template <>
-void gemm_t<float>(const mla_ctx* h, const float* A, int64_t lda, int64_t sA, const float* W,
-                   int64_t ldw, int64_t sW, float* C, int M, int N, int K, int batch,
-                   int ksplit) {
-  mla::gemm_generic<float>(A, lda, sA, W, ldw, sW, C, M, N, K, batch, ksplit, h->stream);
+void gemm_out(const mla_ctx* h, const T* A, int64_t lda, int64_t sA, const T* W, int64_t ldw,
+              int64_t sW, int M, int N, int K, int batch, const mla::GemmOut& out,
+              float* scratch) {
+  if constexpr (sizeof(T) == 2) {
+    if (mfma_gemm(h, N, K)) {
+      const int ks = gemm_ks(h, M, N, K, batch);
+      mla::gemm_bf16_mfma(A, lda, sA, W, ldw, sW, M, N, K, batch, ks, scratch, out, h->stream);
+      if (ks > 1) mla::gemm_store(scratch, ks, M, N, batch, out, h->stream);
+      return;
+    }
+  }
+  mla::gemm_generic<T>(A, lda, sA, W, ldw, sW, scratch, M, N, K, batch, 1, h->stream);
+  mla::gemm_store(scratch, 1, M, N, batch, out, h->stream);
 }
 
-template <>
-void gemm_t<bf16>(const mla_ctx* h, const bf16* A, int64_t lda, int64_t sA, const bf16* W,
-                  int64_t ldw, int64_t sW, float* C, int M, int N, int K, int batch,
-                  int ksplit) {
-  if (h->mfma && K % (32 * ksplit) == 0 && N % 16 == 0)
-    mla::gemm_bf16_mfma(A, lda, sA, W, ldw, sW, C, M, N, K, batch, ksplit, h->stream);
-  else
-    mla::gemm_generic<bf16>(A, lda, sA, W, ldw, sW, C, M, N, K, batch, ksplit, h->stream);
+// A W^T (batch 1) left as fp32 split-K partials in `part` for the consuming
+// kernel to sum (part_floats() floats).
+template <typename T>
+mla::Part gemm_part(const mla_ctx* h, const T* A, int64_t lda, const T* W, int64_t ldw, int M,
+                    int N, int K, float* part) {
+  if constexpr (sizeof(T) == 2) {
+    if (mfma_gemm(h, N, K)) {
+      const int ks = gemm_ks(h, M, N, K, 1);
+      mla::gemm_bf16_mfma(A, lda, 0, W, ldw, 0, M, N, K, 1, ks, part,
+                          mla::GemmOut{part, nullptr, N, 0, 1.f}, h->stream);
+      return mla::Part{part, ks, N, (int64_t)M * N};
+    }
+  }
+  mla::gemm_generic<T>(A, lda, 0, W, ldw, 0, part, M, N, K, 1, 1, h->stream);
+  return mla::Part{part, 1, N, (int64_t)M * N};
+}
+
+mla::GemmOut out_f32(float* p, int64_t ldo, int64_t so = 0, float alpha = 1.f) {
+  return mla::GemmOut{p, nullptr, ldo, so, alpha};
+}
+template <typename T>
+mla::GemmOut out_t(T* p, int64_t ldo, int64_t so = 0, float alpha = 1.f) {
+  if constexpr (sizeof(T) == 4) return mla::GemmOut{(float*)p, nullptr, ldo, so, alpha};
+  else return mla::GemmOut{nullptr, (bf16*)p, ldo, so, alpha};
 }
 
 // ------------------------------------------------------------------------
 // decode plan
 // ------------------------------------------------------------------------
 struct DecodeLayout {
-  int ks_qa = 1, ks_q = 1, ks_abs = 1, ks_uv = 1, ks_o = 1;
   int max_segs = 0;
-  size_t meta, cq_part, cq, q_part, q_nope, q_cat, abs_part, acc, ml, o_lat, uv_part, o, y_part;
+  bool step = false;  // fused append (mla_decode_step)
+  size_t meta, scratch, pin, pq, cq, q_nope, q_cat, acc, ml, o_lat, o;
   size_t total = 0;
 };
 
@@ -194,49 +244,53 @@ int max_parts(const mla_ctx* h, int64_t total_rows) {
 }
 
 size_t meta_bytes(int B, int parts, int max_segs) {
-  return align_up((size_t)B * 8) + 4 * align_up((size_t)B * 4) + align_up((size_t)(parts + 1) * 4) +
-         align_up((size_t)max_segs * sizeof(DecodeSeg));
+  return 2 * align_up((size_t)B * 8) + 4 * align_up((size_t)B * 4) +
+         align_up((size_t)(parts + 1) * 4) + align_up((size_t)max_segs * sizeof(DecodeSeg));
 }
 
-DecodeLayout decode_layout(const mla_ctx* h, int B, int64_t total_rows) {
+int qw_of(const Dims& d) { return d.H * (d.dn + d.dr); }
+
+DecodeLayout decode_layout(const mla_ctx* h, int B, int64_t total_rows, bool step) {
   const Dims& d = h->d;
   DecodeLayout L;
+  L.step = step;
   const int parts = max_parts(h, total_rows);
   L.max_segs = parts + B;
-  if (d.dq) {
-    L.ks_qa = choose_ksplit(h, B, d.dq, d.D, 1);
-    L.ks_q = choose_ksplit(h, B, d.H * (d.dn + d.dr), d.dq, 1);
-  } else {
-    L.ks_q = choose_ksplit(h, B, d.H * (d.dn + d.dr), d.D, 1);
-  }
-  L.ks_abs = choose_ksplit(h, B, d.dc, d.dn, d.H);
-  L.ks_uv = choose_ksplit(h, B, d.dv, d.dc, d.H);
-  L.ks_o = choose_ksplit(h, B, d.D, d.H * d.dv, 1);
+  const int qw = qw_of(d);
+  const size_t scr = std::max({out_scratch(h, B, d.dc, d.dn, d.H),
+                               out_scratch(h, B, d.dv, d.dc, d.H),
+                               out_scratch(h, B, d.D, d.H * d.dv, 1)});
+  // partials of the first projection (in-projection for a step, else q or q_a)
+  size_t pin = 0, pq = 0;
+  if (step) pin = part_floats(h, B, h->n_in, d.D);
+  else pin = part_floats(h, B, d.dq ? d.dq : qw, d.D);
+  if (d.dq) pq = part_floats(h, B, qw, d.dq);
   const size_t e = h->esz;
   Carve c;
   L.meta = c.take(meta_bytes(B, parts, L.max_segs));
-  L.cq_part = c.take(d.dq ? (size_t)L.ks_qa * B * d.dq * 4 : 0);
+  L.scratch = c.take(scr * 4);
+  L.pin = c.take(pin * 4);
+  L.pq = c.take(pq * 4);
   L.cq = c.take(d.dq ? (size_t)B * d.dq * e : 0);
-  L.q_part = c.take((size_t)L.ks_q * B * d.H * (d.dn + d.dr) * 4);
   L.q_nope = c.take((size_t)B * d.H * d.dn * e);
   L.q_cat = c.take((size_t)B * d.H * d.R * e);
-  L.abs_part = c.take((size_t)L.ks_abs * d.H * B * d.dc * 4);
   L.acc = c.take((size_t)L.max_segs * d.H * d.dc * 4);
   L.ml = c.take((size_t)L.max_segs * d.H * 2 * 4);
   L.o_lat = c.take((size_t)B * d.H * d.dc * e);
-  L.uv_part = c.take((size_t)L.ks_uv * d.H * B * d.dv * 4);
   L.o = c.take((size_t)B * d.H * d.dv * e);
-  L.y_part = c.take((size_t)L.ks_o * B * d.D * 4);
   L.total = c.off;
   return L;
 }
 
+struct MetaOffsets {
+  size_t seq_off, seq_len, pos, pstart, nseg, part, segs, slot;
+};
+
 // Host-side work list: equal spans of the concatenated rows, cut at sequence
 // boundaries.  Returns parts and fills the packed metadata blob.
 int build_decode_meta(const mla_ctx* h, int B, const int64_t* seq_off, const int32_t* seq_len,
-                      const int32_t* pos, int64_t total, std::vector<char>& blob,
-                      size_t* o_seq_off, size_t* o_seq_len, size_t* o_pos, size_t* o_pstart,
-                      size_t* o_nseg, size_t* o_part, size_t* o_segs, int* nseg_total) {
+                      const int32_t* pos, int64_t total, bool with_slot, std::vector<char>& blob,
+                      MetaOffsets* mo, int* nseg_total) {
   int parts = max_parts(h, total);
   const int64_t per = (total + parts - 1) / parts;
   parts = (int)((total + per - 1) / per);
@@ -262,21 +316,26 @@ int build_decode_meta(const mla_ctx* h, int B, const int64_t* seq_off, const int
     part_begin.push_back((int32_t)segs.size());
   }
   Carve c;
-  *o_seq_off = c.take((size_t)B * 8);
-  *o_seq_len = c.take((size_t)B * 4);
-  *o_pos = c.take((size_t)B * 4);
-  *o_pstart = c.take((size_t)B * 4);
-  *o_nseg = c.take((size_t)B * 4);
-  *o_part = c.take((size_t)(parts + 1) * 4);
-  *o_segs = c.take(segs.size() * sizeof(DecodeSeg));
+  mo->seq_off = c.take((size_t)B * 8);
+  mo->slot = c.take(with_slot ? (size_t)B * 8 : 0);
+  mo->seq_len = c.take((size_t)B * 4);
+  mo->pos = c.take((size_t)B * 4);
+  mo->pstart = c.take((size_t)B * 4);
+  mo->nseg = c.take((size_t)B * 4);
+  mo->part = c.take((size_t)(parts + 1) * 4);
+  mo->segs = c.take(segs.size() * sizeof(DecodeSeg));
   blob.assign(c.off, 0);
-  memcpy(blob.data() + *o_seq_off, seq_off, (size_t)B * 8);
-  memcpy(blob.data() + *o_seq_len, seq_len, (size_t)B * 4);
-  memcpy(blob.data() + *o_pos, pos, (size_t)B * 4);
-  memcpy(blob.data() + *o_pstart, pstart.data(), (size_t)B * 4);
-  memcpy(blob.data() + *o_nseg, nseg.data(), (size_t)B * 4);
-  memcpy(blob.data() + *o_part, part_begin.data(), part_begin.size() * 4);
-  memcpy(blob.data() + *o_segs, segs.data(), segs.size() * sizeof(DecodeSeg));
+  memcpy(blob.data() + mo->seq_off, seq_off, (size_t)B * 8);
+  if (with_slot) {
+    int64_t* sl = reinterpret_cast<int64_t*>(blob.data() + mo->slot);
+    for (int i = 0; i < B; ++i) sl[i] = seq_off[i] + seq_len[i] - 1;
+  }
+  memcpy(blob.data() + mo->seq_len, seq_len, (size_t)B * 4);
+  memcpy(blob.data() + mo->pos, pos, (size_t)B * 4);
+  memcpy(blob.data() + mo->pstart, pstart.data(), (size_t)B * 4);
+  memcpy(blob.data() + mo->nseg, nseg.data(), (size_t)B * 4);
+  memcpy(blob.data() + mo->part, part_begin.data(), part_begin.size() * 4);
+  memcpy(blob.data() + mo->segs, segs.data(), segs.size() * sizeof(DecodeSeg));
   *nseg_total = (int)segs.size();
   return parts;
 }
@@ -331,6 +390,7 @@ int mla_config_check(const mla_config* c) {
   if (c->qk_rope % 2) return MLA_ERR_SHAPE;  // RoPE rotates pairs
   // kernel limits of the VALU paths: latent width and v_head per thread block
   if (c->kv_lora > 1024 || c->v_head > 256) return MLA_ERR_SHAPE;
+  if (c->qk_rope > 2 * mla::kMaxRopePairs) return MLA_ERR_SHAPE;
   return MLA_OK;
 }
 
@@ -400,18 +460,21 @@ int mla_create(const mla_config* cfg, void* stream, mla_handle* out) {
   d.dv = cfg->v_head; d.dc = cfg->kv_lora; d.dq = cfg->q_lora; d.R = d.dc + d.dr;
   d.rope_base = cfg->rope_base; d.eps = cfg->rms_eps;
   d.scale = cfg->softmax_scale > 0.f ? cfg->softmax_scale : 1.0f / sqrtf((float)(d.dn + d.dr));
+  for (int i = 0; i < d.dr / 2; ++i)
+    h->rope.theta[i] = pow((double)cfg->rope_base, -2.0 * i / (double)d.dr);
   int ncu = 0;
   if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
       ncu > 0)
     h->n_cu = ncu;
   h->mfma = cfg->dtype == MLA_BF16 && d.dc == 512 && d.dr == 64 && d.H % 16 == 0;
+  h->n_in = d.R + (d.dq ? d.dq : qw_of(d));
   *out = h;
   return MLA_OK;
 }
 
 static void free_weights(mla_ctx* h) {
-  void** ws[] = {&h->w_q, &h->w_qa, &h->q_norm_g, &h->w_qb, &h->w_kva,
-                 &h->kv_norm_g, &h->w_kvb, &h->w_ukT, &h->w_uv, &h->w_o};
+  void** ws[] = {&h->w_q, &h->w_qa, &h->q_norm_g, &h->w_qb, &h->w_kva, &h->kv_norm_g,
+                 &h->w_kvb, &h->w_ukT, &h->w_uv, &h->w_o, &h->w_in};
   for (void** p : ws) {
     if (*p) (void)hipFree(*p);
     *p = nullptr;
@@ -428,7 +491,17 @@ int mla_destroy(mla_handle h) {
     if (s.ev) (void)hipEventDestroy(s.ev);
     if (s.host) (void)hipHostFree(s.host);
   }
+  for (void* p : h->captured) (void)hipHostFree(p);
   delete h;
+  return MLA_OK;
+}
+
+int mla_set_timing_events(mla_handle h, void* start, void* stop) {
+  if (!h) return MLA_ERR_INVALID_ARG;
+  if ((start == nullptr) != (stop == nullptr))
+    return fail(h, MLA_ERR_INVALID_ARG, "timing events: give both or neither");
+  h->t_start = (hipEvent_t)start;
+  h->t_stop = (hipEvent_t)stop;
   return MLA_OK;
 }
 
@@ -460,7 +533,7 @@ int mla_absorb_weights(mla_handle h, const void* w_q, const void* w_qa, const vo
     return MLA_OK;
   };
   int rc;
-  const size_t qw = (size_t)d.H * (d.dn + d.dr);
+  const size_t qw = (size_t)qw_of(d);
   if (d.dq) {
     if ((rc = dup(&h->w_qa, w_qa, (size_t)d.dq * d.D))) return rc;
     if ((rc = dup(&h->q_norm_g, q_norm_g, (size_t)d.dq))) return rc;
@@ -474,6 +547,13 @@ int mla_absorb_weights(mla_handle h, const void* w_q, const void* w_qa, const vo
   }
   if ((rc = dup(&h->w_kvb, w_kvb, (size_t)d.H * (d.dn + d.dv) * d.dc))) return rc;
   if ((rc = dup(&h->w_o, w_o, (size_t)d.D * d.H * d.dv))) return rc;
+  // in-projection rows [W_kva ; W_q] (or [W_kva ; W_qa]): both read the hidden state
+  HIP_TRY(h, hipMalloc(&h->w_in, (size_t)h->n_in * d.D * e));
+  HIP_TRY(h, hipMemcpyAsync(h->w_in, w_kva, (size_t)d.R * d.D * e, hipMemcpyDeviceToDevice,
+                            h->stream));
+  HIP_TRY(h, hipMemcpyAsync(static_cast<char*>(h->w_in) + (size_t)d.R * d.D * e,
+                            d.dq ? w_qa : w_q, (size_t)(h->n_in - d.R) * d.D * e,
+                            hipMemcpyDeviceToDevice, h->stream));
   // W_UV per head: rows dn .. dn+dv of each head's kv_b block, packed (H, dv, dc)
   HIP_TRY(h, hipMalloc(&h->w_uv, (size_t)d.H * d.dv * d.dc * e));
   HIP_TRY(h, hipMemcpy2DAsync(h->w_uv, (size_t)d.dv * d.dc * e,
@@ -494,14 +574,37 @@ int mla_absorb_weights(mla_handle h, const void* w_q, const void* w_qa, const vo
   return MLA_OK;
 }
 
+// ------------------------------------------------------------------------
+// append
+// ------------------------------------------------------------------------
+namespace {
+struct AppendLayout {
+  size_t pos, slot, part, total;
+};
+AppendLayout append_layout(const mla_ctx* h, int T) {
+  AppendLayout L;
+  Carve c;
+  L.pos = c.take((size_t)T * 4);
+  L.slot = c.take((size_t)T * 8);
+  L.part = c.take(part_floats(h, T, h->d.R, h->d.D) * 4);
+  L.total = c.off;
+  return L;
+}
+}  // namespace
+
 size_t mla_append_workspace_bytes(mla_handle h, int32_t T) {
   if (!h || T <= 0) return 0;
-  Carve c;
-  c.take((size_t)T * 4);
-  c.take((size_t)T * 8);
-  const int ks = choose_ksplit(h, T, h->d.R, h->d.D, 1);
-  c.take((size_t)ks * T * h->d.R * 4);
-  return c.off;
+  return append_layout(h, T).total;
+}
+
+template <typename T>
+static void run_append(mla_ctx* h, const T* hidden, int ntok, T* cache, void* ws,
+                       const AppendLayout& L) {
+  const Dims& d = h->d;
+  const mla::Part a =
+      gemm_part<T>(h, hidden, d.D, (const T*)h->w_kva, d.D, ntok, d.R, d.D, at<float>(ws, L.part));
+  mla::append_rows<T>(a, ntok, at<int32_t>(ws, L.pos), at<int64_t>(ws, L.slot),
+                      (const T*)h->kv_norm_g, cache, d, h->rope, h->stream);
 }
 
 int mla_append_latent(mla_handle h, const void* hidden, const int32_t* pos, const int64_t* slot,
@@ -512,31 +615,18 @@ int mla_append_latent(mla_handle h, const void* hidden, const int32_t* pos, cons
   if (rc) return fail(h, rc, "append: %s (T=%d, cache_rows=%lld)", mla_status_string(rc), T,
                       (long long)cache_rows);
   if (!h->absorbed) return fail(h, MLA_ERR_STATE, "append before mla_absorb_weights");
-  const size_t need = mla_append_workspace_bytes(h, T);
-  if ((rc = check_ws(h, ws, ws_bytes, need))) return rc;
+  const AppendLayout L = append_layout(h, T);
+  if ((rc = check_ws(h, ws, ws_bytes, L.total))) return rc;
   DeviceGuard g(h->device);
   if (!g.ok) return fail(h, MLA_ERR_HIP, "cannot select device %d", h->device);
-  Carve c;
-  const size_t o_pos = c.take((size_t)T * 4), o_slot = c.take((size_t)T * 8);
-  const int ks = choose_ksplit(h, T, h->d.R, h->d.D, 1);
-  const size_t o_part = c.take((size_t)ks * T * h->d.R * 4);
-  std::vector<char> blob(o_part, 0);
-  memcpy(blob.data() + o_pos, pos, (size_t)T * 4);
-  memcpy(blob.data() + o_slot, slot, (size_t)T * 8);
+  std::vector<char> blob(L.part, 0);
+  memcpy(blob.data() + L.pos, pos, (size_t)T * 4);
+  memcpy(blob.data() + L.slot, slot, (size_t)T * 8);
   if ((rc = stage_upload(h, ws, blob.data(), blob.size()))) return rc;
-  const Dims& d = h->d;
-  float* part = at<float>(ws, o_part);
-  if (is_f32(h)) {
-    gemm_t<float>(h, (const float*)hidden, d.D, 0, (const float*)h->w_kva, d.D, 0, part, T, d.R,
-                  d.D, 1, ks);
-    mla::append_rows<float>(part, ks, T, at<int32_t>(ws, o_pos), at<int64_t>(ws, o_slot),
-                            (const float*)h->kv_norm_g, (float*)cache, d, h->stream);
-  } else {
-    gemm_t<bf16>(h, (const bf16*)hidden, d.D, 0, (const bf16*)h->w_kva, d.D, 0, part, T, d.R, d.D,
-                 1, ks);
-    mla::append_rows<bf16>(part, ks, T, at<int32_t>(ws, o_pos), at<int64_t>(ws, o_slot),
-                           (const bf16*)h->kv_norm_g, (bf16*)cache, d, h->stream);
-  }
+  if (is_f32(h))
+    run_append<float>(h, (const float*)hidden, T, (float*)cache, ws, L);
+  else
+    run_append<bf16>(h, (const bf16*)hidden, T, (bf16*)cache, ws, L);
   return check_launch(h, "append");
 }
 
@@ -567,123 +657,163 @@ int mla_cache_write(mla_handle h, const void* rows, const int64_t* slot, int32_t
   return check_launch(h, "cache_write");
 }
 
+// ------------------------------------------------------------------------
+// decode
+// ------------------------------------------------------------------------
 size_t mla_decode_workspace_bytes(mla_handle h, int32_t B, int64_t total_rows) {
   if (!h || B <= 0 || total_rows <= 0) return 0;
-  return decode_layout(h, B, total_rows).total;
+  return decode_layout(h, B, total_rows, false).total;
+}
+
+size_t mla_decode_step_workspace_bytes(mla_handle h, int32_t B, int64_t total_rows) {
+  if (!h || B <= 0 || total_rows <= 0) return 0;
+  return decode_layout(h, B, total_rows, true).total;
 }
 
 int mla_decode_stage_offsets(mla_handle h, int32_t B, int64_t total_rows, size_t* q_cat_off,
                              size_t* o_lat_off) {
   if (!h || B <= 0 || total_rows <= 0 || !q_cat_off || !o_lat_off) return MLA_ERR_INVALID_ARG;
-  const DecodeLayout L = decode_layout(h, B, total_rows);
+  const DecodeLayout L = decode_layout(h, B, total_rows, false);
   *q_cat_off = L.q_cat;
   *o_lat_off = L.o_lat;
   return MLA_OK;
 }
 
+// A3 (+ A2 for a step): query projection, RoPE of the rope part (scaled into
+// q_cat) and, for a step, the new latent rows.
 template <typename T>
-static void run_q_path(mla_ctx* h, const T* x, int ntok, const DecodeLayout* L, void* ws,
-                       float* cq_part, T* cq, float* q_part, int ks_qa, int ks_q, T* q_nope,
-                       T* rope_out, int64_t tok_stride, int64_t head_stride, float scale,
-                       const int32_t* pos_dev) {
-  (void)L;
-  (void)ws;
+static void run_q_and_append(mla_ctx* h, const T* x, int B, void* ws, const DecodeLayout& L,
+                             const DecodeMeta& mt, const int64_t* slot_dev, T* cache) {
   const Dims& d = h->d;
-  const int qw = d.H * (d.dn + d.dr);
-  if (d.dq) {
-    gemm_t<T>(h, x, d.D, 0, (const T*)h->w_qa, d.D, 0, cq_part, ntok, d.dq, d.D, 1, ks_qa);
-    mla::rmsnorm_rows<T>(cq_part, ks_qa, ntok, d.dq, (const T*)h->q_norm_g, d.eps, cq, h->stream);
-    gemm_t<T>(h, cq, d.dq, 0, (const T*)h->w_qb, d.dq, 0, q_part, ntok, qw, d.dq, 1, ks_q);
+  const int qw = qw_of(d);
+  T* q_nope = at<T>(ws, L.q_nope);
+  T* q_rope = at<T>(ws, L.q_cat) + d.dc;
+  const int64_t tok_stride = (int64_t)d.H * d.R;
+  mla::Part pq;
+  if (L.step) {
+    // one GEMM for [kv_a | q (or q_a)] over the same hidden states
+    const mla::Part pin = gemm_part<T>(h, x, d.D, (const T*)h->w_in, d.D, B, h->n_in, d.D,
+                                       at<float>(ws, L.pin));
+    if (!d.dq) {
+      mla::step_finish<T>(pin, B, mt.pos, slot_dev, (const T*)h->kv_norm_g, cache, q_nope, q_rope,
+                          tok_stride, d.R, d.scale, d, h->rope, h->stream);
+      return;
+    }
+    mla::append_rows<T>(pin, B, mt.pos, slot_dev, (const T*)h->kv_norm_g, cache, d, h->rope,
+                        h->stream);
+    mla::Part pa = pin;
+    pa.p += d.R;
+    mla::rmsnorm_rows<T>(pa, B, d.dq, (const T*)h->q_norm_g, d.eps, at<T>(ws, L.cq), h->stream);
+    pq = gemm_part<T>(h, at<T>(ws, L.cq), d.dq, (const T*)h->w_qb, d.dq, B, qw, d.dq,
+                      at<float>(ws, L.pq));
+  } else if (d.dq) {
+    const mla::Part pa = gemm_part<T>(h, x, d.D, (const T*)h->w_qa, d.D, B, d.dq, d.D,
+                                      at<float>(ws, L.pin));
+    mla::rmsnorm_rows<T>(pa, B, d.dq, (const T*)h->q_norm_g, d.eps, at<T>(ws, L.cq), h->stream);
+    pq = gemm_part<T>(h, at<T>(ws, L.cq), d.dq, (const T*)h->w_qb, d.dq, B, qw, d.dq,
+                      at<float>(ws, L.pq));
   } else {
-    gemm_t<T>(h, x, d.D, 0, (const T*)h->w_q, d.D, 0, q_part, ntok, qw, d.D, 1, ks_q);
+    pq = gemm_part<T>(h, x, d.D, (const T*)h->w_q, d.D, B, qw, d.D, at<float>(ws, L.pin));
   }
-  mla::q_finish<T>(q_part, ks_q, ntok, pos_dev, q_nope, rope_out, tok_stride, head_stride, scale,
-                   d, h->stream);
+  mla::q_finish<T>(pq, B, mt.pos, q_nope, q_rope, tok_stride, d.R, d.scale, d, h->rope,
+                   h->stream);
 }
 
 template <typename T>
-static int run_decode(mla_ctx* h, const T* hidden, int B, const T* cache, T* out, void* ws,
+static int run_decode(mla_ctx* h, const T* hidden, int B, T* cache, T* out, void* ws,
                       const DecodeLayout& L, const DecodeMeta& mt, int parts, int nseg_total,
-                      const int32_t* pos_dev) {
+                      const int64_t* slot_dev) {
   const Dims& d = h->d;
+  float* scratch = at<float>(ws, L.scratch);
   T* q_nope = at<T>(ws, L.q_nope);
   T* q_cat = at<T>(ws, L.q_cat);
-  // A3: query projection + RoPE of the rope part (scaled, into q_cat)
-  run_q_path<T>(h, hidden, B, &L, ws, at<float>(ws, L.cq_part), at<T>(ws, L.cq),
-                at<float>(ws, L.q_part), L.ks_qa, L.ks_q, q_nope, q_cat + d.dc,
-                (int64_t)d.H * d.R, d.R, d.scale, pos_dev);
+  run_q_and_append<T>(h, hidden, B, ws, L, mt, slot_dev, cache);
   // A4: absorbed query q_abs_h = W_UK_h^T q_nope_h, scaled into q_cat[:, :, :dc]
-  float* abs_part = at<float>(ws, L.abs_part);
-  gemm_t<T>(h, q_nope, (int64_t)d.H * d.dn, d.dn, (const T*)h->w_ukT, d.dn, (int64_t)d.dc * d.dn,
-            abs_part, B, d.dc, d.dn, d.H, L.ks_abs);
-  mla::sum_store<T>(abs_part, L.ks_abs, B, d.dc, d.H, q_cat, (int64_t)d.H * d.R, d.R, d.scale,
-                    h->stream);
+  gemm_out<T>(h, q_nope, (int64_t)d.H * d.dn, d.dn, (const T*)h->w_ukT, d.dn,
+              (int64_t)d.dc * d.dn, B, d.dc, d.dn, d.H,
+              out_t<T>(q_cat, (int64_t)d.H * d.R, d.R, d.scale), scratch);
   // A5: split-S latent attention core
   float* acc = at<float>(ws, L.acc);
   float* ml = at<float>(ws, L.ml);
-  if constexpr (sizeof(T) == 2) {
-    if (h->mfma)
-      mla::decode_core_mfma(q_cat, cache, mt, parts, B, acc, ml, d, h->stream);
-    else
-      mla::decode_core_generic<T>(q_cat, cache, mt, nseg_total, acc, ml, d, h->stream);
-  } else {
-    mla::decode_core_generic<T>(q_cat, cache, mt, nseg_total, acc, ml, d, h->stream);
-  }
-  // A6: combine the partials of each sequence
   T* o_lat = at<T>(ws, L.o_lat);
-  mla::decode_combine<T>(acc, ml, mt, B, o_lat, d, h->stream);
+  bool mfma_core = false;
+  if (h->t_start) HIP_TRY(h, hipEventRecord(h->t_start, h->stream));
+  if constexpr (sizeof(T) == 2) {
+    if (h->mfma) {
+      mla::decode_core_mfma(q_cat, cache, mt, parts, B, acc, ml, d, h->stream);
+      mfma_core = true;
+    }
+  }
+  if (!mfma_core) mla::decode_core_generic<T>(q_cat, cache, mt, nseg_total, acc, ml, d, h->stream);
+  if (h->t_stop) HIP_TRY(h, hipEventRecord(h->t_stop, h->stream));
+  // A6: combine the partials of each sequence (fixed slot order)
+  if constexpr (sizeof(T) == 2) {
+    if (mfma_core) mla::decode_combine_512(acc, ml, mt, B, d.H, (bf16*)o_lat, h->stream);
+  }
+  if (!mfma_core) mla::decode_combine<T>(acc, ml, mt, B, o_lat, d, h->stream);
   // A7: o_h = W_UV_h o_lat_h
-  float* uv_part = at<float>(ws, L.uv_part);
   T* o = at<T>(ws, L.o);
-  gemm_t<T>(h, o_lat, (int64_t)d.H * d.dc, d.dc, (const T*)h->w_uv, d.dc, (int64_t)d.dv * d.dc,
-            uv_part, B, d.dv, d.dc, d.H, L.ks_uv);
-  mla::sum_store<T>(uv_part, L.ks_uv, B, d.dv, d.H, o, (int64_t)d.H * d.dv, d.dv, 1.f, h->stream);
+  gemm_out<T>(h, o_lat, (int64_t)d.H * d.dc, d.dc, (const T*)h->w_uv, d.dc, (int64_t)d.dv * d.dc,
+              B, d.dv, d.dc, d.H, out_t<T>(o, (int64_t)d.H * d.dv, d.dv), scratch);
   // A8: y = W_o o
-  float* y_part = at<float>(ws, L.y_part);
-  gemm_t<T>(h, o, (int64_t)d.H * d.dv, 0, (const T*)h->w_o, (int64_t)d.H * d.dv, 0, y_part, B, d.D,
-            d.H * d.dv, 1, L.ks_o);
-  mla::sum_store<T>(y_part, L.ks_o, B, d.D, 1, out, d.D, 0, 1.f, h->stream);
+  gemm_out<T>(h, o, (int64_t)d.H * d.dv, 0, (const T*)h->w_o, (int64_t)d.H * d.dv, 0, B, d.D,
+              d.H * d.dv, 1, out_t<T>(out, d.D), scratch);
   return check_launch(h, "decode");
 }
 
-int mla_decode(mla_handle h, const void* hidden, const int32_t* pos, const int64_t* seq_off,
-               const int32_t* seq_len, int32_t B, const void* cache, int64_t cache_rows, void* out,
-               void* ws, size_t ws_bytes) {
+static int decode_common(mla_handle h, const void* hidden, const int32_t* pos,
+                         const int64_t* seq_off, const int32_t* seq_len, int32_t B, void* cache,
+                         int64_t cache_rows, void* out, void* ws, size_t ws_bytes, bool step) {
   if (!h) return MLA_ERR_INVALID_ARG;
-  if (!hidden || !cache || !out) return fail(h, MLA_ERR_INVALID_ARG, "decode: NULL tensor");
-  int rc0 = mla_decode_check(&h->cfg, pos, seq_off, seq_len, B, cache_rows);
-  if (rc0) return fail(h, rc0, "decode: %s (B=%d, cache_rows=%lld)", mla_status_string(rc0), B,
-                       (long long)cache_rows);
-  if (!h->absorbed) return fail(h, MLA_ERR_STATE, "decode before mla_absorb_weights");
+  const char* what = step ? "decode_step" : "decode";
+  if (!hidden || !cache || !out) return fail(h, MLA_ERR_INVALID_ARG, "%s: NULL tensor", what);
+  int rc = mla_decode_check(&h->cfg, pos, seq_off, seq_len, B, cache_rows);
+  if (rc) return fail(h, rc, "%s: %s (B=%d, cache_rows=%lld)", what, mla_status_string(rc), B,
+                      (long long)cache_rows);
+  if (!h->absorbed) return fail(h, MLA_ERR_STATE, "%s before mla_absorb_weights", what);
   int64_t total = 0;
   for (int32_t b = 0; b < B; ++b) total += seq_len[b];
-  const DecodeLayout L = decode_layout(h, B, total);
-  int rc = check_ws(h, ws, ws_bytes, L.total);
-  if (rc) return rc;
+  const DecodeLayout L = decode_layout(h, B, total, step);
+  if ((rc = check_ws(h, ws, ws_bytes, L.total))) return rc;
   DeviceGuard g(h->device);
   if (!g.ok) return fail(h, MLA_ERR_HIP, "cannot select device %d", h->device);
   std::vector<char> blob;
-  size_t o_so, o_sl, o_pos, o_ps, o_ns, o_pb, o_sg;
+  MetaOffsets mo;
   int nseg_total = 0;
-  const int parts = build_decode_meta(h, B, seq_off, seq_len, pos, total, blob, &o_so, &o_sl,
-                                      &o_pos, &o_ps, &o_ns, &o_pb, &o_sg, &nseg_total);
+  const int parts =
+      build_decode_meta(h, B, seq_off, seq_len, pos, total, step, blob, &mo, &nseg_total);
   if (blob.size() > meta_bytes(B, max_parts(h, total), L.max_segs))
     return fail(h, MLA_ERR_WORKSPACE, "internal: decode metadata larger than planned");
   void* meta = at<char>(ws, L.meta);
   if ((rc = stage_upload(h, meta, blob.data(), blob.size()))) return rc;
   DecodeMeta mt;
-  mt.seq_off = at<int64_t>(meta, o_so);
-  mt.seq_len = at<int32_t>(meta, o_sl);
-  mt.pos = at<int32_t>(meta, o_pos);
-  mt.pstart = at<int32_t>(meta, o_ps);
-  mt.nseg = at<int32_t>(meta, o_ns);
-  mt.part_begin = at<int32_t>(meta, o_pb);
-  mt.segs = at<DecodeSeg>(meta, o_sg);
+  mt.seq_off = at<int64_t>(meta, mo.seq_off);
+  mt.seq_len = at<int32_t>(meta, mo.seq_len);
+  mt.pos = at<int32_t>(meta, mo.pos);
+  mt.pstart = at<int32_t>(meta, mo.pstart);
+  mt.nseg = at<int32_t>(meta, mo.nseg);
+  mt.part_begin = at<int32_t>(meta, mo.part);
+  mt.segs = at<DecodeSeg>(meta, mo.segs);
+  const int64_t* slot_dev = step ? at<int64_t>(meta, mo.slot) : nullptr;
   if (is_f32(h))
-    return run_decode<float>(h, (const float*)hidden, B, (const float*)cache, (float*)out, ws, L,
-                             mt, parts, nseg_total, mt.pos);
-  return run_decode<bf16>(h, (const bf16*)hidden, B, (const bf16*)cache, (bf16*)out, ws, L, mt,
-                          parts, nseg_total, mt.pos);
+    return run_decode<float>(h, (const float*)hidden, B, (float*)cache, (float*)out, ws, L, mt,
+                             parts, nseg_total, slot_dev);
+  return run_decode<bf16>(h, (const bf16*)hidden, B, (bf16*)cache, (bf16*)out, ws, L, mt, parts,
+                          nseg_total, slot_dev);
+}
+
+int mla_decode(mla_handle h, const void* hidden, const int32_t* pos, const int64_t* seq_off,
+               const int32_t* seq_len, int32_t B, const void* cache, int64_t cache_rows, void* out,
+               void* ws, size_t ws_bytes) {
+  return decode_common(h, hidden, pos, seq_off, seq_len, B, const_cast<void*>(cache), cache_rows,
+                       out, ws, ws_bytes, false);
+}
+
+int mla_decode_step(mla_handle h, const void* hidden, const int32_t* pos, const int64_t* seq_off,
+                    const int32_t* seq_len, int32_t B, void* cache, int64_t cache_rows, void* out,
+                    void* ws, size_t ws_bytes) {
+  return decode_common(h, hidden, pos, seq_off, seq_len, B, cache, cache_rows, out, ws, ws_bytes,
+                       true);
 }
 
 // ------------------------------------------------------------------------
@@ -691,31 +821,28 @@ int mla_decode(mla_handle h, const void* hidden, const int32_t* pos, const int64
 // ------------------------------------------------------------------------
 namespace {
 struct PrefillLayout {
-  int ks_qa = 1, ks_q = 1, ks_o = 1;
-  size_t meta, cq_part, cq, q_part, q_nope, q_rope, kv, o, y_part, total;
+  size_t meta, scratch, pin, pq, cq, q_nope, q_rope, kv, o, total;
 };
 
-PrefillLayout prefill_layout(const mla_ctx* h, int T, int B, int64_t rows) {
+PrefillLayout prefill_layout(const mla_ctx* h, int T, int B, int64_t rows, int max_rows) {
   const Dims& d = h->d;
   PrefillLayout L;
-  if (d.dq) {
-    L.ks_qa = choose_ksplit(h, T, d.dq, d.D, 1);
-    L.ks_q = choose_ksplit(h, T, d.H * (d.dn + d.dr), d.dq, 1);
-  } else {
-    L.ks_q = choose_ksplit(h, T, d.H * (d.dn + d.dr), d.D, 1);
-  }
-  L.ks_o = choose_ksplit(h, T, d.D, d.H * d.dv, 1);
+  const int qw = qw_of(d);
+  const size_t scr = std::max(out_scratch(h, T, d.D, d.H * d.dv, 1),
+                              out_scratch(h, max_rows, d.H * (d.dn + d.dv), d.dc, 1));
+  const size_t pin = part_floats(h, T, d.dq ? d.dq : qw, d.D);
+  const size_t pq = d.dq ? part_floats(h, T, qw, d.dq) : 0;
   const size_t e = h->esz;
   Carve c;
   L.meta = c.take(align_up((size_t)T * 4) * 2 + align_up((size_t)B * 8) * 2);
-  L.cq_part = c.take(d.dq ? (size_t)L.ks_qa * T * d.dq * 4 : 0);
+  L.scratch = c.take(scr * 4);
+  L.pin = c.take(pin * 4);
+  L.pq = c.take(pq * 4);
   L.cq = c.take(d.dq ? (size_t)T * d.dq * e : 0);
-  L.q_part = c.take((size_t)L.ks_q * T * d.H * (d.dn + d.dr) * 4);
   L.q_nope = c.take((size_t)T * d.H * d.dn * e);
   L.q_rope = c.take((size_t)T * d.H * std::max(d.dr, 1) * e);
   L.kv = c.take((size_t)rows * d.H * (d.dn + d.dv) * 4);
   L.o = c.take((size_t)T * d.H * d.dv * e);
-  L.y_part = c.take((size_t)L.ks_o * T * d.D * 4);
   L.total = c.off;
   return L;
 }
@@ -723,7 +850,8 @@ PrefillLayout prefill_layout(const mla_ctx* h, int T, int B, int64_t rows) {
 
 size_t mla_prefill_workspace_bytes(mla_handle h, int32_t T, int32_t B, int64_t total_key_rows) {
   if (!h || T <= 0 || B <= 0 || total_key_rows <= 0) return 0;
-  return prefill_layout(h, T, B, total_key_rows).total;
+  const int max_rows = (int)std::min<int64_t>(total_key_rows, INT32_MAX);
+  return prefill_layout(h, T, B, total_key_rows, max_rows).total;
 }
 
 template <typename T>
@@ -731,33 +859,45 @@ static int run_prefill(mla_ctx* h, const T* hidden, int ntok, int B, const int32
                        const int32_t* prior, const int64_t* seq_off, const T* cache, T* out,
                        void* ws, const PrefillLayout& L, const int64_t* kv_off_h) {
   const Dims& d = h->d;
+  const int qw = qw_of(d);
   char* meta = at<char>(ws, L.meta);
   const int32_t* tok_seq = reinterpret_cast<const int32_t*>(meta);
   const int32_t* tok_pos = reinterpret_cast<const int32_t*>(meta + align_up((size_t)ntok * 4));
   const int64_t* kv_off =
       reinterpret_cast<const int64_t*>(meta + 2 * align_up((size_t)ntok * 4));
   const int64_t* seq_off_d = kv_off + align_up((size_t)B * 8) / 8;
+  float* scratch = at<float>(ws, L.scratch);
   T* q_nope = at<T>(ws, L.q_nope);
   T* q_rope = at<T>(ws, L.q_rope);
-  run_q_path<T>(h, hidden, ntok, nullptr, ws, at<float>(ws, L.cq_part), at<T>(ws, L.cq),
-                at<float>(ws, L.q_part), L.ks_qa, L.ks_q, q_nope, q_rope,
-                (int64_t)d.H * d.dr, d.dr, 1.f, tok_pos);
+  mla::Part pq;
+  if (d.dq) {
+    const mla::Part pa = gemm_part<T>(h, hidden, d.D, (const T*)h->w_qa, d.D, ntok, d.dq, d.D,
+                                      at<float>(ws, L.pin));
+    mla::rmsnorm_rows<T>(pa, ntok, d.dq, (const T*)h->q_norm_g, d.eps, at<T>(ws, L.cq),
+                         h->stream);
+    pq = gemm_part<T>(h, at<T>(ws, L.cq), d.dq, (const T*)h->w_qb, d.dq, ntok, qw, d.dq,
+                      at<float>(ws, L.pq));
+  } else {
+    pq = gemm_part<T>(h, hidden, d.D, (const T*)h->w_q, d.D, ntok, qw, d.D, at<float>(ws, L.pin));
+  }
+  mla::q_finish<T>(pq, ntok, tok_pos, q_nope, q_rope, (int64_t)d.H * d.dr, d.dr, 1.f, d, h->rope,
+                   h->stream);
   // expansion of every key row: [K_nope_h | V_h] = W_kvb c_t
   float* kv = at<float>(ws, L.kv);
+  const int wkv = d.H * (d.dn + d.dv);
   for (int b = 0; b < B; ++b) {
     const int rows = prior[b] + (cu_new[b + 1] - cu_new[b]);
     if (rows == 0) continue;
-    gemm_t<T>(h, cache + seq_off[b] * d.R, d.R, 0, (const T*)h->w_kvb, d.dc, 0,
-              kv + kv_off_h[b] * (int64_t)d.H * (d.dn + d.dv), rows, d.H * (d.dn + d.dv), d.dc, 1,
-              1);
+    gemm_out<T>(h, cache + seq_off[b] * d.R, d.R, 0, (const T*)h->w_kvb, d.dc, 0, rows, wkv, d.dc,
+                1, out_f32(kv + kv_off_h[b] * (int64_t)wkv, wkv), scratch);
   }
   T* o = at<T>(ws, L.o);
+  if (h->t_start) HIP_TRY(h, hipEventRecord(h->t_start, h->stream));
   mla::prefill_attn_generic<T>(q_nope, q_rope, kv, cache, tok_seq, tok_pos, kv_off, seq_off_d,
                                ntok, o, d, h->stream);
-  float* y_part = at<float>(ws, L.y_part);
-  gemm_t<T>(h, o, (int64_t)d.H * d.dv, 0, (const T*)h->w_o, (int64_t)d.H * d.dv, 0, y_part, ntok,
-            d.D, d.H * d.dv, 1, L.ks_o);
-  mla::sum_store<T>(y_part, L.ks_o, ntok, d.D, 1, out, d.D, 0, 1.f, h->stream);
+  if (h->t_stop) HIP_TRY(h, hipEventRecord(h->t_stop, h->stream));
+  gemm_out<T>(h, o, (int64_t)d.H * d.dv, 0, (const T*)h->w_o, (int64_t)d.H * d.dv, 0, ntok, d.D,
+              d.H * d.dv, 1, out_t<T>(out, d.D), scratch);
   return check_launch(h, "prefill");
 }
 
@@ -777,7 +917,7 @@ int mla_prefill(mla_handle h, const void* hidden, const int32_t* cu_new, const i
     rows += (int64_t)prior_len[b] + (cu_new[b + 1] - cu_new[b]);
   }
   const int32_t T = cu_new[B];
-  const PrefillLayout L = prefill_layout(h, T, B, rows);
+  const PrefillLayout L = prefill_layout(h, T, B, rows, (int)std::min<int64_t>(rows, INT32_MAX));
   int rc = check_ws(h, ws, ws_bytes, L.total);
   if (rc) return rc;
   DeviceGuard g(h->device);
@@ -802,4 +942,3 @@ int mla_prefill(mla_handle h, const void* hidden, const int32_t* cu_new, const i
   return run_prefill<bf16>(h, (const bf16*)hidden, T, B, cu_new, prior_len, seq_off,
                            (const bf16*)cache, (bf16*)out, ws, L, kv_off.data());
 }
-

@@ -65,9 +65,13 @@ _SIGS = {
     "mla_decode_workspace_bytes": (ctypes.c_size_t, [_P, ctypes.c_int32, ctypes.c_int64]),
     "mla_decode": (ctypes.c_int, [_P, _P, _I32P, _I64P, _I32P, ctypes.c_int32, _P,
                                   ctypes.c_int64, _P, _P, ctypes.c_size_t]),
+    "mla_decode_step_workspace_bytes": (ctypes.c_size_t, [_P, ctypes.c_int32, ctypes.c_int64]),
+    "mla_decode_step": (ctypes.c_int, [_P, _P, _I32P, _I64P, _I32P, ctypes.c_int32, _P,
+                                       ctypes.c_int64, _P, _P, ctypes.c_size_t]),
     "mla_decode_stage_offsets": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.c_int64,
                                                 ctypes.POINTER(ctypes.c_size_t),
                                                 ctypes.POINTER(ctypes.c_size_t)]),
+    "mla_set_timing_events": (ctypes.c_int, [_P, _P, _P]),
     "mla_prefill_workspace_bytes": (ctypes.c_size_t, [_P, ctypes.c_int32, ctypes.c_int32,
                                                       ctypes.c_int64]),
     "mla_prefill": (ctypes.c_int, [_P, _P, _I32P, _I32P, _I64P, ctypes.c_int32, _P,
@@ -180,6 +184,13 @@ class MLALayer:
         except Exception:
             pass
 
+    def set_timing_events(self, start=None, stop=None):
+        """start/stop: torch.cuda.Event(enable_timing=True) already recorded once
+        (so the underlying hipEvent_t exists), or None to stop timing."""
+        sp = ctypes.c_void_p(start.cuda_event) if start is not None else None
+        ep = ctypes.c_void_p(stop.cuda_event) if stop is not None else None
+        self._check(self.lib.mla_set_timing_events(self.h, sp, ep), self.h, "timing events")
+
     # -- A1
     def absorb_weights(self, w: dict):
         """w: dict of device tensors in the layer dtype (keys as synth.make_weights)."""
@@ -239,6 +250,24 @@ class MLALayer:
         q_cat = q_cat.view(self.torch_dtype).reshape(B, d.n_heads, d.row).clone()
         o_lat = o_lat.view(self.torch_dtype).reshape(B, d.n_heads, d.kv_lora).clone()
         return out, q_cat, o_lat
+
+    def decode_step(self, hidden, seq_off, seq_len, cache, out=None):
+        """Append each sequence's new token (row seq_off[b] + seq_len[b] - 1,
+        position seq_len[b] - 1) and decode it, in one call."""
+        import torch
+        self._sync_stream()
+        B = int(hidden.shape[0])
+        sl_a, sl_p = _i32(seq_len)
+        pos_a, pos_p = _i32(sl_a - 1)
+        so_a, so_p = _i64(seq_off)
+        total = int(sl_a.astype(np.int64).sum())
+        if out is None:
+            out = torch.empty((B, self.dims.hidden), dtype=self.torch_dtype, device=self.device)
+        wsp, wsn = self.ws.get(self.lib.mla_decode_step_workspace_bytes(self.h, B, max(total, 1)))
+        rc = self.lib.mla_decode_step(self.h, _ptr(hidden), pos_p, so_p, sl_p, B, _ptr(cache),
+                                      int(cache.shape[0]), _ptr(out), wsp, wsn)
+        self._check(rc, self.h, "mla_decode_step")
+        return out
 
     # -- P1
     def prefill(self, hidden, cu_new, prior_len, seq_off, cache, out=None):

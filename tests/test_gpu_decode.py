@@ -92,3 +92,33 @@ def test_decode_is_deterministic():
     assert bool((y1.view(dtype=y1.dtype) == y2).all())
     import torch
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+def _step_case(dims, lens, std=0.02):
+    """Cache holds only the cached rows; decode_step appends the new token
+    itself and must match the oracle (and the append + decode path)."""
+    import torch
+    from tests.helpers import dev
+    case = DecodeCase(dims, "bf16", std, lens)
+    # wipe each sequence's new-token row, then let decode_step write it
+    last = case.seq_off + case.seq_len - 1
+    ref_rows = case.cache[torch.as_tensor(last, device="cuda")].clone()
+    case.cache[torch.as_tensor(last, device="cuda")] = 0
+    y = case.layer.decode_step(dev(case.x_new, torch.bfloat16), case.seq_off, case.seq_len,
+                               case.cache)
+    rows = case.cache[torch.as_tensor(last, device="cuda")]
+    # same arithmetic up to the split-K summation order of the fused projection
+    assert row_rel_err(host(rows), host(ref_rows)).max() < tol("bf16")
+    y = host(y)
+    for b in range(case.B):
+        y_ref, _ = case.oracle(b)
+        err = row_rel_err(y[b:b + 1], y_ref[None])[0]
+        assert err < tol("bf16"), f"seq {b}: y rel err {err:.3e}"
+
+
+def test_decode_step_v2lite():
+    _step_case(synth.V2_LITE, [0, 1, 16, 63, 300, 1500])
+
+
+def test_decode_step_v3():
+    _step_case(synth.V3, [0, 40, 700])
