@@ -196,6 +196,28 @@ int mla_decode_step(mla_handle h, const void* hidden, const int32_t* pos,
 int mla_decode_stage_offsets(mla_handle h, int32_t B, int64_t total_rows,
                              size_t* q_cat_off, size_t* o_lat_off);
 
+/* Host-only view of the split-S work list mla_decode / mla_decode_step build
+ * ("Multi-Head Latent Attention" post, section 3.6: every cached latent row is
+ * read once per head group; here the rows of the whole batch are spread over
+ * the compute units).  The concatenated rows of the B sequences are cut into
+ * at most max_parts contiguous spans (one persistent workgroup each), each span
+ * split at sequence boundaries into segments; spans are balanced on rows plus
+ * a fixed per-segment cost, and cuts inside a sequence fall on multiples of 16
+ * rows.  The library itself uses max_parts = the device's compute units times
+ * the workgroups of the core kernel that share one.
+ *   seq_len: HOST (B), each >= 1.
+ *   part_begin: HOST out (max_parts + 1): segments of part p are
+ *     [part_begin[p], part_begin[p+1]).
+ *   seg_b, seg_r0, seg_r1: HOST out (B + max_parts - 1 each): segment i covers
+ *     rows [seg_r0[i], seg_r1[i]) of sequence seg_b[i]; segments are in
+ *     row order.
+ *   n_parts, n_segs: HOST out.
+ * No device work.  Errors: INVALID_ARG (null pointer, B or max_parts < 1, a
+ * length < 1). */
+int mla_decode_plan(int32_t B, const int32_t* seq_len, int32_t max_parts, int32_t* part_begin,
+                    int32_t* seg_b, int32_t* seg_r0, int32_t* seg_r1, int32_t* n_parts,
+                    int32_t* n_segs);
+
 /* Workspace bytes mla_prefill needs for T new tokens in B sequences whose
  * caches hold total_key_rows rows in all after the append. */
 size_t mla_prefill_workspace_bytes(mla_handle h, int32_t T, int32_t B,

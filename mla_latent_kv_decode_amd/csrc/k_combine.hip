@@ -1,0 +1,154 @@
+// Split combine for a 512-wide latent (bf16 output).
+//
+// Each split j of sequence b left (m_j, l_j, acc_j) per head, with m_j the
+// reference maximum in log2 units, l_j = sum_t 2^(s_t - m_j) and acc_j the
+// matching unnormalised sum of latent rows.  The pages take one softmax over
+// all cached rows ("Multi-Head Latent Attention" post, section 3.3
+// Absorption); splitting the rows is this library's, and rescaling every split
+// to the common maximum M recovers that softmax exactly:
+//   o_lat = sum_j 2^(m_j - M) acc_j / sum_j 2^(m_j - M) l_j.
+// Splits are summed in slot order, so the result does not depend on timing.
+//
+// Pass 1: one block per (sequence, head, chunk of kCombineChunk slots); its 4
+// waves take every 4th slot of the chunk (all loads issued before the adds)
+// and are summed through LDS in wave order.  A sequence whose slots fit one
+// chunk is finished here; otherwise the chunk's (M, L, acc) goes to a chunk
+// slot.  Pass 2 (only launched if some sequence has several chunks) merges the
+// chunk slots of those sequences the same way.
+#include "kernels.h"
+
+namespace mla {
+namespace cmb {
+
+constexpr int DC = 512;
+constexpr int JC = kCombineChunk;
+constexpr int NW = 4;
+constexpr int PER_WAVE = JC / NW;
+static_assert(JC % NW == 0, "chunk must split evenly over the waves");
+
+__device__ __forceinline__ void store_bf16x8(bf16* dst, const float* r, float inv) {
+  uint4 pk;
+  pk.x = pack_bf16x2(r[0] * inv, r[1] * inv);
+  pk.y = pack_bf16x2(r[2] * inv, r[3] * inv);
+  pk.z = pack_bf16x2(r[4] * inv, r[5] * inv);
+  pk.w = pack_bf16x2(r[6] * inv, r[7] * inv);
+  *reinterpret_cast<uint4*>(dst) = pk;
+}
+
+// lane owns columns 8 lane .. 8 lane + 7
+__global__ void __launch_bounds__(256)
+combine_chunks_512_k(const float* __restrict__ acc, const float* __restrict__ ml, DecodeMeta mt,
+                     int H, float* __restrict__ cacc, float* __restrict__ cml,
+                     bf16* __restrict__ o_lat) {
+  const int b = blockIdx.x, h = blockIdx.y, c = blockIdx.z;
+  const int ns = mt.nseg[b];
+  const int nch = (ns + JC - 1) / JC;
+  if (c >= nch) return;
+  const int j0 = mt.pstart[b] + c * JC;
+  const int nj = min(JC, ns - c * JC);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __shared__ float4 red[NW][64][2];
+  __shared__ float redl[NW];
+
+  float M = -INFINITY;
+  for (int j = 0; j < nj; ++j) M = fmaxf(M, ml[((int64_t)(j0 + j) * H + h) * 2]);
+  float4 v[PER_WAVE][2];
+  float w[PER_WAVE], l[PER_WAVE];
+#pragma unroll
+  for (int u = 0; u < PER_WAVE; ++u) {
+    const int jj = wave + NW * u;
+    const int64_t idx = (int64_t)(j0 + min(jj, nj - 1)) * H + h;
+    const float* p = acc + idx * DC + 8 * lane;
+    v[u][0] = *reinterpret_cast<const float4*>(p);
+    v[u][1] = *reinterpret_cast<const float4*>(p + 4);
+    w[u] = jj < nj ? ml[idx * 2] : -INFINITY;
+    l[u] = ml[idx * 2 + 1];
+  }
+  float r[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float L = 0.f;
+#pragma unroll
+  for (int u = 0; u < PER_WAVE; ++u) {
+    const float s = exp2f(w[u] - M);  // 0 for slots past the chunk
+    L = fmaf(s, l[u], L);
+    r[0] = fmaf(s, v[u][0].x, r[0]); r[1] = fmaf(s, v[u][0].y, r[1]);
+    r[2] = fmaf(s, v[u][0].z, r[2]); r[3] = fmaf(s, v[u][0].w, r[3]);
+    r[4] = fmaf(s, v[u][1].x, r[4]); r[5] = fmaf(s, v[u][1].y, r[5]);
+    r[6] = fmaf(s, v[u][1].z, r[6]); r[7] = fmaf(s, v[u][1].w, r[7]);
+  }
+  red[wave][lane][0] = make_float4(r[0], r[1], r[2], r[3]);
+  red[wave][lane][1] = make_float4(r[4], r[5], r[6], r[7]);
+  if (lane == 0) redl[wave] = L;
+  __syncthreads();
+  if (wave != 0) return;
+  L = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) r[k] = 0.f;
+#pragma unroll
+  for (int u = 0; u < NW; ++u) {
+    const float4 a = red[u][lane][0], e = red[u][lane][1];
+    r[0] += a.x; r[1] += a.y; r[2] += a.z; r[3] += a.w;
+    r[4] += e.x; r[5] += e.y; r[6] += e.z; r[7] += e.w;
+    L += redl[u];
+  }
+  if (nch == 1) {
+    store_bf16x8(o_lat + ((int64_t)b * H + h) * DC + 8 * lane, r, 1.f / L);
+    return;
+  }
+  const int64_t k = (int64_t)(mt.cstart[b] + c) * H + h;
+  float* q = cacc + k * DC + 8 * lane;
+  *reinterpret_cast<float4*>(q) = make_float4(r[0], r[1], r[2], r[3]);
+  *reinterpret_cast<float4*>(q + 4) = make_float4(r[4], r[5], r[6], r[7]);
+  if (lane == 0) {
+    cml[k * 2] = M;
+    cml[k * 2 + 1] = L;
+  }
+}
+
+// one wave per (sequence, head) with several chunks; lane owns 8 columns
+__global__ void __launch_bounds__(64)
+combine_final_512_k(const float* __restrict__ cacc, const float* __restrict__ cml, DecodeMeta mt,
+                    int H, bf16* __restrict__ o_lat) {
+  const int b = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+  const int nch = (mt.nseg[b] + JC - 1) / JC;
+  if (nch <= 1) return;
+  const int k0 = mt.cstart[b];
+  float M = -INFINITY;
+  for (int k = 0; k < nch; ++k) M = fmaxf(M, cml[((int64_t)(k0 + k) * H + h) * 2]);
+  float r[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float L = 0.f;
+  for (int k = 0; k < nch; k += 4) {
+    float4 v[4][2];
+    float w[4], l[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t idx = (int64_t)(k0 + min(k + u, nch - 1)) * H + h;
+      const float* p = cacc + idx * DC + 8 * lane;
+      v[u][0] = *reinterpret_cast<const float4*>(p);
+      v[u][1] = *reinterpret_cast<const float4*>(p + 4);
+      w[u] = k + u < nch ? cml[idx * 2] : -INFINITY;
+      l[u] = cml[idx * 2 + 1];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float s = exp2f(w[u] - M);
+      L = fmaf(s, l[u], L);
+      r[0] = fmaf(s, v[u][0].x, r[0]); r[1] = fmaf(s, v[u][0].y, r[1]);
+      r[2] = fmaf(s, v[u][0].z, r[2]); r[3] = fmaf(s, v[u][0].w, r[3]);
+      r[4] = fmaf(s, v[u][1].x, r[4]); r[5] = fmaf(s, v[u][1].y, r[5]);
+      r[6] = fmaf(s, v[u][1].z, r[6]); r[7] = fmaf(s, v[u][1].w, r[7]);
+    }
+  }
+  store_bf16x8(o_lat + ((int64_t)b * H + h) * DC + 8 * lane, r, 1.f / L);
+}
+
+}  // namespace cmb
+
+void decode_combine_512(const float* acc, const float* ml, const DecodeMeta& m, int B, int H,
+                        int max_chunks, float* cacc, float* cml, bf16* o_lat, hipStream_t st) {
+  cmb::combine_chunks_512_k<<<dim3(B, H, max_chunks), 256, 0, st>>>(acc, ml, m, H, cacc, cml,
+                                                                      o_lat);
+  if (max_chunks > 1)
+    cmb::combine_final_512_k<<<dim3(B, H), 64, 0, st>>>(cacc, cml, m, H, o_lat);
+}
+
+}  // namespace mla

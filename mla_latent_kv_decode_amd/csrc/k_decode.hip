@@ -9,13 +9,13 @@
 //
 // Work decomposition: the host cuts the concatenated rows of all sequences
 // into `parts` equal spans (one persistent workgroup each) and splits spans at
-// sequence boundaries into segments.  Inside a workgroup the 4 waves take
+// sequence boundaries into segments.  Inside a workgroup the waves take
 // 16-row sub-tiles of the segment round-robin, each with its own online
 // softmax state and a private double-buffered LDS stage filled by
 // global_load_lds_dwordx4 (no VGPRs held by loads in flight).  At the end of a
-// segment the 4 wave states are merged through LDS and one partial
-// (max, sum, unnormalised acc) is written; a separate combine kernel merges
-// the partials of each sequence in a fixed order.
+// segment the wave states are merged through LDS and one partial
+// (max, sum, unnormalised acc) is written; the combine kernels merge the
+// partials of each sequence in a fixed order.
 //
 // Per 16-row sub-tile and wave:
 //   S^T (16 rows x 16 heads) = K (16 x 576) . Q^T   -- 18 x mfma 16x16x32,
@@ -41,10 +41,17 @@ constexpr int RW = 576;                      // row width in elements
 constexpr int SUB = 16;                      // rows per sub-tile
 constexpr int SUB_BYTES = SUB * RW * 2;      // 18432
 constexpr int LOADS = SUB + 2;               // 18 wave-wide 16-byte loads per sub-tile
-constexpr int NWAVE = 4;
+#ifndef MLA_DEC_NWAVE
+#define MLA_DEC_NWAVE 4
+#endif
+constexpr int NWAVE = MLA_DEC_NWAVE;         // waves per workgroup
+constexpr int NTHR = 64 * NWAVE;
 constexpr int NSTAGE = 2;
 constexpr float kRescale = 8.0f;             // lazy-rescale threshold, log2 units
-constexpr int LDS_BYTES = NWAVE * NSTAGE * SUB_BYTES;  // 147456
+constexpr int LDS_BYTES = NWAVE * NSTAGE * SUB_BYTES;  // 36 KB per wave
+// merge mapping: TPH threads per head, CPT latent columns per thread
+constexpr int TPH = NTHR / 16;
+constexpr int CPT = DC / TPH;
 static_assert(NWAVE * 16 * DC * 4 + NWAVE * 16 * 2 * 4 <= LDS_BYTES, "merge space");
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
@@ -99,7 +106,7 @@ __device__ __forceinline__ uint32_t lds_u32(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-__global__ void __launch_bounds__(256, 1)
+__global__ void __launch_bounds__(NTHR, 1)
 decode_core_mfma_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cache, DecodeMeta mt,
                    float* __restrict__ acc_out, float* __restrict__ ml_out, int H) {
   __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
@@ -140,7 +147,7 @@ decode_core_mfma_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
     const int nsub = (n + SUB - 1) / SUB;
     const bf16* rows = cache + (mt.seq_off[sg.b] + sg.r0) * (int64_t)RW;
 
-    // this wave's sub-tiles: wave, wave + 4, ...
+    // this wave's sub-tiles: wave, wave + NWAVE, ...
     const int my_n = wave < nsub ? (nsub - 1 - wave) / NWAVE + 1 : 0;
     if (my_n > 0) issue_subtile(rows, wave * SUB, n, my_addr, lane);
     if (my_n > 1) issue_subtile(rows, (wave + NWAVE) * SUB, n, my_addr + SUB_BYTES, lane);
@@ -249,7 +256,7 @@ decode_core_mfma_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
       }
     }
 
-    // ---- merge the 4 wave states through LDS (staging buffers are free now)
+    // ---- merge the NWAVE wave states through LDS (staging buffers are free now)
     __syncthreads();
     float* om = reinterpret_cast<float*>(lds);             // [wave][16 heads][512]
     float* mlm = om + NWAVE * 16 * DC;                      // [wave][16][2]
@@ -268,11 +275,11 @@ decode_core_mfma_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
       }
     }
     __syncthreads();
-    // thread t: head t / 16, columns (t % 16) * 32 .. + 31
-    const int h = threadIdx.x >> 4;
-    const int c0 = (threadIdx.x & 15) * 32;
+    // thread t: head t / TPH, columns (t % TPH) * CPT .. + CPT - 1
+    const int h = threadIdx.x / TPH;
+    const int c0 = (threadIdx.x % TPH) * CPT;
     const int gh = hg * 16 + h;  // global head index
-    float r[32];
+    float r[CPT];
     float M = -INFINITY, L = 0.f;
     {
       float mw[NWAVE], sc[NWAVE];
@@ -287,7 +294,7 @@ decode_core_mfma_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
         L += sc[w] * mlm[(w * 16 + h) * 2 + 1];
       }
 #pragma unroll
-      for (int c = 0; c < 32; c += 4) {
+      for (int c = 0; c < CPT; c += 4) {
         float4 acc4 = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
         for (int w = 0; w < NWAVE; ++w) {
@@ -302,9 +309,9 @@ decode_core_mfma_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
     }
     float* pacc = acc_out + ((int64_t)sg.pidx * H + gh) * DC + c0;
 #pragma unroll
-    for (int c = 0; c < 32; c += 4)
+    for (int c = 0; c < CPT; c += 4)
       *reinterpret_cast<float4*>(pacc + c) = make_float4(r[c], r[c + 1], r[c + 2], r[c + 3]);
-    if ((threadIdx.x & 15) == 0) {
+    if (threadIdx.x % TPH == 0) {
       ml_out[((int64_t)sg.pidx * H + gh) * 2] = M;
       ml_out[((int64_t)sg.pidx * H + gh) * 2 + 1] = L;
     }
@@ -312,65 +319,15 @@ decode_core_mfma_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
   }
 }
 
-// Split combine for a 512-wide latent: block = (sequence b, 4 heads); thread t
-// owns head 4*blockIdx.y + t/64, columns 8*(t%64) .. +7.
-//   o_lat = sum_j e^(m_j - M) acc_j / sum_j e^(m_j - M) l_j,
-// summed in slot order j (deterministic); partial loads are issued 4 slots at
-// a time before any add.
-__global__ void __launch_bounds__(256)
-decode_combine_512_k(const float* __restrict__ acc, const float* __restrict__ ml, DecodeMeta mt,
-                     int H, bf16* __restrict__ o_lat) {
-  const int b = blockIdx.x;
-  const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
-  const int c = (threadIdx.x & 63) * 8;
-  const int j0 = mt.pstart[b], nj = mt.nseg[b];
-  float M = -INFINITY;
-  for (int j = 0; j < nj; ++j) M = fmaxf(M, ml[((int64_t)(j0 + j) * H + h) * 2]);
-  float L = 0.f;
-  float r[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < nj; j += 4) {
-    float4 v[4][2];
-    float w[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int jj = min(j + u, nj - 1);
-      const int64_t idx = (int64_t)(j0 + jj) * H + h;
-      const float* p = acc + idx * DC + c;
-      v[u][0] = *reinterpret_cast<const float4*>(p);
-      v[u][1] = *reinterpret_cast<const float4*>(p + 4);
-      w[u] = (j + u < nj) ? exp2f(ml[idx * 2] - M) : 0.f;
-      L = fmaf(w[u], (j + u < nj) ? ml[idx * 2 + 1] : 0.f, L);
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      r[0] = fmaf(w[u], v[u][0].x, r[0]); r[1] = fmaf(w[u], v[u][0].y, r[1]);
-      r[2] = fmaf(w[u], v[u][0].z, r[2]); r[3] = fmaf(w[u], v[u][0].w, r[3]);
-      r[4] = fmaf(w[u], v[u][1].x, r[4]); r[5] = fmaf(w[u], v[u][1].y, r[5]);
-      r[6] = fmaf(w[u], v[u][1].z, r[6]); r[7] = fmaf(w[u], v[u][1].w, r[7]);
-    }
-  }
-  const float inv = 1.f / L;
-  uint4 pk;
-  pk.x = pack_bf16x2(r[0] * inv, r[1] * inv);
-  pk.y = pack_bf16x2(r[2] * inv, r[3] * inv);
-  pk.z = pack_bf16x2(r[4] * inv, r[5] * inv);
-  pk.w = pack_bf16x2(r[6] * inv, r[7] * inv);
-  *reinterpret_cast<uint4*>(o_lat + ((int64_t)b * H + h) * DC + c) = pk;
-}
-
 }  // namespace dec
 
-void decode_combine_512(const float* acc, const float* ml, const DecodeMeta& m, int B, int H,
-                        bf16* o_lat, hipStream_t st) {
-  dim3 grid(B, H / 4);
-  dec::decode_combine_512_k<<<grid, 256, 0, st>>>(acc, ml, m, H, o_lat);
-}
+int decode_core_wg_per_cu() { return dec::NWAVE >= 4 ? 1 : 4 / dec::NWAVE; }
 
 void decode_core_mfma(const bf16* q_cat, const bf16* cache, const DecodeMeta& m, int parts,
                       int B, float* acc, float* ml, const Dims& d, hipStream_t st) {
   (void)B;
   dim3 grid(parts, d.H / 16);
-  dec::decode_core_mfma_k<<<grid, 256, 0, st>>>(q_cat, cache, m, acc, ml, d.H);
+  dec::decode_core_mfma_k<<<grid, dec::NTHR, 0, st>>>(q_cat, cache, m, acc, ml, d.H);
 }
 
 }  // namespace mla

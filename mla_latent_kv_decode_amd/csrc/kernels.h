@@ -38,7 +38,12 @@ struct DecodeMeta {
   const int32_t* nseg;      // (B) number of partial slots of sequence b
   const DecodeSeg* segs;    // (nseg_total)
   const int32_t* part_begin;  // (parts + 1) segment range of each persistent part
+  const int32_t* cstart;    // (B) first chunk slot of sequence b (two-stage combine)
 };
+
+// The 512-wide combine merges the partials of a sequence in chunks of
+// kCombineChunk slots; a sequence with more than one chunk gets a second pass.
+constexpr int kCombineChunk = 16;
 
 // ---- GEMM: Cpart[z][bt][m][n] = sum_{k in split z} A[bt][m][k] * W[bt][n][k]
 // A row m of batch bt at A + bt*sA + m*lda; W row n at W + bt*sW + n*ldw.
@@ -113,9 +118,13 @@ void decode_core_generic(const T* q_cat, const T* cache, const DecodeMeta& m, in
 // MFMA version: bf16, dc == 512, dr == 64, H % 16 == 0.  parts = persistent groups.
 void decode_core_mfma(const bf16* q_cat, const bf16* cache, const DecodeMeta& m, int parts,
                       int B, float* acc, float* ml, const Dims& d, hipStream_t st);
-// combine for dc == 512, bf16 output: all partial loads of a thread in flight at once
+// persistent workgroups of the MFMA core that share one compute unit
+int decode_core_wg_per_cu();
+// combine for dc == 512, bf16 output.  max_chunks = max over sequences of
+// ceil(nseg / kCombineChunk); cacc (chunk slots x H x 512) and cml (chunk slots
+// x H x 2) hold the chunk partials of sequences with more than one chunk.
 void decode_combine_512(const float* acc, const float* ml, const DecodeMeta& m, int B, int H,
-                        bf16* o_lat, hipStream_t st);
+                        int max_chunks, float* cacc, float* cml, bf16* o_lat, hipStream_t st);
 template <typename T>
 void decode_combine(const float* acc, const float* ml, const DecodeMeta& m, int B, T* o_lat,
                     const Dims& d, hipStream_t st);

@@ -20,6 +20,11 @@
 #include "mla.h"
 #include "kernels.h"
 
+// rows-equivalent cost of a segment start in the split-S work list
+#ifndef MLA_SEG_ROWS
+#define MLA_SEG_ROWS 320
+#endif
+
 using mla::bf16;
 using mla::DecodeMeta;
 using mla::DecodeSeg;
@@ -232,19 +237,21 @@ mla::GemmOut out_t(T* p, int64_t ldo, int64_t so = 0, float alpha = 1.f) {
 struct DecodeLayout {
   int max_segs = 0;
   bool step = false;  // fused append (mla_decode_step)
-  size_t meta, scratch, pin, pq, cq, q_nope, q_cat, acc, ml, o_lat, o;
+  int max_cslots = 0;  // chunk slots of the two-pass combine
+  size_t meta, scratch, pin, pq, cq, q_nope, q_cat, acc, ml, cacc, cml, o_lat, o;
   size_t total = 0;
 };
 
 int max_parts(const mla_ctx* h, int64_t total_rows) {
   int64_t p = (total_rows + 63) / 64;
-  if (p > h->n_cu) p = h->n_cu;
+  const int64_t wgs = (int64_t)h->n_cu * (h->mfma ? mla::decode_core_wg_per_cu() : 1);
+  if (p > wgs) p = wgs;
   if (p < 1) p = 1;
   return (int)p;
 }
 
 size_t meta_bytes(int B, int parts, int max_segs) {
-  return 2 * align_up((size_t)B * 8) + 4 * align_up((size_t)B * 4) +
+  return 2 * align_up((size_t)B * 8) + 5 * align_up((size_t)B * 4) +
          align_up((size_t)(parts + 1) * 4) + align_up((size_t)max_segs * sizeof(DecodeSeg));
 }
 
@@ -256,6 +263,10 @@ DecodeLayout decode_layout(const mla_ctx* h, int B, int64_t total_rows, bool ste
   L.step = step;
   const int parts = max_parts(h, total_rows);
   L.max_segs = parts + B;
+  // only sequences with more than kCombineChunk slots use chunk slots: there are
+  // at most max_segs / (kCombineChunk + 1) of them, each with at most
+  // nseg / kCombineChunk + 1 chunks
+  L.max_cslots = 2 * (L.max_segs / mla::kCombineChunk) + 2;
   const int qw = qw_of(d);
   const size_t scr = std::max({out_scratch(h, B, d.dc, d.dn, d.H),
                                out_scratch(h, B, d.dv, d.dc, d.H),
@@ -276,6 +287,8 @@ DecodeLayout decode_layout(const mla_ctx* h, int B, int64_t total_rows, bool ste
   L.q_cat = c.take((size_t)B * d.H * d.R * e);
   L.acc = c.take((size_t)L.max_segs * d.H * d.dc * 4);
   L.ml = c.take((size_t)L.max_segs * d.H * 2 * 4);
+  L.cacc = c.take((size_t)L.max_cslots * d.H * d.dc * 4);
+  L.cml = c.take((size_t)L.max_cslots * d.H * 2 * 4);
   L.o_lat = c.take((size_t)B * d.H * d.dc * e);
   L.o = c.take((size_t)B * d.H * d.dv * e);
   L.total = c.off;
@@ -283,37 +296,95 @@ DecodeLayout decode_layout(const mla_ctx* h, int B, int64_t total_rows, bool ste
 }
 
 struct MetaOffsets {
-  size_t seq_off, seq_len, pos, pstart, nseg, part, segs, slot;
+  size_t seq_off, seq_len, pos, pstart, nseg, cstart, part, segs, slot;
 };
 
-// Host-side work list: equal spans of the concatenated rows, cut at sequence
-// boundaries.  Returns parts and fills the packed metadata blob.
+// Host-side work list.  The concatenated rows of all sequences are cut into
+// at most `max_parts(total)` contiguous spans, one persistent workgroup each,
+// and every span is split at sequence boundaries into segments.  A segment
+// start costs its workgroup about kSegRows rows' worth of time (pipeline
+// restart, query load, wave merge and partial write), so spans are balanced
+// on rows + kSegRows * segments: the smallest per-part budget for which a
+// greedy left-to-right fill needs no more than the available parts is found by
+// bisection.  Cuts inside a sequence fall on 16-row sub-tile boundaries.
+constexpr int64_t kSegRows = MLA_SEG_ROWS;
+constexpr int64_t kCutAlign = 16;
+
+struct SpanPlan {
+  std::vector<DecodeSeg> segs;
+  std::vector<int32_t> part_begin;
+};
+
+// Greedy fill with per-part budget `budget`; returns the parts used.
+int fill_spans(int B, const int32_t* seq_len, int64_t budget, SpanPlan* plan) {
+  if (plan) {
+    plan->segs.clear();
+    plan->part_begin.assign(1, 0);
+  }
+  int used = 0;
+  int64_t cost = 0;  // cost of the open part; 0 = no part open
+  for (int b = 0; b < B; ++b) {
+    int32_t in_b = 0;
+    while (in_b < seq_len[b]) {
+      const int64_t rem = seq_len[b] - in_b;
+      int64_t room = budget - cost - kSegRows;
+      if (cost > 0 && room < std::min<int64_t>(rem, kCutAlign)) {
+        if (plan) plan->part_begin.push_back((int32_t)plan->segs.size());
+        cost = 0;  // close the part, open a new one below
+        continue;
+      }
+      if (cost == 0) ++used;
+      int64_t take = rem;
+      if (take > room) take = std::max<int64_t>(kCutAlign, room / kCutAlign * kCutAlign);
+      if (take > rem) take = rem;
+      if (plan)
+        plan->segs.push_back(
+            DecodeSeg{b, in_b, (int32_t)(in_b + take), (int32_t)plan->segs.size()});
+      cost += kSegRows + take;
+      in_b += (int32_t)take;
+    }
+  }
+  if (plan && cost > 0) plan->part_begin.push_back((int32_t)plan->segs.size());
+  return used;
+}
+
+// Balanced plan over at most max_p parts; returns the parts used.
+int plan_spans(int B, const int32_t* seq_len, int max_p, SpanPlan* plan) {
+  int64_t total = 0;
+  for (int b = 0; b < B; ++b) total += seq_len[b];
+  int64_t lo = (total + max_p - 1) / max_p, hi = lo + kSegRows * 2 + kCutAlign;
+  while (fill_spans(B, seq_len, hi, nullptr) > max_p) hi *= 2;
+  while (lo < hi) {  // smallest budget that fits
+    const int64_t mid = lo + (hi - lo) / 2;
+    if (fill_spans(B, seq_len, mid, nullptr) <= max_p) hi = mid;
+    else lo = mid + 1;
+  }
+  return fill_spans(B, seq_len, hi, plan);
+}
+
 int build_decode_meta(const mla_ctx* h, int B, const int64_t* seq_off, const int32_t* seq_len,
                       const int32_t* pos, int64_t total, bool with_slot, std::vector<char>& blob,
-                      MetaOffsets* mo, int* nseg_total) {
-  int parts = max_parts(h, total);
-  const int64_t per = (total + parts - 1) / parts;
-  parts = (int)((total + per - 1) / per);
-  std::vector<DecodeSeg> segs;
-  std::vector<int32_t> part_begin(1, 0), pstart(B, 0), nseg(B, 0);
-  int b = 0;
-  int32_t in_b = 0;
-  int64_t cur = 0;
-  for (int p = 0; p < parts; ++p) {
-    const int64_t hi = std::min(total, (int64_t)(p + 1) * per);
-    while (cur < hi) {
-      const int32_t take = (int32_t)std::min<int64_t>(hi - cur, (int64_t)seq_len[b] - in_b);
-      if (in_b == 0) pstart[b] = (int32_t)segs.size();
-      segs.push_back(DecodeSeg{b, in_b, in_b + take, (int32_t)segs.size()});
-      nseg[b]++;
-      cur += take;
-      in_b += take;
-      if (in_b == seq_len[b]) {
-        ++b;
-        in_b = 0;
-      }
+                      MetaOffsets* mo, int* nseg_total, int* max_chunks, int* cslots) {
+  SpanPlan plan;
+  const int parts = plan_spans(B, seq_len, max_parts(h, total), &plan);
+  std::vector<DecodeSeg>& segs = plan.segs;
+  std::vector<int32_t>& part_begin = plan.part_begin;
+  std::vector<int32_t> pstart(B, 0), nseg(B, 0);
+  for (const DecodeSeg& sg : segs) {
+    if (sg.r0 == 0) pstart[sg.b] = sg.pidx;
+    nseg[sg.b]++;
+  }
+  // chunk slots of the combine's second pass, for sequences with several chunks
+  std::vector<int32_t> cstart(B, 0);
+  *max_chunks = 1;
+  *cslots = 0;
+  for (int b = 0; b < B; ++b) {
+    const int nch = (nseg[b] + mla::kCombineChunk - 1) / mla::kCombineChunk;
+    *max_chunks = std::max(*max_chunks, nch);
+    if (nch > 1) {
+      cstart[b] = *cslots;
+      *cslots += nch;
     }
-    part_begin.push_back((int32_t)segs.size());
   }
   Carve c;
   mo->seq_off = c.take((size_t)B * 8);
@@ -322,6 +393,7 @@ int build_decode_meta(const mla_ctx* h, int B, const int64_t* seq_off, const int
   mo->pos = c.take((size_t)B * 4);
   mo->pstart = c.take((size_t)B * 4);
   mo->nseg = c.take((size_t)B * 4);
+  mo->cstart = c.take((size_t)B * 4);
   mo->part = c.take((size_t)(parts + 1) * 4);
   mo->segs = c.take(segs.size() * sizeof(DecodeSeg));
   blob.assign(c.off, 0);
@@ -334,6 +406,7 @@ int build_decode_meta(const mla_ctx* h, int B, const int64_t* seq_off, const int
   memcpy(blob.data() + mo->pos, pos, (size_t)B * 4);
   memcpy(blob.data() + mo->pstart, pstart.data(), (size_t)B * 4);
   memcpy(blob.data() + mo->nseg, nseg.data(), (size_t)B * 4);
+  memcpy(blob.data() + mo->cstart, cstart.data(), (size_t)B * 4);
   memcpy(blob.data() + mo->part, part_begin.data(), part_begin.size() * 4);
   memcpy(blob.data() + mo->segs, segs.data(), segs.size() * sizeof(DecodeSeg));
   *nseg_total = (int)segs.size();
@@ -670,6 +743,27 @@ size_t mla_decode_step_workspace_bytes(mla_handle h, int32_t B, int64_t total_ro
   return decode_layout(h, B, total_rows, true).total;
 }
 
+int mla_decode_plan(int32_t B, const int32_t* seq_len, int32_t max_parts, int32_t* part_begin,
+                    int32_t* seg_b, int32_t* seg_r0, int32_t* seg_r1, int32_t* n_parts,
+                    int32_t* n_segs) {
+  if (B <= 0 || max_parts <= 0 || !seq_len || !part_begin || !seg_b || !seg_r0 || !seg_r1 ||
+      !n_parts || !n_segs)
+    return MLA_ERR_INVALID_ARG;
+  for (int b = 0; b < B; ++b)
+    if (seq_len[b] < 1) return MLA_ERR_INVALID_ARG;
+  SpanPlan plan;
+  const int parts = plan_spans(B, seq_len, max_parts, &plan);
+  for (int p = 0; p <= parts; ++p) part_begin[p] = plan.part_begin[p];
+  for (size_t i = 0; i < plan.segs.size(); ++i) {
+    seg_b[i] = plan.segs[i].b;
+    seg_r0[i] = plan.segs[i].r0;
+    seg_r1[i] = plan.segs[i].r1;
+  }
+  *n_parts = parts;
+  *n_segs = (int32_t)plan.segs.size();
+  return MLA_OK;
+}
+
 int mla_decode_stage_offsets(mla_handle h, int32_t B, int64_t total_rows, size_t* q_cat_off,
                              size_t* o_lat_off) {
   if (!h || B <= 0 || total_rows <= 0 || !q_cat_off || !o_lat_off) return MLA_ERR_INVALID_ARG;
@@ -722,7 +816,7 @@ static void run_q_and_append(mla_ctx* h, const T* x, int B, void* ws, const Deco
 template <typename T>
 static int run_decode(mla_ctx* h, const T* hidden, int B, T* cache, T* out, void* ws,
                       const DecodeLayout& L, const DecodeMeta& mt, int parts, int nseg_total,
-                      const int64_t* slot_dev) {
+                      int max_chunks, const int64_t* slot_dev) {
   const Dims& d = h->d;
   float* scratch = at<float>(ws, L.scratch);
   T* q_nope = at<T>(ws, L.q_nope);
@@ -748,7 +842,9 @@ static int run_decode(mla_ctx* h, const T* hidden, int B, T* cache, T* out, void
   if (h->t_stop) HIP_TRY(h, hipEventRecord(h->t_stop, h->stream));
   // A6: combine the partials of each sequence (fixed slot order)
   if constexpr (sizeof(T) == 2) {
-    if (mfma_core) mla::decode_combine_512(acc, ml, mt, B, d.H, (bf16*)o_lat, h->stream);
+    if (mfma_core)
+      mla::decode_combine_512(acc, ml, mt, B, d.H, max_chunks, at<float>(ws, L.cacc),
+                              at<float>(ws, L.cml), (bf16*)o_lat, h->stream);
   }
   if (!mfma_core) mla::decode_combine<T>(acc, ml, mt, B, o_lat, d, h->stream);
   // A7: o_h = W_UV_h o_lat_h
@@ -779,9 +875,11 @@ static int decode_common(mla_handle h, const void* hidden, const int32_t* pos,
   if (!g.ok) return fail(h, MLA_ERR_HIP, "cannot select device %d", h->device);
   std::vector<char> blob;
   MetaOffsets mo;
-  int nseg_total = 0;
-  const int parts =
-      build_decode_meta(h, B, seq_off, seq_len, pos, total, step, blob, &mo, &nseg_total);
+  int nseg_total = 0, max_chunks = 1, cslots = 0;
+  const int parts = build_decode_meta(h, B, seq_off, seq_len, pos, total, step, blob, &mo,
+                                      &nseg_total, &max_chunks, &cslots);
+  if (cslots > L.max_cslots)
+    return fail(h, MLA_ERR_WORKSPACE, "internal: combine chunk slots larger than planned");
   if (blob.size() > meta_bytes(B, max_parts(h, total), L.max_segs))
     return fail(h, MLA_ERR_WORKSPACE, "internal: decode metadata larger than planned");
   void* meta = at<char>(ws, L.meta);
@@ -792,14 +890,15 @@ static int decode_common(mla_handle h, const void* hidden, const int32_t* pos,
   mt.pos = at<int32_t>(meta, mo.pos);
   mt.pstart = at<int32_t>(meta, mo.pstart);
   mt.nseg = at<int32_t>(meta, mo.nseg);
+  mt.cstart = at<int32_t>(meta, mo.cstart);
   mt.part_begin = at<int32_t>(meta, mo.part);
   mt.segs = at<DecodeSeg>(meta, mo.segs);
   const int64_t* slot_dev = step ? at<int64_t>(meta, mo.slot) : nullptr;
   if (is_f32(h))
     return run_decode<float>(h, (const float*)hidden, B, (float*)cache, (float*)out, ws, L, mt,
-                             parts, nseg_total, slot_dev);
+                             parts, nseg_total, max_chunks, slot_dev);
   return run_decode<bf16>(h, (const bf16*)hidden, B, (bf16*)cache, (bf16*)out, ws, L, mt, parts,
-                          nseg_total, slot_dev);
+                          nseg_total, max_chunks, slot_dev);
 }
 
 int mla_decode(mla_handle h, const void* hidden, const int32_t* pos, const int64_t* seq_off,

@@ -71,6 +71,8 @@ _SIGS = {
     "mla_decode_stage_offsets": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.c_int64,
                                                 ctypes.POINTER(ctypes.c_size_t),
                                                 ctypes.POINTER(ctypes.c_size_t)]),
+    "mla_decode_plan": (ctypes.c_int, [ctypes.c_int32, _I32P, ctypes.c_int32, _I32P, _I32P,
+                                       _I32P, _I32P, _I32P, _I32P]),
     "mla_set_timing_events": (ctypes.c_int, [_P, _P, _P]),
     "mla_prefill_workspace_bytes": (ctypes.c_size_t, [_P, ctypes.c_int32, ctypes.c_int32,
                                                       ctypes.c_int64]),
@@ -286,6 +288,25 @@ class MLALayer:
                                   int(cache.shape[0]), _ptr(out), wsp, wsn)
         self._check(rc, self.h, "mla_prefill")
         return out
+
+
+def decode_plan(seq_len, max_parts: int):
+    """The split-S work list for these lengths (host only): returns
+    (part_begin, seg_b, seg_r0, seg_r1) as int32 arrays."""
+    lib = load()
+    sl, slp = _i32(seq_len)
+    B = len(sl)
+    nseg_max = B + max_parts - 1
+    pb = np.zeros(max_parts + 1, np.int32)
+    sb, r0, r1 = (np.zeros(nseg_max, np.int32) for _ in range(3))
+    npart, nseg = ctypes.c_int32(), ctypes.c_int32()
+    st = lib.mla_decode_plan(B, slp, max_parts, pb.ctypes.data_as(_I32P),
+                             sb.ctypes.data_as(_I32P), r0.ctypes.data_as(_I32P),
+                             r1.ctypes.data_as(_I32P), ctypes.byref(npart), ctypes.byref(nseg))
+    if st != 0:
+        raise MLAError(st, lib.mla_status_string(st).decode())
+    p, n = npart.value, nseg.value
+    return pb[:p + 1].copy(), sb[:n].copy(), r0[:n].copy(), r1[:n].copy()
 
 
 def header_functions(header: str = None) -> list:

@@ -145,3 +145,52 @@ def test_product_path_has_no_oracle_dependency():
             L.load(os.path.join(os.path.dirname(L._PKG), "no_such_lib.so"))
     finally:
         L._lib = old
+
+
+def _plan_invariants(lens, max_parts):
+    from mla_latent_kv_decode_amd import lib
+    pb, sb, r0, r1 = lib.decode_plan(lens, max_parts)
+    P = len(pb) - 1
+    assert 1 <= P <= max_parts
+    assert pb[0] == 0 and pb[-1] == len(sb) and np.all(np.diff(pb) >= 1)
+    assert len(sb) <= len(lens) + max_parts - 1
+    # segments in row order cover every row of every sequence exactly once
+    nxt = np.zeros(len(lens), np.int64)
+    for b, a, e in zip(sb, r0, r1):
+        assert a == nxt[b] and a < e <= lens[b]
+        assert b == 0 or nxt[b - 1] == lens[b - 1]
+        if e < lens[b]:
+            assert e % 16 == 0, "cuts inside a sequence fall on sub-tile boundaries"
+        nxt[b] = e
+    assert np.array_equal(nxt, lens)
+    rows = np.array([(r1[pb[p]:pb[p + 1]] - r0[pb[p]:pb[p + 1]]).sum() for p in range(P)])
+    return rows, np.diff(pb)
+
+
+def test_decode_plan_covers_rows_once():
+    """Host work list of the split-S core: random ragged batches."""
+    rng = np.random.default_rng(7)
+    for _ in range(400):
+        B = int(rng.integers(1, 80))
+        lens = rng.integers(1, int(rng.choice([3, 40, 3000, 40000])), B)
+        _plan_invariants(lens, int(rng.integers(1, 600)))
+
+
+def test_decode_plan_balances_cost():
+    """The 64-sequence ragged batch over 256 parts: every part's rows plus its
+    per-segment charge is within a sub-tile plus one charge of the mean."""
+    from mla_latent_kv_decode_amd import synth
+    lens = synth.lengths(synth.WORKLOADS["v2lite_decode_b64"]) + 1
+    rows, segs = _plan_invariants(lens, 256)
+    assert len(rows) == 256
+    seg_rows = 320  # the library's per-segment charge
+    cost = rows + seg_rows * segs
+    assert cost.max() - cost.mean() < 16 + seg_rows
+
+
+def test_decode_plan_errors():
+    from mla_latent_kv_decode_amd import lib
+    with pytest.raises(lib.MLAError):
+        lib.decode_plan([5, 0, 3], 8)
+    with pytest.raises(lib.MLAError):
+        lib.decode_plan([5], 0)

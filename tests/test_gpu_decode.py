@@ -64,6 +64,14 @@ def test_v2lite_decode_b1_s4096():
     _check(case, [0])
 
 
+def test_v2lite_long_and_short_mixed():
+    """One long sequence split over many workgroups (its partials need the
+    combine's second pass) next to short ones finished in the first pass."""
+    lens = [3000, 5, 40, 1, 700]
+    case = DecodeCase(synth.V2_LITE, "bf16", 0.02, lens)
+    _check(case, range(len(lens)))
+
+
 def test_v2lite_decode_b64_full_size_sampled():
     """The full B=64 ragged batch (lengths ~ U{512..8192}), in the launch
     configuration the benchmark times; outputs of the shortest, the longest and
