@@ -12,7 +12,8 @@ alternately so consecutive steps do not find the previous step's cache in the
 (one replay = K steps).  Events recorded inside a captured graph do not time
 the kernels between them, so right after the timed replay the same K steps are
 run eagerly with HIP events that the library records on its own stream around
-every split-S core launch; their mean is the core kernel's duration.
+every split-S core launch (created without the system-scope fence, so they do
+not flush caches); their mean is the core kernel's duration.
 
 Prints ONE JSON line.  Default workload: V2-Lite shapes, B = 64 sequences with
 cached lengths ~ U{512..8192} (``v2lite_decode_b64``).
@@ -179,12 +180,6 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(K)]
-    for a, b_ in ev:  # materialise the hipEvent_t handles
-        a.record()
-        b_.record()
-    torch.cuda.synchronize()
 
     graph = None
     if not args.eager:
@@ -200,10 +195,12 @@ def main():
         torch.cuda.synchronize()
 
     def eager_steps_with_core_events():
+        layer.core_timing(K)
         for i in range(K):
-            layer.set_timing_events(*ev[i])
             step(i)
-        layer.set_timing_events()
+        core = layer.core_timing_read(K)
+        layer.core_timing(0)
+        return core
 
     # ---- timed region: exactly K steps
     torch.cuda.synchronize()
@@ -211,16 +208,16 @@ def main():
     if graph is not None:
         graph.replay()
     else:
-        eager_steps_with_core_events()
+        core = eager_steps_with_core_events()
     torch.cuda.synchronize()
     t_step = (time.perf_counter() - t0) / K
     if graph is not None:
         # events recorded inside a captured graph do not time the kernel between
         # them, so the core kernel is timed on the same K steps run eagerly
-        eager_steps_with_core_events()
+        core = eager_steps_with_core_events()
         torch.cuda.synchronize()
-
-    core_ms = float(np.mean([a.elapsed_time(b_) for a, b_ in ev]))
+    assert len(core) == K
+    core_ms = float(np.mean(core))
     cache_bytes = float(int(seq_len.sum()) * ROW_BYTES)
     weight_bytes = 2.0 * sum(v.size for v in w.values())
     act_bytes = 2.0 * (2 * B * d.hidden + B * d.row)  # hidden in, y out, appended rows
@@ -250,7 +247,8 @@ def main():
                    "weight_bytes": int(weight_bytes), "hidden": d.hidden, "heads": d.n_heads,
                    "kv_lora": d.kv_lora, "qk_rope": d.qk_rope},
         "roofline": {"kernel": "decode_core_mfma_k", "bound": "hbm",
-                     "kernel_timing": "HIP events around every split-S core launch, K eager steps",
+                     "kernel_timing": "HIP events (no system fence) around every split-S core "
+                                      "launch, K eager steps",
                      "achieved": round(core_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(core_gbs / HBM_PEAK_GBS, 4),
                      "kernel_ms": round(core_ms, 5),

@@ -238,12 +238,20 @@ int mla_prefill(mla_handle h, const void* hidden, const int32_t* cu_new,
                 const void* cache, int64_t cache_rows, void* out, void* ws,
                 size_t ws_bytes);
 
-/* Measurement hook: when both are non-NULL hipEvent_t handles, later calls
- * record `start` on the handle's stream right before the split-S core kernel
- * of mla_decode (the attention kernel of mla_prefill) and `stop` right after
- * it, so the caller can time that kernel alone with hipEventElapsedTime.
- * NULL, NULL turns it off.  The events stay owned by the caller. */
-int mla_set_timing_events(mla_handle h, void* start, void* stop);
+/* Measurement: with n_slots > 0, every later launch of the attention core
+ * (the split-S kernel of mla_decode / mla_decode_step, the attention kernel of
+ * mla_prefill) is bracketed by a pair of HIP events on the handle's stream,
+ * kept in a ring of n_slots pairs.  The events are created without the
+ * system-scope fence, so recording them neither writes back nor invalidates
+ * caches.  Launches recorded while the stream is being captured into a graph
+ * are not timed.  n_slots = 0 turns timing off.  Waits for the stream first.
+ * Errors: INVALID_ARG (n_slots < 0), HIP. */
+int mla_core_timing(mla_handle h, int32_t n_slots);
+
+/* Durations in ms of the last min(n, timed launches, n_slots) timed core
+ * launches, oldest first, into ms (HOST, n floats); *n_out = how many.  Waits
+ * for those launches to finish. */
+int mla_core_timing_read(mla_handle h, float* ms, int32_t n, int32_t* n_out);
 
 /* Static text for a status code. */
 const char* mla_status_string(int status);

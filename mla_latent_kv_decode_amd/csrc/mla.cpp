@@ -72,7 +72,10 @@ struct mla_ctx {
   Staging ring[kRing];
   int ring_next = 0;
   std::vector<void*> captured;  // pinned staging owned by captured graphs
-  hipEvent_t t_start = nullptr, t_stop = nullptr;  // caller's timing events
+  // timing ring of the attention-core launches: events 2i, 2i+1 bracket slot i
+  std::vector<hipEvent_t> tev;
+  int t_next = 0;
+  int64_t t_count = 0;
   std::string err;
 };
 
@@ -413,6 +416,19 @@ int build_decode_meta(const mla_ctx* h, int B, const int64_t* seq_off, const int
   return parts;
 }
 
+// Slot of the timing ring for the next core launch, or -1 (timing off, or the
+// stream is being captured into a graph, where event records do not time).
+int timing_slot(mla_ctx* h) {
+  if (h->tev.empty()) return -1;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(h->stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
+    return -1;
+  const int slot = h->t_next;
+  h->t_next = (h->t_next + 1) % (int)(h->tev.size() / 2);
+  h->t_count++;
+  return slot;
+}
+
 int check_ws(mla_ctx* h, void* ws, size_t ws_bytes, size_t need) {
   if (need == 0) return MLA_OK;
   if (!ws) return fail(h, MLA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
@@ -555,6 +571,8 @@ static void free_weights(mla_ctx* h) {
   h->absorbed = false;
 }
 
+static void drop_timing(mla_ctx* h);
+
 int mla_destroy(mla_handle h) {
   if (!h) return MLA_ERR_INVALID_ARG;
   DeviceGuard g(h->device);
@@ -565,16 +583,46 @@ int mla_destroy(mla_handle h) {
     if (s.host) (void)hipHostFree(s.host);
   }
   for (void* p : h->captured) (void)hipHostFree(p);
+  drop_timing(h);
   delete h;
   return MLA_OK;
 }
 
-int mla_set_timing_events(mla_handle h, void* start, void* stop) {
-  if (!h) return MLA_ERR_INVALID_ARG;
-  if ((start == nullptr) != (stop == nullptr))
-    return fail(h, MLA_ERR_INVALID_ARG, "timing events: give both or neither");
-  h->t_start = (hipEvent_t)start;
-  h->t_stop = (hipEvent_t)stop;
+static void drop_timing(mla_ctx* h) {
+  for (hipEvent_t e : h->tev) (void)hipEventDestroy(e);
+  h->tev.clear();
+  h->t_next = 0;
+  h->t_count = 0;
+}
+
+int mla_core_timing(mla_handle h, int32_t n_slots) {
+  if (!h || n_slots < 0) return MLA_ERR_INVALID_ARG;
+  DeviceGuard g(h->device);
+  if (!g.ok) return fail(h, MLA_ERR_HIP, "cannot select device %d", h->device);
+  (void)hipStreamSynchronize(h->stream);
+  drop_timing(h);
+  for (int i = 0; i < 2 * n_slots; ++i) {
+    hipEvent_t e;
+    // no system-scope fence: recording must not write back or invalidate caches
+    HIP_TRY(h, hipEventCreateWithFlags(&e, hipEventDisableSystemFence));
+    h->tev.push_back(e);
+  }
+  return MLA_OK;
+}
+
+int mla_core_timing_read(mla_handle h, float* ms, int32_t n, int32_t* n_out) {
+  if (!h || !ms || !n_out || n < 0) return MLA_ERR_INVALID_ARG;
+  DeviceGuard g(h->device);
+  if (!g.ok) return fail(h, MLA_ERR_HIP, "cannot select device %d", h->device);
+  const int slots = (int)h->tev.size() / 2;
+  const int avail = (int)std::min<int64_t>(h->t_count, slots);
+  const int k = std::min(n, avail);
+  for (int i = 0; i < k; ++i) {
+    const int slot = ((h->t_next - k + i) % slots + slots) % slots;
+    HIP_TRY(h, hipEventSynchronize(h->tev[2 * slot + 1]));
+    HIP_TRY(h, hipEventElapsedTime(&ms[i], h->tev[2 * slot], h->tev[2 * slot + 1]));
+  }
+  *n_out = k;
   return MLA_OK;
 }
 
@@ -831,7 +879,8 @@ static int run_decode(mla_ctx* h, const T* hidden, int B, T* cache, T* out, void
   float* ml = at<float>(ws, L.ml);
   T* o_lat = at<T>(ws, L.o_lat);
   bool mfma_core = false;
-  if (h->t_start) HIP_TRY(h, hipEventRecord(h->t_start, h->stream));
+  const int ts = timing_slot(h);
+  if (ts >= 0) HIP_TRY(h, hipEventRecord(h->tev[2 * ts], h->stream));
   if constexpr (sizeof(T) == 2) {
     if (h->mfma) {
       mla::decode_core_mfma(q_cat, cache, mt, parts, B, acc, ml, d, h->stream);
@@ -839,7 +888,7 @@ static int run_decode(mla_ctx* h, const T* hidden, int B, T* cache, T* out, void
     }
   }
   if (!mfma_core) mla::decode_core_generic<T>(q_cat, cache, mt, nseg_total, acc, ml, d, h->stream);
-  if (h->t_stop) HIP_TRY(h, hipEventRecord(h->t_stop, h->stream));
+  if (ts >= 0) HIP_TRY(h, hipEventRecord(h->tev[2 * ts + 1], h->stream));
   // A6: combine the partials of each sequence (fixed slot order)
   if constexpr (sizeof(T) == 2) {
     if (mfma_core)
@@ -991,10 +1040,11 @@ static int run_prefill(mla_ctx* h, const T* hidden, int ntok, int B, const int32
                 1, out_f32(kv + kv_off_h[b] * (int64_t)wkv, wkv), scratch);
   }
   T* o = at<T>(ws, L.o);
-  if (h->t_start) HIP_TRY(h, hipEventRecord(h->t_start, h->stream));
+  const int ts = timing_slot(h);
+  if (ts >= 0) HIP_TRY(h, hipEventRecord(h->tev[2 * ts], h->stream));
   mla::prefill_attn_generic<T>(q_nope, q_rope, kv, cache, tok_seq, tok_pos, kv_off, seq_off_d,
                                ntok, o, d, h->stream);
-  if (h->t_stop) HIP_TRY(h, hipEventRecord(h->t_stop, h->stream));
+  if (ts >= 0) HIP_TRY(h, hipEventRecord(h->tev[2 * ts + 1], h->stream));
   gemm_out<T>(h, o, (int64_t)d.H * d.dv, 0, (const T*)h->w_o, (int64_t)d.H * d.dv, 0, ntok, d.D,
               d.H * d.dv, 1, out_t<T>(out, d.D), scratch);
   return check_launch(h, "prefill");

@@ -73,7 +73,9 @@ _SIGS = {
                                                 ctypes.POINTER(ctypes.c_size_t)]),
     "mla_decode_plan": (ctypes.c_int, [ctypes.c_int32, _I32P, ctypes.c_int32, _I32P, _I32P,
                                        _I32P, _I32P, _I32P, _I32P]),
-    "mla_set_timing_events": (ctypes.c_int, [_P, _P, _P]),
+    "mla_core_timing": (ctypes.c_int, [_P, ctypes.c_int32]),
+    "mla_core_timing_read": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_float), ctypes.c_int32,
+                                            _I32P]),
     "mla_prefill_workspace_bytes": (ctypes.c_size_t, [_P, ctypes.c_int32, ctypes.c_int32,
                                                       ctypes.c_int64]),
     "mla_prefill": (ctypes.c_int, [_P, _P, _I32P, _I32P, _I64P, ctypes.c_int32, _P,
@@ -186,12 +188,18 @@ class MLALayer:
         except Exception:
             pass
 
-    def set_timing_events(self, start=None, stop=None):
-        """start/stop: torch.cuda.Event(enable_timing=True) already recorded once
-        (so the underlying hipEvent_t exists), or None to stop timing."""
-        sp = ctypes.c_void_p(start.cuda_event) if start is not None else None
-        ep = ctypes.c_void_p(stop.cuda_event) if stop is not None else None
-        self._check(self.lib.mla_set_timing_events(self.h, sp, ep), self.h, "timing events")
+    def core_timing(self, n_slots: int):
+        """Time the next attention-core launches in a ring of n_slots (0 = off)."""
+        self._check(self.lib.mla_core_timing(self.h, int(n_slots)), self.h, "core timing")
+
+    def core_timing_read(self, n: int) -> np.ndarray:
+        """Durations (ms) of the last n timed core launches, oldest first."""
+        ms = np.zeros(max(int(n), 1), np.float32)
+        got = ctypes.c_int32()
+        self._check(self.lib.mla_core_timing_read(
+            self.h, ms.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), int(n),
+            ctypes.byref(got)), self.h, "core timing read")
+        return ms[:got.value].copy()
 
     # -- A1
     def absorb_weights(self, w: dict):

@@ -130,3 +130,17 @@ def test_decode_step_v2lite():
 
 def test_decode_step_v3():
     _step_case(synth.V3, [0, 40, 700])
+
+
+def test_core_timing_ring():
+    """The library's core-launch timing: a ring of 3 slots after 5 decodes
+    holds the last 3 durations, each positive and below a second."""
+    case = DecodeCase(synth.V2_LITE, "bf16", 0.02, [300, 40])
+    case.layer.core_timing(3)
+    for _ in range(5):
+        case.run(stages=False)
+    ms = case.layer.core_timing_read(10)
+    case.layer.core_timing(0)
+    assert len(ms) == 3
+    assert np.all(ms > 0) and np.all(ms < 1000)
+    assert len(case.layer.core_timing_read(10)) == 0
