@@ -49,10 +49,13 @@ constexpr int NTHR = 64 * NWAVE;
 constexpr int NSTAGE = 2;
 constexpr float kRescale = 8.0f;             // lazy-rescale threshold, log2 units
 constexpr int LDS_BYTES = NWAVE * NSTAGE * SUB_BYTES;  // 36 KB per wave
-// merge mapping: TPH threads per head, CPT latent columns per thread
-constexpr int TPH = NTHR / 16;
-constexpr int CPT = DC / TPH;
-static_assert(NWAVE * 16 * DC * 4 + NWAVE * 16 * 2 * 4 <= LDS_BYTES, "merge space");
+// merge: each wave finalises CB_PER_WAVE of the 32 16-column blocks; the
+// exchange area holds every wave's value of every block (1 KB each)
+constexpr int CB_PER_WAVE = 32 / NWAVE;
+constexpr int XO_BYTES = NWAVE * 32 * 1024;
+static_assert(32 % NWAVE == 0, "column blocks must split evenly over the waves");
+static_assert(XO_BYTES + NWAVE * 16 * 2 * 4 <= LDS_BYTES, "merge space");
+
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
@@ -102,6 +105,20 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+typedef const __attribute__((address_space(4))) DecodeWork* ConstWorkPtr;
+
+// Field by field: a constant-address-space object cannot bind to the implicit
+// copy constructor.
+__device__ __forceinline__ DecodeWork load_work(ConstWorkPtr p) {
+  DecodeWork w;
+  w.row = p->row;
+  w.n = p->n;
+  w.b = p->b;
+  w.pidx = p->pidx;
+  w.next = p->next;
+  return w;
+}
+
 __device__ __forceinline__ uint32_t lds_u32(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
@@ -140,22 +157,30 @@ decode_core_mfma_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
     for (int t = 0; t < 4; ++t) pv_off[t] = r * 1024 + 8 * (lr & 1) + 16 * hh + 32 * (t ^ y);
   }
 
-  const int sbeg = mt.part_begin[part], send = mt.part_begin[part + 1];
-  for (int si = sbeg; si < send; ++si) {
-    const DecodeSeg sg = mt.segs[si];
-    const int n = sg.r1 - sg.r0;
+  // the part's first work record is work[part]; further ones are chained.  The
+  // records are read through the constant address space: the kernel never
+  // writes them, and this keeps them on scalar loads (the inline-asm memory
+  // clobbers would otherwise turn them into vector loads plus waits that also
+  // drain the stage prefetches).
+  const ConstWorkPtr works = reinterpret_cast<ConstWorkPtr>((uintptr_t)mt.work);
+  DecodeWork wk = load_work(works + part);
+  for (;;) {
+    const int n = wk.n;
     const int nsub = (n + SUB - 1) / SUB;
-    const bf16* rows = cache + (mt.seq_off[sg.b] + sg.r0) * (int64_t)RW;
+    const bf16* rows = cache + wk.row * (int64_t)RW;
 
     // this wave's sub-tiles: wave, wave + NWAVE, ...
     const int my_n = wave < nsub ? (nsub - 1 - wave) / NWAVE + 1 : 0;
     if (my_n > 0) issue_subtile(rows, wave * SUB, n, my_addr, lane);
     if (my_n > 1) issue_subtile(rows, (wave + NWAVE) * SUB, n, my_addr + SUB_BYTES, lane);
+    // the next record is fetched now and used after this segment
+    DecodeWork nx = wk;
+    if (wk.next >= 0) nx = load_work(works + wk.next);
 
     // Q^T fragments of head (hg*16 + lr): columns 32 s + 8 lg .. + 7
     bf16x8_t qf[18];
     {
-      const bf16* qrow = q_cat + ((int64_t)sg.b * H + hg * 16 + lr) * RW + lg * 8;
+      const bf16* qrow = q_cat + ((int64_t)wk.b * H + hg * 16 + lr) * RW + lg * 8;
 #pragma unroll
       for (int s = 0; s < 18; ++s) qf[s] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * s);
       // Consume the Q loads here so the compiler's own waits for them sit before
@@ -256,66 +281,64 @@ decode_core_mfma_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
       }
     }
 
-    // ---- merge the NWAVE wave states through LDS (staging buffers are free now)
+    // ---- merge the wave states through LDS (staging buffers are free now).
+    // Every wave holds (head lr, columns 16 cb + 4 lg .. +3) for all 32 column
+    // blocks cb; wave w finalises the blocks of its own range, reading the
+    // other waves' values of those blocks from lane-contiguous 1 KB slots
+    // (conflict-free), and sums the waves in order 0..NWAVE-1.
     __syncthreads();
-    float* om = reinterpret_cast<float*>(lds);             // [wave][16 heads][512]
-    float* mlm = om + NWAVE * 16 * DC;                      // [wave][16][2]
-    {
-      float* ow = om + (wave * 16 + lr) * DC + 4 * lg;
+    float4* xo = reinterpret_cast<float4*>(lds);              // [src wave][cb][64 lanes]
+    float* mlx = reinterpret_cast<float*>(lds + XO_BYTES);    // [wave][16 heads][2]
 #pragma unroll
-      for (int cb = 0; cb < 32; ++cb)
-        *reinterpret_cast<float4*>(ow + 16 * cb) =
-            make_float4(o[cb][0], o[cb][1], o[cb][2], o[cb][3]);
-      // per-lane partial sums -> per-head sum over the 4 lane groups
-      l_run += __shfl_xor(l_run, 16, 64);
-      l_run += __shfl_xor(l_run, 32, 64);
-      if (lg == 0) {
-        mlm[(wave * 16 + lr) * 2] = m_run;
-        mlm[(wave * 16 + lr) * 2 + 1] = l_run;
-      }
+    for (int cb = 0; cb < 32; ++cb)
+      if (cb / CB_PER_WAVE != wave)
+        xo[(wave * 32 + cb) * 64 + lane] = make_float4(o[cb][0], o[cb][1], o[cb][2], o[cb][3]);
+    // per-lane partial sums -> per-head sum over the 4 lane groups
+    l_run += __shfl_xor(l_run, 16, 64);
+    l_run += __shfl_xor(l_run, 32, 64);
+    if (lg == 0) {
+      mlx[(wave * 16 + lr) * 2] = m_run;
+      mlx[(wave * 16 + lr) * 2 + 1] = l_run;
     }
     __syncthreads();
-    // thread t: head t / TPH, columns (t % TPH) * CPT .. + CPT - 1
-    const int h = threadIdx.x / TPH;
-    const int c0 = (threadIdx.x % TPH) * CPT;
-    const int gh = hg * 16 + h;  // global head index
-    float r[CPT];
-    float M = -INFINITY, L = 0.f;
     {
       float mw[NWAVE], sc[NWAVE];
+      float M = -INFINITY, L = 0.f;
 #pragma unroll
       for (int w = 0; w < NWAVE; ++w) {
-        mw[w] = mlm[(w * 16 + h) * 2];
+        mw[w] = mlx[(w * 16 + lr) * 2];
         M = fmaxf(M, mw[w]);
       }
 #pragma unroll
       for (int w = 0; w < NWAVE; ++w) {
         sc[w] = exp2f(mw[w] - M);
-        L += sc[w] * mlm[(w * 16 + h) * 2 + 1];
+        L += sc[w] * mlx[(w * 16 + lr) * 2 + 1];
       }
+      const int gh = hg * 16 + lr;  // global head index
+      float* pacc = acc_out + ((int64_t)wk.pidx * H + gh) * DC + 4 * lg;
 #pragma unroll
-      for (int c = 0; c < CPT; c += 4) {
-        float4 acc4 = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int cb = 0; cb < 32; ++cb) {
+        if (cb / CB_PER_WAVE != wave) continue;
+        float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
         for (int w = 0; w < NWAVE; ++w) {
-          const float4 v = *reinterpret_cast<const float4*>(om + (w * 16 + h) * DC + c0 + c);
-          acc4.x = fmaf(sc[w], v.x, acc4.x);
-          acc4.y = fmaf(sc[w], v.y, acc4.y);
-          acc4.z = fmaf(sc[w], v.z, acc4.z);
-          acc4.w = fmaf(sc[w], v.w, acc4.w);
+          const float4 v = w == wave ? make_float4(o[cb][0], o[cb][1], o[cb][2], o[cb][3])
+                                     : xo[(w * 32 + cb) * 64 + lane];
+          a.x = fmaf(sc[w], v.x, a.x);
+          a.y = fmaf(sc[w], v.y, a.y);
+          a.z = fmaf(sc[w], v.z, a.z);
+          a.w = fmaf(sc[w], v.w, a.w);
         }
-        r[c] = acc4.x; r[c + 1] = acc4.y; r[c + 2] = acc4.z; r[c + 3] = acc4.w;
+        *reinterpret_cast<float4*>(pacc + 16 * cb) = a;
+      }
+      if (wave == 0 && lg == 0) {
+        ml_out[((int64_t)wk.pidx * H + gh) * 2] = M;
+        ml_out[((int64_t)wk.pidx * H + gh) * 2 + 1] = L;
       }
     }
-    float* pacc = acc_out + ((int64_t)sg.pidx * H + gh) * DC + c0;
-#pragma unroll
-    for (int c = 0; c < CPT; c += 4)
-      *reinterpret_cast<float4*>(pacc + c) = make_float4(r[c], r[c + 1], r[c + 2], r[c + 3]);
-    if (threadIdx.x % TPH == 0) {
-      ml_out[((int64_t)sg.pidx * H + gh) * 2] = M;
-      ml_out[((int64_t)sg.pidx * H + gh) * 2 + 1] = L;
-    }
-    __syncthreads();
+    __syncthreads();  // the stages are refilled by the next segment
+    if (wk.next < 0) break;
+    wk = nx;
   }
 }
 

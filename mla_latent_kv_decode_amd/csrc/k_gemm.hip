@@ -130,9 +130,16 @@ gemm_bf16_tile_k(const bf16* __restrict__ A, int64_t lda, int64_t sA, const bf16
     }
 }
 
+#ifndef MLA_NOSPLIT_KB
+#define MLA_NOSPLIT_KB 0
+#endif
+
 int gemm_bf16_ksplit(int M, int N, int K, int batch, int n_cu) {
   const long tiles = (long)((N + 63) / 64) * ((M + 63) / 64) * batch;
   int ks = 1;
+  // a block whose whole weight tile is small streams it faster than a split
+  // costs (the split needs a second kernel to sum the partials)
+  if ((long)64 * K * 2 <= (long)MLA_NOSPLIT_KB * 1024) return 1;
   // split K over blocks while the grid stays within one block per CU; each
   // wave keeps >= 1 whole k-step
   while (tiles * ks * 2 <= (long)n_cu && (K / 32) % (ks * 2 * KSL) == 0 && ks < kMaxSplit) ks *= 2;

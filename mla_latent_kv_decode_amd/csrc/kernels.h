@@ -29,6 +29,15 @@ struct DecodeSeg {
   int32_t b, r0, r1, pidx;
 };
 
+// The same segment as the persistent core reads it: one self-contained record
+// (absolute first cache row, row count, sequence, partial slot).  Record p <
+// parts is the first segment of part p; `next` chains the part's further
+// segments (-1 ends the chain).
+struct DecodeWork {
+  int64_t row;
+  int32_t n, b, pidx, next;
+};
+
 // Per-sequence decode metadata on the device.
 struct DecodeMeta {
   const int64_t* seq_off;   // (B)
@@ -39,6 +48,7 @@ struct DecodeMeta {
   const DecodeSeg* segs;    // (nseg_total)
   const int32_t* part_begin;  // (parts + 1) segment range of each persistent part
   const int32_t* cstart;    // (B) first chunk slot of sequence b (two-stage combine)
+  const DecodeWork* work;   // (nseg_total) work records of the MFMA core
 };
 
 // The 512-wide combine merges the partials of a sequence in chunks of

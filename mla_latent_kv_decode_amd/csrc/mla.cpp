@@ -22,7 +22,7 @@
 
 // rows-equivalent cost of a segment start in the split-S work list
 #ifndef MLA_SEG_ROWS
-#define MLA_SEG_ROWS 320
+#define MLA_SEG_ROWS 192
 #endif
 
 using mla::bf16;
@@ -255,7 +255,8 @@ int max_parts(const mla_ctx* h, int64_t total_rows) {
 
 size_t meta_bytes(int B, int parts, int max_segs) {
   return 2 * align_up((size_t)B * 8) + 5 * align_up((size_t)B * 4) +
-         align_up((size_t)(parts + 1) * 4) + align_up((size_t)max_segs * sizeof(DecodeSeg));
+         align_up((size_t)(parts + 1) * 4) + align_up((size_t)max_segs * sizeof(DecodeSeg)) +
+         align_up((size_t)max_segs * sizeof(mla::DecodeWork));
 }
 
 int qw_of(const Dims& d) { return d.H * (d.dn + d.dr); }
@@ -299,7 +300,7 @@ DecodeLayout decode_layout(const mla_ctx* h, int B, int64_t total_rows, bool ste
 }
 
 struct MetaOffsets {
-  size_t seq_off, seq_len, pos, pstart, nseg, cstart, part, segs, slot;
+  size_t seq_off, seq_len, pos, pstart, nseg, cstart, part, segs, work, slot;
 };
 
 // Host-side work list.  The concatenated rows of all sequences are cut into
@@ -399,6 +400,7 @@ int build_decode_meta(const mla_ctx* h, int B, const int64_t* seq_off, const int
   mo->cstart = c.take((size_t)B * 4);
   mo->part = c.take((size_t)(parts + 1) * 4);
   mo->segs = c.take(segs.size() * sizeof(DecodeSeg));
+  mo->work = c.take(segs.size() * sizeof(mla::DecodeWork));
   blob.assign(c.off, 0);
   memcpy(blob.data() + mo->seq_off, seq_off, (size_t)B * 8);
   if (with_slot) {
@@ -412,6 +414,28 @@ int build_decode_meta(const mla_ctx* h, int B, const int64_t* seq_off, const int
   memcpy(blob.data() + mo->cstart, cstart.data(), (size_t)B * 4);
   memcpy(blob.data() + mo->part, part_begin.data(), part_begin.size() * 4);
   memcpy(blob.data() + mo->segs, segs.data(), segs.size() * sizeof(DecodeSeg));
+  {
+    // work records: part p's first segment at p, the rest chained after the parts
+    std::vector<mla::DecodeWork> work(segs.size());
+    int extra = parts;
+    for (int p = 0; p < parts; ++p) {
+      int slot = p;
+      for (int si = part_begin[p]; si < part_begin[p + 1]; ++si) {
+        const DecodeSeg& sg = segs[si];
+        mla::DecodeWork& w = work[slot];
+        w.row = seq_off[sg.b] + sg.r0;
+        w.n = sg.r1 - sg.r0;
+        w.b = sg.b;
+        w.pidx = sg.pidx;
+        w.next = -1;
+        if (si + 1 < part_begin[p + 1]) {
+          w.next = extra;
+          slot = extra++;
+        }
+      }
+    }
+    memcpy(blob.data() + mo->work, work.data(), work.size() * sizeof(mla::DecodeWork));
+  }
   *nseg_total = (int)segs.size();
   return parts;
 }
@@ -940,6 +964,7 @@ static int decode_common(mla_handle h, const void* hidden, const int32_t* pos,
   mt.pstart = at<int32_t>(meta, mo.pstart);
   mt.nseg = at<int32_t>(meta, mo.nseg);
   mt.cstart = at<int32_t>(meta, mo.cstart);
+  mt.work = at<mla::DecodeWork>(meta, mo.work);
   mt.part_begin = at<int32_t>(meta, mo.part);
   mt.segs = at<DecodeSeg>(meta, mo.segs);
   const int64_t* slot_dev = step ? at<int64_t>(meta, mo.slot) : nullptr;

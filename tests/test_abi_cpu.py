@@ -183,7 +183,7 @@ def test_decode_plan_balances_cost():
     lens = synth.lengths(synth.WORKLOADS["v2lite_decode_b64"]) + 1
     rows, segs = _plan_invariants(lens, 256)
     assert len(rows) == 256
-    seg_rows = 320  # the library's per-segment charge
+    seg_rows = 192  # the library's per-segment charge
     cost = rows + seg_rows * segs
     assert cost.max() - cost.mean() < 16 + seg_rows
 
