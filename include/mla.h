@@ -203,8 +203,8 @@ int mla_decode_stage_offsets(mla_handle h, int32_t B, int64_t total_rows,
  * at most max_parts contiguous spans (one persistent workgroup each), each span
  * split at sequence boundaries into segments; spans are balanced on rows plus
  * a fixed per-segment cost, and cuts inside a sequence fall on multiples of 16
- * rows.  The library itself uses max_parts = the device's compute units times
- * the workgroups of the core kernel that share one.
+ * rows.  The library itself uses max_parts = the device's compute units divided
+ * by the number of 16-head groups (each part runs one workgroup per group).
  *   seq_len: HOST (B), each >= 1.
  *   part_begin: HOST out (max_parts + 1): segments of part p are
  *     [part_begin[p], part_begin[p+1]).

@@ -47,7 +47,8 @@ constexpr int LOADS = SUB + 2;               // 18 wave-wide 16-byte loads per s
 constexpr int NWAVE = MLA_DEC_NWAVE;         // waves per workgroup
 constexpr int NTHR = 64 * NWAVE;
 constexpr int NSTAGE = 2;
-constexpr float kRescale = 8.0f;             // lazy-rescale threshold, log2 units
+constexpr float kRescale = 8.0f;
+constexpr int kXcds = 8;                     // XCDs of an MI355X             // lazy-rescale threshold, log2 units
 constexpr int LDS_BYTES = NWAVE * NSTAGE * SUB_BYTES;  // 36 KB per wave
 // merge: each wave finalises CB_PER_WAVE of the 32 16-column blocks; the
 // exchange area holds every wave's value of every block (1 KB each)
@@ -125,10 +126,17 @@ __device__ __forceinline__ uint32_t lds_u32(const void* p) {
 
 __global__ void __launch_bounds__(NTHR, 1)
 decode_core_mfma_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cache, DecodeMeta mt,
-                   float* __restrict__ acc_out, float* __restrict__ ml_out, int H) {
+                   float* __restrict__ acc_out, float* __restrict__ ml_out, int H, int nparts) {
   __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
-  const int part = blockIdx.x;
-  const int hg = blockIdx.y;
+  // Block -> (part, head group).  Workgroups are handed to the XCDs round
+  // robin (block i to XCD i % 8), so the HG head-group blocks of part p are
+  // numbered p % 8 modulo 8: they share an XCD and its L2, start together and
+  // stream the same rows, which HBM then delivers once.
+  const int HG = H / 16;
+  const int bid = blockIdx.x;
+  const int part = (bid / (kXcds * HG)) * kXcds + bid % kXcds;
+  const int hg = (bid / kXcds) % HG;
+  if (part >= nparts) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int lr = lane & 15, lg = lane >> 4;
@@ -349,8 +357,9 @@ int decode_core_wg_per_cu() { return dec::NWAVE >= 4 ? 1 : 4 / dec::NWAVE; }
 void decode_core_mfma(const bf16* q_cat, const bf16* cache, const DecodeMeta& m, int parts,
                       int B, float* acc, float* ml, const Dims& d, hipStream_t st) {
   (void)B;
-  dim3 grid(parts, d.H / 16);
-  dec::decode_core_mfma_k<<<grid, dec::NTHR, 0, st>>>(q_cat, cache, m, acc, ml, d.H);
+  const int hg = d.H / 16;
+  const int blocks = (parts + dec::kXcds - 1) / dec::kXcds * dec::kXcds * hg;
+  dec::decode_core_mfma_k<<<blocks, dec::NTHR, 0, st>>>(q_cat, cache, m, acc, ml, d.H, parts);
 }
 
 }  // namespace mla

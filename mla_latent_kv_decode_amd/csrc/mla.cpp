@@ -247,7 +247,11 @@ struct DecodeLayout {
 
 int max_parts(const mla_ctx* h, int64_t total_rows) {
   int64_t p = (total_rows + 63) / 64;
-  const int64_t wgs = (int64_t)h->n_cu * (h->mfma ? mla::decode_core_wg_per_cu() : 1);
+  // the MFMA core runs one workgroup per 16-head group of a part
+  const int64_t wgs = h->mfma ? std::max<int64_t>(1, (int64_t)h->n_cu *
+                                                         mla::decode_core_wg_per_cu() /
+                                                         (h->d.H / 16))
+                              : h->n_cu;
   if (p > wgs) p = wgs;
   if (p < 1) p = 1;
   return (int)p;
