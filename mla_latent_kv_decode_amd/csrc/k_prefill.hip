@@ -1,0 +1,307 @@
+// Causal chunked-prefill attention on CDNA4 MFMA (bf16 in, fp32 accumulate),
+// expanded (non-absorbed) form: per head h and new token at position p,
+//   s_t = q_h . [K_nope_h,t ; k_rope_t] * scale  for cached rows t <= p,
+//   o_h = softmax_t(s) . V_h,t
+// ("Multi-Head Latent Attention" post, sections 3.2 and 3.6: keys are the
+// expanded K_nope with the shared rope key appended, values the expanded V;
+// "Transformer and KV Cache Basics", mask design: a query at position p sees
+// rows 0..p of its sequence).  K_nope and V come from the expansion GEMM
+// (rows x H x [K_nope | V], bf16); k_rope is read from the latent cache row.
+//
+// Block = (tile of up to 256 new tokens of one sequence, head).  Wave w owns
+// queries 64w .. 64w+63 of the tile as 4 blocks of 16.  Keys stream in tiles of
+// 32 through a 4-stage LDS ring filled by global_load_lds_dwordx4 (each wave
+// issues a quarter of every tile; one barrier per tile both publishes the tile
+// and frees the stage the next prefetch overwrites).  Per 16-key block:
+//   S^T (16 keys x 16 queries) = K . Q^T  -- 6 x mfma 16x16x32 per query block,
+//       each K fragment (LDS) reused for the wave's 4 query blocks;
+//   online softmax per query with a lazily moved reference maximum;
+//   O^T (128 dims x 16 queries) += V^T . P^T -- mfma 16x16x16 with V^T read
+//       straight into operand layout by ds_read_b64_tr_b16, each fragment
+//       reused for the 4 query blocks.
+// Key blocks past a wave's last query are skipped (the causal diagonal).
+#include <utility>
+
+#include "kernels.h"
+
+namespace mla {
+namespace pf {
+
+constexpr int DN = 128, DR = 64, DV = 128;
+constexpr int KT = 32;                       // keys per tile
+constexpr int NW = 4;                        // waves per block
+constexpr int QW = 64;                       // queries per wave
+constexpr int NQB = QW / 16;                 // 16-query blocks per wave
+constexpr int NST = 4;                       // LDS stages
+constexpr int KR_OFF = KT * DN * 2;          // K_nope: 256 B per key
+constexpr int V_OFF = KR_OFF + KT * DR * 2;  // k_rope: 128 B per key
+constexpr int ST_BYTES = V_OFF + KT * DV * 2;  // V: 256 B per key; 20 KB per stage
+constexpr int NLOAD = ST_BYTES / 1024;       // 20 wave-wide 16-byte loads per tile
+constexpr int LPW = NLOAD / NW;              // 5 per wave
+constexpr int KN_LOADS = KR_OFF / 1024, KR_LOADS = (V_OFF - KR_OFF) / 1024;
+constexpr float kRescale = 8.0f;             // lazy-rescale threshold, log2 units
+constexpr int kXcds = 8;
+static_assert(NLOAD % NW == 0 && NW == 4, "tile loads split evenly over 4 waves");
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+// LDS layout of one stage, 16-byte chunks XOR-swizzled per key so the reads
+// of both products spread over all banks:
+//   K_nope chunk c (0..15) of key r at r*256 + 16*(c ^ (r & 15));
+//   k_rope chunk c (0..7)  at KR_OFF + r*128 + 16*(c ^ ((r >> 1) & 7));
+//   V      chunk c (0..15) at V_OFF  + r*256 + 16*(c ^ (2 * (r & 7))).
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(lds_addr)
+               : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+typedef const __attribute__((address_space(4))) PrefillTile* ConstTilePtr;
+
+// Load I (0..NLOAD-1) of key tile [k0, k0 + KT): first K_nope (4 keys per
+// load), then k_rope (8 keys per load), then V (4 keys per load).  Keys at or
+// past kend re-read the last key (their scores are masked).
+template <int I>
+__device__ __forceinline__ void issue_load(const char* kvh, const char* rope, int64_t kv_stride,
+                                           int k0, int kend, uint32_t stage, int lane) {
+  if constexpr (I < KN_LOADS) {
+    const int r = 4 * I + (lane >> 4);
+    const int kk = min(k0 + r, kend - 1);
+    const int c = (lane & 15) ^ (r & 15);
+    dma16(kvh + kk * kv_stride + c * 16, stage + I * 1024);
+  } else if constexpr (I < KN_LOADS + KR_LOADS) {
+    constexpr int J = I - KN_LOADS;
+    const int r = 8 * J + (lane >> 3);
+    const int kk = min(k0 + r, kend - 1);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    dma16(rope + (int64_t)kk * 1152 + c * 16, stage + KR_OFF + J * 1024);
+  } else {
+    constexpr int J = I - KN_LOADS - KR_LOADS;
+    const int r = 4 * J + (lane >> 4);
+    const int kk = min(k0 + r, kend - 1);
+    const int c = (lane & 15) ^ (2 * (r & 7));
+    dma16(kvh + kk * kv_stride + 256 + c * 16, stage + V_OFF + J * 1024);
+  }
+}
+
+template <int W, int... U>
+__device__ __forceinline__ void issue_wave(const char* kvh, const char* rope, int64_t kv_stride,
+                                           int k0, int kend, uint32_t stage, int lane,
+                                           std::integer_sequence<int, U...>) {
+  (issue_load<W * LPW + U>(kvh, rope, kv_stride, k0, kend, stage, lane), ...);
+}
+
+// This wave's LPW loads of the tile: straight-line code per wave.
+__device__ __forceinline__ void issue_tile(const char* kvh, const char* rope, int64_t kv_stride,
+                                           int k0, int kend, uint32_t stage, int wave,
+                                           int lane) {
+  const auto seq = std::make_integer_sequence<int, LPW>{};
+  switch (wave) {
+    case 0: issue_wave<0>(kvh, rope, kv_stride, k0, kend, stage, lane, seq); break;
+    case 1: issue_wave<1>(kvh, rope, kv_stride, k0, kend, stage, lane, seq); break;
+    case 2: issue_wave<2>(kvh, rope, kv_stride, k0, kend, stage, lane, seq); break;
+    default: issue_wave<3>(kvh, rope, kv_stride, k0, kend, stage, lane, seq); break;
+  }
+}
+
+__global__ void __launch_bounds__(256, 1)
+prefill_attn_mfma_k(const bf16* __restrict__ q_nope, const bf16* __restrict__ q_rope,
+                    const bf16* __restrict__ kv, const bf16* __restrict__ cache,
+                    const PrefillTile* tiles, int ntiles, int H, float qk_scale,
+                    bf16* __restrict__ o_out) {
+  __shared__ __attribute__((aligned(1024))) char lds[NST * ST_BYTES];
+  // Block -> (tile, head): every block of head h runs on XCD h % 8, so the
+  // tiles of one head share that XCD's L2 for their keys and values.
+  const int bid = blockIdx.x;
+  const int r8 = bid / kXcds;
+  const int h = (r8 / ntiles) * kXcds + bid % kXcds;
+  const int tix = r8 % ntiles;
+  if (h >= H) return;
+  const ConstTilePtr tp = reinterpret_cast<ConstTilePtr>((uintptr_t)tiles) + tix;
+  const int64_t kv_row0 = tp->kv_row0, cache_row0 = tp->cache_row0;
+  const int t0 = tp->t0, nq = tp->nq, pos0 = tp->pos0;
+  const int kend = pos0 + nq;  // keys 0 .. kend-1
+  const int nkt = (kend + KT - 1) / KT;
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int lr = lane & 15, lg = lane >> 4;
+  const uint32_t lds0 = lds_u32(lds);
+  const int64_t kv_stride = (int64_t)H * (DN + DV) * 2;  // bytes per expanded row
+  const char* kvh = reinterpret_cast<const char*>(kv) + kv_row0 * kv_stride + h * (DN + DV) * 2;
+  const char* rope = reinterpret_cast<const char*>(cache) + cache_row0 * 1152 + 1024;
+
+  // prologue: tiles 0 .. NST-2 in flight
+#pragma unroll
+  for (int t = 0; t < NST - 1; ++t)
+    if (t < nkt) issue_tile(kvh, rope, kv_stride, t * KT, kend, lds0 + t * ST_BYTES, wave, lane);
+
+  // this wave's queries; lanes past the tile's last query repeat it
+  const int qw0 = wave * QW;
+  const bool wave_active = qw0 < nq;
+  const int wmax_pos = pos0 + min(qw0 + QW, nq) - 1;
+  bf16x8_t qf[NQB][6];
+  int qpos[NQB];
+#pragma unroll
+  for (int nb = 0; nb < NQB; ++nb) {
+    const int qi = min(qw0 + 16 * nb + lr, nq - 1);
+    qpos[nb] = pos0 + qi;
+    const bf16* qn = q_nope + ((int64_t)(t0 + qi) * H + h) * DN + 8 * lg;
+    const bf16* qr = q_rope + ((int64_t)(t0 + qi) * H + h) * DR + 8 * lg;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qf[nb][s] = *reinterpret_cast<const bf16x8_t*>(qn + 32 * s);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) qf[nb][4 + s] = *reinterpret_cast<const bf16x8_t*>(qr + 32 * s);
+  }
+#pragma unroll
+  for (int nb = 0; nb < NQB; ++nb)
+#pragma unroll
+    for (int s = 0; s < 6; ++s) asm volatile("" ::"v"(qf[nb][s]));
+
+  // K fragment of key row lr, 16-byte chunk c of k-step s: byte offsets
+  const int kn_off = lr * 256;
+  const int kr_off = KR_OFF + lr * 128;
+  const int kn_x = lr & 15, kr_x = (lr >> 1) & 7;
+  // V^T fragment (transposing read): lane (g = lg, s = lr) addresses key
+  // 4g + s/4, dims 16 db + 4(s % 4): chunk 2 db + (s % 4)/2, byte 8(s & 1)
+  const int vr = 4 * lg + (lr >> 2);
+  const int v_base = V_OFF + vr * 256 + 8 * (lr & 1);
+  const int v_h = (lr & 3) >> 1, v_x = 2 * (vr & 7);
+
+  float m_run[NQB], l_run[NQB];
+  f32x4_t o[8][NQB];  // o[db][nb][i]: dim 16 db + 4 lg + i of query 16 nb + lr
+#pragma unroll
+  for (int nb = 0; nb < NQB; ++nb) {
+    m_run[nb] = -INFINITY;
+    l_run[nb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) o[db][nb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  }
+
+  for (int kt = 0; kt < nkt; ++kt) {
+    // tiles kt+1 .. kt+NST-2 may stay in flight
+    static_assert(NST == 4, "wait counts below assume 4 stages");
+    if (kt + 2 < nkt) wait_vmcnt<2 * LPW>();
+    else if (kt + 1 < nkt) wait_vmcnt<LPW>();
+    else wait_vmcnt<0>();
+    __syncthreads();  // tile kt is in LDS; every wave is done with tile kt-1
+    if (kt + NST - 1 < nkt)
+      issue_tile(kvh, rope, kv_stride, (kt + NST - 1) * KT, kend,
+                 lds0 + ((kt + NST - 1) % NST) * ST_BYTES, wave, lane);
+    if (!wave_active) continue;
+    const char* st = lds + (kt % NST) * ST_BYTES;
+    const int k0 = kt * KT;
+#pragma unroll 1
+    for (int mb = 0; mb < KT / 16; ++mb) {
+      const int kb0 = k0 + 16 * mb;
+      if (kb0 > wmax_pos) break;  // every key of the block is masked for this wave
+      const char* sb = st + mb * 16 * 256;         // K_nope / V rows of this block
+      const char* sr = st + mb * 16 * 128;         // k_rope rows of this block
+      bf16x8_t kf[6];
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        kf[s] = *reinterpret_cast<const bf16x8_t*>(sb + kn_off + (((4 * s + lg) ^ kn_x) << 4));
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        kf[4 + s] = *reinterpret_cast<const bf16x8_t*>(sr + kr_off + (((4 * s + lg) ^ kr_x) << 4));
+      f32x4_t sacc[NQB];
+#pragma unroll
+      for (int nb = 0; nb < NQB; ++nb) {
+        sacc[nb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 6; ++s)
+          sacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], qf[nb][s], sacc[nb], 0, 0, 0);
+      }
+      // softmax: lane holds keys kb0 + 4 lg + i of query 16 nb + lr
+      s16x4_t pf[NQB];
+#pragma unroll
+      for (int nb = 0; nb < NQB; ++nb) {
+        float sv[4];
+        bool grow = false;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool valid = kb0 + 4 * lg + i <= qpos[nb];
+          sv[i] = valid ? sacc[nb][i] * qk_scale : -INFINITY;
+          grow |= sv[i] > m_run[nb] + kRescale;
+        }
+        if (__any(grow)) {
+          float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+          mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+          mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+          const float m_new = fmaxf(m_run[nb], mx);
+          const float alpha = __builtin_amdgcn_exp2f(m_run[nb] - m_new);
+          l_run[nb] *= alpha;
+          m_run[nb] = m_new;
+#pragma unroll
+          for (int db = 0; db < 8; ++db) o[db][nb] *= alpha;
+        }
+        float pv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pv[i] = __builtin_amdgcn_exp2f(sv[i] - m_run[nb]);
+          l_run[nb] += pv[i];
+        }
+        const uint32_t p01 = pack_bf16x2(pv[0], pv[1]);
+        const uint32_t p23 = pack_bf16x2(pv[2], pv[3]);
+        pf[nb][0] = (short)(p01 & 0xffff);
+        pf[nb][1] = (short)(p01 >> 16);
+        pf[nb][2] = (short)(p23 & 0xffff);
+        pf[nb][3] = (short)(p23 >> 16);
+      }
+      // O^T += V^T . P^T
+      const char* sv_base = sb + v_base;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const int c = (2 * db + v_h) ^ v_x;
+        const s16x4_t cf = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4_t*)(sv_base + (c << 4)));
+#pragma unroll
+        for (int nb = 0; nb < NQB; ++nb)
+          o[db][nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(cf, pf[nb], o[db][nb], 0, 0, 0);
+      }
+    }
+  }
+
+  if (!wave_active) return;
+#pragma unroll
+  for (int nb = 0; nb < NQB; ++nb) {
+    float l = l_run[nb];
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    const float inv = 1.f / l;
+    const int qi = qw0 + 16 * nb + lr;
+    if (qi >= nq) continue;
+    bf16* dst = o_out + ((int64_t)(t0 + qi) * H + h) * DV + 4 * lg;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      uint2 pk;
+      pk.x = pack_bf16x2(o[db][nb][0] * inv, o[db][nb][1] * inv);
+      pk.y = pack_bf16x2(o[db][nb][2] * inv, o[db][nb][3] * inv);
+      *reinterpret_cast<uint2*>(dst + 16 * db) = pk;
+    }
+  }
+}
+
+}  // namespace pf
+
+int prefill_tile_queries() { return pf::NW * pf::QW; }
+
+void prefill_attn_mfma(const bf16* q_nope, const bf16* q_rope, const bf16* kv, const bf16* cache,
+                       const PrefillTile* tiles, int ntiles, int H, float scale, bf16* o,
+                       hipStream_t st) {
+  const int blocks = ntiles * ((H + pf::kXcds - 1) / pf::kXcds) * pf::kXcds;
+  pf::prefill_attn_mfma_k<<<blocks, 256, 0, st>>>(q_nope, q_rope, kv, cache, tiles, ntiles, H,
+                                                  scale * kLog2e, o);
+}
+
+}  // namespace mla

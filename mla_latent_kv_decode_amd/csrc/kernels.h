@@ -140,6 +140,20 @@ void decode_combine(const float* acc, const float* ml, const DecodeMeta& m, int 
                     const Dims& d, hipStream_t st);
 
 // ---- prefill attention (non-absorbed, causal)
+// One query tile of the MFMA prefill kernel: new tokens t0 .. t0+nq-1 of one
+// sequence at positions pos0 .. pos0+nq-1; the sequence's expanded rows start
+// at kv_row0 and its cache rows at cache_row0.
+struct PrefillTile {
+  int64_t kv_row0, cache_row0;
+  int32_t t0, nq, pos0, pad;
+};
+// queries per tile of prefill_attn_mfma
+int prefill_tile_queries();
+// MFMA version: bf16, qk_nope = v_head = 128, qk_rope = 64.  kv: expanded rows
+// (H x [K_nope | V]) in bf16; o: (T, H, 128); scale: softmax scale.
+void prefill_attn_mfma(const bf16* q_nope, const bf16* q_rope, const bf16* kv, const bf16* cache,
+                       const PrefillTile* tiles, int ntiles, int H, float scale, bf16* o,
+                       hipStream_t st);
 // kv: per sequence the expanded rows [K_nope_h | V_h] (fp32, row width H*(dn+dv)),
 // sequence b at row kv_off[b]; q_nope (T,H,dn), q_rope (T,H,dr) already rotated.
 template <typename T>

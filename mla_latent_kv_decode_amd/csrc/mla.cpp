@@ -999,7 +999,16 @@ int mla_decode_step(mla_handle h, const void* hidden, const int32_t* pos, const 
 namespace {
 struct PrefillLayout {
   size_t meta, scratch, pin, pq, cq, q_nope, q_rope, kv, o, total;
+  size_t meta_bytes, tiles_off;  // blob size and offset of the MFMA query tiles
 };
+
+// the MFMA prefill attention applies (bf16, 128 + 64 query/key dims, 128 values)
+bool prefill_mfma(const mla_ctx* h) {
+  const Dims& d = h->d;
+  return h->cfg.dtype == MLA_BF16 && d.dn == 128 && d.dr == 64 && d.dv == 128;
+}
+
+int max_prefill_tiles(int T, int B) { return T / mla::prefill_tile_queries() + B; }
 
 PrefillLayout prefill_layout(const mla_ctx* h, int T, int B, int64_t rows, int max_rows) {
   const Dims& d = h->d;
@@ -1011,7 +1020,9 @@ PrefillLayout prefill_layout(const mla_ctx* h, int T, int B, int64_t rows, int m
   const size_t pq = d.dq ? part_floats(h, T, qw, d.dq) : 0;
   const size_t e = h->esz;
   Carve c;
-  L.meta = c.take(align_up((size_t)T * 4) * 2 + align_up((size_t)B * 8) * 2);
+  L.tiles_off = align_up((size_t)T * 4) * 2 + align_up((size_t)B * 8) * 2;
+  L.meta_bytes = L.tiles_off + (size_t)max_prefill_tiles(T, B) * sizeof(mla::PrefillTile);
+  L.meta = c.take(L.meta_bytes);
   L.scratch = c.take(scr * 4);
   L.pin = c.take(pin * 4);
   L.pq = c.take(pq * 4);
@@ -1034,7 +1045,8 @@ size_t mla_prefill_workspace_bytes(mla_handle h, int32_t T, int32_t B, int64_t t
 template <typename T>
 static int run_prefill(mla_ctx* h, const T* hidden, int ntok, int B, const int32_t* cu_new,
                        const int32_t* prior, const int64_t* seq_off, const T* cache, T* out,
-                       void* ws, const PrefillLayout& L, const int64_t* kv_off_h) {
+                       void* ws, const PrefillLayout& L, const int64_t* kv_off_h,
+                       int ntiles) {
   const Dims& d = h->d;
   const int qw = qw_of(d);
   char* meta = at<char>(ws, L.meta);
@@ -1059,20 +1071,32 @@ static int run_prefill(mla_ctx* h, const T* hidden, int ntok, int B, const int32
   }
   mla::q_finish<T>(pq, ntok, tok_pos, q_nope, q_rope, (int64_t)d.H * d.dr, d.dr, 1.f, d, h->rope,
                    h->stream);
-  // expansion of every key row: [K_nope_h | V_h] = W_kvb c_t
-  float* kv = at<float>(ws, L.kv);
+  // expansion of every key row: [K_nope_h | V_h] = W_kvb c_t (bf16 for the
+  // MFMA attention, fp32 for the generic one)
+  bool mfma_attn = false;
+  if constexpr (sizeof(T) == 2) mfma_attn = prefill_mfma(h);
   const int wkv = d.H * (d.dn + d.dv);
   for (int b = 0; b < B; ++b) {
     const int rows = prior[b] + (cu_new[b + 1] - cu_new[b]);
     if (rows == 0) continue;
+    const int64_t o0 = kv_off_h[b] * (int64_t)wkv;
+    const mla::GemmOut go = mfma_attn ? out_t<T>(at<T>(ws, L.kv) + o0, wkv)
+                                      : out_f32(at<float>(ws, L.kv) + o0, wkv);
     gemm_out<T>(h, cache + seq_off[b] * d.R, d.R, 0, (const T*)h->w_kvb, d.dc, 0, rows, wkv, d.dc,
-                1, out_f32(kv + kv_off_h[b] * (int64_t)wkv, wkv), scratch);
+                1, go, scratch);
   }
   T* o = at<T>(ws, L.o);
   const int ts = timing_slot(h);
   if (ts >= 0) HIP_TRY(h, hipEventRecord(h->tev[2 * ts], h->stream));
-  mla::prefill_attn_generic<T>(q_nope, q_rope, kv, cache, tok_seq, tok_pos, kv_off, seq_off_d,
-                               ntok, o, d, h->stream);
+  if constexpr (sizeof(T) == 2) {
+    if (mfma_attn)
+      mla::prefill_attn_mfma(q_nope, q_rope, at<bf16>(ws, L.kv), cache,
+                             reinterpret_cast<const mla::PrefillTile*>(meta + L.tiles_off),
+                             ntiles, d.H, d.scale, o, h->stream);
+  }
+  if (!mfma_attn)
+    mla::prefill_attn_generic<T>(q_nope, q_rope, at<float>(ws, L.kv), cache, tok_seq, tok_pos,
+                                 kv_off, seq_off_d, ntok, o, d, h->stream);
   if (ts >= 0) HIP_TRY(h, hipEventRecord(h->tev[2 * ts + 1], h->stream));
   gemm_out<T>(h, o, (int64_t)d.H * d.dv, 0, (const T*)h->w_o, (int64_t)d.H * d.dv, 0, ntok, d.D,
               d.H * d.dv, 1, out_t<T>(out, d.D), scratch);
@@ -1100,7 +1124,7 @@ int mla_prefill(mla_handle h, const void* hidden, const int32_t* cu_new, const i
   if (rc) return rc;
   DeviceGuard g(h->device);
   if (!g.ok) return fail(h, MLA_ERR_HIP, "cannot select device %d", h->device);
-  std::vector<char> blob(align_up((size_t)T * 4) * 2 + align_up((size_t)B * 8) * 2, 0);
+  std::vector<char> blob(L.meta_bytes, 0);
   int32_t* tok_seq = reinterpret_cast<int32_t*>(blob.data());
   int32_t* tok_pos = reinterpret_cast<int32_t*>(blob.data() + align_up((size_t)T * 4));
   int64_t* kvo = reinterpret_cast<int64_t*>(blob.data() + 2 * align_up((size_t)T * 4));
@@ -1113,10 +1137,35 @@ int mla_prefill(mla_handle h, const void* hidden, const int32_t* cu_new, const i
     kvo[b] = kv_off[b];
     so[b] = seq_off[b];
   }
+  // query tiles of the MFMA attention, longest key range first
+  std::vector<mla::PrefillTile> tiles;
+  const int tq = mla::prefill_tile_queries();
+  for (int32_t b = 0; b < B; ++b) {
+    const int32_t n = cu_new[b + 1] - cu_new[b];
+    for (int32_t i = 0; i < n; i += tq) {
+      mla::PrefillTile t;
+      t.kv_row0 = kv_off[b];
+      t.cache_row0 = seq_off[b];
+      t.t0 = cu_new[b] + i;
+      t.nq = std::min(tq, n - i);
+      t.pos0 = prior_len[b] + i;
+      t.pad = 0;
+      tiles.push_back(t);
+    }
+  }
+  std::stable_sort(tiles.begin(), tiles.end(), [](const mla::PrefillTile& a,
+                                                  const mla::PrefillTile& b) {
+    return a.pos0 + a.nq > b.pos0 + b.nq;
+  });
+  if ((int)tiles.size() > max_prefill_tiles(T, B))
+    return fail(h, MLA_ERR_WORKSPACE, "internal: more prefill tiles than planned");
+  memcpy(blob.data() + L.tiles_off, tiles.data(), tiles.size() * sizeof(mla::PrefillTile));
   if ((rc = stage_upload(h, at<char>(ws, L.meta), blob.data(), blob.size()))) return rc;
   if (is_f32(h))
     return run_prefill<float>(h, (const float*)hidden, T, B, cu_new, prior_len, seq_off,
-                              (const float*)cache, (float*)out, ws, L, kv_off.data());
+                              (const float*)cache, (float*)out, ws, L, kv_off.data(),
+                              (int)tiles.size());
   return run_prefill<bf16>(h, (const bf16*)hidden, T, B, cu_new, prior_len, seq_off,
-                           (const bf16*)cache, (bf16*)out, ws, L, kv_off.data());
+                           (const bf16*)cache, (bf16*)out, ws, L, kv_off.data(),
+                           (int)tiles.size());
 }

@@ -51,5 +51,11 @@ def test_v2lite_prefill_small():
     run_prefill_case(synth.V2_LITE, "bf16", 0.02, [0, 37, 100], [40, 13, 1])
 
 
+def test_v2lite_prefill_multi_tile():
+    """Several 256-query tiles and 32-key tiles per sequence, ragged tails,
+    a 1-token chunk and a long prior."""
+    run_prefill_case(synth.V2_LITE, "bf16", 0.02, [0, 300, 33], [600, 70, 1])
+
+
 def test_v3_prefill_small():
     run_prefill_case(synth.V3, "bf16", 0.02, [0, 21], [24, 9])
