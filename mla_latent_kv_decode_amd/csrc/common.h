@@ -17,17 +17,18 @@ __device__ __forceinline__ float bf16_to_f32(bf16 v) {
   return __uint_as_float(((uint32_t)v) << 16);
 }
 
-// Round to nearest, ties to even (finite inputs; NaN stays NaN).
-__device__ __forceinline__ bf16 f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7f800000u) == 0x7f800000u) return (bf16)((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16)(u >> 16);
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed bf16 pair (lo in bits 0..15), rounded to nearest, ties
+// to even (one v_cvt_pk_bf16_f32 on gfx950; NaN stays NaN).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const bf16x2_t r = __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, r);
 }
 
-// Two floats -> packed bf16 pair (lo in bits 0..15).
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+__device__ __forceinline__ bf16 f32_to_bf16(float f) {
+  return (bf16)(pack_bf16x2(f, 0.f) & 0xffffu);
 }
 
 // Storage-type traits: float or bf16.

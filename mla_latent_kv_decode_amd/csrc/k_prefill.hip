@@ -8,17 +8,19 @@
 // rows 0..p of its sequence).  K_nope and V come from the expansion GEMM
 // (rows x H x [K_nope | V], bf16); k_rope is read from the latent cache row.
 //
-// Block = (tile of up to 256 new tokens of one sequence, head).  Wave w owns
-// queries 64w .. 64w+63 of the tile as 4 blocks of 16.  Keys stream in tiles of
+// Block = (tile of up to 128 new tokens of one sequence, head).  Wave w owns
+// queries 32w .. 32w+31 of the tile as 2 blocks of 16.  Every value of a wave
+// fits in 256 VGPRs (no accumulation registers), so two blocks share a
+// compute unit and one's softmax overlaps the other's MFMAs.  Keys stream in tiles of
 // 32 through a 4-stage LDS ring filled by global_load_lds_dwordx4 (each wave
 // issues a quarter of every tile; one barrier per tile both publishes the tile
 // and frees the stage the next prefetch overwrites).  Per 16-key block:
 //   S^T (16 keys x 16 queries) = K . Q^T  -- 6 x mfma 16x16x32 per query block,
-//       each K fragment (LDS) reused for the wave's 4 query blocks;
+//       each K fragment (LDS) reused for the wave's query blocks;
 //   online softmax per query with a lazily moved reference maximum;
-//   O^T (128 dims x 16 queries) += V^T . P^T -- mfma 16x16x16 with V^T read
-//       straight into operand layout by ds_read_b64_tr_b16, each fragment
-//       reused for the 4 query blocks.
+//   O (16 queries x 128 dims) += P . V -- mfma 16x16x16: P is the A operand
+//       exactly as S^T left it, V the B operand read straight into layout by
+//       ds_read_b64_tr_b16, each V fragment reused for the wave's query blocks.
 // Key blocks past a wave's last query are skipped (the causal diagonal).
 #include <utility>
 
@@ -30,7 +32,7 @@ namespace pf {
 constexpr int DN = 128, DR = 64, DV = 128;
 constexpr int KT = 32;                       // keys per tile
 constexpr int NW = 4;                        // waves per block
-constexpr int QW = 64;                       // queries per wave
+constexpr int QW = 32;                       // queries per wave
 constexpr int NQB = QW / 16;                 // 16-query blocks per wave
 constexpr int NST = 4;                       // LDS stages
 constexpr int KR_OFF = KT * DN * 2;          // K_nope: 256 B per key
@@ -114,7 +116,7 @@ __device__ __forceinline__ void issue_tile(const char* kvh, const char* rope, in
   }
 }
 
-__global__ void __launch_bounds__(256, 1)
+__global__ void __launch_bounds__(256, 2)
 prefill_attn_mfma_k(const bf16* __restrict__ q_nope, const bf16* __restrict__ q_rope,
                     const bf16* __restrict__ kv, const bf16* __restrict__ cache,
                     const PrefillTile* tiles, int ntiles, int H, float qk_scale,
@@ -150,6 +152,7 @@ prefill_attn_mfma_k(const bf16* __restrict__ q_nope, const bf16* __restrict__ q_
   const int qw0 = wave * QW;
   const bool wave_active = qw0 < nq;
   const int wmax_pos = pos0 + min(qw0 + QW, nq) - 1;
+  const int wmin_pos = pos0 + qw0;
   bf16x8_t qf[NQB][6];
   int qpos[NQB];
 #pragma unroll
@@ -179,7 +182,7 @@ prefill_attn_mfma_k(const bf16* __restrict__ q_nope, const bf16* __restrict__ q_
   const int v_h = (lr & 3) >> 1, v_x = 2 * (vr & 7);
 
   float m_run[NQB], l_run[NQB];
-  f32x4_t o[8][NQB];  // o[db][nb][i]: dim 16 db + 4 lg + i of query 16 nb + lr
+  f32x4_t o[8][NQB];  // o[db][nb][i]: query 16 nb + 4 lg + i, dim 16 db + lr
 #pragma unroll
   for (int nb = 0; nb < NQB; ++nb) {
     m_run[nb] = -INFINITY;
@@ -222,19 +225,30 @@ prefill_attn_mfma_k(const bf16* __restrict__ q_nope, const bf16* __restrict__ q_
         for (int s = 0; s < 6; ++s)
           sacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], qf[nb][s], sacc[nb], 0, 0, 0);
       }
-      // softmax: lane holds keys kb0 + 4 lg + i of query 16 nb + lr
+      // softmax: lane holds keys kb0 + 4 lg + i of query 16 nb + lr.  In log2
+      // units t = s * scale - m_run; the reference maximum m_run only moves
+      // when some t exceeds kRescale (a wave vote), so p = 2^t <= 2^kRescale.
+      // The causal mask is applied only to blocks that reach past the
+      // wave's first query.
+      const bool diag = kb0 + 15 > wmin_pos;
       s16x4_t pf[NQB];
 #pragma unroll
       for (int nb = 0; nb < NQB; ++nb) {
-        float sv[4];
+        float t[4];
         bool grow = false;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const bool valid = kb0 + 4 * lg + i <= qpos[nb];
-          sv[i] = valid ? sacc[nb][i] * qk_scale : -INFINITY;
-          grow |= sv[i] > m_run[nb] + kRescale;
+          t[i] = fmaf(sacc[nb][i], qk_scale, -m_run[nb]);
+          if (diag && kb0 + 4 * lg + i > qpos[nb]) t[i] = -INFINITY;
+          grow |= t[i] > kRescale;
         }
         if (__any(grow)) {
+          float sv[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const bool valid = !diag || kb0 + 4 * lg + i <= qpos[nb];
+            sv[i] = valid ? sacc[nb][i] * qk_scale : -INFINITY;
+          }
           float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
           mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
           mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
@@ -244,11 +258,13 @@ prefill_attn_mfma_k(const bf16* __restrict__ q_nope, const bf16* __restrict__ q_
           m_run[nb] = m_new;
 #pragma unroll
           for (int db = 0; db < 8; ++db) o[db][nb] *= alpha;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) t[i] = sv[i] - m_new;
         }
         float pv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          pv[i] = __builtin_amdgcn_exp2f(sv[i] - m_run[nb]);
+          pv[i] = __builtin_amdgcn_exp2f(t[i]);
           l_run[nb] += pv[i];
         }
         const uint32_t p01 = pack_bf16x2(pv[0], pv[1]);
@@ -258,7 +274,7 @@ prefill_attn_mfma_k(const bf16* __restrict__ q_nope, const bf16* __restrict__ q_
         pf[nb][2] = (short)(p23 & 0xffff);
         pf[nb][3] = (short)(p23 >> 16);
       }
-      // O^T += V^T . P^T
+      // O += P . V
       const char* sv_base = sb + v_base;
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
@@ -267,7 +283,7 @@ prefill_attn_mfma_k(const bf16* __restrict__ q_nope, const bf16* __restrict__ q_
             (__attribute__((address_space(3))) s16x4_t*)(sv_base + (c << 4)));
 #pragma unroll
         for (int nb = 0; nb < NQB; ++nb)
-          o[db][nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(cf, pf[nb], o[db][nb], 0, 0, 0);
+          o[db][nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pf[nb], cf, o[db][nb], 0, 0, 0);
       }
     }
   }
@@ -275,19 +291,20 @@ prefill_attn_mfma_k(const bf16* __restrict__ q_nope, const bf16* __restrict__ q_
   if (!wave_active) return;
 #pragma unroll
   for (int nb = 0; nb < NQB; ++nb) {
+    // after the reduction every lane (lr, *) holds the sum of query lr
     float l = l_run[nb];
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
-    const float inv = 1.f / l;
-    const int qi = qw0 + 16 * nb + lr;
-    if (qi >= nq) continue;
-    bf16* dst = o_out + ((int64_t)(t0 + qi) * H + h) * DV + 4 * lg;
+    float inv[4];
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      uint2 pk;
-      pk.x = pack_bf16x2(o[db][nb][0] * inv, o[db][nb][1] * inv);
-      pk.y = pack_bf16x2(o[db][nb][2] * inv, o[db][nb][3] * inv);
-      *reinterpret_cast<uint2*>(dst + 16 * db) = pk;
+    for (int i = 0; i < 4; ++i) inv[i] = 1.f / __shfl(l, 4 * lg + i, 64);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int qi = qw0 + 16 * nb + 4 * lg + i;
+      if (qi >= nq) continue;
+      bf16* dst = o_out + ((int64_t)(t0 + qi) * H + h) * DV + lr;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) dst[16 * db] = f32_to_bf16(o[db][nb][i] * inv[i]);
     }
   }
 }
