@@ -6,6 +6,7 @@
 // memory the handle owns (a small ring, so a call never overwrites staging
 // data an earlier asynchronous copy may still be reading).
 #include <hip/hip_runtime.h>
+#include <rocblas/rocblas.h>
 
 #include <math.h>
 #include <stdarg.h>
@@ -76,6 +77,12 @@ struct mla_ctx {
   std::vector<hipEvent_t> tev;
   int t_next = 0;
   int64_t t_count = 0;
+  // library GEMM (rocBLAS) for the large-M projections of prefill; created on
+  // first use.  lib_gemm_ok is set only while a prefill call runs, so decode
+  // calls (which callers capture into graphs) never reach it.
+  rocblas_handle rb = nullptr;
+  bool lib_gemm_ok = false;
+  int lib_err = 0;
   std::string err;
 };
 
@@ -115,6 +122,11 @@ struct DeviceGuard {
 };
 
 int check_launch(mla_ctx* h, const char* what) {
+  if (h->lib_err) {
+    const int le = h->lib_err;
+    h->lib_err = 0;
+    return fail(h, MLA_ERR_HIP, "%s: rocBLAS GEMM failed (status %d)", what, le);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(h, MLA_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
   return MLA_OK;
@@ -175,12 +187,54 @@ bool mfma_gemm(const mla_ctx* h, int N, int K) {
   return h->cfg.dtype == MLA_BF16 && N % 16 == 0 && K % 128 == 0;
 }
 
+// Projections with many rows (prefill) are plain GEMMs with enough work for a
+// library kernel's large tiles: rocBLAS, bf16 in, fp32 accumulation.
+constexpr int kLibGemmMinM = 256;
+bool lib_gemm(const mla_ctx* h, int M) {
+  return h->lib_gemm_ok && h->cfg.dtype == MLA_BF16 && M >= kLibGemmMinM;
+}
+
 int gemm_ks(const mla_ctx* h, int M, int N, int K, int batch) {
+  if (lib_gemm(h, M)) return 1;
   return mfma_gemm(h, N, K) ? mla::gemm_bf16_ksplit(M, N, K, batch, h->n_cu) : 1;
+}
+
+// Enables the library GEMM for the duration of a call (prefill, bulk append).
+struct LibGemmScope {
+  mla_ctx* h;
+  explicit LibGemmScope(mla_ctx* c) : h(c) { h->lib_gemm_ok = true; }
+  ~LibGemmScope() { h->lib_gemm_ok = false; }
+};
+
+// C (row-major M x N, row stride out.ldo) = alpha A W^T with A (M x K, lda) and
+// W (N x K, ldw) row-major: in rocBLAS's column-major terms C^T = W^T-op(W) A.
+void rocblas_out(mla_ctx* h, const bf16* A, int64_t lda, int64_t sA, const bf16* W, int64_t ldw,
+                 int64_t sW, int M, int N, int K, int batch, const mla::GemmOut& out) {
+  rocblas_status st = rocblas_status_success;
+  if (!h->rb) st = rocblas_create_handle(&h->rb);
+  if (st == rocblas_status_success) st = rocblas_set_stream(h->rb, h->stream);
+  const float alpha = out.alpha, beta = 0.f;
+  void* c = out.f32 ? (void*)out.f32 : (void*)out.b16;
+  const rocblas_datatype ct = out.f32 ? rocblas_datatype_f32_r : rocblas_datatype_bf16_r;
+  if (st == rocblas_status_success) {
+    if (batch == 1)
+      st = rocblas_gemm_ex(h->rb, rocblas_operation_transpose, rocblas_operation_none, N, M, K,
+                           &alpha, W, rocblas_datatype_bf16_r, ldw, A, rocblas_datatype_bf16_r,
+                           lda, &beta, c, ct, out.ldo, c, ct, out.ldo, rocblas_datatype_f32_r,
+                           rocblas_gemm_algo_standard, 0, 0);
+    else
+      st = rocblas_gemm_strided_batched_ex(
+          h->rb, rocblas_operation_transpose, rocblas_operation_none, N, M, K, &alpha, W,
+          rocblas_datatype_bf16_r, ldw, sW, A, rocblas_datatype_bf16_r, lda, sA, &beta, c, ct,
+          out.ldo, out.so, c, ct, out.ldo, out.so, batch, rocblas_datatype_f32_r,
+          rocblas_gemm_algo_standard, 0, 0);
+  }
+  if (st != rocblas_status_success && !h->lib_err) h->lib_err = (int)st;
 }
 
 // fp32 scratch floats of gemm_out (split-K partials, or the VALU path's C)
 size_t out_scratch(const mla_ctx* h, int M, int N, int K, int batch) {
+  if (lib_gemm(h, M)) return 0;
   const int ks = gemm_ks(h, M, N, K, batch);
   if (mfma_gemm(h, N, K) && ks == 1) return 0;
   return (size_t)ks * batch * M * N;
@@ -193,10 +247,14 @@ size_t part_floats(const mla_ctx* h, int M, int N, int K) {
 // out = alpha * A W^T (batched, strided).  MFMA path: epilogue fused when K is
 // not split, else partials in `scratch` and a store kernel sums them.
 template <typename T>
-void gemm_out(const mla_ctx* h, const T* A, int64_t lda, int64_t sA, const T* W, int64_t ldw,
+void gemm_out(mla_ctx* h, const T* A, int64_t lda, int64_t sA, const T* W, int64_t ldw,
               int64_t sW, int M, int N, int K, int batch, const mla::GemmOut& out,
               float* scratch) {
   if constexpr (sizeof(T) == 2) {
+    if (lib_gemm(h, M)) {
+      rocblas_out(h, A, lda, sA, W, ldw, sW, M, N, K, batch, out);
+      return;
+    }
     if (mfma_gemm(h, N, K)) {
       const int ks = gemm_ks(h, M, N, K, batch);
       mla::gemm_bf16_mfma(A, lda, sA, W, ldw, sW, M, N, K, batch, ks, scratch, out, h->stream);
@@ -211,9 +269,13 @@ void gemm_out(const mla_ctx* h, const T* A, int64_t lda, int64_t sA, const T* W,
 // A W^T (batch 1) left as fp32 split-K partials in `part` for the consuming
 // kernel to sum (part_floats() floats).
 template <typename T>
-mla::Part gemm_part(const mla_ctx* h, const T* A, int64_t lda, const T* W, int64_t ldw, int M,
+mla::Part gemm_part(mla_ctx* h, const T* A, int64_t lda, const T* W, int64_t ldw, int M,
                     int N, int K, float* part) {
   if constexpr (sizeof(T) == 2) {
+    if (lib_gemm(h, M)) {
+      rocblas_out(h, A, lda, 0, W, ldw, 0, M, N, K, 1, mla::GemmOut{part, nullptr, N, 0, 1.f});
+      return mla::Part{part, 1, N, (int64_t)M * N};
+    }
     if (mfma_gemm(h, N, K)) {
       const int ks = gemm_ks(h, M, N, K, 1);
       mla::gemm_bf16_mfma(A, lda, 0, W, ldw, 0, M, N, K, 1, ks, part,
@@ -612,6 +674,7 @@ int mla_destroy(mla_handle h) {
   }
   for (void* p : h->captured) (void)hipHostFree(p);
   drop_timing(h);
+  if (h->rb) (void)rocblas_destroy_handle(h->rb);
   delete h;
   return MLA_OK;
 }
@@ -1049,6 +1112,7 @@ static int run_prefill(mla_ctx* h, const T* hidden, int ntok, int B, const int32
                        int ntiles) {
   const Dims& d = h->d;
   const int qw = qw_of(d);
+  LibGemmScope lib_scope(h);
   char* meta = at<char>(ws, L.meta);
   const int32_t* tok_seq = reinterpret_cast<const int32_t*>(meta);
   const int32_t* tok_pos = reinterpret_cast<const int32_t*>(meta + align_up((size_t)ntok * 4));
