@@ -142,6 +142,34 @@ __device__ __forceinline__ void rope_pair(float u, float v, int pos, double thet
   *ov = u * sf + v * cf;
 }
 
+// In-place RoPE of the rope part of every head of q (bf16 rows of H * (dn + dr)
+// elements: per head [q_nope | q_rope]) at each token's position ("Multi-Head
+// Latent Attention" post, section 3.7: RoPE is applied per head to the decoupled
+// query part).  One thread per (token, head, pair).
+__global__ void __launch_bounds__(256)
+rope_q_inplace_k(bf16* __restrict__ q, int ntok, int H, int dn, int dr,
+                 const int32_t* __restrict__ pos, RopeTab rt) {
+  const int npair = dr / 2;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)ntok * H * npair) return;
+  const int k = (int)(i % npair);
+  const int64_t th = i / npair;  // token * H + head
+  const int t = (int)(th / H);
+  bf16* e = q + th * (dn + dr) + dn + 2 * k;
+  const uint32_t uv = *reinterpret_cast<const uint32_t*>(e);
+  float ou, ov;
+  rope_pair(bf16_to_f32((bf16)(uv & 0xffff)), bf16_to_f32((bf16)(uv >> 16)), pos[t], rt.theta[k],
+            &ou, &ov);
+  *reinterpret_cast<uint32_t*>(e) = pack_bf16x2(ou, ov);
+}
+
+void rope_q_inplace(bf16* q, int ntok, const int32_t* pos, const Dims& d, const RopeTab& rt,
+                    hipStream_t st) {
+  const int64_t n = (int64_t)ntok * d.H * (d.dr / 2);
+  if (n == 0) return;
+  rope_q_inplace_k<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(q, ntok, d.H, d.dn, d.dr, pos, rt);
+}
+
 // Latent row of token t ("Deepseek V2 Lite Inference Engine in C", MLA notes:
 // kv_a_proj gives [latent | rope key]; the latent is RMS-normalised and the key
 // rotated; then the row is written to its cache slot).  One block per token.

@@ -117,8 +117,8 @@ __device__ __forceinline__ void issue_tile(const char* kvh, const char* rope, in
 }
 
 __global__ void __launch_bounds__(256, 2)
-prefill_attn_mfma_k(const bf16* __restrict__ q_nope, const bf16* __restrict__ q_rope,
-                    const bf16* __restrict__ kv, const bf16* __restrict__ cache,
+prefill_attn_mfma_k(const bf16* __restrict__ q, const bf16* __restrict__ kv,
+                    const bf16* __restrict__ cache,
                     const PrefillTile* tiles, int ntiles, int H, float qk_scale,
                     bf16* __restrict__ o_out) {
   __shared__ __attribute__((aligned(1024))) char lds[NST * ST_BYTES];
@@ -159,8 +159,8 @@ prefill_attn_mfma_k(const bf16* __restrict__ q_nope, const bf16* __restrict__ q_
   for (int nb = 0; nb < NQB; ++nb) {
     const int qi = min(qw0 + 16 * nb + lr, nq - 1);
     qpos[nb] = pos0 + qi;
-    const bf16* qn = q_nope + ((int64_t)(t0 + qi) * H + h) * DN + 8 * lg;
-    const bf16* qr = q_rope + ((int64_t)(t0 + qi) * H + h) * DR + 8 * lg;
+    const bf16* qn = q + ((int64_t)(t0 + qi) * H + h) * (DN + DR) + 8 * lg;
+    const bf16* qr = qn + DN;
 #pragma unroll
     for (int s = 0; s < 4; ++s) qf[nb][s] = *reinterpret_cast<const bf16x8_t*>(qn + 32 * s);
 #pragma unroll
@@ -313,11 +313,11 @@ prefill_attn_mfma_k(const bf16* __restrict__ q_nope, const bf16* __restrict__ q_
 
 int prefill_tile_queries() { return pf::NW * pf::QW; }
 
-void prefill_attn_mfma(const bf16* q_nope, const bf16* q_rope, const bf16* kv, const bf16* cache,
+void prefill_attn_mfma(const bf16* q, const bf16* kv, const bf16* cache,
                        const PrefillTile* tiles, int ntiles, int H, float scale, bf16* o,
                        hipStream_t st) {
   const int blocks = ntiles * ((H + pf::kXcds - 1) / pf::kXcds) * pf::kXcds;
-  pf::prefill_attn_mfma_k<<<blocks, 256, 0, st>>>(q_nope, q_rope, kv, cache, tiles, ntiles, H,
+  pf::prefill_attn_mfma_k<<<blocks, 256, 0, st>>>(q, kv, cache, tiles, ntiles, H,
                                                   scale * kLog2e, o);
 }
 

@@ -105,6 +105,9 @@ template <typename T>
 void q_finish(const Part& q, int ntok, const int32_t* pos, T* q_nope, T* rope_out,
               int64_t tok_stride, int64_t head_stride, float scale, const Dims& d,
               const RopeTab& rt, hipStream_t st);
+// RoPE in place on the rope part of q (ntok, H, dn + dr) bf16
+void rope_q_inplace(bf16* q, int ntok, const int32_t* pos, const Dims& d, const RopeTab& rt,
+                    hipStream_t st);
 // append_rows on columns [0, R) and q_finish on columns [R, R + H(dn+dr)) of
 // one fused in-projection, one block per token
 template <typename T>
@@ -149,9 +152,10 @@ struct PrefillTile {
 };
 // queries per tile of prefill_attn_mfma
 int prefill_tile_queries();
-// MFMA version: bf16, qk_nope = v_head = 128, qk_rope = 64.  kv: expanded rows
-// (H x [K_nope | V]) in bf16; o: (T, H, 128); scale: softmax scale.
-void prefill_attn_mfma(const bf16* q_nope, const bf16* q_rope, const bf16* kv, const bf16* cache,
+// MFMA version: bf16, qk_nope = v_head = 128, qk_rope = 64.  q: (T, H, 192)
+// rows [q_nope | rotated q_rope]; kv: expanded rows (H x [K_nope | V]) in bf16;
+// o: (T, H, 128); scale: softmax scale.
+void prefill_attn_mfma(const bf16* q, const bf16* kv, const bf16* cache,
                        const PrefillTile* tiles, int ntiles, int H, float scale, bf16* o,
                        hipStream_t st);
 // kv: per sequence the expanded rows [K_nope_h | V_h] (fp32, row width H*(dn+dv)),

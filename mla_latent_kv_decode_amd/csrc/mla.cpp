@@ -1077,8 +1077,9 @@ PrefillLayout prefill_layout(const mla_ctx* h, int T, int B, int64_t rows, int m
   const Dims& d = h->d;
   PrefillLayout L;
   const int qw = qw_of(d);
-  const size_t scr = std::max(out_scratch(h, T, d.D, d.H * d.dv, 1),
-                              out_scratch(h, max_rows, d.H * (d.dn + d.dv), d.dc, 1));
+  const size_t scr = std::max({out_scratch(h, T, d.D, d.H * d.dv, 1),
+                               out_scratch(h, max_rows, d.H * (d.dn + d.dv), d.dc, 1),
+                               out_scratch(h, T, qw, d.dq ? d.dq : d.D, 1)});
   const size_t pin = part_floats(h, T, d.dq ? d.dq : qw, d.D);
   const size_t pq = d.dq ? part_floats(h, T, qw, d.dq) : 0;
   const size_t e = h->esz;
@@ -1090,7 +1091,8 @@ PrefillLayout prefill_layout(const mla_ctx* h, int T, int B, int64_t rows, int m
   L.pin = c.take(pin * 4);
   L.pq = c.take(pq * 4);
   L.cq = c.take(d.dq ? (size_t)T * d.dq * e : 0);
-  L.q_nope = c.take((size_t)T * d.H * d.dn * e);
+  // q_nope (generic path), or the whole (T, H, dn + dr) query (MFMA path)
+  L.q_nope = c.take((size_t)T * d.H * (d.dn + d.dr) * e);
   L.q_rope = c.take((size_t)T * d.H * std::max(d.dr, 1) * e);
   L.kv = c.take((size_t)rows * d.H * (d.dn + d.dv) * 4);
   L.o = c.take((size_t)T * d.H * d.dv * e);
@@ -1122,23 +1124,34 @@ static int run_prefill(mla_ctx* h, const T* hidden, int ntok, int B, const int32
   float* scratch = at<float>(ws, L.scratch);
   T* q_nope = at<T>(ws, L.q_nope);
   T* q_rope = at<T>(ws, L.q_rope);
-  mla::Part pq;
+  bool mfma_attn = false;
+  if constexpr (sizeof(T) == 2) mfma_attn = prefill_mfma(h);
+  // query (A3): c_q = RMSNorm(W_qa x) for a query LoRA
+  const T* qin = hidden;
+  int qk = d.D;
+  const T* wq = (const T*)h->w_q;
   if (d.dq) {
     const mla::Part pa = gemm_part<T>(h, hidden, d.D, (const T*)h->w_qa, d.D, ntok, d.dq, d.D,
                                       at<float>(ws, L.pin));
     mla::rmsnorm_rows<T>(pa, ntok, d.dq, (const T*)h->q_norm_g, d.eps, at<T>(ws, L.cq),
                          h->stream);
-    pq = gemm_part<T>(h, at<T>(ws, L.cq), d.dq, (const T*)h->w_qb, d.dq, ntok, qw, d.dq,
-                      at<float>(ws, L.pq));
-  } else {
-    pq = gemm_part<T>(h, hidden, d.D, (const T*)h->w_q, d.D, ntok, qw, d.D, at<float>(ws, L.pin));
+    qin = at<T>(ws, L.cq);
+    qk = d.dq;
+    wq = (const T*)h->w_qb;
   }
-  mla::q_finish<T>(pq, ntok, tok_pos, q_nope, q_rope, (int64_t)d.H * d.dr, d.dr, 1.f, d, h->rope,
-                   h->stream);
+  if (mfma_attn) {
+    // the projection writes the bf16 query rows (T, H, dn + dr) directly; the
+    // rope parts are then rotated in place
+    gemm_out<T>(h, qin, qk, 0, wq, qk, 0, ntok, qw, qk, 1, out_t<T>(q_nope, qw), scratch);
+    if constexpr (sizeof(T) == 2) mla::rope_q_inplace(q_nope, ntok, tok_pos, d, h->rope, h->stream);
+  } else {
+    const mla::Part pq = gemm_part<T>(h, qin, qk, wq, qk, ntok, qw, qk,
+                                      at<float>(ws, d.dq ? L.pq : L.pin));
+    mla::q_finish<T>(pq, ntok, tok_pos, q_nope, q_rope, (int64_t)d.H * d.dr, d.dr, 1.f, d,
+                     h->rope, h->stream);
+  }
   // expansion of every key row: [K_nope_h | V_h] = W_kvb c_t (bf16 for the
   // MFMA attention, fp32 for the generic one)
-  bool mfma_attn = false;
-  if constexpr (sizeof(T) == 2) mfma_attn = prefill_mfma(h);
   const int wkv = d.H * (d.dn + d.dv);
   for (int b = 0; b < B; ++b) {
     const int rows = prior[b] + (cu_new[b + 1] - cu_new[b]);
@@ -1154,7 +1167,7 @@ static int run_prefill(mla_ctx* h, const T* hidden, int ntok, int B, const int32
   if (ts >= 0) HIP_TRY(h, hipEventRecord(h->tev[2 * ts], h->stream));
   if constexpr (sizeof(T) == 2) {
     if (mfma_attn)
-      mla::prefill_attn_mfma(q_nope, q_rope, at<bf16>(ws, L.kv), cache,
+      mla::prefill_attn_mfma(q_nope, at<bf16>(ws, L.kv), cache,
                              reinterpret_cast<const mla::PrefillTile*>(meta + L.tiles_off),
                              ntiles, d.H, d.scale, o, h->stream);
   }
