@@ -1,0 +1,304 @@
+// Split-S latent attention core for many heads: 64 heads per workgroup.
+//
+// Same computation as the 16-head core (absorbed decode, "Multi-Head Latent
+// Attention" post, sections 3.3 and 3.6: scores of every head against the
+// whole 576-wide latent row, softmax, latent sum of the 512 c_kv columns), for
+// layers with many heads (DeepSeek-V3: 128), where the work per latent row is
+// 8x larger and the 16-head kernel's per-head-group workgroups would stream
+// every row 8 times from L2.  Here one workgroup of 4 waves covers 64 heads
+// (wave w owns the 16-head group w; the per-wave state of one group, its
+// accumulators and query fragments, is what the register file holds), and the
+// two workgroups of a part run on one XCD.  The rows of a segment stream once
+// per workgroup through a 4-stage ring of 32-row tiles
+// shared by the waves (global_load_lds_dwordx4; each wave issues a quarter of
+// every tile; one barrier per tile publishes it and frees the stage the next
+// prefetch overwrites).  Each wave sees every row of the segment for its own
+// heads, so its (max, sum, acc) state is the segment's partial: no cross-wave
+// merge.  MFMA operand layouts, the LDS swizzle of a 16-row block and the lazy
+// rescale are those of the 16-head core.
+#include <utility>
+
+#include "kernels.h"
+
+namespace mla {
+namespace decw {
+
+constexpr int DC = 512;
+constexpr int RW = 576;
+constexpr int NW = 4;                         // waves
+constexpr int G = 1;                          // 16-head groups per wave
+constexpr int HEADS = 16 * G * NW;            // heads per workgroup
+constexpr int TR = 32;                        // rows per tile
+constexpr int NST = 4;                        // stages
+constexpr int ROPE_OFF = TR * 1024;           // latent of row r at r*1024, rope after
+constexpr int ST_BYTES = TR * RW * 2;         // 36 KB
+constexpr int NLOAD = TR + TR / 8;            // 36 wave-wide 16-byte loads per tile
+constexpr int LPW = NLOAD / NW;               // 9 per wave
+constexpr float kRescale = 8.0f;
+constexpr int kXcds = 8;
+static_assert(NLOAD % NW == 0 && NW == 4, "tile loads split evenly over 4 waves");
+static_assert(ROPE_OFF + TR * 128 == ST_BYTES, "stage layout");
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef const __attribute__((address_space(4))) DecodeWork* ConstWorkPtr;
+
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(lds_addr)
+               : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+__device__ __forceinline__ DecodeWork load_work(ConstWorkPtr p) {
+  DecodeWork w;
+  w.row = p->row;
+  w.n = p->n;
+  w.b = p->b;
+  w.pidx = p->pidx;
+  w.next = p->next;
+  return w;
+}
+
+// Load I of a tile whose first row is at `base` and whose last valid row is
+// `last`: I < 32 copies the latent part of row I (source chunk lane ^ (I & 7)),
+// I >= 32 the rope parts of rows 8j .. 8j+7.  Rows past `last` re-read it.
+template <int I>
+__device__ __forceinline__ void tile_load(const char* base, int last, uint32_t stage, int lane) {
+  if constexpr (I < TR) {
+    const int r = I <= last ? I : last;
+    dma16(base + r * (RW * 2) + ((lane ^ (I & 7)) << 4), stage + I * 1024);
+  } else {
+    constexpr int J = I - TR;
+    int r = 8 * J + (lane >> 3);
+    r = r <= last ? r : last;
+    const int cc = (lane & 7) ^ (lane >> 3);
+    dma16(base + r * (RW * 2) + 1024 + (cc << 4), stage + ROPE_OFF + J * 1024);
+  }
+}
+
+template <int W, int... U>
+__device__ __forceinline__ void wave_loads(const char* base, int last, uint32_t stage, int lane,
+                                           std::integer_sequence<int, U...>) {
+  (tile_load<W * LPW + U>(base, last, stage, lane), ...);
+}
+
+__device__ __forceinline__ void issue_tile(const char* base, int last, uint32_t stage, int wave,
+                                           int lane) {
+  const auto seq = std::make_integer_sequence<int, LPW>{};
+  switch (wave) {
+    case 0: wave_loads<0>(base, last, stage, lane, seq); break;
+    case 1: wave_loads<1>(base, last, stage, lane, seq); break;
+    case 2: wave_loads<2>(base, last, stage, lane, seq); break;
+    default: wave_loads<3>(base, last, stage, lane, seq); break;
+  }
+}
+
+__global__ void __launch_bounds__(256, 1)
+decode_core_wide_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cache, DecodeMeta mt,
+                   float* __restrict__ acc_out, float* __restrict__ ml_out, int H, int nparts) {
+  __shared__ __attribute__((aligned(1024))) char lds[NST * ST_BYTES];
+  // block -> (part, 64-head block), the head blocks of a part on one XCD
+  const int WG = H / HEADS;
+  const int bid = blockIdx.x;
+  const int part = (bid / (kXcds * WG)) * kXcds + bid % kXcds;
+  const int hb = (bid / kXcds) % WG;
+  if (part >= nparts) return;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int h0 = hb * HEADS + wave * 16 * G;  // group g: heads h0 + 16g .. h0 + 16g + 15
+  const uint32_t lds0 = lds_u32(lds);
+
+  // operand offsets inside a 16-row block (as in the 16-head core)
+  const int qk_b = (lr >> 2) & 1;
+  const int qk_lo = (lg ^ (lr & 3)) * 16;
+  const int qk_base0 = lr * 1024 + 64 * qk_b + qk_lo;
+  const int qk_base1 = lr * 1024 + 64 * (qk_b ^ 1) + qk_lo;
+  const int qk_rope0 = ROPE_OFF + lr * 128 + 64 * qk_b + qk_lo;
+  const int qk_rope1 = ROPE_OFF + lr * 128 + 64 * (qk_b ^ 1) + qk_lo;
+  int pv_off[4];
+  {
+    const int r = 4 * lg + (lr >> 2);
+    const int x = r & 7, y = x >> 1, hh = ((lr & 3) >> 1) ^ (x & 1);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) pv_off[t] = r * 1024 + 8 * (lr & 1) + 16 * hh + 32 * (t ^ y);
+  }
+
+  const ConstWorkPtr works = reinterpret_cast<ConstWorkPtr>((uintptr_t)mt.work);
+  DecodeWork wk = load_work(works + part);
+  for (;;) {
+    const int n = wk.n;
+    const int ntile = (n + TR - 1) / TR;
+    const char* rows = reinterpret_cast<const char*>(cache + wk.row * (int64_t)RW);
+#pragma unroll
+    for (int t = 0; t < NST - 1; ++t)
+      if (t < ntile)
+        issue_tile(rows + t * TR * (RW * 2), n - t * TR - 1, lds0 + t * ST_BYTES, wave, lane);
+    DecodeWork nx = wk;
+    if (wk.next >= 0) nx = load_work(works + wk.next);
+
+    // Q^T fragments of heads h0 + 16g + lr: columns 32 s + 8 lg .. + 7
+    bf16x8_t qf[G][18];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const bf16* qrow = q_cat + ((int64_t)wk.b * H + h0 + 16 * g + lr) * RW + lg * 8;
+#pragma unroll
+      for (int s = 0; s < 18; ++s) qf[g][s] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * s);
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int s = 0; s < 18; ++s) asm volatile("" ::"v"(qf[g][s]));
+
+    float m_run[G], l_run[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      m_run[g] = -INFINITY;
+      l_run[g] = 0.f;
+    }
+    f32x4_t o[G][32];  // o[g][cb][i]: head h0 + 16g + lr, column 16 cb + 4 lg + i
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int cb = 0; cb < 32; ++cb) o[g][cb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+
+    for (int t = 0; t < ntile; ++t) {
+      static_assert(NST == 4, "wait counts below assume 4 stages");
+      if (t + 2 < ntile) wait_vmcnt<2 * LPW>();
+      else if (t + 1 < ntile) wait_vmcnt<LPW>();
+      else wait_vmcnt<0>();
+      __syncthreads();  // tile t is in LDS; every wave is done with tile t-1
+      if (t + NST - 1 < ntile)
+        issue_tile(rows + (t + NST - 1) * TR * (RW * 2), n - (t + NST - 1) * TR - 1,
+                   lds0 + ((t + NST - 1) % NST) * ST_BYTES, wave, lane);
+      const char* st = lds + (t % NST) * ST_BYTES;
+#pragma unroll 1
+      for (int rb = 0; rb < TR / 16; ++rb) {
+        const int row0 = t * TR + 16 * rb;
+        if (row0 >= n) break;
+        const char* sl = st + rb * 16 * 1024;  // latent rows of this block
+        const char* sr = st + rb * 16 * 128;   // rope rows (offsets include ROPE_OFF)
+        // ---- S^T = K . Q^T for both head groups, K fragments read once
+        f32x4_t sa[G], sb[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) sa[g] = sb[g] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          bf16x8_t kf[9];
+#pragma unroll
+          for (int u = 0; u < 9; ++u) {
+            const int s = 9 * half + u;
+            if (s < 16)
+              kf[u] = *reinterpret_cast<const bf16x8_t*>(sl + ((s & 1) ? qk_base1 : qk_base0) +
+                                                         128 * (s >> 1));
+            else
+              kf[u] = *reinterpret_cast<const bf16x8_t*>(sr + (s == 16 ? qk_rope0 : qk_rope1));
+          }
+#pragma unroll
+          for (int u = 0; u < 9; ++u) {
+            const int s = 9 * half + u;
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+              if (s & 1)
+                sb[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[u], qf[g][s], sb[g], 0, 0, 0);
+              else
+                sa[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[u], qf[g][s], sa[g], 0, 0, 0);
+            }
+          }
+        }
+        // ---- online softmax per head group (lazy reference maximum)
+        s16x4_t pf[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const f32x4_t sacc = sa[g] + sb[g];
+          float sv[4];
+          bool grow = false;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const bool valid = row0 + 4 * lg + i < n;
+            sv[i] = valid ? sacc[i] * kLog2e : -INFINITY;
+            grow |= sv[i] > m_run[g] + kRescale;
+          }
+          if (__any(grow)) {
+            float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            const float m_new = fmaxf(m_run[g], mx);
+            const float alpha = __builtin_amdgcn_exp2f(m_run[g] - m_new);
+            l_run[g] *= alpha;
+            m_run[g] = m_new;
+#pragma unroll
+            for (int cb = 0; cb < 32; ++cb) o[g][cb] *= alpha;
+          }
+          float pv[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            pv[i] = __builtin_amdgcn_exp2f(sv[i] - m_run[g]);
+            l_run[g] += pv[i];
+          }
+          const uint32_t p01 = pack_bf16x2(pv[0], pv[1]);
+          const uint32_t p23 = pack_bf16x2(pv[2], pv[3]);
+          pf[g][0] = (short)(p01 & 0xffff);
+          pf[g][1] = (short)(p01 >> 16);
+          pf[g][2] = (short)(p23 & 0xffff);
+          pf[g][3] = (short)(p23 >> 16);
+        }
+        // ---- O^T += C^T . P^T, each C^T fragment feeding both head groups
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt) {
+            const s16x4_t cf = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4_t*)(sl + pv_off[tt] + 128 * q));
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+              o[g][4 * q + tt] =
+                  __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(cf, pf[g], o[g][4 * q + tt], 0, 0, 0);
+          }
+      }
+    }
+
+    // ---- this wave's heads are complete for the segment: write the partials
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float l = l_run[g];
+      l += __shfl_xor(l, 16, 64);
+      l += __shfl_xor(l, 32, 64);
+      const int gh = h0 + 16 * g + lr;
+      float* pacc = acc_out + ((int64_t)wk.pidx * H + gh) * DC + 4 * lg;
+#pragma unroll
+      for (int cb = 0; cb < 32; ++cb)
+        *reinterpret_cast<float4*>(pacc + 16 * cb) =
+            make_float4(o[g][cb][0], o[g][cb][1], o[g][cb][2], o[g][cb][3]);
+      if (lg == 0) {
+        ml_out[((int64_t)wk.pidx * H + gh) * 2] = m_run[g];
+        ml_out[((int64_t)wk.pidx * H + gh) * 2 + 1] = l;
+      }
+    }
+    __syncthreads();  // the stages are refilled by the next segment
+    if (wk.next < 0) break;
+    wk = nx;
+  }
+}
+
+}  // namespace decw
+
+int decode_core_wide_heads() { return decw::HEADS; }
+
+void decode_core_wide(const bf16* q_cat, const bf16* cache, const DecodeMeta& m, int parts,
+                      float* acc, float* ml, const Dims& d, hipStream_t st) {
+  const int wg = d.H / decw::HEADS;
+  const int blocks = (parts + decw::kXcds - 1) / decw::kXcds * decw::kXcds * wg;
+  decw::decode_core_wide_k<<<blocks, 256, 0, st>>>(q_cat, cache, m, acc, ml, d.H, parts);
+}
+
+}  // namespace mla

@@ -131,6 +131,12 @@ void decode_core_generic(const T* q_cat, const T* cache, const DecodeMeta& m, in
 // MFMA version: bf16, dc == 512, dr == 64, H % 16 == 0.  parts = persistent groups.
 void decode_core_mfma(const bf16* q_cat, const bf16* cache, const DecodeMeta& m, int parts,
                       int B, float* acc, float* ml, const Dims& d, hipStream_t st);
+// MFMA core for head counts that are a multiple of decode_core_wide_heads()
+// (64): each workgroup covers that many heads of a part over shared row tiles;
+// the H / 64 workgroups of a part run on one XCD.
+int decode_core_wide_heads();
+void decode_core_wide(const bf16* q_cat, const bf16* cache, const DecodeMeta& m, int parts,
+                      float* acc, float* ml, const Dims& d, hipStream_t st);
 // persistent workgroups of the MFMA core that share one compute unit
 int decode_core_wg_per_cu();
 // combine for dc == 512, bf16 output.  max_chunks = max over sequences of

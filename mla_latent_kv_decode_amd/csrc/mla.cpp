@@ -307,13 +307,19 @@ struct DecodeLayout {
   size_t total = 0;
 };
 
+// layers with many heads use the shared-tile core
+bool wide_core(const mla_ctx* h) { return h->mfma && h->d.H % mla::decode_core_wide_heads() == 0; }
+
 int max_parts(const mla_ctx* h, int64_t total_rows) {
   int64_t p = (total_rows + 63) / 64;
-  // the MFMA core runs one workgroup per 16-head group of a part
-  const int64_t wgs = h->mfma ? std::max<int64_t>(1, (int64_t)h->n_cu *
-                                                         mla::decode_core_wg_per_cu() /
-                                                         (h->d.H / 16))
-                              : h->n_cu;
+  // the MFMA cores run one workgroup per 16-head group (or per 64 heads for
+  // the shared-tile core) of a part
+  const int64_t wgs = !h->mfma ? h->n_cu
+                      : wide_core(h)
+                          ? std::max<int64_t>(1, (int64_t)h->n_cu /
+                                                     (h->d.H / mla::decode_core_wide_heads()))
+                          : std::max<int64_t>(1, (int64_t)h->n_cu *
+                                                     mla::decode_core_wg_per_cu() / (h->d.H / 16));
   if (p > wgs) p = wgs;
   if (p < 1) p = 1;
   return (int)p;
@@ -974,7 +980,10 @@ static int run_decode(mla_ctx* h, const T* hidden, int B, T* cache, T* out, void
   if (ts >= 0) HIP_TRY(h, hipEventRecord(h->tev[2 * ts], h->stream));
   if constexpr (sizeof(T) == 2) {
     if (h->mfma) {
-      mla::decode_core_mfma(q_cat, cache, mt, parts, B, acc, ml, d, h->stream);
+      if (wide_core(h))
+        mla::decode_core_wide(q_cat, cache, mt, parts, acc, ml, d, h->stream);
+      else
+        mla::decode_core_mfma(q_cat, cache, mt, parts, B, acc, ml, d, h->stream);
       mfma_core = true;
     }
   }
