@@ -32,6 +32,7 @@
 //       column c0 + i).  Lane l accumulates columns c0 + 4(l/16) .. +3 of head
 //       l % 16 for every 16-column block c0.
 #include "kernels.h"
+#include "stage_layout.h"
 
 namespace mla {
 namespace dec {
@@ -61,9 +62,8 @@ static_assert(XO_BYTES + NWAVE * 16 * 2 * 4 <= LDS_BYTES, "merge space");
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 // Stage layout (18 KB for 16 rows): the latent part of row r (64 chunks of 16
-// bytes) at byte r*1024, the rope part (8 chunks) at 16384 + r*128.  Chunk c
-// of a row is stored at position c ^ (r & 7) inside its aligned group of 8:
-// 8 consecutive rows read at one column hit 8 different bank groups.
+// bytes) at byte r*1024, the rope part (8 chunks) at 16384 + r*128, chunks
+// swizzled per row as described in stage_layout.h.
 constexpr int ROPE_OFF = SUB * 1024;
 static_assert(ROPE_OFF + SUB * 128 == SUB_BYTES, "stage layout");
 
@@ -80,7 +80,7 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
 }
 
 // 18 loads per 16-row sub-tile: load i < 16 copies the latent part of row i
-// (lane = physical chunk, source chunk lane ^ (i & 7)); loads 16 and 17 copy
+// (lane = physical chunk, source chunk lane ^ lat_swz(i)); loads 16 and 17 copy
 // the rope parts of rows 8j + lane/8.  Rows at or past `nvalid` re-read the
 // last valid row (their scores are masked).
 __device__ __forceinline__ void issue_subtile(const bf16* rows, int row0, int n,
@@ -90,12 +90,12 @@ __device__ __forceinline__ void issue_subtile(const bf16* rows, int row0, int n,
 #pragma unroll
   for (int i = 0; i < SUB; ++i) {
     const int r = i <= last ? i : last;
-    dma16(base + r * (RW * 2) + ((lane ^ (i & 7)) << 4), stage_addr + i * 1024);
+    dma16(base + r * (RW * 2) + ((lane ^ lat_swz(i)) << 4), stage_addr + i * 1024);
   }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     int r = 8 * j + (lane >> 3);
-    const int cc = (lane & 7) ^ (lane >> 3);
+    const int cc = (lane & 7) ^ rope_swz(r);
     r = r <= last ? r : last;
     dma16(base + r * (RW * 2) + 1024 + (cc << 4), stage_addr + ROPE_OFF + j * 1024);
   }
@@ -146,23 +146,26 @@ decode_core_mfma_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
   // 4s + lg (s < 16) sits at lr*1024 + 16*((4s + lg) ^ (lr & 7)) =
   // base(s & 1) + 128*(s >> 1) with b = bit 2 of lr selecting the order of each
   // even/odd pair; rope chunk 4(s-16) + lg at ROPE_OFF + lr*128 + 16*((...) ^ (lr & 7)).
-  const int qk_b = (lr >> 2) & 1;
-  const int qk_lo = (lg ^ (lr & 3)) * 16;
-  const int qk_base0 = lr * 1024 + 64 * qk_b + qk_lo;          // even s
-  const int qk_base1 = lr * 1024 + 64 * (qk_b ^ 1) + qk_lo;    // odd s
-  const int qk_rope0 = ROPE_OFF + lr * 128 + 64 * qk_b + qk_lo;        // s = 16
-  const int qk_rope1 = ROPE_OFF + lr * 128 + 64 * (qk_b ^ 1) + qk_lo;  // s = 17
-  // PV operand (transposing read): lane = (group g = lg, s = lr) addresses row
-  // r = 4g + s/4, column 16cb + 4(s % 4), i.e. latent chunk 2cb + h (h = (s%4)/2)
-  // at byte 8(s & 1).  With x = r & 7, y = x >> 1: the physical chunk is
-  // 2(cb ^ y) + (h ^ (x & 1)), so for cb = 4q + t the byte offset is
-  // pv_off[t] + 128q.
-  int pv_off[4];
+  // row-wise operand of k-step s < 16: row lr, chunk 4s + lg, i.e. at
+  // qk_off[s & 3] + 256 (s >> 2); rope chunk 4(s - 16) + lg at qk_rope[s - 16]
+  int qk_off[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) qk_off[k] = lr * 1024 + 16 * ((4 * k + lg) ^ lat_swz(lr));
+  const int qk_rope0 = ROPE_OFF + lr * 128 + 16 * (lg ^ rope_swz(lr));
+  const int qk_rope1 = ROPE_OFF + lr * 128 + 16 * ((4 + lg) ^ rope_swz(lr));
+  // transposing operand of column block cb = 4q + t: lane (g = lg, s = lr)
+  // addresses row r = 4g + s/4, columns 16 cb + 4(s % 4): chunk 2cb + h with
+  // h = (s % 4) / 2, byte 8(s & 1).  Its position 2(cb ^ a) + (h ^ b) (a = r & 7,
+  // b = r >> 3) puts it at pv_e[t] + 128q for even q and pv_e[t] - pv_d + 128q
+  // for odd q.
+  int pv_e[4], pv_d;
   {
     const int r = 4 * lg + (lr >> 2);
-    const int x = r & 7, y = x >> 1, hh = ((lr & 3) >> 1) ^ (x & 1);
+    const int a = r & 7, b = (r >> 3) & 1, h = (lr & 3) >> 1;
+    pv_d = 256 * (a >> 2);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) pv_off[t] = r * 1024 + 8 * (lr & 1) + 16 * hh + 32 * (t ^ y);
+    for (int t = 0; t < 4; ++t)
+      pv_e[t] = r * 1024 + 16 * (h ^ b) + 8 * (lr & 1) + 32 * (t ^ (a & 3)) + 128 * (a >> 2);
   }
 
   // the part's first work record is work[part]; further ones are chained.  The
@@ -214,8 +217,7 @@ decode_core_mfma_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
       bf16x8_t kf[18];
 #pragma unroll
       for (int s = 0; s < 16; ++s)
-        kf[s] = *reinterpret_cast<const bf16x8_t*>(stage + ((s & 1) ? qk_base1 : qk_base0) +
-                                                   128 * (s >> 1));
+        kf[s] = *reinterpret_cast<const bf16x8_t*>(stage + qk_off[s & 3] + 256 * (s >> 2));
       kf[16] = *reinterpret_cast<const bf16x8_t*>(stage + qk_rope0);
       kf[17] = *reinterpret_cast<const bf16x8_t*>(stage + qk_rope1);
       f32x4_t sa = (f32x4_t){0.f, 0.f, 0.f, 0.f}, sb = sa;
@@ -277,7 +279,8 @@ decode_core_mfma_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const s16x4_t cf = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4_t*)(stage + pv_off[t] + 128 * q));
+              (__attribute__((address_space(3))) s16x4_t*)(stage + pv_e[t] -
+                                                          (q & 1) * pv_d + 128 * q));
           o[4 * q + t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(cf, pf, o[4 * q + t], 0, 0, 0);
         }
 

@@ -1,31 +1,32 @@
-// Split-S latent attention core for many heads: 64 heads per workgroup.
+// Split-S latent attention core for many heads: 128 heads per workgroup.
 //
 // Same computation as the 16-head core (absorbed decode, "Multi-Head Latent
 // Attention" post, sections 3.3 and 3.6: scores of every head against the
 // whole 576-wide latent row, softmax, latent sum of the 512 c_kv columns), for
 // layers with many heads (DeepSeek-V3: 128), where the work per latent row is
 // 8x larger and the 16-head kernel's per-head-group workgroups would stream
-// every row 8 times from L2.  Here one workgroup of 4 waves covers 64 heads
-// (wave w owns the 16-head group w; the per-wave state of one group, its
-// accumulators and query fragments, is what the register file holds), and the
-// two workgroups of a part run on one XCD.  The rows of a segment stream once
-// per workgroup through a 4-stage ring of 32-row tiles
-// shared by the waves (global_load_lds_dwordx4; each wave issues a quarter of
-// every tile; one barrier per tile publishes it and frees the stage the next
-// prefetch overwrites).  Each wave sees every row of the segment for its own
+// every row 8 times from L2.  Here one workgroup of 8 waves (two per SIMD)
+// covers 128 heads: wave w owns the 16-head group w, whose accumulators and
+// query fragments fit the 256 registers a wave gets at that occupancy; the
+// second wave of a SIMD runs its MFMAs while the first reads LDS or does its
+// softmax.  The rows of a segment stream once per workgroup through a 4-stage
+// ring of 32-row tiles shared by the waves (global_load_lds_dwordx4; waves 0-3
+// each issue a quarter of every tile; one barrier per tile publishes it and
+// frees the stage the next prefetch overwrites).  Each wave sees every row of the segment for its own
 // heads, so its (max, sum, acc) state is the segment's partial: no cross-wave
 // merge.  MFMA operand layouts, the LDS swizzle of a 16-row block and the lazy
 // rescale are those of the 16-head core.
 #include <utility>
 
 #include "kernels.h"
+#include "stage_layout.h"
 
 namespace mla {
 namespace decw {
 
 constexpr int DC = 512;
 constexpr int RW = 576;
-constexpr int NW = 4;                         // waves
+constexpr int NW = 8;                         // waves (two per SIMD)
 constexpr int G = 1;                          // 16-head groups per wave
 constexpr int HEADS = 16 * G * NW;            // heads per workgroup
 constexpr int TR = 32;                        // rows per tile
@@ -33,10 +34,12 @@ constexpr int NST = 4;                        // stages
 constexpr int ROPE_OFF = TR * 1024;           // latent of row r at r*1024, rope after
 constexpr int ST_BYTES = TR * RW * 2;         // 36 KB
 constexpr int NLOAD = TR + TR / 8;            // 36 wave-wide 16-byte loads per tile
-constexpr int LPW = NLOAD / NW;               // 9 per wave
+constexpr int LOADERS = 4;                    // waves that issue the tile loads
+constexpr int LPW = NLOAD / LOADERS;          // 9 per loading wave
+static_assert(NLOAD % LOADERS == 0 && LOADERS <= NW, "tile loads split evenly");
 constexpr float kRescale = 8.0f;
 constexpr int kXcds = 8;
-static_assert(NLOAD % NW == 0 && NW == 4, "tile loads split evenly over 4 waves");
+
 static_assert(ROPE_OFF + TR * 128 == ST_BYTES, "stage layout");
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
@@ -69,18 +72,18 @@ __device__ __forceinline__ DecodeWork load_work(ConstWorkPtr p) {
 }
 
 // Load I of a tile whose first row is at `base` and whose last valid row is
-// `last`: I < 32 copies the latent part of row I (source chunk lane ^ (I & 7)),
+// `last`: I < 32 copies the latent part of row I (source chunk lane ^ lat_swz(I & 15)),
 // I >= 32 the rope parts of rows 8j .. 8j+7.  Rows past `last` re-read it.
 template <int I>
 __device__ __forceinline__ void tile_load(const char* base, int last, uint32_t stage, int lane) {
   if constexpr (I < TR) {
     const int r = I <= last ? I : last;
-    dma16(base + r * (RW * 2) + ((lane ^ (I & 7)) << 4), stage + I * 1024);
+    dma16(base + r * (RW * 2) + ((lane ^ lat_swz(I & 15)) << 4), stage + I * 1024);
   } else {
     constexpr int J = I - TR;
     int r = 8 * J + (lane >> 3);
+    const int cc = (lane & 7) ^ rope_swz(r & 15);
     r = r <= last ? r : last;
-    const int cc = (lane & 7) ^ (lane >> 3);
     dma16(base + r * (RW * 2) + 1024 + (cc << 4), stage + ROPE_OFF + J * 1024);
   }
 }
@@ -91,22 +94,32 @@ __device__ __forceinline__ void wave_loads(const char* base, int last, uint32_t 
   (tile_load<W * LPW + U>(base, last, stage, lane), ...);
 }
 
-__device__ __forceinline__ void issue_tile(const char* base, int last, uint32_t stage, int wave,
-                                           int lane) {
+// The lane index is re-read through an opaque instruction so the per-lane load
+// addresses are recomputed per tile instead of being hoisted out of the tile
+// loop (where they would take registers the accumulators need).
+__device__ __forceinline__ int lane_id_opaque() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
+__device__ __forceinline__ void issue_tile(const char* base, int last, uint32_t stage, int wave) {
+  const int lane = lane_id_opaque();
   const auto seq = std::make_integer_sequence<int, LPW>{};
   switch (wave) {
     case 0: wave_loads<0>(base, last, stage, lane, seq); break;
     case 1: wave_loads<1>(base, last, stage, lane, seq); break;
     case 2: wave_loads<2>(base, last, stage, lane, seq); break;
-    default: wave_loads<3>(base, last, stage, lane, seq); break;
+    case 3: wave_loads<3>(base, last, stage, lane, seq); break;
+    default: break;
   }
 }
 
-__global__ void __launch_bounds__(256, 1)
+__global__ void __launch_bounds__(512, 1)
 decode_core_wide_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cache, DecodeMeta mt,
                    float* __restrict__ acc_out, float* __restrict__ ml_out, int H, int nparts) {
   __shared__ __attribute__((aligned(1024))) char lds[NST * ST_BYTES];
-  // block -> (part, 64-head block), the head blocks of a part on one XCD
+  // block -> (part, 128-head block), the head blocks of a part on one XCD
   const int WG = H / HEADS;
   const int bid = blockIdx.x;
   const int part = (bid / (kXcds * WG)) * kXcds + bid % kXcds;
@@ -119,18 +132,26 @@ decode_core_wide_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
   const uint32_t lds0 = lds_u32(lds);
 
   // operand offsets inside a 16-row block (as in the 16-head core)
-  const int qk_b = (lr >> 2) & 1;
-  const int qk_lo = (lg ^ (lr & 3)) * 16;
-  const int qk_base0 = lr * 1024 + 64 * qk_b + qk_lo;
-  const int qk_base1 = lr * 1024 + 64 * (qk_b ^ 1) + qk_lo;
-  const int qk_rope0 = ROPE_OFF + lr * 128 + 64 * qk_b + qk_lo;
-  const int qk_rope1 = ROPE_OFF + lr * 128 + 64 * (qk_b ^ 1) + qk_lo;
-  int pv_off[4];
+  // row-wise operand of k-step s < 16: row lr, chunk 4s + lg, i.e. at
+  // qk_off[s & 3] + 256 (s >> 2); rope chunk 4(s - 16) + lg at qk_rope[s - 16]
+  int qk_off[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) qk_off[k] = lr * 1024 + 16 * ((4 * k + lg) ^ lat_swz(lr));
+  const int qk_rope0 = ROPE_OFF + lr * 128 + 16 * (lg ^ rope_swz(lr));
+  const int qk_rope1 = ROPE_OFF + lr * 128 + 16 * ((4 + lg) ^ rope_swz(lr));
+  // transposing operand of column block cb = 4q + t: lane (g = lg, s = lr)
+  // addresses row r = 4g + s/4, columns 16 cb + 4(s % 4): chunk 2cb + h with
+  // h = (s % 4) / 2, byte 8(s & 1).  Its position 2(cb ^ a) + (h ^ b) (a = r & 7,
+  // b = r >> 3) puts it at pv_e[t] + 128q for even q and pv_e[t] - pv_d + 128q
+  // for odd q.
+  int pv_e[4], pv_d;
   {
     const int r = 4 * lg + (lr >> 2);
-    const int x = r & 7, y = x >> 1, hh = ((lr & 3) >> 1) ^ (x & 1);
+    const int a = r & 7, b = (r >> 3) & 1, h = (lr & 3) >> 1;
+    pv_d = 256 * (a >> 2);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) pv_off[t] = r * 1024 + 8 * (lr & 1) + 16 * hh + 32 * (t ^ y);
+    for (int t = 0; t < 4; ++t)
+      pv_e[t] = r * 1024 + 16 * (h ^ b) + 8 * (lr & 1) + 32 * (t ^ (a & 3)) + 128 * (a >> 2);
   }
 
   const ConstWorkPtr works = reinterpret_cast<ConstWorkPtr>((uintptr_t)mt.work);
@@ -142,7 +163,7 @@ decode_core_wide_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
 #pragma unroll
     for (int t = 0; t < NST - 1; ++t)
       if (t < ntile)
-        issue_tile(rows + t * TR * (RW * 2), n - t * TR - 1, lds0 + t * ST_BYTES, wave, lane);
+        issue_tile(rows + t * TR * (RW * 2), n - t * TR - 1, lds0 + t * ST_BYTES, wave);
     DecodeWork nx = wk;
     if (wk.next >= 0) nx = load_work(works + wk.next);
 
@@ -173,13 +194,14 @@ decode_core_wide_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
 
     for (int t = 0; t < ntile; ++t) {
       static_assert(NST == 4, "wait counts below assume 4 stages");
-      if (t + 2 < ntile) wait_vmcnt<2 * LPW>();
+      if (wave >= LOADERS) {
+      } else if (t + 2 < ntile) wait_vmcnt<2 * LPW>();
       else if (t + 1 < ntile) wait_vmcnt<LPW>();
       else wait_vmcnt<0>();
       __syncthreads();  // tile t is in LDS; every wave is done with tile t-1
       if (t + NST - 1 < ntile)
         issue_tile(rows + (t + NST - 1) * TR * (RW * 2), n - (t + NST - 1) * TR - 1,
-                   lds0 + ((t + NST - 1) % NST) * ST_BYTES, wave, lane);
+                   lds0 + ((t + NST - 1) % NST) * ST_BYTES, wave);
       const char* st = lds + (t % NST) * ST_BYTES;
 #pragma unroll 1
       for (int rb = 0; rb < TR / 16; ++rb) {
@@ -192,20 +214,19 @@ decode_core_wide_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
 #pragma unroll
         for (int g = 0; g < G; ++g) sa[g] = sb[g] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          bf16x8_t kf[9];
+        for (int part3 = 0; part3 < 3; ++part3) {
+          bf16x8_t kf[6];
 #pragma unroll
-          for (int u = 0; u < 9; ++u) {
-            const int s = 9 * half + u;
+          for (int u = 0; u < 6; ++u) {
+            const int s = 6 * part3 + u;
             if (s < 16)
-              kf[u] = *reinterpret_cast<const bf16x8_t*>(sl + ((s & 1) ? qk_base1 : qk_base0) +
-                                                         128 * (s >> 1));
+              kf[u] = *reinterpret_cast<const bf16x8_t*>(sl + qk_off[s & 3] + 256 * (s >> 2));
             else
               kf[u] = *reinterpret_cast<const bf16x8_t*>(sr + (s == 16 ? qk_rope0 : qk_rope1));
           }
 #pragma unroll
-          for (int u = 0; u < 9; ++u) {
-            const int s = 9 * half + u;
+          for (int u = 0; u < 6; ++u) {
+            const int s = 6 * part3 + u;
 #pragma unroll
             for (int g = 0; g < G; ++g) {
               if (s & 1)
@@ -258,7 +279,8 @@ decode_core_wide_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
 #pragma unroll
           for (int tt = 0; tt < 4; ++tt) {
             const s16x4_t cf = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4_t*)(sl + pv_off[tt] + 128 * q));
+                (__attribute__((address_space(3))) s16x4_t*)(sl + pv_e[tt] -
+                                                          (q & 1) * pv_d + 128 * q));
 #pragma unroll
             for (int g = 0; g < G; ++g)
               o[g][4 * q + tt] =
@@ -298,7 +320,7 @@ void decode_core_wide(const bf16* q_cat, const bf16* cache, const DecodeMeta& m,
                       float* acc, float* ml, const Dims& d, hipStream_t st) {
   const int wg = d.H / decw::HEADS;
   const int blocks = (parts + decw::kXcds - 1) / decw::kXcds * decw::kXcds * wg;
-  decw::decode_core_wide_k<<<blocks, 256, 0, st>>>(q_cat, cache, m, acc, ml, d.H, parts);
+  decw::decode_core_wide_k<<<blocks, 64 * decw::NW, 0, st>>>(q_cat, cache, m, acc, ml, d.H, parts);
 }
 
 }  // namespace mla
