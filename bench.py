@@ -36,7 +36,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 ROW_BYTES = 1152               # one bf16 latent row: 512 + 64 values
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_core_v2lite_b64_traffic.json")
-CORE_SRC = os.path.join(ROOT, "mla_latent_kv_decode_amd", "csrc", "k_decode.hip")
+CORE_SRC = os.path.join(ROOT, "mla_latent_kv_decode_amd", "csrc", "k_decode_ring.hip")
 
 
 def parse():
@@ -246,7 +246,7 @@ def main():
                    "latent_rows": int(seq_len.sum()), "cache_bytes": int(cache_bytes),
                    "weight_bytes": int(weight_bytes), "hidden": d.hidden, "heads": d.n_heads,
                    "kv_lora": d.kv_lora, "qk_rope": d.qk_rope},
-        "roofline": {"kernel": "decode_core_mfma_k", "bound": "hbm",
+        "roofline": {"kernel": "decode_core_ring_k", "bound": "hbm",
                      "kernel_timing": "HIP events (no system fence) around every split-S core "
                                       "launch, K eager steps",
                      "achieved": round(core_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

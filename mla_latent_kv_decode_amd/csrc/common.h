@@ -60,35 +60,4 @@ __device__ __forceinline__ float warp_sum(float v) {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Cross-workgroup hand-off without cache-wide fences.  gfx950's L2 is per XCD
-// and not coherent across XCDs, so an agent-scope fence writes back and
-// invalidates a whole L2.  Instead, data handed to another workgroup is
-// stored and loaded with agent-scope relaxed atomics (sc1: coherent per
-// access), the writer waits for its stores to complete before bumping the
-// counter, and the reader only loads after observing the counter.
-__device__ __forceinline__ void st_agent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float ld_agent(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// All of this thread's memory operations have completed (stores acknowledged).
-__device__ __forceinline__ void wait_all_memory() {
-  __builtin_amdgcn_s_waitcnt(0);
-}
-// Returns true in every thread of the block iff this block is the last of
-// `expected` blocks to arrive at `counter`; the last one resets it to 0.
-__device__ __forceinline__ bool arrive_last(int* counter, int expected, int* flag_lds) {
-  wait_all_memory();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const bool last = old == expected - 1;
-    if (last) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *flag_lds = last;
-  }
-  __syncthreads();
-  return *flag_lds != 0;
-}
-
 }  // namespace mla

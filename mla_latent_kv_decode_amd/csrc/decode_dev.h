@@ -1,0 +1,51 @@
+// Device helpers shared by the LDS-streaming kernels (gfx950): the LDS-DMA
+// copy, explicit memory-counter waits and the decode work-record read.
+#pragma once
+
+#include "kernels.h"
+#include "stage_layout.h"
+
+namespace mla {
+namespace ddev {
+
+// One wave-wide 16-byte-per-lane copy global -> LDS.  The LDS destination is
+// M0 + 16 * lane (a 1 KB block per instruction).  Issued from inline asm so the
+// compiler neither reorders it nor adds its own (conservative) waits; the
+// kernels wait with explicit s_waitcnt vmcnt.  An SALU write of M0 needs one
+// wait state before an LDS-DMA load.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(lds_addr)
+               : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt is a 6-bit field");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+typedef const __attribute__((address_space(4))) DecodeWork* ConstWorkPtr;
+
+// Field by field: a constant-address-space object cannot bind to the implicit
+// copy constructor.  Read through the constant address space, the records stay
+// on scalar loads.
+__device__ __forceinline__ DecodeWork load_work(ConstWorkPtr p) {
+  DecodeWork w;
+  w.row = p->row;
+  w.n = p->n;
+  w.b = p->b;
+  w.pidx = p->pidx;
+  w.next = p->next;
+  w.nseg = p->nseg;
+  w.pstart = p->pstart;
+  return w;
+}
+
+}  // namespace ddev
+}  // namespace mla

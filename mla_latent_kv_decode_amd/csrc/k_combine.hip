@@ -39,11 +39,11 @@ __device__ __forceinline__ void store_bf16x8(bf16* dst, const float* r, float in
 __global__ void __launch_bounds__(256)
 combine_chunks_512_k(const float* __restrict__ acc, const float* __restrict__ ml, DecodeMeta mt,
                      int H, float* __restrict__ cacc, float* __restrict__ cml,
-                     bf16* __restrict__ o_lat) {
+                     bf16* __restrict__ o_lat, int chunked_only) {
   const int b = blockIdx.x, h = blockIdx.y, c = blockIdx.z;
   const int ns = mt.nseg[b];
   const int nch = (ns + JC - 1) / JC;
-  if (c >= nch) return;
+  if (c >= nch || (chunked_only && nch == 1)) return;
   const int j0 = mt.pstart[b] + c * JC;
   const int nj = min(JC, ns - c * JC);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -141,14 +141,151 @@ combine_final_512_k(const float* __restrict__ cacc, const float* __restrict__ cm
   store_bf16x8(o_lat + ((int64_t)b * H + h) * DC + 8 * lane, r, 1.f / L);
 }
 
+// ---- combine fused with the value un-absorb (dc = 512, dv = 128)
+//
+// Block (head h, group of SB sequences), 8 waves.  Phase 1: wave w merges the
+// partials of sequence w of the group (lane: columns 8 lane .. + 7),
+// either the core's slots (at most JC of them) or the chunk slots the first
+// pass left for sequences with more; all loads of up to 8 slots are in flight
+// together.  Sequences the core finished itself are read back from o_lat.
+// The rows o_lat_h (bf16) go to LDS and to o_lat.
+// Phase 2 ("Multi-Head Latent Attention" post, eq. 3.3.3: W_UV after the
+// softmax-weighted latent sum): o_h (SB x 128) = o_lat_h (SB x 512) W_UV_h^T
+// with mfma 16x16x32, A from LDS, B = W_UV_h rows (K-contiguous) fetched into
+// VGPRs at kernel start, while phase 1 runs (rows SB .. 15 of the MFMA row
+// block are zero).  Wave w owns output columns 16 w .. 16 w + 15; o is rounded
+// to bf16.
+constexpr int SB = 8;                  // sequences per block
+constexpr int UV_NW = 8;               // waves
+constexpr int UV_DV = 128;
+constexpr int OROW = DC * 2 + 16;      // LDS row stride in bytes (padding: no bank conflicts)
+constexpr int MB = 8;                  // slots merged per round
+
+// merged (unnormalised) sums r over slots j0 .. j0 + nj - 1 and their total L
+__device__ __forceinline__ void merge_slots(const float* __restrict__ a, const float* __restrict__ m,
+                                            int j0, int nj, int H, int h, int lane, float* r,
+                                            float* Lout) {
+  float M = -INFINITY, L = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) r[k] = 0.f;
+  for (int j = 0; j < nj; j += MB) {
+    float4 v[MB][2];
+    float2 w[MB];
+#pragma unroll
+    for (int u = 0; u < MB; ++u) {
+      const int64_t idx = (int64_t)(j0 + min(j + u, nj - 1)) * H + h;
+      const float* p = a + idx * DC + 8 * lane;
+      v[u][0] = *reinterpret_cast<const float4*>(p);
+      v[u][1] = *reinterpret_cast<const float4*>(p + 4);
+      w[u] = *reinterpret_cast<const float2*>(m + idx * 2);
+    }
+    float Mn = M;
+#pragma unroll
+    for (int u = 0; u < MB; ++u) Mn = fmaxf(Mn, w[u].x);  // repeats of the last slot change nothing
+    const float g = exp2f(M - Mn);  // 0 on the first round
+    L *= g;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) r[k] *= g;
+#pragma unroll
+    for (int u = 0; u < MB; ++u) {
+      const float s = j + u < nj ? exp2f(w[u].x - Mn) : 0.f;
+      L = fmaf(s, w[u].y, L);
+      r[0] = fmaf(s, v[u][0].x, r[0]); r[1] = fmaf(s, v[u][0].y, r[1]);
+      r[2] = fmaf(s, v[u][0].z, r[2]); r[3] = fmaf(s, v[u][0].w, r[3]);
+      r[4] = fmaf(s, v[u][1].x, r[4]); r[5] = fmaf(s, v[u][1].y, r[5]);
+      r[6] = fmaf(s, v[u][1].z, r[6]); r[7] = fmaf(s, v[u][1].w, r[7]);
+    }
+    M = Mn;
+  }
+  *Lout = L;
+}
+
+__global__ void __launch_bounds__(UV_NW * 64)
+combine_uv_k(const float* __restrict__ acc, const float* __restrict__ ml,
+             const float* __restrict__ cacc, const float* __restrict__ cml, DecodeMeta mt,
+             int direct_single, const bf16* __restrict__ w_uv, int B, int H,
+             bf16* __restrict__ o_lat, bf16* __restrict__ o) {
+  __shared__ __attribute__((aligned(16))) char rows[16 * OROW];
+  const int h = blockIdx.x, b0 = blockIdx.y * SB;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int lr = lane & 15, lg = lane >> 4;
+
+  // W_UV_h fragments of this wave's column block, all 16 k-steps
+  bf16x8_t wf[16];
+  {
+    const bf16* wb = w_uv + ((int64_t)h * UV_DV + 16 * wave + lr) * DC + 8 * lg;
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) wf[ks] = *reinterpret_cast<const bf16x8_t*>(wb + 32 * ks);
+  }
+
+  // phase 1: o_lat rows of the group's sequences
+  for (int i = wave; i < 16; i += UV_NW) {
+    const int b = b0 + i;
+    uint4* dst = reinterpret_cast<uint4*>(rows + i * OROW + 16 * lane);
+    if (i >= SB || b >= B) {
+      *dst = make_uint4(0u, 0u, 0u, 0u);
+      continue;
+    }
+    bf16* og = o_lat + ((int64_t)b * H + h) * DC + 8 * lane;
+    const int ns = mt.nseg[b];
+    if (direct_single && ns == 1) {
+      *dst = *reinterpret_cast<const uint4*>(og);
+      continue;
+    }
+    float r[8], L;
+    if (ns <= JC) merge_slots(acc, ml, mt.pstart[b], ns, H, h, lane, r, &L);
+    else merge_slots(cacc, cml, mt.cstart[b], (ns + JC - 1) / JC, H, h, lane, r, &L);
+    const float inv = 1.f / L;
+    uint4 pk;
+    pk.x = pack_bf16x2(r[0] * inv, r[1] * inv);
+    pk.y = pack_bf16x2(r[2] * inv, r[3] * inv);
+    pk.z = pack_bf16x2(r[4] * inv, r[5] * inv);
+    pk.w = pack_bf16x2(r[6] * inv, r[7] * inv);
+    *dst = pk;
+    *reinterpret_cast<uint4*>(og) = pk;
+  }
+  __syncthreads();
+
+  // phase 2: o (SB x 128) = o_lat_h (SB x 512) . W_UV_h^T, this wave's 16 columns
+  f32x4_t d0 = (f32x4_t){0.f, 0.f, 0.f, 0.f}, d1 = d0;
+  const char* arow = rows + lr * OROW + 16 * lg;
+#pragma unroll
+  for (int ks = 0; ks < 16; ks += 2) {
+    d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8_t*>(arow + 64 * ks),
+                                                 wf[ks], d0, 0, 0, 0);
+    d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+        *reinterpret_cast<const bf16x8_t*>(arow + 64 * (ks + 1)), wf[ks + 1], d1, 0, 0, 0);
+  }
+  const f32x4_t d = d0 + d1;
+  // lane holds rows 4 lg + i of column 16 wave + lr
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int b = b0 + 4 * lg + i;
+    if (4 * lg + i < SB && b < B) o[(int64_t)b * H * UV_DV + h * UV_DV + 16 * wave + lr] = f32_to_bf16(d[i]);
+  }
+}
+
 }  // namespace cmb
 
 void decode_combine_512(const float* acc, const float* ml, const DecodeMeta& m, int B, int H,
                         int max_chunks, float* cacc, float* cml, bf16* o_lat, hipStream_t st) {
   cmb::combine_chunks_512_k<<<dim3(B, H, max_chunks), 256, 0, st>>>(acc, ml, m, H, cacc, cml,
-                                                                      o_lat);
+                                                                      o_lat, 0);
   if (max_chunks > 1)
     cmb::combine_final_512_k<<<dim3(B, H), 64, 0, st>>>(cacc, cml, m, H, o_lat);
+}
+
+// A6 + A7 with the split combine's first pass only for sequences with more
+// than kCombineChunk partials.
+void decode_combine_uv(const float* acc, const float* ml, const DecodeMeta& m, int B, int H,
+                       int max_chunks, float* cacc, float* cml, bool direct_single,
+                       const bf16* w_uv, bf16* o_lat, bf16* o, hipStream_t st) {
+  if (max_chunks > 1)
+    cmb::combine_chunks_512_k<<<dim3(B, H, max_chunks), 256, 0, st>>>(acc, ml, m, H, cacc, cml,
+                                                                        o_lat, 1);
+  cmb::combine_uv_k<<<dim3(H, (B + cmb::SB - 1) / cmb::SB), cmb::UV_NW * 64, 0, st>>>(
+      acc, ml, cacc, cml, m, direct_single ? 1 : 0, w_uv, B, H, o_lat, o);
 }
 
 }  // namespace mla

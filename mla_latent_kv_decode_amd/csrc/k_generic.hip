@@ -3,6 +3,7 @@
 // append, the query finish, the raw cache scatter, the VALU split-S decode
 // core, the split combine and the non-absorbed prefill attention.
 #include "kernels.h"
+#include "row_dev.h"
 
 #include <math.h>
 
@@ -49,22 +50,6 @@ void gemm_generic(const T* A, int64_t lda, int64_t sA, const T* W, int64_t ldw, 
 // ---------------------------------------------------------------------------
 // epilogues over split-K partials (summed in split order z = 0..ks-1)
 // ---------------------------------------------------------------------------
-// Sum over the ks split slices; the loads of 4 slices are independent (issued
-// together), the adds follow a fixed order (deterministic).
-__device__ __forceinline__ float part_at(const Part& a, int64_t row, int col) {
-  const float* p = a.p + row * a.ld + col;
-  if (a.ks == 1) return p[0];
-  float s = 0.f;
-  int z = 0;
-  for (; z + 4 <= a.ks; z += 4) {
-    const float v0 = p[(int64_t)z * a.zs], v1 = p[(int64_t)(z + 1) * a.zs];
-    const float v2 = p[(int64_t)(z + 2) * a.zs], v3 = p[(int64_t)(z + 3) * a.zs];
-    s += (v0 + v1) + (v2 + v3);
-  }
-  for (; z < a.ks; ++z) s += p[(int64_t)z * a.zs];
-  return s;
-}
-
 __global__ void gemm_store_k(const float* __restrict__ C, int ks, int M, int N, int batch,
                              GemmOut out) {
   const int64_t total = (int64_t)batch * M * N;
@@ -93,17 +78,6 @@ void gemm_store(const float* C, int ks, int M, int N, int batch, const GemmOut& 
   gemm_store_k<<<blocks, 256, 0, st>>>(C, ks, M, N, batch, out);
 }
 
-__device__ __forceinline__ float block_sum_256(float v, float* red) {
-  v = warp_sum(v);
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-  __syncthreads();
-  if (l == 0) red[w] = v;
-  __syncthreads();
-  float s = 0.f;
-  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) s += red[i];
-  return s;
-}
-
 template <typename T>
 __global__ void __launch_bounds__(256)
 rmsnorm_rows_k(Part x, int n, const T* __restrict__ gamma, float eps, T* __restrict__ out) {
@@ -123,23 +97,6 @@ template <typename T>
 void rmsnorm_rows(const Part& x, int rows, int n, const T* gamma, float eps, T* out,
                   hipStream_t st) {
   rmsnorm_rows_k<T><<<rows, 256, 0, st>>>(x, n, gamma, eps, out);
-}
-
-// RoPE of one pair (u, v) at position pos with frequency theta ("Multi-Head
-// Latent Attention" post, section 3.7: adjacent pairs as complex numbers times
-// cos + i sin of pos * theta).  The angle is formed and reduced to [-pi, pi]
-// in double precision (positions reach 10^4..10^5 radians), then sin/cos are
-// taken in fp32.
-__device__ __forceinline__ void rope_pair(float u, float v, int pos, double theta, float* ou,
-                                          float* ov) {
-  const double ang = (double)pos * theta;
-  const double k = rint(ang * 0.15915494309189535);       // 1 / (2 pi)
-  double r = fma(-k, 6.283185307179586, ang);             // 2 pi, high part
-  r = fma(-k, 2.4492935982947064e-16, r);                 // 2 pi, low part
-  float sf, cf;
-  sincosf((float)r, &sf, &cf);
-  *ou = u * cf - v * sf;
-  *ov = u * sf + v * cf;
 }
 
 // In-place RoPE of the rope part of every head of q (bf16 rows of H * (dn + dr)
@@ -168,32 +125,6 @@ void rope_q_inplace(bf16* q, int ntok, const int32_t* pos, const Dims& d, const 
   const int64_t n = (int64_t)ntok * d.H * (d.dr / 2);
   if (n == 0) return;
   rope_q_inplace_k<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(q, ntok, d.H, d.dn, d.dr, pos, rt);
-}
-
-// Latent row of token t ("Deepseek V2 Lite Inference Engine in C", MLA notes:
-// kv_a_proj gives [latent | rope key]; the latent is RMS-normalised and the key
-// rotated; then the row is written to its cache slot).  One block per token.
-template <typename T>
-__device__ __forceinline__ void append_row_block(const Part& a, int t, int p, int64_t slot,
-                                                 const T* __restrict__ gamma,
-                                                 T* __restrict__ cache, const Dims& d,
-                                                 const RopeTab& rt, float* red) {
-  float ss = 0.f;
-  for (int j = threadIdx.x; j < d.dc; j += blockDim.x) {
-    const float v = part_at(a, t, j);
-    ss += v * v;
-  }
-  const float inv = rsqrtf(block_sum_256(ss, red) / (float)d.dc + d.eps);
-  T* row = cache + slot * (int64_t)d.R;
-  for (int j = threadIdx.x; j < d.dc; j += blockDim.x)
-    stf(row + j, part_at(a, t, j) * inv * (gamma ? ldf(gamma + j) : 1.f));
-  for (int i = threadIdx.x; i < d.dr / 2; i += blockDim.x) {
-    float ou, ov;
-    rope_pair(part_at(a, t, d.dc + 2 * i), part_at(a, t, d.dc + 2 * i + 1), p, rt.theta[i], &ou,
-              &ov);
-    stf(row + d.dc + 2 * i, ou);
-    stf(row + d.dc + 2 * i + 1, ov);
-  }
 }
 
 // Query heads of token t: the nope part of each head is stored for the absorb

@@ -1,0 +1,318 @@
+// The decode step's weight-streaming GEMMs (M = batch <= 64 rows) with their
+// epilogues applied in place, and the kernel that finishes the projections
+// (latent-row append, query RMSNorm, absorbed query).
+//
+// C (M x N) = A (M x K) W^T with A row-major activations and W a row-major
+// (N, K) weight (a linear layer), bf16 in, fp32 accumulation, on
+// v_mfma_f32_16x16x32_bf16:
+//   A (16 x 32): lane l holds A[l % 16][8 (l / 16) .. + 7]
+//   B (32 x 16): lane l holds B[8 (l / 16) .. + 7][l % 16]
+//   D (16 x 16): lane l holds D[4 (l / 16) .. + 3][l % 16]
+// A block computes a 16 x 32 tile over all of K, streaming 256-wide K chunks
+// of its 32 weight rows and 16 activation rows into a 3-stage LDS ring with
+// global_load_lds_dwordx4 (each copy is 1 KB: two 512-byte row pieces, so the
+// weights are read in long contiguous runs and the copies hold no registers),
+// two chunks in flight and two blocks per compute unit.  Inside a row piece the 16-byte chunk c of row r is
+// stored at c ^ (r % 16): the operand reads (16 lanes = 16 rows at one K
+// offset) then hit distinct banks.  Wave w takes k-steps w and w + 4 of every
+// chunk; the four waves' sums are added through LDS in wave order
+// (deterministic).  Nothing is split over blocks, so the epilogue sees final
+// sums and is applied right there, on adjacent column pairs: a bf16 store, an
+// fp32 store, or the query finish (per head: the nope part stored, the rope
+// part rotated and scaled into q_cat).  The 16-row blocks of a column tile are
+// numbered 8 apart, so they run on one XCD and share its L2 for the weights.
+#include "decode_dev.h"
+#include "row_dev.h"
+
+namespace mla {
+namespace skn {
+
+using ddev::dma16;
+using ddev::lds_u32;
+using ddev::wait_vmcnt;
+
+constexpr int NWV = 4;                    // waves
+constexpr int NT = 32;                    // output columns per block
+constexpr int KC = 256;                   // K per chunk
+constexpr int ROWB = KC * 2;              // 512 bytes per row piece
+constexpr int W_OFF = 0, A_OFF = NT * ROWB;
+constexpr int ST_BYTES = (NT + 16) * ROWB;  // 24 KB per stage
+constexpr int NST = 3;                    // 72 KB: two blocks per compute unit
+constexpr int NCOPY = (NT + 16) / 2;      // 24 one-KB copies per chunk
+constexpr int CPW = NCOPY / NWV;          // 6 per wave
+constexpr int kXcds = 8;
+static_assert(NCOPY % NWV == 0, "copies split evenly over the waves");
+static_assert((NST - 2) * CPW <= 63, "copies in flight fit the vmcnt field");
+
+// copy i of chunk k0 (rows 2i, 2i + 1 of the stage: weight rows first, then
+// activation rows), lanes 0-31 on the first row, 32-63 on the second
+__device__ __forceinline__ void chunk_copy(int i, const bf16* W, int64_t ldw, int n0, int N,
+                                           const bf16* A, int64_t lda, int m0, int M, int k0,
+                                           uint32_t stage, int lane) {
+  const int r = 2 * i + (lane >> 5);
+  const int c = (lane & 31) ^ (r & 15);  // source chunk stored at position lane & 31
+  const bf16* src = r < NT ? W + (int64_t)min(n0 + r, N - 1) * ldw
+                           : A + (int64_t)min(m0 + r - NT, M - 1) * lda;
+  dma16(src + k0 + 8 * c, stage + (uint32_t)i * 1024);
+}
+
+template <class Epi>
+__global__ void __launch_bounds__(NWV * 64)
+gemm_stream_k(const bf16* __restrict__ A, int64_t lda, const bf16* __restrict__ W, int64_t ldw,
+              int M, int N, int K, int mtiles, Epi epi) {
+  __shared__ __attribute__((aligned(1024))) char lds[NST * ST_BYTES];
+  // block -> (column tile, row tile); the row tiles of a column tile share an XCD
+  const int bid = blockIdx.x;
+  const int mt = (bid / kXcds) % mtiles;
+  const int ntile = (bid / (kXcds * mtiles)) * kXcds + bid % kXcds;
+  const int n0 = ntile * NT, m0 = 16 * mt;
+  if (n0 >= N) return;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int lr = lane & 15, lg = lane >> 4;
+  const uint32_t lds0 = lds_u32(lds);
+  const int nchunk = K / KC;
+  auto issue = [&](int ch) {
+    const uint32_t stage = lds0 + (uint32_t)(ch % NST) * ST_BYTES;
+#pragma unroll
+    for (int j = 0; j < CPW; ++j)
+      chunk_copy(wave * CPW + j, W, ldw, n0, N, A, lda, m0, M, ch * KC, stage, lane);
+  };
+#pragma unroll 1
+  for (int ch = 0; ch < NST - 1 && ch < nchunk; ++ch) issue(ch);
+
+  f32x4_t acc[2] = {(f32x4_t){0.f, 0.f, 0.f, 0.f}, (f32x4_t){0.f, 0.f, 0.f, 0.f}};
+  static_assert(NST == 3, "the waits below assume at most one chunk issued after the awaited one");
+#pragma unroll 1
+  for (int ch = 0; ch < nchunk; ++ch) {
+    if (ch + 1 < nchunk) wait_vmcnt<CPW>();
+    else wait_vmcnt<0>();
+    __syncthreads();  // chunk ch is in LDS; every wave is done with chunk ch - 1
+    if (ch + NST - 1 < nchunk) issue(ch + NST - 1);
+    const char* st = lds + (ch % NST) * ST_BYTES;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int c = 4 * (wave + 4 * u) + lg;  // 16-byte chunk of this lane's operands
+      const bf16x8_t af =
+          *reinterpret_cast<const bf16x8_t*>(st + A_OFF + lr * ROWB + 16 * (c ^ lr));
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const bf16x8_t wf = *reinterpret_cast<const bf16x8_t*>(
+            st + W_OFF + (16 * nb + lr) * ROWB + 16 * (c ^ lr));
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, wf, acc[nb], 0, 0, 0);
+      }
+    }
+  }
+
+  // sum the four waves' tiles: red[w][row][col]
+  __syncthreads();  // the ring is free
+  float* red = reinterpret_cast<float*>(lds);
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[(wave * 16 + 4 * lg + i) * NT + 16 * nb + lr] = acc[nb][i];
+  __syncthreads();
+  const int t = threadIdx.x;  // row t / 16, columns 2 (t % 16), + 1
+  const int row = t >> 4, col = 2 * (t & 15);
+  float v0 = 0.f, v1 = 0.f;
+#pragma unroll
+  for (int w = 0; w < NWV; ++w) {
+    const float2 p = *reinterpret_cast<const float2*>(red + (w * 16 + row) * NT + col);
+    v0 += p.x;
+    v1 += p.y;
+  }
+  if (m0 + row < M && n0 + col < N) epi(m0 + row, n0 + col, v0, v1);
+}
+
+// epilogues on the column pair (c, c + 1) of row r (c even; c + 1 < N)
+struct EpiStore {
+  bf16* out;
+  int64_t ldo;
+  float alpha;
+  __device__ void operator()(int r, int c, float v0, float v1) const {
+    *reinterpret_cast<uint32_t*>(out + (int64_t)r * ldo + c) = pack_bf16x2(alpha * v0, alpha * v1);
+  }
+};
+
+struct EpiF32 {
+  float* out;
+  int64_t ldo;
+  __device__ void operator()(int r, int c, float v0, float v1) const {
+    *reinterpret_cast<float2*>(out + (int64_t)r * ldo + c) = make_float2(v0, v1);
+  }
+};
+
+// Columns [0, R) go to `a` (fp32, row stride R); the rest are query heads of
+// dn + dr columns: the nope part to q_nope (T, H, dn), the rope part rotated at
+// the row's position ("Multi-Head Latent Attention" post, section 3.7: RoPE
+// per head on the decoupled query part) and scaled into q_cat[t][h][dc + i].
+struct EpiQuery {
+  float* a;
+  int R;
+  bf16* q_nope;
+  bf16* q_cat;
+  int H, dn, dr, dc;
+  float scale;
+  RopeTab rt;
+  int32_t pos[64];  // positions of the (at most 64) rows, passed by value
+  __device__ void operator()(int r, int c, float v0, float v1) const {
+    if (c < R) {
+      *reinterpret_cast<float2*>(a + (int64_t)r * R + c) = make_float2(v0, v1);
+      return;
+    }
+    const int cc = c - R, w = dn + dr, h = cc / w, j = cc - h * w;
+    if (j < dn) {
+      *reinterpret_cast<uint32_t*>(q_nope + ((int64_t)r * H + h) * dn + j) = pack_bf16x2(v0, v1);
+      return;
+    }
+    const int i = j - dn;
+    float ou, ov;
+    rope_pair(v0, v1, pos[r], rt.theta[i >> 1], &ou, &ov);
+    *reinterpret_cast<uint32_t*>(q_cat + ((int64_t)r * H + h) * (dc + dr) + dc + i) =
+        pack_bf16x2(scale * ou, scale * ov);
+  }
+};
+
+template <class Epi>
+void launch_stream(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int M, int N, int K,
+                   const Epi& epi, hipStream_t st) {
+  const int mtiles = (M + 15) / 16;
+  const int ntiles = (N + NT - 1) / NT;
+  const int blocks = (ntiles + kXcds - 1) / kXcds * kXcds * mtiles;
+  gemm_stream_k<Epi><<<blocks, NWV * 64, 0, st>>>(A, lda, W, ldw, M, N, K, mtiles, epi);
+}
+
+// ---- projection finish: blocks [0, nab) absorbed query tiles, then nap
+// latent-row appends, then nqn query RMSNorm rows.
+//
+// Absorbed query ("Multi-Head Latent Attention" post, section 3.3): for head h
+// q_cat[t][h][c] = scale * sum_k q_nope[t][h][k] W_ukT[h][c][k] (c < 512,
+// K = dn), one block per (head, 128 columns), wave w on 32 of them.
+template <int MT>
+__global__ void __launch_bounds__(256)
+finish_k(const bf16* __restrict__ q_nope, const bf16* __restrict__ w_ukT,
+         bf16* __restrict__ q_cat, int B, int nab, int nap, const float* __restrict__ a, int lda,
+         int qa_col, const int32_t* __restrict__ pos, const int64_t* __restrict__ slot,
+         const bf16* __restrict__ kv_gamma, bf16* __restrict__ cache, const bf16* q_gamma,
+         bf16* __restrict__ cq, Dims d, RopeTab rt) {
+  __shared__ float red[4];
+  const int blk = blockIdx.x;
+  if (blk >= nab + nap) {  // RMSNorm of the query down-projection row
+    const int t = blk - nab - nap;
+    const float* x = a + (int64_t)t * lda + qa_col;
+    float ss = 0.f;
+    for (int j = threadIdx.x; j < d.dq; j += blockDim.x) ss += x[j] * x[j];
+    const float inv = rsqrtf(block_sum_256(ss, red) / (float)d.dq + d.eps);
+    for (int j = threadIdx.x; j < d.dq; j += blockDim.x)
+      cq[(int64_t)t * d.dq + j] = f32_to_bf16(x[j] * inv * bf16_to_f32(q_gamma[j]));
+    return;
+  }
+  if (blk >= nab) {  // latent row of token t
+    const int t = blk - nab;
+    Part p;
+    p.p = a;
+    p.ks = 1;
+    p.ld = lda;
+    p.zs = 0;
+    append_row_block<bf16>(p, t, pos[t], slot[t], kv_gamma, cache, d, rt, red);
+    return;
+  }
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int h = blk >> 2, c0 = (blk & 3) * 128 + 32 * wave;
+  const int nks = d.dn / 32;
+  f32x4_t acc[MT][2];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) acc[mt][nb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  const bf16* wb = w_ukT + ((int64_t)h * d.dc + c0 + lr) * d.dn + 8 * lg;
+  // four k-steps per round, all their loads issued before the MFMAs
+  for (int ks0 = 0; ks0 < nks; ks0 += 4) {
+    bf16x8_t fa[4][MT], fw[4][2];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int ks = min(ks0 + u, nks - 1);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        fa[u][mt] = *reinterpret_cast<const bf16x8_t*>(
+            q_nope + ((int64_t)min(16 * mt + lr, B - 1) * d.H + h) * d.dn + 32 * ks + 8 * lg);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+        fw[u][nb] = *reinterpret_cast<const bf16x8_t*>(wb + (int64_t)16 * nb * d.dn + 32 * ks);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (ks0 + u < nks)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb)
+            acc[mt][nb] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[u][mt], fw[u][nb], acc[mt][nb], 0, 0, 0);
+  }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * mt + 4 * lg + i;
+        if (t < B)
+          q_cat[((int64_t)t * d.H + h) * d.R + c0 + 16 * nb + lr] = f32_to_bf16(d.scale * acc[mt][nb][i]);
+      }
+}
+
+}  // namespace skn
+
+bool skinny_ok(int M, int N, int K) { return M >= 1 && M <= 64 && N >= 2 && N % 2 == 0 && K % skn::KC == 0; }
+
+void skinny_store(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int M, int N, int K,
+                  bf16* out, int64_t ldo, float alpha, hipStream_t st) {
+  skn::launch_stream(A, lda, W, ldw, M, N, K, skn::EpiStore{out, ldo, alpha}, st);
+}
+
+void skinny_f32(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int M, int N, int K,
+                float* out, int64_t ldo, hipStream_t st) {
+  skn::launch_stream(A, lda, W, ldw, M, N, K, skn::EpiF32{out, ldo}, st);
+}
+
+void skinny_query(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int M, int N, int K,
+                  float* a, int R, bf16* q_nope, bf16* q_cat, const int32_t* pos_host,
+                  const Dims& d, const RopeTab& rt, hipStream_t st) {
+  skn::EpiQuery e;
+  e.a = a;
+  e.R = R;
+  e.q_nope = q_nope;
+  e.q_cat = q_cat;
+  for (int i = 0; i < 64; ++i) e.pos[i] = i < M ? pos_host[i] : 0;
+  e.H = d.H;
+  e.dn = d.dn;
+  e.dr = d.dr;
+  e.dc = d.dc;
+  e.scale = d.scale;
+  e.rt = rt;
+  skn::launch_stream(A, lda, W, ldw, M, N, K, e, st);
+}
+
+void decode_finish(const bf16* q_nope, const bf16* w_ukT, bf16* q_cat, int B, bool absorb,
+                   bool append, bool qnorm, const float* a, int lda, int qa_col, const int32_t* pos,
+                   const int64_t* slot, const bf16* kv_gamma, bf16* cache, const bf16* q_gamma,
+                   bf16* cq, const Dims& d, const RopeTab& rt, hipStream_t st) {
+  const int nab = absorb ? d.H * 4 : 0, nap = append ? B : 0, nqn = qnorm ? B : 0;
+  const int blocks = nab + nap + nqn;
+  if (blocks == 0) return;
+#define MLA_FIN(MT)                                                                          \
+  skn::finish_k<MT><<<blocks, 256, 0, st>>>(q_nope, w_ukT, q_cat, B, nab, nap, a, lda, qa_col, pos, \
+                                            slot, kv_gamma, cache, q_gamma, cq, d, rt)
+  switch ((B + 15) / 16) {
+    case 1: MLA_FIN(1); break;
+    case 2: MLA_FIN(2); break;
+    case 3: MLA_FIN(3); break;
+    default: MLA_FIN(4); break;
+  }
+#undef MLA_FIN
+}
+
+}  // namespace mla

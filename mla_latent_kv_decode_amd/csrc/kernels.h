@@ -29,14 +29,17 @@ struct DecodeSeg {
   int32_t b, r0, r1, pidx;
 };
 
-// The same segment as the persistent core reads it: one self-contained record
-// (absolute first cache row, row count, sequence, partial slot).  Record p <
-// parts is the first segment of part p; `next` chains the part's further
-// segments (-1 ends the chain).
+// The same segment as the persistent cores read it: one self-contained record
+// (absolute first cache row, row count, sequence, partial slot, and the
+// sequence's partial slots [pstart, pstart + nseg)).  Record p < parts is the
+// first segment of part p; `next` chains the part's further segments (-1 ends
+// the chain).
 struct DecodeWork {
   int64_t row;
   int32_t n, b, pidx, next;
+  int32_t nseg, pstart;
 };
+static_assert(sizeof(DecodeWork) == 32, "work records are read as 32-byte scalar loads");
 
 // Per-sequence decode metadata on the device.
 struct DecodeMeta {
@@ -123,22 +126,50 @@ void transpose_heads(const T* in, T* out, int H, int rows, int cols, int64_t str
 template <typename T>
 void cache_write(const T* rows, const int64_t* slot, int ntok, int R, T* cache, hipStream_t st);
 
+// ---- decode-step GEMMs with in-place epilogues (no split over blocks):
+// C = A W^T for M <= 64 rows and K % 512 == 0 (skinny_ok), bf16 operands.
+bool skinny_ok(int M, int N, int K);
+// out (bf16, row stride ldo) = alpha C
+void skinny_store(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int M, int N, int K,
+                  bf16* out, int64_t ldo, float alpha, hipStream_t st);
+// out (fp32, row stride ldo) = C
+void skinny_f32(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int M, int N, int K,
+                float* out, int64_t ldo, hipStream_t st);
+// columns [0, R) of C to a (fp32, row stride R); the remaining columns are
+// query heads [nope (dn) | rope (dr)]: nope to q_nope (M, H, dn), rope rotated
+// at pos_host[row] (a host array, passed to the kernel by value) and scaled by
+// d.scale into q_cat[row][h][dc ..] (row stride H R)
+void skinny_query(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int M, int N, int K,
+                  float* a, int R, bf16* q_nope, bf16* q_cat, const int32_t* pos_host,
+                  const Dims& d, const RopeTab& rt, hipStream_t st);
+// One launch finishing the projections of B tokens, each part optional:
+// absorb: q_cat[t][h][0:dc] = scale * W_ukT_h q_nope[t][h] (dc = 512);
+// append: cache[slot[t]] = [RMSNorm(a[t][0:dc]) * kv_gamma | RoPE(a[t][dc:R], pos[t])];
+// qnorm:  cq[t] = RMSNorm(a[t][qa_col : qa_col + dq]) * q_gamma (bf16).
+void decode_finish(const bf16* q_nope, const bf16* w_ukT, bf16* q_cat, int B, bool absorb,
+                   bool append, bool qnorm, const float* a, int lda, int qa_col,
+                   const int32_t* pos, const int64_t* slot, const bf16* kv_gamma, bf16* cache,
+                   const bf16* q_gamma, bf16* cq, const Dims& d, const RopeTab& rt,
+                   hipStream_t st);
+
 // ---- decode core (split-S) and combine
 // partial layout: acc[pidx][h][dc] fp32, ml[pidx][h][2] = (max in log2 units, sum)
 template <typename T>
 void decode_core_generic(const T* q_cat, const T* cache, const DecodeMeta& m, int nseg_total,
                          float* acc, float* ml, const Dims& d, hipStream_t st);
-// MFMA version: bf16, dc == 512, dr == 64, H % 16 == 0.  parts = persistent groups.
-void decode_core_mfma(const bf16* q_cat, const bf16* cache, const DecodeMeta& m, int parts,
-                      int B, float* acc, float* ml, const Dims& d, hipStream_t st);
 // MFMA core for head counts that are a multiple of decode_core_wide_heads()
-// (64): each workgroup covers that many heads of a part over shared row tiles;
-// the H / 64 workgroups of a part run on one XCD.
+// (128): each workgroup covers that many heads of a part over shared row
+// tiles; the H / 128 workgroups of a part run on one XCD.
 int decode_core_wide_heads();
 void decode_core_wide(const bf16* q_cat, const bf16* cache, const DecodeMeta& m, int parts,
                       float* acc, float* ml, const Dims& d, hipStream_t st);
-// persistent workgroups of the MFMA core that share one compute unit
-int decode_core_wg_per_cu();
+// MFMA core over a ring of shared row tiles (bf16, dc == 512, dr == 64,
+// H % 16 == 0): one workgroup per (part, 16-head group), parts = persistent
+// workgroups per head group.  Partials as for the generic core, except that a
+// sequence contained in one segment is normalised and written to o_lat
+// (B, H, 512) directly.
+void decode_core_ring(const bf16* q_cat, const bf16* cache, const DecodeMeta& m, int parts,
+                      float* acc, float* ml, bf16* o_lat, const Dims& d, hipStream_t st);
 // combine for dc == 512, bf16 output.  max_chunks = max over sequences of
 // ceil(nseg / kCombineChunk); cacc (chunk slots x H x 512) and cml (chunk slots
 // x H x 2) hold the chunk partials of sequences with more than one chunk.
@@ -147,6 +178,13 @@ void decode_combine_512(const float* acc, const float* ml, const DecodeMeta& m, 
 template <typename T>
 void decode_combine(const float* acc, const float* ml, const DecodeMeta& m, int B, T* o_lat,
                     const Dims& d, hipStream_t st);
+// combine fused with the value un-absorb for dc == 512, dv == 128 (bf16):
+// o_lat (B, H, 512) = merged latent sums (read back instead for sequences with
+// one partial when direct_single: the core wrote them), o (B, H * 128) =
+// per head W_UV_h o_lat_h; w_uv is (H, 128, 512).
+void decode_combine_uv(const float* acc, const float* ml, const DecodeMeta& m, int B, int H,
+                       int max_chunks, float* cacc, float* cml, bool direct_single,
+                       const bf16* w_uv, bf16* o_lat, bf16* o, hipStream_t st);
 
 // ---- prefill attention (non-absorbed, causal)
 // One query tile of the MFMA prefill kernel: new tokens t0 .. t0+nq-1 of one

@@ -23,7 +23,7 @@
 
 // rows-equivalent cost of a segment start in the split-S work list
 #ifndef MLA_SEG_ROWS
-#define MLA_SEG_ROWS 192
+#define MLA_SEG_ROWS 64
 #endif
 
 using mla::bf16;
@@ -136,8 +136,9 @@ int check_launch(mla_ctx* h, const char* what) {
 // pinned staging ring.
 int stage_upload(mla_ctx* h, void* dst, const void* src, size_t bytes) {
   if (bytes == 0) return MLA_OK;
+  hipStream_t st = h->stream;
   hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-  HIP_TRY(h, hipStreamIsCapturing(h->stream, &cap));
+  HIP_TRY(h, hipStreamIsCapturing(st, &cap));
   if (cap == hipStreamCaptureStatusActive) {
     // the graph's copy node reads this buffer at every replay: keep it for
     // the life of the handle and never reuse it
@@ -145,7 +146,7 @@ int stage_upload(mla_ctx* h, void* dst, const void* src, size_t bytes) {
     HIP_TRY(h, hipHostMalloc(&p, bytes, hipHostMallocDefault));
     h->captured.push_back(p);
     memcpy(p, src, bytes);
-    HIP_TRY(h, hipMemcpyAsync(dst, p, bytes, hipMemcpyHostToDevice, h->stream));
+    HIP_TRY(h, hipMemcpyAsync(dst, p, bytes, hipMemcpyHostToDevice, st));
     return MLA_OK;
   }
   Staging& s = h->ring[h->ring_next];
@@ -164,8 +165,8 @@ int stage_upload(mla_ctx* h, void* dst, const void* src, size_t bytes) {
   }
   if (!s.ev) HIP_TRY(h, hipEventCreateWithFlags(&s.ev, hipEventDisableTiming));
   memcpy(s.host, src, bytes);
-  HIP_TRY(h, hipMemcpyAsync(dst, s.host, bytes, hipMemcpyHostToDevice, h->stream));
-  HIP_TRY(h, hipEventRecord(s.ev, h->stream));
+  HIP_TRY(h, hipMemcpyAsync(dst, s.host, bytes, hipMemcpyHostToDevice, st));
+  HIP_TRY(h, hipEventRecord(s.ev, st));
   s.pending = true;
   return MLA_OK;
 }
@@ -309,17 +310,20 @@ struct DecodeLayout {
 
 // layers with many heads use the shared-tile core
 bool wide_core(const mla_ctx* h) { return h->mfma && h->d.H % mla::decode_core_wide_heads() == 0; }
+// other MFMA layers use the ring core
+bool ring_core(const mla_ctx* h) { return h->mfma && !wide_core(h); }
+// the split combine fused with the value un-absorb (MFMA layers with dv = 128)
+bool combine_uv(const mla_ctx* h) { return h->mfma && h->d.dv == 128; }
 
 int max_parts(const mla_ctx* h, int64_t total_rows) {
   int64_t p = (total_rows + 63) / 64;
-  // the MFMA cores run one workgroup per 16-head group (or per 64 heads for
-  // the shared-tile core) of a part
+  // the MFMA cores run one workgroup per compute unit: per 16-head group (or
+  // per 128 heads for the many-head core) of a part
   const int64_t wgs = !h->mfma ? h->n_cu
                       : wide_core(h)
                           ? std::max<int64_t>(1, (int64_t)h->n_cu /
                                                      (h->d.H / mla::decode_core_wide_heads()))
-                          : std::max<int64_t>(1, (int64_t)h->n_cu *
-                                                     mla::decode_core_wg_per_cu() / (h->d.H / 16));
+                          : std::max<int64_t>(1, (int64_t)h->n_cu / (h->d.H / 16));
   if (p > wgs) p = wgs;
   if (p < 1) p = 1;
   return (int)p;
@@ -384,7 +388,7 @@ struct MetaOffsets {
 // greedy left-to-right fill needs no more than the available parts is found by
 // bisection.  Cuts inside a sequence fall on 16-row sub-tile boundaries.
 constexpr int64_t kSegRows = MLA_SEG_ROWS;
-constexpr int64_t kCutAlign = 16;
+constexpr int64_t kCutAlign = 32;  // rows per tile of the MFMA cores
 
 struct SpanPlan {
   std::vector<DecodeSeg> segs;
@@ -500,6 +504,8 @@ int build_decode_meta(const mla_ctx* h, int B, const int64_t* seq_off, const int
         w.b = sg.b;
         w.pidx = sg.pidx;
         w.next = -1;
+        w.nseg = nseg[sg.b];
+        w.pstart = pstart[sg.b];
         if (si + 1 < part_begin[p + 1]) {
           w.next = extra;
           slot = extra++;
@@ -958,19 +964,82 @@ static void run_q_and_append(mla_ctx* h, const T* x, int B, void* ws, const Deco
                    h->stream);
 }
 
+// A2-A4 through the decode-step GEMMs with in-place epilogues (bf16 MFMA
+// layers, B <= 64): the first projection leaves the kv_a columns (and q_a) in
+// fp32 and finishes the query heads itself; one more launch appends the latent
+// rows, normalises q_a and / or forms the absorbed query.
+static bool q_skinny_fits(const mla_ctx* h, int B, const DecodeLayout& L) {
+  const Dims& d = h->d;
+  if (!h->mfma || d.dc != 512 || d.dn % 32 != 0 || d.dr % 2 != 0) return false;
+  const int qw = qw_of(d);
+  const int n1 = L.step ? h->n_in : (d.dq ? d.dq : qw);
+  return mla::skinny_ok(B, n1, d.D) && (!d.dq || mla::skinny_ok(B, qw, d.dq));
+}
+
+// the first projection (positions come by value)
+static void q_skinny_first(mla_ctx* h, const bf16* x, int B, void* ws, const DecodeLayout& L,
+                           const int32_t* pos_host) {
+  const Dims& d = h->d;
+  const int qw = qw_of(d);
+  const int n1 = L.step ? h->n_in : (d.dq ? d.dq : qw);
+  float* a = at<float>(ws, L.pin);  // fp32 rows of the first GEMM's non-query columns
+  const bf16* w1 = (const bf16*)(L.step ? h->w_in : (d.dq ? h->w_qa : h->w_q));
+  if (!d.dq)
+    mla::skinny_query(x, d.D, w1, d.D, B, n1, d.D, a, L.step ? d.R : 0, at<bf16>(ws, L.q_nope),
+                      at<bf16>(ws, L.q_cat), pos_host, d, h->rope, h->stream);
+  else
+    mla::skinny_f32(x, d.D, w1, d.D, B, n1, d.D, a, n1, h->stream);
+}
+
+static void q_skinny_rest(mla_ctx* h, int B, void* ws, const DecodeLayout& L,
+                          const DecodeMeta& mt, const int64_t* slot_dev, bf16* cache,
+                          const int32_t* pos_host) {
+  const Dims& d = h->d;
+  const int qw = qw_of(d);
+  const int n1 = L.step ? h->n_in : (d.dq ? d.dq : qw);
+  bf16* q_nope = at<bf16>(ws, L.q_nope);
+  bf16* q_cat = at<bf16>(ws, L.q_cat);
+  float* a = at<float>(ws, L.pin);
+  const bf16* w_ukT = (const bf16*)h->w_ukT;
+  const bf16* kv_g = (const bf16*)h->kv_norm_g;
+  const int R = L.step ? d.R : 0;  // kv_a columns in front of the query columns
+  if (!d.dq) {
+    mla::decode_finish(q_nope, w_ukT, q_cat, B, true, L.step, false, a, R, 0, mt.pos, slot_dev,
+                       kv_g, cache, nullptr, nullptr, d, h->rope, h->stream);
+    return;
+  }
+  bf16* cq = at<bf16>(ws, L.cq);
+  mla::decode_finish(q_nope, w_ukT, q_cat, B, false, L.step, true, a, n1, R, mt.pos, slot_dev,
+                     kv_g, cache, (const bf16*)h->q_norm_g, cq, d, h->rope, h->stream);
+  mla::skinny_query(cq, d.dq, (const bf16*)h->w_qb, d.dq, B, qw, d.dq, nullptr, 0, q_nope, q_cat,
+                    pos_host, d, h->rope, h->stream);
+  mla::decode_finish(q_nope, w_ukT, q_cat, B, true, false, false, nullptr, 0, 0, mt.pos,
+                     slot_dev, kv_g, cache, nullptr, nullptr, d, h->rope, h->stream);
+}
+
 template <typename T>
 static int run_decode(mla_ctx* h, const T* hidden, int B, T* cache, T* out, void* ws,
                       const DecodeLayout& L, const DecodeMeta& mt, int parts, int nseg_total,
-                      int max_chunks, const int64_t* slot_dev) {
+                      int max_chunks, const int64_t* slot_dev, const int32_t* pos_host) {
   const Dims& d = h->d;
   float* scratch = at<float>(ws, L.scratch);
   T* q_nope = at<T>(ws, L.q_nope);
   T* q_cat = at<T>(ws, L.q_cat);
-  run_q_and_append<T>(h, hidden, B, ws, L, mt, slot_dev, cache);
-  // A4: absorbed query q_abs_h = W_UK_h^T q_nope_h, scaled into q_cat[:, :, :dc]
-  gemm_out<T>(h, q_nope, (int64_t)d.H * d.dn, d.dn, (const T*)h->w_ukT, d.dn,
-              (int64_t)d.dc * d.dn, B, d.dc, d.dn, d.H,
-              out_t<T>(q_cat, (int64_t)d.H * d.R, d.R, d.scale), scratch);
+  bool fast = false;
+  if constexpr (sizeof(T) == 2) {
+    fast = q_skinny_fits(h, B, L);
+    if (fast) q_skinny_first(h, (const bf16*)hidden, B, ws, L, pos_host);
+  }
+  if constexpr (sizeof(T) == 2) {
+    if (fast) q_skinny_rest(h, B, ws, L, mt, slot_dev, (bf16*)cache, pos_host);
+  }
+  if (!fast) {
+    run_q_and_append<T>(h, hidden, B, ws, L, mt, slot_dev, cache);
+    // A4: absorbed query q_abs_h = W_UK_h^T q_nope_h, scaled into q_cat[:, :, :dc]
+    gemm_out<T>(h, q_nope, (int64_t)d.H * d.dn, d.dn, (const T*)h->w_ukT, d.dn,
+                (int64_t)d.dc * d.dn, B, d.dc, d.dn, d.H,
+                out_t<T>(q_cat, (int64_t)d.H * d.R, d.R, d.scale), scratch);
+  }
   // A5: split-S latent attention core
   float* acc = at<float>(ws, L.acc);
   float* ml = at<float>(ws, L.ml);
@@ -982,27 +1051,46 @@ static int run_decode(mla_ctx* h, const T* hidden, int B, T* cache, T* out, void
     if (h->mfma) {
       if (wide_core(h))
         mla::decode_core_wide(q_cat, cache, mt, parts, acc, ml, d, h->stream);
-      else
-        mla::decode_core_mfma(q_cat, cache, mt, parts, B, acc, ml, d, h->stream);
+      else  // sequences inside one segment are finished into o_lat by the core
+        mla::decode_core_ring(q_cat, cache, mt, parts, acc, ml, (bf16*)o_lat, d, h->stream);
       mfma_core = true;
     }
   }
   if (!mfma_core) mla::decode_core_generic<T>(q_cat, cache, mt, nseg_total, acc, ml, d, h->stream);
   if (ts >= 0) HIP_TRY(h, hipEventRecord(h->tev[2 * ts + 1], h->stream));
-  // A6: combine the partials of each sequence (fixed slot order)
+  T* o = at<T>(ws, L.o);
+  bool uv_done = false;
   if constexpr (sizeof(T) == 2) {
-    if (mfma_core)
+    if (combine_uv(h)) {
+      // A6 + A7: combine the partials of each sequence (fixed slot order) and
+      // apply W_UV_h to the merged latent sums
+      mla::decode_combine_uv(acc, ml, mt, B, d.H, max_chunks, at<float>(ws, L.cacc),
+                             at<float>(ws, L.cml), ring_core(h), (const bf16*)h->w_uv,
+                             (bf16*)o_lat, (bf16*)o, h->stream);
+      uv_done = true;
+    } else if (mfma_core) {
       mla::decode_combine_512(acc, ml, mt, B, d.H, max_chunks, at<float>(ws, L.cacc),
                               at<float>(ws, L.cml), (bf16*)o_lat, h->stream);
+    }
   }
   if (!mfma_core) mla::decode_combine<T>(acc, ml, mt, B, o_lat, d, h->stream);
   // A7: o_h = W_UV_h o_lat_h
-  T* o = at<T>(ws, L.o);
-  gemm_out<T>(h, o_lat, (int64_t)d.H * d.dc, d.dc, (const T*)h->w_uv, d.dc, (int64_t)d.dv * d.dc,
-              B, d.dv, d.dc, d.H, out_t<T>(o, (int64_t)d.H * d.dv, d.dv), scratch);
+  if (!uv_done)
+    gemm_out<T>(h, o_lat, (int64_t)d.H * d.dc, d.dc, (const T*)h->w_uv, d.dc,
+                (int64_t)d.dv * d.dc, B, d.dv, d.dc, d.H, out_t<T>(o, (int64_t)d.H * d.dv, d.dv),
+                scratch);
   // A8: y = W_o o
-  gemm_out<T>(h, o, (int64_t)d.H * d.dv, 0, (const T*)h->w_o, (int64_t)d.H * d.dv, 0, B, d.D,
-              d.H * d.dv, 1, out_t<T>(out, d.D), scratch);
+  const int ko = d.H * d.dv;
+  bool o_done = false;
+  if constexpr (sizeof(T) == 2) {
+    if (h->mfma && mla::skinny_ok(B, d.D, ko)) {
+      mla::skinny_store((const bf16*)o, ko, (const bf16*)h->w_o, ko, B, d.D, ko, (bf16*)out, d.D,
+                        1.f, h->stream);
+      o_done = true;
+    }
+  }
+  if (!o_done)
+    gemm_out<T>(h, o, ko, 0, (const T*)h->w_o, ko, 0, B, d.D, ko, 1, out_t<T>(out, d.D), scratch);
   return check_launch(h, "decode");
 }
 
@@ -1046,9 +1134,9 @@ static int decode_common(mla_handle h, const void* hidden, const int32_t* pos,
   const int64_t* slot_dev = step ? at<int64_t>(meta, mo.slot) : nullptr;
   if (is_f32(h))
     return run_decode<float>(h, (const float*)hidden, B, (float*)cache, (float*)out, ws, L, mt,
-                             parts, nseg_total, max_chunks, slot_dev);
+                             parts, nseg_total, max_chunks, slot_dev, pos);
   return run_decode<bf16>(h, (const bf16*)hidden, B, (bf16*)cache, (bf16*)out, ws, L, mt, parts,
-                          nseg_total, max_chunks, slot_dev);
+                          nseg_total, max_chunks, slot_dev, pos);
 }
 
 int mla_decode(mla_handle h, const void* hidden, const int32_t* pos, const int64_t* seq_off,

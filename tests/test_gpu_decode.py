@@ -102,6 +102,21 @@ def test_decode_is_deterministic():
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
 
 
+def test_partials_fresh_across_calls():
+    """Split partials are handed between workgroups (possibly on different
+    XCDs) through the workspace; a second call on the same workspace with other
+    sequences in the same slots must see its own partials, not the first
+    call's.  The first batch is then decoded again and must be bit-identical."""
+    a = DecodeCase(synth.V2_LITE, "bf16", 0.02, [3000, 900, 5, 1600])
+    ya = a.run().clone()
+    b = DecodeCase(synth.V2_LITE, "bf16", 0.02, [1600, 5, 3000, 900], layer=a.layer,
+                   weights=a.w)
+    _check(b, range(b.B), stages=False)
+    ya2 = a.run()
+    import torch
+    assert torch.equal(ya.view(torch.int16), ya2.view(torch.int16))
+
+
 def _step_case(dims, lens, std=0.02):
     """Cache holds only the cached rows; decode_step appends the new token
     itself and must match the oracle (and the append + decode path)."""
