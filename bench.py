@@ -45,7 +45,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="v2lite_decode_b64")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the oracle (CPU baseline) sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager calls, no HIP graph")
@@ -101,18 +101,24 @@ def cpu_baseline(wl, w, lens, budget_s: float):
     shp = O.MLAShape(hidden=d.hidden, n_heads=d.n_heads, qk_nope=d.qk_nope,
                      qk_rope=d.qk_rope, v_head=d.v_head, kv_lora=d.kv_lora, q_lora=d.q_lora,
                      rope_base=d.rope_base, rms_eps=d.rms_eps)
-    spent, rows, toks = 0.0, 0, 0
-    for b in range(len(lens)):
-        L = int(lens[b])
-        x = synth.hidden_states(b, L + 1, d.hidden, wl.dtype)
-        prior = O.latent_rows(x[:L], np.arange(L), w["w_kva"], w["kv_norm_g"], shp)
-        t0 = time.perf_counter()
-        O.mla_step(x[L:], np.array([L]), prior, w, shp)
-        spent += time.perf_counter() - t0
-        rows += L + 1
-        toks += 1
-        if spent >= budget_s:
-            break
+    spent, rows, toks, passes = 0.0, 0, 0, 0
+    prepared = {}
+    while spent < budget_s:  # whole passes over the batch until the budget is used
+        for b in range(len(lens)):
+            L = int(lens[b])
+            if b not in prepared:
+                x = synth.hidden_states(b, L + 1, d.hidden, wl.dtype)
+                prepared[b] = (x, O.latent_rows(x[:L], np.arange(L), w["w_kva"], w["kv_norm_g"],
+                                                shp))
+            x, prior = prepared[b]
+            t0 = time.perf_counter()
+            O.mla_step(x[L:], np.array([L]), prior, w, shp)
+            spent += time.perf_counter() - t0
+            rows += L + 1
+            toks += 1
+            if spent >= budget_s:
+                break
+        passes += 1
     try:
         from threadpoolctl import threadpool_info
         cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
@@ -120,8 +126,8 @@ def cpu_baseline(wl, w, lens, budget_s: float):
         cores = os.cpu_count()
     return {"value": rows * ROW_BYTES / spent / 1e9, "unit": "GB/s", "cores": int(cores),
             "kind": "oracle", "tokens_per_s": toks / spent,
-            "sample": f"first {toks} of {len(lens)} sequences ({rows} latent rows), "
-                      f"fp64 non-absorbed oracle, {spent:.1f} s"}
+            "sample": f"{toks} sequence decodes over {passes} pass(es) of the {len(lens)}-sequence "
+                      f"batch ({rows} latent rows), fp64 non-absorbed oracle, {spent:.1f} s"}
 
 
 def main():
