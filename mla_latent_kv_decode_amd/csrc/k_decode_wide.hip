@@ -43,6 +43,7 @@ constexpr int kXcds = 8;
 static_assert(ROPE_OFF + TR * 128 == ST_BYTES, "stage layout");
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x8_t __attribute__((ext_vector_type(8)));
 typedef const __attribute__((address_space(4))) DecodeWork* ConstWorkPtr;
 
 __device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
@@ -203,30 +204,30 @@ decode_core_wide_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
         issue_tile(rows + (t + NST - 1) * TR * (RW * 2), n - (t + NST - 1) * TR - 1,
                    lds0 + ((t + NST - 1) % NST) * ST_BYTES, wave);
       const char* st = lds + (t % NST) * ST_BYTES;
-#pragma unroll 1
-      for (int rb = 0; rb < TR / 16; ++rb) {
-        const int row0 = t * TR + 16 * rb;
-        if (row0 >= n) break;
+      const int row0 = t * TR;
+      // ---- S^T = K . Q^T for both 16-row blocks, K fragments read once per head group
+      f32x4_t sc[2][G];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
         const char* sl = st + rb * 16 * 1024;  // latent rows of this block
         const char* sr = st + rb * 16 * 128;   // rope rows (offsets include ROPE_OFF)
-        // ---- S^T = K . Q^T for both head groups, K fragments read once
         f32x4_t sa[G], sb[G];
 #pragma unroll
         for (int g = 0; g < G; ++g) sa[g] = sb[g] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int part3 = 0; part3 < 3; ++part3) {
-          bf16x8_t kf[6];
+        for (int part = 0; part < 6; ++part) {
+          bf16x8_t kf[3];
 #pragma unroll
-          for (int u = 0; u < 6; ++u) {
-            const int s = 6 * part3 + u;
+          for (int u = 0; u < 3; ++u) {
+            const int s = 3 * part + u;
             if (s < 16)
               kf[u] = *reinterpret_cast<const bf16x8_t*>(sl + qk_off[s & 3] + 256 * (s >> 2));
             else
               kf[u] = *reinterpret_cast<const bf16x8_t*>(sr + (s == 16 ? qk_rope0 : qk_rope1));
           }
 #pragma unroll
-          for (int u = 0; u < 6; ++u) {
-            const int s = 6 * part3 + u;
+          for (int u = 0; u < 3; ++u) {
+            const int s = 3 * part + u;
 #pragma unroll
             for (int g = 0; g < G; ++g) {
               if (s & 1)
@@ -236,56 +237,71 @@ decode_core_wide_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
             }
           }
         }
-        // ---- online softmax per head group (lazy reference maximum)
-        s16x4_t pf[G];
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const f32x4_t sacc = sa[g] + sb[g];
-          float sv[4];
-          bool grow = false;
+        for (int g = 0; g < G; ++g) sc[rb][g] = sa[g] + sb[g];
+      }
+      // ---- online softmax per head group (lazy reference maximum); lane holds
+      // rows row0 + 16 rb + 4 lg + i of its head
+      bf16x8_t pf[G];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const bool valid = row0 + 4 * lg + i < n;
-            sv[i] = valid ? sacc[i] * kLog2e : -INFINITY;
-            grow |= sv[i] > m_run[g] + kRescale;
-          }
-          if (__any(grow)) {
-            float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            const float m_new = fmaxf(m_run[g], mx);
-            const float alpha = __builtin_amdgcn_exp2f(m_run[g] - m_new);
-            l_run[g] *= alpha;
-            m_run[g] = m_new;
+      for (int g = 0; g < G; ++g) {
+        float sv[8];
+        bool grow = false;
 #pragma unroll
-            for (int cb = 0; cb < 32; ++cb) o[g][cb] *= alpha;
-          }
-          float pv[4];
+        for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            pv[i] = __builtin_amdgcn_exp2f(sv[i] - m_run[g]);
-            l_run[g] += pv[i];
+            const bool valid = row0 + 16 * rb + 4 * lg + i < n;
+            sv[4 * rb + i] = valid ? sc[rb][g][i] * kLog2e : -INFINITY;
+            grow |= sv[4 * rb + i] > m_run[g] + kRescale;
           }
-          const uint32_t p01 = pack_bf16x2(pv[0], pv[1]);
-          const uint32_t p23 = pack_bf16x2(pv[2], pv[3]);
-          pf[g][0] = (short)(p01 & 0xffff);
-          pf[g][1] = (short)(p01 >> 16);
-          pf[g][2] = (short)(p23 & 0xffff);
-          pf[g][3] = (short)(p23 >> 16);
+        if (__any(grow)) {
+          float mx = sv[0];
+#pragma unroll
+          for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
+          mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+          mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+          const float m_new = fmaxf(m_run[g], mx);
+          const float alpha = __builtin_amdgcn_exp2f(m_run[g] - m_new);
+          l_run[g] *= alpha;
+          m_run[g] = m_new;
+#pragma unroll
+          for (int cb = 0; cb < 32; ++cb) o[g][cb] *= alpha;
         }
-        // ---- O^T += C^T . P^T, each C^T fragment feeding both head groups
+        float pv[8];
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
+        for (int i = 0; i < 8; ++i) {
+          pv[i] = __builtin_amdgcn_exp2f(sv[i] - m_run[g]);
+          l_run[g] += pv[i];
+        }
+        uint32_t pk[4];
 #pragma unroll
-          for (int tt = 0; tt < 4; ++tt) {
-            const s16x4_t cf = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4_t*)(sl + pv_e[tt] -
-                                                          (q & 1) * pv_d + 128 * q));
+        for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(pv[2 * i], pv[2 * i + 1]);
+        pf[g] = __builtin_bit_cast(bf16x8_t, pk);
+      }
+      // ---- O^T += C^T . P^T over the 32 rows: mfma 16x16x32 whose k index runs
+      // over rows 4g..4g+3 of row block 0, then of row block 1, for lane group g;
+      // C^T from two transposing reads per 16-column block
 #pragma unroll
-            for (int g = 0; g < G; ++g)
-              o[g][4 * q + tt] =
-                  __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(cf, pf[g], o[g][4 * q + tt], 0, 0, 0);
-          }
+      for (int q = 0; q < 8; ++q)
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          typedef __attribute__((address_space(3))) s16x4_t* lptr;
+          const int off = pv_e[tt] - (q & 1) * pv_d + 128 * q;
+          const s16x4_t c0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lptr)(st + off));
+          const s16x4_t c1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lptr)(st + 16 * 1024 + off));
+          const s16x8_t c8 = __builtin_shufflevector(c0, c1, 0, 1, 2, 3, 4, 5, 6, 7);
+          const bf16x8_t cf = __builtin_bit_cast(bf16x8_t, c8);
+#pragma unroll
+          for (int g = 0; g < G; ++g)
+            o[g][4 * q + tt] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(cf, pf[g], o[g][4 * q + tt], 0, 0, 0);
+        }
+      // keep at most a few transposing reads ahead of their MFMAs (registers)
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, G, 0);  // then the MFMAs using them
       }
     }
 

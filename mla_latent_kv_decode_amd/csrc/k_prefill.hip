@@ -14,14 +14,17 @@
 // compute unit and one's softmax overlaps the other's MFMAs.  Keys stream in tiles of
 // 32 through a 4-stage LDS ring filled by global_load_lds_dwordx4 (each wave
 // issues a quarter of every tile; one barrier per tile both publishes the tile
-// and frees the stage the next prefetch overwrites).  Per 16-key block:
-//   S^T (16 keys x 16 queries) = K . Q^T  -- 6 x mfma 16x16x32 per query block,
-//       each K fragment (LDS) reused for the wave's query blocks;
+// and frees the stage the next prefetch overwrites).  Per 32-key tile:
+//   S^T (16 keys x 16 queries) = K . Q^T  -- 6 x mfma 16x16x32 per 16-key
+//       block and query block, each K fragment (LDS) reused for the wave's
+//       query blocks;
 //   online softmax per query with a lazily moved reference maximum;
-//   O (16 queries x 128 dims) += P . V -- mfma 16x16x16: P is the A operand
-//       exactly as S^T left it, V the B operand read straight into layout by
-//       ds_read_b64_tr_b16, each V fragment reused for the wave's query blocks.
-// Key blocks past a wave's last query are skipped (the causal diagonal).
+//   O (16 queries x 128 dims) += P . V -- mfma 16x16x32 over all 32 keys: P is
+//       the A operand exactly as the two S^T blocks left it (k index = keys
+//       4g..4g+3 of block 0, then of block 1, for lane group g), V the B
+//       operand from two transposing reads (ds_read_b64_tr_b16) per 16-dim
+//       block, each V fragment reused for the wave's query blocks.
+// Key tiles past a wave's last query are skipped (the causal diagonal).
 #include <utility>
 
 #include "kernels.h"
@@ -46,6 +49,7 @@ constexpr int kXcds = 8;
 static_assert(NLOAD % NW == 0 && NW == 4, "tile loads split evenly over 4 waves");
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x8_t __attribute__((ext_vector_type(8)));
 
 // LDS layout of one stage, 16-byte chunks XOR-swizzled per key so the reads
 // of both products spread over all banks:
@@ -204,12 +208,13 @@ prefill_attn_mfma_k(const bf16* __restrict__ q, const bf16* __restrict__ kv,
     if (!wave_active) continue;
     const char* st = lds + (kt % NST) * ST_BYTES;
     const int k0 = kt * KT;
-#pragma unroll 1
-    for (int mb = 0; mb < KT / 16; ++mb) {
-      const int kb0 = k0 + 16 * mb;
-      if (kb0 > wmax_pos) break;  // every key of the block is masked for this wave
-      const char* sb = st + mb * 16 * 256;         // K_nope / V rows of this block
-      const char* sr = st + mb * 16 * 128;         // k_rope rows of this block
+    if (k0 > wmax_pos) continue;  // every key of the tile is masked for this wave
+    // ---- S^T (16 keys x 16 queries) = K . Q^T for both 16-key blocks of the tile
+    f32x4_t sacc[2][NQB];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const char* sb = st + mb * 16 * 256;  // K_nope rows of this block
+      const char* sr = st + mb * 16 * 128;  // k_rope rows of this block
       bf16x8_t kf[6];
 #pragma unroll
       for (int s = 0; s < 4; ++s)
@@ -217,74 +222,84 @@ prefill_attn_mfma_k(const bf16* __restrict__ q, const bf16* __restrict__ kv,
 #pragma unroll
       for (int s = 0; s < 2; ++s)
         kf[4 + s] = *reinterpret_cast<const bf16x8_t*>(sr + kr_off + (((4 * s + lg) ^ kr_x) << 4));
-      f32x4_t sacc[NQB];
 #pragma unroll
       for (int nb = 0; nb < NQB; ++nb) {
-        sacc[nb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+        sacc[mb][nb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 6; ++s)
-          sacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], qf[nb][s], sacc[nb], 0, 0, 0);
+          sacc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], qf[nb][s], sacc[mb][nb], 0, 0, 0);
       }
-      // softmax: lane holds keys kb0 + 4 lg + i of query 16 nb + lr.  In log2
-      // units t = s * scale - m_run; the reference maximum m_run only moves
-      // when some t exceeds kRescale (a wave vote), so p = 2^t <= 2^kRescale.
-      // The causal mask is applied only to blocks that reach past the
-      // wave's first query.
-      const bool diag = kb0 + 15 > wmin_pos;
-      s16x4_t pf[NQB];
+    }
+    // softmax: lane holds keys k0 + 16 mb + 4 lg + i of query 16 nb + lr.  In
+    // log2 units t = s * scale - m_run; the reference maximum m_run only moves
+    // when some t exceeds kRescale (a wave vote), so p = 2^t <= 2^kRescale.
+    // The causal mask is applied only to tiles that reach past the wave's
+    // first query.
+    const bool diag = k0 + KT - 1 > wmin_pos;
+    bf16x8_t pf[NQB];
 #pragma unroll
-      for (int nb = 0; nb < NQB; ++nb) {
-        float t[4];
-        bool grow = false;
+    for (int nb = 0; nb < NQB; ++nb) {
+      float t[8];
+      bool grow = false;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          t[i] = fmaf(sacc[nb][i], qk_scale, -m_run[nb]);
-          if (diag && kb0 + 4 * lg + i > qpos[nb]) t[i] = -INFINITY;
-          grow |= t[i] > kRescale;
+          float v = fmaf(sacc[mb][nb][i], qk_scale, -m_run[nb]);
+          if (diag && k0 + 16 * mb + 4 * lg + i > qpos[nb]) v = -INFINITY;
+          t[4 * mb + i] = v;
+          grow |= v > kRescale;
         }
-        if (__any(grow)) {
-          float sv[4];
+      if (__any(grow)) {
+        float sv[8];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const bool valid = !diag || kb0 + 4 * lg + i <= qpos[nb];
-            sv[i] = valid ? sacc[nb][i] * qk_scale : -INFINITY;
+            const bool valid = !diag || k0 + 16 * mb + 4 * lg + i <= qpos[nb];
+            sv[4 * mb + i] = valid ? sacc[mb][nb][i] * qk_scale : -INFINITY;
           }
-          float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-          mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-          mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-          const float m_new = fmaxf(m_run[nb], mx);
-          const float alpha = __builtin_amdgcn_exp2f(m_run[nb] - m_new);
-          l_run[nb] *= alpha;
-          m_run[nb] = m_new;
+        float mx = sv[0];
 #pragma unroll
-          for (int db = 0; db < 8; ++db) o[db][nb] *= alpha;
+        for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float m_new = fmaxf(m_run[nb], mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[nb] - m_new);
+        l_run[nb] *= alpha;
+        m_run[nb] = m_new;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) t[i] = sv[i] - m_new;
-        }
-        float pv[4];
+        for (int db = 0; db < 8; ++db) o[db][nb] *= alpha;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pv[i] = __builtin_amdgcn_exp2f(t[i]);
-          l_run[nb] += pv[i];
-        }
-        const uint32_t p01 = pack_bf16x2(pv[0], pv[1]);
-        const uint32_t p23 = pack_bf16x2(pv[2], pv[3]);
-        pf[nb][0] = (short)(p01 & 0xffff);
-        pf[nb][1] = (short)(p01 >> 16);
-        pf[nb][2] = (short)(p23 & 0xffff);
-        pf[nb][3] = (short)(p23 >> 16);
+        for (int i = 0; i < 8; ++i) t[i] = sv[i] - m_new;
       }
-      // O += P . V
-      const char* sv_base = sb + v_base;
+      float pv[8];
 #pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        const int c = (2 * db + v_h) ^ v_x;
-        const s16x4_t cf = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4_t*)(sv_base + (c << 4)));
-#pragma unroll
-        for (int nb = 0; nb < NQB; ++nb)
-          o[db][nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pf[nb], cf, o[db][nb], 0, 0, 0);
+      for (int i = 0; i < 8; ++i) {
+        pv[i] = __builtin_amdgcn_exp2f(t[i]);
+        l_run[nb] += pv[i];
       }
+      uint32_t pk[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(pv[2 * i], pv[2 * i + 1]);
+      pf[nb] = __builtin_bit_cast(bf16x8_t, pk);
+    }
+    // ---- O += P . V over the 32 keys: mfma 16x16x32 whose k index runs over
+    // keys 4g..4g+3 of block 0, then of block 1, for lane group g (how the
+    // lanes hold P); V comes from two transposing reads per 16-dim block.
+    const char* sv_base = st + v_base;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const int c = (2 * db + v_h) ^ v_x;
+      typedef __attribute__((address_space(3))) s16x4_t* lptr;
+      const s16x4_t c0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lptr)(sv_base + (c << 4)));
+      const s16x4_t c1 =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lptr)(sv_base + 16 * 256 + (c << 4)));
+      const s16x8_t c8 = __builtin_shufflevector(c0, c1, 0, 1, 2, 3, 4, 5, 6, 7);
+      const bf16x8_t cf = __builtin_bit_cast(bf16x8_t, c8);
+#pragma unroll
+      for (int nb = 0; nb < NQB; ++nb)
+        o[db][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[nb], cf, o[db][nb], 0, 0, 0);
     }
   }
 
