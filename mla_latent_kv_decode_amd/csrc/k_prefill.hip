@@ -28,13 +28,15 @@
 #include <utility>
 
 #include "kernels.h"
+#include "row_dev.h"
 
 namespace mla {
 namespace pf {
 
 constexpr int DN = 128, DR = 64, DV = 128;
 constexpr int KT = 32;                       // keys per tile
-constexpr int NW = 4;                        // waves per block
+constexpr int NW = 8;                        // waves per block (two per SIMD)
+constexpr int LOADERS = 4;                   // waves that issue the tile loads
 constexpr int QW = 32;                       // queries per wave
 constexpr int NQB = QW / 16;                 // 16-query blocks per wave
 constexpr int NST = 4;                       // LDS stages
@@ -42,11 +44,12 @@ constexpr int KR_OFF = KT * DN * 2;          // K_nope: 256 B per key
 constexpr int V_OFF = KR_OFF + KT * DR * 2;  // k_rope: 128 B per key
 constexpr int ST_BYTES = V_OFF + KT * DV * 2;  // V: 256 B per key; 20 KB per stage
 constexpr int NLOAD = ST_BYTES / 1024;       // 20 wave-wide 16-byte loads per tile
-constexpr int LPW = NLOAD / NW;              // 5 per wave
+constexpr int LPW = NLOAD / LOADERS;         // 5 per loading wave
 constexpr int KN_LOADS = KR_OFF / 1024, KR_LOADS = (V_OFF - KR_OFF) / 1024;
 constexpr float kRescale = 8.0f;             // lazy-rescale threshold, log2 units
 constexpr int kXcds = 8;
-static_assert(NLOAD % NW == 0 && NW == 4, "tile loads split evenly over 4 waves");
+static_assert(NLOAD % LOADERS == 0 && LOADERS == 4 && LOADERS <= NW,
+              "tile loads split evenly over 4 waves");
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x8_t __attribute__((ext_vector_type(8)));
@@ -75,56 +78,79 @@ __device__ __forceinline__ uint32_t lds_u32(const void* p) {
 typedef const __attribute__((address_space(4))) PrefillTile* ConstTilePtr;
 
 // Load I (0..NLOAD-1) of key tile [k0, k0 + KT): first K_nope (4 keys per
-// load), then k_rope (8 keys per load), then V (4 keys per load).  Keys at or
-// past kend re-read the last key (their scores are masked).
-template <int I>
+// load), then k_rope (8 keys per load), then V (4 keys per load).  In a full
+// tile every key exists: the per-lane row offsets (lrow4 = (lane / 16) rows of
+// the expanded K/V, lrow8 = (lane / 8) cache rows) are loop invariants and
+// the tile's base addresses are uniform, so an address costs one add.  In the
+// last tile keys at or past kend re-read the last key (their scores are
+// masked).
+template <int I, bool FULL>
 __device__ __forceinline__ void issue_load(const char* kvh, const char* rope, int64_t kv_stride,
-                                           int k0, int kend, uint32_t stage, int lane) {
+                                           int k0, int kend, uint32_t stage, int lane,
+                                           int64_t lrow4, int64_t lrow8) {
   if constexpr (I < KN_LOADS) {
     const int r = 4 * I + (lane >> 4);
-    const int kk = min(k0 + r, kend - 1);
     const int c = (lane & 15) ^ (r & 15);
-    dma16(kvh + kk * kv_stride + c * 16, stage + I * 1024);
+    if constexpr (FULL)
+      dma16(kvh + (k0 + 4 * I) * kv_stride + lrow4 + c * 16, stage + I * 1024);
+    else
+      dma16(kvh + min(k0 + r, kend - 1) * kv_stride + c * 16, stage + I * 1024);
   } else if constexpr (I < KN_LOADS + KR_LOADS) {
     constexpr int J = I - KN_LOADS;
     const int r = 8 * J + (lane >> 3);
-    const int kk = min(k0 + r, kend - 1);
     const int c = (lane & 7) ^ ((r >> 1) & 7);
-    dma16(rope + (int64_t)kk * 1152 + c * 16, stage + KR_OFF + J * 1024);
+    if constexpr (FULL)
+      dma16(rope + (int64_t)(k0 + 8 * J) * 1152 + lrow8 + c * 16, stage + KR_OFF + J * 1024);
+    else
+      dma16(rope + (int64_t)min(k0 + r, kend - 1) * 1152 + c * 16, stage + KR_OFF + J * 1024);
   } else {
     constexpr int J = I - KN_LOADS - KR_LOADS;
     const int r = 4 * J + (lane >> 4);
-    const int kk = min(k0 + r, kend - 1);
     const int c = (lane & 15) ^ (2 * (r & 7));
-    dma16(kvh + kk * kv_stride + 256 + c * 16, stage + V_OFF + J * 1024);
+    if constexpr (FULL)
+      dma16(kvh + (k0 + 4 * J) * kv_stride + lrow4 + 256 + c * 16, stage + V_OFF + J * 1024);
+    else
+      dma16(kvh + min(k0 + r, kend - 1) * kv_stride + 256 + c * 16, stage + V_OFF + J * 1024);
   }
 }
 
-template <int W, int... U>
+template <int W, bool FULL, int... U>
 __device__ __forceinline__ void issue_wave(const char* kvh, const char* rope, int64_t kv_stride,
                                            int k0, int kend, uint32_t stage, int lane,
+                                           int64_t lrow4, int64_t lrow8,
                                            std::integer_sequence<int, U...>) {
-  (issue_load<W * LPW + U>(kvh, rope, kv_stride, k0, kend, stage, lane), ...);
+  (issue_load<W * LPW + U, FULL>(kvh, rope, kv_stride, k0, kend, stage, lane, lrow4, lrow8), ...);
 }
 
 // This wave's LPW loads of the tile: straight-line code per wave.
-__device__ __forceinline__ void issue_tile(const char* kvh, const char* rope, int64_t kv_stride,
-                                           int k0, int kend, uint32_t stage, int wave,
-                                           int lane) {
+template <bool FULL>
+__device__ __forceinline__ void issue_tile_w(const char* kvh, const char* rope, int64_t kv_stride,
+                                             int k0, int kend, uint32_t stage, int wave, int lane,
+                                             int64_t lrow4, int64_t lrow8) {
   const auto seq = std::make_integer_sequence<int, LPW>{};
   switch (wave) {
-    case 0: issue_wave<0>(kvh, rope, kv_stride, k0, kend, stage, lane, seq); break;
-    case 1: issue_wave<1>(kvh, rope, kv_stride, k0, kend, stage, lane, seq); break;
-    case 2: issue_wave<2>(kvh, rope, kv_stride, k0, kend, stage, lane, seq); break;
-    default: issue_wave<3>(kvh, rope, kv_stride, k0, kend, stage, lane, seq); break;
+    case 0: issue_wave<0, FULL>(kvh, rope, kv_stride, k0, kend, stage, lane, lrow4, lrow8, seq); break;
+    case 1: issue_wave<1, FULL>(kvh, rope, kv_stride, k0, kend, stage, lane, lrow4, lrow8, seq); break;
+    case 2: issue_wave<2, FULL>(kvh, rope, kv_stride, k0, kend, stage, lane, lrow4, lrow8, seq); break;
+    case 3: issue_wave<3, FULL>(kvh, rope, kv_stride, k0, kend, stage, lane, lrow4, lrow8, seq); break;
+    default: break;
   }
 }
 
-__global__ void __launch_bounds__(256, 2)
+__device__ __forceinline__ void issue_tile(const char* kvh, const char* rope, int64_t kv_stride,
+                                           int k0, int kend, uint32_t stage, int wave, int lane,
+                                           int64_t lrow4, int64_t lrow8) {
+  if (k0 + KT <= kend)
+    issue_tile_w<true>(kvh, rope, kv_stride, k0, kend, stage, wave, lane, lrow4, lrow8);
+  else
+    issue_tile_w<false>(kvh, rope, kv_stride, k0, kend, stage, wave, lane, lrow4, lrow8);
+}
+
+__global__ void __launch_bounds__(NW * 64, 1)
 prefill_attn_mfma_k(const bf16* __restrict__ q, const bf16* __restrict__ kv,
                     const bf16* __restrict__ cache,
                     const PrefillTile* tiles, int ntiles, int H, float qk_scale,
-                    bf16* __restrict__ o_out) {
+                    bf16* __restrict__ o_out, RopeTab rt) {
   __shared__ __attribute__((aligned(1024))) char lds[NST * ST_BYTES];
   // Block -> (tile, head): every block of head h runs on XCD h % 8, so the
   // tiles of one head share that XCD's L2 for their keys and values.
@@ -146,11 +172,13 @@ prefill_attn_mfma_k(const bf16* __restrict__ q, const bf16* __restrict__ kv,
   const int64_t kv_stride = (int64_t)H * (DN + DV) * 2;  // bytes per expanded row
   const char* kvh = reinterpret_cast<const char*>(kv) + kv_row0 * kv_stride + h * (DN + DV) * 2;
   const char* rope = reinterpret_cast<const char*>(cache) + cache_row0 * 1152 + 1024;
+  const int64_t lrow4 = (int64_t)(lane >> 4) * kv_stride, lrow8 = (int64_t)(lane >> 3) * 1152;
 
   // prologue: tiles 0 .. NST-2 in flight
 #pragma unroll
   for (int t = 0; t < NST - 1; ++t)
-    if (t < nkt) issue_tile(kvh, rope, kv_stride, t * KT, kend, lds0 + t * ST_BYTES, wave, lane);
+    if (t < nkt)
+      issue_tile(kvh, rope, kv_stride, t * KT, kend, lds0 + t * ST_BYTES, wave, lane, lrow4, lrow8);
 
   // this wave's queries; lanes past the tile's last query repeat it
   const int qw0 = wave * QW;
@@ -167,8 +195,23 @@ prefill_attn_mfma_k(const bf16* __restrict__ q, const bf16* __restrict__ kv,
     const bf16* qr = qn + DN;
 #pragma unroll
     for (int s = 0; s < 4; ++s) qf[nb][s] = *reinterpret_cast<const bf16x8_t*>(qn + 32 * s);
+    // the rope part is rotated here, at the query's position ("Multi-Head
+    // Latent Attention" post, section 3.7): elements 32 s + 8 lg + 2 j, + 1
+    // form pair 16 s + 4 lg + j; the rotated pair is rounded to bf16
 #pragma unroll
-    for (int s = 0; s < 2; ++s) qf[nb][4 + s] = *reinterpret_cast<const bf16x8_t*>(qr + 32 * s);
+    for (int s = 0; s < 2; ++s) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(qr + 32 * s);
+      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+      uint32_t rw[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float ou, ov;
+        rope_pair(bf16_to_f32((bf16)(w[j] & 0xffff)), bf16_to_f32((bf16)(w[j] >> 16)), qpos[nb],
+                  rt.theta[16 * s + 4 * lg + j], &ou, &ov);
+        rw[j] = pack_bf16x2(ou, ov);
+      }
+      qf[nb][4 + s] = __builtin_bit_cast(bf16x8_t, rw);
+    }
   }
 #pragma unroll
   for (int nb = 0; nb < NQB; ++nb)
@@ -185,26 +228,31 @@ prefill_attn_mfma_k(const bf16* __restrict__ q, const bf16* __restrict__ kv,
   const int v_base = V_OFF + vr * 256 + 8 * (lr & 1);
   const int v_h = (lr & 3) >> 1, v_x = 2 * (vr & 7);
 
-  float m_run[NQB], l_run[NQB];
-  f32x4_t o[8][NQB];  // o[db][nb][i]: query 16 nb + 4 lg + i, dim 16 db + lr
+  // o[db][nb][i]: query 16 nb + 4 lg + i, dim 16 db + lr; block db = 8 multiplies
+  // P by a block of ones, so every lane holds the row sums of its queries
+  float m_run[NQB];
+  f32x4_t o[9][NQB];
 #pragma unroll
   for (int nb = 0; nb < NQB; ++nb) {
     m_run[nb] = -INFINITY;
-    l_run[nb] = 0.f;
 #pragma unroll
-    for (int db = 0; db < 8; ++db) o[db][nb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    for (int db = 0; db < 9; ++db) o[db][nb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
   }
+  bf16x8_t ones;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones[i] = (__bf16)1.0f;
 
   for (int kt = 0; kt < nkt; ++kt) {
     // tiles kt+1 .. kt+NST-2 may stay in flight
     static_assert(NST == 4, "wait counts below assume 4 stages");
-    if (kt + 2 < nkt) wait_vmcnt<2 * LPW>();
+    if (wave >= LOADERS) {
+    } else if (kt + 2 < nkt) wait_vmcnt<2 * LPW>();
     else if (kt + 1 < nkt) wait_vmcnt<LPW>();
     else wait_vmcnt<0>();
     __syncthreads();  // tile kt is in LDS; every wave is done with tile kt-1
     if (kt + NST - 1 < nkt)
       issue_tile(kvh, rope, kv_stride, (kt + NST - 1) * KT, kend,
-                 lds0 + ((kt + NST - 1) % NST) * ST_BYTES, wave, lane);
+                 lds0 + ((kt + NST - 1) % NST) * ST_BYTES, wave, lane, lrow4, lrow8);
     if (!wave_active) continue;
     const char* st = lds + (kt % NST) * ST_BYTES;
     const int k0 = kt * KT;
@@ -240,7 +288,6 @@ prefill_attn_mfma_k(const bf16* __restrict__ q, const bf16* __restrict__ kv,
 #pragma unroll
     for (int nb = 0; nb < NQB; ++nb) {
       float t[8];
-      bool grow = false;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -248,9 +295,11 @@ prefill_attn_mfma_k(const bf16* __restrict__ q, const bf16* __restrict__ kv,
           float v = fmaf(sacc[mb][nb][i], qk_scale, -m_run[nb]);
           if (diag && k0 + 16 * mb + 4 * lg + i > qpos[nb]) v = -INFINITY;
           t[4 * mb + i] = v;
-          grow |= v > kRescale;
         }
-      if (__any(grow)) {
+      float tmax = t[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, t[i]);
+      if (__any(tmax > kRescale)) {
         float sv[8];
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
@@ -266,19 +315,15 @@ prefill_attn_mfma_k(const bf16* __restrict__ q, const bf16* __restrict__ kv,
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
         const float m_new = fmaxf(m_run[nb], mx);
         const float alpha = __builtin_amdgcn_exp2f(m_run[nb] - m_new);
-        l_run[nb] *= alpha;
         m_run[nb] = m_new;
 #pragma unroll
-        for (int db = 0; db < 8; ++db) o[db][nb] *= alpha;
+        for (int db = 0; db < 9; ++db) o[db][nb] *= alpha;
 #pragma unroll
         for (int i = 0; i < 8; ++i) t[i] = sv[i] - m_new;
       }
       float pv[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        pv[i] = __builtin_amdgcn_exp2f(t[i]);
-        l_run[nb] += pv[i];
-      }
+      for (int i = 0; i < 8; ++i) pv[i] = __builtin_amdgcn_exp2f(t[i]);
       uint32_t pk[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(pv[2 * i], pv[2 * i + 1]);
@@ -301,25 +346,22 @@ prefill_attn_mfma_k(const bf16* __restrict__ q, const bf16* __restrict__ kv,
       for (int nb = 0; nb < NQB; ++nb)
         o[db][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[nb], cf, o[db][nb], 0, 0, 0);
     }
+#pragma unroll
+    for (int nb = 0; nb < NQB; ++nb)
+      o[8][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[nb], ones, o[8][nb], 0, 0, 0);
   }
 
   if (!wave_active) return;
 #pragma unroll
   for (int nb = 0; nb < NQB; ++nb) {
-    // after the reduction every lane (lr, *) holds the sum of query lr
-    float l = l_run[nb];
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
-    float inv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) inv[i] = 1.f / __shfl(l, 4 * lg + i, 64);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int qi = qw0 + 16 * nb + 4 * lg + i;
       if (qi >= nq) continue;
+      const float inv = 1.f / o[8][nb][i];  // row sum of query 16 nb + 4 lg + i
       bf16* dst = o_out + ((int64_t)(t0 + qi) * H + h) * DV + lr;
 #pragma unroll
-      for (int db = 0; db < 8; ++db) dst[16 * db] = f32_to_bf16(o[db][nb][i] * inv[i]);
+      for (int db = 0; db < 8; ++db) dst[16 * db] = f32_to_bf16(o[db][nb][i] * inv);
     }
   }
 }
@@ -330,10 +372,10 @@ int prefill_tile_queries() { return pf::NW * pf::QW; }
 
 void prefill_attn_mfma(const bf16* q, const bf16* kv, const bf16* cache,
                        const PrefillTile* tiles, int ntiles, int H, float scale, bf16* o,
-                       hipStream_t st) {
+                       const RopeTab& rt, hipStream_t st) {
   const int blocks = ntiles * ((H + pf::kXcds - 1) / pf::kXcds) * pf::kXcds;
-  pf::prefill_attn_mfma_k<<<blocks, 256, 0, st>>>(q, kv, cache, tiles, ntiles, H,
-                                                  scale * kLog2e, o);
+  pf::prefill_attn_mfma_k<<<blocks, pf::NW * 64, 0, st>>>(q, kv, cache, tiles, ntiles, H,
+                                                  scale * kLog2e, o, rt);
 }
 
 }  // namespace mla

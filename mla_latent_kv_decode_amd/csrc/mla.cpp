@@ -1238,9 +1238,8 @@ static int run_prefill(mla_ctx* h, const T* hidden, int ntok, int B, const int32
   }
   if (mfma_attn) {
     // the projection writes the bf16 query rows (T, H, dn + dr) directly; the
-    // rope parts are then rotated in place
+    // attention kernel rotates the rope parts as it loads them
     gemm_out<T>(h, qin, qk, 0, wq, qk, 0, ntok, qw, qk, 1, out_t<T>(q_nope, qw), scratch);
-    if constexpr (sizeof(T) == 2) mla::rope_q_inplace(q_nope, ntok, tok_pos, d, h->rope, h->stream);
   } else {
     const mla::Part pq = gemm_part<T>(h, qin, qk, wq, qk, ntok, qw, qk,
                                       at<float>(ws, d.dq ? L.pq : L.pin));
@@ -1249,15 +1248,25 @@ static int run_prefill(mla_ctx* h, const T* hidden, int ntok, int B, const int32
   }
   // expansion of every key row: [K_nope_h | V_h] = W_kvb c_t (bf16 for the
   // MFMA attention, fp32 for the generic one)
+  // Sequences whose cache rows and expanded rows both follow each other
+  // directly are expanded by one GEMM.
   const int wkv = d.H * (d.dn + d.dv);
-  for (int b = 0; b < B; ++b) {
-    const int rows = prior[b] + (cu_new[b + 1] - cu_new[b]);
-    if (rows == 0) continue;
-    const int64_t o0 = kv_off_h[b] * (int64_t)wkv;
-    const mla::GemmOut go = mfma_attn ? out_t<T>(at<T>(ws, L.kv) + o0, wkv)
-                                      : out_f32(at<float>(ws, L.kv) + o0, wkv);
-    gemm_out<T>(h, cache + seq_off[b] * d.R, d.R, 0, (const T*)h->w_kvb, d.dc, 0, rows, wkv, d.dc,
-                1, go, scratch);
+  for (int b = 0; b < B;) {
+    int64_t rows = prior[b] + (cu_new[b + 1] - cu_new[b]);
+    int e = b + 1;
+    while (e < B && seq_off[e] == seq_off[b] + rows && kv_off_h[e] == kv_off_h[b] + rows &&
+           rows + prior[e] + (cu_new[e + 1] - cu_new[e]) <= INT32_MAX) {
+      rows += prior[e] + (cu_new[e + 1] - cu_new[e]);
+      ++e;
+    }
+    if (rows > 0) {
+      const int64_t o0 = kv_off_h[b] * (int64_t)wkv;
+      const mla::GemmOut go = mfma_attn ? out_t<T>(at<T>(ws, L.kv) + o0, wkv)
+                                        : out_f32(at<float>(ws, L.kv) + o0, wkv);
+      gemm_out<T>(h, cache + seq_off[b] * d.R, d.R, 0, (const T*)h->w_kvb, d.dc, 0, (int)rows,
+                  wkv, d.dc, 1, go, scratch);
+    }
+    b = e;
   }
   T* o = at<T>(ws, L.o);
   const int ts = timing_slot(h);
@@ -1266,7 +1275,7 @@ static int run_prefill(mla_ctx* h, const T* hidden, int ntok, int B, const int32
     if (mfma_attn)
       mla::prefill_attn_mfma(q_nope, at<bf16>(ws, L.kv), cache,
                              reinterpret_cast<const mla::PrefillTile*>(meta + L.tiles_off),
-                             ntiles, d.H, d.scale, o, h->stream);
+                             ntiles, d.H, d.scale, o, h->rope, h->stream);
   }
   if (!mfma_attn)
     mla::prefill_attn_generic<T>(q_nope, q_rope, at<float>(ws, L.kv), cache, tok_seq, tok_pos,
