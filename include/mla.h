@@ -202,9 +202,11 @@ int mla_decode_stage_offsets(mla_handle h, int32_t B, int64_t total_rows,
  * the compute units).  The concatenated rows of the B sequences are cut into
  * at most max_parts contiguous spans (one persistent workgroup each), each span
  * split at sequence boundaries into segments; spans are balanced on rows plus
- * a fixed per-segment cost, and cuts inside a sequence fall on multiples of 16
- * rows.  The library itself uses max_parts = the device's compute units divided
- * by the number of 16-head groups (each part runs one workgroup per group).
+ * a fixed per-segment cost, and cuts inside a sequence fall on multiples of 32
+ * rows (one tile of the MFMA cores).  The library itself uses max_parts = the
+ * device's compute units divided by the number of workgroups a part runs (one
+ * per 16-head group; one per 128 heads for layers with a multiple of 128
+ * heads).
  *   seq_len: HOST (B), each >= 1.
  *   part_begin: HOST out (max_parts + 1): segments of part p are
  *     [part_begin[p], part_begin[p+1]).

@@ -99,41 +99,6 @@ void rmsnorm_rows(const Part& x, int rows, int n, const T* gamma, float eps, T* 
   rmsnorm_rows_k<T><<<rows, 256, 0, st>>>(x, n, gamma, eps, out);
 }
 
-// In-place RoPE of the rope part of every head of q (bf16 rows of H * (dn + dr)
-// elements: per head [q_nope | q_rope]) at each token's position ("Multi-Head
-// Latent Attention" post, section 3.7: RoPE is applied per head to the decoupled
-// query part).  One thread per (token, head, pair).
-__global__ void __launch_bounds__(256)
-rope_q_inplace_k(bf16* __restrict__ q, int ntok, int H, int dn, int dr,
-                 const int32_t* __restrict__ pos, RopeTab rt) {
-  const int npair = dr / 2;
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (int64_t)ntok * H * npair) return;
-  const int k = (int)(i % npair);
-  const int64_t th = i / npair;  // token * H + head
-  const int t = (int)(th / H);
-  bf16* e = q + th * (dn + dr) + dn + 2 * k;
-  const uint32_t uv = *reinterpret_cast<const uint32_t*>(e);
-  float ou, ov;
-  rope_pair(bf16_to_f32((bf16)(uv & 0xffff)), bf16_to_f32((bf16)(uv >> 16)), pos[t], rt.theta[k],
-            &ou, &ov);
-  *reinterpret_cast<uint32_t*>(e) = pack_bf16x2(ou, ov);
-}
-
-void rope_q_inplace(bf16* q, int ntok, const int32_t* pos, const Dims& d, const RopeTab& rt,
-                    hipStream_t st) {
-  const int64_t n = (int64_t)ntok * d.H * (d.dr / 2);
-  if (n == 0) return;
-  rope_q_inplace_k<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(q, ntok, d.H, d.dn, d.dr, pos, rt);
-}
-
-// Query heads of token t: the nope part of each head is stored for the absorb
-// GEMM and the rope part rotated per head ("Multi-Head Latent Attention" post,
-// section 3.7: embedding is done per head) and scaled into its destination.
-// Query heads [h0, h1) of token t: the nope part of each head is stored for
-// the absorb GEMM and the rope part rotated per head ("Multi-Head Latent
-// Attention" post, section 3.7: embedding is done per head) and scaled into
-// its destination.
 template <typename T>
 __device__ __forceinline__ void q_finish_block(const Part& q, int t, int p, int h0, int h1,
                                                T* __restrict__ q_nope, T* __restrict__ rope_out,

@@ -108,9 +108,6 @@ template <typename T>
 void q_finish(const Part& q, int ntok, const int32_t* pos, T* q_nope, T* rope_out,
               int64_t tok_stride, int64_t head_stride, float scale, const Dims& d,
               const RopeTab& rt, hipStream_t st);
-// RoPE in place on the rope part of q (ntok, H, dn + dr) bf16
-void rope_q_inplace(bf16* q, int ntok, const int32_t* pos, const Dims& d, const RopeTab& rt,
-                    hipStream_t st);
 // append_rows on columns [0, R) and q_finish on columns [R, R + H(dn+dr)) of
 // one fused in-projection, one block per token
 template <typename T>
