@@ -39,11 +39,13 @@ __device__ __forceinline__ void store_bf16x8(bf16* dst, const float* r, float in
 __global__ void __launch_bounds__(256)
 combine_chunks_512_k(const float* __restrict__ acc, const float* __restrict__ ml, DecodeMeta mt,
                      int H, float* __restrict__ cacc, float* __restrict__ cml,
-                     bf16* __restrict__ o_lat, int chunked_only) {
+                     bf16* __restrict__ o_lat, int chunked_only, int direct_single) {
   const int b = blockIdx.x, h = blockIdx.y, c = blockIdx.z;
   const int ns = mt.nseg[b];
   const int nch = (ns + JC - 1) / JC;
-  if (c >= nch || (chunked_only && nch == 1)) return;
+  // chunked_only: sequences with one chunk are merged by the consumer;
+  // direct_single: the core wrote o_lat of one-segment sequences itself
+  if (c >= nch || (chunked_only && nch == 1) || (direct_single && ns == 1)) return;
   const int j0 = mt.pstart[b] + c * JC;
   const int nj = min(JC, ns - c * JC);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -269,9 +271,10 @@ combine_uv_k(const float* __restrict__ acc, const float* __restrict__ ml,
 }  // namespace cmb
 
 void decode_combine_512(const float* acc, const float* ml, const DecodeMeta& m, int B, int H,
-                        int max_chunks, float* cacc, float* cml, bf16* o_lat, hipStream_t st) {
+                        int max_chunks, float* cacc, float* cml, bool direct_single,
+                        bf16* o_lat, hipStream_t st) {
   cmb::combine_chunks_512_k<<<dim3(B, H, max_chunks), 256, 0, st>>>(acc, ml, m, H, cacc, cml,
-                                                                      o_lat, 0);
+                                                                      o_lat, 0, direct_single);
   if (max_chunks > 1)
     cmb::combine_final_512_k<<<dim3(B, H), 64, 0, st>>>(cacc, cml, m, H, o_lat);
 }
@@ -283,7 +286,7 @@ void decode_combine_uv(const float* acc, const float* ml, const DecodeMeta& m, i
                        const bf16* w_uv, bf16* o_lat, bf16* o, hipStream_t st) {
   if (max_chunks > 1)
     cmb::combine_chunks_512_k<<<dim3(B, H, max_chunks), 256, 0, st>>>(acc, ml, m, H, cacc, cml,
-                                                                        o_lat, 1);
+                                                                        o_lat, 1, 0);
   cmb::combine_uv_k<<<dim3(H, (B + cmb::SB - 1) / cmb::SB), cmb::UV_NW * 64, 0, st>>>(
       acc, ml, cacc, cml, m, direct_single ? 1 : 0, w_uv, B, H, o_lat, o);
 }

@@ -170,8 +170,11 @@ void decode_core_ring(const bf16* q_cat, const bf16* cache, const DecodeMeta& m,
 // combine for dc == 512, bf16 output.  max_chunks = max over sequences of
 // ceil(nseg / kCombineChunk); cacc (chunk slots x H x 512) and cml (chunk slots
 // x H x 2) hold the chunk partials of sequences with more than one chunk.
+// direct_single: sequences with one partial were finished into o_lat by the
+// core (the ring core does that) and are left alone.
 void decode_combine_512(const float* acc, const float* ml, const DecodeMeta& m, int B, int H,
-                        int max_chunks, float* cacc, float* cml, bf16* o_lat, hipStream_t st);
+                        int max_chunks, float* cacc, float* cml, bool direct_single,
+                        bf16* o_lat, hipStream_t st);
 template <typename T>
 void decode_combine(const float* acc, const float* ml, const DecodeMeta& m, int B, T* o_lat,
                     const Dims& d, hipStream_t st);

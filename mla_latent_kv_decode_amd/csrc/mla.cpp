@@ -1070,7 +1070,7 @@ static int run_decode(mla_ctx* h, const T* hidden, int B, T* cache, T* out, void
       uv_done = true;
     } else if (mfma_core) {
       mla::decode_combine_512(acc, ml, mt, B, d.H, max_chunks, at<float>(ws, L.cacc),
-                              at<float>(ws, L.cml), (bf16*)o_lat, h->stream);
+                              at<float>(ws, L.cml), ring_core(h), (bf16*)o_lat, h->stream);
     }
   }
   if (!mfma_core) mla::decode_combine<T>(acc, ml, mt, B, o_lat, d, h->stream);

@@ -93,6 +93,34 @@ def test_v3_ragged_small():
     _check(case, range(4))
 
 
+def test_v3_decode_b32_full_size_sampled():
+    """The full V3 B=32 ragged batch (cached lengths ~ U{2048..16384}) in the
+    launch configuration of the many-head core; the shortest sequence and one
+    more are compared with the oracle, every row is checked to be finite."""
+    w = synth.WORKLOADS["v3_decode_b32"]
+    lens = synth.lengths(w)
+    pick = sorted({int(np.argmin(lens)), 5})
+    case = DecodeCase(w.dims, "bf16", w.weight_std, lens, random_gains=False, keep=pick)
+    y = _check(case, pick, stages=True)
+    assert np.all(np.isfinite(y))
+
+
+def test_ring_core_two_head_groups():
+    """32 heads: two 16-head workgroups per part of the ring core, on one XCD."""
+    import dataclasses
+    dims = dataclasses.replace(synth.V2_LITE, n_heads=32)
+    case = DecodeCase(dims, "bf16", 0.02, [0, 40, 700, 2000])
+    _check(case, range(4))
+
+
+def test_value_head_64():
+    """v_head = 64: the MFMA core with the separate combine and value GEMM."""
+    import dataclasses
+    dims = dataclasses.replace(synth.V2_LITE, v_head=64)
+    case = DecodeCase(dims, "bf16", 0.02, [5, 300, 1200])
+    _check(case, range(3))
+
+
 def test_decode_is_deterministic():
     case = DecodeCase(synth.V2_LITE, "bf16", 0.02, [300, 2000, 5])
     y1 = case.run().clone()
@@ -145,6 +173,12 @@ def test_decode_step_v2lite():
 
 def test_decode_step_v3():
     _step_case(synth.V3, [0, 40, 700])
+
+
+def test_decode_step_batch_80():
+    """More than 64 tokens: the projections leave the stream GEMMs for the
+    split-K tile GEMM path."""
+    _step_case(synth.V2_LITE, [3 * b + (b % 7) * 11 for b in range(80)])
 
 
 def test_core_timing_ring():
