@@ -17,6 +17,13 @@ not flush caches); their mean is the core kernel's duration.
 
 Prints ONE JSON line.  Default workload: V2-Lite shapes, B = 64 sequences with
 cached lengths ~ U{512..8192} (``v2lite_decode_b64``).
+
+``--workload v3_prefill_4x4096`` measures the chunked causal prefill instead
+(V3 shapes, 4 sequences of 4096 new tokens after 0 / 2048 cached rows): a step
+is the append of the new tokens' latent rows plus one mla_prefill call over the
+batch, timed eagerly; the figure is expanded-form TFLOP/s against the bf16
+MFMA peak, with the attention kernel's own rate (library events around its
+launches) as the roofline entry.
 """
 
 from __future__ import annotations
@@ -34,6 +41,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, vendor figure
 ROW_BYTES = 1152               # one bf16 latent row: 512 + 64 values
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_core_v2lite_b64_traffic.json")
 CORE_SRC = os.path.join(ROOT, "mla_latent_kv_decode_amd", "csrc", "k_decode_ring.hip")
@@ -130,6 +138,139 @@ def cpu_baseline(wl, w, lens, budget_s: float):
                       f"batch ({rows} latent rows), fp64 non-absorbed oracle, {spent:.1f} s"}
 
 
+def prefill_flops(d, T, key_rows, pairs):
+    """Expanded-form flops of one prefill step: the projections of the T new
+    tokens (q_a / q_b or q, kv_a), the K_nope / V expansion of every key row,
+    causal attention over the (query, key) pairs, and the output projection."""
+    H, dn, dr, dv, dc, D, dq = (d.n_heads, d.qk_nope, d.qk_rope, d.v_head, d.kv_lora, d.hidden,
+                                d.q_lora)
+    qw = H * (dn + dr)
+    proj = 2.0 * T * D * (dc + dr)                               # kv_a (append)
+    proj += 2.0 * T * (D * dq + dq * qw) if dq else 2.0 * T * D * qw
+    expand = 2.0 * key_rows * dc * H * (dn + dv)
+    attn = 2.0 * H * (dn + dr + dv) * pairs
+    out = 2.0 * T * H * dv * D
+    return proj + expand + attn + out, attn
+
+
+def cpu_baseline_prefill(wl, w, budget_s: float):
+    """The fp64 oracle (as it stands) on a bounded sample of the same workload:
+    chunks of 512 new tokens of sequence 0 (no cached rows) until the time
+    budget is used; TFLOP/s over the same expanded-form flop count."""
+    from oracle import mla as O
+    from mla_latent_kv_decode_amd import synth
+    d = wl.dims
+    shp = O.MLAShape(hidden=d.hidden, n_heads=d.n_heads, qk_nope=d.qk_nope,
+                     qk_rope=d.qk_rope, v_head=d.v_head, kv_lora=d.kv_lora, q_lora=d.q_lora,
+                     rope_base=d.rope_base, rms_eps=d.rms_eps)
+    n = 512
+    x = synth.hidden_states(0, n, d.hidden, wl.dtype)
+    spent, chunks, flops = 0.0, 0, 0.0
+    while spent < budget_s:
+        t0 = time.perf_counter()
+        O.mla_step(x, np.arange(n), np.zeros((0, shp.row)), w, shp)
+        spent += time.perf_counter() - t0
+        chunks += 1
+        flops += prefill_flops(d, n, n, n * (n + 1) // 2)[0]
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count()
+    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle", "tokens_per_s": chunks * n / spent,
+            "sample": f"{chunks} prefill(s) of {n} new tokens with no cached rows (sequence 0), "
+                      f"fp64 non-absorbed oracle, {spent:.1f} s"}
+
+
+def bench_prefill(args, wl):
+    import torch
+    from mla_latent_kv_decode_amd import synth
+    from mla_latent_kv_decode_amd.lib import MLALayer
+    d = wl.dims
+    tdt = torch.bfloat16
+    w = synth.make_weights(d, wl.weight_std, wl.dtype)
+    layer = MLALayer(d, wl.dtype)
+    layer.absorb_weights({k: torch.from_numpy(v).cuda().to(tdt) for k, v in w.items()})
+    seq_off, prior, cu_new, total = synth.prefill_layout(wl)
+    B = wl.batch
+    T = int(cu_new[-1])
+    # cached rows before the chunk: latent rows appended from seeded hidden states
+    cache = torch.zeros((total, d.row), dtype=tdt, device="cuda")
+    for b in range(B):
+        if prior[b]:
+            xp = synth.hidden_states(b, int(prior[b]), d.hidden, wl.dtype)
+            layer.append(torch.from_numpy(xp).cuda().to(tdt), np.arange(prior[b]),
+                         int(seq_off[b]) + np.arange(prior[b]), cache)
+    x = np.concatenate([synth.hidden_states(b, wl.new_tokens, d.hidden, wl.dtype,
+                                            start=int(prior[b])) for b in range(B)])
+    xd = torch.from_numpy(x).cuda().to(tdt)
+    pos = np.concatenate([prior[b] + np.arange(cu_new[b + 1] - cu_new[b]) for b in range(B)])
+    slot = np.concatenate([seq_off[b] + pos[cu_new[b]:cu_new[b + 1]] for b in range(B)])
+    y = torch.empty((T, d.hidden), dtype=tdt, device="cuda")
+
+    def step():
+        layer.append(xd, pos, slot, cache)
+        layer.prefill(xd, cu_new, prior, seq_off, cache, out=y)
+
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    t0 = time.perf_counter()
+    for _ in range(K):
+        step()
+    torch.cuda.synchronize()
+    t_step = (time.perf_counter() - t0) / K
+    layer.core_timing(K)
+    for _ in range(K):
+        step()
+    attn = layer.core_timing_read(K)
+    layer.core_timing(0)
+    torch.cuda.synchronize()
+    attn_ms = float(np.mean(attn))
+    key_rows = int(sum(int(prior[b]) + int(cu_new[b + 1] - cu_new[b]) for b in range(B)))
+    pairs = int(sum(int(prior[b]) * int(cu_new[b + 1] - cu_new[b])
+                    + int(cu_new[b + 1] - cu_new[b]) * int(cu_new[b + 1] - cu_new[b] + 1) // 2
+                    for b in range(B)))
+    flops, attn_flops = prefill_flops(d, T, key_rows, pairs)
+    tfs = flops / t_step / 1e12
+    attn_tfs = attn_flops / (attn_ms * 1e-3) / 1e12
+    res = {
+        "metric": "MLA chunked prefill TFLOP/s (V3 shapes, 4 x 4096 new tokens), % of bf16 "
+                  "MFMA peak",
+        "value": round(tfs, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_step * 1e3, 4),
+        "tokens_per_s": round(T / t_step, 1),
+        "mfma_frac_step": round(tfs / MFMA_BF16_PEAK_TFLOPS, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "timing": "eager steps (append + mla_prefill)",
+        "config": {"workload": wl.name, "batch": B, "new_tokens": wl.new_tokens,
+                   "prior": [int(p) for p in prior], "key_rows": key_rows,
+                   "causal_pairs": pairs, "step_tflop": round(flops / 1e12, 4),
+                   "hidden": d.hidden, "heads": d.n_heads, "kv_lora": d.kv_lora,
+                   "q_lora": d.q_lora},
+        "roofline": {"kernel": "prefill_attn_mfma_k", "bound": "mfma",
+                     "kernel_timing": "HIP events (no system fence) around every prefill "
+                                      "attention launch, K eager steps",
+                     "achieved": round(attn_tfs, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tfs / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "kernel_ms": round(attn_ms, 4), "algorithmic_flops_per_launch": attn_flops,
+                     "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_prefill(wl, w, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -148,7 +289,11 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     wl = synth.WORKLOADS[args.workload]
-    assert wl.kind == "decode" and wl.dtype == "bf16"
+    assert wl.dtype == "bf16"
+    if wl.kind == "prefill":
+        bench_prefill(args, wl)
+        return
+    assert wl.kind == "decode"
     d = wl.dims
     tdt = torch.bfloat16
 

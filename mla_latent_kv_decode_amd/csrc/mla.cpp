@@ -77,9 +77,10 @@ struct mla_ctx {
   std::vector<hipEvent_t> tev;
   int t_next = 0;
   int64_t t_count = 0;
-  // library GEMM (rocBLAS) for the large-M projections of prefill; created on
-  // first use.  lib_gemm_ok is set only while a prefill call runs, so decode
-  // calls (which callers capture into graphs) never reach it.
+  // library GEMM (rocBLAS) for the large-M projections of prefill and bulk
+  // appends; created on first use.  lib_gemm_ok is set only while such a call
+  // runs on a stream that is not being captured, so decode calls and captured
+  // graphs never reach it.
   rocblas_handle rb = nullptr;
   bool lib_gemm_ok = false;
   int lib_err = 0;
@@ -200,10 +201,15 @@ int gemm_ks(const mla_ctx* h, int M, int N, int K, int batch) {
   return mfma_gemm(h, N, K) ? mla::gemm_bf16_ksplit(M, N, K, batch, h->n_cu) : 1;
 }
 
-// Enables the library GEMM for the duration of a call (prefill, bulk append).
+// Enables the library GEMM for the duration of a call (prefill, bulk append),
+// unless the stream is being captured into a graph.
 struct LibGemmScope {
   mla_ctx* h;
-  explicit LibGemmScope(mla_ctx* c) : h(c) { h->lib_gemm_ok = true; }
+  explicit LibGemmScope(mla_ctx* c) : h(c) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    h->lib_gemm_ok =
+        hipStreamIsCapturing(h->stream, &cs) == hipSuccess && cs == hipStreamCaptureStatusNone;
+  }
   ~LibGemmScope() { h->lib_gemm_ok = false; }
 };
 
@@ -839,6 +845,7 @@ int mla_append_latent(mla_handle h, const void* hidden, const int32_t* pos, cons
   if (rc) return fail(h, rc, "append: %s (T=%d, cache_rows=%lld)", mla_status_string(rc), T,
                       (long long)cache_rows);
   if (!h->absorbed) return fail(h, MLA_ERR_STATE, "append before mla_absorb_weights");
+  LibGemmScope lib_scope(h);  // many rows: the kv_a projection on the library GEMM
   const AppendLayout L = append_layout(h, T);
   if ((rc = check_ws(h, ws, ws_bytes, L.total))) return rc;
   DeviceGuard g(h->device);
