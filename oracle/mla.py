@@ -210,7 +210,7 @@ def output_projection(o, w_o) -> np.ndarray:
 
 
 def mla_step(x_new, pos_new, rows_prior, w: dict, shape: MLAShape,
-             return_probs: bool = False):
+             return_probs: bool = False, kv_store=None):
     """One cached MLA step for ONE sequence, non-absorbed.
 
     The new tokens' latent rows are appended to the cache and the cache is then
@@ -220,14 +220,19 @@ def mla_step(x_new, pos_new, rows_prior, w: dict, shape: MLAShape,
     treats the same way apart from the offset mask.
 
     x_new (T, D) at positions pos_new (T,); rows_prior (P, R) are the cached
-    rows for positions 0..P-1 (P may be 0).  Returns a dict with the new rows
-    and y (T, D) [and the attention probabilities].
+    rows for positions 0..P-1 (P may be 0).  ``kv_store`` (optional) maps the
+    rows to what the cache hands back when read (e.g. ``oracle.fp8.fp8_rows``
+    for a low-precision cache); it is applied to all rows before attention.
+    Returns a dict with the new rows and y (T, D) [and the attention
+    probabilities].
     """
     x_new = _f64(x_new)
     pos_new = np.asarray(pos_new)
     rows_new = latent_rows(x_new, pos_new, w["w_kva"], w["kv_norm_g"], shape)
     rows_prior = _f64(rows_prior).reshape(-1, shape.row)
     rows = np.concatenate([rows_prior, rows_new], axis=0)
+    if kv_store is not None:
+        rows = kv_store(rows)
     dc = shape.kv_lora
     k_n, v = expand_kv(rows[:, :dc], w["w_kvb"], shape)
     q_n, q_r = query_heads(x_new, pos_new, w, shape)

@@ -324,3 +324,112 @@ def test_hidden_state_stream_is_positional():
     w = synth.WORKLOADS["v2lite_decode_b64"]
     L = synth.lengths(w)
     assert L.shape == (64,) and L.min() >= 512 and L.max() <= 8192
+
+
+# ---------------------------------------------------------------- FP8 storage
+from oracle import fp8 as F8
+
+
+def _e4m3_by_hand(code: int) -> float:
+    """E4M3 value from the format definition, written out bit by bit (pure
+    Python): sign, 4-bit exponent with bias 7, 3-bit mantissa, subnormals at
+    exponent 0, NaN at exponent 15 / mantissa 7."""
+    sign = -1.0 if code >> 7 else 1.0
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    if e == 0xF and m == 0x7:
+        return float("nan")
+    if e == 0:
+        return sign * m / 8.0 * 2.0 ** (1 - 7)
+    return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+def test_e4m3_decode_matches_the_format_definition():
+    got = F8.e4m3_decode(np.arange(256))
+    want = np.array([_e4m3_by_hand(c) for c in range(256)])
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    ok = ~np.isnan(want)
+    assert np.array_equal(got[ok], want[ok])
+    # landmarks of the format
+    assert got[0x00] == 0.0 and got[0x01] == 2.0 ** -9 and got[0x07] == 7 * 2.0 ** -9
+    assert got[0x08] == 2.0 ** -6 and got[0x38] == 1.0 and got[0x7E] == 448.0
+    assert got[0xFE] == -448.0 and np.isnan(got[0x7F]) and np.isnan(got[0xFF])
+    assert np.all(np.diff(got[:0x7F]) > 0)                 # monotone over the finite codes
+    assert np.array_equal(got[0x80:0xFF], -got[0x00:0x7F])  # sign bit
+
+
+def test_e4m3_encode_round_trip_ties_and_saturation():
+    finite = [c for c in range(256) if c not in (0x7F, 0xFF)]
+    vals = F8.e4m3_decode(np.array(finite))
+    assert np.array_equal(F8.e4m3_encode(vals), np.array(finite, dtype=np.uint8))
+    cases = [
+        (1.0625, 0x38),            # halfway 1.0 / 1.125: even mantissa
+        (1.1875, 0x3A),            # halfway 1.125 / 1.25: even mantissa
+        (1.5 * 2.0 ** -9, 0x02),   # halfway between subnormals 1 and 2
+        (0.5 * 2.0 ** -9, 0x00),   # halfway 0 / smallest subnormal
+        (0.75 * 2.0 ** -9, 0x01),
+        (1.96, 0x40),              # rounds up into the next binade (2.0)
+        (440.0, 0x7E),             # halfway 416 / 448: even mantissa (448)
+        (464.0, 0x7E), (1e9, 0x7E), (-1e9, 0xFE), (0.0, 0x00), (-0.0, 0x80),
+    ]
+    for x, code in cases:
+        assert int(F8.e4m3_encode(np.array([x]))[0]) == code, x
+
+
+def test_e4m3_encode_is_nearest_value_brute_force():
+    """Encoding == the finite E4M3 value nearest to x (ties to the even code),
+    found by scanning all 254 finite values in pure Python."""
+    finite = [c for c in range(256) if c not in (0x7F, 0xFF, 0x80)]
+    table = [(_e4m3_by_hand(c), c) for c in finite]
+    rng = np.random.default_rng(5)
+    xs = np.concatenate([rng.uniform(-500, 500, 400), rng.uniform(-0.05, 0.05, 400),
+                         rng.uniform(-3e-3, 3e-3, 200)])
+    got = F8.e4m3_encode(xs)
+    for x, g in zip(xs, got):
+        a = min(abs(x), 448.0)
+        best = min(table, key=lambda vc: (abs(abs(vc[0]) - a) if vc[0] >= 0 else 1e9,
+                                          vc[1] & 1))
+        want = best[1] | (0x80 if x < 0 else 0)
+        assert int(g) == want, (x, int(g), want)
+
+
+def test_fp8_row_quantisation():
+    rng = np.random.default_rng(6)
+    c = rng.standard_normal((5, 64)) * np.array([1, 1e-3, 50, 1, 1])[:, None]
+    c[4] = 0.0
+    s, q = F8.quantize_latent(c)
+    assert s[4] == 1.0 and not q[4].any()            # an all-zero row
+    amax = np.abs(c[:4]).max(axis=1)
+    assert np.allclose(s[:4], amax / 448.0, rtol=0, atol=0)
+    # the largest element of each row lands on +-448
+    i = np.abs(c[:4]).argmax(axis=1)
+    assert np.all(np.abs(F8.e4m3_decode(q[np.arange(4), i])) == 448.0)
+    # read-back error: at most half a grid step of the binade, relative 2^-4
+    back = F8.dequantize_latent(s, q)
+    rel = np.abs(back - c) / np.maximum(np.abs(c), 1e-300)
+    big = np.abs(c) / s[:, None] >= 2.0 ** -6
+    assert np.all(rel[big] <= 2.0 ** -4 + 1e-12)
+    # the fp32 decision path agrees with the fp64 one away from ties
+    s32, q32 = F8.quantize_latent(c.astype(np.float32), f32=True)
+    assert np.mean(q32 == q) > 0.99
+    # fp8_rows: latent read back, rope untouched, idempotent
+    rows = np.concatenate([c, rng.standard_normal((5, 8))], axis=1)
+    r1 = F8.fp8_rows(rows, 64)
+    assert np.array_equal(r1[:, 64:], rows[:, 64:])
+    assert np.allclose(F8.fp8_rows(r1, 64), r1, rtol=1e-14, atol=0)
+
+
+def test_fp8_cache_decode_step_stays_near_the_exact_one():
+    """A decode step through an FP8 cache (oracle.mla.mla_step with the
+    fp8_rows read-back) differs from the exact step, but by no more than the
+    format's relative precision 2^-4 (every latent value is read back within
+    2^-4 of itself), here on the tiny layer's 16-wide latent."""
+    d = synth.TINY
+    shp = shape_of(d)
+    w = synth.make_weights(d, 0.05, "f32", random_gains=True)
+    x = synth.hidden_states(0, 301, d.hidden, "f32")
+    prior = O.latent_rows(x[:300], np.arange(300), w["w_kva"], w["kv_norm_g"], shp)
+    exact = O.mla_step(x[300:], np.array([300]), prior, w, shp)["y"]
+    q8 = O.mla_step(x[300:], np.array([300]), prior, w, shp,
+                    kv_store=lambda r: F8.fp8_rows(r, shp.kv_lora))["y"]
+    assert 0 < rel_err(q8, exact) < 2.0 ** -4
