@@ -18,6 +18,10 @@ not flush caches); their mean is the core kernel's duration.
 Prints ONE JSON line.  Default workload: V2-Lite shapes, B = 64 sequences with
 cached lengths ~ U{512..8192} (``v2lite_decode_b64``).
 
+``--workload v2lite_decode_b64_fp8`` is the same decode batch on an FP8 latent
+cache (656-byte rows: E4M3 codes, bf16 RoPE key, per-row scale); its GB/s
+count those bytes.
+
 ``--workload v3_prefill_4x4096`` measures the chunked causal prefill instead
 (V3 shapes, 4 sequences of 4096 new tokens after 0 / 2048 cached rows): a step
 is the append of the new tokens' latent rows plus one mla_prefill call over the
@@ -43,6 +47,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, vendor figure
 ROW_BYTES = 1152               # one bf16 latent row: 512 + 64 values
+FP8_ROW_BYTES = 656            # one FP8 row: 512 codes, 64 bf16 rope values, scale, pad
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_core_v2lite_b64_traffic.json")
 CORE_SRC = os.path.join(ROOT, "mla_latent_kv_decode_amd", "csrc", "k_decode_ring.hip")
 
@@ -106,6 +111,12 @@ def cpu_baseline(wl, w, lens, budget_s: float):
     from oracle import mla as O
     from mla_latent_kv_decode_amd import synth
     d = wl.dims
+    store = None
+    row_bytes = ROW_BYTES
+    if wl.kv == "fp8":
+        from oracle import fp8 as F8
+        store = lambda r: F8.fp8_rows(r, d.kv_lora)  # noqa: E731
+        row_bytes = FP8_ROW_BYTES
     shp = O.MLAShape(hidden=d.hidden, n_heads=d.n_heads, qk_nope=d.qk_nope,
                      qk_rope=d.qk_rope, v_head=d.v_head, kv_lora=d.kv_lora, q_lora=d.q_lora,
                      rope_base=d.rope_base, rms_eps=d.rms_eps)
@@ -120,7 +131,7 @@ def cpu_baseline(wl, w, lens, budget_s: float):
                                                 shp))
             x, prior = prepared[b]
             t0 = time.perf_counter()
-            O.mla_step(x[L:], np.array([L]), prior, w, shp)
+            O.mla_step(x[L:], np.array([L]), prior, w, shp, kv_store=store)
             spent += time.perf_counter() - t0
             rows += L + 1
             toks += 1
@@ -132,7 +143,7 @@ def cpu_baseline(wl, w, lens, budget_s: float):
         cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
         cores = os.cpu_count()
-    return {"value": rows * ROW_BYTES / spent / 1e9, "unit": "GB/s", "cores": int(cores),
+    return {"value": rows * row_bytes / spent / 1e9, "unit": "GB/s", "cores": int(cores),
             "kind": "oracle", "tokens_per_s": toks / spent,
             "sample": f"{toks} sequence decodes over {passes} pass(es) of the {len(lens)}-sequence "
                       f"batch ({rows} latent rows), fp64 non-absorbed oracle, {spent:.1f} s"}
@@ -160,6 +171,12 @@ def cpu_baseline_prefill(wl, w, budget_s: float):
     from oracle import mla as O
     from mla_latent_kv_decode_amd import synth
     d = wl.dims
+    store = None
+    row_bytes = ROW_BYTES
+    if wl.kv == "fp8":
+        from oracle import fp8 as F8
+        store = lambda r: F8.fp8_rows(r, d.kv_lora)  # noqa: E731
+        row_bytes = FP8_ROW_BYTES
     shp = O.MLAShape(hidden=d.hidden, n_heads=d.n_heads, qk_nope=d.qk_nope,
                      qk_rope=d.qk_rope, v_head=d.v_head, kv_lora=d.kv_lora, q_lora=d.q_lora,
                      rope_base=d.rope_base, rms_eps=d.rms_eps)
@@ -299,12 +316,13 @@ def main():
 
     # ---- set-up (untimed): weights, caches filled by append
     w = synth.make_weights(d, wl.weight_std, wl.dtype)
-    layer = MLALayer(d, wl.dtype)
+    layer = MLALayer(d, wl.dtype, kv=wl.kv)
     layer.absorb_weights({k: torch.from_numpy(v).cuda().to(tdt) for k, v in w.items()})
     lens = synth.lengths(wl)
     seq_off, seq_len, total = synth.decode_layout(lens)
     B = len(lens)
-    caches = [torch.empty((total, d.row), dtype=tdt, device="cuda") for _ in range(2)]
+    caches = [layer.new_cache(total) for _ in range(2)]
+    row_bytes = layer.row_bytes()
     x_new = np.empty((B, d.hidden), np.float32)
     chunk = 8192
     for b in range(B):
@@ -369,15 +387,17 @@ def main():
         torch.cuda.synchronize()
     assert len(core) == K
     core_ms = float(np.mean(core))
-    cache_bytes = float(int(seq_len.sum()) * ROW_BYTES)
+    cache_bytes = float(int(seq_len.sum()) * row_bytes)
     weight_bytes = 2.0 * sum(v.size for v in w.values())
-    act_bytes = 2.0 * (2 * B * d.hidden + B * d.row)  # hidden in, y out, appended rows
+    act_bytes = 2.0 * 2 * B * d.hidden + B * row_bytes  # hidden in, y out, appended rows
     gbs = cache_bytes / t_step / 1e9
     core_gbs = cache_bytes / (core_ms * 1e-3) / 1e9
-    traffic = traffic_from_profile(cache_bytes)
+    fp8 = wl.kv == "fp8"
+    traffic = None if fp8 else traffic_from_profile(cache_bytes)
 
     res = {
-        "metric": "MLA decode latent-KV GB/s + tokens/s (V2-Lite shapes, B=64), % of HBM peak",
+        "metric": "MLA decode latent-KV GB/s + tokens/s (V2-Lite shapes, B=64), % of HBM peak"
+                  + (", FP8 latent cache" if fp8 else ""),
         "value": round(gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -394,10 +414,12 @@ def main():
         "data": "synthetic",
         "timing": "eager" if graph is None else "hip-graph replay of the K steps",
         "config": {"workload": wl.name, "batch": B, "len_lo": wl.len_lo, "len_hi": wl.len_hi,
-                   "latent_rows": int(seq_len.sum()), "cache_bytes": int(cache_bytes),
+                   "latent_rows": int(seq_len.sum()), "cache_row_bytes": row_bytes,
+                   "cache_bytes": int(cache_bytes),
                    "weight_bytes": int(weight_bytes), "hidden": d.hidden, "heads": d.n_heads,
                    "kv_lora": d.kv_lora, "qk_rope": d.qk_rope},
-        "roofline": {"kernel": "decode_core_ring_k", "bound": "hbm",
+        "roofline": {"kernel": "decode_core_ring8_k" if fp8 else "decode_core_ring_k",
+                     "bound": "hbm",
                      "kernel_timing": "HIP events (no system fence) around every split-S core "
                                       "launch, K eager steps",
                      "achieved": round(core_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

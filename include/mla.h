@@ -28,7 +28,8 @@
  *   [K_nope_h ; V_h] ("Deepseek V2 Lite Inference Engine in C", MLA notes:
  *   the K and V values of each head are interleaved).  kv_a_proj rows are
  *   [latent (kv_lora) ; rope key (qk_rope)].  The cache is (cache_rows, R)
- *   with R = kv_lora + qk_rope.
+ *   with R = kv_lora + qk_rope, or cache_rows rows of mla_cache_row_bytes
+ *   bytes when the config asks for FP8 rows (mla_kv_storage).
  * Ownership.  The caller owns every tensor, cache, output and workspace
  *   buffer.  The library owns only the handle, its repacked weight copies and
  *   its pinned staging memory.
@@ -56,7 +57,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 1
+#define MLA_ABI_VERSION 2
 
 typedef enum mla_status {
   MLA_OK = 0,
@@ -69,6 +70,18 @@ typedef enum mla_status {
 } mla_status;
 
 typedef enum mla_dtype { MLA_BF16 = 0, MLA_F32 = 1 } mla_dtype;
+
+/* How the latent cache stores a row.  MLA_KV_DTYPE: R = kv_lora + qk_rope
+ * values of the layer dtype.  MLA_KV_FP8_E4M3 ("Multi-Head Latent Attention"
+ * post: low-precision storage, introduction; 1-byte FP8 cache elements,
+ * section 3.1): fp8_row_bytes = 656 bytes per row for kv_lora 512 / qk_rope
+ * 64, laid out as [kv_lora OCP FP8 E4M3 codes | qk_rope bf16 | fp32 scale s |
+ * zero pad to a multiple of 16]; the latent values are c_i = s * value(code_i)
+ * with s = max_i |c_i| / 448 (1 for an all-zero row) and code_i the E4M3
+ * value nearest c_i / s (ties to even).  FP8 needs dtype MLA_BF16, kv_lora
+ * 512, qk_rope 64 and n_heads a multiple of 16 that is not a multiple of 128;
+ * it serves append and decode (mla_prefill reads bf16 caches only). */
+typedef enum mla_kv_storage { MLA_KV_DTYPE = 0, MLA_KV_FP8_E4M3 = 1 } mla_kv_storage;
 
 /* Layer dimensions (MLA post, section 3.2 constructor; section 3.6 widths).
  * qk_rope must be even (RoPE rotates pairs; MLA post section 3.7).  q_lora = 0
@@ -85,17 +98,24 @@ typedef struct mla_config {
   float rope_base;   /* RoPE base, e.g. 10000 */
   float rms_eps;     /* RMSNorm epsilon, e.g. 1e-6 */
   float softmax_scale; /* 0 -> 1/sqrt(dn + dr) */
-  int32_t dtype;     /* mla_dtype: storage type of every tensor */
+  int32_t dtype;     /* mla_dtype: storage type of every tensor (but see kv_storage) */
+  int32_t kv_storage; /* mla_kv_storage: format of the latent cache rows */
 } mla_config;
 
 typedef struct mla_ctx* mla_handle;
 
 /* Host-only check of a configuration: MLA_OK, MLA_ERR_INVALID_ARG (cfg NULL,
  * a dimension <= 0 other than qk_rope/q_lora, a negative one, unknown dtype,
- * non-finite or non-positive base/eps) or MLA_ERR_SHAPE (odd qk_rope,
- * qk_rope > 128, kv_lora > 1024, v_head > 256).  Makes no HIP call;
- * mla_create runs it first. */
+ * non-finite or non-positive base/eps, unknown kv_storage) or MLA_ERR_SHAPE
+ * (odd qk_rope, qk_rope > 128, kv_lora > 1024, v_head > 256, FP8 rows for a
+ * layer outside the FP8 shapes).  Makes no HIP call; mla_create runs it
+ * first. */
 int mla_config_check(const mla_config* cfg);
+
+/* Bytes of one cached latent row under cfg (R * element size, or the FP8 row
+ * size); 0 if mla_config_check fails.  Host only.  A cache of cache_rows rows
+ * is cache_rows * mla_cache_row_bytes(cfg) bytes. */
+size_t mla_cache_row_bytes(const mla_config* cfg);
 
 /* Host-only argument checks, run first by the corresponding calls and exported
  * so callers (and tests without a GPU) can validate before enqueuing.  They
@@ -136,9 +156,11 @@ size_t mla_append_workspace_bytes(mla_handle h, int32_t T);
 
 /* A2 -- append T tokens to the latent cache: a = W_kva x;
  * cache[slot[t]] = [RMSNorm(a[:dc]) * kv_norm_g | RoPE(a[dc:], pos[t])],
- * rounded to the storage type ("Deepseek V2 Lite Inference Engine in C", MLA
- * notes: kv_a_proj fuses the down-projection and the shared rope key; MLA post
- * sections 3.5 and 3.7).  hidden: device (T, D).  pos, slot: HOST arrays of T
+ * rounded to the storage type, or for FP8 rows the latent part quantised
+ * from its fp32 values as mla_kv_storage describes and the rope part rounded
+ * to bf16 ("Deepseek V2 Lite Inference Engine in C", MLA notes: kv_a_proj
+ * fuses the down-projection and the shared rope key; MLA post sections 3.5
+ * and 3.7).  hidden: device (T, D).  pos, slot: HOST arrays of T
  * entries; pos >= 0; slots must be distinct and in [0, cache_rows)
  * (MLA_ERR_CAPACITY otherwise, the KV-cache page's overflow condition).
  * Rows not named in slot are not touched. */
@@ -146,10 +168,17 @@ int mla_append_latent(mla_handle h, const void* hidden, const int32_t* pos,
                       const int64_t* slot, int32_t T, void* cache, int64_t cache_rows,
                       void* ws, size_t ws_bytes);
 
-/* Raw scatter of T ready-made rows (T, R) into cache[slot[t]] -- the indexing
- * half of mla_append_latent on its own (bit-exact copy).  Same slot rules. */
+/* Raw scatter of T ready-made rows into cache[slot[t]] -- the indexing half of
+ * mla_append_latent on its own (bit-exact copy).  rows: device, T rows in the
+ * cache's own format (T x R values, or T x mla_cache_row_bytes bytes for FP8
+ * rows).  Same slot rules.  mla_cache_store takes the same arguments but rows
+ * of R values in the layer dtype and stores them in the cache's format
+ * (quantised as mla_kv_storage describes for FP8 rows, from the values as
+ * given; a plain copy otherwise); its workspace is mla_cache_write's. */
 size_t mla_cache_write_workspace_bytes(mla_handle h, int32_t T);
 int mla_cache_write(mla_handle h, const void* rows, const int64_t* slot, int32_t T,
+                    void* cache, int64_t cache_rows, void* ws, size_t ws_bytes);
+int mla_cache_store(mla_handle h, const void* rows, const int64_t* slot, int32_t T,
                     void* cache, int64_t cache_rows, void* ws, size_t ws_bytes);
 
 /* Workspace bytes mla_decode needs for B sequences holding total_rows cache
@@ -234,7 +263,8 @@ size_t mla_prefill_workspace_bytes(mla_handle h, int32_t T, int32_t B,
  *   hidden: device (T, D), T = cu_new[B]; out: device (T, D).
  *   cu_new: HOST (B+1), cu_new[0] = 0, non-decreasing; prior_len, seq_off:
  *   HOST (B).
- * Errors as for mla_decode (CAPACITY if a sequence's rows leave the cache). */
+ * Errors as for mla_decode (CAPACITY if a sequence's rows leave the cache);
+ * SHAPE for a handle whose cache holds FP8 rows. */
 int mla_prefill(mla_handle h, const void* hidden, const int32_t* cu_new,
                 const int32_t* prior_len, const int64_t* seq_off, int32_t B,
                 const void* cache, int64_t cache_rows, void* out, void* ws,

@@ -170,10 +170,17 @@ __global__ void __launch_bounds__(256)
 step_finish_k(Part a, const int32_t* __restrict__ pos, const int64_t* __restrict__ slot,
               const T* __restrict__ gamma, T* __restrict__ cache, T* __restrict__ q_nope,
               T* __restrict__ rope_out, int64_t tok_stride, int64_t head_stride, float scale,
-              Dims d, RopeTab rt) {
+              Dims d, RopeTab rt, int kv8) {
   __shared__ float red[4];
   const int t = blockIdx.x;
   if (blockIdx.y == 0) {
+    if constexpr (sizeof(T) == 2) {
+      if (kv8) {  // the cache holds FP8 rows
+        append_row_block_fp8(a, t, pos[t], slot[t], gamma, reinterpret_cast<uint8_t*>(cache), d,
+                             rt, red);
+        return;
+      }
+    }
     append_row_block<T>(a, t, pos[t], slot[t], gamma, cache, d, rt, red);
     return;
   }
@@ -189,11 +196,11 @@ template <typename T>
 void step_finish(const Part& a, int ntok, const int32_t* pos, const int64_t* slot,
                  const T* gamma, T* cache, T* q_nope, T* rope_out, int64_t tok_stride,
                  int64_t head_stride, float scale, const Dims& d, const RopeTab& rt,
-                 hipStream_t st) {
+                 hipStream_t st, bool kv8) {
   const int g = q_heads_per_block(d);
   dim3 grid(ntok, 1 + (d.H + g - 1) / g);
   step_finish_k<T><<<grid, 256, 0, st>>>(a, pos, slot, gamma, cache, q_nope, rope_out,
-                                          tok_stride, head_stride, scale, d, rt);
+                                          tok_stride, head_stride, scale, d, rt, kv8 ? 1 : 0);
 }
 
 template <typename T>
@@ -213,6 +220,54 @@ void transpose_heads(const T* in, T* out, int H, int rows, int cols, int64_t str
                      hipStream_t st) {
   dim3 grid((unsigned)(((int64_t)rows * cols + 255) / 256), H);
   transpose_heads_k<T><<<grid, 256, 0, st>>>(in, out, rows, cols, stride);
+}
+
+__global__ void __launch_bounds__(256)
+append_rows_fp8_k(Part a, const int32_t* __restrict__ pos, const int64_t* __restrict__ slot,
+                  const bf16* __restrict__ gamma, uint8_t* __restrict__ cache, Dims d, RopeTab rt) {
+  __shared__ float red[4];
+  const int t = blockIdx.x;
+  append_row_block_fp8(a, t, pos[t], slot[t], gamma, cache, d, rt, red);
+}
+
+void append_rows_fp8(const Part& a, int ntok, const int32_t* pos, const int64_t* slot,
+                     const bf16* gamma, uint8_t* cache, const Dims& d, const RopeTab& rt,
+                     hipStream_t st) {
+  append_rows_fp8_k<<<ntok, 256, 0, st>>>(a, pos, slot, gamma, cache, d, rt);
+}
+
+// rows (T x R, bf16) -> FP8 rows: the latent part quantised as the append
+// does, the rope part copied
+__global__ void __launch_bounds__(256)
+cache_store_fp8_k(const bf16* __restrict__ rows, const int64_t* __restrict__ slot,
+                  uint8_t* __restrict__ cache, Dims d) {
+  __shared__ float red[4];
+  const int t = blockIdx.x;
+  const bf16* src = rows + (int64_t)t * d.R;
+  uint8_t* row = cache + slot[t] * (int64_t)fp8_row_bytes(d.dc, d.dr);
+  store_latent_fp8([&](int j) { return bf16_to_f32(src[j]); }, row, d, red);
+  bf16* rope = reinterpret_cast<bf16*>(row + d.dc);
+  for (int i = threadIdx.x; i < d.dr; i += blockDim.x) rope[i] = src[d.dc + i];
+}
+
+void cache_store_fp8(const bf16* rows, const int64_t* slot, int ntok, uint8_t* cache,
+                     const Dims& d, hipStream_t st) {
+  cache_store_fp8_k<<<ntok, 256, 0, st>>>(rows, slot, cache, d);
+}
+
+// raw scatter of whole rows (row_bytes a multiple of 16)
+__global__ void cache_write_bytes_k(const uint8_t* __restrict__ rows,
+                                    const int64_t* __restrict__ slot, int row_bytes,
+                                    uint8_t* __restrict__ cache) {
+  const int t = blockIdx.x;
+  const uint4* src = reinterpret_cast<const uint4*>(rows + (int64_t)t * row_bytes);
+  uint4* dst = reinterpret_cast<uint4*>(cache + slot[t] * (int64_t)row_bytes);
+  for (int j = threadIdx.x; j < row_bytes / 16; j += blockDim.x) dst[j] = src[j];
+}
+
+void cache_write_bytes(const uint8_t* rows, const int64_t* slot, int ntok, int row_bytes,
+                       uint8_t* cache, hipStream_t st) {
+  cache_write_bytes_k<<<ntok, 64, 0, st>>>(rows, slot, row_bytes, cache);
 }
 
 template <typename T>
@@ -421,7 +476,7 @@ void prefill_attn_generic(const T* q_nope, const T* q_rope, const float* kv, con
                             float, const Dims&, const RopeTab&, hipStream_t);                \
   template void step_finish<T>(const Part&, int, const int32_t*, const int64_t*, const T*,   \
                                T*, T*, T*, int64_t, int64_t, float, const Dims&,             \
-                               const RopeTab&, hipStream_t);                                 \
+                               const RopeTab&, hipStream_t, bool);                           \
   template void cache_write<T>(const T*, const int64_t*, int, int, T*, hipStream_t);         \
   template void transpose_heads<T>(const T*, T*, int, int, int, int64_t, hipStream_t);        \
   template void decode_core_generic<T>(const T*, const T*, const DecodeMeta&, int, float*,   \

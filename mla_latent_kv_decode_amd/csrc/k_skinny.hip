@@ -193,8 +193,8 @@ __global__ void __launch_bounds__(256)
 finish_k(const bf16* __restrict__ q_nope, const bf16* __restrict__ w_ukT,
          bf16* __restrict__ q_cat, int B, int nab, int nap, const float* __restrict__ a, int lda,
          int qa_col, const int32_t* __restrict__ pos, const int64_t* __restrict__ slot,
-         const bf16* __restrict__ kv_gamma, bf16* __restrict__ cache, const bf16* q_gamma,
-         bf16* __restrict__ cq, Dims d, RopeTab rt) {
+         const bf16* __restrict__ kv_gamma, void* __restrict__ cache, const bf16* q_gamma,
+         bf16* __restrict__ cq, Dims d, RopeTab rt, int kv8) {
   __shared__ float red[4];
   const int blk = blockIdx.x;
   if (blk >= nab + nap) {  // RMSNorm of the query down-projection row
@@ -214,7 +214,12 @@ finish_k(const bf16* __restrict__ q_nope, const bf16* __restrict__ w_ukT,
     p.ks = 1;
     p.ld = lda;
     p.zs = 0;
-    append_row_block<bf16>(p, t, pos[t], slot[t], kv_gamma, cache, d, rt, red);
+    if (kv8)
+      append_row_block_fp8(p, t, pos[t], slot[t], kv_gamma, static_cast<uint8_t*>(cache), d, rt,
+                           red);
+    else
+      append_row_block<bf16>(p, t, pos[t], slot[t], kv_gamma, static_cast<bf16*>(cache), d, rt,
+                             red);
     return;
   }
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -298,14 +303,14 @@ void skinny_query(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int M,
 
 void decode_finish(const bf16* q_nope, const bf16* w_ukT, bf16* q_cat, int B, bool absorb,
                    bool append, bool qnorm, const float* a, int lda, int qa_col, const int32_t* pos,
-                   const int64_t* slot, const bf16* kv_gamma, bf16* cache, const bf16* q_gamma,
-                   bf16* cq, const Dims& d, const RopeTab& rt, hipStream_t st) {
+                   const int64_t* slot, const bf16* kv_gamma, void* cache, const bf16* q_gamma,
+                   bf16* cq, const Dims& d, const RopeTab& rt, hipStream_t st, bool kv8) {
   const int nab = absorb ? d.H * 4 : 0, nap = append ? B : 0, nqn = qnorm ? B : 0;
   const int blocks = nab + nap + nqn;
   if (blocks == 0) return;
 #define MLA_FIN(MT)                                                                          \
   skn::finish_k<MT><<<blocks, 256, 0, st>>>(q_nope, w_ukT, q_cat, B, nab, nap, a, lda, qa_col, pos, \
-                                            slot, kv_gamma, cache, q_gamma, cq, d, rt)
+                                            slot, kv_gamma, cache, q_gamma, cq, d, rt, kv8 ? 1 : 0)
   switch ((B + 15) / 16) {
     case 1: MLA_FIN(1); break;
     case 2: MLA_FIN(2); break;

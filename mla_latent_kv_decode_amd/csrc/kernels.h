@@ -23,6 +23,12 @@ struct RopeTab {
   double theta[kMaxRopePairs];
 };
 
+// Bytes per cached row of an FP8 latent cache: dc OCP E4M3 codes, dr bf16
+// rope values, the fp32 row scale, zero-padded to a multiple of 16.
+__host__ __device__ constexpr int fp8_row_bytes(int dc, int dr) {
+  return (dc + 2 * dr + 4 + 15) / 16 * 16;
+}
+
 // One decode work segment: rows [r0, r1) of sequence b (row indices relative
 // to the sequence start), whose partial result goes to slot pidx.
 struct DecodeSeg {
@@ -114,7 +120,7 @@ template <typename T>
 void step_finish(const Part& a, int ntok, const int32_t* pos, const int64_t* slot,
                  const T* gamma, T* cache, T* q_nope, T* rope_out, int64_t tok_stride,
                  int64_t head_stride, float scale, const Dims& d, const RopeTab& rt,
-                 hipStream_t st);
+                 hipStream_t st, bool kv8 = false);  // kv8: `cache` holds FP8 rows (bf16 only)
 // per-head transpose: out[h][c][n] = in[h*stride + n*cols + c], n < rows, c < cols
 template <typename T>
 void transpose_heads(const T* in, T* out, int H, int rows, int cols, int64_t stride,
@@ -145,9 +151,9 @@ void skinny_query(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int M,
 // qnorm:  cq[t] = RMSNorm(a[t][qa_col : qa_col + dq]) * q_gamma (bf16).
 void decode_finish(const bf16* q_nope, const bf16* w_ukT, bf16* q_cat, int B, bool absorb,
                    bool append, bool qnorm, const float* a, int lda, int qa_col,
-                   const int32_t* pos, const int64_t* slot, const bf16* kv_gamma, bf16* cache,
+                   const int32_t* pos, const int64_t* slot, const bf16* kv_gamma, void* cache,
                    const bf16* q_gamma, bf16* cq, const Dims& d, const RopeTab& rt,
-                   hipStream_t st);
+                   hipStream_t st, bool kv8 = false);  // kv8: `cache` holds FP8 rows
 
 // ---- decode core (split-S) and combine
 // partial layout: acc[pidx][h][dc] fp32, ml[pidx][h][2] = (max in log2 units, sum)
@@ -160,6 +166,19 @@ void decode_core_generic(const T* q_cat, const T* cache, const DecodeMeta& m, in
 int decode_core_wide_heads();
 void decode_core_wide(const bf16* q_cat, const bf16* cache, const DecodeMeta& m, int parts,
                       float* acc, float* ml, const Dims& d, hipStream_t st);
+// FP8 latent cache (rows of fp8_row_bytes(dc, dr) bytes, dc == 512, dr == 64):
+// the latent row append (as append_rows, into FP8 rows), the store of rows
+// given in bf16 (T x R) into FP8 rows, a raw row-byte scatter, and the ring
+// core reading FP8 rows (otherwise as decode_core_ring).
+void append_rows_fp8(const Part& a, int ntok, const int32_t* pos, const int64_t* slot,
+                     const bf16* gamma, uint8_t* cache, const Dims& d, const RopeTab& rt,
+                     hipStream_t st);
+void cache_store_fp8(const bf16* rows, const int64_t* slot, int ntok, uint8_t* cache,
+                     const Dims& d, hipStream_t st);
+void cache_write_bytes(const uint8_t* rows, const int64_t* slot, int ntok, int row_bytes,
+                       uint8_t* cache, hipStream_t st);
+void decode_core_ring8(const bf16* q_cat, const uint8_t* cache, const DecodeMeta& m, int parts,
+                       float* acc, float* ml, bf16* o_lat, const Dims& d, hipStream_t st);
 // MFMA core over a ring of shared row tiles (bf16, dc == 512, dr == 64,
 // H % 16 == 0): one workgroup per (part, 16-head group), parts = persistent
 // workgroups per head group.  Partials as for the generic core, except that a

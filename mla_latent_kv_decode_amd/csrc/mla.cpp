@@ -57,6 +57,7 @@ struct mla_ctx {
   size_t esz = 2;
   bool absorbed = false;
   bool mfma = false;  // bf16 MFMA kernels apply to these shapes
+  bool kv8 = false;   // the latent cache holds FP8 rows (mla_config.kv_storage)
   // owned device weights
   void* w_q = nullptr;
   void* w_qa = nullptr;
@@ -588,7 +589,21 @@ int mla_config_check(const mla_config* c) {
   // kernel limits of the VALU paths: latent width and v_head per thread block
   if (c->kv_lora > 1024 || c->v_head > 256) return MLA_ERR_SHAPE;
   if (c->qk_rope > 2 * mla::kMaxRopePairs) return MLA_ERR_SHAPE;
+  if (c->kv_storage != MLA_KV_DTYPE && c->kv_storage != MLA_KV_FP8_E4M3)
+    return MLA_ERR_INVALID_ARG;
+  if (c->kv_storage == MLA_KV_FP8_E4M3) {
+    // the FP8 rows are read by the 16-head-group MFMA core only
+    if (c->dtype != MLA_BF16 || c->kv_lora != 512 || c->qk_rope != 64 || c->n_heads % 16 ||
+        c->n_heads % mla::decode_core_wide_heads() == 0)
+      return MLA_ERR_SHAPE;
+  }
   return MLA_OK;
+}
+
+size_t mla_cache_row_bytes(const mla_config* c) {
+  if (mla_config_check(c) != MLA_OK) return 0;
+  if (c->kv_storage == MLA_KV_FP8_E4M3) return (size_t)mla::fp8_row_bytes(c->kv_lora, c->qk_rope);
+  return (size_t)(c->kv_lora + c->qk_rope) * (c->dtype == MLA_F32 ? 4 : 2);
 }
 
 static int check_slots_pure(const int64_t* slot, int32_t T, int64_t cache_rows, int32_t* bad) {
@@ -664,6 +679,7 @@ int mla_create(const mla_config* cfg, void* stream, mla_handle* out) {
       ncu > 0)
     h->n_cu = ncu;
   h->mfma = cfg->dtype == MLA_BF16 && d.dc == 512 && d.dr == 64 && d.H % 16 == 0;
+  h->kv8 = cfg->kv_storage == MLA_KV_FP8_E4M3;
   h->n_in = d.R + (d.dq ? d.dq : qw_of(d));
   *out = h;
   return MLA_OK;
@@ -854,10 +870,17 @@ int mla_append_latent(mla_handle h, const void* hidden, const int32_t* pos, cons
   memcpy(blob.data() + L.pos, pos, (size_t)T * 4);
   memcpy(blob.data() + L.slot, slot, (size_t)T * 8);
   if ((rc = stage_upload(h, ws, blob.data(), blob.size()))) return rc;
-  if (is_f32(h))
+  if (is_f32(h)) {
     run_append<float>(h, (const float*)hidden, T, (float*)cache, ws, L);
-  else
+  } else if (h->kv8) {
+    const Dims& d = h->d;
+    const mla::Part a = gemm_part<bf16>(h, (const bf16*)hidden, d.D, (const bf16*)h->w_kva, d.D, T,
+                                        d.R, d.D, at<float>(ws, L.part));
+    mla::append_rows_fp8(a, T, at<int32_t>(ws, L.pos), at<int64_t>(ws, L.slot),
+                         (const bf16*)h->kv_norm_g, (uint8_t*)cache, d, h->rope, h->stream);
+  } else {
     run_append<bf16>(h, (const bf16*)hidden, T, (bf16*)cache, ws, L);
+  }
   return check_launch(h, "append");
 }
 
@@ -879,13 +902,35 @@ int mla_cache_write(mla_handle h, const void* rows, const int64_t* slot, int32_t
   DeviceGuard g(h->device);
   if (!g.ok) return fail(h, MLA_ERR_HIP, "cannot select device %d", h->device);
   if ((rc = stage_upload(h, ws, slot, (size_t)T * 8))) return rc;
-  if (is_f32(h))
+  if (h->kv8)
+    mla::cache_write_bytes((const uint8_t*)rows, (const int64_t*)ws, T,
+                           (int)mla_cache_row_bytes(&h->cfg), (uint8_t*)cache, h->stream);
+  else if (is_f32(h))
     mla::cache_write<float>((const float*)rows, (const int64_t*)ws, T, h->d.R, (float*)cache,
                             h->stream);
   else
     mla::cache_write<bf16>((const bf16*)rows, (const int64_t*)ws, T, h->d.R, (bf16*)cache,
                            h->stream);
   return check_launch(h, "cache_write");
+}
+
+int mla_cache_store(mla_handle h, const void* rows, const int64_t* slot, int32_t T, void* cache,
+                    int64_t cache_rows, void* ws, size_t ws_bytes) {
+  if (!h) return MLA_ERR_INVALID_ARG;
+  if (!h->kv8) return mla_cache_write(h, rows, slot, T, cache, cache_rows, ws, ws_bytes);
+  if (T <= 0 || !rows || !slot || !cache || cache_rows <= 0)
+    return fail(h, MLA_ERR_INVALID_ARG, "cache_store: bad argument (T=%d)", T);
+  int32_t bad = 0;
+  int rc = check_slots_pure(slot, T, cache_rows, &bad);
+  if (rc) return fail(h, rc, "cache_store: slot[%d] = %lld is out of range or repeated", bad,
+                      (long long)slot[bad]);
+  if ((rc = check_ws(h, ws, ws_bytes, mla_cache_write_workspace_bytes(h, T)))) return rc;
+  DeviceGuard g(h->device);
+  if (!g.ok) return fail(h, MLA_ERR_HIP, "cannot select device %d", h->device);
+  if ((rc = stage_upload(h, ws, slot, (size_t)T * 8))) return rc;
+  mla::cache_store_fp8((const bf16*)rows, (const int64_t*)ws, T, (uint8_t*)cache, h->d,
+                       h->stream);
+  return check_launch(h, "cache_store");
 }
 
 // ------------------------------------------------------------------------
@@ -948,11 +993,15 @@ static void run_q_and_append(mla_ctx* h, const T* x, int B, void* ws, const Deco
                                        at<float>(ws, L.pin));
     if (!d.dq) {
       mla::step_finish<T>(pin, B, mt.pos, slot_dev, (const T*)h->kv_norm_g, cache, q_nope, q_rope,
-                          tok_stride, d.R, d.scale, d, h->rope, h->stream);
+                          tok_stride, d.R, d.scale, d, h->rope, h->stream, h->kv8);
       return;
     }
-    mla::append_rows<T>(pin, B, mt.pos, slot_dev, (const T*)h->kv_norm_g, cache, d, h->rope,
-                        h->stream);
+    if (h->kv8)
+      mla::append_rows_fp8(pin, B, mt.pos, slot_dev, (const bf16*)h->kv_norm_g,
+                           (uint8_t*)(void*)cache, d, h->rope, h->stream);
+    else
+      mla::append_rows<T>(pin, B, mt.pos, slot_dev, (const T*)h->kv_norm_g, cache, d, h->rope,
+                          h->stream);
     mla::Part pa = pin;
     pa.p += d.R;
     mla::rmsnorm_rows<T>(pa, B, d.dq, (const T*)h->q_norm_g, d.eps, at<T>(ws, L.cq), h->stream);
@@ -1012,12 +1061,12 @@ static void q_skinny_rest(mla_ctx* h, int B, void* ws, const DecodeLayout& L,
   const int R = L.step ? d.R : 0;  // kv_a columns in front of the query columns
   if (!d.dq) {
     mla::decode_finish(q_nope, w_ukT, q_cat, B, true, L.step, false, a, R, 0, mt.pos, slot_dev,
-                       kv_g, cache, nullptr, nullptr, d, h->rope, h->stream);
+                       kv_g, cache, nullptr, nullptr, d, h->rope, h->stream, h->kv8);
     return;
   }
   bf16* cq = at<bf16>(ws, L.cq);
   mla::decode_finish(q_nope, w_ukT, q_cat, B, false, L.step, true, a, n1, R, mt.pos, slot_dev,
-                     kv_g, cache, (const bf16*)h->q_norm_g, cq, d, h->rope, h->stream);
+                     kv_g, cache, (const bf16*)h->q_norm_g, cq, d, h->rope, h->stream, h->kv8);
   mla::skinny_query(cq, d.dq, (const bf16*)h->w_qb, d.dq, B, qw, d.dq, nullptr, 0, q_nope, q_cat,
                     pos_host, d, h->rope, h->stream);
   mla::decode_finish(q_nope, w_ukT, q_cat, B, true, false, false, nullptr, 0, 0, mt.pos,
@@ -1058,6 +1107,9 @@ static int run_decode(mla_ctx* h, const T* hidden, int B, T* cache, T* out, void
     if (h->mfma) {
       if (wide_core(h))
         mla::decode_core_wide(q_cat, cache, mt, parts, acc, ml, d, h->stream);
+      else if (h->kv8)  // FP8 rows; otherwise as the bf16 ring core
+        mla::decode_core_ring8(q_cat, (const uint8_t*)(const void*)cache, mt, parts, acc, ml,
+                               (bf16*)o_lat, d, h->stream);
       else  // sequences inside one segment are finished into o_lat by the core
         mla::decode_core_ring(q_cat, cache, mt, parts, acc, ml, (bf16*)o_lat, d, h->stream);
       mfma_core = true;
@@ -1302,6 +1354,9 @@ int mla_prefill(mla_handle h, const void* hidden, const int32_t* cu_new, const i
   if (rc0) return fail(h, rc0, "prefill: %s (B=%d, cache_rows=%lld)", mla_status_string(rc0), B,
                        (long long)cache_rows);
   if (!h->absorbed) return fail(h, MLA_ERR_STATE, "prefill before mla_absorb_weights");
+  if (h->kv8)
+    return fail(h, MLA_ERR_SHAPE, "prefill: the expansion reads bf16 latent rows; FP8 caches "
+                                  "are decode-only");
   int64_t rows = 0;
   std::vector<int64_t> kv_off(B);
   for (int32_t b = 0; b < B; ++b) {

@@ -25,6 +25,8 @@ MLA_ERR_HIP = -5
 MLA_ERR_WORKSPACE = -6
 MLA_BF16 = 0
 MLA_F32 = 1
+MLA_KV_DTYPE = 0
+MLA_KV_FP8_E4M3 = 1
 
 _P = ctypes.c_void_p
 _I32P = ctypes.POINTER(ctypes.c_int32)
@@ -37,7 +39,7 @@ class MLAConfig(ctypes.Structure):
                 ("v_head", ctypes.c_int32), ("kv_lora", ctypes.c_int32),
                 ("q_lora", ctypes.c_int32), ("rope_base", ctypes.c_float),
                 ("rms_eps", ctypes.c_float), ("softmax_scale", ctypes.c_float),
-                ("dtype", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("kv_storage", ctypes.c_int32)]
 
 
 # name -> (restype, argtypes)
@@ -46,6 +48,7 @@ _SIGS = {
     "mla_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "mla_last_error": (ctypes.c_char_p, [_P]),
     "mla_config_check": (ctypes.c_int, [ctypes.POINTER(MLAConfig)]),
+    "mla_cache_row_bytes": (ctypes.c_size_t, [ctypes.POINTER(MLAConfig)]),
     "mla_append_check": (ctypes.c_int, [ctypes.POINTER(MLAConfig), _I32P, _I64P, ctypes.c_int32,
                                         ctypes.c_int64]),
     "mla_decode_check": (ctypes.c_int, [ctypes.POINTER(MLAConfig), _I32P, _I64P, _I32P,
@@ -61,6 +64,8 @@ _SIGS = {
                                          ctypes.c_int64, _P, ctypes.c_size_t]),
     "mla_cache_write_workspace_bytes": (ctypes.c_size_t, [_P, ctypes.c_int32]),
     "mla_cache_write": (ctypes.c_int, [_P, _P, _I64P, ctypes.c_int32, _P, ctypes.c_int64, _P,
+                                       ctypes.c_size_t]),
+    "mla_cache_store": (ctypes.c_int, [_P, _P, _I64P, ctypes.c_int32, _P, ctypes.c_int64, _P,
                                        ctypes.c_size_t]),
     "mla_decode_workspace_bytes": (ctypes.c_size_t, [_P, ctypes.c_int32, ctypes.c_int64]),
     "mla_decode": (ctypes.c_int, [_P, _P, _I32P, _I64P, _I32P, ctypes.c_int32, _P,
@@ -108,10 +113,12 @@ class MLAError(RuntimeError):
         self.status = status
 
 
-def make_config(dims, dtype: str, softmax_scale: float = 0.0) -> MLAConfig:
+def make_config(dims, dtype: str, softmax_scale: float = 0.0, kv: str = "dtype") -> MLAConfig:
+    """kv: "dtype" (cache rows in the layer dtype) or "fp8" (FP8 E4M3 rows)."""
     return MLAConfig(dims.hidden, dims.n_heads, dims.qk_nope, dims.qk_rope, dims.v_head,
                      dims.kv_lora, dims.q_lora, float(dims.rope_base), float(dims.rms_eps),
-                     float(softmax_scale), MLA_BF16 if dtype == "bf16" else MLA_F32)
+                     float(softmax_scale), MLA_BF16 if dtype == "bf16" else MLA_F32,
+                     MLA_KV_FP8_E4M3 if kv == "fp8" else MLA_KV_DTYPE)
 
 
 def _i32(a):
@@ -154,13 +161,15 @@ class Workspace:
 class MLALayer:
     """One MLA layer bound to a library handle on the current device/stream."""
 
-    def __init__(self, dims, dtype: str = "bf16", softmax_scale: float = 0.0, device="cuda"):
+    def __init__(self, dims, dtype: str = "bf16", softmax_scale: float = 0.0, device="cuda",
+                 kv: str = "dtype"):
         import torch
         self.lib = load()
         self.dims = dims
         self.dtype = dtype
+        self.kv = kv
         self.torch_dtype = torch.bfloat16 if dtype == "bf16" else torch.float32
-        self.cfg = make_config(dims, dtype, softmax_scale)
+        self.cfg = make_config(dims, dtype, softmax_scale, kv)
         self.device = torch.device(device)
         h = ctypes.c_void_p()
         self._check(self.lib.mla_create(ctypes.byref(self.cfg), _stream_ptr(), ctypes.byref(h)),
@@ -230,6 +239,27 @@ class MLALayer:
         rc = self.lib.mla_cache_write(self.h, _ptr(rows), slot_p, T, _ptr(cache),
                                       int(cache.shape[0]), wsp, wsn)
         self._check(rc, self.h, "mla_cache_write")
+
+    def cache_store(self, rows, slot, cache):
+        """rows (T, R) in the layer dtype, stored in the cache's own format."""
+        self._sync_stream()
+        T = int(rows.shape[0])
+        slot_a, slot_p = _i64(slot)
+        wsp, wsn = self.ws.get(self.lib.mla_cache_write_workspace_bytes(self.h, T))
+        rc = self.lib.mla_cache_store(self.h, _ptr(rows), slot_p, T, _ptr(cache),
+                                      int(cache.shape[0]), wsp, wsn)
+        self._check(rc, self.h, "mla_cache_store")
+
+    def row_bytes(self) -> int:
+        return int(self.lib.mla_cache_row_bytes(ctypes.byref(self.cfg)))
+
+    def new_cache(self, rows: int, fill=None):
+        """An empty latent cache of `rows` rows on the layer's device: (rows, R)
+        of the layer dtype, or (rows, row_bytes) uint8 for FP8 rows."""
+        import torch
+        if self.kv == "fp8":
+            return torch.zeros((rows, self.row_bytes()), dtype=torch.uint8, device=self.device)
+        return torch.zeros((rows, self.dims.row), dtype=self.torch_dtype, device=self.device)
 
     # -- A3..A8
     def decode(self, hidden, pos, seq_off, seq_len, cache, out=None, stages=False):

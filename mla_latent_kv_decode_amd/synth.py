@@ -69,6 +69,7 @@ class Workload:
     new_tokens: int = 1        # prefill: new tokens per sequence
     prior: tuple = field(default_factory=tuple)  # prefill: cached rows before
     fixed_lengths: tuple = field(default_factory=tuple)
+    kv: str = "dtype"          # latent cache rows: "dtype" or "fp8" (E4M3 + row scale)
 
 
 WORKLOADS = {
@@ -81,6 +82,9 @@ WORKLOADS = {
     # V2-Lite ragged decode, B=64, cached rows ~ U{512..8192}
     "v2lite_decode_b64": Workload("v2lite_decode_b64", V2_LITE, "bf16", 0.02,
                                   "decode", 64, len_lo=512, len_hi=8192),
+    # the same batch on an FP8 latent cache (656-byte rows)
+    "v2lite_decode_b64_fp8": Workload("v2lite_decode_b64_fp8", V2_LITE, "bf16", 0.02,
+                                      "decode", 64, len_lo=512, len_hi=8192, kv="fp8"),
     # V3 ragged decode, B=32, cached rows ~ U{2048..16384}
     "v3_decode_b32": Workload("v3_decode_b32", V3, "bf16", 0.02, "decode", 32,
                               len_lo=2048, len_hi=16384),

@@ -7,6 +7,7 @@ from __future__ import annotations
 import numpy as np
 
 from mla_latent_kv_decode_amd import synth
+from oracle import fp8 as F8
 from oracle import mla as O
 
 APPEND_CHUNK = 8192
@@ -40,10 +41,10 @@ def host(t) -> np.ndarray:
     return t.detach().to(torch.float32).cpu().numpy()
 
 
-def make_layer(dims, dtype, weights):
+def make_layer(dims, dtype, weights, kv="dtype"):
     import torch
     from mla_latent_kv_decode_amd.lib import MLALayer
-    layer = MLALayer(dims, dtype)
+    layer = MLALayer(dims, dtype, kv=kv)
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     layer.absorb_weights({k: dev(v, tdt) for k, v in weights.items()})
     return layer
@@ -52,7 +53,7 @@ def make_layer(dims, dtype, weights):
 def fill_sequence(layer, dims, dtype, b, n_tokens, cache, base_slot, keep=False):
     """Append tokens 0..n_tokens-1 of sequence b (hidden states from synth) into
     cache rows base_slot + i; returns the hidden states if ``keep``."""
-    tdt = cache.dtype
+    tdt = layer.torch_dtype
     kept = []
     x = None
     for s in range(0, n_tokens, APPEND_CHUNK):
@@ -70,17 +71,16 @@ class DecodeCase:
     first: write, then read through the new position)."""
 
     def __init__(self, dims, dtype, std, lens, random_gains=True, keep=None, layer=None,
-                 weights=None):
+                 weights=None, kv="dtype"):
         import torch
-        self.dims, self.dtype = dims, dtype
+        self.dims, self.dtype, self.kv = dims, dtype, kv
         self.lens = np.asarray(lens, dtype=np.int64)
         self.B = len(self.lens)
         self.w = weights if weights is not None else synth.make_weights(
             dims, std, dtype, random_gains=random_gains)
-        self.layer = layer if layer is not None else make_layer(dims, dtype, self.w)
+        self.layer = layer if layer is not None else make_layer(dims, dtype, self.w, kv)
         self.seq_off, self.seq_len, self.total = synth.decode_layout(self.lens)
-        tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
-        self.cache = torch.zeros((self.total, dims.row), dtype=tdt, device="cuda")
+        self.cache = self.layer.new_cache(self.total)
         keep = set(range(self.B)) if keep is None else set(keep)
         self.hidden = {}
         last = []
@@ -94,7 +94,7 @@ class DecodeCase:
         torch.cuda.synchronize()
 
     def run(self, stages=False):
-        x = dev(self.x_new, self.cache.dtype)
+        x = dev(self.x_new, self.layer.torch_dtype)
         return self.layer.decode(x, self.seq_len - 1, self.seq_off, self.seq_len, self.cache,
                                  stages=stages)
 
@@ -104,7 +104,10 @@ class DecodeCase:
         xb = self.hidden[b]
         rows_prior = (O.latent_rows(xb[:L], np.arange(L), self.w["w_kva"], self.w["kv_norm_g"],
                                     shp) if L else np.zeros((0, shp.row)))
-        r = O.mla_step(xb[L:L + 1], np.array([L]), rows_prior, self.w, shp)
+        store = (lambda r: F8.fp8_rows(r, shp.kv_lora)) if self.kv == "fp8" else None
+        r = O.mla_step(xb[L:L + 1], np.array([L]), rows_prior, self.w, shp, kv_store=store)
         rows = np.concatenate([rows_prior, r["rows_new"]])
+        if store is not None:
+            rows = store(rows)
         a = O.absorbed_step(xb[L:L + 1], np.array([L]), rows, self.w, shp)
         return r["y"][0], a

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(mla):
     missing = [n for n in names if not hasattr(mla, n)]
     assert not missing, missing
     assert set(names) == set(L._SIGS), set(names) ^ set(L._SIGS)
-    assert mla.mla_abi_version() == 1
+    assert mla.mla_abi_version() == 2
 
 
 def test_status_strings(mla):
@@ -59,6 +59,25 @@ def test_config_check(mla):
     assert ok(cfg(rms_eps=float("nan"))) == L.MLA_ERR_INVALID_ARG
     assert ok(cfg(softmax_scale=-1.0)) == L.MLA_ERR_INVALID_ARG
     assert mla.mla_config_check(None) == L.MLA_ERR_INVALID_ARG
+
+
+def test_fp8_cache_config_and_row_bytes(mla):
+    """FP8 latent rows: accepted for the shapes the FP8 core serves (bf16
+    layer, latent 512, rope 64, a multiple of 16 heads below a multiple of
+    128), refused otherwise; 656 bytes per row (512 codes + 64 bf16 + scale,
+    padded to 16)."""
+    ok = lambda c: mla.mla_config_check(ctypes.byref(c))
+    rb = lambda c: mla.mla_cache_row_bytes(ctypes.byref(c))
+    c8 = cfg(kv_storage=L.MLA_KV_FP8_E4M3)
+    assert ok(c8) == L.MLA_OK and rb(c8) == 656
+    assert rb(cfg()) == 576 * 2 and rb(cfg(synth.TINY, "f32")) == 24 * 4
+    assert ok(cfg(kv_storage=2)) == L.MLA_ERR_INVALID_ARG
+    assert rb(cfg(kv_storage=2)) == 0
+    for bad in (cfg(synth.V3, kv_storage=1), cfg(synth.TINY, "f32", kv_storage=1),
+                cfg(kv_lora=256, kv_storage=1), cfg(qk_rope=32, kv_storage=1),
+                cfg(n_heads=24, kv_storage=1)):
+        assert ok(bad) == L.MLA_ERR_SHAPE
+    assert ok(cfg(n_heads=32, kv_storage=1)) == L.MLA_OK
 
 
 def _i32(a):
