@@ -17,34 +17,50 @@
 // + q_rope . k_rope_t, and folded into the probabilities of the latent sum,
 // sum_t (p_t s_t) code_t.
 //
-// Work, waves and pipeline as in the bf16 ring core: the host cuts the
-// concatenated rows into one contiguous span per persistent workgroup, split
-// at sequence boundaries into segments; two producer waves stream every
-// position (the segment's query tile, then its 32-row tiles) into a 7-stage
-// LDS ring with global_load_lds_dwordx4 (22 one-KB copies per position, five
-// positions in flight), four consumer waves compute, one barrier per position.
+// Work and waves as in the bf16 ring core: the host cuts the concatenated rows
+// into one contiguous span per persistent workgroup, split at sequence
+// boundaries into segments; two producer waves stream every position (the
+// segment's query tile, then its 32-row tiles) into a 7-stage LDS ring with
+// global_load_lds_dwordx4 (22 one-KB copies per position), four consumer
+// waves compute, one barrier per position.
 //
-// LDS stage of a row tile (22 KB):
+// The per-row work is larger than in the bf16 core (every code is converted
+// before each of the two MFMA products that use it, and the conversion issues
+// at about two thirds of an MFMA's rate), so the score product is not
+// repeated in every consumer wave: wave w computes, for row block w >> 1 and
+// half w & 1 of the query dimensions (256 latent + 32 rope), the partial
+// score s_r (q_lat . code) + q_rope . k_rope over its half and writes it to
+// LDS (1 KB per wave and tile, two buffers).  The softmax and the latent sum
+// of a tile run one position later, after the barrier that makes the four
+// partials visible, so a tile's stage stays in use for two positions: the
+// producers refill the stage of position gt - 2 after barrier gt (four
+// positions in flight), and both sides pass one extra barrier at the end.
+//
+// LDS stage of a row tile (21 KB):
 //   latent codes  row r at r * 512, 16-byte chunk c at c ^ f8(r),
 //                 f8(r) = (r & 15) ^ 8 ((r >> 4) & 1)
 //   rope (bf16)   row r at 16384 + r * 128, chunk c at c ^ rope_swz(r)
-//   scales        row r at 20480 + 16 r (a second copy at + 512)
-//   1 KB spare    (the copy count is the same for every position)
+//   scales        row r at 20480 + 16 r (the spare copy writes the same bytes)
 // f8 makes both reads conflict-free on 64 four-byte banks (32 lanes per
 // cycle for 8-byte reads): the score operand (16 rows, one chunk) and the
 // transposing read of the latent sum (rows 4g .. 4g + 3 of both 16-row blocks
 // for lane groups g = 0, 1 and g = 2, 3) each hit 16 distinct chunks.
 // A query tile keeps the bf16 ring core's layout: 16 rows of 1 KB (latent
-// part, chunk c at c ^ lat_swz(r)) and the rope parts at 16384.
+// part, chunk c at c ^ lat_swz(r)) and the rope parts at 16384; its spare
+// copies fill 18432 .. 21503 (the last one twice).
+// After the 7 stages: the partial scores, [buffer][wave][lane] as f32x4.
 //
-// Per 32-row tile and consumer wave (column quarter cq):
-//   S^T latent = K8 . Q^T: 2 x 16 mfma 16x16x32 on converted codes (8 codes
-//     per lane from one ds_read_b64), S^T rope: 2 x 2 mfma on bf16;
-//   scores s_r * latent + rope, online softmax in log2 units with a lazily
-//     moved reference maximum (as the bf16 core), p' = p * s_r;
-//   O^T += C8^T . P'^T: 8 mfma 16x16x32; one ds_read_b64_tr_b8 per 16-column
-//     block gives each lane 8 codes of one column (rows 4g .. 4g + 3 of both
-//     row blocks for lane group g: the k order the score layout holds P in).
+// Per 32-row tile and consumer wave w:
+//   partial S^T over rows 16 (w >> 1) .. + 15 and dimension half w & 1:
+//     8 mfma 16x16x32 on converted codes (8 codes per lane from one
+//     ds_read_b64) + 1 mfma on the bf16 rope part, scaled by s_r in fp32;
+//   next position: S^T = sum of the two partials of each row block, online
+//     softmax in log2 units with a lazily moved reference maximum (as the
+//     bf16 core, repeated in every wave), p' = p * s_r;
+//   O^T += C8^T . P'^T over column quarter w: 8 mfma 16x16x32; one
+//     ds_read_b64_tr_b8 per 16-column block gives each lane 8 codes of one
+//     column (rows 4g .. 4g + 3 of both row blocks for lane group g: the k
+//     order the score layout holds P in).
 // Outputs are those of the bf16 core (normalised o_lat rows for sequences in
 // one segment, else fp32 partials for the combine).
 #include <utility>
@@ -63,9 +79,10 @@ constexpr int TR = 32;                       // rows per tile
 constexpr int NST = 7;                       // ring stages
 constexpr int ROPE_OFF = 16384;              // rope rows (data and query tiles)
 constexpr int SC_OFF = 20480;                // row scales
-constexpr int SPARE_OFF = 21504;
 constexpr int QSPARE_OFF = 18432;            // query tiles: after 16 rope rows
-constexpr int ST_BYTES = 22528;              // 22 KB
+constexpr int ST_BYTES = 21504;              // 21 KB
+constexpr int PS_OFF = NST * ST_BYTES;       // partial scores: 2 buffers x 4 waves x 1 KB
+constexpr int PS_BYTES = 2 * 4096;
 constexpr int NCOPY = 22;                    // one-KB copies per position
 constexpr int NPROD = 2;
 constexpr int LPW = NCOPY / NPROD;           // 11
@@ -75,8 +92,9 @@ constexpr int NTHR = 64 * (NCONS + NPROD);
 constexpr float kRescale = 8.0f;
 constexpr int kXcds = 8;
 static_assert(NCOPY % NPROD == 0, "copies split evenly over the producers");
-static_assert((NST - 2) * LPW <= 63, "copies in flight fit the vmcnt field");
-static_assert(NST * ST_BYTES <= 160 * 1024, "ring fits the LDS");
+static_assert((NST - 3) * LPW <= 63, "copies in flight fit the vmcnt field");
+static_assert(PS_OFF + PS_BYTES <= 160 * 1024, "ring and partial scores fit the LDS");
+static_assert(QSPARE_OFF + 3 * 1024 == ST_BYTES, "query spares fill the stage");
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x8_t __attribute__((ext_vector_type(8)));
@@ -99,12 +117,10 @@ __device__ __forceinline__ void row_copy(const char* base, int last, uint32_t st
     const int cc = (lane & 7) ^ rope_swz(r & 15);
     const int rs = r <= last ? r : last;
     dma16(base + rs * RB + 512 + (cc << 4), stage + ROPE_OFF + J * 1024);
-  } else if constexpr (I == 20) {  // scales of rows 0 .. 31 (twice)
+  } else {  // scales of rows 0 .. 31 (twice); the spare copy I = 21 repeats it
     const int r = lane & 31;
     const int rs = r <= last ? r : last;
     dma16(base + rs * RB + 640, stage + SC_OFF);
-  } else {  // spare: the first 512 bytes of row 0 (inside the buffer even for a 1-row tile)
-    dma16(base + ((lane & 31) << 4), stage + SPARE_OFF);
   }
 }
 
@@ -118,8 +134,9 @@ __device__ __forceinline__ void query_copy(const char* qb, uint32_t stage, int l
     const int r = 8 * J + (lane >> 3);
     const int cc = (lane & 7) ^ rope_swz(r & 15);
     dma16(qb + r * (QRW * 2) + 1024 + (cc << 4), stage + ROPE_OFF + J * 1024);
-  } else {
-    dma16(qb + (lane << 4), stage + QSPARE_OFF + (I - 18) * 1024);
+  } else {  // spares: the first KB of row 0, into 18432 .. 21503 (I = 21 repeats I = 20)
+    constexpr int J = I < 21 ? I - 18 : 2;
+    dma16(qb + (lane << 4), stage + QSPARE_OFF + J * 1024);
   }
 }
 
@@ -173,7 +190,7 @@ __global__ void __launch_bounds__(NTHR, 1)
 decode_core_ring8_k(const bf16* __restrict__ q_cat, const uint8_t* __restrict__ cache,
                     DecodeMeta mt, float* __restrict__ acc, float* __restrict__ ml,
                     bf16* __restrict__ o_lat, int H, int nparts) {
-  __shared__ __attribute__((aligned(1024))) char lds[NST * ST_BYTES];
+  __shared__ __attribute__((aligned(1024))) char lds[PS_OFF + PS_BYTES];
   const int HG = H / 16;
   const int bid = blockIdx.x;
   const int part = (bid / (kXcds * HG)) * kXcds + bid % kXcds;
@@ -213,34 +230,34 @@ decode_core_ring8_k(const bf16* __restrict__ q_cat, const uint8_t* __restrict__ 
       ++issued;
     };
 #pragma unroll 1
-    for (int i = 0; i < NST - 1; ++i) issue_next();
+    for (int i = 0; i < NST - 2; ++i) issue_next();
 #pragma unroll 1
     for (int gt = 0; gt < issued; ++gt) {
-      wait_ahead<NST - 2>(issued - gt - 1);  // positions issued after position gt
-      __syncthreads();  // position gt is in LDS; the consumers are done with gt - 1
-      if (issued == gt + NST - 1) issue_next();  // refills the stage of position gt - 1
+      wait_ahead<NST - 3>(issued - gt - 1);  // positions issued after position gt
+      __syncthreads();  // position gt is in LDS; the consumers are done with gt - 2
+      if (issued == gt + NST - 2) issue_next();  // refills the stage of position gt - 2
     }
+    __syncthreads();  // the consumers' last exchange of partial scores
     return;
   }
 
   // -------------------------------------------------------------- consumers
-  const int cq = wave;  // column quarter: columns 128 cq .. 128 cq + 127
+  const int cq = wave;                    // latent-sum column quarter: 128 cq .. 128 cq + 127
+  const int rbq = cq >> 1, hq = cq & 1;   // score row block and dimension half
   const int lr = lane & 15, lg = lane >> 4;
-  // score operand of latent k-step s in row block rb: row 16 rb + lr, codes
-  // 32 s + 8 lg .. + 7, i.e. half (lg & 1) of chunk c = 2 s + (lg >> 1) at
-  // c ^ f8(row) = 2 (s ^ x1) + h1 with x1, h1 from lr ^ 8 rb: qk8[rb][s & 7] +
-  // 256 (s >> 3)
-  int qk8[2][8];
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const int x = lr ^ (8 * rb);
+  // score operand of latent k-step s = 8 hq + j (row 16 rbq + lr, codes
+  // 32 s + 8 lg .. + 7): half (lg & 1) of chunk c = 2 s + (lg >> 1), stored at
+  // c ^ f8(row) = 2 (s ^ x1) + h1 with x1, h1 from lr ^ 8 rbq
+  int qk8[8];
+  {
+    const int x = lr ^ (8 * rbq);
     const int h1 = (lg >> 1) ^ (x & 1);
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
-      qk8[rb][s] = (16 * rb + lr) * 512 + 32 * (s ^ (x >> 1)) + 16 * h1 + 8 * (lg & 1);
+    for (int j = 0; j < 8; ++j)
+      qk8[j] = (16 * rbq + lr) * 512 + 32 * (j ^ (x >> 1)) + 16 * h1 + 8 * (lg & 1) + 256 * hq;
   }
-  const int qk_rope0 = ROPE_OFF + lr * 128 + 16 * (lg ^ rope_swz(lr));
-  const int qk_rope1 = ROPE_OFF + lr * 128 + 16 * ((4 + lg) ^ rope_swz(lr));
+  // rope operand: row 16 rbq + lr, rope dims 32 hq + 8 lg .. + 7
+  const int qk_rope = ROPE_OFF + (16 * rbq + lr) * 128 + 16 * ((4 * hq + lg) ^ rope_swz(lr));
   // transposing read of column block cb for lane (g = lg, i = lr): row
   // j < 4 ? 4g + j : 16 + 4g + j - 4 with j = i / 2, bytes 8 (i & 1) of chunk
   // cb ^ f8(row); cb = 8 cq + k: pv8[k] = base + 16 (k ^ (f8 & 7))
@@ -255,115 +272,98 @@ decode_core_ring8_k(const bf16* __restrict__ q_cat, const uint8_t* __restrict__ 
   }
   const int gh = hg * 16 + lr;  // this lane's head in the score and sum layouts
   const int sc0 = SC_OFF + 16 * 4 * lg;  // scale of row 16 rb + 4 lg + i at sc0 + 256 rb + 16 i
+  char* const ps = lds + PS_OFF + 16 * lane;  // + 4096 buffer + 1024 wave
+
+  // partial scores of the tile in stage st -> buffer par
+  auto partial = [&](const char* st, int par, const bf16x8_t (&ql)[8], const bf16x8_t& qr) {
+    f32x4_t sa = (f32x4_t){0.f, 0.f, 0.f, 0.f}, sb = sa, sr = sa;
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+      const i32x2_t c0 = *reinterpret_cast<const i32x2_t*>(st + qk8[j]);
+      const i32x2_t c1 = *reinterpret_cast<const i32x2_t*>(st + qk8[j + 1]);
+      sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16(c0), ql[j], sa, 0, 0, 0);
+      sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16(c1), ql[j + 1], sb, 0, 0, 0);
+    }
+    sr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8_t*>(st + qk_rope),
+                                                 qr, sr, 0, 0, 0);
+    const f32x4_t sl = sa + sb;
+    f32x4_t out;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float scale = *reinterpret_cast<const float*>(st + sc0 + 256 * rbq + 16 * i);
+      out[i] = fmaf(scale, sl[i], sr[i]);
+    }
+    *reinterpret_cast<f32x4_t*>(ps + par * 4096 + cq * 1024) = out;
+  };
 
   DecodeWork wk = first, nx = first;
   if (wk.next >= 0) nx = load_work(works + wk.next);
   int gt = 0;
-#pragma unroll 1
-  for (;;) {
-    bf16x8_t qf[18];
-    float m_run, l_run;
-    f32x4_t o[NCB];
-    const int n = wk.n;
-    const int ntile = (n + TR - 1) / TR;
-    {
-      // the segment's query tile: Q^T fragments of head gh, columns 32 s + 8 lg .. + 7
-      __syncthreads();
-      const char* st = lds + (gt % NST) * ST_BYTES;
-#pragma unroll
-      for (int s = 0; s < 16; ++s) {
-        const int off = lr * 1024 + 16 * ((4 * (s & 3) + lg) ^ lat_swz(lr)) + 256 * (s >> 2);
-        qf[s] = *reinterpret_cast<const bf16x8_t*>(st + off);
-      }
-      qf[16] = *reinterpret_cast<const bf16x8_t*>(st + qk_rope0);
-      qf[17] = *reinterpret_cast<const bf16x8_t*>(st + qk_rope1);
-      ++gt;
-    }
-    m_run = -INFINITY;
-    l_run = 0.f;
-#pragma unroll
-    for (int j = 0; j < NCB; ++j) o[j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-#pragma unroll 1
-    for (int k = 0; k < ntile; ++k, ++gt) {
-      __syncthreads();  // tile gt is in LDS
-      const char* st = lds + (gt % NST) * ST_BYTES;
-      const int row0 = k * TR;
-      float sv[8], rs[8];
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        // ---- S^T = s_r (K8 . Q_lat^T) + K_rope . Q_rope^T for this 16-row block
-        f32x4_t sa = (f32x4_t){0.f, 0.f, 0.f, 0.f}, sb = sa, sr = sa;
-#pragma unroll
-        for (int s = 0; s < 16; s += 2) {
-          const i32x2_t c0 =
-              *reinterpret_cast<const i32x2_t*>(st + qk8[rb][s & 7] + 256 * (s >> 3));
-          const i32x2_t c1 =
-              *reinterpret_cast<const i32x2_t*>(st + qk8[rb][(s + 1) & 7] + 256 * ((s + 1) >> 3));
-          sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16(c0), qf[s], sa, 0, 0, 0);
-          sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16(c1), qf[s + 1], sb, 0, 0, 0);
-        }
-        const char* srp = st + rb * 16 * 128;  // rope offsets include ROPE_OFF
-        sr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            *reinterpret_cast<const bf16x8_t*>(srp + qk_rope0), qf[16], sr, 0, 0, 0);
-        sr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            *reinterpret_cast<const bf16x8_t*>(srp + qk_rope1), qf[17], sr, 0, 0, 0);
-        const f32x4_t sl = sa + sb;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float scale = *reinterpret_cast<const float*>(st + sc0 + 256 * rb + 16 * i);
-          rs[4 * rb + i] = scale;
-          const bool valid = row0 + 16 * rb + 4 * lg + i < n;
-          sv[4 * rb + i] = valid ? fmaf(scale, sl[i], sr[i]) * kLog2e : -INFINITY;
-        }
-      }
-      // ---- online softmax: lane holds rows row0 + 16 rb + 4 lg + i of head gh
-      bool grow = false;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) grow |= sv[i] > m_run + kRescale;
-      if (__any(grow)) {
-        float mx = sv[0];
-#pragma unroll
-        for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        l_run *= alpha;
-        m_run = m_new;
-#pragma unroll
-        for (int j = 0; j < NCB; ++j) o[j] *= alpha;
-      }
-      bf16x8_t pf;
-      {
-        float pv[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          pv[i] = __builtin_amdgcn_exp2f(sv[i] - m_run);
-          l_run += pv[i];
-        }
-        uint32_t pk[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          pk[i] = pack_bf16x2(pv[2 * i] * rs[2 * i], pv[2 * i + 1] * rs[2 * i + 1]);
-        pf = __builtin_bit_cast(bf16x8_t, pk);
-      }
-      // ---- O^T += C8^T . P'^T over this wave's column blocks 8 cq .. 8 cq + 7
-#pragma unroll
-      for (int j = 0; j < NCB; ++j) {
-        typedef __attribute__((address_space(3))) i32x2_t* lptr;
-        const i32x2_t c = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lptr)(st + pv8[j]));
-        o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16(c), pf, o[j], 0, 0, 0);
-      }
-    }
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4_t o[NCB];
 
-    // ---- end of the segment: lane holds columns 128 cq + 16 j + 4 lg .. +3 of head gh
+  // softmax and latent sum of the tile whose partials are in buffer par
+  auto finish = [&](const char* st, int par, int row0, int n) {
+    float sv[8], rs[8];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const f32x4_t a = *reinterpret_cast<const f32x4_t*>(ps + par * 4096 + (2 * rb) * 1024);
+      const f32x4_t b = *reinterpret_cast<const f32x4_t*>(ps + par * 4096 + (2 * rb + 1) * 1024);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        rs[4 * rb + i] = *reinterpret_cast<const float*>(st + sc0 + 256 * rb + 16 * i);
+        const bool valid = row0 + 16 * rb + 4 * lg + i < n;
+        sv[4 * rb + i] = valid ? (a[i] + b[i]) * kLog2e : -INFINITY;
+      }
+    }
+    // ---- online softmax: lane holds rows row0 + 16 rb + 4 lg + i of head gh
+    bool grow = false;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) grow |= sv[i] > m_run + kRescale;
+    if (__any(grow)) {
+      float mx = sv[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+      m_run = m_new;
+#pragma unroll
+      for (int j = 0; j < NCB; ++j) o[j] *= alpha;
+    }
+    bf16x8_t pf;
+    {
+      float pv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        pv[i] = __builtin_amdgcn_exp2f(sv[i] - m_run);
+        l_run += pv[i];
+      }
+      uint32_t pk[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        pk[i] = pack_bf16x2(pv[2 * i] * rs[2 * i], pv[2 * i + 1] * rs[2 * i + 1]);
+      pf = __builtin_bit_cast(bf16x8_t, pk);
+    }
+    // ---- O^T += C8^T . P'^T over this wave's column blocks 8 cq .. 8 cq + 7
+#pragma unroll
+    for (int j = 0; j < NCB; ++j) {
+      typedef __attribute__((address_space(3))) i32x2_t* lptr;
+      const i32x2_t c = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lptr)(st + pv8[j]));
+      o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16(c), pf, o[j], 0, 0, 0);
+    }
+  };
+
+  // ---- end of a segment: lane holds columns 128 cq + 16 j + 4 lg .. +3 of head gh
+  auto store = [&](const DecodeWork& w) {
     float l = l_run;
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
-    const int b = wk.b;
-    if (wk.nseg == 1) {
+    if (w.nseg == 1) {
       const float inv = 1.f / l;
-      bf16* dst = o_lat + ((int64_t)b * H + gh) * DC + 128 * cq + 4 * lg;
+      bf16* dst = o_lat + ((int64_t)w.b * H + gh) * DC + 128 * cq + 4 * lg;
 #pragma unroll
       for (int j = 0; j < NCB; ++j) {
         uint2 pk;
@@ -372,17 +372,64 @@ decode_core_ring8_k(const bf16* __restrict__ q_cat, const uint8_t* __restrict__ 
         *reinterpret_cast<uint2*>(dst + 16 * j) = pk;
       }
     } else {
-      float* pacc = acc + ((int64_t)wk.pidx * H + gh) * DC + 128 * cq + 4 * lg;
+      float* pacc = acc + ((int64_t)w.pidx * H + gh) * DC + 128 * cq + 4 * lg;
 #pragma unroll
       for (int j = 0; j < NCB; ++j)
         *reinterpret_cast<float4*>(pacc + 16 * j) = make_float4(o[j][0], o[j][1], o[j][2], o[j][3]);
       if (cq == 0 && lg == 0)
-        *reinterpret_cast<float2*>(ml + ((int64_t)wk.pidx * H + gh) * 2) = make_float2(m_run, l);
+        *reinterpret_cast<float2*>(ml + ((int64_t)w.pidx * H + gh) * 2) = make_float2(m_run, l);
     }
+  };
+
+  // The tile of position gt - 1 (the segment's last) is finished after the
+  // barrier of the next segment's query position, or after the final barrier.
+  DecodeWork done = first;  // segment of the pending last tile
+  bool pending = false;
+#pragma unroll 1
+  for (;;) {
+    bf16x8_t ql[8], qr;
+    const int n = wk.n;
+    const int ntile = (n + TR - 1) / TR;
+    {
+      __syncthreads();  // the query tile is in LDS; the partials of gt - 1 are visible
+      const char* st = lds + (gt % NST) * ST_BYTES;
+      if (pending) {
+        finish(lds + ((gt - 1) % NST) * ST_BYTES, (gt - 1) & 1, (done.n - 1) / TR * TR, done.n);
+        store(done);
+      }
+      // Q^T fragments of head gh, columns 32 s + 8 lg .. + 7 for s = 8 hq + j
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int s = 8 * hq + j;
+        const int off = lr * 1024 + 16 * ((4 * (s & 3) + lg) ^ lat_swz(lr)) + 256 * (s >> 2);
+        ql[j] = *reinterpret_cast<const bf16x8_t*>(st + off);
+      }
+      qr = *reinterpret_cast<const bf16x8_t*>(st + ROPE_OFF + lr * 128 +
+                                               16 * ((4 * hq + lg) ^ rope_swz(lr)));
+      ++gt;
+    }
+    m_run = -INFINITY;
+    l_run = 0.f;
+#pragma unroll
+    for (int j = 0; j < NCB; ++j) o[j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    __syncthreads();  // first row tile
+    partial(lds + (gt % NST) * ST_BYTES, gt & 1, ql, qr);
+    ++gt;
+#pragma unroll 1
+    for (int k = 1; k < ntile; ++k, ++gt) {
+      __syncthreads();  // tile gt is in LDS; the partials of tile gt - 1 are visible
+      partial(lds + (gt % NST) * ST_BYTES, gt & 1, ql, qr);
+      finish(lds + ((gt - 1) % NST) * ST_BYTES, (gt - 1) & 1, (k - 1) * TR, n);
+    }
+    pending = true;
+    done = wk;
     if (wk.next < 0) break;
     wk = nx;
     if (wk.next >= 0) nx = load_work(works + wk.next);
   }
+  __syncthreads();  // the partials of the last tile are visible
+  finish(lds + ((gt - 1) % NST) * ST_BYTES, (gt - 1) & 1, (done.n - 1) / TR * TR, done.n);
+  store(done);
 }
 
 }  // namespace decr8
