@@ -22,7 +22,11 @@
 // boundaries into segments; two producer waves stream every position (the
 // segment's query tile, then its 32-row tiles) into a 7-stage LDS ring with
 // global_load_lds_dwordx4 (22 one-KB copies per position), four consumer
-// waves compute, one barrier per position.
+// waves compute, one barrier per position.  (Measured: with the consumers'
+// math removed the stream takes 93 % of the kernel's time, and a deeper ring
+// - six positions in flight, bought with a second barrier per tile - does
+// not speed the stream up: its in-loop rate is that of the bf16 core, and
+// launch and tail make up the rest.)
 //
 // The per-row work is larger than in the bf16 core (every code is converted
 // before each of the two MFMA products that use it, and the conversion issues
@@ -274,25 +278,55 @@ decode_core_ring8_k(const bf16* __restrict__ q_cat, const uint8_t* __restrict__ 
   const int sc0 = SC_OFF + 16 * 4 * lg;  // scale of row 16 rb + 4 lg + i at sc0 + 256 rb + 16 i
   char* const ps = lds + PS_OFF + 16 * lane;  // + 4096 buffer + 1024 wave
 
-  // partial scores of the tile in stage st -> buffer par
-  auto partial = [&](const char* st, int par, const bf16x8_t (&ql)[8], const bf16x8_t& qr) {
+  // LDS reads of a position's two computations, issued together before either
+  // (the partial scores of the new tile, the softmax and latent sum of the
+  // previous one), so that one wave per SIMD keeps many reads in flight
+  struct PartIn {
+    i32x2_t c[8];
+    bf16x8_t kr;
+    float scale[4];
+  };
+  struct FinIn {
+    f32x4_t pa[4];
+    float rs[8];
+    i32x2_t cr[NCB];
+  };
+  auto part_load = [&](const char* st, PartIn& in) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) in.c[j] = *reinterpret_cast<const i32x2_t*>(st + qk8[j]);
+    in.kr = *reinterpret_cast<const bf16x8_t*>(st + qk_rope);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      in.scale[i] = *reinterpret_cast<const float*>(st + sc0 + 256 * rbq + 16 * i);
+  };
+  auto fin_load = [&](const char* st, int par, FinIn& in) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      in.pa[i] = *reinterpret_cast<const f32x4_t*>(ps + par * 4096 + i * 1024);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      in.rs[i] = *reinterpret_cast<const float*>(st + sc0 + 256 * (i >> 2) + 16 * (i & 3));
+#pragma unroll
+    for (int j = 0; j < NCB; ++j) {
+      typedef __attribute__((address_space(3))) i32x2_t* lptr;
+      in.cr[j] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lptr)(st + pv8[j]));
+    }
+  };
+
+  // partial scores of a tile -> buffer par
+  auto partial = [&](const PartIn& in, int par, const bf16x8_t (&ql)[8], const bf16x8_t& qr) {
     f32x4_t sa = (f32x4_t){0.f, 0.f, 0.f, 0.f}, sb = sa, sr = sa;
+    sr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(in.kr, qr, sr, 0, 0, 0);
 #pragma unroll
     for (int j = 0; j < 8; j += 2) {
-      const i32x2_t c0 = *reinterpret_cast<const i32x2_t*>(st + qk8[j]);
-      const i32x2_t c1 = *reinterpret_cast<const i32x2_t*>(st + qk8[j + 1]);
-      sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16(c0), ql[j], sa, 0, 0, 0);
-      sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16(c1), ql[j + 1], sb, 0, 0, 0);
+      sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16(in.c[j]), ql[j], sa, 0, 0, 0);
+      sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16(in.c[j + 1]), ql[j + 1], sb, 0, 0,
+                                                   0);
     }
-    sr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8_t*>(st + qk_rope),
-                                                 qr, sr, 0, 0, 0);
     const f32x4_t sl = sa + sb;
     f32x4_t out;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float scale = *reinterpret_cast<const float*>(st + sc0 + 256 * rbq + 16 * i);
-      out[i] = fmaf(scale, sl[i], sr[i]);
-    }
+    for (int i = 0; i < 4; ++i) out[i] = fmaf(in.scale[i], sl[i], sr[i]);
     *reinterpret_cast<f32x4_t*>(ps + par * 4096 + cq * 1024) = out;
   };
 
@@ -302,19 +336,21 @@ decode_core_ring8_k(const bf16* __restrict__ q_cat, const uint8_t* __restrict__ 
   float m_run = -INFINITY, l_run = 0.f;
   f32x4_t o[NCB];
 
-  // softmax and latent sum of the tile whose partials are in buffer par
-  auto finish = [&](const char* st, int par, int row0, int n) {
-    float sv[8], rs[8];
+  // softmax and latent sum of a tile; only a segment's last tile (finished on
+  // the pending path) can hold rows past the segment's end, so only that call
+  // masks
+  auto finish = [&](const FinIn& in, int row0, int n, bool last) {
+    bf16x8_t cf[NCB];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const f32x4_t a = *reinterpret_cast<const f32x4_t*>(ps + par * 4096 + (2 * rb) * 1024);
-      const f32x4_t b = *reinterpret_cast<const f32x4_t*>(ps + par * 4096 + (2 * rb + 1) * 1024);
+    for (int j = 0; j < NCB; ++j) cf[j] = codes_to_bf16(in.cr[j]);
+    float sv[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        rs[4 * rb + i] = *reinterpret_cast<const float*>(st + sc0 + 256 * rb + 16 * i);
-        const bool valid = row0 + 16 * rb + 4 * lg + i < n;
-        sv[4 * rb + i] = valid ? (a[i] + b[i]) * kLog2e : -INFINITY;
-      }
+    for (int i = 0; i < 8; ++i)
+      sv[i] = (in.pa[2 * (i >> 2)][i & 3] + in.pa[2 * (i >> 2) + 1][i & 3]) * kLog2e;
+    if (last) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (row0 + 16 * (i >> 2) + 4 * lg + (i & 3) >= n) sv[i] = -INFINITY;
     }
     // ---- online softmax: lane holds rows row0 + 16 rb + 4 lg + i of head gh
     bool grow = false;
@@ -344,16 +380,19 @@ decode_core_ring8_k(const bf16* __restrict__ q_cat, const uint8_t* __restrict__ 
       uint32_t pk[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        pk[i] = pack_bf16x2(pv[2 * i] * rs[2 * i], pv[2 * i + 1] * rs[2 * i + 1]);
+        pk[i] = pack_bf16x2(pv[2 * i] * in.rs[2 * i], pv[2 * i + 1] * in.rs[2 * i + 1]);
       pf = __builtin_bit_cast(bf16x8_t, pk);
     }
     // ---- O^T += C8^T . P'^T over this wave's column blocks 8 cq .. 8 cq + 7
 #pragma unroll
-    for (int j = 0; j < NCB; ++j) {
-      typedef __attribute__((address_space(3))) i32x2_t* lptr;
-      const i32x2_t c = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lptr)(st + pv8[j]));
-      o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16(c), pf, o[j], 0, 0, 0);
-    }
+    for (int j = 0; j < NCB; ++j)
+      o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cf[j], pf, o[j], 0, 0, 0);
+  };
+  // finish of the tile in stage st with partials in buffer par, on its own
+  auto finish_alone = [&](const char* st, int par, int row0, int n) {
+    FinIn in;
+    fin_load(st, par, in);
+    finish(in, row0, n, true);
   };
 
   // ---- end of a segment: lane holds columns 128 cq + 16 j + 4 lg .. +3 of head gh
@@ -394,7 +433,8 @@ decode_core_ring8_k(const bf16* __restrict__ q_cat, const uint8_t* __restrict__ 
       __syncthreads();  // the query tile is in LDS; the partials of gt - 1 are visible
       const char* st = lds + (gt % NST) * ST_BYTES;
       if (pending) {
-        finish(lds + ((gt - 1) % NST) * ST_BYTES, (gt - 1) & 1, (done.n - 1) / TR * TR, done.n);
+        finish_alone(lds + ((gt - 1) % NST) * ST_BYTES, (gt - 1) & 1, (done.n - 1) / TR * TR,
+                     done.n);
         store(done);
       }
       // Q^T fragments of head gh, columns 32 s + 8 lg .. + 7 for s = 8 hq + j
@@ -413,13 +453,22 @@ decode_core_ring8_k(const bf16* __restrict__ q_cat, const uint8_t* __restrict__ 
 #pragma unroll
     for (int j = 0; j < NCB; ++j) o[j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
     __syncthreads();  // first row tile
-    partial(lds + (gt % NST) * ST_BYTES, gt & 1, ql, qr);
+    {
+      PartIn pin;
+      part_load(lds + (gt % NST) * ST_BYTES, pin);
+      partial(pin, gt & 1, ql, qr);
+    }
     ++gt;
 #pragma unroll 1
     for (int k = 1; k < ntile; ++k, ++gt) {
       __syncthreads();  // tile gt is in LDS; the partials of tile gt - 1 are visible
-      partial(lds + (gt % NST) * ST_BYTES, gt & 1, ql, qr);
-      finish(lds + ((gt - 1) % NST) * ST_BYTES, (gt - 1) & 1, (k - 1) * TR, n);
+      PartIn pin;
+      FinIn fin;
+      part_load(lds + (gt % NST) * ST_BYTES, pin);
+      fin_load(lds + ((gt - 1) % NST) * ST_BYTES, (gt - 1) & 1, fin);
+      __builtin_amdgcn_sched_barrier(0);  // keep every read of the position ahead of the math
+      partial(pin, gt & 1, ql, qr);
+      finish(fin, (k - 1) * TR, n, false);
     }
     pending = true;
     done = wk;
@@ -428,7 +477,7 @@ decode_core_ring8_k(const bf16* __restrict__ q_cat, const uint8_t* __restrict__ 
     if (wk.next >= 0) nx = load_work(works + wk.next);
   }
   __syncthreads();  // the partials of the last tile are visible
-  finish(lds + ((gt - 1) % NST) * ST_BYTES, (gt - 1) & 1, (done.n - 1) / TR * TR, done.n);
+  finish_alone(lds + ((gt - 1) % NST) * ST_BYTES, (gt - 1) & 1, (done.n - 1) / TR * TR, done.n);
   store(done);
 }
 
