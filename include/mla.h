@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 2
+#define MLA_ABI_VERSION 3
 
 typedef enum mla_status {
   MLA_OK = 0,
@@ -127,6 +127,11 @@ int mla_decode_check(const mla_config* cfg, const int32_t* pos, const int64_t* s
                      const int32_t* seq_len, int32_t B, int64_t cache_rows);
 int mla_prefill_check(const mla_config* cfg, const int32_t* cu_new, const int32_t* prior_len,
                       const int64_t* seq_off, int32_t B, int64_t cache_rows);
+/* The checks of mla_decode_paged (writes = 0) and mla_decode_step_paged
+ * (writes = 1); see there. */
+int mla_decode_paged_check(const mla_config* cfg, const int32_t* pos, const int32_t* block_table,
+                           int32_t max_pages, int32_t page_rows, const int32_t* seq_len, int32_t B,
+                           int64_t cache_rows, int32_t writes);
 
 /* Create a handle on the current HIP device.  stream: a hipStream_t or NULL.
  * *out receives the handle (NULL on failure). */
@@ -216,6 +221,38 @@ size_t mla_decode_step_workspace_bytes(mla_handle h, int32_t B, int64_t total_ro
 int mla_decode_step(mla_handle h, const void* hidden, const int32_t* pos,
                     const int64_t* seq_off, const int32_t* seq_len, int32_t B, void* cache,
                     int64_t cache_rows, void* out, void* ws, size_t ws_bytes);
+
+/* Paged latent cache -- mla_decode and mla_decode_step over a cache managed
+ * as a pool of pages (the KV-cache page grows its cache as a memory pool; the
+ * MLA post's reference code preallocates one contiguous buffer).  The cache
+ * holds cache_rows rows in its usual row format; page k is rows
+ * [k * page_rows, (k + 1) * page_rows), k < cache_rows / page_rows.  Position
+ * t of sequence b is row block_table[b * max_pages + t / page_rows] *
+ * page_rows + t % page_rows.  Pages may be shared between sequences (a
+ * common prefix) and need not be in any order.
+ *   block_table: HOST (B, max_pages) int32; only the first
+ *     ceil(seq_len[b] / page_rows) entries of row b are read.
+ *   page_rows: a power of two, 32 .. 2^30 (a 32-row tile of the decode cores
+ *     never crosses a page).
+ *   pos, seq_len: HOST, as for mla_decode (pos[b] == seq_len[b] - 1).
+ * mla_decode_step_paged writes each new row at position seq_len[b] - 1,
+ * through the block table; those rows must be distinct.  Results are those of
+ * mla_decode / mla_decode_step on a contiguous cache holding the same rows
+ * (bit for bit: the work split depends on seq_len only).  Workspace: the
+ * contiguous call's (mla_decode_workspace_bytes,
+ * mla_decode_step_workspace_bytes with the same B and total rows).
+ * Errors: as mla_decode; page_rows not a power of two in range, max_pages < 1
+ * or a NULL table -> INVALID_ARG; more pages needed than max_pages, or a page
+ * index outside [0, cache_rows / page_rows) -> CAPACITY; two new rows of a
+ * step on the same cache row -> INVALID_ARG. */
+int mla_decode_paged(mla_handle h, const void* hidden, const int32_t* pos,
+                     const int32_t* block_table, int32_t max_pages, int32_t page_rows,
+                     const int32_t* seq_len, int32_t B, const void* cache, int64_t cache_rows,
+                     void* out, void* ws, size_t ws_bytes);
+int mla_decode_step_paged(mla_handle h, const void* hidden, const int32_t* pos,
+                          const int32_t* block_table, int32_t max_pages, int32_t page_rows,
+                          const int32_t* seq_len, int32_t B, void* cache, int64_t cache_rows,
+                          void* out, void* ws, size_t ws_bytes);
 
 /* Where the staged intermediates of the last mla_decode with these (B,
  * total_rows) live inside its workspace, as byte offsets from ws:

@@ -47,5 +47,18 @@ __device__ __forceinline__ DecodeWork load_work(ConstWorkPtr p) {
   return w;
 }
 
+// Cache row of position r of a work record's segment (r counted from the
+// segment's first position; a tile start, so a tile never crosses a page:
+// segments start on multiples of 32 positions and pages hold 2^k >= 32 rows).
+// The page list is read through the constant address space (scalar loads).
+__device__ __forceinline__ int64_t seg_row(const DecodeMeta& mt, int64_t wrow, int r) {
+  if (mt.page_shift == 0) return wrow + r;
+  typedef const __attribute__((address_space(4))) int32_t* ConstI32Ptr;
+  const int32_t pg = (int32_t)(wrow >> 32);
+  const int32_t t = (int32_t)(wrow & 0x7fffffff) + r;
+  const int32_t page = reinterpret_cast<ConstI32Ptr>((uintptr_t)mt.pages)[pg + (t >> mt.page_shift)];
+  return ((int64_t)page << mt.page_shift) + (t & ((1 << mt.page_shift) - 1));
+}
+
 }  // namespace ddev
 }  // namespace mla

@@ -144,7 +144,7 @@ decode_core_ring_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
         issue_tile(qb, 15, stage, p, lane);
       } else {
         const int t = ik - 1;
-        const char* rb = reinterpret_cast<const char*>(cache + (iw.row + (int64_t)t * TR) * RW);
+        const char* rb = reinterpret_cast<const char*>(cache + seg_row(mt, iw.row, t * TR) * RW);
         issue_tile(rb, iw.n - t * TR - 1, stage, p, lane);
       }
       ++ik;

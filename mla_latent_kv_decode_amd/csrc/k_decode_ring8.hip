@@ -227,7 +227,7 @@ decode_core_ring8_k(const bf16* __restrict__ q_cat, const uint8_t* __restrict__ 
                     stage, p, lane);
       } else {
         const int t = ik - 1;
-        issue_rows(reinterpret_cast<const char*>(cache) + (iw.row + (int64_t)t * TR) * RB,
+        issue_rows(reinterpret_cast<const char*>(cache) + seg_row(mt, iw.row, t * TR) * RB,
                    iw.n - t * TR - 1, stage, p, lane);
       }
       ++ik;

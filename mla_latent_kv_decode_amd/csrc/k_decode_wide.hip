@@ -18,11 +18,12 @@
 // rescale are those of the 16-head core.
 #include <utility>
 
-#include "kernels.h"
-#include "stage_layout.h"
+#include "decode_dev.h"
 
 namespace mla {
 namespace decw {
+
+using namespace ddev;
 
 constexpr int DC = 512;
 constexpr int RW = 576;
@@ -44,34 +45,6 @@ static_assert(ROPE_OFF + TR * 128 == ST_BYTES, "stage layout");
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x8_t __attribute__((ext_vector_type(8)));
-typedef const __attribute__((address_space(4))) DecodeWork* ConstWorkPtr;
-
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(g), "s"(lds_addr)
-               : "memory", "m0");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_u32(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-__device__ __forceinline__ DecodeWork load_work(ConstWorkPtr p) {
-  DecodeWork w;
-  w.row = p->row;
-  w.n = p->n;
-  w.b = p->b;
-  w.pidx = p->pidx;
-  w.next = p->next;
-  return w;
-}
-
 // Load I of a tile whose first row is at `base` and whose last valid row is
 // `last`: I < 32 copies the latent part of row I (source chunk lane ^ lat_swz(I & 15)),
 // I >= 32 the rope parts of rows 8j .. 8j+7.  Rows past `last` re-read it.
@@ -160,11 +133,12 @@ decode_core_wide_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
   for (;;) {
     const int n = wk.n;
     const int ntile = (n + TR - 1) / TR;
-    const char* rows = reinterpret_cast<const char*>(cache + wk.row * (int64_t)RW);
+    const int64_t wrow = wk.row;
 #pragma unroll
     for (int t = 0; t < NST - 1; ++t)
       if (t < ntile)
-        issue_tile(rows + t * TR * (RW * 2), n - t * TR - 1, lds0 + t * ST_BYTES, wave);
+        issue_tile(reinterpret_cast<const char*>(cache + seg_row(mt, wrow, t * TR) * RW),
+                   n - t * TR - 1, lds0 + t * ST_BYTES, wave);
     DecodeWork nx = wk;
     if (wk.next >= 0) nx = load_work(works + wk.next);
 
@@ -201,8 +175,8 @@ decode_core_wide_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
       else wait_vmcnt<0>();
       __syncthreads();  // tile t is in LDS; every wave is done with tile t-1
       if (t + NST - 1 < ntile)
-        issue_tile(rows + (t + NST - 1) * TR * (RW * 2), n - (t + NST - 1) * TR - 1,
-                   lds0 + ((t + NST - 1) % NST) * ST_BYTES, wave);
+        issue_tile(reinterpret_cast<const char*>(cache + seg_row(mt, wrow, (t + NST - 1) * TR) * RW),
+                   n - (t + NST - 1) * TR - 1, lds0 + ((t + NST - 1) % NST) * ST_BYTES, wave);
       const char* st = lds + (t % NST) * ST_BYTES;
       const int row0 = t * TR;
       // ---- S^T = K . Q^T for both 16-row blocks, K fragments read once per head group

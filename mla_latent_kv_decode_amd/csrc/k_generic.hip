@@ -301,15 +301,26 @@ decode_core_generic_k(const T* __restrict__ q_cat, const T* __restrict__ cache, 
   for (int j = threadIdx.x; j < R; j += blockDim.x)
     q[j] = ldf(q_cat + ((int64_t)sg.b * d.H + h) * R + j);
   __syncthreads();
-  const T* rows = cache + (mt.seq_off[sg.b] + sg.r0) * (int64_t)R;
   const int n = sg.r1 - sg.r0;
+  // cache row of the segment's position t (contiguous, or through the page list)
+  auto row_of = [&](int t) -> const T* {
+    int64_t r;
+    if (mt.page_shift) {
+      const int pos = sg.r0 + t;
+      r = ((int64_t)mt.pages[mt.pg_off[sg.b] + (pos >> mt.page_shift)] << mt.page_shift) +
+          (pos & ((1 << mt.page_shift) - 1));
+    } else {
+      r = mt.seq_off[sg.b] + sg.r0 + t;
+    }
+    return cache + r * (int64_t)R;
+  };
   float m = -INFINITY, l = 0.f;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};  // dc <= 1024
   for (int t0 = 0; t0 < n; t0 += 256) {
     const int t = t0 + threadIdx.x;
     float s = -INFINITY;
     if (t < n) {
-      const T* r = rows + (int64_t)t * R;
+      const T* r = row_of(t);
       float dot = 0.f;
       for (int j = 0; j < R; ++j) dot = fmaf(q[j], ldf(r + j), dot);
       s = dot * kLog2e;
@@ -332,7 +343,7 @@ decode_core_generic_k(const T* __restrict__ q_cat, const T* __restrict__ cache, 
       const int c = threadIdx.x + c4 * 256;
       if (c < d.dc) {
         float a = acc[c4] * alpha;
-        for (int k = 0; k < cnt; ++k) a = fmaf(p[k], ldf(rows + (int64_t)(t0 + k) * R + c), a);
+        for (int k = 0; k < cnt; ++k) a = fmaf(p[k], ldf(row_of(t0 + k) + c), a);
         acc[c4] = a;
       }
     }

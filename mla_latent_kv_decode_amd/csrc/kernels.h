@@ -58,6 +58,15 @@ struct DecodeMeta {
   const int32_t* part_begin;  // (parts + 1) segment range of each persistent part
   const int32_t* cstart;    // (B) first chunk slot of sequence b (two-stage combine)
   const DecodeWork* work;   // (nseg_total) work records of the MFMA core
+  // Paged cache (page_shift > 0): pages of 2^page_shift rows; position t of
+  // sequence b is cache row pages[pg_off[b] + (t >> page_shift)] *
+  // 2^page_shift + t % 2^page_shift, and a work record's `row` holds
+  // pg_off[b] << 32 | (the segment's first position).  page_shift == 0: rows
+  // of sequence b are contiguous from seq_off[b] and `row` is the segment's
+  // first cache row.
+  const int32_t* pages;     // (sum_b ceil(seq_len[b] / page_rows))
+  const int32_t* pg_off;    // (B)
+  int32_t page_shift;
 };
 
 // The 512-wide combine merges the partials of a sequence in chunks of

@@ -336,10 +336,16 @@ int max_parts(const mla_ctx* h, int64_t total_rows) {
   return (int)p;
 }
 
-size_t meta_bytes(int B, int parts, int max_segs) {
+// page lists of a paged cache: at most total_rows / 32 + B pages (pages hold
+// 32 rows or more)
+size_t page_list_bytes(int B, int64_t total_rows) {
+  return align_up((size_t)B * 4) + align_up((size_t)(total_rows / 32 + B) * 4);
+}
+
+size_t meta_bytes(int B, int parts, int max_segs, int64_t total_rows) {
   return 2 * align_up((size_t)B * 8) + 5 * align_up((size_t)B * 4) +
          align_up((size_t)(parts + 1) * 4) + align_up((size_t)max_segs * sizeof(DecodeSeg)) +
-         align_up((size_t)max_segs * sizeof(mla::DecodeWork));
+         align_up((size_t)max_segs * sizeof(mla::DecodeWork)) + page_list_bytes(B, total_rows);
 }
 
 int qw_of(const Dims& d) { return d.H * (d.dn + d.dr); }
@@ -365,7 +371,7 @@ DecodeLayout decode_layout(const mla_ctx* h, int B, int64_t total_rows, bool ste
   if (d.dq) pq = part_floats(h, B, qw, d.dq);
   const size_t e = h->esz;
   Carve c;
-  L.meta = c.take(meta_bytes(B, parts, L.max_segs));
+  L.meta = c.take(meta_bytes(B, parts, L.max_segs, total_rows));
   L.scratch = c.take(scr * 4);
   L.pin = c.take(pin * 4);
   L.pq = c.take(pq * 4);
@@ -383,8 +389,20 @@ DecodeLayout decode_layout(const mla_ctx* h, int B, int64_t total_rows, bool ste
 }
 
 struct MetaOffsets {
-  size_t seq_off, seq_len, pos, pstart, nseg, cstart, part, segs, work, slot;
+  size_t seq_off, seq_len, pos, pstart, nseg, cstart, part, segs, work, slot, pg_off, pages;
 };
+
+// A paged cache view (NULL for a contiguous cache): block_table (B x max_pages,
+// host) lists the pages of each sequence, pages hold page_rows = 2^shift rows.
+struct PageArgs {
+  const int32_t* table;
+  int32_t max_pages, page_rows, shift;
+};
+
+int64_t paged_row(const PageArgs& pg, int b, int64_t t) {
+  return (int64_t)pg.table[(int64_t)b * pg.max_pages + (t >> pg.shift)] * pg.page_rows +
+         (t & (pg.page_rows - 1));
+}
 
 // Host-side work list.  The concatenated rows of all sequences are cut into
 // at most `max_parts(total)` contiguous spans, one persistent workgroup each,
@@ -450,8 +468,9 @@ int plan_spans(int B, const int32_t* seq_len, int max_p, SpanPlan* plan) {
 }
 
 int build_decode_meta(const mla_ctx* h, int B, const int64_t* seq_off, const int32_t* seq_len,
-                      const int32_t* pos, int64_t total, bool with_slot, std::vector<char>& blob,
-                      MetaOffsets* mo, int* nseg_total, int* max_chunks, int* cslots) {
+                      const int32_t* pos, int64_t total, bool with_slot, const PageArgs* pg,
+                      std::vector<char>& blob, MetaOffsets* mo, int* nseg_total, int* max_chunks,
+                      int* cslots) {
   SpanPlan plan;
   const int parts = plan_spans(B, seq_len, max_parts(h, total), &plan);
   std::vector<DecodeSeg>& segs = plan.segs;
@@ -484,11 +503,33 @@ int build_decode_meta(const mla_ctx* h, int B, const int64_t* seq_off, const int
   mo->part = c.take((size_t)(parts + 1) * 4);
   mo->segs = c.take(segs.size() * sizeof(DecodeSeg));
   mo->work = c.take(segs.size() * sizeof(mla::DecodeWork));
+  // paged: each sequence's used pages, back to back (pg_off[b]: its first)
+  std::vector<int32_t> pg_off;
+  int64_t npages = 0;
+  if (pg) {
+    pg_off.resize(B);
+    for (int b = 0; b < B; ++b) {
+      pg_off[b] = (int32_t)npages;
+      npages += (seq_len[b] + pg->page_rows - 1) / pg->page_rows;
+    }
+  }
+  mo->pg_off = c.take(pg ? (size_t)B * 4 : 0);
+  mo->pages = c.take((size_t)npages * 4);
   blob.assign(c.off, 0);
-  memcpy(blob.data() + mo->seq_off, seq_off, (size_t)B * 8);
+  if (pg) {
+    memcpy(blob.data() + mo->pg_off, pg_off.data(), (size_t)B * 4);
+    int32_t* pl = reinterpret_cast<int32_t*>(blob.data() + mo->pages);
+    for (int b = 0; b < B; ++b) {
+      const int np = (seq_len[b] + pg->page_rows - 1) / pg->page_rows;
+      memcpy(pl + pg_off[b], pg->table + (int64_t)b * pg->max_pages, (size_t)np * 4);
+    }
+  } else {
+    memcpy(blob.data() + mo->seq_off, seq_off, (size_t)B * 8);
+  }
   if (with_slot) {
     int64_t* sl = reinterpret_cast<int64_t*>(blob.data() + mo->slot);
-    for (int i = 0; i < B; ++i) sl[i] = seq_off[i] + seq_len[i] - 1;
+    for (int i = 0; i < B; ++i)
+      sl[i] = pg ? paged_row(*pg, i, seq_len[i] - 1) : seq_off[i] + seq_len[i] - 1;
   }
   memcpy(blob.data() + mo->seq_len, seq_len, (size_t)B * 4);
   memcpy(blob.data() + mo->pos, pos, (size_t)B * 4);
@@ -506,7 +547,7 @@ int build_decode_meta(const mla_ctx* h, int B, const int64_t* seq_off, const int
       for (int si = part_begin[p]; si < part_begin[p + 1]; ++si) {
         const DecodeSeg& sg = segs[si];
         mla::DecodeWork& w = work[slot];
-        w.row = seq_off[sg.b] + sg.r0;
+        w.row = pg ? ((int64_t)pg_off[sg.b] << 32) | sg.r0 : seq_off[sg.b] + sg.r0;
         w.n = sg.r1 - sg.r0;
         w.b = sg.b;
         w.pidx = sg.pidx;
@@ -636,6 +677,38 @@ int mla_decode_check(const mla_config* cfg, const int32_t* pos, const int64_t* s
   for (int32_t b = 0; b < B; ++b) {
     if (seq_len[b] < 1 || pos[b] != seq_len[b] - 1) return MLA_ERR_INVALID_ARG;
     if (seq_off[b] < 0 || seq_off[b] > cache_rows - seq_len[b]) return MLA_ERR_CAPACITY;
+  }
+  return MLA_OK;
+}
+
+int mla_decode_paged_check(const mla_config* cfg, const int32_t* pos, const int32_t* block_table,
+                           int32_t max_pages, int32_t page_rows, const int32_t* seq_len, int32_t B,
+                           int64_t cache_rows, int32_t writes) {
+  int rc = mla_config_check(cfg);
+  if (rc) return rc;
+  if (B <= 0 || !pos || !block_table || !seq_len || cache_rows <= 0 || max_pages <= 0)
+    return MLA_ERR_INVALID_ARG;
+  if (page_rows < 32 || page_rows > (1 << 30) || (page_rows & (page_rows - 1)))
+    return MLA_ERR_INVALID_ARG;
+  const int64_t n_pages = cache_rows / page_rows;
+  for (int32_t b = 0; b < B; ++b)
+    if (seq_len[b] < 1 || pos[b] != seq_len[b] - 1) return MLA_ERR_INVALID_ARG;
+  for (int32_t b = 0; b < B; ++b) {
+    const int64_t np = ((int64_t)seq_len[b] + page_rows - 1) / page_rows;
+    if (np > max_pages) return MLA_ERR_CAPACITY;
+    const int32_t* row = block_table + (int64_t)b * max_pages;
+    for (int64_t i = 0; i < np; ++i)
+      if (row[i] < 0 || row[i] >= n_pages) return MLA_ERR_CAPACITY;
+  }
+  if (writes) {  // the new rows of a step: one cache row each, all distinct
+    std::vector<int64_t> w(B);
+    for (int32_t b = 0; b < B; ++b) {
+      const int32_t t = seq_len[b] - 1;
+      w[b] = (int64_t)block_table[(int64_t)b * max_pages + t / page_rows] * page_rows +
+             t % page_rows;
+    }
+    std::sort(w.begin(), w.end());
+    if (std::adjacent_find(w.begin(), w.end()) != w.end()) return MLA_ERR_INVALID_ARG;
   }
   return MLA_OK;
 }
@@ -1155,11 +1228,16 @@ static int run_decode(mla_ctx* h, const T* hidden, int B, T* cache, T* out, void
 
 static int decode_common(mla_handle h, const void* hidden, const int32_t* pos,
                          const int64_t* seq_off, const int32_t* seq_len, int32_t B, void* cache,
-                         int64_t cache_rows, void* out, void* ws, size_t ws_bytes, bool step) {
+                         int64_t cache_rows, void* out, void* ws, size_t ws_bytes, bool step,
+                         const PageArgs* pg = nullptr) {
   if (!h) return MLA_ERR_INVALID_ARG;
-  const char* what = step ? "decode_step" : "decode";
+  const char* what = pg ? (step ? "decode_step_paged" : "decode_paged")
+                        : (step ? "decode_step" : "decode");
   if (!hidden || !cache || !out) return fail(h, MLA_ERR_INVALID_ARG, "%s: NULL tensor", what);
-  int rc = mla_decode_check(&h->cfg, pos, seq_off, seq_len, B, cache_rows);
+  int rc = pg ? mla_decode_paged_check(&h->cfg, pos, pg ? pg->table : nullptr,
+                                       pg ? pg->max_pages : 0, pg ? pg->page_rows : 0, seq_len,
+                                       B, cache_rows, step ? 1 : 0)
+              : mla_decode_check(&h->cfg, pos, seq_off, seq_len, B, cache_rows);
   if (rc) return fail(h, rc, "%s: %s (B=%d, cache_rows=%lld)", what, mla_status_string(rc), B,
                       (long long)cache_rows);
   if (!h->absorbed) return fail(h, MLA_ERR_STATE, "%s before mla_absorb_weights", what);
@@ -1172,11 +1250,11 @@ static int decode_common(mla_handle h, const void* hidden, const int32_t* pos,
   std::vector<char> blob;
   MetaOffsets mo;
   int nseg_total = 0, max_chunks = 1, cslots = 0;
-  const int parts = build_decode_meta(h, B, seq_off, seq_len, pos, total, step, blob, &mo,
+  const int parts = build_decode_meta(h, B, seq_off, seq_len, pos, total, step, pg, blob, &mo,
                                       &nseg_total, &max_chunks, &cslots);
   if (cslots > L.max_cslots)
     return fail(h, MLA_ERR_WORKSPACE, "internal: combine chunk slots larger than planned");
-  if (blob.size() > meta_bytes(B, max_parts(h, total), L.max_segs))
+  if (blob.size() > meta_bytes(B, max_parts(h, total), L.max_segs, total))
     return fail(h, MLA_ERR_WORKSPACE, "internal: decode metadata larger than planned");
   void* meta = at<char>(ws, L.meta);
   if ((rc = stage_upload(h, meta, blob.data(), blob.size()))) return rc;
@@ -1190,6 +1268,9 @@ static int decode_common(mla_handle h, const void* hidden, const int32_t* pos,
   mt.work = at<mla::DecodeWork>(meta, mo.work);
   mt.part_begin = at<int32_t>(meta, mo.part);
   mt.segs = at<DecodeSeg>(meta, mo.segs);
+  mt.pages = pg ? at<int32_t>(meta, mo.pages) : nullptr;
+  mt.pg_off = pg ? at<int32_t>(meta, mo.pg_off) : nullptr;
+  mt.page_shift = pg ? pg->shift : 0;
   const int64_t* slot_dev = step ? at<int64_t>(meta, mo.slot) : nullptr;
   if (is_f32(h))
     return run_decode<float>(h, (const float*)hidden, B, (float*)cache, (float*)out, ws, L, mt,
@@ -1210,6 +1291,30 @@ int mla_decode_step(mla_handle h, const void* hidden, const int32_t* pos, const 
                     void* ws, size_t ws_bytes) {
   return decode_common(h, hidden, pos, seq_off, seq_len, B, cache, cache_rows, out, ws, ws_bytes,
                        true);
+}
+
+static int page_shift_of(int32_t page_rows) {
+  int k = 0;
+  while ((1 << k) < page_rows && k < 30) ++k;
+  return k;
+}
+
+int mla_decode_paged(mla_handle h, const void* hidden, const int32_t* pos,
+                     const int32_t* block_table, int32_t max_pages, int32_t page_rows,
+                     const int32_t* seq_len, int32_t B, const void* cache, int64_t cache_rows,
+                     void* out, void* ws, size_t ws_bytes) {
+  const PageArgs pg{block_table, max_pages, page_rows, page_shift_of(page_rows)};
+  return decode_common(h, hidden, pos, nullptr, seq_len, B, const_cast<void*>(cache), cache_rows,
+                       out, ws, ws_bytes, false, &pg);
+}
+
+int mla_decode_step_paged(mla_handle h, const void* hidden, const int32_t* pos,
+                          const int32_t* block_table, int32_t max_pages, int32_t page_rows,
+                          const int32_t* seq_len, int32_t B, void* cache, int64_t cache_rows,
+                          void* out, void* ws, size_t ws_bytes) {
+  const PageArgs pg{block_table, max_pages, page_rows, page_shift_of(page_rows)};
+  return decode_common(h, hidden, pos, nullptr, seq_len, B, cache, cache_rows, out, ws, ws_bytes,
+                       true, &pg);
 }
 
 // ------------------------------------------------------------------------

@@ -55,6 +55,9 @@ _SIGS = {
                                         ctypes.c_int32, ctypes.c_int64]),
     "mla_prefill_check": (ctypes.c_int, [ctypes.POINTER(MLAConfig), _I32P, _I32P, _I64P,
                                          ctypes.c_int32, ctypes.c_int64]),
+    "mla_decode_paged_check": (ctypes.c_int, [ctypes.POINTER(MLAConfig), _I32P, _I32P,
+                                              ctypes.c_int32, ctypes.c_int32, _I32P,
+                                              ctypes.c_int32, ctypes.c_int64, ctypes.c_int32]),
     "mla_create": (ctypes.c_int, [ctypes.POINTER(MLAConfig), _P, ctypes.POINTER(_P)]),
     "mla_destroy": (ctypes.c_int, [_P]),
     "mla_set_stream": (ctypes.c_int, [_P, _P]),
@@ -73,6 +76,12 @@ _SIGS = {
     "mla_decode_step_workspace_bytes": (ctypes.c_size_t, [_P, ctypes.c_int32, ctypes.c_int64]),
     "mla_decode_step": (ctypes.c_int, [_P, _P, _I32P, _I64P, _I32P, ctypes.c_int32, _P,
                                        ctypes.c_int64, _P, _P, ctypes.c_size_t]),
+    "mla_decode_paged": (ctypes.c_int, [_P, _P, _I32P, _I32P, ctypes.c_int32, ctypes.c_int32,
+                                        _I32P, ctypes.c_int32, _P, ctypes.c_int64, _P, _P,
+                                        ctypes.c_size_t]),
+    "mla_decode_step_paged": (ctypes.c_int, [_P, _P, _I32P, _I32P, ctypes.c_int32,
+                                             ctypes.c_int32, _I32P, ctypes.c_int32, _P,
+                                             ctypes.c_int64, _P, _P, ctypes.c_size_t]),
     "mla_decode_stage_offsets": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.c_int64,
                                                 ctypes.POINTER(ctypes.c_size_t),
                                                 ctypes.POINTER(ctypes.c_size_t)]),
@@ -278,6 +287,9 @@ class MLALayer:
         self._check(rc, self.h, "mla_decode")
         if not stages:
             return out
+        return (out,) + self._stages(B, total, wsp)
+
+    def _stages(self, B, total, wsp):
         qo, oo = ctypes.c_size_t(), ctypes.c_size_t()
         self._check(self.lib.mla_decode_stage_offsets(self.h, B, total, ctypes.byref(qo),
                                                       ctypes.byref(oo)), self.h, "stages")
@@ -289,7 +301,51 @@ class MLALayer:
         o_lat = raw[base + oo.value: base + oo.value + B * d.n_heads * d.kv_lora * es]
         q_cat = q_cat.view(self.torch_dtype).reshape(B, d.n_heads, d.row).clone()
         o_lat = o_lat.view(self.torch_dtype).reshape(B, d.n_heads, d.kv_lora).clone()
-        return out, q_cat, o_lat
+        return q_cat, o_lat
+
+    # -- A3..A8 over a paged cache
+    def decode_paged(self, hidden, pos, block_table, page_rows, seq_len, cache, out=None,
+                     stages=False):
+        """mla_decode_paged: block_table (B, max_pages) int32 host array; page
+        k of the cache is rows [k * page_rows, (k + 1) * page_rows)."""
+        import torch
+        self._sync_stream()
+        B = int(hidden.shape[0])
+        pos_a, pos_p = _i32(pos)
+        bt = np.ascontiguousarray(block_table, dtype=np.int32)
+        bt_a, bt_p = _i32(bt.reshape(-1))
+        sl_a, sl_p = _i32(seq_len)
+        total = int(sl_a.astype(np.int64).sum())
+        if out is None:
+            out = torch.empty((B, self.dims.hidden), dtype=self.torch_dtype, device=self.device)
+        wsp, wsn = self.ws.get(self.lib.mla_decode_workspace_bytes(self.h, B, max(total, 1)))
+        rc = self.lib.mla_decode_paged(self.h, _ptr(hidden), pos_p, bt_p, int(bt.shape[1]),
+                                       int(page_rows), sl_p, B, _ptr(cache),
+                                       int(cache.shape[0]), _ptr(out), wsp, wsn)
+        self._check(rc, self.h, "mla_decode_paged")
+        if not stages:
+            return out
+        return (out,) + self._stages(B, total, wsp)
+
+    def decode_step_paged(self, hidden, block_table, page_rows, seq_len, cache, out=None):
+        """mla_decode_step_paged: appends each new token at position
+        seq_len[b] - 1 through the block table, then decodes."""
+        import torch
+        self._sync_stream()
+        B = int(hidden.shape[0])
+        bt = np.ascontiguousarray(block_table, dtype=np.int32)
+        bt_a, bt_p = _i32(bt.reshape(-1))
+        sl_a, sl_p = _i32(seq_len)
+        pos_a, pos_p = _i32(sl_a - 1)
+        total = int(sl_a.astype(np.int64).sum())
+        if out is None:
+            out = torch.empty((B, self.dims.hidden), dtype=self.torch_dtype, device=self.device)
+        wsp, wsn = self.ws.get(self.lib.mla_decode_step_workspace_bytes(self.h, B, max(total, 1)))
+        rc = self.lib.mla_decode_step_paged(self.h, _ptr(hidden), pos_p, bt_p, int(bt.shape[1]),
+                                            int(page_rows), sl_p, B, _ptr(cache),
+                                            int(cache.shape[0]), _ptr(out), wsp, wsn)
+        self._check(rc, self.h, "mla_decode_step_paged")
+        return out
 
     def decode_step(self, hidden, seq_off, seq_len, cache, out=None):
         """Append each sequence's new token (row seq_off[b] + seq_len[b] - 1,

@@ -18,6 +18,11 @@ Sources (cited by page title and section in each docstring):
   * "Transformer and KV Cache Basics" (KV Cache section) -- prefill vs decode
     and the offset causal mask for multi-token steps.
 
+Two storage modules sit beside the layer: ``oracle.fp8`` (an FP8 E4M3 latent
+cache with one scale per row, read back as the cache would hand it out) and
+``oracle.paged`` (the row lookup of a cache kept in pages named by a block
+table).
+
 Parity status: every function here is pinned by the ``-m "not gpu"`` tests in
 ``tests/test_oracle_pins.py`` (brute force, identities, closed forms, special
 cases); no function is "parity unpinned".

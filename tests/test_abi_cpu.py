@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(mla):
     missing = [n for n in names if not hasattr(mla, n)]
     assert not missing, missing
     assert set(names) == set(L._SIGS), set(names) ^ set(L._SIGS)
-    assert mla.mla_abi_version() == 2
+    assert mla.mla_abi_version() == 3
 
 
 def test_status_strings(mla):
@@ -128,6 +128,34 @@ def test_decode_check(mla):
     assert chk([], [], [], 6) == L.MLA_ERR_INVALID_ARG              # B = 0
     # int64 offsets near the top of the range must not overflow into "fits"
     assert chk([4], [2 ** 62], [5], 2 ** 62) == L.MLA_ERR_CAPACITY
+
+
+def test_decode_paged_check(mla):
+    c = cfg()
+
+    def chk(pos, table, page_rows, ln, rows, writes=0):
+        pa, pp = _i32(pos)
+        t = np.ascontiguousarray(table, dtype=np.int32)
+        ta, tp = _i32(t.reshape(-1))
+        la, lp = _i32(ln)
+        return mla.mla_decode_paged_check(ctypes.byref(c), pp, tp, t.shape[1], page_rows, lp,
+                                          len(pa), rows, writes)
+
+    # 4 pages of 32 rows; sequence 0 (40 rows) on pages 3, 1; sequence 1 (5 rows) on page 0
+    ok = ([39, 4], [[3, 1], [0, -7]], 32, [40, 5], 128)
+    assert chk(*ok) == L.MLA_OK
+    assert chk(*ok, writes=1) == L.MLA_OK
+    assert chk([39, 4], [[3, 1], [0, -7]], 32, [40, 5], 127) == L.MLA_ERR_CAPACITY  # page 3 gone
+    assert chk([39, 4], [[4, 1], [0, 0]], 32, [40, 5], 128) == L.MLA_ERR_CAPACITY   # page >= 4
+    assert chk([39, 4], [[3, -1], [0, 0]], 32, [40, 5], 128) == L.MLA_ERR_CAPACITY  # negative
+    assert chk([64, 4], [[3, 1], [0, 0]], 32, [65, 5], 128) == L.MLA_ERR_CAPACITY   # 3 pages > 2
+    for bad_p in (16, 48, 0, -32):                                                   # power of 2 >= 32
+        assert chk([39, 4], [[3, 1], [0, 0]], bad_p, [40, 5], 128) == L.MLA_ERR_INVALID_ARG
+    assert chk([38, 4], [[3, 1], [0, 0]], 32, [40, 5], 128) == L.MLA_ERR_INVALID_ARG  # pos
+    # a step writing two new rows onto one cache row (shared last page, same offset)
+    assert chk([4, 4], [[2], [2]], 32, [5, 5], 128, writes=1) == L.MLA_ERR_INVALID_ARG
+    assert chk([4, 4], [[2], [2]], 32, [5, 5], 128, writes=0) == L.MLA_OK  # reads may share
+    assert chk([4, 5], [[2], [2]], 32, [5, 6], 128, writes=1) == L.MLA_OK  # different offsets
 
 
 def test_prefill_check(mla):

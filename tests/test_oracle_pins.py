@@ -433,3 +433,82 @@ def test_fp8_cache_decode_step_stays_near_the_exact_one():
     q8 = O.mla_step(x[300:], np.array([300]), prior, w, shp,
                     kv_store=lambda r: F8.fp8_rows(r, shp.kv_lora))["y"]
     assert 0 < rel_err(q8, exact) < 2.0 ** -4
+
+
+# ---------------------------------------------------------------- paged cache
+from oracle import paged as PG  # noqa: E402
+
+
+def _paged_fixture(seed, lens, P, n_pages, R=5):
+    """Random rows per sequence and a block table of distinct random pages."""
+    rng = np.random.default_rng(seed)
+    rows = [rng.standard_normal((n, R)) for n in lens]
+    need = [(n + P - 1) // P for n in lens]
+    perm = rng.permutation(n_pages)
+    table = np.full((len(lens), max(need)), -1, dtype=np.int32)
+    k = 0
+    for b, m in enumerate(need):
+        table[b, :m] = perm[k:k + m]
+        k += m
+    return rows, table
+
+
+def test_paged_gather_brute_force():
+    """Write every sequence page by page with plain loops (page k of sequence
+    b receives its positions k P .. k P + P - 1), then read back through the
+    block table: the rows come back in position order, untouched pool rows
+    stay untouched."""
+    P, n_pages, lens = 4, 40, [1, 4, 5, 11, 16, 3]
+    rows, table = _paged_fixture(7, lens, P, n_pages)
+    pool = [[float("nan")] * 5 for _ in range(P * n_pages)]
+    used = set()
+    for b, n in enumerate(lens):
+        for k in range((n + P - 1) // P):
+            page = int(table[b][k])
+            for j in range(P):
+                t = k * P + j
+                if t < n:
+                    pool[page * P + j] = list(rows[b][t])
+                    used.add(page * P + j)
+    pool = np.array(pool)
+    got = PG.gather(pool, table, P, lens)
+    for b in range(len(lens)):
+        assert np.array_equal(got[b], rows[b]), b
+    untouched = np.array(sorted(set(range(P * n_pages)) - used))
+    assert np.all(np.isnan(pool[untouched]))
+    assert list(PG.pages_needed(lens, P)) == [1, 1, 2, 3, 4, 1]
+
+
+def test_paged_identity_table_is_the_contiguous_cache():
+    """Pages laid out back to back in sequence order (each sequence starting
+    on a page boundary): the paged read is the contiguous slice."""
+    P, lens = 8, [3, 8, 17, 30]
+    starts = np.concatenate([[0], np.cumsum(PG.pages_needed(lens, P))[:-1]])
+    table = np.zeros((len(lens), 4), dtype=np.int32)
+    for b, n in enumerate(lens):
+        m = int(PG.pages_needed([n], P)[0])
+        table[b, :m] = starts[b] + np.arange(m)
+    pool = np.random.default_rng(8).standard_normal((P * 12, 3))
+    got = PG.gather(pool, table, P, lens)
+    for b, n in enumerate(lens):
+        off = int(starts[b]) * P
+        assert np.array_equal(got[b], pool[off:off + n])
+
+
+def test_paged_shared_prefix_and_page_permutation():
+    P = 4
+    pool = np.random.default_rng(9).standard_normal((P * 10, 2))
+    # two sequences share their first page
+    table = np.array([[3, 7, 1], [3, 5, 0]], dtype=np.int32)
+    a, b = PG.gather(pool, table, P, [10, 9])
+    assert np.array_equal(a[:P], b[:P]) and not np.array_equal(a[P:8], b[P:8])
+    # moving the pool's pages and renaming them in the table changes nothing
+    perm = np.random.default_rng(10).permutation(10)       # page k moves to perm[k]
+    moved = np.empty_like(pool)
+    for k in range(10):
+        moved[perm[k] * P:(perm[k] + 1) * P] = pool[k * P:(k + 1) * P]
+    a2, b2 = PG.gather(moved, perm[table], P, [10, 9])
+    assert np.array_equal(a2, a) and np.array_equal(b2, b)
+    # the row of position t: page t // P of the table, offset t % P
+    assert PG.row_index(table, P, 0, 9) == 1 * P + 1
+    assert PG.row_index(table, P, 1, 4) == 5 * P + 0
