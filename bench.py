@@ -22,6 +22,9 @@ cached lengths ~ U{512..8192} (``v2lite_decode_b64``).
 cache (656-byte rows: E4M3 codes, bf16 RoPE key, per-row scale); its GB/s
 count those bytes.
 
+``--workload v2lite_decode_b64_paged`` is the same batch on a paged cache
+(64-row pages handed out in a seeded random order, mla_decode_step_paged).
+
 ``--workload v3_prefill_4x4096`` measures the chunked causal prefill instead
 (V3 shapes, 4 sequences of 4096 new tokens after 0 / 2048 cached rows): a step
 is the append of the new tokens' latent rows plus one mla_prefill call over the
@@ -333,7 +336,24 @@ def main():
             layer.append(torch.from_numpy(x).cuda().to(tdt), np.arange(s, s + m),
                          int(seq_off[b]) + np.arange(s, s + m), caches[0])
         x_new[b] = x[-1]
-    caches[1].copy_(caches[0])
+    P = wl.page_rows
+    if P:
+        # a paged cache: the same rows moved into 64-row pages handed out in a
+        # seeded random order (two pools alternate like the two caches)
+        table, n_pages = synth.page_table(seq_len, P)
+        src, dst = [], []
+        for b in range(B):
+            t = np.arange(int(seq_len[b]))
+            src.append(int(seq_off[b]) + t)
+            dst.append(table[b, t // P].astype(np.int64) * P + t % P)
+        src_t = torch.as_tensor(np.concatenate(src), device="cuda")
+        dst_t = torch.as_tensor(np.concatenate(dst), device="cuda")
+        pool = layer.new_cache(n_pages * P)
+        pool[dst_t] = caches[0][src_t]
+        caches = [pool, pool.clone()]
+        del src_t, dst_t
+    else:
+        caches[1].copy_(caches[0])
     xd = torch.from_numpy(x_new).cuda().to(tdt)
     pos = (seq_len - 1).astype(np.int32)
     slot = seq_off + pos
@@ -342,7 +362,10 @@ def main():
 
     def step(i):
         # append the B new rows and decode them in one library call
-        layer.decode_step(xd, seq_off, seq_len, caches[i % 2], out=y)
+        if P:
+            layer.decode_step_paged(xd, table, P, seq_len, caches[i % 2], out=y)
+        else:
+            layer.decode_step(xd, seq_off, seq_len, caches[i % 2], out=y)
 
     for i in range(args.warmup):
         step(i)
@@ -393,11 +416,12 @@ def main():
     gbs = cache_bytes / t_step / 1e9
     core_gbs = cache_bytes / (core_ms * 1e-3) / 1e9
     fp8 = wl.kv == "fp8"
-    traffic = None if fp8 else traffic_from_profile(cache_bytes)
+    traffic = None if (fp8 or P) else traffic_from_profile(cache_bytes)
 
     res = {
         "metric": "MLA decode latent-KV GB/s + tokens/s (V2-Lite shapes, B=64), % of HBM peak"
-                  + (", FP8 latent cache" if fp8 else ""),
+                  + (", FP8 latent cache" if fp8 else "")
+                  + (f", paged cache ({P}-row pages)" if P else ""),
         "value": round(gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -415,6 +439,7 @@ def main():
         "timing": "eager" if graph is None else "hip-graph replay of the K steps",
         "config": {"workload": wl.name, "batch": B, "len_lo": wl.len_lo, "len_hi": wl.len_hi,
                    "latent_rows": int(seq_len.sum()), "cache_row_bytes": row_bytes,
+                   "page_rows": P,
                    "cache_bytes": int(cache_bytes),
                    "weight_bytes": int(weight_bytes), "hidden": d.hidden, "heads": d.n_heads,
                    "kv_lora": d.kv_lora, "qk_rope": d.qk_rope},

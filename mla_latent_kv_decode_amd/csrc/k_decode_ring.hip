@@ -128,6 +128,7 @@ decode_core_ring_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
     if (iw.next >= 0) inx = load_work(works + iw.next);
     int ik = 0, intl = 1 + (iw.n + TR - 1) / TR;  // next tile of segment iw, its tile count
     int issued = 0;
+    int64_t next_row = 0;
     // issue the next tile of the part's stream (query tile, then row tiles,
     // segment after segment) into stage issued % NST
     auto issue_next = [&]() {
@@ -144,9 +145,12 @@ decode_core_ring_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
         issue_tile(qb, 15, stage, p, lane);
       } else {
         const int t = ik - 1;
-        const char* rb = reinterpret_cast<const char*>(cache + seg_row(mt, iw.row, t * TR) * RW);
+        const char* rb = reinterpret_cast<const char*>(cache + next_row * RW);
         issue_tile(rb, iw.n - t * TR - 1, stage, p, lane);
       }
+      // the cache row of the segment's next tile, one issue ahead (a paged
+      // cache's page lookup is a load)
+      if (ik + 1 < intl) next_row = seg_row(mt, iw.row, ik * TR);
       ++ik;
       ++issued;
     };

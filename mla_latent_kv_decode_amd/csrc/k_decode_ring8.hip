@@ -213,6 +213,7 @@ decode_core_ring8_k(const bf16* __restrict__ q_cat, const uint8_t* __restrict__ 
     if (iw.next >= 0) inx = load_work(works + iw.next);
     int ik = 0, intl = 1 + (iw.n + TR - 1) / TR;  // next position of segment iw, its count
     int issued = 0;
+    int64_t next_row = 0;
     auto issue_next = [&]() {
       if (ik == intl) {
         if (iw.next < 0) return;
@@ -227,9 +228,12 @@ decode_core_ring8_k(const bf16* __restrict__ q_cat, const uint8_t* __restrict__ 
                     stage, p, lane);
       } else {
         const int t = ik - 1;
-        issue_rows(reinterpret_cast<const char*>(cache) + seg_row(mt, iw.row, t * TR) * RB,
-                   iw.n - t * TR - 1, stage, p, lane);
+        issue_rows(reinterpret_cast<const char*>(cache) + next_row * RB, iw.n - t * TR - 1, stage,
+                   p, lane);
       }
+      // the cache row of the segment's next tile, one issue ahead (a paged
+      // cache's page lookup is a load)
+      if (ik + 1 < intl) next_row = seg_row(mt, iw.row, ik * TR);
       ++ik;
       ++issued;
     };

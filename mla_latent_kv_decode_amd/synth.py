@@ -70,6 +70,7 @@ class Workload:
     prior: tuple = field(default_factory=tuple)  # prefill: cached rows before
     fixed_lengths: tuple = field(default_factory=tuple)
     kv: str = "dtype"          # latent cache rows: "dtype" or "fp8" (E4M3 + row scale)
+    page_rows: int = 0         # > 0: a paged cache, pages handed out in a seeded random order
 
 
 WORKLOADS = {
@@ -85,6 +86,9 @@ WORKLOADS = {
     # the same batch on an FP8 latent cache (656-byte rows)
     "v2lite_decode_b64_fp8": Workload("v2lite_decode_b64_fp8", V2_LITE, "bf16", 0.02,
                                       "decode", 64, len_lo=512, len_hi=8192, kv="fp8"),
+    # the same batch on a paged cache: 64-row pages in a seeded random order
+    "v2lite_decode_b64_paged": Workload("v2lite_decode_b64_paged", V2_LITE, "bf16", 0.02,
+                                        "decode", 64, len_lo=512, len_hi=8192, page_rows=64),
     # V3 ragged decode, B=32, cached rows ~ U{2048..16384}
     "v3_decode_b32": Workload("v3_decode_b32", V3, "bf16", 0.02, "decode", 32,
                               len_lo=2048, len_hi=16384),
@@ -161,6 +165,21 @@ def lengths(w: Workload, seed: int = LENGTH_SEED) -> np.ndarray:
         return np.asarray(w.fixed_lengths, dtype=np.int64)
     rng = np.random.default_rng(seed)
     return rng.integers(w.len_lo, w.len_hi + 1, w.batch).astype(np.int64)
+
+
+def page_table(seq_len, page_rows: int, seed: int = 1237):
+    """Block table of a paged cache: every sequence's ceil(len / P) pages
+    drawn without replacement from a pool of exactly that many pages, in a
+    seeded random order.  Returns (table (B, max_pages) int32, n_pages)."""
+    need = (np.asarray(seq_len, dtype=np.int64) + page_rows - 1) // page_rows
+    n_pages = int(need.sum())
+    perm = np.random.default_rng(seed).permutation(n_pages).astype(np.int32)
+    table = np.zeros((len(need), int(need.max())), dtype=np.int32)
+    k = 0
+    for b, m in enumerate(need):
+        table[b, :m] = perm[k:k + m]
+        k += m
+    return table, n_pages
 
 
 def decode_layout(lens: np.ndarray):
