@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 3
+#define MLA_ABI_VERSION 4
 
 typedef enum mla_status {
   MLA_OK = 0,
@@ -253,6 +253,50 @@ int mla_decode_step_paged(mla_handle h, const void* hidden, const int32_t* pos,
                           const int32_t* block_table, int32_t max_pages, int32_t page_rows,
                           const int32_t* seq_len, int32_t B, void* cache, int64_t cache_rows,
                           void* out, void* ws, size_t ws_bytes);
+
+/* General decode call: q_len new tokens per sequence (multi-token decode: the
+ * offset causal mask of "Transformer and KV Cache Basics", KV Cache section --
+ * new token j of sequence b sits at position seq_len[b] - q_len + j and
+ * attends to positions 0 .. that position; the MLA post's section 3.2 code
+ * writes the new tokens' rows before reading), over a contiguous or a paged
+ * cache, with or without the append of the new rows.  q_len = 1 is
+ * mla_decode / mla_decode_step (or their paged forms), bit for bit. */
+#define MLA_MAX_Q_LEN 16
+typedef struct mla_decode_args {
+  const void* hidden;         /* device (B * q_len, D): row b * q_len + j is token j of b */
+  void* out;                  /* device (B * q_len, D), same order */
+  int32_t B;                  /* sequences, >= 1 */
+  int32_t q_len;              /* new tokens per sequence, 1 .. MLA_MAX_Q_LEN */
+  const int32_t* seq_len;     /* HOST (B): rows of sequence b including its q_len new ones;
+                                 >= q_len */
+  const int64_t* seq_off;     /* HOST (B): contiguous cache, rows [seq_off[b], + seq_len[b]);
+                                 NULL for a paged cache */
+  const int32_t* block_table; /* HOST (B, max_pages): paged cache as for mla_decode_paged;
+                                 NULL for a contiguous cache */
+  int32_t max_pages;
+  int32_t page_rows;
+  void* cache;                /* device, cache_rows rows in the cache's row format */
+  int64_t cache_rows;
+  int32_t append;             /* 1: write the q_len new rows of every sequence from hidden
+                                 first (as mla_append_latent would), then decode */
+  void* ws;                   /* workspace of mla_decode_ex_workspace_bytes bytes */
+  size_t ws_bytes;
+} mla_decode_args;
+
+/* Host-only checks of mla_decode_ex.  Errors: NULL args/seq_len, B < 1, q_len
+ * outside 1 .. MLA_MAX_Q_LEN, seq_len[b] < q_len, both or neither of seq_off
+ * and block_table -> INVALID_ARG; a contiguous sequence outside
+ * [0, cache_rows) -> CAPACITY; paged: the errors of mla_decode_paged (with
+ * append, all B * q_len new rows must land on distinct cache rows). */
+int mla_decode_ex_check(const mla_config* cfg, const mla_decode_args* a);
+/* Workspace bytes for B sequences of total_rows rows in all (sum of seq_len),
+ * q_len new tokens each, with (append = 1) or without the append. */
+size_t mla_decode_ex_workspace_bytes(mla_handle h, int32_t B, int32_t q_len, int64_t total_rows,
+                                     int32_t append);
+/* Runs the decode described by a (A2 if append, then A3..A8 for all B * q_len
+ * query rows).  Errors: those of mla_decode_ex_check, weights not absorbed ->
+ * STATE, workspace too small -> WORKSPACE. */
+int mla_decode_ex(mla_handle h, const mla_decode_args* a);
 
 /* Where the staged intermediates of the last mla_decode with these (B,
  * total_rows) live inside its workspace, as byte offsets from ws:

@@ -60,5 +60,12 @@ __device__ __forceinline__ int64_t seg_row(const DecodeMeta& mt, int64_t wrow, i
   return ((int64_t)page << mt.page_shift) + (t & ((1 << mt.page_shift) - 1));
 }
 
+// Rows of a work record's segment that token j (of q_len) sees: all of them,
+// except on the sequence's last segment, where the tokens after j are not
+// visible to it.
+__device__ __forceinline__ int token_rows(const DecodeWork& w, int q_len, int j) {
+  return w.pidx == w.pstart + w.nseg - 1 ? w.n - (q_len - 1 - j) : w.n;
+}
+
 }  // namespace ddev
 }  // namespace mla

@@ -106,14 +106,15 @@ __device__ __forceinline__ bf16x8_t cat_bf16(s16x4_t lo, s16x4_t hi) {
 __global__ void __launch_bounds__(NTHR, 1)
 decode_core_ring_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cache, DecodeMeta mt,
                    float* __restrict__ acc, float* __restrict__ ml, bf16* __restrict__ o_lat,
-                   int H, int nparts) {
+                   int H, int nparts, int q_len, int nseg_total) {
   __shared__ __attribute__((aligned(1024))) char lds[NST * ST_BYTES];
-  // block -> (part, head group); the groups of a part are numbered part % 8
-  // modulo 8, so they share an XCD (blocks go to XCDs round robin)
+  // block -> (part, token, head group); the groups of a part are numbered
+  // part % 8 modulo 8, so they share an XCD (blocks go to XCDs round robin)
   const int HG = H / 16;
   const int bid = blockIdx.x;
-  const int part = (bid / (kXcds * HG)) * kXcds + bid % kXcds;
-  const int hg = (bid / kXcds) % HG;
+  const int part = (bid / (kXcds * HG * q_len)) * kXcds + bid % kXcds;
+  const int hgq = (bid / kXcds) % (HG * q_len);
+  const int tok = hgq / HG, hg = hgq % HG;
   if (part >= nparts) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -141,7 +142,8 @@ decode_core_ring_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
       }
       const uint32_t stage = lds0 + (uint32_t)(issued % NST) * ST_BYTES;
       if (ik == 0) {
-        const char* qb = reinterpret_cast<const char*>(q_cat + ((int64_t)iw.b * H + hg * 16) * RW);
+        const char* qb = reinterpret_cast<const char*>(
+            q_cat + ((int64_t)(iw.b * q_len + tok) * H + hg * 16) * RW);
         issue_tile(qb, 15, stage, p, lane);
       } else {
         const int t = ik - 1;
@@ -203,8 +205,8 @@ decode_core_ring_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
     bf16x8_t qf[18];
     float m_run, l_run;
     f32x4_t o[NCB];
-    const int n = wk.n;
-    const int ntile = (n + TR - 1) / TR;
+    const int ntile = (wk.n + TR - 1) / TR;  // the producers' count
+    const int n = token_rows(wk, q_len, tok);  // rows this token sees
     {
       // the segment's query tile: Q^T fragments of head gh, columns 32 s + 8 lg .. + 7
       __syncthreads();
@@ -301,7 +303,7 @@ decode_core_ring_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
     const int b = wk.b;
     if (wk.nseg == 1) {
       const float inv = 1.f / l;
-      bf16* dst = o_lat + ((int64_t)b * H + gh) * DC + 128 * cq + 4 * lg;
+      bf16* dst = o_lat + ((int64_t)(b * q_len + tok) * H + gh) * DC + 128 * cq + 4 * lg;
 #pragma unroll
       for (int j = 0; j < NCB; ++j) {
         uint2 pk;
@@ -312,12 +314,13 @@ decode_core_ring_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
     } else {
       // partial of this segment: unnormalised sums (this wave's quarter) and,
       // from the first wave, the (max, sum) pair of each head
-      float* pacc = acc + ((int64_t)wk.pidx * H + gh) * DC + 128 * cq + 4 * lg;
+      const int64_t slot = (int64_t)tok * nseg_total + wk.pidx;
+      float* pacc = acc + (slot * H + gh) * DC + 128 * cq + 4 * lg;
 #pragma unroll
       for (int j = 0; j < NCB; ++j)
         *reinterpret_cast<float4*>(pacc + 16 * j) = make_float4(o[j][0], o[j][1], o[j][2], o[j][3]);
       if (cq == 0 && lg == 0)
-        *reinterpret_cast<float2*>(ml + ((int64_t)wk.pidx * H + gh) * 2) = make_float2(m_run, l);
+        *reinterpret_cast<float2*>(ml + (slot * H + gh) * 2) = make_float2(m_run, l);
     }
     if (wk.next < 0) break;
     wk = nx;
@@ -328,11 +331,12 @@ decode_core_ring_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
 }  // namespace decr
 
 void decode_core_ring(const bf16* q_cat, const bf16* cache, const DecodeMeta& m, int parts,
-                      float* acc, float* ml, bf16* o_lat, const Dims& d, hipStream_t st) {
-  const int hg = d.H / 16;
+                      const TokenSplit& tk, float* acc, float* ml, bf16* o_lat, const Dims& d,
+                      hipStream_t st) {
+  const int hg = d.H / 16 * tk.q_len;
   const int blocks = (parts + decr::kXcds - 1) / decr::kXcds * decr::kXcds * hg;
   decr::decode_core_ring_k<<<blocks, decr::NTHR, 0, st>>>(q_cat, cache, m, acc, ml, o_lat, d.H,
-                                                          parts);
+                                                          parts, tk.q_len, tk.nseg_total);
 }
 
 }  // namespace mla

@@ -193,12 +193,13 @@ __device__ __forceinline__ bf16x8_t codes_to_bf16(i32x2_t v) {
 __global__ void __launch_bounds__(NTHR, 1)
 decode_core_ring8_k(const bf16* __restrict__ q_cat, const uint8_t* __restrict__ cache,
                     DecodeMeta mt, float* __restrict__ acc, float* __restrict__ ml,
-                    bf16* __restrict__ o_lat, int H, int nparts) {
+                    bf16* __restrict__ o_lat, int H, int nparts, int q_len, int nseg_total) {
   __shared__ __attribute__((aligned(1024))) char lds[PS_OFF + PS_BYTES];
   const int HG = H / 16;
   const int bid = blockIdx.x;
-  const int part = (bid / (kXcds * HG)) * kXcds + bid % kXcds;
-  const int hg = (bid / kXcds) % HG;
+  const int part = (bid / (kXcds * HG * q_len)) * kXcds + bid % kXcds;
+  const int hgq = (bid / kXcds) % (HG * q_len);
+  const int tok = hgq / HG, hg = hgq % HG;  // new token and 16-head group
   if (part >= nparts) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -224,7 +225,8 @@ decode_core_ring8_k(const bf16* __restrict__ q_cat, const uint8_t* __restrict__ 
       }
       const uint32_t stage = lds0 + (uint32_t)(issued % NST) * ST_BYTES;
       if (ik == 0) {
-        issue_query(reinterpret_cast<const char*>(q_cat + ((int64_t)iw.b * H + hg * 16) * QRW),
+        issue_query(reinterpret_cast<const char*>(
+                        q_cat + ((int64_t)(iw.b * q_len + tok) * H + hg * 16) * QRW),
                     stage, p, lane);
       } else {
         const int t = ik - 1;
@@ -406,7 +408,7 @@ decode_core_ring8_k(const bf16* __restrict__ q_cat, const uint8_t* __restrict__ 
     l += __shfl_xor(l, 32, 64);
     if (w.nseg == 1) {
       const float inv = 1.f / l;
-      bf16* dst = o_lat + ((int64_t)w.b * H + gh) * DC + 128 * cq + 4 * lg;
+      bf16* dst = o_lat + ((int64_t)(w.b * q_len + tok) * H + gh) * DC + 128 * cq + 4 * lg;
 #pragma unroll
       for (int j = 0; j < NCB; ++j) {
         uint2 pk;
@@ -415,12 +417,13 @@ decode_core_ring8_k(const bf16* __restrict__ q_cat, const uint8_t* __restrict__ 
         *reinterpret_cast<uint2*>(dst + 16 * j) = pk;
       }
     } else {
-      float* pacc = acc + ((int64_t)w.pidx * H + gh) * DC + 128 * cq + 4 * lg;
+      const int64_t slot = (int64_t)tok * nseg_total + w.pidx;
+      float* pacc = acc + (slot * H + gh) * DC + 128 * cq + 4 * lg;
 #pragma unroll
       for (int j = 0; j < NCB; ++j)
         *reinterpret_cast<float4*>(pacc + 16 * j) = make_float4(o[j][0], o[j][1], o[j][2], o[j][3]);
       if (cq == 0 && lg == 0)
-        *reinterpret_cast<float2*>(ml + ((int64_t)w.pidx * H + gh) * 2) = make_float2(m_run, l);
+        *reinterpret_cast<float2*>(ml + (slot * H + gh) * 2) = make_float2(m_run, l);
     }
   };
 
@@ -431,14 +434,14 @@ decode_core_ring8_k(const bf16* __restrict__ q_cat, const uint8_t* __restrict__ 
 #pragma unroll 1
   for (;;) {
     bf16x8_t ql[8], qr;
-    const int n = wk.n;
-    const int ntile = (n + TR - 1) / TR;
+    const int ntile = (wk.n + TR - 1) / TR;  // the producers' count
+    const int n = token_rows(wk, q_len, tok);  // rows this token sees
     {
       __syncthreads();  // the query tile is in LDS; the partials of gt - 1 are visible
       const char* st = lds + (gt % NST) * ST_BYTES;
       if (pending) {
         finish_alone(lds + ((gt - 1) % NST) * ST_BYTES, (gt - 1) & 1, (done.n - 1) / TR * TR,
-                     done.n);
+                     token_rows(done, q_len, tok));
         store(done);
       }
       // Q^T fragments of head gh, columns 32 s + 8 lg .. + 7 for s = 8 hq + j
@@ -472,7 +475,7 @@ decode_core_ring8_k(const bf16* __restrict__ q_cat, const uint8_t* __restrict__ 
       fin_load(lds + ((gt - 1) % NST) * ST_BYTES, (gt - 1) & 1, fin);
       __builtin_amdgcn_sched_barrier(0);  // keep every read of the position ahead of the math
       partial(pin, gt & 1, ql, qr);
-      finish(fin, (k - 1) * TR, n, false);
+      finish(fin, (k - 1) * TR, n, k * TR > n);  // a tile past the token's last row masks
     }
     pending = true;
     done = wk;
@@ -481,18 +484,20 @@ decode_core_ring8_k(const bf16* __restrict__ q_cat, const uint8_t* __restrict__ 
     if (wk.next >= 0) nx = load_work(works + wk.next);
   }
   __syncthreads();  // the partials of the last tile are visible
-  finish_alone(lds + ((gt - 1) % NST) * ST_BYTES, (gt - 1) & 1, (done.n - 1) / TR * TR, done.n);
+  finish_alone(lds + ((gt - 1) % NST) * ST_BYTES, (gt - 1) & 1, (done.n - 1) / TR * TR,
+               token_rows(done, q_len, tok));
   store(done);
 }
 
 }  // namespace decr8
 
 void decode_core_ring8(const bf16* q_cat, const uint8_t* cache, const DecodeMeta& m, int parts,
-                       float* acc, float* ml, bf16* o_lat, const Dims& d, hipStream_t st) {
-  const int hg = d.H / 16;
+                       const TokenSplit& tk, float* acc, float* ml, bf16* o_lat, const Dims& d,
+                       hipStream_t st) {
+  const int hg = d.H / 16 * tk.q_len;
   const int blocks = (parts + decr8::kXcds - 1) / decr8::kXcds * decr8::kXcds * hg;
   decr8::decode_core_ring8_k<<<blocks, decr8::NTHR, 0, st>>>(q_cat, cache, m, acc, ml, o_lat,
-                                                             d.H, parts);
+                                                             d.H, parts, tk.q_len, tk.nseg_total);
 }
 
 }  // namespace mla

@@ -91,13 +91,15 @@ __device__ __forceinline__ void issue_tile(const char* base, int last, uint32_t 
 
 __global__ void __launch_bounds__(512, 1)
 decode_core_wide_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cache, DecodeMeta mt,
-                   float* __restrict__ acc_out, float* __restrict__ ml_out, int H, int nparts) {
+                   float* __restrict__ acc_out, float* __restrict__ ml_out, int H, int nparts,
+                   int q_len, int nseg_total) {
   __shared__ __attribute__((aligned(1024))) char lds[NST * ST_BYTES];
-  // block -> (part, 128-head block), the head blocks of a part on one XCD
+  // block -> (part, token, 128-head block), the blocks of a part on one XCD
   const int WG = H / HEADS;
   const int bid = blockIdx.x;
-  const int part = (bid / (kXcds * WG)) * kXcds + bid % kXcds;
-  const int hb = (bid / kXcds) % WG;
+  const int part = (bid / (kXcds * WG * q_len)) * kXcds + bid % kXcds;
+  const int hbq = (bid / kXcds) % (WG * q_len);
+  const int tok = hbq / WG, hb = hbq % WG;
   if (part >= nparts) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -131,7 +133,8 @@ decode_core_wide_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
   const ConstWorkPtr works = reinterpret_cast<ConstWorkPtr>((uintptr_t)mt.work);
   DecodeWork wk = load_work(works + part);
   for (;;) {
-    const int n = wk.n;
+    const int n = wk.n;                         // rows streamed
+    const int nv = token_rows(wk, q_len, tok);  // rows this token sees
     const int ntile = (n + TR - 1) / TR;
     const int64_t wrow = wk.row;
 #pragma unroll
@@ -146,7 +149,8 @@ decode_core_wide_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
     bf16x8_t qf[G][18];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const bf16* qrow = q_cat + ((int64_t)wk.b * H + h0 + 16 * g + lr) * RW + lg * 8;
+      const bf16* qrow =
+          q_cat + ((int64_t)(wk.b * q_len + tok) * H + h0 + 16 * g + lr) * RW + lg * 8;
 #pragma unroll
       for (int s = 0; s < 18; ++s) qf[g][s] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * s);
     }
@@ -225,7 +229,7 @@ decode_core_wide_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const bool valid = row0 + 16 * rb + 4 * lg + i < n;
+            const bool valid = row0 + 16 * rb + 4 * lg + i < nv;
             sv[4 * rb + i] = valid ? sc[rb][g][i] * kLog2e : -INFINITY;
             grow |= sv[4 * rb + i] > m_run[g] + kRescale;
           }
@@ -286,14 +290,15 @@ decode_core_wide_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
       l += __shfl_xor(l, 16, 64);
       l += __shfl_xor(l, 32, 64);
       const int gh = h0 + 16 * g + lr;
-      float* pacc = acc_out + ((int64_t)wk.pidx * H + gh) * DC + 4 * lg;
+      const int64_t slot = (int64_t)tok * nseg_total + wk.pidx;
+      float* pacc = acc_out + (slot * H + gh) * DC + 4 * lg;
 #pragma unroll
       for (int cb = 0; cb < 32; ++cb)
         *reinterpret_cast<float4*>(pacc + 16 * cb) =
             make_float4(o[g][cb][0], o[g][cb][1], o[g][cb][2], o[g][cb][3]);
       if (lg == 0) {
-        ml_out[((int64_t)wk.pidx * H + gh) * 2] = m_run[g];
-        ml_out[((int64_t)wk.pidx * H + gh) * 2 + 1] = l;
+        ml_out[(slot * H + gh) * 2] = m_run[g];
+        ml_out[(slot * H + gh) * 2 + 1] = l;
       }
     }
     __syncthreads();  // the stages are refilled by the next segment
@@ -307,10 +312,12 @@ decode_core_wide_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
 int decode_core_wide_heads() { return decw::HEADS; }
 
 void decode_core_wide(const bf16* q_cat, const bf16* cache, const DecodeMeta& m, int parts,
-                      float* acc, float* ml, const Dims& d, hipStream_t st) {
-  const int wg = d.H / decw::HEADS;
+                      const TokenSplit& tk, float* acc, float* ml, const Dims& d,
+                      hipStream_t st) {
+  const int wg = d.H / decw::HEADS * tk.q_len;
   const int blocks = (parts + decw::kXcds - 1) / decw::kXcds * decw::kXcds * wg;
-  decw::decode_core_wide_k<<<blocks, 64 * decw::NW, 0, st>>>(q_cat, cache, m, acc, ml, d.H, parts);
+  decw::decode_core_wide_k<<<blocks, 64 * decw::NW, 0, st>>>(q_cat, cache, m, acc, ml, d.H, parts,
+                                                             tk.q_len, tk.nseg_total);
 }
 
 }  // namespace mla

@@ -290,18 +290,20 @@ void cache_write(const T* rows, const int64_t* slot, int ntok, int R, T* cache, 
 template <typename T>
 __global__ void __launch_bounds__(256)
 decode_core_generic_k(const T* __restrict__ q_cat, const T* __restrict__ cache, DecodeMeta mt,
-                      float* __restrict__ acc_out, float* __restrict__ ml_out, Dims d) {
+                      float* __restrict__ acc_out, float* __restrict__ ml_out, Dims d, int q_len,
+                      int nseg_total) {
   extern __shared__ float sm[];
   float* q = sm;              // R
   float* p = q + d.R;         // 256
   float* red = p + 256;       // 4
   const DecodeSeg sg = mt.segs[blockIdx.x];
-  const int h = blockIdx.y;
+  const int h = blockIdx.y % d.H, tok = blockIdx.y / d.H;  // head, new token
   const int R = d.R;
   for (int j = threadIdx.x; j < R; j += blockDim.x)
-    q[j] = ldf(q_cat + ((int64_t)sg.b * d.H + h) * R + j);
+    q[j] = ldf(q_cat + ((int64_t)(sg.b * q_len + tok) * d.H + h) * R + j);
   __syncthreads();
-  const int n = sg.r1 - sg.r0;
+  // rows token tok sees: on the sequence's last segment, not the later tokens'
+  const int n = sg.r1 - sg.r0 - (sg.r1 == mt.seq_len[sg.b] ? q_len - 1 - tok : 0);
   // cache row of the segment's position t (contiguous, or through the page list)
   auto row_of = [&](int t) -> const T* {
     int64_t r;
@@ -349,23 +351,25 @@ decode_core_generic_k(const T* __restrict__ q_cat, const T* __restrict__ cache, 
     }
     __syncthreads();
   }
-  float* ao = acc_out + ((int64_t)sg.pidx * d.H + h) * d.dc;
+  const int64_t slot = (int64_t)tok * nseg_total + sg.pidx;
+  float* ao = acc_out + (slot * d.H + h) * d.dc;
   for (int c4 = 0; c4 < 4; ++c4) {
     const int c = threadIdx.x + c4 * 256;
     if (c < d.dc) ao[c] = acc[c4];
   }
   if (threadIdx.x == 0) {
-    ml_out[((int64_t)sg.pidx * d.H + h) * 2] = m;
-    ml_out[((int64_t)sg.pidx * d.H + h) * 2 + 1] = l;
+    ml_out[(slot * d.H + h) * 2] = m;
+    ml_out[(slot * d.H + h) * 2 + 1] = l;
   }
 }
 
 template <typename T>
 void decode_core_generic(const T* q_cat, const T* cache, const DecodeMeta& m, int nseg_total,
-                         float* acc, float* ml, const Dims& d, hipStream_t st) {
-  dim3 grid(nseg_total, d.H);
+                         int q_len, float* acc, float* ml, const Dims& d, hipStream_t st) {
+  dim3 grid(nseg_total, d.H * q_len);
   const size_t smem = (size_t)(d.R + 256 + 4) * sizeof(float);
-  decode_core_generic_k<T><<<grid, 256, smem, st>>>(q_cat, cache, m, acc, ml, d);
+  decode_core_generic_k<T><<<grid, 256, smem, st>>>(q_cat, cache, m, acc, ml, d, q_len,
+                                                    nseg_total);
 }
 
 // Split combine: o_lat[b][h] = sum_j e^(m_j - M) acc_j / sum_j e^(m_j - M) l_j,
@@ -490,8 +494,8 @@ void prefill_attn_generic(const T* q_nope, const T* q_rope, const float* kv, con
                                const RopeTab&, hipStream_t, bool);                           \
   template void cache_write<T>(const T*, const int64_t*, int, int, T*, hipStream_t);         \
   template void transpose_heads<T>(const T*, T*, int, int, int, int64_t, hipStream_t);        \
-  template void decode_core_generic<T>(const T*, const T*, const DecodeMeta&, int, float*,   \
-                                       float*, const Dims&, hipStream_t);                    \
+  template void decode_core_generic<T>(const T*, const T*, const DecodeMeta&, int, int,      \
+                                       float*, float*, const Dims&, hipStream_t);            \
   template void decode_combine<T>(const float*, const float*, const DecodeMeta&, int, T*,    \
                                   const Dims&, hipStream_t);                                 \
   template void prefill_attn_generic<T>(const T*, const T*, const float*, const T*,          \

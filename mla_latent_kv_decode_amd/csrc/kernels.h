@@ -165,16 +165,24 @@ void decode_finish(const bf16* q_nope, const bf16* w_ukT, bf16* q_cat, int B, bo
                    hipStream_t st, bool kv8 = false);  // kv8: `cache` holds FP8 rows
 
 // ---- decode core (split-S) and combine
-// partial layout: acc[pidx][h][dc] fp32, ml[pidx][h][2] = (max in log2 units, sum)
+// q_len new tokens per sequence: query row b * q_len + j (q_cat, o_lat) is
+// token j of sequence b, at position seq_len[b] - q_len + j; on the
+// sequence's last segment it sees q_len - 1 - j rows fewer.  Partial layout:
+// acc[j * nseg_total + pidx][h][dc] fp32, ml[...][h][2] = (max in log2 units,
+// sum).
+struct TokenSplit {
+  int q_len, nseg_total;
+};
 template <typename T>
 void decode_core_generic(const T* q_cat, const T* cache, const DecodeMeta& m, int nseg_total,
-                         float* acc, float* ml, const Dims& d, hipStream_t st);
+                         int q_len, float* acc, float* ml, const Dims& d, hipStream_t st);
 // MFMA core for head counts that are a multiple of decode_core_wide_heads()
 // (128): each workgroup covers that many heads of a part over shared row
 // tiles; the H / 128 workgroups of a part run on one XCD.
 int decode_core_wide_heads();
 void decode_core_wide(const bf16* q_cat, const bf16* cache, const DecodeMeta& m, int parts,
-                      float* acc, float* ml, const Dims& d, hipStream_t st);
+                      const TokenSplit& tk, float* acc, float* ml, const Dims& d,
+                      hipStream_t st);
 // FP8 latent cache (rows of fp8_row_bytes(dc, dr) bytes, dc == 512, dr == 64):
 // the latent row append (as append_rows, into FP8 rows), the store of rows
 // given in bf16 (T x R) into FP8 rows, a raw row-byte scatter, and the ring
@@ -187,14 +195,16 @@ void cache_store_fp8(const bf16* rows, const int64_t* slot, int ntok, uint8_t* c
 void cache_write_bytes(const uint8_t* rows, const int64_t* slot, int ntok, int row_bytes,
                        uint8_t* cache, hipStream_t st);
 void decode_core_ring8(const bf16* q_cat, const uint8_t* cache, const DecodeMeta& m, int parts,
-                       float* acc, float* ml, bf16* o_lat, const Dims& d, hipStream_t st);
+                       const TokenSplit& tk, float* acc, float* ml, bf16* o_lat, const Dims& d,
+                       hipStream_t st);
 // MFMA core over a ring of shared row tiles (bf16, dc == 512, dr == 64,
-// H % 16 == 0): one workgroup per (part, 16-head group), parts = persistent
-// workgroups per head group.  Partials as for the generic core, except that a
-// sequence contained in one segment is normalised and written to o_lat
-// (B, H, 512) directly.
+// H % 16 == 0): one workgroup per (part, token, 16-head group), parts =
+// persistent workgroups per (token, head group).  Partials as for the generic
+// core, except that a sequence contained in one segment is normalised and
+// written to o_lat (B * q_len, H, 512) directly.
 void decode_core_ring(const bf16* q_cat, const bf16* cache, const DecodeMeta& m, int parts,
-                      float* acc, float* ml, bf16* o_lat, const Dims& d, hipStream_t st);
+                      const TokenSplit& tk, float* acc, float* ml, bf16* o_lat, const Dims& d,
+                      hipStream_t st);
 // combine for dc == 512, bf16 output.  max_chunks = max over sequences of
 // ceil(nseg / kCombineChunk); cacc (chunk slots x H x 512) and cml (chunk slots
 // x H x 2) hold the chunk partials of sequences with more than one chunk.

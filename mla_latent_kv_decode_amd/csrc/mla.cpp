@@ -322,15 +322,16 @@ bool ring_core(const mla_ctx* h) { return h->mfma && !wide_core(h); }
 // the split combine fused with the value un-absorb (MFMA layers with dv = 128)
 bool combine_uv(const mla_ctx* h) { return h->mfma && h->d.dv == 128; }
 
-int max_parts(const mla_ctx* h, int64_t total_rows) {
+int max_parts(const mla_ctx* h, int64_t total_rows, int q_len = 1) {
   int64_t p = (total_rows + 63) / 64;
   // the MFMA cores run one workgroup per compute unit: per 16-head group (or
-  // per 128 heads for the many-head core) of a part
+  // per 128 heads for the many-head core) and new token of a part
   const int64_t wgs = !h->mfma ? h->n_cu
                       : wide_core(h)
                           ? std::max<int64_t>(1, (int64_t)h->n_cu /
-                                                     (h->d.H / mla::decode_core_wide_heads()))
-                          : std::max<int64_t>(1, (int64_t)h->n_cu / (h->d.H / 16));
+                                                     (h->d.H / mla::decode_core_wide_heads() *
+                                                      q_len))
+                          : std::max<int64_t>(1, (int64_t)h->n_cu / (h->d.H / 16 * q_len));
   if (p > wgs) p = wgs;
   if (p < 1) p = 1;
   return (int)p;
@@ -342,24 +343,33 @@ size_t page_list_bytes(int B, int64_t total_rows) {
   return align_up((size_t)B * 4) + align_up((size_t)(total_rows / 32 + B) * 4);
 }
 
-size_t meta_bytes(int B, int parts, int max_segs, int64_t total_rows) {
-  return 2 * align_up((size_t)B * 8) + 5 * align_up((size_t)B * 4) +
-         align_up((size_t)(parts + 1) * 4) + align_up((size_t)max_segs * sizeof(DecodeSeg)) +
+// per sequence: seq_off, seq_len, pstart, nseg, cstart; per query row (B *
+// q_len): slot, pos and the combine's pstart, nseg, cstart
+size_t meta_bytes(int B, int parts, int max_segs, int64_t total_rows, int q_len = 1) {
+  const size_t Bq = (size_t)B * q_len;
+  return align_up((size_t)B * 8) + align_up(Bq * 8) + 4 * align_up((size_t)B * 4) +
+         4 * align_up(Bq * 4) + align_up((size_t)(parts + 1) * 4) +
+         align_up((size_t)max_segs * sizeof(DecodeSeg)) +
          align_up((size_t)max_segs * sizeof(mla::DecodeWork)) + page_list_bytes(B, total_rows);
 }
 
 int qw_of(const Dims& d) { return d.H * (d.dn + d.dr); }
 
-DecodeLayout decode_layout(const mla_ctx* h, int B, int64_t total_rows, bool step) {
+// B sequences with q_len new tokens each: the query path, the combine and the
+// output projections run over B * q_len rows; the core keeps one partial per
+// segment and token.
+DecodeLayout decode_layout(const mla_ctx* h, int Bs, int64_t total_rows, bool step,
+                           int q_len = 1) {
   const Dims& d = h->d;
   DecodeLayout L;
   L.step = step;
-  const int parts = max_parts(h, total_rows);
-  L.max_segs = parts + B;
+  const int parts = max_parts(h, total_rows, q_len);
+  L.max_segs = parts + Bs;
+  const int B = Bs * q_len;  // query rows
   // only sequences with more than kCombineChunk slots use chunk slots: there are
   // at most max_segs / (kCombineChunk + 1) of them, each with at most
-  // nseg / kCombineChunk + 1 chunks
-  L.max_cslots = 2 * (L.max_segs / mla::kCombineChunk) + 2;
+  // nseg / kCombineChunk + 1 chunks (per token)
+  L.max_cslots = (2 * (L.max_segs / mla::kCombineChunk) + 2) * q_len;
   const int qw = qw_of(d);
   const size_t scr = std::max({out_scratch(h, B, d.dc, d.dn, d.H),
                                out_scratch(h, B, d.dv, d.dc, d.H),
@@ -371,15 +381,15 @@ DecodeLayout decode_layout(const mla_ctx* h, int B, int64_t total_rows, bool ste
   if (d.dq) pq = part_floats(h, B, qw, d.dq);
   const size_t e = h->esz;
   Carve c;
-  L.meta = c.take(meta_bytes(B, parts, L.max_segs, total_rows));
+  L.meta = c.take(meta_bytes(Bs, parts, L.max_segs, total_rows, q_len));
   L.scratch = c.take(scr * 4);
   L.pin = c.take(pin * 4);
   L.pq = c.take(pq * 4);
   L.cq = c.take(d.dq ? (size_t)B * d.dq * e : 0);
   L.q_nope = c.take((size_t)B * d.H * d.dn * e);
   L.q_cat = c.take((size_t)B * d.H * d.R * e);
-  L.acc = c.take((size_t)L.max_segs * d.H * d.dc * 4);
-  L.ml = c.take((size_t)L.max_segs * d.H * 2 * 4);
+  L.acc = c.take((size_t)L.max_segs * q_len * d.H * d.dc * 4);
+  L.ml = c.take((size_t)L.max_segs * q_len * d.H * 2 * 4);
   L.cacc = c.take((size_t)L.max_cslots * d.H * d.dc * 4);
   L.cml = c.take((size_t)L.max_cslots * d.H * 2 * 4);
   L.o_lat = c.take((size_t)B * d.H * d.dc * e);
@@ -390,6 +400,7 @@ DecodeLayout decode_layout(const mla_ctx* h, int B, int64_t total_rows, bool ste
 
 struct MetaOffsets {
   size_t seq_off, seq_len, pos, pstart, nseg, cstart, part, segs, work, slot, pg_off, pages;
+  size_t vpstart, vnseg, vcstart;  // the combine's view: one virtual sequence per query row
 };
 
 // A paged cache view (NULL for a contiguous cache): block_table (B x max_pages,
@@ -421,7 +432,10 @@ struct SpanPlan {
 };
 
 // Greedy fill with per-part budget `budget`; returns the parts used.
-int fill_spans(int B, const int32_t* seq_len, int64_t budget, SpanPlan* plan) {
+// min_tail: the last segment of every sequence keeps at least this many rows
+// (its q_len new tokens mask their last rows there; no segment is left empty
+// for any of them).
+int fill_spans(int B, const int32_t* seq_len, int64_t budget, SpanPlan* plan, int min_tail = 1) {
   if (plan) {
     plan->segs.clear();
     plan->part_begin.assign(1, 0);
@@ -442,6 +456,10 @@ int fill_spans(int B, const int32_t* seq_len, int64_t budget, SpanPlan* plan) {
       int64_t take = rem;
       if (take > room) take = std::max<int64_t>(kCutAlign, room / kCutAlign * kCutAlign);
       if (take > rem) take = rem;
+      if (take < rem && rem - take < min_tail) {  // leave a long enough last segment
+        const int64_t t2 = (rem - min_tail) / kCutAlign * kCutAlign;
+        take = t2 >= kCutAlign ? t2 : rem;
+      }
       if (plan)
         plan->segs.push_back(
             DecodeSeg{b, in_b, (int32_t)(in_b + take), (int32_t)plan->segs.size()});
@@ -454,25 +472,28 @@ int fill_spans(int B, const int32_t* seq_len, int64_t budget, SpanPlan* plan) {
 }
 
 // Balanced plan over at most max_p parts; returns the parts used.
-int plan_spans(int B, const int32_t* seq_len, int max_p, SpanPlan* plan) {
+int plan_spans(int B, const int32_t* seq_len, int max_p, SpanPlan* plan, int min_tail = 1) {
   int64_t total = 0;
   for (int b = 0; b < B; ++b) total += seq_len[b];
   int64_t lo = (total + max_p - 1) / max_p, hi = lo + kSegRows * 2 + kCutAlign;
-  while (fill_spans(B, seq_len, hi, nullptr) > max_p) hi *= 2;
+  while (fill_spans(B, seq_len, hi, nullptr, min_tail) > max_p) hi *= 2;
   while (lo < hi) {  // smallest budget that fits
     const int64_t mid = lo + (hi - lo) / 2;
-    if (fill_spans(B, seq_len, mid, nullptr) <= max_p) hi = mid;
+    if (fill_spans(B, seq_len, mid, nullptr, min_tail) <= max_p) hi = mid;
     else lo = mid + 1;
   }
-  return fill_spans(B, seq_len, hi, plan);
+  return fill_spans(B, seq_len, hi, plan, min_tail);
 }
 
+// Query row b * q_len + j is token j of sequence b, at position
+// seq_len[b] - q_len + j.
 int build_decode_meta(const mla_ctx* h, int B, const int64_t* seq_off, const int32_t* seq_len,
-                      const int32_t* pos, int64_t total, bool with_slot, const PageArgs* pg,
+                      int q_len, int64_t total, bool with_slot, const PageArgs* pg,
                       std::vector<char>& blob, MetaOffsets* mo, int* nseg_total, int* max_chunks,
                       int* cslots) {
   SpanPlan plan;
-  const int parts = plan_spans(B, seq_len, max_parts(h, total), &plan);
+  const int parts = plan_spans(B, seq_len, max_parts(h, total, q_len), &plan, q_len);
+  const int Bq = B * q_len;
   std::vector<DecodeSeg>& segs = plan.segs;
   std::vector<int32_t>& part_begin = plan.part_begin;
   std::vector<int32_t> pstart(B, 0), nseg(B, 0);
@@ -492,14 +513,31 @@ int build_decode_meta(const mla_ctx* h, int B, const int64_t* seq_off, const int
       *cslots += nch;
     }
   }
+  // the combine's view: query row b * q_len + j is a sequence of its own whose
+  // partials are slots j * nseg_total + pstart[b] ..; chunk slots likewise
+  const int cs_real = *cslots;
+  const int nsegs = (int)segs.size();
+  std::vector<int32_t> vpstart(Bq), vnseg(Bq), vcstart(Bq), qpos(Bq);
+  for (int b = 0; b < B; ++b)
+    for (int j = 0; j < q_len; ++j) {
+      const int i = b * q_len + j;
+      vpstart[i] = j * nsegs + pstart[b];
+      vnseg[i] = nseg[b];
+      vcstart[i] = j * cs_real + cstart[b];
+      qpos[i] = seq_len[b] - q_len + j;
+    }
+  *cslots = cs_real * q_len;
   Carve c;
   mo->seq_off = c.take((size_t)B * 8);
-  mo->slot = c.take(with_slot ? (size_t)B * 8 : 0);
+  mo->slot = c.take(with_slot ? (size_t)Bq * 8 : 0);
   mo->seq_len = c.take((size_t)B * 4);
-  mo->pos = c.take((size_t)B * 4);
+  mo->pos = c.take((size_t)Bq * 4);
   mo->pstart = c.take((size_t)B * 4);
   mo->nseg = c.take((size_t)B * 4);
   mo->cstart = c.take((size_t)B * 4);
+  mo->vpstart = c.take((size_t)Bq * 4);
+  mo->vnseg = c.take((size_t)Bq * 4);
+  mo->vcstart = c.take((size_t)Bq * 4);
   mo->part = c.take((size_t)(parts + 1) * 4);
   mo->segs = c.take(segs.size() * sizeof(DecodeSeg));
   mo->work = c.take(segs.size() * sizeof(mla::DecodeWork));
@@ -528,11 +566,16 @@ int build_decode_meta(const mla_ctx* h, int B, const int64_t* seq_off, const int
   }
   if (with_slot) {
     int64_t* sl = reinterpret_cast<int64_t*>(blob.data() + mo->slot);
-    for (int i = 0; i < B; ++i)
-      sl[i] = pg ? paged_row(*pg, i, seq_len[i] - 1) : seq_off[i] + seq_len[i] - 1;
+    for (int i = 0; i < Bq; ++i) {
+      const int b = i / q_len;
+      sl[i] = pg ? paged_row(*pg, b, qpos[i]) : seq_off[b] + qpos[i];
+    }
   }
   memcpy(blob.data() + mo->seq_len, seq_len, (size_t)B * 4);
-  memcpy(blob.data() + mo->pos, pos, (size_t)B * 4);
+  memcpy(blob.data() + mo->pos, qpos.data(), (size_t)Bq * 4);
+  memcpy(blob.data() + mo->vpstart, vpstart.data(), (size_t)Bq * 4);
+  memcpy(blob.data() + mo->vnseg, vnseg.data(), (size_t)Bq * 4);
+  memcpy(blob.data() + mo->vcstart, vcstart.data(), (size_t)Bq * 4);
   memcpy(blob.data() + mo->pstart, pstart.data(), (size_t)B * 4);
   memcpy(blob.data() + mo->nseg, nseg.data(), (size_t)B * 4);
   memcpy(blob.data() + mo->cstart, cstart.data(), (size_t)B * 4);
@@ -681,18 +724,16 @@ int mla_decode_check(const mla_config* cfg, const int32_t* pos, const int64_t* s
   return MLA_OK;
 }
 
-int mla_decode_paged_check(const mla_config* cfg, const int32_t* pos, const int32_t* block_table,
-                           int32_t max_pages, int32_t page_rows, const int32_t* seq_len, int32_t B,
-                           int64_t cache_rows, int32_t writes) {
-  int rc = mla_config_check(cfg);
-  if (rc) return rc;
-  if (B <= 0 || !pos || !block_table || !seq_len || cache_rows <= 0 || max_pages <= 0)
-    return MLA_ERR_INVALID_ARG;
+// The block table of a paged decode: page size, table width, every used page
+// in range; with `writes`, the q_len new rows of every sequence land on
+// distinct cache rows.
+static int paged_table_check(const int32_t* block_table, int32_t max_pages, int32_t page_rows,
+                             const int32_t* seq_len, int32_t B, int64_t cache_rows, int q_len,
+                             int32_t writes) {
+  if (!block_table || max_pages <= 0) return MLA_ERR_INVALID_ARG;
   if (page_rows < 32 || page_rows > (1 << 30) || (page_rows & (page_rows - 1)))
     return MLA_ERR_INVALID_ARG;
   const int64_t n_pages = cache_rows / page_rows;
-  for (int32_t b = 0; b < B; ++b)
-    if (seq_len[b] < 1 || pos[b] != seq_len[b] - 1) return MLA_ERR_INVALID_ARG;
   for (int32_t b = 0; b < B; ++b) {
     const int64_t np = ((int64_t)seq_len[b] + page_rows - 1) / page_rows;
     if (np > max_pages) return MLA_ERR_CAPACITY;
@@ -701,15 +742,46 @@ int mla_decode_paged_check(const mla_config* cfg, const int32_t* pos, const int3
       if (row[i] < 0 || row[i] >= n_pages) return MLA_ERR_CAPACITY;
   }
   if (writes) {  // the new rows of a step: one cache row each, all distinct
-    std::vector<int64_t> w(B);
-    for (int32_t b = 0; b < B; ++b) {
-      const int32_t t = seq_len[b] - 1;
-      w[b] = (int64_t)block_table[(int64_t)b * max_pages + t / page_rows] * page_rows +
-             t % page_rows;
-    }
+    std::vector<int64_t> w;
+    w.reserve((size_t)B * q_len);
+    for (int32_t b = 0; b < B; ++b)
+      for (int j = 0; j < q_len; ++j) {
+        const int32_t t = seq_len[b] - q_len + j;
+        w.push_back((int64_t)block_table[(int64_t)b * max_pages + t / page_rows] * page_rows +
+                    t % page_rows);
+      }
     std::sort(w.begin(), w.end());
     if (std::adjacent_find(w.begin(), w.end()) != w.end()) return MLA_ERR_INVALID_ARG;
   }
+  return MLA_OK;
+}
+
+int mla_decode_paged_check(const mla_config* cfg, const int32_t* pos, const int32_t* block_table,
+                           int32_t max_pages, int32_t page_rows, const int32_t* seq_len, int32_t B,
+                           int64_t cache_rows, int32_t writes) {
+  int rc = mla_config_check(cfg);
+  if (rc) return rc;
+  if (B <= 0 || !pos || !block_table || !seq_len || cache_rows <= 0 || max_pages <= 0)
+    return MLA_ERR_INVALID_ARG;
+  for (int32_t b = 0; b < B; ++b)
+    if (seq_len[b] < 1 || pos[b] != seq_len[b] - 1) return MLA_ERR_INVALID_ARG;
+  return paged_table_check(block_table, max_pages, page_rows, seq_len, B, cache_rows, 1, writes);
+}
+
+int mla_decode_ex_check(const mla_config* cfg, const mla_decode_args* a) {
+  int rc = mla_config_check(cfg);
+  if (rc) return rc;
+  if (!a || a->B <= 0 || !a->seq_len || a->cache_rows <= 0) return MLA_ERR_INVALID_ARG;
+  if (a->q_len < 1 || a->q_len > MLA_MAX_Q_LEN) return MLA_ERR_INVALID_ARG;
+  if ((a->seq_off != nullptr) == (a->block_table != nullptr)) return MLA_ERR_INVALID_ARG;
+  for (int32_t b = 0; b < a->B; ++b)
+    if (a->seq_len[b] < a->q_len) return MLA_ERR_INVALID_ARG;
+  if (a->block_table)
+    return paged_table_check(a->block_table, a->max_pages, a->page_rows, a->seq_len, a->B,
+                             a->cache_rows, a->q_len, a->append);
+  for (int32_t b = 0; b < a->B; ++b)
+    if (a->seq_off[b] < 0 || a->seq_off[b] > a->cache_rows - a->seq_len[b])
+      return MLA_ERR_CAPACITY;
   return MLA_OK;
 }
 
@@ -1146,10 +1218,13 @@ static void q_skinny_rest(mla_ctx* h, int B, void* ws, const DecodeLayout& L,
                      slot_dev, kv_g, cache, nullptr, nullptr, d, h->rope, h->stream);
 }
 
+// B query rows (q_len per sequence); mt: the core's metadata, mc: the
+// combine's (one virtual sequence per query row)
 template <typename T>
-static int run_decode(mla_ctx* h, const T* hidden, int B, T* cache, T* out, void* ws,
-                      const DecodeLayout& L, const DecodeMeta& mt, int parts, int nseg_total,
-                      int max_chunks, const int64_t* slot_dev, const int32_t* pos_host) {
+static int run_decode(mla_ctx* h, const T* hidden, int B, int q_len, T* cache, T* out, void* ws,
+                      const DecodeLayout& L, const DecodeMeta& mt, const DecodeMeta& mc,
+                      int parts, int nseg_total, int max_chunks, const int64_t* slot_dev,
+                      const int32_t* pos_host) {
   const Dims& d = h->d;
   float* scratch = at<float>(ws, L.scratch);
   T* q_nope = at<T>(ws, L.q_nope);
@@ -1178,17 +1253,19 @@ static int run_decode(mla_ctx* h, const T* hidden, int B, T* cache, T* out, void
   if (ts >= 0) HIP_TRY(h, hipEventRecord(h->tev[2 * ts], h->stream));
   if constexpr (sizeof(T) == 2) {
     if (h->mfma) {
+      const mla::TokenSplit tk{q_len, nseg_total};
       if (wide_core(h))
-        mla::decode_core_wide(q_cat, cache, mt, parts, acc, ml, d, h->stream);
+        mla::decode_core_wide(q_cat, cache, mt, parts, tk, acc, ml, d, h->stream);
       else if (h->kv8)  // FP8 rows; otherwise as the bf16 ring core
-        mla::decode_core_ring8(q_cat, (const uint8_t*)(const void*)cache, mt, parts, acc, ml,
+        mla::decode_core_ring8(q_cat, (const uint8_t*)(const void*)cache, mt, parts, tk, acc, ml,
                                (bf16*)o_lat, d, h->stream);
       else  // sequences inside one segment are finished into o_lat by the core
-        mla::decode_core_ring(q_cat, cache, mt, parts, acc, ml, (bf16*)o_lat, d, h->stream);
+        mla::decode_core_ring(q_cat, cache, mt, parts, tk, acc, ml, (bf16*)o_lat, d, h->stream);
       mfma_core = true;
     }
   }
-  if (!mfma_core) mla::decode_core_generic<T>(q_cat, cache, mt, nseg_total, acc, ml, d, h->stream);
+  if (!mfma_core)
+    mla::decode_core_generic<T>(q_cat, cache, mt, nseg_total, q_len, acc, ml, d, h->stream);
   if (ts >= 0) HIP_TRY(h, hipEventRecord(h->tev[2 * ts + 1], h->stream));
   T* o = at<T>(ws, L.o);
   bool uv_done = false;
@@ -1196,16 +1273,16 @@ static int run_decode(mla_ctx* h, const T* hidden, int B, T* cache, T* out, void
     if (combine_uv(h)) {
       // A6 + A7: combine the partials of each sequence (fixed slot order) and
       // apply W_UV_h to the merged latent sums
-      mla::decode_combine_uv(acc, ml, mt, B, d.H, max_chunks, at<float>(ws, L.cacc),
+      mla::decode_combine_uv(acc, ml, mc, B, d.H, max_chunks, at<float>(ws, L.cacc),
                              at<float>(ws, L.cml), ring_core(h), (const bf16*)h->w_uv,
                              (bf16*)o_lat, (bf16*)o, h->stream);
       uv_done = true;
     } else if (mfma_core) {
-      mla::decode_combine_512(acc, ml, mt, B, d.H, max_chunks, at<float>(ws, L.cacc),
+      mla::decode_combine_512(acc, ml, mc, B, d.H, max_chunks, at<float>(ws, L.cacc),
                               at<float>(ws, L.cml), ring_core(h), (bf16*)o_lat, h->stream);
     }
   }
-  if (!mfma_core) mla::decode_combine<T>(acc, ml, mt, B, o_lat, d, h->stream);
+  if (!mfma_core) mla::decode_combine<T>(acc, ml, mc, B, o_lat, d, h->stream);
   // A7: o_h = W_UV_h o_lat_h
   if (!uv_done)
     gemm_out<T>(h, o_lat, (int64_t)d.H * d.dc, d.dc, (const T*)h->w_uv, d.dc,
@@ -1226,6 +1303,72 @@ static int run_decode(mla_ctx* h, const T* hidden, int B, T* cache, T* out, void
   return check_launch(h, "decode");
 }
 
+// One decode call after its arguments have been checked: B sequences with
+// q_len new tokens each (query row b * q_len + j), a contiguous cache
+// (seq_off) or a paged one (pg), appending the new rows first for a step.
+struct DecodeCall {
+  const void* hidden;
+  void* out;
+  int B, q_len;
+  const int32_t* seq_len;
+  const int64_t* seq_off;
+  const PageArgs* pg;
+  void* cache;
+  bool step;
+  void* ws;
+  size_t ws_bytes;
+};
+
+static int decode_exec(mla_ctx* h, const DecodeCall& c, const char* what) {
+  if (!h->absorbed) return fail(h, MLA_ERR_STATE, "%s before mla_absorb_weights", what);
+  const int B = c.B, q_len = c.q_len, Bq = B * q_len;
+  int64_t total = 0;
+  for (int32_t b = 0; b < B; ++b) total += c.seq_len[b];
+  const DecodeLayout L = decode_layout(h, B, total, c.step, q_len);
+  int rc;
+  if ((rc = check_ws(h, c.ws, c.ws_bytes, L.total))) return rc;
+  DeviceGuard g(h->device);
+  if (!g.ok) return fail(h, MLA_ERR_HIP, "cannot select device %d", h->device);
+  std::vector<char> blob;
+  MetaOffsets mo;
+  int nseg_total = 0, max_chunks = 1, cslots = 0;
+  const int parts = build_decode_meta(h, B, c.seq_off, c.seq_len, q_len, total, c.step, c.pg,
+                                      blob, &mo, &nseg_total, &max_chunks, &cslots);
+  if (cslots > L.max_cslots)
+    return fail(h, MLA_ERR_WORKSPACE, "internal: combine chunk slots larger than planned");
+  if (blob.size() > meta_bytes(B, max_parts(h, total, q_len), L.max_segs, total, q_len))
+    return fail(h, MLA_ERR_WORKSPACE, "internal: decode metadata larger than planned");
+  void* ws = c.ws;
+  void* meta = at<char>(ws, L.meta);
+  if ((rc = stage_upload(h, meta, blob.data(), blob.size()))) return rc;
+  DecodeMeta mt;
+  mt.seq_off = at<int64_t>(meta, mo.seq_off);
+  mt.seq_len = at<int32_t>(meta, mo.seq_len);
+  mt.pos = at<int32_t>(meta, mo.pos);
+  mt.pstart = at<int32_t>(meta, mo.pstart);
+  mt.nseg = at<int32_t>(meta, mo.nseg);
+  mt.cstart = at<int32_t>(meta, mo.cstart);
+  mt.work = at<mla::DecodeWork>(meta, mo.work);
+  mt.part_begin = at<int32_t>(meta, mo.part);
+  mt.segs = at<DecodeSeg>(meta, mo.segs);
+  mt.pages = c.pg ? at<int32_t>(meta, mo.pages) : nullptr;
+  mt.pg_off = c.pg ? at<int32_t>(meta, mo.pg_off) : nullptr;
+  mt.page_shift = c.pg ? c.pg->shift : 0;
+  DecodeMeta mc = mt;  // the combine's view: one sequence per query row
+  mc.pstart = at<int32_t>(meta, mo.vpstart);
+  mc.nseg = at<int32_t>(meta, mo.vnseg);
+  mc.cstart = at<int32_t>(meta, mo.vcstart);
+  std::vector<int32_t> qpos(Bq);
+  for (int i = 0; i < Bq; ++i) qpos[i] = c.seq_len[i / q_len] - q_len + i % q_len;
+  const int64_t* slot_dev = c.step ? at<int64_t>(meta, mo.slot) : nullptr;
+  if (is_f32(h))
+    return run_decode<float>(h, (const float*)c.hidden, Bq, q_len, (float*)c.cache,
+                             (float*)c.out, ws, L, mt, mc, parts, nseg_total, max_chunks,
+                             slot_dev, qpos.data());
+  return run_decode<bf16>(h, (const bf16*)c.hidden, Bq, q_len, (bf16*)c.cache, (bf16*)c.out, ws,
+                          L, mt, mc, parts, nseg_total, max_chunks, slot_dev, qpos.data());
+}
+
 static int decode_common(mla_handle h, const void* hidden, const int32_t* pos,
                          const int64_t* seq_off, const int32_t* seq_len, int32_t B, void* cache,
                          int64_t cache_rows, void* out, void* ws, size_t ws_bytes, bool step,
@@ -1240,43 +1383,8 @@ static int decode_common(mla_handle h, const void* hidden, const int32_t* pos,
               : mla_decode_check(&h->cfg, pos, seq_off, seq_len, B, cache_rows);
   if (rc) return fail(h, rc, "%s: %s (B=%d, cache_rows=%lld)", what, mla_status_string(rc), B,
                       (long long)cache_rows);
-  if (!h->absorbed) return fail(h, MLA_ERR_STATE, "%s before mla_absorb_weights", what);
-  int64_t total = 0;
-  for (int32_t b = 0; b < B; ++b) total += seq_len[b];
-  const DecodeLayout L = decode_layout(h, B, total, step);
-  if ((rc = check_ws(h, ws, ws_bytes, L.total))) return rc;
-  DeviceGuard g(h->device);
-  if (!g.ok) return fail(h, MLA_ERR_HIP, "cannot select device %d", h->device);
-  std::vector<char> blob;
-  MetaOffsets mo;
-  int nseg_total = 0, max_chunks = 1, cslots = 0;
-  const int parts = build_decode_meta(h, B, seq_off, seq_len, pos, total, step, pg, blob, &mo,
-                                      &nseg_total, &max_chunks, &cslots);
-  if (cslots > L.max_cslots)
-    return fail(h, MLA_ERR_WORKSPACE, "internal: combine chunk slots larger than planned");
-  if (blob.size() > meta_bytes(B, max_parts(h, total), L.max_segs, total))
-    return fail(h, MLA_ERR_WORKSPACE, "internal: decode metadata larger than planned");
-  void* meta = at<char>(ws, L.meta);
-  if ((rc = stage_upload(h, meta, blob.data(), blob.size()))) return rc;
-  DecodeMeta mt;
-  mt.seq_off = at<int64_t>(meta, mo.seq_off);
-  mt.seq_len = at<int32_t>(meta, mo.seq_len);
-  mt.pos = at<int32_t>(meta, mo.pos);
-  mt.pstart = at<int32_t>(meta, mo.pstart);
-  mt.nseg = at<int32_t>(meta, mo.nseg);
-  mt.cstart = at<int32_t>(meta, mo.cstart);
-  mt.work = at<mla::DecodeWork>(meta, mo.work);
-  mt.part_begin = at<int32_t>(meta, mo.part);
-  mt.segs = at<DecodeSeg>(meta, mo.segs);
-  mt.pages = pg ? at<int32_t>(meta, mo.pages) : nullptr;
-  mt.pg_off = pg ? at<int32_t>(meta, mo.pg_off) : nullptr;
-  mt.page_shift = pg ? pg->shift : 0;
-  const int64_t* slot_dev = step ? at<int64_t>(meta, mo.slot) : nullptr;
-  if (is_f32(h))
-    return run_decode<float>(h, (const float*)hidden, B, (float*)cache, (float*)out, ws, L, mt,
-                             parts, nseg_total, max_chunks, slot_dev, pos);
-  return run_decode<bf16>(h, (const bf16*)hidden, B, (bf16*)cache, (bf16*)out, ws, L, mt, parts,
-                          nseg_total, max_chunks, slot_dev, pos);
+  const DecodeCall c{hidden, out, B, 1, seq_len, seq_off, pg, cache, step, ws, ws_bytes};
+  return decode_exec(h, c, what);
 }
 
 int mla_decode(mla_handle h, const void* hidden, const int32_t* pos, const int64_t* seq_off,
@@ -1291,6 +1399,30 @@ int mla_decode_step(mla_handle h, const void* hidden, const int32_t* pos, const 
                     void* ws, size_t ws_bytes) {
   return decode_common(h, hidden, pos, seq_off, seq_len, B, cache, cache_rows, out, ws, ws_bytes,
                        true);
+}
+
+size_t mla_decode_ex_workspace_bytes(mla_handle h, int32_t B, int32_t q_len, int64_t total_rows,
+                                     int32_t append) {
+  if (!h || B <= 0 || q_len < 1 || q_len > MLA_MAX_Q_LEN || total_rows <= 0) return 0;
+  return decode_layout(h, B, total_rows, append != 0, q_len).total;
+}
+
+static int page_shift_of(int32_t page_rows);
+
+int mla_decode_ex(mla_handle h, const mla_decode_args* a) {
+  if (!h) return MLA_ERR_INVALID_ARG;
+  const char* what = "decode_ex";
+  if (!a || !a->hidden || !a->cache || !a->out)
+    return fail(h, MLA_ERR_INVALID_ARG, "%s: NULL argument or tensor", what);
+  const int rc = mla_decode_ex_check(&h->cfg, a);
+  if (rc) return fail(h, rc, "%s: %s (B=%d, q_len=%d, cache_rows=%lld)", what,
+                      mla_status_string(rc), a->B, a->q_len, (long long)a->cache_rows);
+  PageArgs pg{a->block_table, a->max_pages, a->page_rows, 0};
+  if (a->block_table) pg.shift = page_shift_of(a->page_rows);
+  const DecodeCall c{a->hidden, a->out,   a->B,           a->q_len,  a->seq_len,
+                     a->seq_off, a->block_table ? &pg : nullptr, a->cache, a->append != 0,
+                     a->ws,     a->ws_bytes};
+  return decode_exec(h, c, what);
 }
 
 static int page_shift_of(int32_t page_rows) {

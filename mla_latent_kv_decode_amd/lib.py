@@ -42,6 +42,21 @@ class MLAConfig(ctypes.Structure):
                 ("dtype", ctypes.c_int32), ("kv_storage", ctypes.c_int32)]
 
 
+class MLADecodeArgs(ctypes.Structure):
+    """struct mla_decode_args (include/mla.h)."""
+    _fields_ = [("hidden", ctypes.c_void_p), ("out", ctypes.c_void_p),
+                ("B", ctypes.c_int32), ("q_len", ctypes.c_int32),
+                ("seq_len", ctypes.POINTER(ctypes.c_int32)),
+                ("seq_off", ctypes.POINTER(ctypes.c_int64)),
+                ("block_table", ctypes.POINTER(ctypes.c_int32)),
+                ("max_pages", ctypes.c_int32), ("page_rows", ctypes.c_int32),
+                ("cache", ctypes.c_void_p), ("cache_rows", ctypes.c_int64),
+                ("append", ctypes.c_int32), ("ws", ctypes.c_void_p),
+                ("ws_bytes", ctypes.c_size_t)]
+
+
+MLA_MAX_Q_LEN = 16
+
 # name -> (restype, argtypes)
 _SIGS = {
     "mla_abi_version": (ctypes.c_int, []),
@@ -82,6 +97,11 @@ _SIGS = {
     "mla_decode_step_paged": (ctypes.c_int, [_P, _P, _I32P, _I32P, ctypes.c_int32,
                                              ctypes.c_int32, _I32P, ctypes.c_int32, _P,
                                              ctypes.c_int64, _P, _P, ctypes.c_size_t]),
+    "mla_decode_ex_check": (ctypes.c_int, [ctypes.POINTER(MLAConfig),
+                                           ctypes.POINTER(MLADecodeArgs)]),
+    "mla_decode_ex_workspace_bytes": (ctypes.c_size_t, [_P, ctypes.c_int32, ctypes.c_int32,
+                                                        ctypes.c_int64, ctypes.c_int32]),
+    "mla_decode_ex": (ctypes.c_int, [_P, ctypes.POINTER(MLADecodeArgs)]),
     "mla_decode_stage_offsets": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.c_int64,
                                                 ctypes.POINTER(ctypes.c_size_t),
                                                 ctypes.POINTER(ctypes.c_size_t)]),
@@ -327,6 +347,29 @@ class MLALayer:
             return out
         return (out,) + self._stages(B, total, wsp)
 
+    def decode_ex(self, hidden, seq_len, cache, q_len=1, seq_off=None, block_table=None,
+                  page_rows=0, append=False, out=None):
+        """mla_decode_ex: q_len new tokens per sequence (hidden / out rows
+        b * q_len + j), over a contiguous (seq_off) or paged (block_table,
+        page_rows) cache, appending the new rows first if `append`."""
+        import torch
+        self._sync_stream()
+        args, keep = decode_args(hidden.shape[0] // q_len, q_len, seq_len, seq_off, block_table,
+                                 page_rows, cache, append)
+        B = args.B
+        if out is None:
+            out = torch.empty((B * q_len, self.dims.hidden), dtype=self.torch_dtype,
+                              device=self.device)
+        total = int(keep[0].astype(np.int64).sum())
+        wsp, wsn = self.ws.get(self.lib.mla_decode_ex_workspace_bytes(self.h, B, q_len,
+                                                                      max(total, 1),
+                                                                      int(bool(append))))
+        args.hidden, args.out = hidden.data_ptr(), out.data_ptr()
+        args.ws, args.ws_bytes = wsp.value, wsn
+        rc = self.lib.mla_decode_ex(self.h, ctypes.byref(args))
+        self._check(rc, self.h, "mla_decode_ex")
+        return out
+
     def decode_step_paged(self, hidden, block_table, page_rows, seq_len, cache, out=None):
         """mla_decode_step_paged: appends each new token at position
         seq_len[b] - 1 through the block table, then decodes."""
@@ -401,6 +444,28 @@ def decode_plan(seq_len, max_parts: int):
         raise MLAError(st, lib.mla_status_string(st).decode())
     p, n = npart.value, nseg.value
     return pb[:p + 1].copy(), sb[:n].copy(), r0[:n].copy(), r1[:n].copy()
+
+
+def decode_args(B, q_len, seq_len, seq_off=None, block_table=None, page_rows=0, cache=None,
+                append=False):
+    """An MLADecodeArgs for the host metadata (tensors and workspace left for
+    the caller); returns (args, arrays that must stay alive)."""
+    sl_a, sl_p = _i32(seq_len)
+    keep = [sl_a]
+    a = MLADecodeArgs()
+    a.B, a.q_len, a.seq_len = int(B), int(q_len), sl_p
+    if seq_off is not None:
+        so_a, a.seq_off = _i64(seq_off)
+        keep.append(so_a)
+    if block_table is not None:
+        bt = np.ascontiguousarray(block_table, dtype=np.int32)
+        bt_a, a.block_table = _i32(bt.reshape(-1))
+        a.max_pages, a.page_rows = int(bt.shape[1]), int(page_rows)
+        keep.append(bt_a)
+    if cache is not None:
+        a.cache, a.cache_rows = cache.data_ptr(), int(cache.shape[0])
+    a.append = int(bool(append))
+    return a, keep
 
 
 def header_functions(header: str = None) -> list:

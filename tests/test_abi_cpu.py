@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(mla):
     missing = [n for n in names if not hasattr(mla, n)]
     assert not missing, missing
     assert set(names) == set(L._SIGS), set(names) ^ set(L._SIGS)
-    assert mla.mla_abi_version() == 3
+    assert mla.mla_abi_version() == 4
 
 
 def test_status_strings(mla):
@@ -156,6 +156,35 @@ def test_decode_paged_check(mla):
     assert chk([4, 4], [[2], [2]], 32, [5, 5], 128, writes=1) == L.MLA_ERR_INVALID_ARG
     assert chk([4, 4], [[2], [2]], 32, [5, 5], 128, writes=0) == L.MLA_OK  # reads may share
     assert chk([4, 5], [[2], [2]], 32, [5, 6], 128, writes=1) == L.MLA_OK  # different offsets
+
+
+def test_decode_ex_check(mla):
+    c = cfg()
+
+    def chk(B, q, ln, off=None, table=None, P=0, rows=1000, append=0):
+        args, keep = L.decode_args(B, q, ln, off, table, P, None, append)
+        args.cache_rows = rows
+        return mla.mla_decode_ex_check(ctypes.byref(c), ctypes.byref(args))
+
+    assert chk(2, 3, [5, 3], off=[0, 10]) == L.MLA_OK
+    assert chk(2, 1, [5, 3], off=[0, 10]) == L.MLA_OK
+    assert chk(2, 4, [5, 3], off=[0, 10]) == L.MLA_ERR_INVALID_ARG    # seq_len < q_len
+    assert chk(2, 0, [5, 3], off=[0, 10]) == L.MLA_ERR_INVALID_ARG    # q_len < 1
+    assert chk(2, 17, [50, 30], off=[0, 100]) == L.MLA_ERR_INVALID_ARG  # q_len > 16
+    assert chk(2, 16, [50, 30], off=[0, 100]) == L.MLA_OK
+    assert chk(2, 2, [5, 3], off=[0, 998]) == L.MLA_ERR_CAPACITY      # past the end
+    assert chk(2, 2, [5, 3]) == L.MLA_ERR_INVALID_ARG                 # neither layout
+    both = dict(off=[0, 10], table=[[0], [1]], P=32)
+    assert chk(2, 2, [5, 3], **both) == L.MLA_ERR_INVALID_ARG         # both layouts
+    # paged: 31 pages of 32 rows; the 3 new rows of sequence 0 (positions 30..32)
+    # straddle its pages 4 and 9
+    assert chk(2, 3, [33, 3], table=[[4, 9], [2, 0]], P=32, rows=1000, append=1) == L.MLA_OK
+    assert chk(2, 3, [33, 3], table=[[4, 31], [2, 0]], P=32) == L.MLA_ERR_CAPACITY
+    # sequence 1's new rows (positions 0..2 of page 4) collide with sequence 0's
+    # position 32 only if both name page 4 at offset 0: position 32 -> page 9
+    # offset 0, so pointing sequence 1 at page 9 collides
+    assert chk(2, 3, [33, 3], table=[[4, 9], [9, 0]], P=32, append=1) == L.MLA_ERR_INVALID_ARG
+    assert chk(2, 3, [33, 3], table=[[4, 9], [9, 0]], P=32, append=0) == L.MLA_OK
 
 
 def test_prefill_check(mla):
