@@ -25,6 +25,9 @@ count those bytes.
 ``--workload v2lite_decode_b64_paged`` is the same batch on a paged cache
 (64-row pages handed out in a seeded random order, mla_decode_step_paged).
 
+``--workload v2lite_decode_b64_q2``: the same sequences decoding two new tokens
+each per step (mla_decode_ex with the append; 128 query rows).
+
 ``--workload v3_prefill_4x4096`` measures the chunked causal prefill instead
 (V3 shapes, 4 sequences of 4096 new tokens after 0 / 2048 cached rows): a step
 is the append of the new tokens' latent rows plus one mla_prefill call over the
@@ -128,16 +131,17 @@ def cpu_baseline(wl, w, lens, budget_s: float):
     while spent < budget_s:  # whole passes over the batch until the budget is used
         for b in range(len(lens)):
             L = int(lens[b])
+            q = wl.q_len
             if b not in prepared:
-                x = synth.hidden_states(b, L + 1, d.hidden, wl.dtype)
+                x = synth.hidden_states(b, L + q, d.hidden, wl.dtype)
                 prepared[b] = (x, O.latent_rows(x[:L], np.arange(L), w["w_kva"], w["kv_norm_g"],
                                                 shp))
             x, prior = prepared[b]
             t0 = time.perf_counter()
-            O.mla_step(x[L:], np.array([L]), prior, w, shp, kv_store=store)
+            O.mla_step(x[L:], np.arange(L, L + q), prior, w, shp, kv_store=store)
             spent += time.perf_counter() - t0
-            rows += L + 1
-            toks += 1
+            rows += L + q
+            toks += q
             if spent >= budget_s:
                 break
         passes += 1
@@ -322,20 +326,21 @@ def main():
     layer = MLALayer(d, wl.dtype, kv=wl.kv)
     layer.absorb_weights({k: torch.from_numpy(v).cuda().to(tdt) for k, v in w.items()})
     lens = synth.lengths(wl)
-    seq_off, seq_len, total = synth.decode_layout(lens)
+    q = wl.q_len  # new tokens per sequence and step
+    seq_off, seq_len, total = synth.decode_layout(lens, q)
     B = len(lens)
     caches = [layer.new_cache(total) for _ in range(2)]
     row_bytes = layer.row_bytes()
-    x_new = np.empty((B, d.hidden), np.float32)
+    x_new = np.empty((B * q, d.hidden), np.float32)
     chunk = 8192
     for b in range(B):
-        n = int(lens[b]) + 1
+        n = int(lens[b]) + q
         for s in range(0, n, chunk):
             m = min(chunk, n - s)
             x = synth.hidden_states(b, m, d.hidden, wl.dtype, start=s)
             layer.append(torch.from_numpy(x).cuda().to(tdt), np.arange(s, s + m),
                          int(seq_off[b]) + np.arange(s, s + m), caches[0])
-        x_new[b] = x[-1]
+        x_new[b * q:(b + 1) * q] = x[-q:]
     P = wl.page_rows
     if P:
         # a paged cache: the same rows moved into 64-row pages handed out in a
@@ -357,12 +362,15 @@ def main():
     xd = torch.from_numpy(x_new).cuda().to(tdt)
     pos = (seq_len - 1).astype(np.int32)
     slot = seq_off + pos
-    y = torch.empty((B, d.hidden), dtype=tdt, device="cuda")
+    y = torch.empty((B * q, d.hidden), dtype=tdt, device="cuda")
     torch.cuda.synchronize()
 
     def step(i):
         # append the B new rows and decode them in one library call
-        if P:
+        if q > 1:
+            layer.decode_ex(xd, seq_len, caches[i % 2], q_len=q, seq_off=seq_off, append=True,
+                            out=y)
+        elif P:
             layer.decode_step_paged(xd, table, P, seq_len, caches[i % 2], out=y)
         else:
             layer.decode_step(xd, seq_off, seq_len, caches[i % 2], out=y)
@@ -412,23 +420,24 @@ def main():
     core_ms = float(np.mean(core))
     cache_bytes = float(int(seq_len.sum()) * row_bytes)
     weight_bytes = 2.0 * sum(v.size for v in w.values())
-    act_bytes = 2.0 * 2 * B * d.hidden + B * row_bytes  # hidden in, y out, appended rows
+    act_bytes = 2.0 * 2 * B * q * d.hidden + B * q * row_bytes  # hidden in, y out, new rows
     gbs = cache_bytes / t_step / 1e9
     core_gbs = cache_bytes / (core_ms * 1e-3) / 1e9
     fp8 = wl.kv == "fp8"
-    traffic = None if (fp8 or P) else traffic_from_profile(cache_bytes)
+    traffic = None if (fp8 or P or q > 1) else traffic_from_profile(cache_bytes)
 
     res = {
         "metric": "MLA decode latent-KV GB/s + tokens/s (V2-Lite shapes, B=64), % of HBM peak"
                   + (", FP8 latent cache" if fp8 else "")
-                  + (f", paged cache ({P}-row pages)" if P else ""),
+                  + (f", paged cache ({P}-row pages)" if P else "")
+                  + (f", {q} new tokens per sequence" if q > 1 else ""),
         "value": round(gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
         "ms_per_step": round(t_step * 1e3, 5),
-        "tokens_per_s": round(B / t_step, 1),
+        "tokens_per_s": round(B * q / t_step, 1),
         "hbm_frac_step": round((cache_bytes + weight_bytes + act_bytes) / t_step / 1e9
                                / HBM_PEAK_GBS, 4),
         "higher_is_better": True,
@@ -439,7 +448,7 @@ def main():
         "timing": "eager" if graph is None else "hip-graph replay of the K steps",
         "config": {"workload": wl.name, "batch": B, "len_lo": wl.len_lo, "len_hi": wl.len_hi,
                    "latent_rows": int(seq_len.sum()), "cache_row_bytes": row_bytes,
-                   "page_rows": P,
+                   "page_rows": P, "q_len": q,
                    "cache_bytes": int(cache_bytes),
                    "weight_bytes": int(weight_bytes), "hidden": d.hidden, "heads": d.n_heads,
                    "kv_lora": d.kv_lora, "qk_rope": d.qk_rope},

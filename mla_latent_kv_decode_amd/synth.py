@@ -71,6 +71,7 @@ class Workload:
     fixed_lengths: tuple = field(default_factory=tuple)
     kv: str = "dtype"          # latent cache rows: "dtype" or "fp8" (E4M3 + row scale)
     page_rows: int = 0         # > 0: a paged cache, pages handed out in a seeded random order
+    q_len: int = 1             # decode: new tokens per sequence and step
 
 
 WORKLOADS = {
@@ -89,6 +90,9 @@ WORKLOADS = {
     # the same batch on a paged cache: 64-row pages in a seeded random order
     "v2lite_decode_b64_paged": Workload("v2lite_decode_b64_paged", V2_LITE, "bf16", 0.02,
                                         "decode", 64, len_lo=512, len_hi=8192, page_rows=64),
+    # the same batch decoding two new tokens per sequence and step
+    "v2lite_decode_b64_q2": Workload("v2lite_decode_b64_q2", V2_LITE, "bf16", 0.02,
+                                     "decode", 64, len_lo=512, len_hi=8192, q_len=2),
     # V3 ragged decode, B=32, cached rows ~ U{2048..16384}
     "v3_decode_b32": Workload("v3_decode_b32", V3, "bf16", 0.02, "decode", 32,
                               len_lo=2048, len_hi=16384),
@@ -182,10 +186,11 @@ def page_table(seq_len, page_rows: int, seed: int = 1237):
     return table, n_pages
 
 
-def decode_layout(lens: np.ndarray):
+def decode_layout(lens: np.ndarray, q_len: int = 1):
     """Contiguous per-sequence cache layout for decode: sequence b owns rows
-    [seq_off[b], seq_off[b] + lens[b] + 1) (cached rows plus the new token)."""
-    s = np.asarray(lens, dtype=np.int64) + 1
+    [seq_off[b], seq_off[b] + lens[b] + q_len) (cached rows plus its new
+    tokens)."""
+    s = np.asarray(lens, dtype=np.int64) + q_len
     seq_off = np.concatenate([[0], np.cumsum(s)[:-1]]).astype(np.int64)
     return seq_off, s.astype(np.int32), int(s.sum())
 
