@@ -57,7 +57,7 @@ constexpr int NLOAD = TR + TR / 8;           // one-KB copies per tile
 constexpr int NPROD = 2;                     // producer waves
 constexpr int LPW = NLOAD / NPROD;           // copies per producer wave and tile
 constexpr int NCONS = 4;                     // consumer waves = column quarters
-constexpr int NCB = 32 / NCONS;              // 16-column blocks per consumer wave
+constexpr int NCB1 = 32 / NCONS;             // 16-column blocks per consumer wave (one token)
 constexpr int NTHR = 64 * (NCONS + NPROD);
 constexpr float kRescale = 8.0f;
 constexpr int kXcds = 8;
@@ -71,31 +71,37 @@ typedef short s16x8_t __attribute__((ext_vector_type(8)));
 // Copy I of a tile whose first row is at `base` and whose last valid row is
 // `last`: I < 32 copies the latent part of row I, I >= 32 the rope parts of
 // rows 8(I-32) .. +7.  Rows past `last` re-read it (their scores are masked).
+// jump16: bytes added to the address of rows 16 .. 31 (a query tile holding
+// two tokens' 16 heads: their q_cat rows are H rows apart; 0 for cache tiles)
 template <int I>
-__device__ __forceinline__ void tile_copy(const char* base, int last, uint32_t stage, int lane) {
+__device__ __forceinline__ void tile_copy(const char* base, int last, uint32_t stage, int lane,
+                                          int jump16) {
   if constexpr (I < TR) {
     const int r = I <= last ? I : last;
-    dma16(base + r * (RW * 2) + ((lane ^ lat_swz(I & 15)) << 4), stage + I * 1024);
+    dma16(base + r * (RW * 2) + (r >= 16 ? jump16 : 0) + ((lane ^ lat_swz(I & 15)) << 4),
+          stage + I * 1024);
   } else {
     constexpr int J = I - TR;
     int r = 8 * J + (lane >> 3);
     const int cc = (lane & 7) ^ rope_swz(r & 15);
     r = r <= last ? r : last;
-    dma16(base + r * (RW * 2) + 1024 + (cc << 4), stage + ROPE_OFF + J * 1024);
+    dma16(base + r * (RW * 2) + (r >= 16 ? jump16 : 0) + 1024 + (cc << 4),
+          stage + ROPE_OFF + J * 1024);
   }
 }
 
 template <int P, int... U>
 __device__ __forceinline__ void producer_copies(const char* base, int last, uint32_t stage,
-                                                int lane, std::integer_sequence<int, U...>) {
-  (tile_copy<P * LPW + U>(base, last, stage, lane), ...);
+                                                int lane, int jump16,
+                                                std::integer_sequence<int, U...>) {
+  (tile_copy<P * LPW + U>(base, last, stage, lane, jump16), ...);
 }
 
 __device__ __forceinline__ void issue_tile(const char* base, int last, uint32_t stage, int p,
-                                           int lane) {
+                                           int lane, int jump16 = 0) {
   const auto seq = std::make_integer_sequence<int, LPW>{};
-  if (p == 0) producer_copies<0>(base, last, stage, lane, seq);
-  else producer_copies<1>(base, last, stage, lane, seq);
+  if (p == 0) producer_copies<0>(base, last, stage, lane, jump16, seq);
+  else producer_copies<1>(base, last, stage, lane, jump16, seq);
 }
 
 __device__ __forceinline__ bf16x8_t cat_bf16(s16x4_t lo, s16x4_t hi) {
@@ -103,18 +109,26 @@ __device__ __forceinline__ bf16x8_t cat_bf16(s16x4_t lo, s16x4_t hi) {
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
+// TOK tokens per workgroup: 1, or 2 (a pair of a sequence's new tokens: the
+// query tile holds both tokens' 16 heads, consumer wave w takes token w >> 1
+// and half w & 1 of the latent columns, so the part's rows stream once for
+// both)
+template <int TOK>
 __global__ void __launch_bounds__(NTHR, 1)
 decode_core_ring_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cache, DecodeMeta mt,
                    float* __restrict__ acc, float* __restrict__ ml, bf16* __restrict__ o_lat,
                    int H, int nparts, int q_len, int nseg_total) {
   __shared__ __attribute__((aligned(1024))) char lds[NST * ST_BYTES];
-  // block -> (part, token, head group); the groups of a part are numbered
-  // part % 8 modulo 8, so they share an XCD (blocks go to XCDs round robin)
+  // block -> (part, token group, head group); the groups of a part are
+  // numbered part % 8 modulo 8, so they share an XCD (blocks go to XCDs round
+  // robin)
+  constexpr int NCB = NCB1 * TOK;  // 16-column blocks per consumer wave
   const int HG = H / 16;
+  const int NG = HG * q_len / TOK;
   const int bid = blockIdx.x;
-  const int part = (bid / (kXcds * HG * q_len)) * kXcds + bid % kXcds;
-  const int hgq = (bid / kXcds) % (HG * q_len);
-  const int tok = hgq / HG, hg = hgq % HG;
+  const int part = (bid / (kXcds * NG)) * kXcds + bid % kXcds;
+  const int g = (bid / kXcds) % NG;
+  const int tok0 = TOK * (g / HG), hg = g % HG;  // first token of the group
   if (part >= nparts) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -143,8 +157,8 @@ decode_core_ring_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
       const uint32_t stage = lds0 + (uint32_t)(issued % NST) * ST_BYTES;
       if (ik == 0) {
         const char* qb = reinterpret_cast<const char*>(
-            q_cat + ((int64_t)(iw.b * q_len + tok) * H + hg * 16) * RW);
-        issue_tile(qb, 15, stage, p, lane);
+            q_cat + ((int64_t)(iw.b * q_len + tok0) * H + hg * 16) * RW);
+        issue_tile(qb, 16 * TOK - 1, stage, p, lane, (H - 16) * RW * 2);
       } else {
         const int t = ik - 1;
         const char* rb = reinterpret_cast<const char*>(cache + next_row * RW);
@@ -172,7 +186,10 @@ decode_core_ring_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
   }
 
   // -------------------------------------------------------------- consumers
-  const int cq = wave;  // column quarter: columns 128 cq .. 128 cq + 127
+  // this wave's token and columns: 16 NCB cq .. 16 NCB (cq + 1) - 1
+  const int tw = TOK == 2 ? wave >> 1 : 0, cq = TOK == 2 ? wave & 1 : wave;
+  const int tok = tok0 + tw;
+  const int qrow = 16 * tw;  // the token's rows in the query tile
   const int lr = lane & 15, lg = lane >> 4;
   // row-wise operand of k-step s < 16 in a 16-row block: row lr, chunk 4s + lg,
   // at qk_off[s & 3] + 256 (s >> 2); rope chunk 4(s - 16) + lg at qk_rope[s - 16]
@@ -213,9 +230,10 @@ decode_core_ring_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
       const char* st = lds + (gt % NST) * ST_BYTES;
 #pragma unroll
       for (int s = 0; s < 16; ++s)
-        qf[s] = *reinterpret_cast<const bf16x8_t*>(st + qk_off[s & 3] + 256 * (s >> 2));
-      qf[16] = *reinterpret_cast<const bf16x8_t*>(st + qk_rope0);
-      qf[17] = *reinterpret_cast<const bf16x8_t*>(st + qk_rope1);
+        qf[s] = *reinterpret_cast<const bf16x8_t*>(st + qrow * 1024 + qk_off[s & 3] +
+                                                    256 * (s >> 2));
+      qf[16] = *reinterpret_cast<const bf16x8_t*>(st + qrow * 128 + qk_rope0);
+      qf[17] = *reinterpret_cast<const bf16x8_t*>(st + qrow * 128 + qk_rope1);
       ++gt;
     }
     m_run = -INFINITY;
@@ -287,7 +305,7 @@ decode_core_ring_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
       // ---- O^T += C^T . P^T over this wave's column blocks 8 cq .. 8 cq + 7
 #pragma unroll
       for (int j = 0; j < NCB; ++j) {
-        const int q = 2 * cq + j / 4, t = j % 4;
+        const int q = NCB / 4 * cq + j / 4, t = j % 4;
         const int off = pv_e[t] - (q & 1) * pv_d + 128 * q;
         typedef __attribute__((address_space(3))) s16x4_t* lptr;
         const s16x4_t c0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lptr)(st + off));
@@ -303,7 +321,7 @@ decode_core_ring_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
     const int b = wk.b;
     if (wk.nseg == 1) {
       const float inv = 1.f / l;
-      bf16* dst = o_lat + ((int64_t)(b * q_len + tok) * H + gh) * DC + 128 * cq + 4 * lg;
+      bf16* dst = o_lat + ((int64_t)(b * q_len + tok) * H + gh) * DC + 16 * NCB * cq + 4 * lg;
 #pragma unroll
       for (int j = 0; j < NCB; ++j) {
         uint2 pk;
@@ -315,7 +333,7 @@ decode_core_ring_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
       // partial of this segment: unnormalised sums (this wave's quarter) and,
       // from the first wave, the (max, sum) pair of each head
       const int64_t slot = (int64_t)tok * nseg_total + wk.pidx;
-      float* pacc = acc + (slot * H + gh) * DC + 128 * cq + 4 * lg;
+      float* pacc = acc + (slot * H + gh) * DC + 16 * NCB * cq + 4 * lg;
 #pragma unroll
       for (int j = 0; j < NCB; ++j)
         *reinterpret_cast<float4*>(pacc + 16 * j) = make_float4(o[j][0], o[j][1], o[j][2], o[j][3]);
@@ -330,13 +348,20 @@ decode_core_ring_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
 
 }  // namespace decr
 
+int decode_core_ring_tokens(int q_len) { return q_len % 2 == 0 ? 2 : 1; }
+
 void decode_core_ring(const bf16* q_cat, const bf16* cache, const DecodeMeta& m, int parts,
                       const TokenSplit& tk, float* acc, float* ml, bf16* o_lat, const Dims& d,
                       hipStream_t st) {
-  const int hg = d.H / 16 * tk.q_len;
-  const int blocks = (parts + decr::kXcds - 1) / decr::kXcds * decr::kXcds * hg;
-  decr::decode_core_ring_k<<<blocks, decr::NTHR, 0, st>>>(q_cat, cache, m, acc, ml, o_lat, d.H,
-                                                          parts, tk.q_len, tk.nseg_total);
+  const int tok = decode_core_ring_tokens(tk.q_len);
+  const int ng = d.H / 16 * tk.q_len / tok;
+  const int blocks = (parts + decr::kXcds - 1) / decr::kXcds * decr::kXcds * ng;
+  if (tok == 2)
+    decr::decode_core_ring_k<2><<<blocks, decr::NTHR, 0, st>>>(q_cat, cache, m, acc, ml, o_lat,
+                                                               d.H, parts, tk.q_len, tk.nseg_total);
+  else
+    decr::decode_core_ring_k<1><<<blocks, decr::NTHR, 0, st>>>(q_cat, cache, m, acc, ml, o_lat,
+                                                               d.H, parts, tk.q_len, tk.nseg_total);
 }
 
 }  // namespace mla

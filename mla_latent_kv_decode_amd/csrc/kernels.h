@@ -202,6 +202,9 @@ void decode_core_ring8(const bf16* q_cat, const uint8_t* cache, const DecodeMeta
 // persistent workgroups per (token, head group).  Partials as for the generic
 // core, except that a sequence contained in one segment is normalised and
 // written to o_lat (B * q_len, H, 512) directly.
+// tokens of a sequence one workgroup of the ring core covers (2 for an even
+// q_len: the part's rows then stream once per token pair)
+int decode_core_ring_tokens(int q_len);
 void decode_core_ring(const bf16* q_cat, const bf16* cache, const DecodeMeta& m, int parts,
                       const TokenSplit& tk, float* acc, float* ml, bf16* o_lat, const Dims& d,
                       hipStream_t st);

@@ -331,7 +331,10 @@ int max_parts(const mla_ctx* h, int64_t total_rows, int q_len = 1) {
                           ? std::max<int64_t>(1, (int64_t)h->n_cu /
                                                      (h->d.H / mla::decode_core_wide_heads() *
                                                       q_len))
-                          : std::max<int64_t>(1, (int64_t)h->n_cu / (h->d.H / 16 * q_len));
+                          : std::max<int64_t>(1, (int64_t)h->n_cu /
+                                                     (h->d.H / 16 * q_len /
+                                                      (h->kv8 ? 1 : mla::decode_core_ring_tokens(
+                                                                        q_len))));
   if (p > wgs) p = wgs;
   if (p < 1) p = 1;
   return (int)p;
