@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 4
+#define MLA_ABI_VERSION 5
 
 typedef enum mla_status {
   MLA_OK = 0,
@@ -100,13 +100,27 @@ typedef struct mla_config {
   float softmax_scale; /* 0 -> 1/sqrt(dn + dr) */
   int32_t dtype;     /* mla_dtype: storage type of every tensor (but see kv_storage) */
   int32_t kv_storage; /* mla_kv_storage: format of the latent cache rows */
+  /* YaRN context extension of the RoPE frequencies (the C-engine notes name
+   * YaRN without a formula; read as the published YaRN "NTK-by-parts"
+   * interpolation): with rope_scale = s > 1, pair i of base frequency
+   * theta_i = base^(-2i/dr) turns r_i = rope_orig_max * theta_i / (2 pi)
+   * times over the original context; gamma = clamp((r_i - yarn_beta_slow) /
+   * (yarn_beta_fast - yarn_beta_slow), 0, 1) and the frequency used is
+   * (1 - gamma) theta_i / s + gamma theta_i.  rope_scale <= 1 (0 included):
+   * plain RoPE, the other three fields unused.  YaRN's attention temperature
+   * is a factor on softmax_scale, set by the caller. */
+  float rope_scale;
+  int32_t rope_orig_max;  /* original context length, >= 1 when rope_scale > 1 */
+  float yarn_beta_fast;   /* e.g. 32 */
+  float yarn_beta_slow;   /* e.g. 1; 0 <= slow < fast */
 } mla_config;
 
 typedef struct mla_ctx* mla_handle;
 
 /* Host-only check of a configuration: MLA_OK, MLA_ERR_INVALID_ARG (cfg NULL,
  * a dimension <= 0 other than qk_rope/q_lora, a negative one, unknown dtype,
- * non-finite or non-positive base/eps, unknown kv_storage) or MLA_ERR_SHAPE
+ * non-finite or non-positive base/eps, unknown kv_storage, rope_scale > 1 with
+ * rope_orig_max < 1 or not 0 <= yarn_beta_slow < yarn_beta_fast) or MLA_ERR_SHAPE
  * (odd qk_rope, qk_rope > 128, kv_lora > 1024, v_head > 256, FP8 rows for a
  * layer outside the FP8 shapes).  Makes no HIP call; mla_create runs it
  * first. */

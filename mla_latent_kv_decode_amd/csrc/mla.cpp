@@ -678,6 +678,11 @@ int mla_config_check(const mla_config* c) {
   if (c->qk_rope > 2 * mla::kMaxRopePairs) return MLA_ERR_SHAPE;
   if (c->kv_storage != MLA_KV_DTYPE && c->kv_storage != MLA_KV_FP8_E4M3)
     return MLA_ERR_INVALID_ARG;
+  if (!isfinite(c->rope_scale)) return MLA_ERR_INVALID_ARG;
+  if (c->rope_scale > 1.f &&
+      (c->rope_orig_max < 1 || !isfinite(c->yarn_beta_fast) || !isfinite(c->yarn_beta_slow) ||
+       !(c->yarn_beta_slow >= 0.f) || !(c->yarn_beta_fast > c->yarn_beta_slow)))
+    return MLA_ERR_INVALID_ARG;
   if (c->kv_storage == MLA_KV_FP8_E4M3) {
     // the FP8 rows are read by the 16-head-group MFMA core only
     if (c->dtype != MLA_BF16 || c->kv_lora != 512 || c->qk_rope != 64 || c->n_heads % 16 ||
@@ -820,8 +825,20 @@ int mla_create(const mla_config* cfg, void* stream, mla_handle* out) {
   d.dv = cfg->v_head; d.dc = cfg->kv_lora; d.dq = cfg->q_lora; d.R = d.dc + d.dr;
   d.rope_base = cfg->rope_base; d.eps = cfg->rms_eps;
   d.scale = cfg->softmax_scale > 0.f ? cfg->softmax_scale : 1.0f / sqrtf((float)(d.dn + d.dr));
-  for (int i = 0; i < d.dr / 2; ++i)
-    h->rope.theta[i] = pow((double)cfg->rope_base, -2.0 * i / (double)d.dr);
+  for (int i = 0; i < d.dr / 2; ++i) {
+    // RoPE frequency of pair i, YaRN-interpolated for rope_scale > 1
+    const double th = pow((double)cfg->rope_base, -2.0 * i / (double)d.dr);
+    double f = th;
+    if (cfg->rope_scale > 1.f) {
+      const double s = cfg->rope_scale;
+      const double turns = cfg->rope_orig_max * th / (2.0 * M_PI);
+      const double g = std::min(1.0, std::max(0.0, (turns - cfg->yarn_beta_slow) /
+                                                       (double)(cfg->yarn_beta_fast -
+                                                                cfg->yarn_beta_slow)));
+      f = (1.0 - g) * th / s + g * th;
+    }
+    h->rope.theta[i] = (float)f;
+  }
   int ncu = 0;
   if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
       ncu > 0)

@@ -39,7 +39,9 @@ class MLAConfig(ctypes.Structure):
                 ("v_head", ctypes.c_int32), ("kv_lora", ctypes.c_int32),
                 ("q_lora", ctypes.c_int32), ("rope_base", ctypes.c_float),
                 ("rms_eps", ctypes.c_float), ("softmax_scale", ctypes.c_float),
-                ("dtype", ctypes.c_int32), ("kv_storage", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("kv_storage", ctypes.c_int32),
+                ("rope_scale", ctypes.c_float), ("rope_orig_max", ctypes.c_int32),
+                ("yarn_beta_fast", ctypes.c_float), ("yarn_beta_slow", ctypes.c_float)]
 
 
 class MLADecodeArgs(ctypes.Structure):
@@ -147,7 +149,11 @@ def make_config(dims, dtype: str, softmax_scale: float = 0.0, kv: str = "dtype")
     return MLAConfig(dims.hidden, dims.n_heads, dims.qk_nope, dims.qk_rope, dims.v_head,
                      dims.kv_lora, dims.q_lora, float(dims.rope_base), float(dims.rms_eps),
                      float(softmax_scale), MLA_BF16 if dtype == "bf16" else MLA_F32,
-                     MLA_KV_FP8_E4M3 if kv == "fp8" else MLA_KV_DTYPE)
+                     MLA_KV_FP8_E4M3 if kv == "fp8" else MLA_KV_DTYPE,
+                     float(getattr(dims, "rope_scale", 1.0)),
+                     int(getattr(dims, "rope_orig_max", 4096)),
+                     float(getattr(dims, "yarn_beta_fast", 32.0)),
+                     float(getattr(dims, "yarn_beta_slow", 1.0)))
 
 
 def _i32(a):

@@ -42,6 +42,10 @@ class LayerDims:
     q_lora: int = 0
     rope_base: float = 10000.0
     rms_eps: float = 1e-6
+    rope_scale: float = 1.0        # YaRN factor; 1 = plain RoPE
+    rope_orig_max: int = 4096
+    yarn_beta_fast: float = 32.0
+    yarn_beta_slow: float = 1.0
 
     @property
     def row(self) -> int:

@@ -23,7 +23,12 @@ cache with one scale per row, read back as the cache would hand it out) and
 ``oracle.paged`` (the row lookup of a cache kept in pages named by a block
 table).
 
-Parity status: every function here is pinned by the ``-m "not gpu"`` tests in
+YaRN (``rope_theta`` with a context-extension factor > 1) is named on the
+pages without a formula; its branch follows the published YaRN method
+(outside the pages) and is pinned only to that method's defining properties:
+parity unpinned with respect to the pages.
+
+Parity status: apart from that branch, every function here is pinned by the ``-m "not gpu"`` tests in
 ``tests/test_oracle_pins.py`` (brute force, identities, closed forms, special
 cases); no function is "parity unpinned".
 """

@@ -50,6 +50,16 @@ class MLAShape:
     rope_base: float = 10000.0
     rms_eps: float = 1e-6
     softmax_scale: float = 0.0  # 0 -> 1/sqrt(qk_nope + qk_rope)
+    # YaRN context extension of RoPE (see rope_theta): factor 1 = plain RoPE
+    rope_scale: float = 1.0
+    rope_orig_max: int = 4096
+    yarn_beta_fast: float = 32.0
+    yarn_beta_slow: float = 1.0
+
+    @property
+    def theta(self) -> np.ndarray:
+        return rope_theta(self.qk_rope, self.rope_base, self.rope_scale, self.rope_orig_max,
+                          self.yarn_beta_fast, self.yarn_beta_slow)
 
     @property
     def row(self) -> int:
@@ -78,19 +88,47 @@ def rms_norm(a, gamma, eps: float) -> np.ndarray:
     return a / np.sqrt(ms + eps) * _f64(gamma)
 
 
-def rope(x, pos, base: float) -> np.ndarray:
+def rope_theta(d: int, base: float, scale: float = 1.0, orig_max: int = 4096,
+               beta_fast: float = 32.0, beta_slow: float = 1.0) -> np.ndarray:
+    """Per-pair rotation frequencies theta_i (i < d / 2).
+
+    Plain RoPE (MLA post, section 3.7): theta_i = base^(-2i/d).  With a
+    context-extension factor scale > 1, YaRN, which the C-engine notes ("Deepseek
+    V2 Lite Inference Engine in C", MLA notes) name without a formula; the
+    reading here is the published YaRN method ("YaRN: Efficient Context
+    Window Extension of Large Language Models", Peng et al. 2023, section
+    3.2, "NTK-by-parts" interpolation): pair i turns r_i = orig_max theta_i /
+    (2 pi) times over the original context; pairs that turn fewer than
+    beta_slow times are interpolated (theta_i / scale), pairs that turn more
+    than beta_fast times are kept, and in between the two blend linearly in
+    r_i:  gamma = clip((r_i - beta_slow) / (beta_fast - beta_slow), 0, 1),
+    theta'_i = (1 - gamma) theta_i / scale + gamma theta_i.  (YaRN's attention
+    temperature is a factor on the softmax scale, left to the caller.)
+    """
+    theta = base ** (-np.arange(0, d, 2, dtype=F64) / d)
+    if scale <= 1.0:
+        return theta
+    r = orig_max * theta / (2.0 * np.pi)
+    gamma = np.clip((r - beta_slow) / (beta_fast - beta_slow), 0.0, 1.0)
+    return (1.0 - gamma) * theta / scale + gamma * theta
+
+
+def rope(x, pos, base: float, theta=None) -> np.ndarray:
     """Rotary position embedding on the last axis.
 
     MLA post, section 3.7 Code (``RoPE`` / ``apply_rope``): pair i of the last
     axis, (x[2i], x[2i+1]), is read as the complex number x[2i] + j x[2i+1] and
-    multiplied by exp(j * pos * theta_i) with theta_i = base^(-2i/d), d even.
+    multiplied by exp(j * pos * theta_i) with theta_i = base^(-2i/d), d even
+    (or the given per-pair frequencies ``theta``, e.g. from ``rope_theta``).
     ``pos`` broadcasts against ``x.shape[:-1]``.
     """
     x = _f64(x)
     d = x.shape[-1]
     if d % 2:
         raise ValueError("RoPE needs an even dimension")
-    theta = base ** (-np.arange(0, d, 2, dtype=F64) / d)
+    if theta is None:
+        theta = base ** (-np.arange(0, d, 2, dtype=F64) / d)
+    theta = _f64(theta)
     ang = _f64(pos)[..., None] * theta
     cos, sin = np.cos(ang), np.sin(ang)
     u, v = x[..., 0::2], x[..., 1::2]
@@ -114,7 +152,7 @@ def latent_rows(x, pos, w_kva, kv_norm_g, shape: MLAShape) -> np.ndarray:
     a = x @ _f64(w_kva).T
     dc = shape.kv_lora
     c = rms_norm(a[:, :dc], kv_norm_g, shape.rms_eps)
-    k_r = rope(a[:, dc:], _f64(pos), shape.rope_base)
+    k_r = rope(a[:, dc:], _f64(pos), shape.rope_base, shape.theta)
     return np.concatenate([c, k_r], axis=1)
 
 
@@ -135,7 +173,7 @@ def query_heads(x, pos, w: dict, shape: MLAShape):
         q = x @ _f64(w["w_q"]).T
     q = q.reshape(x.shape[0], H, dn + dr)
     q_n = q[..., :dn]
-    q_r = rope(q[..., dn:], _f64(pos)[:, None], shape.rope_base)
+    q_r = rope(q[..., dn:], _f64(pos)[:, None], shape.rope_base, shape.theta)
     return q_n, q_r
 
 

@@ -16,7 +16,9 @@ APPEND_CHUNK = 8192
 def oracle_shape(d: synth.LayerDims) -> O.MLAShape:
     return O.MLAShape(hidden=d.hidden, n_heads=d.n_heads, qk_nope=d.qk_nope, qk_rope=d.qk_rope,
                       v_head=d.v_head, kv_lora=d.kv_lora, q_lora=d.q_lora,
-                      rope_base=d.rope_base, rms_eps=d.rms_eps)
+                      rope_base=d.rope_base, rms_eps=d.rms_eps, rope_scale=d.rope_scale,
+                      rope_orig_max=d.rope_orig_max, yarn_beta_fast=d.yarn_beta_fast,
+                      yarn_beta_slow=d.yarn_beta_slow)
 
 
 def tol(dtype: str) -> float:

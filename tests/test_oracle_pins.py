@@ -512,3 +512,40 @@ def test_paged_shared_prefix_and_page_permutation():
     # the row of position t: page t // P of the table, offset t % P
     assert PG.row_index(table, P, 0, 9) == 1 * P + 1
     assert PG.row_index(table, P, 1, 4) == 5 * P + 0
+
+
+# ---------------------------------------------------------------- YaRN frequencies
+def test_yarn_frequencies_properties():
+    """rope_theta with a context-extension factor s (the published YaRN
+    interpolation; the pages only name YaRN): factor 1 is plain RoPE; pairs
+    that turn at least beta_fast times over the original context keep their
+    frequency; pairs that turn at most beta_slow times are slowed by exactly
+    s, so over the extended context s L they turn as often as before over L;
+    every frequency lies between theta / s and theta and they stay ordered."""
+    d, base, L = 64, 10000.0, 4096
+    plain = base ** (-np.arange(0, d, 2) / d)
+    assert np.array_equal(O.rope_theta(d, base), plain)
+    assert np.array_equal(O.rope_theta(d, base, 1.0, L), plain)
+    for s in (4.0, 40.0):
+        th = O.rope_theta(d, base, s, L, 32.0, 1.0)
+        turns = L * plain / (2 * np.pi)
+        fast, slow = turns >= 32.0, turns <= 1.0
+        assert fast.any() and slow.any() and (~fast & ~slow).any()
+        assert np.array_equal(th[fast], plain[fast])
+        assert np.allclose(th[slow] * s * L, plain[slow] * L, rtol=1e-14)
+        assert np.all(th <= plain * (1 + 1e-15)) and np.all(th >= plain / s * (1 - 1e-15))
+        assert np.all(np.diff(th) < 0)
+        # a larger factor never speeds a pair up
+        assert np.all(O.rope_theta(d, base, 2 * s, L) <= th * (1 + 1e-15))
+
+
+def test_yarn_rope_keeps_relative_positions():
+    """Scores of RoPE-rotated vectors depend only on the position difference,
+    whatever the per-pair frequencies (here YaRN's)."""
+    rng = np.random.default_rng(12)
+    th = O.rope_theta(16, 10000.0, 40.0, 4096)
+    q, k = rng.standard_normal(16), rng.standard_normal(16)
+    def score(pq, pk):
+        return float(O.rope(q, pq, 10000.0, th) @ O.rope(k, pk, 10000.0, th))
+    assert abs(score(9000, 8000) - score(1000, 0)) < 1e-9
+    assert abs(score(5, 5) - float(q @ k)) < 1e-12
