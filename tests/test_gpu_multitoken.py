@@ -143,3 +143,44 @@ def test_multitoken_long_sequences_split():
     least q_len rows in each sequence's last segment."""
     case = MTCase(synth.V2_LITE, "bf16", 0.02, [4095, 4096, 4097, 8190, 33], 4, keep=[0, 3, 4])
     case.check(case.run(), [0, 3, 4])
+
+
+def test_multitoken_max_q_len():
+    """q_len = 16, the largest allowed: sequences with no earlier rows (all
+    16 rows are new tokens) and longer ones."""
+    case = MTCase(synth.V2_LITE, "bf16", 0.02, [0, 1, 15, 16, 17, 300], 16)
+    case.check(case.run())
+
+
+def test_multitoken_fp8_paged_append():
+    """FP8 rows, 32-row pages in random order, two new tokens appended by the
+    call: the rows written and the outputs equal the contiguous call's, and
+    the outputs match the oracle reading its quantised rows."""
+    import torch
+    P, q = 32, 2
+    case = MTCase(synth.V2_LITE, "bf16", 0.02, [0, 30, 31, 32, 95, 400], q, kv="fp8")
+    need = PG.pages_needed(case.seq_len, P)
+    perm = np.random.default_rng(4).permutation(int(need.sum()))
+    table = np.zeros((case.B, int(need.max())), dtype=np.int32)
+    k = 0
+    for b, m in enumerate(need):
+        table[b, :m] = perm[k:k + m]
+        k += m
+    pool = case.layer.new_cache(int(need.sum()) * P)
+    new_p, new_c = [], []
+    for b in range(case.B):
+        t = np.arange(int(case.seq_len[b]))
+        pool[torch.as_tensor(PG.row_index(table, P, b, t), device="cuda")] = \
+            case.cache[torch.as_tensor(int(case.seq_off[b]) + t, device="cuda")]
+        new_p.append(PG.row_index(table, P, b, t[-q:]))
+        new_c.append(int(case.seq_off[b]) + t[-q:])
+    new_p = torch.as_tensor(np.concatenate(new_p), device="cuda")
+    new_c = torch.as_tensor(np.concatenate(new_c), device="cuda")
+    pool[new_p] = 0
+    case.cache[new_c] = 0
+    y_c = case.run(append=True)
+    y_p = host(case.layer.decode_ex(case.x(), case.seq_len, pool, q_len=q, block_table=table,
+                                    page_rows=P, append=True))
+    assert torch.equal(pool[new_p], case.cache[new_c])
+    assert np.array_equal(y_p, y_c)
+    case.check(y_p)

@@ -141,3 +141,10 @@ def test_paged_decode_b64_full_size():
     pick = sorted({int(np.argmin(lens)), int(np.argmax(lens))})
     case = DecodeCase(w.dims, "bf16", w.weight_std, lens, random_gains=False, keep=pick)
     _paged_vs_contiguous(case, 64, 12, pick)
+
+
+def test_paged_decode_large_pages():
+    """4096-row pages: a sequence filling exactly one page, one crossing into
+    a second, short ones sharing nothing."""
+    case = DecodeCase(synth.V2_LITE, "bf16", 0.02, [4095, 4096, 10, 5000], keep=[0, 1, 3])
+    _paged_vs_contiguous(case, 4096, 13, [0, 1, 3])
