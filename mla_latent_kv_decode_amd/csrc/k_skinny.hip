@@ -36,13 +36,20 @@ constexpr int NT = 32;                    // output columns per block
 constexpr int KC = 256;                   // K per chunk
 constexpr int ROWB = KC * 2;              // 512 bytes per row piece
 constexpr int W_OFF = 0, A_OFF = NT * ROWB;
-constexpr int ST_BYTES = (NT + 16) * ROWB;  // 24 KB per stage
-constexpr int NST = 3;                    // 72 KB: two blocks per compute unit
-constexpr int NCOPY = (NT + 16) / 2;      // 24 one-KB copies per chunk
-constexpr int CPW = NCOPY / NWV;          // 6 per wave
+constexpr int NST = 3;                    // stages
 constexpr int kXcds = 8;
-static_assert(NCOPY % NWV == 0, "copies split evenly over the waves");
-static_assert((NST - 2) * CPW <= 63, "copies in flight fit the vmcnt field");
+// MR activation rows per block (16: 24 KB stages, two blocks per compute
+// unit; 32: 32 KB stages, one block).  A block copies (NT + MR) rows over all
+// of K, so the copy volume of a launch is (N / NT) (M / MR) (NT + MR) K 2
+// bytes: taller tiles re-read the weights fewer times.
+template <int MR>
+struct Tile {
+  static constexpr int ST_BYTES = (NT + MR) * ROWB;
+  static constexpr int NCOPY = (NT + MR) / 2;  // one-KB copies per chunk
+  static constexpr int CPW = NCOPY / NWV;
+  static_assert(NCOPY % NWV == 0, "copies split evenly over the waves");
+  static_assert((NST - 2) * CPW <= 63, "copies in flight fit the vmcnt field");
+};
 
 // copy i of chunk k0 (rows 2i, 2i + 1 of the stage: weight rows first, then
 // activation rows), lanes 0-31 on the first row, 32-63 on the second
@@ -56,16 +63,17 @@ __device__ __forceinline__ void chunk_copy(int i, const bf16* W, int64_t ldw, in
   dma16(src + k0 + 8 * c, stage + (uint32_t)i * 1024);
 }
 
-template <class Epi>
+template <int MR, class Epi>
 __global__ void __launch_bounds__(NWV * 64)
 gemm_stream_k(const bf16* __restrict__ A, int64_t lda, const bf16* __restrict__ W, int64_t ldw,
               int M, int N, int K, int mtiles, Epi epi) {
+  constexpr int ST_BYTES = Tile<MR>::ST_BYTES, CPW = Tile<MR>::CPW, NMB = MR / 16;
   __shared__ __attribute__((aligned(1024))) char lds[NST * ST_BYTES];
   // block -> (column tile, row tile); the row tiles of a column tile share an XCD
   const int bid = blockIdx.x;
   const int mt = (bid / kXcds) % mtiles;
   const int ntile = (bid / (kXcds * mtiles)) * kXcds + bid % kXcds;
-  const int n0 = ntile * NT, m0 = 16 * mt;
+  const int n0 = ntile * NT, m0 = MR * mt;
   if (n0 >= N) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -81,7 +89,11 @@ gemm_stream_k(const bf16* __restrict__ A, int64_t lda, const bf16* __restrict__ 
 #pragma unroll 1
   for (int ch = 0; ch < NST - 1 && ch < nchunk; ++ch) issue(ch);
 
-  f32x4_t acc[2] = {(f32x4_t){0.f, 0.f, 0.f, 0.f}, (f32x4_t){0.f, 0.f, 0.f, 0.f}};
+  f32x4_t acc[NMB][2];
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
   static_assert(NST == 3, "the waits below assume at most one chunk issued after the awaited one");
 #pragma unroll 1
   for (int ch = 0; ch < nchunk; ++ch) {
@@ -93,13 +105,18 @@ gemm_stream_k(const bf16* __restrict__ A, int64_t lda, const bf16* __restrict__ 
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int c = 4 * (wave + 4 * u) + lg;  // 16-byte chunk of this lane's operands
-      const bf16x8_t af =
-          *reinterpret_cast<const bf16x8_t*>(st + A_OFF + lr * ROWB + 16 * (c ^ lr));
+      bf16x8_t af[NMB];
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb)
+        af[mb] = *reinterpret_cast<const bf16x8_t*>(st + A_OFF + (16 * mb + lr) * ROWB +
+                                                    16 * (c ^ lr));
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         const bf16x8_t wf = *reinterpret_cast<const bf16x8_t*>(
             st + W_OFF + (16 * nb + lr) * ROWB + 16 * (c ^ lr));
-        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, wf, acc[nb], 0, 0, 0);
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mb], wf, acc[mb][nb], 0, 0, 0);
       }
     }
   }
@@ -108,20 +125,26 @@ gemm_stream_k(const bf16* __restrict__ A, int64_t lda, const bf16* __restrict__ 
   __syncthreads();  // the ring is free
   float* red = reinterpret_cast<float*>(lds);
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb)
+  for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) red[(wave * 16 + 4 * lg + i) * NT + 16 * nb + lr] = acc[nb][i];
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        red[(wave * MR + 16 * mb + 4 * lg + i) * NT + 16 * nb + lr] = acc[mb][nb][i];
   __syncthreads();
-  const int t = threadIdx.x;  // row t / 16, columns 2 (t % 16), + 1
-  const int row = t >> 4, col = 2 * (t & 15);
-  float v0 = 0.f, v1 = 0.f;
 #pragma unroll
-  for (int w = 0; w < NWV; ++w) {
-    const float2 p = *reinterpret_cast<const float2*>(red + (w * 16 + row) * NT + col);
-    v0 += p.x;
-    v1 += p.y;
+  for (int e = 0; e < NMB; ++e) {
+    const int t = threadIdx.x + 256 * e;  // row t / 16, columns 2 (t % 16), + 1
+    const int row = t >> 4, col = 2 * (t & 15);
+    float v0 = 0.f, v1 = 0.f;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) {
+      const float2 p = *reinterpret_cast<const float2*>(red + (w * MR + row) * NT + col);
+      v0 += p.x;
+      v1 += p.y;
+    }
+    if (m0 + row < M && n0 + col < N) epi(m0 + row, n0 + col, v0, v1);
   }
-  if (m0 + row < M && n0 + col < N) epi(m0 + row, n0 + col, v0, v1);
 }
 
 // epilogues on the column pair (c, c + 1) of row r (c even; c + 1 < N)
@@ -173,13 +196,29 @@ struct EpiQuery {
   }
 };
 
+int cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+    return 256;
+  return n;
+}
+
+// 32-row blocks (one per compute unit) where they still occupy three quarters
+// of the compute units: fewer weight re-reads; else 16-row blocks (two per
+// compute unit).
 template <class Epi>
 void launch_stream(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int M, int N, int K,
                    const Epi& epi, hipStream_t st) {
-  const int mtiles = (M + 15) / 16;
   const int ntiles = (N + NT - 1) / NT;
-  const int blocks = (ntiles + kXcds - 1) / kXcds * kXcds * mtiles;
-  gemm_stream_k<Epi><<<blocks, NWV * 64, 0, st>>>(A, lda, W, ldw, M, N, K, mtiles, epi);
+  const int nt8 = (ntiles + kXcds - 1) / kXcds * kXcds;
+  const int m32 = (M + 31) / 32;
+  if (M > 16 && ntiles * m32 * 4 >= cu_count() * 3) {
+    gemm_stream_k<32, Epi><<<nt8 * m32, NWV * 64, 0, st>>>(A, lda, W, ldw, M, N, K, m32, epi);
+    return;
+  }
+  const int mtiles = (M + 15) / 16;
+  gemm_stream_k<16, Epi><<<nt8 * mtiles, NWV * 64, 0, st>>>(A, lda, W, ldw, M, N, K, mtiles, epi);
 }
 
 // ---- projection finish: blocks [0, nab) absorbed query tiles, then nap
