@@ -157,7 +157,7 @@ combine_final_512_k(const float* __restrict__ cacc, const float* __restrict__ cm
 // VGPRs at kernel start, while phase 1 runs (rows SB .. 15 of the MFMA row
 // block are zero).  Wave w owns output columns 16 w .. 16 w + 15; o is rounded
 // to bf16.
-constexpr int SB = 8;                  // sequences per block
+constexpr int SB = 4;                  // sequences per block (256 blocks for 16 heads x 64)
 constexpr int UV_NW = 8;               // waves
 constexpr int UV_DV = 128;
 constexpr int OROW = DC * 2 + 16;      // LDS row stride in bytes (padding: no bank conflicts)
