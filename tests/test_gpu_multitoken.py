@@ -184,3 +184,18 @@ def test_multitoken_fp8_paged_append():
     assert torch.equal(pool[new_p], case.cache[new_c])
     assert np.array_equal(y_p, y_c)
     case.check(y_p)
+
+
+def test_multitoken_generic_core_f32_append():
+    """The fp32 build's generic path with the append: the call writes the
+    q_len new rows itself (zeroed first) and matches the oracle."""
+    import torch
+    q = 3
+    case = MTCase(synth.TINY, "f32", 0.05, [0, 1, 7, 40], q)
+    new = torch.as_tensor(np.concatenate([int(case.seq_off[b]) + np.arange(int(case.seq_len[b]) - q,
+                                                                           int(case.seq_len[b]))
+                                          for b in range(case.B)]), device="cuda")
+    case.cache[new] = 0
+    y = case.run(append=True)
+    assert bool(case.cache[new].abs().sum() > 0)
+    case.check(y)
