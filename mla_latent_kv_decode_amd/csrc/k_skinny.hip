@@ -21,6 +21,8 @@
 // fp32 store, or the query finish (per head: the nope part stored, the rope
 // part rotated and scaled into q_cat).  The 16-row blocks of a column tile are
 // numbered 8 apart, so they run on one XCD and share its L2 for the weights.
+#include <atomic>
+
 #include "decode_dev.h"
 #include "row_dev.h"
 
@@ -196,11 +198,17 @@ struct EpiQuery {
   }
 };
 
+// compute units of the current device, looked up once per device
 int cu_count() {
-  int dev = 0, n = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
-    return 256;
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  const bool slot = dev >= 0 && dev < 64;
+  int n = slot ? cached[dev].load(std::memory_order_relaxed) : 0;
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+    n = 256;
+  if (slot) cached[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 
