@@ -157,7 +157,7 @@ combine_final_512_k(const float* __restrict__ cacc, const float* __restrict__ cm
 // VGPRs at kernel start, while phase 1 runs (rows SB .. 15 of the MFMA row
 // block are zero).  Wave w owns output columns 16 w .. 16 w + 15; o is rounded
 // to bf16.
-constexpr int SB = 4;                  // sequences per block (256 blocks for 16 heads x 64)
+constexpr int SB_MAX = 8;              // sequences per block: 8, or 4 to fill the compute units
 constexpr int UV_NW = 8;               // waves
 constexpr int UV_DV = 128;
 constexpr int OROW = DC * 2 + 16;      // LDS row stride in bytes (padding: no bank conflicts)
@@ -206,9 +206,9 @@ __global__ void __launch_bounds__(UV_NW * 64)
 combine_uv_k(const float* __restrict__ acc, const float* __restrict__ ml,
              const float* __restrict__ cacc, const float* __restrict__ cml, DecodeMeta mt,
              int direct_single, const bf16* __restrict__ w_uv, int B, int H,
-             bf16* __restrict__ o_lat, bf16* __restrict__ o) {
+             bf16* __restrict__ o_lat, bf16* __restrict__ o, int SB) {
   __shared__ __attribute__((aligned(16))) char rows[16 * OROW];
-  const int h = blockIdx.x, b0 = blockIdx.y * SB;
+  const int h = blockIdx.x, b0 = blockIdx.y * SB;  // SB <= SB_MAX sequences
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int lr = lane & 15, lg = lane >> 4;
@@ -287,8 +287,14 @@ void decode_combine_uv(const float* acc, const float* ml, const DecodeMeta& m, i
   if (max_chunks > 1)
     cmb::combine_chunks_512_k<<<dim3(B, H, max_chunks), 256, 0, st>>>(acc, ml, m, H, cacc, cml,
                                                                         o_lat, 1, 0);
-  cmb::combine_uv_k<<<dim3(H, (B + cmb::SB - 1) / cmb::SB), cmb::UV_NW * 64, 0, st>>>(
-      acc, ml, cacc, cml, m, direct_single ? 1 : 0, w_uv, B, H, o_lat, o);
+  // 8 sequences per block when that already gives a block per compute unit,
+  // else 4 (each block reads its head's whole W_UV, so fewer, taller blocks
+  // read less; more blocks spread the reads over more compute units)
+  const int sb = (int64_t)H * ((B + cmb::SB_MAX - 1) / cmb::SB_MAX) >= device_cu_count()
+                     ? cmb::SB_MAX
+                     : cmb::SB_MAX / 2;
+  cmb::combine_uv_k<<<dim3(H, (B + sb - 1) / sb), cmb::UV_NW * 64, 0, st>>>(
+      acc, ml, cacc, cml, m, direct_single ? 1 : 0, w_uv, B, H, o_lat, o, sb);
 }
 
 }  // namespace mla

@@ -198,8 +198,10 @@ struct EpiQuery {
   }
 };
 
+}  // namespace skn
+
 // compute units of the current device, looked up once per device
-int cu_count() {
+int device_cu_count() {
   static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;
@@ -212,6 +214,8 @@ int cu_count() {
   return n;
 }
 
+namespace skn {
+
 // 32-row blocks (one per compute unit) where they still occupy three quarters
 // of the compute units: fewer weight re-reads; else 16-row blocks (two per
 // compute unit).
@@ -221,7 +225,7 @@ void launch_stream(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int M
   const int ntiles = (N + NT - 1) / NT;
   const int nt8 = (ntiles + kXcds - 1) / kXcds * kXcds;
   const int m32 = (M + 31) / 32;
-  if (M > 16 && ntiles * m32 * 4 >= cu_count() * 3) {
+  if (M > 16 && ntiles * m32 * 4 >= device_cu_count() * 3) {
     gemm_stream_k<32, Epi><<<nt8 * m32, NWV * 64, 0, st>>>(A, lda, W, ldw, M, N, K, m32, epi);
     return;
   }

@@ -141,6 +141,8 @@ void cache_write(const T* rows, const int64_t* slot, int ntok, int R, T* cache, 
 // ---- decode-step GEMMs with in-place epilogues (no split over blocks):
 // C = A W^T for M <= 64 rows and K % 512 == 0 (skinny_ok), bf16 operands.
 bool skinny_ok(int M, int N, int K);
+// compute units of the current device (cached per device)
+int device_cu_count();
 // out (bf16, row stride ldo) = alpha C
 void skinny_store(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int M, int N, int K,
                   bf16* out, int64_t ldo, float alpha, hipStream_t st);
