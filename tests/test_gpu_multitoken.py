@@ -199,3 +199,28 @@ def test_multitoken_generic_core_f32_append():
     y = case.run(append=True)
     assert bool(case.cache[new].abs().sum() > 0)
     case.check(y)
+
+
+@pytest.mark.parametrize("kv", ["dtype", "fp8"])
+def test_multitoken_paged_is_deterministic(kv):
+    """Three runs of the same two-token paged decode give the same bits (the
+    partials of a sequence are merged in slot order, independent of timing)."""
+    P, q = 64, 2
+    case = MTCase(synth.V2_LITE, "bf16", 0.02, [10, 700, 3000, 5000, 64], q, kv=kv, keep=[])
+    import torch
+    need = PG.pages_needed(case.seq_len, P)
+    table = np.zeros((case.B, int(need.max())), dtype=np.int32)
+    perm = np.random.default_rng(5).permutation(int(need.sum()))
+    k = 0
+    for b, m in enumerate(need):
+        table[b, :m] = perm[k:k + m]
+        k += m
+    pool = case.layer.new_cache(int(need.sum()) * P)
+    for b in range(case.B):
+        t = np.arange(int(case.seq_len[b]))
+        pool[torch.as_tensor(PG.row_index(table, P, b, t), device="cuda")] = \
+            case.cache[torch.as_tensor(int(case.seq_off[b]) + t, device="cuda")]
+    runs = [host(case.layer.decode_ex(case.x(), case.seq_len, pool, q_len=q, block_table=table,
+                                      page_rows=P)) for _ in range(3)]
+    assert np.array_equal(runs[0], runs[1]) and np.array_equal(runs[0], runs[2])
+    assert np.all(np.isfinite(runs[0]))
