@@ -6,7 +6,8 @@ import numpy as np
 import pytest
 
 from mla_latent_kv_decode_amd import synth
-from tests.helpers import DecodeCase, host, row_rel_err, tol
+from oracle import mla as O
+from tests.helpers import DecodeCase, host, oracle_shape, row_rel_err, tol
 
 pytestmark = pytest.mark.gpu
 
@@ -103,6 +104,28 @@ def test_v3_decode_b32_full_size_sampled():
     case = DecodeCase(w.dims, "bf16", w.weight_std, lens, random_gains=False, keep=pick)
     y = _check(case, pick, stages=True)
     assert np.all(np.isfinite(y))
+
+
+def test_v3_decode_b1_s32768_long_context():
+    """The long-context stress case of the V3 configuration: one sequence with
+    32,768 cached rows plus the new one.  Against the oracle's absorbed form
+    (pinned equal to the non-absorbed definition at V3 shapes; expanding K and
+    V for 32k rows x 128 heads in fp64 would take gigabytes): q_cat, o_lat and
+    y at the bf16 tolerance."""
+    w = synth.WORKLOADS["v3_decode_b1_s32768"]
+    lens = synth.lengths(w)
+    assert int(lens[0]) == 32768
+    case = DecodeCase(w.dims, "bf16", w.weight_std, lens, random_gains=False)
+    y, q_cat, o_lat = case.run(stages=True)
+    shp = oracle_shape(w.dims)
+    L = int(lens[0])
+    x = case.hidden[0]
+    rows = O.latent_rows(x[:L + 1], np.arange(L + 1), case.w["w_kva"], case.w["kv_norm_g"], shp)
+    ref = O.absorbed_step(x[L:L + 1], np.array([L]), rows, case.w, shp)
+    t = tol("bf16")
+    assert row_rel_err(host(y), ref["y"])[0] < t
+    assert row_rel_err(host(q_cat).reshape(1, -1), ref["q_cat"].reshape(1, -1))[0] < t
+    assert row_rel_err(host(o_lat).reshape(1, -1), ref["o_lat"].reshape(1, -1))[0] < t
 
 
 def test_ring_core_two_head_groups():
