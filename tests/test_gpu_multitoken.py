@@ -224,3 +224,12 @@ def test_multitoken_paged_is_deterministic(kv):
                                       page_rows=P)) for _ in range(3)]
     assert np.array_equal(runs[0], runs[1]) and np.array_equal(runs[0], runs[2])
     assert np.all(np.isfinite(runs[0]))
+
+
+def test_multitoken_token_pairs_two_head_groups():
+    """32 heads (two 16-head groups) and two new tokens: the paired query
+    tile takes its second token's rows H rows further on in q_cat."""
+    import dataclasses
+    dims = dataclasses.replace(synth.V2_LITE, n_heads=32)
+    case = MTCase(dims, "bf16", 0.02, [0, 31, 700, 2000], 2)
+    case.check(case.run())
