@@ -299,7 +299,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the sharded "
-              "design is described in DESIGN.md and is not run here", file=sys.stderr)
+              "design shards sequences across GPUs and is not run here", file=sys.stderr)
         sys.exit(2)
 
     import torch

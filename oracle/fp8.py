@@ -5,7 +5,7 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
 The "Multi-Head Latent Attention" post lists low-precision storage among
 DeepSeek's implementation ideas (introduction) and sizes a cache element at
 1 byte for FP8 (section 3.1 C cache); it gives no quantisation formula.
-Reading (also listed in the design doc): the latent part c (d_c values) of each
+Reading: the latent part c (d_c values) of each
 cached row is stored as OCP FP8 E4M3 codes with one fp32 scale per row,
     s = max_i |c_i| / 448   (s = 1 for an all-zero row),
     code_i = E4M3(c_i / s)  (round to nearest, ties to even, saturating at +-448),

@@ -11,8 +11,7 @@ Notation (row-major, one row per token):
   dq q_lora_rank (0 = the query is projected directly from the hidden state)
   R = dc + dr               one cached latent row: [c_kv | k_rope]
 
-Readings of the pages where they are silent or garbled (each also listed in
-DESIGN.md):
+Readings of the pages where they are silent or garbled:
   * RMSNorm is the textbook x / sqrt(mean(x^2) + eps) * gamma; eps = 1e-6.
     It is applied to the dc latent entries only; k_rope gets RoPE only.
   * RoPE rotates adjacent pairs (2i, 2i+1) as complex numbers by

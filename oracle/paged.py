@@ -6,7 +6,7 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
 "Transformer and KV Cache Basics" (KV Cache section, Engineering) keeps its
 cache in one preallocated buffer per sequence and names a growing memory pool
 as the next step; the "Multi-Head Latent Attention" post's code (section 3.7)
-also preallocates.  Reading (also listed in the design doc): a paged cache is a
+also preallocates.  Reading: a paged cache is a
 pool of rows cut into pages of P rows (page k = pool rows [k P, (k + 1) P));
 each sequence lists its pages in a block table, and its position t is pool row
     table[b][t // P] * P + t % P.
