@@ -344,6 +344,17 @@ int mla_decode_plan(int32_t B, const int32_t* seq_len, int32_t max_parts, int32_
                     int32_t* seg_b, int32_t* seg_r0, int32_t* seg_r1, int32_t* n_parts,
                     int32_t* n_segs);
 
+/* mla_decode_plan for q_len new tokens per sequence (mla_decode_ex): the
+ * same work list, except that a sequence's last segment keeps at least q_len
+ * rows, so every new token's causal limit (its own position) falls in that
+ * segment and the segments before it are whole for every token.
+ *   q_len: 1 .. MLA_MAX_Q_LEN; seq_len[b] >= q_len (cached rows + new rows).
+ * Other arguments as mla_decode_plan; q_len = 1 gives its result.  Errors:
+ * INVALID_ARG as there, or q_len out of range, or a length below q_len. */
+int mla_decode_plan_tokens(int32_t B, const int32_t* seq_len, int32_t q_len, int32_t max_parts,
+                           int32_t* part_begin, int32_t* seg_b, int32_t* seg_r0, int32_t* seg_r1,
+                           int32_t* n_parts, int32_t* n_segs);
+
 /* Workspace bytes mla_prefill needs for T new tokens in B sequences whose
  * caches hold total_key_rows rows in all after the append. */
 size_t mla_prefill_workspace_bytes(mla_handle h, int32_t T, int32_t B,

@@ -1114,13 +1114,20 @@ size_t mla_decode_step_workspace_bytes(mla_handle h, int32_t B, int64_t total_ro
 int mla_decode_plan(int32_t B, const int32_t* seq_len, int32_t max_parts, int32_t* part_begin,
                     int32_t* seg_b, int32_t* seg_r0, int32_t* seg_r1, int32_t* n_parts,
                     int32_t* n_segs) {
+  return mla_decode_plan_tokens(B, seq_len, 1, max_parts, part_begin, seg_b, seg_r0, seg_r1,
+                                n_parts, n_segs);
+}
+
+int mla_decode_plan_tokens(int32_t B, const int32_t* seq_len, int32_t q_len, int32_t max_parts,
+                           int32_t* part_begin, int32_t* seg_b, int32_t* seg_r0, int32_t* seg_r1,
+                           int32_t* n_parts, int32_t* n_segs) {
   if (B <= 0 || max_parts <= 0 || !seq_len || !part_begin || !seg_b || !seg_r0 || !seg_r1 ||
-      !n_parts || !n_segs)
+      !n_parts || !n_segs || q_len < 1 || q_len > MLA_MAX_Q_LEN)
     return MLA_ERR_INVALID_ARG;
   for (int b = 0; b < B; ++b)
-    if (seq_len[b] < 1) return MLA_ERR_INVALID_ARG;
+    if (seq_len[b] < q_len) return MLA_ERR_INVALID_ARG;
   SpanPlan plan;
-  const int parts = plan_spans(B, seq_len, max_parts, &plan);
+  const int parts = plan_spans(B, seq_len, max_parts, &plan, q_len);
   for (int p = 0; p <= parts; ++p) part_begin[p] = plan.part_begin[p];
   for (size_t i = 0; i < plan.segs.size(); ++i) {
     seg_b[i] = plan.segs[i].b;

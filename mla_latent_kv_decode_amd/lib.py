@@ -107,6 +107,9 @@ _SIGS = {
     "mla_decode_stage_offsets": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.c_int64,
                                                 ctypes.POINTER(ctypes.c_size_t),
                                                 ctypes.POINTER(ctypes.c_size_t)]),
+    "mla_decode_plan_tokens": (ctypes.c_int, [ctypes.c_int32, _I32P, ctypes.c_int32,
+                                              ctypes.c_int32, _I32P, _I32P, _I32P, _I32P,
+                                              _I32P, _I32P]),
     "mla_decode_plan": (ctypes.c_int, [ctypes.c_int32, _I32P, ctypes.c_int32, _I32P, _I32P,
                                        _I32P, _I32P, _I32P, _I32P]),
     "mla_core_timing": (ctypes.c_int, [_P, ctypes.c_int32]),
@@ -433,9 +436,9 @@ class MLALayer:
         return out
 
 
-def decode_plan(seq_len, max_parts: int):
-    """The split-S work list for these lengths (host only): returns
-    (part_begin, seg_b, seg_r0, seg_r1) as int32 arrays."""
+def decode_plan(seq_len, max_parts: int, q_len: int = 1):
+    """The split-S work list for these lengths (host only), q_len new tokens
+    per sequence: returns (part_begin, seg_b, seg_r0, seg_r1) as int32 arrays."""
     lib = load()
     sl, slp = _i32(seq_len)
     B = len(sl)
@@ -443,7 +446,7 @@ def decode_plan(seq_len, max_parts: int):
     pb = np.zeros(max_parts + 1, np.int32)
     sb, r0, r1 = (np.zeros(nseg_max, np.int32) for _ in range(3))
     npart, nseg = ctypes.c_int32(), ctypes.c_int32()
-    st = lib.mla_decode_plan(B, slp, max_parts, pb.ctypes.data_as(_I32P),
+    st = lib.mla_decode_plan_tokens(B, slp, int(q_len), max_parts, pb.ctypes.data_as(_I32P),
                              sb.ctypes.data_as(_I32P), r0.ctypes.data_as(_I32P),
                              r1.ctypes.data_as(_I32P), ctypes.byref(npart), ctypes.byref(nseg))
     if st != 0:

@@ -275,9 +275,63 @@ def test_decode_plan_balances_cost():
     assert cost.max() - cost.mean() < tile + seg_rows
 
 
+def test_decode_plan_tokens_keeps_tail():
+    """With q_len new tokens per sequence, each sequence's last segment holds
+    at least q_len rows (every token's causal limit lies in it), and the work
+    list keeps the invariants of the one-token plan."""
+    from mla_latent_kv_decode_amd import lib
+    rng = np.random.default_rng(11)
+    for _ in range(300):
+        q = int(rng.integers(2, 17))
+        B = int(rng.integers(1, 70))
+        lens = q + rng.integers(0, int(rng.choice([2, 40, 3000, 40000])), B)
+        max_parts = int(rng.integers(1, 600))
+        _plan_invariants(lens, max_parts)
+        pb, sb, r0, r1 = lib.decode_plan(lens, max_parts, q_len=q)
+        last = {}
+        for b, a, e in zip(sb, r0, r1):
+            last[int(b)] = (int(a), int(e))
+        assert sorted(last) == list(range(B))
+        for b, (a, e) in last.items():
+            assert e == lens[b] and e - a >= q, (q, lens[b], a, e)
+        nxt = np.zeros(B, np.int64)
+        for b, a, e in zip(sb, r0, r1):
+            assert a == nxt[b] and a < e
+            nxt[b] = e
+        assert np.array_equal(nxt, lens)
+        assert len(pb) - 1 <= max_parts
+
+
+def test_decode_plan_tokens_q1_is_plan():
+    """q_len = 1 gives mla_decode_plan's work list."""
+    import ctypes
+    from mla_latent_kv_decode_amd import lib
+    L = lib.load()
+    lens = np.random.default_rng(12).integers(1, 5000, 40).astype(np.int32)
+    P = 64
+    outs = []
+    for tok in (False, True):
+        pb = np.zeros(P + 1, np.int32)
+        sb, r0, r1 = (np.zeros(40 + P - 1, np.int32) for _ in range(3))
+        n_p, n_s = ctypes.c_int32(), ctypes.c_int32()
+        ptr = lambda x: x.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+        args = (ptr(pb), ptr(sb), ptr(r0), ptr(r1), ctypes.byref(n_p), ctypes.byref(n_s))
+        rc = (L.mla_decode_plan_tokens(40, ptr(lens), 1, P, *args) if tok
+              else L.mla_decode_plan(40, ptr(lens), P, *args))
+        assert rc == 0
+        outs.append((pb[:n_p.value + 1].copy(), sb[:n_s.value].copy(), r0[:n_s.value].copy(),
+                     r1[:n_s.value].copy()))
+    for x, y in zip(*outs):
+        assert np.array_equal(x, y)
+
+
 def test_decode_plan_errors():
     from mla_latent_kv_decode_amd import lib
     with pytest.raises(lib.MLAError):
         lib.decode_plan([5, 0, 3], 8)
     with pytest.raises(lib.MLAError):
         lib.decode_plan([5], 0)
+    with pytest.raises(lib.MLAError):
+        lib.decode_plan([5, 3], 8, q_len=4)   # a length below q_len
+    with pytest.raises(lib.MLAError):
+        lib.decode_plan([50], 8, q_len=17)    # beyond the largest q_len
