@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 5
+#define MLA_ABI_VERSION 6
 
 typedef enum mla_status {
   MLA_OK = 0,
@@ -100,19 +100,25 @@ typedef struct mla_config {
   float softmax_scale; /* 0 -> 1/sqrt(dn + dr) */
   int32_t dtype;     /* mla_dtype: storage type of every tensor (but see kv_storage) */
   int32_t kv_storage; /* mla_kv_storage: format of the latent cache rows */
-  /* YaRN context extension of the RoPE frequencies (the C-engine notes name
-   * YaRN without a formula; read as the published YaRN "NTK-by-parts"
-   * interpolation): with rope_scale = s > 1, pair i of base frequency
-   * theta_i = base^(-2i/dr) turns r_i = rope_orig_max * theta_i / (2 pi)
-   * times over the original context; gamma = clamp((r_i - yarn_beta_slow) /
-   * (yarn_beta_fast - yarn_beta_slow), 0, 1) and the frequency used is
-   * (1 - gamma) theta_i / s + gamma theta_i.  rope_scale <= 1 (0 included):
-   * plain RoPE, the other three fields unused.  YaRN's attention temperature
-   * is a factor on softmax_scale, set by the caller. */
+  /* YaRN context extension of the RoPE frequencies (the C-engine notes,
+   * "Deepseek V2 Lite Inference Engine in C", name YaRN without a formula;
+   * read as YaRN's "NTK-by-parts" interpolation in the form DeepSeek layers
+   * run it).  With rope_scale = s > 1: pair i of plain frequency theta_i =
+   * base^(-2i/dr) turns rope_orig_max * theta_i / (2 pi) times over the
+   * original context; let p(n) = dr * ln(rope_orig_max / (2 pi n)) /
+   * (2 ln base) be the pair index that turns n times, lo = max(floor(
+   * p(yarn_beta_fast)), 0), hi = min(ceil(p(yarn_beta_slow)), dr/2 - 1)
+   * (hi = lo + 0.001 if hi <= lo) and w_i = clamp((i - lo) / (hi - lo), 0, 1);
+   * the frequency used is (1 - w_i) theta_i + w_i theta_i / s.  When
+   * softmax_scale is 0 the default scale is multiplied by YaRN's attention
+   * factor (0.1 yarn_mscale ln s + 1)^2 (DeepSeek's per-model coefficient m;
+   * 0 leaves the scale unchanged).  rope_scale <= 1 (0 included): plain RoPE,
+   * the other four fields unused. */
   float rope_scale;
   int32_t rope_orig_max;  /* original context length, >= 1 when rope_scale > 1 */
   float yarn_beta_fast;   /* e.g. 32 */
-  float yarn_beta_slow;   /* e.g. 1; 0 <= slow < fast */
+  float yarn_beta_slow;   /* e.g. 1; 0 < slow < fast */
+  float yarn_mscale;      /* e.g. 0.707 (V2-Lite) or 1 (V3); >= 0 */
 } mla_config;
 
 typedef struct mla_ctx* mla_handle;
@@ -120,7 +126,8 @@ typedef struct mla_ctx* mla_handle;
 /* Host-only check of a configuration: MLA_OK, MLA_ERR_INVALID_ARG (cfg NULL,
  * a dimension <= 0 other than qk_rope/q_lora, a negative one, unknown dtype,
  * non-finite or non-positive base/eps, unknown kv_storage, rope_scale > 1 with
- * rope_orig_max < 1 or not 0 <= yarn_beta_slow < yarn_beta_fast) or MLA_ERR_SHAPE
+ * rope_orig_max < 1, not 0 < yarn_beta_slow < yarn_beta_fast or a negative or
+ * non-finite yarn_mscale) or MLA_ERR_SHAPE
  * (odd qk_rope, qk_rope > 128, kv_lora > 1024, v_head > 256, FP8 rows for a
  * layer outside the FP8 shapes).  Makes no HIP call; mla_create runs it
  * first. */

@@ -681,7 +681,8 @@ int mla_config_check(const mla_config* c) {
   if (!isfinite(c->rope_scale)) return MLA_ERR_INVALID_ARG;
   if (c->rope_scale > 1.f &&
       (c->rope_orig_max < 1 || !isfinite(c->yarn_beta_fast) || !isfinite(c->yarn_beta_slow) ||
-       !(c->yarn_beta_slow >= 0.f) || !(c->yarn_beta_fast > c->yarn_beta_slow)))
+       !(c->yarn_beta_slow > 0.f) || !(c->yarn_beta_fast > c->yarn_beta_slow) ||
+       !isfinite(c->yarn_mscale) || !(c->yarn_mscale >= 0.f)))
     return MLA_ERR_INVALID_ARG;
   if (c->kv_storage == MLA_KV_FP8_E4M3) {
     // the FP8 rows are read by the 16-head-group MFMA core only
@@ -808,6 +809,34 @@ int mla_prefill_check(const mla_config* cfg, const int32_t* cu_new, const int32_
   return MLA_OK;
 }
 
+// RoPE frequency of every pair (dr / 2 of them), YaRN-interpolated for
+// rope_scale > 1: plain theta_i below the blend band, theta_i / s above it,
+// linear in the pair index across it (band ends: the pair indices that turn
+// yarn_beta_fast and yarn_beta_slow times over the original context, floored
+// and ceiled).
+static void yarn_table(const mla_config* cfg, double* theta) {
+  const int half = cfg->qk_rope / 2;
+  const double base = cfg->rope_base;
+  double lo = 0.0, hi = 1.0;
+  if (cfg->rope_scale > 1.f) {
+    auto pair_at = [&](double turns) {
+      return cfg->qk_rope * log(cfg->rope_orig_max / (2.0 * M_PI * turns)) / (2.0 * log(base));
+    };
+    lo = std::max(floor(pair_at(cfg->yarn_beta_fast)), 0.0);
+    hi = std::min(ceil(pair_at(cfg->yarn_beta_slow)), (double)(half - 1));
+    if (hi <= lo) hi = lo + 0.001;
+  }
+  for (int i = 0; i < half; ++i) {
+    const double th = pow(base, -2.0 * i / (double)cfg->qk_rope);
+    double f = th;
+    if (cfg->rope_scale > 1.f) {
+      const double w = std::min(1.0, std::max(0.0, (i - lo) / (hi - lo)));
+      f = (1.0 - w) * th + w * th / cfg->rope_scale;
+    }
+    theta[i] = f;
+  }
+}
+
 int mla_create(const mla_config* cfg, void* stream, mla_handle* out) {
   if (!out) return MLA_ERR_INVALID_ARG;
   *out = nullptr;
@@ -825,19 +854,11 @@ int mla_create(const mla_config* cfg, void* stream, mla_handle* out) {
   d.dv = cfg->v_head; d.dc = cfg->kv_lora; d.dq = cfg->q_lora; d.R = d.dc + d.dr;
   d.rope_base = cfg->rope_base; d.eps = cfg->rms_eps;
   d.scale = cfg->softmax_scale > 0.f ? cfg->softmax_scale : 1.0f / sqrtf((float)(d.dn + d.dr));
-  for (int i = 0; i < d.dr / 2; ++i) {
-    // RoPE frequency of pair i, YaRN-interpolated for rope_scale > 1
-    const double th = pow((double)cfg->rope_base, -2.0 * i / (double)d.dr);
-    double f = th;
-    if (cfg->rope_scale > 1.f) {
-      const double s = cfg->rope_scale;
-      const double turns = cfg->rope_orig_max * th / (2.0 * M_PI);
-      const double g = std::min(1.0, std::max(0.0, (turns - cfg->yarn_beta_slow) /
-                                                       (double)(cfg->yarn_beta_fast -
-                                                                cfg->yarn_beta_slow)));
-      f = (1.0 - g) * th / s + g * th;
-    }
-    h->rope.theta[i] = (float)f;
+  yarn_table(cfg, h->rope.theta);
+  if (cfg->softmax_scale <= 0.f && cfg->rope_scale > 1.f) {
+    // YaRN's attention factor on the default scale
+    const double m = 0.1 * cfg->yarn_mscale * log((double)cfg->rope_scale) + 1.0;
+    d.scale = (float)(m * m / sqrt((double)(d.dn + d.dr)));
   }
   int ncu = 0;
   if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&

@@ -41,7 +41,8 @@ class MLAConfig(ctypes.Structure):
                 ("rms_eps", ctypes.c_float), ("softmax_scale", ctypes.c_float),
                 ("dtype", ctypes.c_int32), ("kv_storage", ctypes.c_int32),
                 ("rope_scale", ctypes.c_float), ("rope_orig_max", ctypes.c_int32),
-                ("yarn_beta_fast", ctypes.c_float), ("yarn_beta_slow", ctypes.c_float)]
+                ("yarn_beta_fast", ctypes.c_float), ("yarn_beta_slow", ctypes.c_float),
+                ("yarn_mscale", ctypes.c_float)]
 
 
 class MLADecodeArgs(ctypes.Structure):
@@ -156,7 +157,8 @@ def make_config(dims, dtype: str, softmax_scale: float = 0.0, kv: str = "dtype")
                      float(getattr(dims, "rope_scale", 1.0)),
                      int(getattr(dims, "rope_orig_max", 4096)),
                      float(getattr(dims, "yarn_beta_fast", 32.0)),
-                     float(getattr(dims, "yarn_beta_slow", 1.0)))
+                     float(getattr(dims, "yarn_beta_slow", 1.0)),
+                     float(getattr(dims, "yarn_mscale", 0.0)))
 
 
 def _i32(a):

@@ -46,6 +46,7 @@ class LayerDims:
     rope_orig_max: int = 4096
     yarn_beta_fast: float = 32.0
     yarn_beta_slow: float = 1.0
+    yarn_mscale: float = 0.0       # YaRN attention-factor coefficient; 0 = none
 
     @property
     def row(self) -> int:

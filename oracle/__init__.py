@@ -23,14 +23,18 @@ cache with one scale per row, read back as the cache would hand it out) and
 ``oracle.paged`` (the row lookup of a cache kept in pages named by a block
 table).
 
-YaRN (``rope_theta`` with a context-extension factor > 1) is named on the
-pages without a formula; its branch follows the published YaRN method
-(outside the pages) and is pinned only to that method's defining properties:
-parity unpinned with respect to the pages.
+YaRN (``rope_theta`` with a context-extension factor > 1, and
+``yarn_attention_factor``) is named on the pages without a formula; its branch
+follows YaRN's NTK-by-parts interpolation in the form DeepSeek's layers run it
+(outside the pages).  It is pinned against an independent implementation of
+that form (the ``transformers`` library's YaRN initialisation and DeepSeek
+attention scaling, importable in the test image) and against the method's
+defining properties.
 
-Parity status: apart from that branch, every function here is pinned by the ``-m "not gpu"`` tests in
+Parity status: every function here is pinned by the ``-m "not gpu"`` tests in
 ``tests/test_oracle_pins.py`` (brute force, identities, closed forms, special
-cases); no function is "parity unpinned".
+cases, the independent YaRN implementation); no function is "parity
+unpinned".
 """
 
 from .mla import (  # noqa: F401

@@ -19,7 +19,8 @@ Readings of the pages where they are silent or garbled:
     sequence has position i.
   * Per-head row layouts: q_proj rows are [q_nope_h (dn) | q_rope_h (dr)] per
     head; kv_b_proj rows are [K_nope_h (dn) ; V_h (dv)] per head.
-  * The softmax scale is 1/sqrt(dn + dr).
+  * The softmax scale is 1/sqrt(dn + dr) (times YaRN's attention factor
+    under context extension, see yarn_attention_factor).
   * A query at position p sees cache rows 0..p of its own sequence (the new
     rows are written to the cache before it is read).
 """
@@ -54,6 +55,7 @@ class MLAShape:
     rope_orig_max: int = 4096
     yarn_beta_fast: float = 32.0
     yarn_beta_slow: float = 1.0
+    yarn_mscale: float = 0.0   # m of yarn_attention_factor; 0 = softmax scale unchanged
 
     @property
     def theta(self) -> np.ndarray:
@@ -68,7 +70,8 @@ class MLAShape:
     def scale(self) -> float:
         if self.softmax_scale:
             return float(self.softmax_scale)
-        return 1.0 / np.sqrt(self.qk_nope + self.qk_rope)
+        return (yarn_attention_factor(self.rope_scale, self.yarn_mscale)
+                / np.sqrt(self.qk_nope + self.qk_rope))
 
 
 def _f64(a) -> np.ndarray:
@@ -87,29 +90,53 @@ def rms_norm(a, gamma, eps: float) -> np.ndarray:
     return a / np.sqrt(ms + eps) * _f64(gamma)
 
 
+def yarn_pair_at(turns: float, d: int, base: float, orig_max: int) -> float:
+    """The (fractional) pair index i at which pair i of plain RoPE turns
+    ``turns`` times over ``orig_max`` positions: orig_max * base^(-2i/d) /
+    (2 pi) = turns, solved for i."""
+    return d * np.log(orig_max / (2.0 * np.pi * turns)) / (2.0 * np.log(base))
+
+
 def rope_theta(d: int, base: float, scale: float = 1.0, orig_max: int = 4096,
                beta_fast: float = 32.0, beta_slow: float = 1.0) -> np.ndarray:
     """Per-pair rotation frequencies theta_i (i < d / 2).
 
     Plain RoPE (MLA post, section 3.7): theta_i = base^(-2i/d).  With a
-    context-extension factor scale > 1, YaRN, which the C-engine notes ("Deepseek
-    V2 Lite Inference Engine in C", MLA notes) name without a formula; the
-    reading here is the published YaRN method ("YaRN: Efficient Context
-    Window Extension of Large Language Models", Peng et al. 2023, section
-    3.2, "NTK-by-parts" interpolation): pair i turns r_i = orig_max theta_i /
-    (2 pi) times over the original context; pairs that turn fewer than
-    beta_slow times are interpolated (theta_i / scale), pairs that turn more
-    than beta_fast times are kept, and in between the two blend linearly in
-    r_i:  gamma = clip((r_i - beta_slow) / (beta_fast - beta_slow), 0, 1),
-    theta'_i = (1 - gamma) theta_i / scale + gamma theta_i.  (YaRN's attention
-    temperature is a factor on the softmax scale, left to the caller.)
+    context-extension factor scale = s > 1: YaRN, which the C-engine notes
+    ("Deepseek V2 Lite Inference Engine in C", Todos and base operations) name
+    without a formula.  Reading: YaRN's "NTK-by-parts" interpolation in the
+    form DeepSeek's layers run it.  Pairs that turn more than beta_fast times
+    over the original context keep theta_i, pairs that turn fewer than
+    beta_slow times are slowed to theta_i / s, and the band in between blends
+    the two with a weight that is linear in the PAIR INDEX: the band runs from
+    lo = floor(pair index where a pair turns beta_fast times) to hi =
+    ceil(pair index where it turns beta_slow times), both clamped to
+    [0, d/2 - 1] (hi raised to lo + 0.001 when they meet);
+    w_i = clip((i - lo) / (hi - lo), 0, 1) and theta'_i = (1 - w_i) theta_i +
+    w_i theta_i / s.
     """
     theta = base ** (-np.arange(0, d, 2, dtype=F64) / d)
     if scale <= 1.0:
         return theta
-    r = orig_max * theta / (2.0 * np.pi)
-    gamma = np.clip((r - beta_slow) / (beta_fast - beta_slow), 0.0, 1.0)
-    return (1.0 - gamma) * theta / scale + gamma * theta
+    half = d // 2
+    lo = max(float(np.floor(yarn_pair_at(beta_fast, d, base, orig_max))), 0.0)
+    hi = min(float(np.ceil(yarn_pair_at(beta_slow, d, base, orig_max))), float(half - 1))
+    if hi <= lo:
+        hi = lo + 0.001
+    w = np.clip((np.arange(half, dtype=F64) - lo) / (hi - lo), 0.0, 1.0)
+    return (1.0 - w) * theta + w * theta / scale
+
+
+def yarn_attention_factor(scale: float, mscale: float) -> float:
+    """Multiplier of the softmax scale under YaRN context extension.
+
+    The published YaRN method sharpens the logits by a temperature with
+    sqrt(1/t) = 0.1 ln(s) + 1; DeepSeek's layers weight the logarithm by a
+    per-model coefficient m (0 = no change) and multiply the softmax scale by
+    (0.1 m ln(s) + 1)^2.  Factor 1 for s <= 1."""
+    if scale <= 1.0:
+        return 1.0
+    return float((0.1 * mscale * np.log(scale) + 1.0) ** 2)
 
 
 def rope(x, pos, base: float, theta=None) -> np.ndarray:

@@ -18,7 +18,7 @@ def oracle_shape(d: synth.LayerDims) -> O.MLAShape:
                       v_head=d.v_head, kv_lora=d.kv_lora, q_lora=d.q_lora,
                       rope_base=d.rope_base, rms_eps=d.rms_eps, rope_scale=d.rope_scale,
                       rope_orig_max=d.rope_orig_max, yarn_beta_fast=d.yarn_beta_fast,
-                      yarn_beta_slow=d.yarn_beta_slow)
+                      yarn_beta_slow=d.yarn_beta_slow, yarn_mscale=d.yarn_mscale)
 
 
 def tol(dtype: str) -> float:

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(mla):
     missing = [n for n in names if not hasattr(mla, n)]
     assert not missing, missing
     assert set(names) == set(L._SIGS), set(names) ^ set(L._SIGS)
-    assert mla.mla_abi_version() == 5
+    assert mla.mla_abi_version() == 6
 
 
 def test_status_strings(mla):
@@ -65,9 +65,13 @@ def test_yarn_config_check(mla):
     ok = cfg(rope_scale=40.0, rope_orig_max=4096, yarn_beta_fast=32.0, yarn_beta_slow=1.0)
     assert mla.mla_config_check(ctypes.byref(ok)) == L.MLA_OK
     assert mla.mla_config_check(ctypes.byref(cfg(rope_scale=0.0, rope_orig_max=0))) == L.MLA_OK
+    assert mla.mla_config_check(ctypes.byref(cfg(rope_scale=40.0, yarn_mscale=0.707))) == L.MLA_OK
     for bad in (dict(rope_scale=4.0, rope_orig_max=0),
                 dict(rope_scale=4.0, yarn_beta_fast=1.0, yarn_beta_slow=1.0),
                 dict(rope_scale=4.0, yarn_beta_slow=-1.0),
+                dict(rope_scale=4.0, yarn_beta_slow=0.0),
+                dict(rope_scale=4.0, yarn_mscale=-0.5),
+                dict(rope_scale=4.0, yarn_mscale=float("inf")),
                 dict(rope_scale=float("nan"))):
         assert mla.mla_config_check(ctypes.byref(cfg(**bad))) == L.MLA_ERR_INVALID_ARG, bad
 

@@ -15,8 +15,10 @@ from tests.test_gpu_prefill import run_prefill_case
 
 pytestmark = pytest.mark.gpu
 
-# DeepSeek-V2-Lite's context extension: 4k original positions, factor 40
-YARN = dict(rope_scale=40.0, rope_orig_max=4096, yarn_beta_fast=32.0, yarn_beta_slow=1.0)
+# DeepSeek-V2-Lite's context extension: 4k original positions, factor 40, the
+# attention factor's coefficient 0.707 (the library derives the softmax scale)
+YARN = dict(rope_scale=40.0, rope_orig_max=4096, yarn_beta_fast=32.0, yarn_beta_slow=1.0,
+            yarn_mscale=0.707)
 
 
 def test_yarn_decode_past_original_context():

@@ -549,3 +549,74 @@ def test_yarn_rope_keeps_relative_positions():
         return float(O.rope(q, pq, 10000.0, th) @ O.rope(k, pk, 10000.0, th))
     assert abs(score(9000, 8000) - score(1000, 0)) < 1e-9
     assert abs(score(5, 5) - float(q @ k)) < 1e-12
+
+
+# YaRN settings: (d, base, factor, original context, beta_fast, beta_slow).  The
+# first is DeepSeek-V2-Lite's and V3's (rope dim 64, base 10000, factor 40, 4k
+# original positions); the others move every boundary of the blend band.
+YARN_SETTINGS = [(64, 10000.0, 40.0, 4096, 32.0, 1.0),
+                 (64, 10000.0, 4.0, 2048, 32.0, 1.0),
+                 (128, 500000.0, 8.0, 8192, 32.0, 1.0),
+                 (64, 10000.0, 40.0, 4096, 16.0, 2.0),
+                 (32, 10000.0, 16.0, 4096, 32.0, 1.0),
+                 (64, 1000000.0, 10.0, 32768, 64.0, 0.5)]
+
+
+def _hf_yarn(d, base, s, L, bf, bs, mscale=None):
+    """The `transformers` library's YaRN initialisation (an implementation of
+    the same method, independent of the oracle) for a DeepSeek-style layer
+    whose rope part is d wide: (per-pair frequencies, cos/sin amplitude)."""
+    from transformers import DeepseekV3Config
+    from transformers.modeling_rope_utils import ROPE_INIT_FUNCTIONS
+    rp = dict(rope_type="yarn", rope_theta=base, factor=s, original_max_position_embeddings=L,
+              beta_fast=bf, beta_slow=bs)
+    if mscale is not None:
+        rp.update(mscale=mscale, mscale_all_dim=mscale)
+    cfg = DeepseekV3Config(qk_rope_head_dim=d, rope_parameters=rp)
+    inv, amp = ROPE_INIT_FUNCTIONS["yarn"](cfg, "cpu")
+    return inv.double().numpy(), amp
+
+
+@pytest.mark.parametrize("setting", YARN_SETTINGS)
+def test_yarn_frequencies_match_independent_implementation(setting):
+    """The blend band of rope_theta (linear over the pair index between the
+    floored and ceiled pair indices where a pair turns beta_fast and beta_slow
+    times) agrees with the `transformers` YaRN initialisation on every pair,
+    to its float32 rounding."""
+    d, base, s, L, bf, bs = setting
+    ref, _ = _hf_yarn(d, base, s, L, bf, bs)
+    th = O.rope_theta(d, base, s, L, bf, bs)
+    assert th.shape == ref.shape
+    assert np.max(np.abs(th - ref) / ref) < 1e-6, np.abs(th - ref) / ref
+    # the band is really exercised: some pairs are neither kept nor divided by s
+    plain = base ** (-np.arange(0, d, 2) / d)
+    mid = (np.abs(th - plain) > 1e-9 * plain) & (np.abs(th - plain / s) > 1e-9 * plain)
+    assert mid.any()
+
+
+def test_yarn_attention_factor_matches_deepseek_scaling():
+    """The softmax-scale multiplier (0.1 m ln s + 1)^2 equals the one
+    `transformers`' DeepSeek attention applies for the same rope parameters,
+    and with equal mscale coefficients the rotation itself keeps amplitude 1
+    (the cache's k_rope is not rescaled)."""
+    import torch
+    from transformers import DeepseekV3Config
+    from transformers.models.deepseek_v3 import modeling_deepseek_v3 as hf
+    for s, m in ((40.0, 0.707), (40.0, 1.0), (4.0, 0.5)):
+        rp = dict(rope_type="yarn", rope_theta=10000.0, factor=s,
+                  original_max_position_embeddings=4096, beta_fast=32, beta_slow=1,
+                  mscale=m, mscale_all_dim=m)
+        cfg = DeepseekV3Config(hidden_size=64, num_attention_heads=2, q_lora_rank=None,
+                               kv_lora_rank=16, qk_nope_head_dim=16, qk_rope_head_dim=8,
+                               v_head_dim=16, rope_parameters=rp)
+        with torch.device("cpu"):
+            attn = hf.DeepseekV3Attention(cfg, 0)
+        shp = O.MLAShape(hidden=64, n_heads=2, qk_nope=16, qk_rope=8, v_head=16, kv_lora=16,
+                         rope_scale=s, yarn_mscale=m)
+        assert abs(shp.scale - attn.scaling) < 1e-12 * attn.scaling
+        _, amp = _hf_yarn(8, 10000.0, s, 4096, 32.0, 1.0, mscale=m)
+        assert amp == 1.0
+    # no context extension, or m = 0: the plain scale
+    assert O.yarn_attention_factor(1.0, 0.707) == 1.0
+    assert O.yarn_attention_factor(40.0, 0.0) == 1.0
+    assert O.MLAShape(64, 2, 16, 8, 16, 16).scale == 1.0 / np.sqrt(24)
