@@ -109,6 +109,27 @@ def traffic_from_profile(n_launch_bytes: float):
     return t.get("hbm_bytes_per_launch")
 
 
+def _oracle_threads() -> int:
+    """Threads the oracle's BLAS actually runs with."""
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([p.get("num_threads", 1) for p in threadpool_info()] or [1]))
+    except Exception:
+        return int(os.cpu_count() or 1)
+
+
+def _cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, w, lens, budget_s: float):
     """The fp64 oracle (as it stands) on a bounded sample of the same workload:
     whole sequences from the start of the batch until the time budget is used.
@@ -145,13 +166,8 @@ def cpu_baseline(wl, w, lens, budget_s: float):
             if spent >= budget_s:
                 break
         passes += 1
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
-        cores = os.cpu_count()
-    return {"value": rows * row_bytes / spent / 1e9, "unit": "GB/s", "cores": int(cores),
-            "kind": "oracle", "tokens_per_s": toks / spent,
+    return {"value": rows * row_bytes / spent / 1e9, "unit": "GB/s", "cores": _oracle_threads(),
+            "cpu_model": _cpu_model(), "kind": "oracle", "tokens_per_s": toks / spent,
             "sample": f"{toks} sequence decodes over {passes} pass(es) of the {len(lens)}-sequence "
                       f"batch ({rows} latent rows), fp64 non-absorbed oracle, {spent:.1f} s"}
 
@@ -196,12 +212,8 @@ def cpu_baseline_prefill(wl, w, budget_s: float):
         spent += time.perf_counter() - t0
         chunks += 1
         flops += prefill_flops(d, n, n, n * (n + 1) // 2)[0]
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
-        cores = os.cpu_count()
-    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": int(cores),
+    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": _oracle_threads(),
+            "cpu_model": _cpu_model(),
             "kind": "oracle", "tokens_per_s": chunks * n / spent,
             "sample": f"{chunks} prefill(s) of {n} new tokens with no cached rows (sequence 0), "
                       f"fp64 non-absorbed oracle, {spent:.1f} s"}

@@ -100,16 +100,23 @@ class DecodeCase:
         return self.layer.decode(x, self.seq_len - 1, self.seq_off, self.seq_len, self.cache,
                                  stages=stages)
 
-    def oracle(self, b):
+    def oracle(self, b, absorbed_only=False):
+        """(y of the non-absorbed fp64 step, the absorbed step's dict) for
+        sequence b; with absorbed_only, y comes from the absorbed form (pinned
+        equal to the non-absorbed one) and the K/V expansion is skipped."""
         shp = oracle_shape(self.dims)
         L = int(self.lens[b])
         xb = self.hidden[b]
         rows_prior = (O.latent_rows(xb[:L], np.arange(L), self.w["w_kva"], self.w["kv_norm_g"],
                                     shp) if L else np.zeros((0, shp.row)))
         store = (lambda r: F8.fp8_rows(r, shp.kv_lora)) if self.kv == "fp8" else None
-        r = O.mla_step(xb[L:L + 1], np.array([L]), rows_prior, self.w, shp, kv_store=store)
-        rows = np.concatenate([rows_prior, r["rows_new"]])
+        if absorbed_only:
+            rows = np.concatenate([rows_prior, O.latent_rows(
+                xb[L:L + 1], np.array([L]), self.w["w_kva"], self.w["kv_norm_g"], shp)])
+        else:
+            r = O.mla_step(xb[L:L + 1], np.array([L]), rows_prior, self.w, shp, kv_store=store)
+            rows = np.concatenate([rows_prior, r["rows_new"]])
         if store is not None:
             rows = store(rows)
         a = O.absorbed_step(xb[L:L + 1], np.array([L]), rows, self.w, shp)
-        return r["y"][0], a
+        return (a["y"][0] if absorbed_only else r["y"][0]), a

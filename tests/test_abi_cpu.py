@@ -170,7 +170,14 @@ def test_decode_paged_check(mla):
     # a step writing two new rows onto one cache row (shared last page, same offset)
     assert chk([4, 4], [[2], [2]], 32, [5, 5], 128, writes=1) == L.MLA_ERR_INVALID_ARG
     assert chk([4, 4], [[2], [2]], 32, [5, 5], 128, writes=0) == L.MLA_OK  # reads may share
-    assert chk([4, 5], [[2], [2]], 32, [5, 6], 128, writes=1) == L.MLA_OK  # different offsets
+    # a shared page that a step writes into: sequence 0's new row (position 4,
+    # row 68) is a cached row of sequence 1, which would read it overwritten
+    assert chk([4, 5], [[2], [2]], 32, [5, 6], 128, writes=1) == L.MLA_ERR_INVALID_ARG
+    assert chk([4, 5], [[2], [2]], 32, [5, 6], 128, writes=0) == L.MLA_OK
+    # a shared prefix page only read, new rows on each sequence's own page
+    assert chk([39, 39], [[2, 3], [2, 1]], 32, [40, 40], 128, writes=1) == L.MLA_OK
+    # a sequence naming the same page twice: its new row lands on its own cached row
+    assert chk([39], [[2, 2]], 32, [40], 128, writes=1) == L.MLA_ERR_INVALID_ARG
 
 
 def test_decode_ex_check(mla):
@@ -200,6 +207,11 @@ def test_decode_ex_check(mla):
     # offset 0, so pointing sequence 1 at page 9 collides
     assert chk(2, 3, [33, 3], table=[[4, 9], [9, 0]], P=32, append=1) == L.MLA_ERR_INVALID_ARG
     assert chk(2, 3, [33, 3], table=[[4, 9], [9, 0]], P=32, append=0) == L.MLA_OK
+    # contiguous ranges that overlap: sequence 0 writes row 4, which sequence 1
+    # (rows 3..5) reads as cached; allowed without the append
+    assert chk(2, 1, [5, 3], off=[0, 3], append=1) == L.MLA_ERR_INVALID_ARG
+    assert chk(2, 1, [5, 3], off=[0, 3], append=0) == L.MLA_OK
+    assert chk(2, 1, [5, 3], off=[0, 5], append=1) == L.MLA_OK
 
 
 def test_prefill_check(mla):

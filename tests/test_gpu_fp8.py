@@ -14,7 +14,7 @@ from mla_latent_kv_decode_amd import synth
 from oracle import fp8 as F8
 from oracle import mla as O
 from tests.helpers import DecodeCase, dev, host, make_layer, oracle_shape, row_rel_err, tol
-from tests.test_gpu_decode import _check
+from tests.test_gpu_decode import _check, _compare, chunk, full_size_case
 
 pytestmark = pytest.mark.gpu
 
@@ -100,15 +100,19 @@ def test_fp8_ring_core_two_head_groups():
     _check(case, range(4))
 
 
-def test_fp8_decode_b64_full_size_sampled():
-    """The benchmark's B=64 ragged batch on an FP8 cache; the shortest, the
-    longest and two more sequences against the oracle, every row finite."""
-    w = synth.WORKLOADS["v2lite_decode_b64"]
-    lens = synth.lengths(w)
-    pick = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 7, 40})
-    case = DecodeCase(w.dims, "bf16", w.weight_std, lens, random_gains=False, keep=pick, kv="fp8")
-    y = _check(case, pick, stages=True)
-    assert np.all(np.isfinite(y))
+@pytest.fixture(scope="module")
+def fp8_b64():
+    return full_size_case("v2lite_decode_b64", kv="fp8")
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("part", range(4))
+def test_fp8_decode_b64_full_size(fp8_b64, part):
+    """The benchmark's B=64 ragged batch on an FP8 cache, decoded once: y,
+    q_cat and o_lat of EVERY sequence against the oracle reading its own
+    quantised rows, a quarter of the batch per test."""
+    case, out = fp8_b64
+    _compare(case, out, chunk(case.B, part))
 
 
 @pytest.mark.parametrize("lens", [[0, 1, 16, 63, 300, 1500],

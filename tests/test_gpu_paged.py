@@ -15,6 +15,7 @@ import pytest
 from mla_latent_kv_decode_amd import synth
 from oracle import paged as PG
 from tests.helpers import DecodeCase, dev, host, row_rel_err, tol
+from tests.test_gpu_decode import _compare, chunk
 
 pytestmark = pytest.mark.gpu
 
@@ -132,15 +133,37 @@ def test_paged_decode_step(kv):
         assert row_rel_err(y_p[b:b + 1], y_ref[None])[0] < tol("bf16"), b
 
 
-def test_paged_decode_b64_full_size():
-    """The benchmark's 64-sequence batch on 64-row pages in random order:
-    the paged core run of the timed configuration equals the contiguous one
-    bit for bit; two sequences against the oracle."""
+@pytest.fixture(scope="module")
+def paged_b64():
+    """The benchmark's 64-sequence batch: contiguous decode, then the same
+    rows on 64-row pages in random order; (case, paged host outputs)."""
     w = synth.WORKLOADS["v2lite_decode_b64"]
-    lens = synth.lengths(w)
-    pick = sorted({int(np.argmin(lens)), int(np.argmax(lens))})
-    case = DecodeCase(w.dims, "bf16", w.weight_std, lens, random_gains=False, keep=pick)
-    _paged_vs_contiguous(case, 64, 12, pick)
+    case = DecodeCase(w.dims, "bf16", w.weight_std, synth.lengths(w), random_gains=False)
+    y_c, q_c, o_c = case.run(stages=True)
+    pool, table = _page_pool(case, 64, 12)
+    x = dev(case.x_new, case.layer.torch_dtype)
+    out = case.layer.decode_paged(x, case.seq_len - 1, table, 64, case.seq_len, pool,
+                                  stages=True)
+    out = tuple(host(t) for t in out)
+    del pool
+    return case, out, (host(y_c), host(q_c), host(o_c))
+
+
+@pytest.mark.timeout(300)
+def test_paged_decode_b64_full_size_bit_exact(paged_b64):
+    """The paged core run of the timed configuration equals the contiguous
+    one bit for bit (y, q_cat, o_lat)."""
+    _, out, contig = paged_b64
+    for a, b in zip(out, contig):
+        assert np.array_equal(a, b)
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("part", range(4))
+def test_paged_decode_b64_full_size(paged_b64, part):
+    """... and every sequence matches the oracle, a quarter per test."""
+    case, out, _ = paged_b64
+    _compare(case, out, chunk(case.B, part))
 
 
 def test_paged_decode_large_pages():

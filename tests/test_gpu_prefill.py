@@ -61,12 +61,14 @@ def test_v3_prefill_small():
     run_prefill_case(synth.V3, "bf16", 0.02, [0, 21], [24, 9])
 
 
-def test_v3_prefill_4x4096_full_size_sampled():
+@pytest.mark.timeout(600)
+def test_v3_prefill_4x4096_full_size():
     """The V3 chunked prefill at its full size (4 sequences x 4096 new tokens
     after 0 / 2048 / 0 / 2048 cached rows) in the launch configuration the
-    timing uses; sampled queries per sequence (first, tile and key-tile edges,
-    last) are compared with the oracle one by one."""
+    timing uses: every 64th query, the tile and key-tile edges and the whole
+    last 256-query tile of every sequence against the oracle."""
     w = synth.WORKLOADS["v3_prefill_4x4096"]
     prior, new = [0, 2048, 0, 2048], [4096] * 4
-    sub = [np.array([0, 1, 31, 32, 255, 256, 2047, 4095])] * 4
-    run_prefill_case(w.dims, "bf16", w.weight_std, prior, new, query_subset=sub)
+    q = np.unique(np.concatenate([np.arange(0, 4096, 64), [1, 31, 32, 255, 256, 2047],
+                                  np.arange(4096 - 256, 4096)]))
+    run_prefill_case(w.dims, "bf16", w.weight_std, prior, new, query_subset=[q] * 4)
