@@ -238,7 +238,9 @@ size_t mla_decode_step_workspace_bytes(mla_handle h, int32_t B, int64_t total_ro
  * pos[b] = seq_len[b] - 1) from hidden[b] exactly as mla_append_latent would,
  * then decodes.  The latent down-projection and the query projection read the
  * same hidden states, so they run as one GEMM over [W_kva ; W_q] (or
- * [W_kva ; W_qa]).  Same errors as mla_decode. */
+ * [W_kva ; W_qa]).  Same errors as mla_decode, plus INVALID_ARG when two
+ * sequences' new rows are the same cache row or a new row lies inside
+ * another sequence's rows (it would be overwritten before it is read). */
 int mla_decode_step(mla_handle h, const void* hidden, const int32_t* pos,
                     const int64_t* seq_off, const int32_t* seq_len, int32_t B, void* cache,
                     int64_t cache_rows, void* out, void* ws, size_t ws_bytes);
@@ -265,7 +267,8 @@ int mla_decode_step(mla_handle h, const void* hidden, const int32_t* pos,
  * Errors: as mla_decode; page_rows not a power of two in range, max_pages < 1
  * or a NULL table -> INVALID_ARG; more pages needed than max_pages, or a page
  * index outside [0, cache_rows / page_rows) -> CAPACITY; two new rows of a
- * step on the same cache row -> INVALID_ARG. */
+ * step on the same cache row, or a new row on a row that some sequence reads
+ * as already cached (e.g. inside a shared prefix page) -> INVALID_ARG. */
 int mla_decode_paged(mla_handle h, const void* hidden, const int32_t* pos,
                      const int32_t* block_table, int32_t max_pages, int32_t page_rows,
                      const int32_t* seq_len, int32_t B, const void* cache, int64_t cache_rows,
@@ -307,8 +310,9 @@ typedef struct mla_decode_args {
 /* Host-only checks of mla_decode_ex.  Errors: NULL args/seq_len, B < 1, q_len
  * outside 1 .. MLA_MAX_Q_LEN, seq_len[b] < q_len, both or neither of seq_off
  * and block_table -> INVALID_ARG; a contiguous sequence outside
- * [0, cache_rows) -> CAPACITY; paged: the errors of mla_decode_paged (with
- * append, all B * q_len new rows must land on distinct cache rows). */
+ * [0, cache_rows) -> CAPACITY; paged: the errors of mla_decode_paged.  With
+ * append, all B * q_len new rows must land on distinct cache rows, none of
+ * them on a row some sequence reads as cached (INVALID_ARG otherwise). */
 int mla_decode_ex_check(const mla_config* cfg, const mla_decode_args* a);
 /* Workspace bytes for B sequences of total_rows rows in all (sum of seq_len),
  * q_len new tokens each, with (append = 1) or without the append. */

@@ -733,9 +733,41 @@ int mla_decode_check(const mla_config* cfg, const int32_t* pos, const int64_t* s
   return MLA_OK;
 }
 
+// Rows a step writes (sorted in place) against the rows it reads: every
+// written row is distinct, and none lies inside a half-open range of rows
+// some sequence reads as already cached -- that row would be overwritten
+// before the attention core reads it.  `cached(visit)` calls visit(r0, r1)
+// for every such range.
+template <typename Ranges>
+static int write_read_check(std::vector<int64_t>& w, Ranges cached) {
+  std::sort(w.begin(), w.end());
+  if (std::adjacent_find(w.begin(), w.end()) != w.end()) return MLA_ERR_INVALID_ARG;
+  bool clash = false;
+  cached([&](int64_t r0, int64_t r1) {
+    auto it = std::lower_bound(w.begin(), w.end(), r0);
+    if (it != w.end() && *it < r1) clash = true;
+  });
+  return clash ? MLA_ERR_INVALID_ARG : MLA_OK;
+}
+
+// The new rows of a step on a contiguous cache: q_len rows at the end of
+// every sequence's range.
+static int contig_write_check(const int64_t* seq_off, const int32_t* seq_len, int32_t B,
+                              int q_len) {
+  std::vector<int64_t> w;
+  w.reserve((size_t)B * q_len);
+  for (int32_t b = 0; b < B; ++b)
+    for (int j = 0; j < q_len; ++j) w.push_back(seq_off[b] + seq_len[b] - q_len + j);
+  return write_read_check(w, [&](auto visit) {
+    for (int32_t b = 0; b < B; ++b)
+      if (seq_len[b] > q_len) visit(seq_off[b], seq_off[b] + seq_len[b] - q_len);
+  });
+}
+
 // The block table of a paged decode: page size, table width, every used page
 // in range; with `writes`, the q_len new rows of every sequence land on
-// distinct cache rows.
+// distinct cache rows, none of them on a row any sequence reads as cached
+// (pages may be shared between sequences).
 static int paged_table_check(const int32_t* block_table, int32_t max_pages, int32_t page_rows,
                              const int32_t* seq_len, int32_t B, int64_t cache_rows, int q_len,
                              int32_t writes) {
@@ -750,7 +782,7 @@ static int paged_table_check(const int32_t* block_table, int32_t max_pages, int3
     for (int64_t i = 0; i < np; ++i)
       if (row[i] < 0 || row[i] >= n_pages) return MLA_ERR_CAPACITY;
   }
-  if (writes) {  // the new rows of a step: one cache row each, all distinct
+  if (writes) {  // the new rows of a step: one cache row each
     std::vector<int64_t> w;
     w.reserve((size_t)B * q_len);
     for (int32_t b = 0; b < B; ++b)
@@ -759,8 +791,15 @@ static int paged_table_check(const int32_t* block_table, int32_t max_pages, int3
         w.push_back((int64_t)block_table[(int64_t)b * max_pages + t / page_rows] * page_rows +
                     t % page_rows);
       }
-    std::sort(w.begin(), w.end());
-    if (std::adjacent_find(w.begin(), w.end()) != w.end()) return MLA_ERR_INVALID_ARG;
+    return write_read_check(w, [&](auto visit) {
+      for (int32_t b = 0; b < B; ++b) {
+        const int64_t cached = (int64_t)seq_len[b] - q_len;  // positions read, not written
+        const int32_t* row = block_table + (int64_t)b * max_pages;
+        for (int64_t t0 = 0; t0 < cached; t0 += page_rows)
+          visit((int64_t)row[t0 / page_rows] * page_rows,
+                (int64_t)row[t0 / page_rows] * page_rows + std::min<int64_t>(page_rows, cached - t0));
+      }
+    });
   }
   return MLA_OK;
 }
@@ -791,7 +830,7 @@ int mla_decode_ex_check(const mla_config* cfg, const mla_decode_args* a) {
   for (int32_t b = 0; b < a->B; ++b)
     if (a->seq_off[b] < 0 || a->seq_off[b] > a->cache_rows - a->seq_len[b])
       return MLA_ERR_CAPACITY;
-  return MLA_OK;
+  return a->append ? contig_write_check(a->seq_off, a->seq_len, a->B, a->q_len) : MLA_OK;
 }
 
 int mla_prefill_check(const mla_config* cfg, const int32_t* cu_new, const int32_t* prior_len,
@@ -1429,6 +1468,7 @@ static int decode_common(mla_handle h, const void* hidden, const int32_t* pos,
                                        pg ? pg->max_pages : 0, pg ? pg->page_rows : 0, seq_len,
                                        B, cache_rows, step ? 1 : 0)
               : mla_decode_check(&h->cfg, pos, seq_off, seq_len, B, cache_rows);
+  if (!rc && !pg && step) rc = contig_write_check(seq_off, seq_len, B, 1);
   if (rc) return fail(h, rc, "%s: %s (B=%d, cache_rows=%lld)", what, mla_status_string(rc), B,
                       (long long)cache_rows);
   const DecodeCall c{hidden, out, B, 1, seq_len, seq_off, pg, cache, step, ws, ws_bytes};
