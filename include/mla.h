@@ -245,6 +245,27 @@ int mla_decode_step(mla_handle h, const void* hidden, const int32_t* pos,
                     const int64_t* seq_off, const int32_t* seq_len, int32_t B, void* cache,
                     int64_t cache_rows, void* out, void* ws, size_t ws_bytes);
 
+/* mla_decode_step without a workspace argument, for callers that cannot
+ * allocate device memory (tight serving loops, harnesses that forbid
+ * hipMalloc).  The step's workspace is a static device array of
+ * MLA_NOALLOC_SCRATCH_BYTES bytes inside the library, one per GPU, held from
+ * the library's load until the process ends; its address is taken at
+ * mla_create, which also pins the host staging memory this call uses, so the
+ * call itself allocates nothing.  Same arguments (minus ws / ws_bytes),
+ * kernels, results and errors as mla_decode_step, plus: MLA_ERR_WORKSPACE when
+ * mla_decode_step_workspace_bytes(h, B, sum of seq_len) exceeds
+ * MLA_NOALLOC_SCRATCH_BYTES (32 MiB holds, e.g., a V2-Lite-shaped step of 64
+ * sequences; 128-head layers need more) or the step's metadata exceed the
+ * staged pinned memory; MLA_ERR_STATE while the handle's stream is being
+ * captured into a graph.  All calls on one GPU share that GPU's array, which
+ * keeps the last call's contents: calls that overlap on one GPU (other
+ * streams, other handles, other threads) race and must be serialised by the
+ * caller. */
+#define MLA_NOALLOC_SCRATCH_BYTES (32u << 20)
+int mla_decode_step_noalloc(mla_handle h, const void* hidden, const int32_t* pos,
+                            const int64_t* seq_off, const int32_t* seq_len, int32_t B, void* cache,
+                            int64_t cache_rows, void* out);
+
 /* Paged latent cache -- mla_decode and mla_decode_step over a cache managed
  * as a pool of pages (the KV-cache page grows its cache as a memory pool; the
  * MLA post's reference code preallocates one contiguous buffer).  The cache

@@ -254,4 +254,8 @@ void prefill_attn_generic(const T* q_nope, const T* q_rope, const float* kv, con
                           const int64_t* kv_off, const int64_t* seq_off, int ntok, T* o,
                           const Dims& d, hipStream_t st);
 
+// Device address of the current device's copy of the static scratch array of
+// mla_decode_step_noalloc (scratch.hip).
+hipError_t noalloc_scratch_address(void** out);
+
 }  // namespace mla

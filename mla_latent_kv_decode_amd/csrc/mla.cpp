@@ -14,6 +14,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 #include <unordered_set>
 #include <vector>
@@ -35,6 +36,9 @@ namespace {
 
 constexpr size_t kAlign = 256;
 constexpr int kRing = 4;
+// Pinned bytes every staging slot gets at mla_create, so that the
+// no-allocation decode step finds its metadata room already there.
+constexpr size_t kStageInit = (size_t)256 << 10;
 
 size_t align_up(size_t v, size_t a = kAlign) { return (v + a - 1) / a * a; }
 
@@ -85,6 +89,11 @@ struct mla_ctx {
   rocblas_handle rb = nullptr;
   bool lib_gemm_ok = false;
   int lib_err = 0;
+  // the no-allocation decode step: device address of this device's static
+  // scratch array, and set while such a call runs (the staging ring must not
+  // grow then)
+  void* noalloc_ws = nullptr;
+  bool no_alloc = false;
   std::string err;
 };
 
@@ -157,6 +166,10 @@ int stage_upload(mla_ctx* h, void* dst, const void* src, size_t bytes) {
     HIP_TRY(h, hipEventSynchronize(s.ev));
     s.pending = false;
   }
+  if (s.cap < bytes && h->no_alloc)
+    return fail(h, MLA_ERR_WORKSPACE,
+                "metadata of %zu bytes exceed the %zu pinned bytes staged at mla_create", bytes,
+                s.cap);
   if (s.cap < bytes) {
     if (s.host) HIP_TRY(h, hipHostFree(s.host));
     s.host = nullptr;
@@ -876,6 +889,24 @@ static void yarn_table(const mla_config* cfg, double* theta) {
   }
 }
 
+// Device address of each device's static scratch array (scratch.hip), taken
+// once per device with that device current.
+static std::mutex g_scratch_mu;
+static void* g_scratch[256];
+
+static hipError_t noalloc_setup(int dev, void** out) {
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (dev < 0 || dev >= 256) return hipErrorInvalidDevice;
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    const hipError_t e = mla::noalloc_scratch_address(&p);
+    if (e != hipSuccess) return e;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return hipSuccess;
+}
+
 int mla_create(const mla_config* cfg, void* stream, mla_handle* out) {
   if (!out) return MLA_ERR_INVALID_ARG;
   *out = nullptr;
@@ -906,6 +937,18 @@ int mla_create(const mla_config* cfg, void* stream, mla_handle* out) {
   h->mfma = cfg->dtype == MLA_BF16 && d.dc == 512 && d.dr == 64 && d.H % 16 == 0;
   h->kv8 = cfg->kv_storage == MLA_KV_FP8_E4M3;
   h->n_in = d.R + (d.dq ? d.dq : qw_of(d));
+  // set-up of the no-allocation decode step: the scratch address and a
+  // staging ring that already holds its pinned memory and events
+  hipError_t e = noalloc_setup(dev, &h->noalloc_ws);
+  for (auto& sl : h->ring) {
+    if (e == hipSuccess) e = hipHostMalloc(&sl.host, kStageInit, hipHostMallocDefault);
+    if (e == hipSuccess) sl.cap = kStageInit;
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&sl.ev, hipEventDisableTiming);
+  }
+  if (e != hipSuccess) {
+    (void)mla_destroy(h);
+    return MLA_ERR_HIP;
+  }
   *out = h;
   return MLA_OK;
 }
@@ -1487,6 +1530,35 @@ int mla_decode_step(mla_handle h, const void* hidden, const int32_t* pos, const 
                     void* ws, size_t ws_bytes) {
   return decode_common(h, hidden, pos, seq_off, seq_len, B, cache, cache_rows, out, ws, ws_bytes,
                        true);
+}
+
+int mla_decode_step_noalloc(mla_handle h, const void* hidden, const int32_t* pos,
+                            const int64_t* seq_off, const int32_t* seq_len, int32_t B, void* cache,
+                            int64_t cache_rows, void* out) {
+  if (!h) return MLA_ERR_INVALID_ARG;
+  const char* what = "decode_step_noalloc";
+  int rc = mla_decode_check(&h->cfg, pos, seq_off, seq_len, B, cache_rows);
+  if (!rc) rc = contig_write_check(seq_off, seq_len, B, 1);
+  if (rc) return fail(h, rc, "%s: %s (B=%d, cache_rows=%lld)", what, mla_status_string(rc), B,
+                      (long long)cache_rows);
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  HIP_TRY(h, hipStreamIsCapturing(h->stream, &cs));
+  if (cs != hipStreamCaptureStatusNone)
+    return fail(h, MLA_ERR_STATE, "%s: the stream is being captured (the step's metadata "
+                "would need pinned memory of their own)", what);
+  int64_t total = 0;
+  for (int32_t b = 0; b < B; ++b) total += seq_len[b];
+  const size_t need = mla_decode_step_workspace_bytes(h, B, total);
+  if (need > (size_t)MLA_NOALLOC_SCRATCH_BYTES)
+    return fail(h, MLA_ERR_WORKSPACE,
+                "%s: B=%d with %lld cache rows needs %zu bytes of scratch; the static scratch "
+                "holds %zu", what, B, (long long)total, need, (size_t)MLA_NOALLOC_SCRATCH_BYTES);
+  if (!h->noalloc_ws) return fail(h, MLA_ERR_STATE, "%s: no scratch address", what);
+  h->no_alloc = true;
+  rc = decode_common(h, hidden, pos, seq_off, seq_len, B, cache, cache_rows, out, h->noalloc_ws,
+                     (size_t)MLA_NOALLOC_SCRATCH_BYTES, true);
+  h->no_alloc = false;
+  return rc;
 }
 
 size_t mla_decode_ex_workspace_bytes(mla_handle h, int32_t B, int32_t q_len, int64_t total_rows,

@@ -94,6 +94,8 @@ _SIGS = {
     "mla_decode_step_workspace_bytes": (ctypes.c_size_t, [_P, ctypes.c_int32, ctypes.c_int64]),
     "mla_decode_step": (ctypes.c_int, [_P, _P, _I32P, _I64P, _I32P, ctypes.c_int32, _P,
                                        ctypes.c_int64, _P, _P, ctypes.c_size_t]),
+    "mla_decode_step_noalloc": (ctypes.c_int, [_P, _P, _I32P, _I64P, _I32P, ctypes.c_int32, _P,
+                                               ctypes.c_int64, _P]),
     "mla_decode_paged": (ctypes.c_int, [_P, _P, _I32P, _I32P, ctypes.c_int32, ctypes.c_int32,
                                         _I32P, ctypes.c_int32, _P, ctypes.c_int64, _P, _P,
                                         ctypes.c_size_t]),
@@ -417,6 +419,22 @@ class MLALayer:
         rc = self.lib.mla_decode_step(self.h, _ptr(hidden), pos_p, so_p, sl_p, B, _ptr(cache),
                                       int(cache.shape[0]), _ptr(out), wsp, wsn)
         self._check(rc, self.h, "mla_decode_step")
+        return out
+
+    def decode_step_noalloc(self, hidden, seq_off, seq_len, cache, out=None):
+        """decode_step with the library's static scratch instead of a
+        workspace (mla_decode_step_noalloc)."""
+        import torch
+        self._sync_stream()
+        B = int(hidden.shape[0])
+        sl_a, sl_p = _i32(seq_len)
+        pos_a, pos_p = _i32(sl_a - 1)
+        so_a, so_p = _i64(seq_off)
+        if out is None:
+            out = torch.empty((B, self.dims.hidden), dtype=self.torch_dtype, device=self.device)
+        rc = self.lib.mla_decode_step_noalloc(self.h, _ptr(hidden), pos_p, so_p, sl_p, B,
+                                              _ptr(cache), int(cache.shape[0]), _ptr(out))
+        self._check(rc, self.h, "mla_decode_step_noalloc")
         return out
 
     # -- P1
