@@ -96,6 +96,13 @@ void gemm_bf16_mfma(const bf16* A, int64_t lda, int64_t sA, const bf16* W, int64
                     const GemmOut& out, hipStream_t st);
 int gemm_bf16_ksplit(int M, int N, int K, int batch, int n_cu);
 
+// Large-tile GEMM (k_gemm_big.hip) for many rows: C = alpha A W^T, batch 1,
+// K a multiple of 32, lda / ldw multiples of 8, out.ldo a multiple of 4.
+// gemm_big_bn: the tile width (256 or 128) it picks for an M x N product.
+int gemm_big_bn(int M, int N, int n_cu);
+void gemm_big(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int M, int N, int K,
+              const GemmOut& out, int n_cu, hipStream_t st);
+
 // Split-K partial sums as a consumer sees them: element (z, row, col) at
 // p[z * zs + row * ld + col], summed over z = 0..ks-1 in order.
 struct Part {

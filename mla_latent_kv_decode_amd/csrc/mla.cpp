@@ -6,7 +6,6 @@
 // memory the handle owns (a small ring, so a call never overwrites staging
 // data an earlier asynchronous copy may still be reading).
 #include <hip/hip_runtime.h>
-#include <rocblas/rocblas.h>
 
 #include <math.h>
 #include <stdarg.h>
@@ -82,13 +81,9 @@ struct mla_ctx {
   std::vector<hipEvent_t> tev;
   int t_next = 0;
   int64_t t_count = 0;
-  // library GEMM (rocBLAS) for the large-M projections of prefill and bulk
-  // appends; created on first use.  lib_gemm_ok is set only while such a call
-  // runs on a stream that is not being captured, so decode calls and captured
-  // graphs never reach it.
-  rocblas_handle rb = nullptr;
-  bool lib_gemm_ok = false;
-  int lib_err = 0;
+  // every dimension that strides a GEMM operand or output is a multiple of 8
+  // elements (16-byte rows for the large-tile GEMM)
+  bool dims_aligned = false;
   // the no-allocation decode step: device address of this device's static
   // scratch array, and set while such a call runs (the staging ring must not
   // grow then)
@@ -133,11 +128,6 @@ struct DeviceGuard {
 };
 
 int check_launch(mla_ctx* h, const char* what) {
-  if (h->lib_err) {
-    const int le = h->lib_err;
-    h->lib_err = 0;
-    return fail(h, MLA_ERR_HIP, "%s: rocBLAS GEMM failed (status %d)", what, le);
-  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(h, MLA_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
   return MLA_OK;
@@ -203,59 +193,27 @@ bool mfma_gemm(const mla_ctx* h, int N, int K) {
   return h->cfg.dtype == MLA_BF16 && N % 16 == 0 && K % 128 == 0;
 }
 
-// Projections with many rows (prefill) are plain GEMMs with enough work for a
-// library kernel's large tiles: rocBLAS, bf16 in, fp32 accumulation.
-constexpr int kLibGemmMinM = 256;
-bool lib_gemm(const mla_ctx* h, int M) {
-  return h->lib_gemm_ok && h->cfg.dtype == MLA_BF16 && M >= kLibGemmMinM;
+// Projections with many rows (prefill, bulk appends) are plain GEMMs with
+// enough work for the large-tile kernel: at least 256 rows and enough tiles to
+// fill half the compute units.
+constexpr int kBigGemmMinM = 256;
+bool big_gemm(const mla_ctx* h, int M, int N, int K, int batch) {
+  if (h->cfg.dtype != MLA_BF16 || !h->dims_aligned || batch != 1 || M < kBigGemmMinM ||
+      K % 32 != 0 || N % 4 != 0)
+    return false;
+  const int bn = mla::gemm_big_bn(M, N, h->n_cu);
+  const long tiles = (long)((M + 255) / 256) * ((N + bn - 1) / bn);
+  return tiles * 2 >= h->n_cu;
 }
 
 int gemm_ks(const mla_ctx* h, int M, int N, int K, int batch) {
-  if (lib_gemm(h, M)) return 1;
+  if (big_gemm(h, M, N, K, batch)) return 1;
   return mfma_gemm(h, N, K) ? mla::gemm_bf16_ksplit(M, N, K, batch, h->n_cu) : 1;
-}
-
-// Enables the library GEMM for the duration of a call (prefill, bulk append),
-// unless the stream is being captured into a graph.
-struct LibGemmScope {
-  mla_ctx* h;
-  explicit LibGemmScope(mla_ctx* c) : h(c) {
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    h->lib_gemm_ok =
-        hipStreamIsCapturing(h->stream, &cs) == hipSuccess && cs == hipStreamCaptureStatusNone;
-  }
-  ~LibGemmScope() { h->lib_gemm_ok = false; }
-};
-
-// C (row-major M x N, row stride out.ldo) = alpha A W^T with A (M x K, lda) and
-// W (N x K, ldw) row-major: in rocBLAS's column-major terms C^T = W^T-op(W) A.
-void rocblas_out(mla_ctx* h, const bf16* A, int64_t lda, int64_t sA, const bf16* W, int64_t ldw,
-                 int64_t sW, int M, int N, int K, int batch, const mla::GemmOut& out) {
-  rocblas_status st = rocblas_status_success;
-  if (!h->rb) st = rocblas_create_handle(&h->rb);
-  if (st == rocblas_status_success) st = rocblas_set_stream(h->rb, h->stream);
-  const float alpha = out.alpha, beta = 0.f;
-  void* c = out.f32 ? (void*)out.f32 : (void*)out.b16;
-  const rocblas_datatype ct = out.f32 ? rocblas_datatype_f32_r : rocblas_datatype_bf16_r;
-  if (st == rocblas_status_success) {
-    if (batch == 1)
-      st = rocblas_gemm_ex(h->rb, rocblas_operation_transpose, rocblas_operation_none, N, M, K,
-                           &alpha, W, rocblas_datatype_bf16_r, ldw, A, rocblas_datatype_bf16_r,
-                           lda, &beta, c, ct, out.ldo, c, ct, out.ldo, rocblas_datatype_f32_r,
-                           rocblas_gemm_algo_standard, 0, 0);
-    else
-      st = rocblas_gemm_strided_batched_ex(
-          h->rb, rocblas_operation_transpose, rocblas_operation_none, N, M, K, &alpha, W,
-          rocblas_datatype_bf16_r, ldw, sW, A, rocblas_datatype_bf16_r, lda, sA, &beta, c, ct,
-          out.ldo, out.so, c, ct, out.ldo, out.so, batch, rocblas_datatype_f32_r,
-          rocblas_gemm_algo_standard, 0, 0);
-  }
-  if (st != rocblas_status_success && !h->lib_err) h->lib_err = (int)st;
 }
 
 // fp32 scratch floats of gemm_out (split-K partials, or the VALU path's C)
 size_t out_scratch(const mla_ctx* h, int M, int N, int K, int batch) {
-  if (lib_gemm(h, M)) return 0;
+  if (big_gemm(h, M, N, K, batch)) return 0;
   const int ks = gemm_ks(h, M, N, K, batch);
   if (mfma_gemm(h, N, K) && ks == 1) return 0;
   return (size_t)ks * batch * M * N;
@@ -272,8 +230,8 @@ void gemm_out(mla_ctx* h, const T* A, int64_t lda, int64_t sA, const T* W, int64
               int64_t sW, int M, int N, int K, int batch, const mla::GemmOut& out,
               float* scratch) {
   if constexpr (sizeof(T) == 2) {
-    if (lib_gemm(h, M)) {
-      rocblas_out(h, A, lda, sA, W, ldw, sW, M, N, K, batch, out);
+    if (big_gemm(h, M, N, K, batch)) {
+      mla::gemm_big(A, lda, W, ldw, M, N, K, out, h->n_cu, h->stream);
       return;
     }
     if (mfma_gemm(h, N, K)) {
@@ -293,8 +251,9 @@ template <typename T>
 mla::Part gemm_part(mla_ctx* h, const T* A, int64_t lda, const T* W, int64_t ldw, int M,
                     int N, int K, float* part) {
   if constexpr (sizeof(T) == 2) {
-    if (lib_gemm(h, M)) {
-      rocblas_out(h, A, lda, 0, W, ldw, 0, M, N, K, 1, mla::GemmOut{part, nullptr, N, 0, 1.f});
+    if (big_gemm(h, M, N, K, 1)) {
+      mla::gemm_big(A, lda, W, ldw, M, N, K, mla::GemmOut{part, nullptr, N, 0, 1.f}, h->n_cu,
+                    h->stream);
       return mla::Part{part, 1, N, (int64_t)M * N};
     }
     if (mfma_gemm(h, N, K)) {
@@ -937,6 +896,9 @@ int mla_create(const mla_config* cfg, void* stream, mla_handle* out) {
   h->mfma = cfg->dtype == MLA_BF16 && d.dc == 512 && d.dr == 64 && d.H % 16 == 0;
   h->kv8 = cfg->kv_storage == MLA_KV_FP8_E4M3;
   h->n_in = d.R + (d.dq ? d.dq : qw_of(d));
+  h->dims_aligned = d.D % 8 == 0 && d.dc % 8 == 0 && d.R % 8 == 0 && d.dq % 8 == 0 &&
+                    qw_of(d) % 8 == 0 && (d.H * d.dv) % 8 == 0 &&
+                    (d.H * (d.dn + d.dv)) % 8 == 0;
   // set-up of the no-allocation decode step: the scratch address and a
   // staging ring that already holds its pinned memory and events
   hipError_t e = noalloc_setup(dev, &h->noalloc_ws);
@@ -976,7 +938,6 @@ int mla_destroy(mla_handle h) {
   }
   for (void* p : h->captured) (void)hipHostFree(p);
   drop_timing(h);
-  if (h->rb) (void)rocblas_destroy_handle(h->rb);
   delete h;
   return MLA_OK;
 }
@@ -1129,7 +1090,6 @@ int mla_append_latent(mla_handle h, const void* hidden, const int32_t* pos, cons
   if (rc) return fail(h, rc, "append: %s (T=%d, cache_rows=%lld)", mla_status_string(rc), T,
                       (long long)cache_rows);
   if (!h->absorbed) return fail(h, MLA_ERR_STATE, "append before mla_absorb_weights");
-  LibGemmScope lib_scope(h);  // many rows: the kv_a projection on the library GEMM
   const AppendLayout L = append_layout(h, T);
   if ((rc = check_ws(h, ws, ws_bytes, L.total))) return rc;
   DeviceGuard g(h->device);
@@ -1667,7 +1627,6 @@ static int run_prefill(mla_ctx* h, const T* hidden, int ntok, int B, const int32
                        int ntiles) {
   const Dims& d = h->d;
   const int qw = qw_of(d);
-  LibGemmScope lib_scope(h);
   char* meta = at<char>(ws, L.meta);
   const int32_t* tok_seq = reinterpret_cast<const int32_t*>(meta);
   const int32_t* tok_pos = reinterpret_cast<const int32_t*>(meta + align_up((size_t)ntok * 4));

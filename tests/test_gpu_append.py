@@ -21,12 +21,15 @@ def _sentinel_cache(rows, width):
                       device="cuda").view(torch.bfloat16)
 
 
-@pytest.mark.parametrize("dims", [synth.V2_LITE, synth.V3])
-def test_append_rows_and_indexing(dims):
+@pytest.mark.parametrize("dims,T", [(synth.V2_LITE, 300), (synth.V3, 300),
+                                    (synth.V2_LITE, 7000), (synth.V3, 4500)])
+def test_append_rows_and_indexing(dims, T):
+    """T = 300 takes the split-K tile GEMM for the kv_a projection; 7000 and
+    4500 rows (not multiples of the 256-row tile) take the large-tile GEMM."""
     import torch
     w = synth.make_weights(dims, 0.02, "bf16", random_gains=True)
     layer = make_layer(dims, "bf16", w)
-    rows, T = 5000, 300
+    rows = max(5000, 2 * T)
     rng = np.random.default_rng(11)
     slot = rng.choice(rows, size=T, replace=False).astype(np.int64)
     pos = rng.integers(0, 40000, size=T).astype(np.int32)

@@ -61,6 +61,17 @@ def test_v3_prefill_small():
     run_prefill_case(synth.V3, "bf16", 0.02, [0, 21], [24, 9])
 
 
+@pytest.mark.timeout(300)
+def test_v3_prefill_ragged_large_tiles():
+    """5,500 new tokens and 6,500 key rows (neither a multiple of the 256-row
+    GEMM tile): every projection and the expansion run on the large-tile
+    GEMM with a ragged last row tile; sampled queries of both sequences,
+    including the last ones."""
+    q0 = np.unique(np.concatenate([np.arange(0, 3000, 97), np.arange(2990, 3000)]))
+    q1 = np.unique(np.concatenate([np.arange(0, 2500, 89), np.arange(2490, 2500)]))
+    run_prefill_case(synth.V3, "bf16", 0.02, [0, 1000], [3000, 2500], query_subset=[q0, q1])
+
+
 @pytest.mark.timeout(600)
 def test_v3_prefill_4x4096_full_size():
     """The V3 chunked prefill at its full size (4 sequences x 4096 new tokens
