@@ -73,35 +73,37 @@ typedef short s16x8_t __attribute__((ext_vector_type(8)));
 // rows 8(I-32) .. +7.  Rows past `last` re-read it (their scores are masked).
 // jump16: bytes added to the address of rows 16 .. 31 (a query tile holding
 // two tokens' 16 heads: their q_cat rows are H rows apart; 0 for cache tiles)
-template <int I>
+template <int I, bool NT>
 __device__ __forceinline__ void tile_copy(const char* base, int last, uint32_t stage, int lane,
                                           int jump16) {
   if constexpr (I < TR) {
     const int r = I <= last ? I : last;
-    dma16(base + r * (RW * 2) + (r >= 16 ? jump16 : 0) + ((lane ^ lat_swz(I & 15)) << 4),
+    dma16h<NT>(base + r * (RW * 2) + (r >= 16 ? jump16 : 0) + ((lane ^ lat_swz(I & 15)) << 4),
           stage + I * 1024);
   } else {
     constexpr int J = I - TR;
     int r = 8 * J + (lane >> 3);
     const int cc = (lane & 7) ^ rope_swz(r & 15);
     r = r <= last ? r : last;
-    dma16(base + r * (RW * 2) + (r >= 16 ? jump16 : 0) + 1024 + (cc << 4),
+    dma16h<NT>(base + r * (RW * 2) + (r >= 16 ? jump16 : 0) + 1024 + (cc << 4),
           stage + ROPE_OFF + J * 1024);
   }
 }
 
-template <int P, int... U>
+template <int P, bool NT, int... U>
 __device__ __forceinline__ void producer_copies(const char* base, int last, uint32_t stage,
                                                 int lane, int jump16,
                                                 std::integer_sequence<int, U...>) {
-  (tile_copy<P * LPW + U>(base, last, stage, lane, jump16), ...);
+  (tile_copy<P * LPW + U, NT>(base, last, stage, lane, jump16), ...);
 }
 
+// NT: the non-temporal copy (cache rows no other workgroup of the part reads)
+template <bool NT>
 __device__ __forceinline__ void issue_tile(const char* base, int last, uint32_t stage, int p,
                                            int lane, int jump16 = 0) {
   const auto seq = std::make_integer_sequence<int, LPW>{};
-  if (p == 0) producer_copies<0>(base, last, stage, lane, jump16, seq);
-  else producer_copies<1>(base, last, stage, lane, jump16, seq);
+  if (p == 0) producer_copies<0, NT>(base, last, stage, lane, jump16, seq);
+  else producer_copies<1, NT>(base, last, stage, lane, jump16, seq);
 }
 
 __device__ __forceinline__ bf16x8_t cat_bf16(s16x4_t lo, s16x4_t hi) {
@@ -158,11 +160,12 @@ decode_core_ring_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
       if (ik == 0) {
         const char* qb = reinterpret_cast<const char*>(
             q_cat + ((int64_t)(iw.b * q_len + tok0) * H + hg * 16) * RW);
-        issue_tile(qb, 16 * TOK - 1, stage, p, lane, (H - 16) * RW * 2);
+        issue_tile<false>(qb, 16 * TOK - 1, stage, p, lane, (H - 16) * RW * 2);
       } else {
         const int t = ik - 1;
         const char* rb = reinterpret_cast<const char*>(cache + next_row * RW);
-        issue_tile(rb, iw.n - t * TR - 1, stage, p, lane);
+        if (NG == 1) issue_tile<true>(rb, iw.n - t * TR - 1, stage, p, lane);
+        else issue_tile<false>(rb, iw.n - t * TR - 1, stage, p, lane);
       }
       // the cache row of the segment's next tile, one issue ahead (a paged
       // cache's page lookup is a load)

@@ -109,22 +109,22 @@ __device__ __forceinline__ constexpr int f8(int r) { return (r & 15) ^ (((r >> 4
 // Copy I of a row tile whose first row is at `base` (byte address) and whose
 // last valid row is `last`; rows past `last` re-read it (their scores are
 // masked).
-template <int I>
+template <int I, bool NT>
 __device__ __forceinline__ void row_copy(const char* base, int last, uint32_t stage, int lane) {
   if constexpr (I < 16) {  // latent codes of rows 2I (lanes 0-31) and 2I + 1
     const int r = 2 * I + (lane >> 5);
     const int rs = r <= last ? r : last;
-    dma16(base + rs * RB + (((lane & 31) ^ f8(r)) << 4), stage + I * 1024);
+    dma16h<NT>(base + rs * RB + (((lane & 31) ^ f8(r)) << 4), stage + I * 1024);
   } else if constexpr (I < 20) {  // rope of rows 8J .. 8J + 7
     constexpr int J = I - 16;
     const int r = 8 * J + (lane >> 3);
     const int cc = (lane & 7) ^ rope_swz(r & 15);
     const int rs = r <= last ? r : last;
-    dma16(base + rs * RB + 512 + (cc << 4), stage + ROPE_OFF + J * 1024);
+    dma16h<NT>(base + rs * RB + 512 + (cc << 4), stage + ROPE_OFF + J * 1024);
   } else {  // scales of rows 0 .. 31 (twice); the spare copy I = 21 repeats it
     const int r = lane & 31;
     const int rs = r <= last ? r : last;
-    dma16(base + rs * RB + 640, stage + SC_OFF);
+    dma16h<NT>(base + rs * RB + 640, stage + SC_OFF);
   }
 }
 
@@ -144,10 +144,10 @@ __device__ __forceinline__ void query_copy(const char* qb, uint32_t stage, int l
   }
 }
 
-template <int P, int... U>
+template <int P, bool NT, int... U>
 __device__ __forceinline__ void producer_rows(const char* base, int last, uint32_t stage, int lane,
                                               std::integer_sequence<int, U...>) {
-  (row_copy<P * LPW + U>(base, last, stage, lane), ...);
+  (row_copy<P * LPW + U, NT>(base, last, stage, lane), ...);
 }
 
 template <int P, int... U>
@@ -156,11 +156,13 @@ __device__ __forceinline__ void producer_query(const char* qb, uint32_t stage, i
   (query_copy<P * LPW + U>(qb, stage, lane), ...);
 }
 
+// NT: the non-temporal copy (rows no other workgroup of the part reads)
+template <bool NT>
 __device__ __forceinline__ void issue_rows(const char* base, int last, uint32_t stage, int p,
                                            int lane) {
   const auto seq = std::make_integer_sequence<int, LPW>{};
-  if (p == 0) producer_rows<0>(base, last, stage, lane, seq);
-  else producer_rows<1>(base, last, stage, lane, seq);
+  if (p == 0) producer_rows<0, NT>(base, last, stage, lane, seq);
+  else producer_rows<1, NT>(base, last, stage, lane, seq);
 }
 
 __device__ __forceinline__ void issue_query(const char* qb, uint32_t stage, int p, int lane) {
@@ -230,8 +232,9 @@ decode_core_ring8_k(const bf16* __restrict__ q_cat, const uint8_t* __restrict__ 
                     stage, p, lane);
       } else {
         const int t = ik - 1;
-        issue_rows(reinterpret_cast<const char*>(cache) + next_row * RB, iw.n - t * TR - 1, stage,
-                   p, lane);
+        const char* rb = reinterpret_cast<const char*>(cache) + next_row * RB;
+        if (HG * q_len == 1) issue_rows<true>(rb, iw.n - t * TR - 1, stage, p, lane);
+        else issue_rows<false>(rb, iw.n - t * TR - 1, stage, p, lane);
       }
       // the cache row of the segment's next tile, one issue ahead (a paged
       // cache's page lookup is a load)

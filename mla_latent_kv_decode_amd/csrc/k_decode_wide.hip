@@ -48,24 +48,24 @@ typedef short s16x8_t __attribute__((ext_vector_type(8)));
 // Load I of a tile whose first row is at `base` and whose last valid row is
 // `last`: I < 32 copies the latent part of row I (source chunk lane ^ lat_swz(I & 15)),
 // I >= 32 the rope parts of rows 8j .. 8j+7.  Rows past `last` re-read it.
-template <int I>
+template <int I, bool NT>
 __device__ __forceinline__ void tile_load(const char* base, int last, uint32_t stage, int lane) {
   if constexpr (I < TR) {
     const int r = I <= last ? I : last;
-    dma16(base + r * (RW * 2) + ((lane ^ lat_swz(I & 15)) << 4), stage + I * 1024);
+    dma16h<NT>(base + r * (RW * 2) + ((lane ^ lat_swz(I & 15)) << 4), stage + I * 1024);
   } else {
     constexpr int J = I - TR;
     int r = 8 * J + (lane >> 3);
     const int cc = (lane & 7) ^ rope_swz(r & 15);
     r = r <= last ? r : last;
-    dma16(base + r * (RW * 2) + 1024 + (cc << 4), stage + ROPE_OFF + J * 1024);
+    dma16h<NT>(base + r * (RW * 2) + 1024 + (cc << 4), stage + ROPE_OFF + J * 1024);
   }
 }
 
-template <int W, int... U>
+template <int W, bool NT, int... U>
 __device__ __forceinline__ void wave_loads(const char* base, int last, uint32_t stage, int lane,
                                            std::integer_sequence<int, U...>) {
-  (tile_load<W * LPW + U>(base, last, stage, lane), ...);
+  (tile_load<W * LPW + U, NT>(base, last, stage, lane), ...);
 }
 
 // The lane index is re-read through an opaque instruction so the per-lane load
@@ -77,14 +77,16 @@ __device__ __forceinline__ int lane_id_opaque() {
   return l;
 }
 
+// NT: the non-temporal copy (cache rows no other workgroup of the part reads)
+template <bool NT>
 __device__ __forceinline__ void issue_tile(const char* base, int last, uint32_t stage, int wave) {
   const int lane = lane_id_opaque();
   const auto seq = std::make_integer_sequence<int, LPW>{};
   switch (wave) {
-    case 0: wave_loads<0>(base, last, stage, lane, seq); break;
-    case 1: wave_loads<1>(base, last, stage, lane, seq); break;
-    case 2: wave_loads<2>(base, last, stage, lane, seq); break;
-    case 3: wave_loads<3>(base, last, stage, lane, seq); break;
+    case 0: wave_loads<0, NT>(base, last, stage, lane, seq); break;
+    case 1: wave_loads<1, NT>(base, last, stage, lane, seq); break;
+    case 2: wave_loads<2, NT>(base, last, stage, lane, seq); break;
+    case 3: wave_loads<3, NT>(base, last, stage, lane, seq); break;
     default: break;
   }
 }
@@ -137,11 +139,17 @@ decode_core_wide_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
     const int nv = token_rows(wk, q_len, tok);  // rows this token sees
     const int ntile = (n + TR - 1) / TR;
     const int64_t wrow = wk.row;
+    // rows no other workgroup of the part streams take the non-temporal copy
+    const bool once = WG * q_len == 1;
+    auto issue = [&](int t) {
+      const char* base = reinterpret_cast<const char*>(cache + seg_row(mt, wrow, t * TR) * RW);
+      const uint32_t stage = lds0 + (t % NST) * ST_BYTES;
+      if (once) issue_tile<true>(base, n - t * TR - 1, stage, wave);
+      else issue_tile<false>(base, n - t * TR - 1, stage, wave);
+    };
 #pragma unroll
     for (int t = 0; t < NST - 1; ++t)
-      if (t < ntile)
-        issue_tile(reinterpret_cast<const char*>(cache + seg_row(mt, wrow, t * TR) * RW),
-                   n - t * TR - 1, lds0 + t * ST_BYTES, wave);
+      if (t < ntile) issue(t);
     DecodeWork nx = wk;
     if (wk.next >= 0) nx = load_work(works + wk.next);
 
@@ -178,9 +186,7 @@ decode_core_wide_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
       else if (t + 1 < ntile) wait_vmcnt<LPW>();
       else wait_vmcnt<0>();
       __syncthreads();  // tile t is in LDS; every wave is done with tile t-1
-      if (t + NST - 1 < ntile)
-        issue_tile(reinterpret_cast<const char*>(cache + seg_row(mt, wrow, (t + NST - 1) * TR) * RW),
-                   n - (t + NST - 1) * TR - 1, lds0 + ((t + NST - 1) % NST) * ST_BYTES, wave);
+      if (t + NST - 1 < ntile) issue(t + NST - 1);
       const char* st = lds + (t % NST) * ST_BYTES;
       const int row0 = t * TR;
       // ---- S^T = K . Q^T for both 16-row blocks, K fragments read once per head group
