@@ -21,6 +21,7 @@
 // fp32 store, or the query finish (per head: the nope part stored, the rope
 // part rotated and scaled into q_cat).  The 16-row blocks of a column tile are
 // numbered 8 apart, so they run on one XCD and share its L2 for the weights.
+#include <algorithm>
 #include <atomic>
 
 #include "decode_dev.h"
@@ -65,14 +66,36 @@ __device__ __forceinline__ void chunk_copy(int i, const bf16* W, int64_t ldw, in
   dma16(src + k0 + 8 * c, stage + (uint32_t)i * 1024);
 }
 
+// The extra blocks of a launch that carries a HostCopy: block `blk` of them
+// copies words blk * 256 + threadIdx.x, then every (blocks * 256)-th, four
+// loads in flight per thread.
+__device__ __forceinline__ void host_copy(const HostCopy& hc, int blk) {
+  const uint4* src = static_cast<const uint4*>(hc.src);
+  uint4* dst = static_cast<uint4*>(hc.dst);
+  const int stride = hc.blocks * NWV * 64;
+  for (int i0 = blk * NWV * 64 + (int)threadIdx.x; i0 < hc.n16; i0 += 4 * stride) {
+    uint4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (i0 + u * stride < hc.n16) v[u] = src[i0 + u * stride];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (i0 + u * stride < hc.n16) dst[i0 + u * stride] = v[u];
+  }
+}
+
 template <int MR, class Epi>
 __global__ void __launch_bounds__(NWV * 64)
 gemm_stream_k(const bf16* __restrict__ A, int64_t lda, const bf16* __restrict__ W, int64_t ldw,
-              int M, int N, int K, int mtiles, Epi epi) {
+              int M, int N, int K, int mtiles, Epi epi, HostCopy hc) {
   constexpr int ST_BYTES = Tile<MR>::ST_BYTES, CPW = Tile<MR>::CPW, NMB = MR / 16;
   __shared__ __attribute__((aligned(1024))) char lds[NST * ST_BYTES];
   // block -> (column tile, row tile); the row tiles of a column tile share an XCD
   const int bid = blockIdx.x;
+  if (hc.n16 > 0 && bid >= hc.first_block) {
+    host_copy(hc, bid - hc.first_block);
+    return;
+  }
   const int mt = (bid / kXcds) % mtiles;
   const int ntile = (bid / (kXcds * mtiles)) * kXcds + bid % kXcds;
   const int n0 = ntile * NT, m0 = MR * mt;
@@ -221,16 +244,20 @@ namespace skn {
 // compute unit).
 template <class Epi>
 void launch_stream(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int M, int N, int K,
-                   const Epi& epi, hipStream_t st) {
+                   const Epi& epi, hipStream_t st, HostCopy hc = HostCopy{}) {
   const int ntiles = (N + NT - 1) / NT;
   const int nt8 = (ntiles + kXcds - 1) / kXcds * kXcds;
   const int m32 = (M + 31) / 32;
   if (M > 16 && ntiles * m32 * 4 >= device_cu_count() * 3) {
-    gemm_stream_k<32, Epi><<<nt8 * m32, NWV * 64, 0, st>>>(A, lda, W, ldw, M, N, K, m32, epi);
+    hc.first_block = nt8 * m32;
+    gemm_stream_k<32, Epi><<<nt8 * m32 + (hc.n16 > 0 ? hc.blocks : 0), NWV * 64, 0, st>>>(
+        A, lda, W, ldw, M, N, K, m32, epi, hc);
     return;
   }
   const int mtiles = (M + 15) / 16;
-  gemm_stream_k<16, Epi><<<nt8 * mtiles, NWV * 64, 0, st>>>(A, lda, W, ldw, M, N, K, mtiles, epi);
+  hc.first_block = nt8 * mtiles;
+  gemm_stream_k<16, Epi><<<nt8 * mtiles + (hc.n16 > 0 ? hc.blocks : 0), NWV * 64, 0, st>>>(
+      A, lda, W, ldw, M, N, K, mtiles, epi, hc);
 }
 
 // ---- projection finish: blocks [0, nab) absorbed query tiles, then nap
@@ -330,13 +357,15 @@ void skinny_store(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int M,
 }
 
 void skinny_f32(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int M, int N, int K,
-                float* out, int64_t ldo, hipStream_t st) {
-  skn::launch_stream(A, lda, W, ldw, M, N, K, skn::EpiF32{out, ldo}, st);
+                float* out, int64_t ldo, hipStream_t st, const HostCopy& hc) {
+  skn::launch_stream(A, lda, W, ldw, M, N, K, skn::EpiF32{out, ldo}, st, hc);
 }
+
+int host_copy_blocks(int n16) { return std::min(16, std::max(1, (n16 + 1023) / 1024)); }
 
 void skinny_query(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int M, int N, int K,
                   float* a, int R, bf16* q_nope, bf16* q_cat, const int32_t* pos_host,
-                  const Dims& d, const RopeTab& rt, hipStream_t st) {
+                  const Dims& d, const RopeTab& rt, hipStream_t st, const HostCopy& hc) {
   skn::EpiQuery e;
   e.a = a;
   e.R = R;
@@ -349,7 +378,7 @@ void skinny_query(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int M,
   e.dc = d.dc;
   e.scale = d.scale;
   e.rt = rt;
-  skn::launch_stream(A, lda, W, ldw, M, N, K, e, st);
+  skn::launch_stream(A, lda, W, ldw, M, N, K, e, st, hc);
 }
 
 void decode_finish(const bf16* q_nope, const bf16* w_ukT, bf16* q_cat, int B, bool absorb,

@@ -81,6 +81,18 @@ void gemm_generic(const T* A, int64_t lda, int64_t sA, const T* W, int64_t ldw, 
                   float* C, int M, int N, int K, int batch, int ksplit, hipStream_t st);
 // Fused GEMM epilogue: out[bt*so + m*ldo + n] = alpha * C (fp32 if f32 is set,
 // else rounded to bf16 into b16).
+// Host-to-device copy folded into a kernel launch: `blocks` extra blocks,
+// numbered from `first_block`, copy n16 16-byte words from pinned host memory
+// (read over the bus, zero-copy) to device memory while the kernel's other
+// blocks run.  n16 = 0: none.
+struct HostCopy {
+  const void* src = nullptr;
+  void* dst = nullptr;
+  int n16 = 0;
+  int first_block = 0;
+  int blocks = 0;
+};
+
 struct GemmOut {
   float* f32;
   bf16* b16;
@@ -155,14 +167,17 @@ void skinny_store(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int M,
                   bf16* out, int64_t ldo, float alpha, hipStream_t st);
 // out (fp32, row stride ldo) = C
 void skinny_f32(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int M, int N, int K,
-                float* out, int64_t ldo, hipStream_t st);
+                float* out, int64_t ldo, hipStream_t st, const HostCopy& hc = HostCopy{});
 // columns [0, R) of C to a (fp32, row stride R); the remaining columns are
 // query heads [nope (dn) | rope (dr)]: nope to q_nope (M, H, dn), rope rotated
 // at pos_host[row] (a host array, passed to the kernel by value) and scaled by
 // d.scale into q_cat[row][h][dc ..] (row stride H R)
 void skinny_query(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int M, int N, int K,
                   float* a, int R, bf16* q_nope, bf16* q_cat, const int32_t* pos_host,
-                  const Dims& d, const RopeTab& rt, hipStream_t st);
+                  const Dims& d, const RopeTab& rt, hipStream_t st,
+                  const HostCopy& hc = HostCopy{});
+// Blocks (of 256 threads) a HostCopy of n16 words takes.
+int host_copy_blocks(int n16);
 // One launch finishing the projections of B tokens, each part optional:
 // absorb: q_cat[t][h][0:dc] = scale * W_ukT_h q_nope[t][h] (dc = 512);
 // append: cache[slot[t]] = [RMSNorm(a[t][0:dc]) * kv_gamma | RoPE(a[t][dc:R], pos[t])];

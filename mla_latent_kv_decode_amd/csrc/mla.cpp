@@ -133,21 +133,24 @@ int check_launch(mla_ctx* h, const char* what) {
   return MLA_OK;
 }
 
-// Copy `bytes` of host data to device `dst` on the handle's stream through the
-// pinned staging ring.
-int stage_upload(mla_ctx* h, void* dst, const void* src, size_t bytes) {
-  if (bytes == 0) return MLA_OK;
-  hipStream_t st = h->stream;
+// Put `bytes` of host data into pinned staging memory the GPU can read: a
+// slot of the handle's ring (reusable once the event *ev, to be recorded after
+// the call's last reader is enqueued, has passed), or, while the stream is
+// being captured into a graph, a buffer kept for the life of the handle (the
+// graph reads it at every replay).  Staging memory is allocated coherent, so a
+// kernel may read it directly over the bus; sizes are padded to 256 bytes.
+int stage_host(mla_ctx* h, const void* src, size_t bytes, const void** pinned,
+               hipEvent_t* ev) {
+  *pinned = nullptr;
+  *ev = nullptr;
   hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-  HIP_TRY(h, hipStreamIsCapturing(st, &cap));
+  HIP_TRY(h, hipStreamIsCapturing(h->stream, &cap));
   if (cap == hipStreamCaptureStatusActive) {
-    // the graph's copy node reads this buffer at every replay: keep it for
-    // the life of the handle and never reuse it
     void* p = nullptr;
-    HIP_TRY(h, hipHostMalloc(&p, bytes, hipHostMallocDefault));
+    HIP_TRY(h, hipHostMalloc(&p, align_up(bytes), hipHostMallocCoherent));
     h->captured.push_back(p);
     memcpy(p, src, bytes);
-    HIP_TRY(h, hipMemcpyAsync(dst, p, bytes, hipMemcpyHostToDevice, st));
+    *pinned = p;
     return MLA_OK;
   }
   Staging& s = h->ring[h->ring_next];
@@ -165,14 +168,27 @@ int stage_upload(mla_ctx* h, void* dst, const void* src, size_t bytes) {
     s.host = nullptr;
     s.cap = 0;
     const size_t cap = std::max(align_up(bytes, 1 << 16), (size_t)1 << 16);
-    HIP_TRY(h, hipHostMalloc(&s.host, cap, hipHostMallocDefault));
+    HIP_TRY(h, hipHostMalloc(&s.host, cap, hipHostMallocCoherent));
     s.cap = cap;
   }
   if (!s.ev) HIP_TRY(h, hipEventCreateWithFlags(&s.ev, hipEventDisableTiming));
   memcpy(s.host, src, bytes);
-  HIP_TRY(h, hipMemcpyAsync(dst, s.host, bytes, hipMemcpyHostToDevice, st));
-  HIP_TRY(h, hipEventRecord(s.ev, st));
   s.pending = true;
+  *pinned = s.host;
+  *ev = s.ev;
+  return MLA_OK;
+}
+
+// Copy `bytes` of host data to device `dst` on the handle's stream through the
+// pinned staging memory.
+int stage_upload(mla_ctx* h, void* dst, const void* src, size_t bytes) {
+  if (bytes == 0) return MLA_OK;
+  const void* p = nullptr;
+  hipEvent_t ev = nullptr;
+  int rc = stage_host(h, src, bytes, &p, &ev);
+  if (rc) return rc;
+  HIP_TRY(h, hipMemcpyAsync(dst, p, bytes, hipMemcpyHostToDevice, h->stream));
+  if (ev) HIP_TRY(h, hipEventRecord(ev, h->stream));
   return MLA_OK;
 }
 
@@ -903,7 +919,7 @@ int mla_create(const mla_config* cfg, void* stream, mla_handle* out) {
   // staging ring that already holds its pinned memory and events
   hipError_t e = noalloc_setup(dev, &h->noalloc_ws);
   for (auto& sl : h->ring) {
-    if (e == hipSuccess) e = hipHostMalloc(&sl.host, kStageInit, hipHostMallocDefault);
+    if (e == hipSuccess) e = hipHostMalloc(&sl.host, kStageInit, hipHostMallocCoherent);
     if (e == hipSuccess) sl.cap = kStageInit;
     if (e == hipSuccess) e = hipEventCreateWithFlags(&sl.ev, hipEventDisableTiming);
   }
@@ -1269,7 +1285,7 @@ static bool q_skinny_fits(const mla_ctx* h, int B, const DecodeLayout& L) {
 
 // the first projection (positions come by value)
 static void q_skinny_first(mla_ctx* h, const bf16* x, int B, void* ws, const DecodeLayout& L,
-                           const int32_t* pos_host) {
+                           const int32_t* pos_host, const mla::HostCopy& hc) {
   const Dims& d = h->d;
   const int qw = qw_of(d);
   const int n1 = L.step ? h->n_in : (d.dq ? d.dq : qw);
@@ -1277,9 +1293,9 @@ static void q_skinny_first(mla_ctx* h, const bf16* x, int B, void* ws, const Dec
   const bf16* w1 = (const bf16*)(L.step ? h->w_in : (d.dq ? h->w_qa : h->w_q));
   if (!d.dq)
     mla::skinny_query(x, d.D, w1, d.D, B, n1, d.D, a, L.step ? d.R : 0, at<bf16>(ws, L.q_nope),
-                      at<bf16>(ws, L.q_cat), pos_host, d, h->rope, h->stream);
+                      at<bf16>(ws, L.q_cat), pos_host, d, h->rope, h->stream, hc);
   else
-    mla::skinny_f32(x, d.D, w1, d.D, B, n1, d.D, a, n1, h->stream);
+    mla::skinny_f32(x, d.D, w1, d.D, B, n1, d.D, a, n1, h->stream, hc);
 }
 
 static void q_skinny_rest(mla_ctx* h, int B, void* ws, const DecodeLayout& L,
@@ -1314,7 +1330,7 @@ template <typename T>
 static int run_decode(mla_ctx* h, const T* hidden, int B, int q_len, T* cache, T* out, void* ws,
                       const DecodeLayout& L, const DecodeMeta& mt, const DecodeMeta& mc,
                       int parts, int nseg_total, int max_chunks, const int64_t* slot_dev,
-                      const int32_t* pos_host) {
+                      const int32_t* pos_host, const mla::HostCopy& hc) {
   const Dims& d = h->d;
   float* scratch = at<float>(ws, L.scratch);
   T* q_nope = at<T>(ws, L.q_nope);
@@ -1322,7 +1338,7 @@ static int run_decode(mla_ctx* h, const T* hidden, int B, int q_len, T* cache, T
   bool fast = false;
   if constexpr (sizeof(T) == 2) {
     fast = q_skinny_fits(h, B, L);
-    if (fast) q_skinny_first(h, (const bf16*)hidden, B, ws, L, pos_host);
+    if (fast) q_skinny_first(h, (const bf16*)hidden, B, ws, L, pos_host, hc);
   }
   if constexpr (sizeof(T) == 2) {
     if (fast) q_skinny_rest(h, B, ws, L, mt, slot_dev, (bf16*)cache, pos_host);
@@ -1430,7 +1446,21 @@ static int decode_exec(mla_ctx* h, const DecodeCall& c, const char* what) {
     return fail(h, MLA_ERR_WORKSPACE, "internal: decode metadata larger than planned");
   void* ws = c.ws;
   void* meta = at<char>(ws, L.meta);
-  if ((rc = stage_upload(h, meta, blob.data(), blob.size()))) return rc;
+  // The metadata is first read by the kernel after the first projection, so
+  // when that projection is a stream GEMM, extra blocks of its launch copy the
+  // metadata from pinned memory (saving the separate copy); else a copy.
+  mla::HostCopy hc;
+  hipEvent_t stage_ev = nullptr;
+  if (!is_f32(h) && q_skinny_fits(h, Bq, L)) {
+    const void* pinned = nullptr;
+    if ((rc = stage_host(h, blob.data(), blob.size(), &pinned, &stage_ev))) return rc;
+    hc.src = pinned;
+    hc.dst = meta;
+    hc.n16 = (int)((blob.size() + 15) / 16);
+    hc.blocks = mla::host_copy_blocks(hc.n16);
+  } else if ((rc = stage_upload(h, meta, blob.data(), blob.size()))) {
+    return rc;
+  }
   DecodeMeta mt;
   mt.seq_off = at<int64_t>(meta, mo.seq_off);
   mt.seq_len = at<int32_t>(meta, mo.seq_len);
@@ -1454,9 +1484,11 @@ static int decode_exec(mla_ctx* h, const DecodeCall& c, const char* what) {
   if (is_f32(h))
     return run_decode<float>(h, (const float*)c.hidden, Bq, q_len, (float*)c.cache,
                              (float*)c.out, ws, L, mt, mc, parts, nseg_total, max_chunks,
-                             slot_dev, qpos.data());
-  return run_decode<bf16>(h, (const bf16*)c.hidden, Bq, q_len, (bf16*)c.cache, (bf16*)c.out, ws,
-                          L, mt, mc, parts, nseg_total, max_chunks, slot_dev, qpos.data());
+                             slot_dev, qpos.data(), hc);
+  rc = run_decode<bf16>(h, (const bf16*)c.hidden, Bq, q_len, (bf16*)c.cache, (bf16*)c.out, ws, L,
+                        mt, mc, parts, nseg_total, max_chunks, slot_dev, qpos.data(), hc);
+  if (stage_ev) HIP_TRY(h, hipEventRecord(stage_ev, h->stream));  // the staging slot's last reader
+  return rc;
 }
 
 static int decode_common(mla_handle h, const void* hidden, const int32_t* pos,
