@@ -5,17 +5,28 @@
 // whole 576-wide latent row, softmax, latent sum of the 512 c_kv columns), for
 // layers with many heads (DeepSeek-V3: 128), where the work per latent row is
 // 8x larger and the 16-head kernel's per-head-group workgroups would stream
-// every row 8 times from L2.  Here one workgroup of 8 waves (two per SIMD)
-// covers 128 heads: wave w owns the 16-head group w, whose accumulators and
-// query fragments fit the 256 registers a wave gets at that occupancy; the
-// second wave of a SIMD runs its MFMAs while the first reads LDS or does its
-// softmax.  The rows of a segment stream once per workgroup through a 4-stage
-// ring of 32-row tiles shared by the waves (global_load_lds_dwordx4; waves 0-3
-// each issue a quarter of every tile; one barrier per tile publishes it and
-// frees the stage the next prefetch overwrites).  Each wave sees every row of the segment for its own
-// heads, so its (max, sum, acc) state is the segment's partial: no cross-wave
-// merge.  MFMA operand layouts, the LDS swizzle of a 16-row block and the lazy
-// rescale are those of the 16-head core.
+// every row 8 times from L2.  One workgroup of 8 waves (two per SIMD) covers
+// 128 heads.  The rows of a segment stream once per workgroup through a
+// 4-stage ring of 32-row tiles shared by the waves (global_load_lds_dwordx4;
+// waves 0-3 each issue a quarter of every tile; one barrier per tile
+// publishes it and frees the stage the next prefetch overwrites).
+//
+// Per tile, two phases split the work two ways so that no wave reads the whole
+// tile twice:
+//  - scores and softmax by head: wave w takes heads 16w .. 16w + 15 (36
+//    mfma 16x16x32 over the 576 columns, K fragments read from LDS, Q^T in
+//    VGPRs; lazy reference maximum) and publishes its P fragment (1 KB, in
+//    the lane order of the latent sum's B operand), the heads' rescale
+//    factors and whether the group rescaled;
+//  - after a second barrier, the latent sum by column: wave w takes columns
+//    64w .. 64w + 63 for all 128 heads (4 transposing C^T fragments, read
+//    once, times the 8 groups' P: 32 mfma), rescaling its accumulators of a
+//    group only when that group's maximum moved.
+// Per tile and wave the LDS reads are 18 KB of K fragments, 4 KB of C^T and
+// 8 KB of P (30 KB, against 50 KB when every wave summed all 512 columns for
+// its own heads).  A segment's partial is the softmax waves' (max, sum) per
+// head and the column waves' latent sums.  MFMA operand layouts and the LDS
+// swizzle of a 16-row block are those of the 16-head core.
 #include <utility>
 
 #include "decode_dev.h"
@@ -28,8 +39,7 @@ using namespace ddev;
 constexpr int DC = 512;
 constexpr int RW = 576;
 constexpr int NW = 8;                         // waves (two per SIMD)
-constexpr int G = 1;                          // 16-head groups per wave
-constexpr int HEADS = 16 * G * NW;            // heads per workgroup
+constexpr int HEADS = 16 * NW;                // heads per workgroup
 constexpr int TR = 32;                        // rows per tile
 constexpr int NST = 4;                        // stages
 constexpr int ROPE_OFF = TR * 1024;           // latent of row r at r*1024, rope after
@@ -38,6 +48,13 @@ constexpr int NLOAD = TR + TR / 8;            // 36 wave-wide 16-byte loads per 
 constexpr int LOADERS = 4;                    // waves that issue the tile loads
 constexpr int LPW = NLOAD / LOADERS;          // 9 per loading wave
 static_assert(NLOAD % LOADERS == 0 && LOADERS <= NW, "tile loads split evenly");
+// exchange area after the ring: every head group's P fragment (1 KB, lane
+// order), the per-head rescale factors and the per-group rescale flags
+constexpr int XP_OFF = NST * ST_BYTES;
+constexpr int XA_OFF = XP_OFF + NW * 1024;
+constexpr int XF_OFF = XA_OFF + HEADS * 4;
+constexpr int LDS_BYTES = XF_OFF + NW * 4;
+constexpr int CB_W = 32 / NW;                  // 16-column blocks of the latent sum per wave
 constexpr float kRescale = 8.0f;
 constexpr int kXcds = 8;
 
@@ -95,18 +112,19 @@ __global__ void __launch_bounds__(512, 1)
 decode_core_wide_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cache, DecodeMeta mt,
                    float* __restrict__ acc_out, float* __restrict__ ml_out, int H, int nparts,
                    int q_len, int nseg_total) {
-  __shared__ __attribute__((aligned(1024))) char lds[NST * ST_BYTES];
+  __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
   // block -> (part, token, 128-head block), the blocks of a part on one XCD
   const int WG = H / HEADS;
   const int bid = blockIdx.x;
   const int part = (bid / (kXcds * WG * q_len)) * kXcds + bid % kXcds;
   const int hbq = (bid / kXcds) % (WG * q_len);
-  const int tok = hbq / WG, hb = hbq % WG;
+  const int tok = hbq / WG, hblk = hbq % WG;
   if (part >= nparts) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int lr = lane & 15, lg = lane >> 4;
-  const int h0 = hb * HEADS + wave * 16 * G;  // group g: heads h0 + 16g .. h0 + 16g + 15
+  const int hbase = hblk * HEADS;
+  const int h0 = hbase + wave * 16;  // this wave's softmax heads h0 .. h0 + 15
   const uint32_t lds0 = lds_u32(lds);
 
   // operand offsets inside a 16-row block (as in the 16-head core)
@@ -153,31 +171,23 @@ decode_core_wide_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
     DecodeWork nx = wk;
     if (wk.next >= 0) nx = load_work(works + wk.next);
 
-    // Q^T fragments of heads h0 + 16g + lr: columns 32 s + 8 lg .. + 7
-    bf16x8_t qf[G][18];
+    // Q^T fragments of head h0 + lr: columns 32 s + 8 lg .. + 7
+    bf16x8_t qf[18];
+    {
+      const bf16* qrow = q_cat + ((int64_t)(wk.b * q_len + tok) * H + h0 + lr) * RW + lg * 8;
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const bf16* qrow =
-          q_cat + ((int64_t)(wk.b * q_len + tok) * H + h0 + 16 * g + lr) * RW + lg * 8;
-#pragma unroll
-      for (int s = 0; s < 18; ++s) qf[g][s] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * s);
+      for (int s = 0; s < 18; ++s) qf[s] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * s);
     }
 #pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int s = 0; s < 18; ++s) asm volatile("" ::"v"(qf[g][s]));
+    for (int s = 0; s < 18; ++s) asm volatile("" ::"v"(qf[s]));
 
-    float m_run[G], l_run[G];
+    float m_run = -INFINITY, l_run = 0.f;
+    // o[g][c][i]: latent sum of head hbase + 16 g + lr, column 16 (CB_W wave + c) + 4 lg + i
+    f32x4_t o[NW][CB_W];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      m_run[g] = -INFINITY;
-      l_run[g] = 0.f;
-    }
-    f32x4_t o[G][32];  // o[g][cb][i]: head h0 + 16g + lr, column 16 cb + 4 lg + i
+    for (int g = 0; g < NW; ++g)
 #pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int cb = 0; cb < 32; ++cb) o[g][cb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+      for (int c = 0; c < CB_W; ++c) o[g][c] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 
     for (int t = 0; t < ntile; ++t) {
       static_assert(NST == 4, "wait counts below assume 4 stages");
@@ -189,15 +199,13 @@ decode_core_wide_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
       if (t + NST - 1 < ntile) issue(t + NST - 1);
       const char* st = lds + (t % NST) * ST_BYTES;
       const int row0 = t * TR;
-      // ---- S^T = K . Q^T for both 16-row blocks, K fragments read once per head group
-      f32x4_t sc[2][G];
+      // ---- scores of this wave's 16 heads: S^T = K . Q^T for both 16-row blocks
+      f32x4_t sc[2];
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
         const char* sl = st + rb * 16 * 1024;  // latent rows of this block
         const char* sr = st + rb * 16 * 128;   // rope rows (offsets include ROPE_OFF)
-        f32x4_t sa[G], sb[G];
-#pragma unroll
-        for (int g = 0; g < G; ++g) sa[g] = sb[g] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+        f32x4_t sa = (f32x4_t){0.f, 0.f, 0.f, 0.f}, sb = sa;
 #pragma unroll
         for (int part = 0; part < 6; ++part) {
           bf16x8_t kf[3];
@@ -212,99 +220,104 @@ decode_core_wide_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
 #pragma unroll
           for (int u = 0; u < 3; ++u) {
             const int s = 3 * part + u;
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-              if (s & 1)
-                sb[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[u], qf[g][s], sb[g], 0, 0, 0);
-              else
-                sa[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[u], qf[g][s], sa[g], 0, 0, 0);
-            }
+            if (s & 1) sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[u], qf[s], sb, 0, 0, 0);
+            else sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[u], qf[s], sa, 0, 0, 0);
           }
         }
-#pragma unroll
-        for (int g = 0; g < G; ++g) sc[rb][g] = sa[g] + sb[g];
+        sc[rb] = sa + sb;
       }
-      // ---- online softmax per head group (lazy reference maximum); lane holds
-      // rows row0 + 16 rb + 4 lg + i of its head
-      bf16x8_t pf[G];
+      // ---- online softmax of this wave's heads (lazy reference maximum); lane
+      // holds rows row0 + 16 rb + 4 lg + i of head h0 + lr
+      float sv[8];
+      bool grow = false;
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float sv[8];
-        bool grow = false;
+      for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const bool valid = row0 + 16 * rb + 4 * lg + i < nv;
-            sv[4 * rb + i] = valid ? sc[rb][g][i] * kLog2e : -INFINITY;
-            grow |= sv[4 * rb + i] > m_run[g] + kRescale;
-          }
-        if (__any(grow)) {
-          float mx = sv[0];
-#pragma unroll
-          for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
-          mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-          mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-          const float m_new = fmaxf(m_run[g], mx);
-          const float alpha = __builtin_amdgcn_exp2f(m_run[g] - m_new);
-          l_run[g] *= alpha;
-          m_run[g] = m_new;
-#pragma unroll
-          for (int cb = 0; cb < 32; ++cb) o[g][cb] *= alpha;
+        for (int i = 0; i < 4; ++i) {
+          const bool valid = row0 + 16 * rb + 4 * lg + i < nv;
+          sv[4 * rb + i] = valid ? sc[rb][i] * kLog2e : -INFINITY;
+          grow |= sv[4 * rb + i] > m_run + kRescale;
         }
-        float pv[8];
+      float alpha = 1.f;
+      const bool resc = __any(grow);
+      if (resc) {
+        float mx = sv[0];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          pv[i] = __builtin_amdgcn_exp2f(sv[i] - m_run[g]);
-          l_run[g] += pv[i];
-        }
+        for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float m_new = fmaxf(m_run, mx);
+        alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+        m_run = m_new;
+      }
+      float pv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        pv[i] = __builtin_amdgcn_exp2f(sv[i] - m_run);
+        l_run += pv[i];
+      }
+      {
         uint32_t pk[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(pv[2 * i], pv[2 * i + 1]);
-        pf[g] = __builtin_bit_cast(bf16x8_t, pk);
+        // publish P (the B operand of the latent sum, in lane order), the
+        // rescale factor of each head and whether this group rescaled
+        *reinterpret_cast<bf16x8_t*>(lds + XP_OFF + wave * 1024 + lane * 16) =
+            __builtin_bit_cast(bf16x8_t, pk);
+        if (lg == 0) reinterpret_cast<float*>(lds + XA_OFF)[16 * wave + lr] = alpha;
+        if (lane == 0) reinterpret_cast<int*>(lds + XF_OFF)[wave] = resc ? 1 : 0;
       }
-      // ---- O^T += C^T . P^T over the 32 rows: mfma 16x16x32 whose k index runs
-      // over rows 4g..4g+3 of row block 0, then of row block 1, for lane group g;
-      // C^T from two transposing reads per 16-column block
+      __syncthreads();  // every group's P of tile t is published
+      // ---- O^T += C^T . P^T for this wave's columns and every head group: mfma
+      // 16x16x32 whose k index runs over rows 4g..4g+3 of row block 0, then of
+      // row block 1, for lane group g (the order the softmax lanes hold P in);
+      // C^T from two transposing reads per 16-column block, read once
+      bf16x8_t cf[CB_W];
 #pragma unroll
-      for (int q = 0; q < 8; ++q)
+      for (int c = 0; c < CB_W; ++c) {
+        typedef __attribute__((address_space(3))) s16x4_t* lptr;
+        const int q = (CB_W * wave + c) >> 2, tt = (CB_W * wave + c) & 3;
+        const int off = pv_e[tt] - (q & 1) * pv_d + 128 * q;
+        const s16x4_t c0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lptr)(st + off));
+        const s16x4_t c1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lptr)(st + 16 * 1024 + off));
+        const s16x8_t c8 = __builtin_shufflevector(c0, c1, 0, 1, 2, 3, 4, 5, 6, 7);
+        cf[c] = __builtin_bit_cast(bf16x8_t, c8);
+      }
+      const int* xf = reinterpret_cast<const int*>(lds + XF_OFF);
+      const float* xa = reinterpret_cast<const float*>(lds + XA_OFF);
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-          typedef __attribute__((address_space(3))) s16x4_t* lptr;
-          const int off = pv_e[tt] - (q & 1) * pv_d + 128 * q;
-          const s16x4_t c0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lptr)(st + off));
-          const s16x4_t c1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lptr)(st + 16 * 1024 + off));
-          const s16x8_t c8 = __builtin_shufflevector(c0, c1, 0, 1, 2, 3, 4, 5, 6, 7);
-          const bf16x8_t cf = __builtin_bit_cast(bf16x8_t, c8);
+      for (int g = 0; g < NW; ++g) {
+        if (xf[g]) {
+          const float a = xa[16 * g + lr];
 #pragma unroll
-          for (int g = 0; g < G; ++g)
-            o[g][4 * q + tt] =
-                __builtin_amdgcn_mfma_f32_16x16x32_bf16(cf, pf[g], o[g][4 * q + tt], 0, 0, 0);
+          for (int c = 0; c < CB_W; ++c) o[g][c] *= a;
         }
-      // keep at most a few transposing reads ahead of their MFMAs (registers)
+        const bf16x8_t pg = *reinterpret_cast<const bf16x8_t*>(lds + XP_OFF + g * 1024 + lane * 16);
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
-        __builtin_amdgcn_sched_group_barrier(0x008, G, 0);  // then the MFMAs using them
+        for (int c = 0; c < CB_W; ++c)
+          o[g][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cf[c], pg, o[g][c], 0, 0, 0);
       }
     }
 
-    // ---- this wave's heads are complete for the segment: write the partials
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float l = l_run[g];
+    // ---- the segment's partial: (max, sum) of this wave's heads; the latent
+    // sums of this wave's columns for every head
+    {
+      float l = l_run;
       l += __shfl_xor(l, 16, 64);
       l += __shfl_xor(l, 32, 64);
-      const int gh = h0 + 16 * g + lr;
       const int64_t slot = (int64_t)tok * nseg_total + wk.pidx;
-      float* pacc = acc_out + (slot * H + gh) * DC + 4 * lg;
-#pragma unroll
-      for (int cb = 0; cb < 32; ++cb)
-        *reinterpret_cast<float4*>(pacc + 16 * cb) =
-            make_float4(o[g][cb][0], o[g][cb][1], o[g][cb][2], o[g][cb][3]);
       if (lg == 0) {
-        ml_out[(slot * H + gh) * 2] = m_run[g];
-        ml_out[(slot * H + gh) * 2 + 1] = l;
+        ml_out[(slot * H + h0 + lr) * 2] = m_run;
+        ml_out[(slot * H + h0 + lr) * 2 + 1] = l;
+      }
+#pragma unroll
+      for (int g = 0; g < NW; ++g) {
+        float* pacc = acc_out + (slot * H + hbase + 16 * g + lr) * DC + 16 * CB_W * wave + 4 * lg;
+#pragma unroll
+        for (int c = 0; c < CB_W; ++c)
+          *reinterpret_cast<float4*>(pacc + 16 * c) =
+              make_float4(o[g][c][0], o[g][c][1], o[g][c][2], o[g][c][3]);
       }
     }
     __syncthreads();  // the stages are refilled by the next segment
