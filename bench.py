@@ -464,7 +464,8 @@ def main():
                    "cache_bytes": int(cache_bytes),
                    "weight_bytes": int(weight_bytes), "hidden": d.hidden, "heads": d.n_heads,
                    "kv_lora": d.kv_lora, "qk_rope": d.qk_rope},
-        "roofline": {"kernel": "decode_core_ring8_k" if fp8 else "decode_core_ring_k",
+        "roofline": {"kernel": "decode_core_ring8_k" if fp8 else
+                     "decode_core_wide_k" if d.n_heads % 128 == 0 else "decode_core_ring_k",
                      "bound": "hbm",
                      "kernel_timing": "HIP events (no system fence) around every split-S core "
                                       "launch, K eager steps",

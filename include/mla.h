@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 6
+#define MLA_ABI_VERSION 7
 
 typedef enum mla_status {
   MLA_OK = 0,
@@ -79,8 +79,8 @@ typedef enum mla_dtype { MLA_BF16 = 0, MLA_F32 = 1 } mla_dtype;
  * zero pad to a multiple of 16]; the latent values are c_i = s * value(code_i)
  * with s = max_i |c_i| / 448 (1 for an all-zero row) and code_i the E4M3
  * value nearest c_i / s (ties to even).  FP8 needs dtype MLA_BF16, kv_lora
- * 512, qk_rope 64 and n_heads a multiple of 16 that is not a multiple of 128;
- * it serves append and decode (mla_prefill reads bf16 caches only). */
+ * 512, qk_rope 64 and n_heads a multiple of 16; it serves append, decode and
+ * prefill (which decodes the key rows it reads to bf16, c_i rounded once). */
 typedef enum mla_kv_storage { MLA_KV_DTYPE = 0, MLA_KV_FP8_E4M3 = 1 } mla_kv_storage;
 
 /* Layer dimensions (MLA post, section 3.2 constructor; section 3.6 widths).
@@ -148,6 +148,10 @@ int mla_decode_check(const mla_config* cfg, const int32_t* pos, const int64_t* s
                      const int32_t* seq_len, int32_t B, int64_t cache_rows);
 int mla_prefill_check(const mla_config* cfg, const int32_t* cu_new, const int32_t* prior_len,
                       const int64_t* seq_off, int32_t B, int64_t cache_rows);
+/* The checks of mla_prefill_paged; see there. */
+int mla_prefill_paged_check(const mla_config* cfg, const int32_t* cu_new,
+                            const int32_t* prior_len, const int32_t* block_table,
+                            int32_t max_pages, int32_t page_rows, int32_t B, int64_t cache_rows);
 /* The checks of mla_decode_paged (writes = 0) and mla_decode_step_paged
  * (writes = 1); see there. */
 int mla_decode_paged_check(const mla_config* cfg, const int32_t* pos, const int32_t* block_table,
@@ -361,8 +365,8 @@ int mla_decode_stage_offsets(mla_handle h, int32_t B, int64_t total_rows,
  * a fixed per-segment cost, and cuts inside a sequence fall on multiples of 32
  * rows (one tile of the MFMA cores).  The library itself uses max_parts = the
  * device's compute units divided by the number of workgroups a part runs (one
- * per 16-head group; one per 128 heads for layers with a multiple of 128
- * heads).
+ * per 16-head group; one per 128 heads for bf16 layers with a multiple of
+ * 128 heads).
  *   seq_len: HOST (B), each >= 1.
  *   part_begin: HOST out (max_parts + 1): segments of part p are
  *     [part_begin[p], part_begin[p+1]).
@@ -387,10 +391,14 @@ int mla_decode_plan_tokens(int32_t B, const int32_t* seq_len, int32_t q_len, int
                            int32_t* part_begin, int32_t* seg_b, int32_t* seg_r0, int32_t* seg_r1,
                            int32_t* n_parts, int32_t* n_segs);
 
-/* Workspace bytes mla_prefill needs for T new tokens in B sequences whose
- * caches hold total_key_rows rows in all after the append. */
+/* Workspace bytes mla_prefill (mla_prefill_paged) needs for T new tokens in
+ * B sequences whose caches hold total_key_rows rows in all after the append.
+ * An FP8 or paged cache adds room for the key rows gathered in the storage
+ * type (total_key_rows * R elements). */
 size_t mla_prefill_workspace_bytes(mla_handle h, int32_t T, int32_t B,
                                    int64_t total_key_rows);
+size_t mla_prefill_paged_workspace_bytes(mla_handle h, int32_t T, int32_t B,
+                                         int64_t total_key_rows);
 
 /* P1 -- causal chunked prefill.  Sequence b has prior_len[b] cached rows and
  * new tokens hidden[cu_new[b] .. cu_new[b+1]) at positions prior_len[b],
@@ -401,12 +409,33 @@ size_t mla_prefill_workspace_bytes(mla_handle h, int32_t T, int32_t B,
  *   hidden: device (T, D), T = cu_new[B]; out: device (T, D).
  *   cu_new: HOST (B+1), cu_new[0] = 0, non-decreasing; prior_len, seq_off:
  *   HOST (B).
- * Errors as for mla_decode (CAPACITY if a sequence's rows leave the cache);
- * SHAPE for a handle whose cache holds FP8 rows. */
+ * An FP8 cache's key rows are first decoded into the workspace (c_i = s *
+ * value(code_i) rounded to bf16), then expanded and attended as bf16 rows.
+ * Errors as for mla_decode (CAPACITY if a sequence's rows leave the cache;
+ * INVALID_ARG if prior_len[b] + n_b exceeds INT32_MAX). */
 int mla_prefill(mla_handle h, const void* hidden, const int32_t* cu_new,
                 const int32_t* prior_len, const int64_t* seq_off, int32_t B,
                 const void* cache, int64_t cache_rows, void* out, void* ws,
                 size_t ws_bytes);
+
+/* mla_prefill over a paged cache (the page pool of mla_decode_paged; the
+ * KV-cache page grows its cache as a memory pool): position t of sequence b
+ * is row block_table[b * max_pages + t / page_rows] * page_rows + t %
+ * page_rows, for t < prior_len[b] + n_b (the caller has appended the new rows
+ * through the same table, e.g. with mla_append_latent).  The key rows are
+ * gathered into the workspace (decoded from FP8 for an FP8 cache) and the
+ * prefill runs on them; results equal mla_prefill's on a contiguous cache
+ * holding the same rows in the same sequence order, bit for bit.
+ *   block_table: HOST (B, max_pages) int32; page_rows: a power of two, 32 ..
+ *   2^30.  Workspace: mla_prefill_paged_workspace_bytes.
+ * Errors: those of mla_prefill; page_rows not a power of two in range,
+ * max_pages < 1 or a NULL table -> INVALID_ARG; more pages needed than
+ * max_pages, or a page index outside [0, cache_rows / page_rows) ->
+ * CAPACITY. */
+int mla_prefill_paged(mla_handle h, const void* hidden, const int32_t* cu_new,
+                      const int32_t* prior_len, const int32_t* block_table, int32_t max_pages,
+                      int32_t page_rows, int32_t B, const void* cache, int64_t cache_rows,
+                      void* out, void* ws, size_t ws_bytes);
 
 /* Measurement: with n_slots > 0, every later launch of the attention core
  * (the split-S kernel of mla_decode / mla_decode_step, the attention kernel of

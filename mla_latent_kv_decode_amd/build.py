@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libmla.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["mla.cpp", "k_generic.hip", "k_gemm.hip", "k_gemm_big.hip", "k_decode_wide.hip", "k_decode_ring.hip", "k_decode_ring8.hip", "k_combine.hip", "k_skinny.hip", "k_prefill.hip", "scratch.hip"]
+SOURCES = ["mla.cpp", "k_generic.hip", "k_gemm.hip", "k_gemm_big.hip", "k_decode_wide.hip", "k_decode_ring.hip", "k_decode_ring8.hip", "k_combine.hip", "k_skinny.hip", "k_prefill.hip", "k_gather.hip", "scratch.hip"]
 
 ARCH = "gfx950"
 # -packed-fp32-ops: hipcc must not emit packed fp32 ALU ops by itself (its host

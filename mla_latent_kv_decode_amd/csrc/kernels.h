@@ -259,6 +259,21 @@ struct PrefillTile {
   int64_t kv_row0, cache_row0;
   int32_t t0, nq, pos0, pad;
 };
+// Where the key rows of prefill sequence b live: contiguous rows from
+// seq_off[b], or row t at pages[page_start[b] + t / 2^page_shift] *
+// 2^page_shift + t % 2^page_shift (a paged cache).
+struct KeyRowSrc {
+  const void* cache;
+  const int64_t* seq_off;     // (B) device; unused for a paged cache
+  const int32_t* page_start;  // (B) device; paged cache only
+  const int32_t* pages;       // device page list, or null for a contiguous cache
+  int page_shift;
+};
+// Copies the nrows[b] key rows of every sequence b to out + kv_off[b] rows
+// (row_bytes per output row); fp8: decodes 656-byte FP8 rows (dc 512, dr 64)
+// into bf16 rows of 576.  Returns nonzero if fp8 rows do not fit row_bytes.
+int gather_key_rows(const KeyRowSrc& s, bool fp8, const int64_t* kv_off, const int32_t* nrows,
+                    int B, int max_rows, int row_bytes, void* out, hipStream_t st);
 // queries per tile of prefill_attn_mfma
 int prefill_tile_queries();
 // MFMA version: bf16, qk_nope = v_head = 128, qk_rope = 64.  q: (T, H, 192)

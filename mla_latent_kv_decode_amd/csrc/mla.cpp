@@ -303,8 +303,11 @@ struct DecodeLayout {
   size_t total = 0;
 };
 
-// layers with many heads use the shared-tile core
-bool wide_core(const mla_ctx* h) { return h->mfma && h->d.H % mla::decode_core_wide_heads() == 0; }
+// bf16 layers with many heads use the shared-tile core (FP8 rows are read by
+// the 16-head-group core, one workgroup per group)
+bool wide_core(const mla_ctx* h) {
+  return h->mfma && !h->kv8 && h->d.H % mla::decode_core_wide_heads() == 0;
+}
 // other MFMA layers use the ring core
 bool ring_core(const mla_ctx* h) { return h->mfma && !wide_core(h); }
 // the split combine fused with the value un-absorb (MFMA layers with dv = 128)
@@ -674,8 +677,7 @@ int mla_config_check(const mla_config* c) {
     return MLA_ERR_INVALID_ARG;
   if (c->kv_storage == MLA_KV_FP8_E4M3) {
     // the FP8 rows are read by the 16-head-group MFMA core only
-    if (c->dtype != MLA_BF16 || c->kv_lora != 512 || c->qk_rope != 64 || c->n_heads % 16 ||
-        c->n_heads % mla::decode_core_wide_heads() == 0)
+    if (c->dtype != MLA_BF16 || c->kv_lora != 512 || c->qk_rope != 64 || c->n_heads % 16)
       return MLA_ERR_SHAPE;
   }
   return MLA_OK;
@@ -830,10 +832,31 @@ int mla_prefill_check(const mla_config* cfg, const int32_t* cu_new, const int32_
   for (int32_t b = 0; b < B; ++b) {
     if (cu_new[b + 1] < cu_new[b] || prior_len[b] < 0) return MLA_ERR_INVALID_ARG;
     const int64_t len = (int64_t)prior_len[b] + (cu_new[b + 1] - cu_new[b]);
+    if (len > INT32_MAX) return MLA_ERR_INVALID_ARG;  // positions are int32
     if (seq_off[b] < 0 || seq_off[b] > cache_rows - len) return MLA_ERR_CAPACITY;
   }
   if (cu_new[B] <= 0) return MLA_ERR_INVALID_ARG;
   return MLA_OK;
+}
+
+int mla_prefill_paged_check(const mla_config* cfg, const int32_t* cu_new,
+                            const int32_t* prior_len, const int32_t* block_table,
+                            int32_t max_pages, int32_t page_rows, int32_t B, int64_t cache_rows) {
+  int rc = mla_config_check(cfg);
+  if (rc) return rc;
+  if (B <= 0 || !cu_new || !prior_len || !block_table || cache_rows <= 0 || max_pages <= 0)
+    return MLA_ERR_INVALID_ARG;
+  if (cu_new[0] != 0) return MLA_ERR_INVALID_ARG;
+  std::vector<int32_t> len(B);
+  for (int32_t b = 0; b < B; ++b) {
+    if (cu_new[b + 1] < cu_new[b] || prior_len[b] < 0) return MLA_ERR_INVALID_ARG;
+    const int64_t l = (int64_t)prior_len[b] + (cu_new[b + 1] - cu_new[b]);
+    if (l > INT32_MAX) return MLA_ERR_INVALID_ARG;
+    len[b] = (int32_t)l;
+  }
+  if (cu_new[B] <= 0) return MLA_ERR_INVALID_ARG;
+  // the prefill only reads the cache: the caller appends the new rows first
+  return paged_table_check(block_table, max_pages, page_rows, len.data(), B, cache_rows, 1, 0);
 }
 
 // RoPE frequency of every pair (dr / 2 of them), YaRN-interpolated for
@@ -1606,8 +1629,12 @@ int mla_decode_step_paged(mla_handle h, const void* hidden, const int32_t* pos,
 // ------------------------------------------------------------------------
 namespace {
 struct PrefillLayout {
-  size_t meta, scratch, pin, pq, cq, q_nope, q_rope, kv, o, total;
+  size_t meta, scratch, pin, pq, cq, q_nope, q_rope, kv, o, keys, total;
   size_t meta_bytes, tiles_off;  // blob size and offset of the MFMA query tiles
+  // gathered key rows (FP8 or paged caches): offsets in the blob of the per-
+  // sequence row counts, source offsets (contiguous) or page list starts
+  // (paged), and the page list
+  size_t nrows_off, gsrc_off, pstart_off, pages_off;
 };
 
 // the MFMA prefill attention applies (bf16, 128 + 64 query/key dims, 128 values)
@@ -1618,7 +1645,14 @@ bool prefill_mfma(const mla_ctx* h) {
 
 int max_prefill_tiles(int T, int B) { return T / mla::prefill_tile_queries() + B; }
 
-PrefillLayout prefill_layout(const mla_ctx* h, int T, int B, int64_t rows, int max_rows) {
+// pages of a paged prefill's key rows: at most rows / 32 + B (pages hold 32
+// rows or more)
+int64_t max_prefill_pages(int B, int64_t rows) { return rows / 32 + B; }
+
+// staged: the key rows are gathered into the workspace first (FP8 or paged
+// caches)
+PrefillLayout prefill_layout(const mla_ctx* h, int T, int B, int64_t rows, int max_rows,
+                             bool staged, bool paged) {
   const Dims& d = h->d;
   PrefillLayout L;
   const int qw = qw_of(d);
@@ -1630,7 +1664,12 @@ PrefillLayout prefill_layout(const mla_ctx* h, int T, int B, int64_t rows, int m
   const size_t e = h->esz;
   Carve c;
   L.tiles_off = align_up((size_t)T * 4) * 2 + align_up((size_t)B * 8) * 2;
-  L.meta_bytes = L.tiles_off + (size_t)max_prefill_tiles(T, B) * sizeof(mla::PrefillTile);
+  L.nrows_off = align_up(L.tiles_off + (size_t)max_prefill_tiles(T, B) * sizeof(mla::PrefillTile));
+  L.gsrc_off = L.nrows_off + align_up((size_t)B * 4);
+  L.pstart_off = L.gsrc_off + align_up((size_t)B * 8);
+  L.pages_off = L.pstart_off + align_up((size_t)B * 4);
+  L.meta_bytes = !staged ? L.nrows_off
+                 : L.pages_off + (paged ? align_up((size_t)max_prefill_pages(B, rows) * 4) : 0);
   L.meta = c.take(L.meta_bytes);
   L.scratch = c.take(scr * 4);
   L.pin = c.take(pin * 4);
@@ -1641,6 +1680,7 @@ PrefillLayout prefill_layout(const mla_ctx* h, int T, int B, int64_t rows, int m
   L.q_rope = c.take((size_t)T * d.H * std::max(d.dr, 1) * e);
   L.kv = c.take((size_t)rows * d.H * (d.dn + d.dv) * 4);
   L.o = c.take((size_t)T * d.H * d.dv * e);
+  L.keys = c.take(staged ? (size_t)rows * d.R * e : 0);
   L.total = c.off;
   return L;
 }
@@ -1649,7 +1689,14 @@ PrefillLayout prefill_layout(const mla_ctx* h, int T, int B, int64_t rows, int m
 size_t mla_prefill_workspace_bytes(mla_handle h, int32_t T, int32_t B, int64_t total_key_rows) {
   if (!h || T <= 0 || B <= 0 || total_key_rows <= 0) return 0;
   const int max_rows = (int)std::min<int64_t>(total_key_rows, INT32_MAX);
-  return prefill_layout(h, T, B, total_key_rows, max_rows).total;
+  return prefill_layout(h, T, B, total_key_rows, max_rows, h->kv8, false).total;
+}
+
+size_t mla_prefill_paged_workspace_bytes(mla_handle h, int32_t T, int32_t B,
+                                         int64_t total_key_rows) {
+  if (!h || T <= 0 || B <= 0 || total_key_rows <= 0) return 0;
+  const int max_rows = (int)std::min<int64_t>(total_key_rows, INT32_MAX);
+  return prefill_layout(h, T, B, total_key_rows, max_rows, true, true).total;
 }
 
 template <typename T>
@@ -1733,26 +1780,38 @@ static int run_prefill(mla_ctx* h, const T* hidden, int ntok, int B, const int32
   return check_launch(h, "prefill");
 }
 
-int mla_prefill(mla_handle h, const void* hidden, const int32_t* cu_new, const int32_t* prior_len,
-                const int64_t* seq_off, int32_t B, const void* cache, int64_t cache_rows,
-                void* out, void* ws, size_t ws_bytes) {
+// A chunked prefill over a contiguous (seq_off) or a paged (pg) cache.  The
+// expansion and the attention read the key rows in place from a contiguous
+// cache in the storage type; FP8 and paged caches have their key rows
+// gathered into the workspace first, at kv_off (the expanded rows' order).
+static int prefill_common(mla_ctx* h, const void* hidden, const int32_t* cu_new,
+                          const int32_t* prior_len, const int64_t* seq_off, const PageArgs* pg,
+                          int32_t B, const void* cache, int64_t cache_rows, void* out, void* ws,
+                          size_t ws_bytes) {
+  const char* what = pg ? "prefill_paged" : "prefill";
   if (!h) return MLA_ERR_INVALID_ARG;
-  if (!hidden || !cache || !out) return fail(h, MLA_ERR_INVALID_ARG, "prefill: NULL tensor");
-  int rc0 = mla_prefill_check(&h->cfg, cu_new, prior_len, seq_off, B, cache_rows);
-  if (rc0) return fail(h, rc0, "prefill: %s (B=%d, cache_rows=%lld)", mla_status_string(rc0), B,
+  if (!hidden || !cache || !out) return fail(h, MLA_ERR_INVALID_ARG, "%s: NULL tensor", what);
+  const int rc0 = pg ? mla_prefill_paged_check(&h->cfg, cu_new, prior_len, pg->table,
+                                               pg->max_pages, pg->page_rows, B, cache_rows)
+                     : mla_prefill_check(&h->cfg, cu_new, prior_len, seq_off, B, cache_rows);
+  if (rc0) return fail(h, rc0, "%s: %s (B=%d, cache_rows=%lld)", what, mla_status_string(rc0), B,
                        (long long)cache_rows);
-  if (!h->absorbed) return fail(h, MLA_ERR_STATE, "prefill before mla_absorb_weights");
-  if (h->kv8)
-    return fail(h, MLA_ERR_SHAPE, "prefill: the expansion reads bf16 latent rows; FP8 caches "
-                                  "are decode-only");
+  if (!h->absorbed) return fail(h, MLA_ERR_STATE, "%s before mla_absorb_weights", what);
+  const bool staged = h->kv8 || pg;
   int64_t rows = 0;
+  int32_t max_n = 0;
   std::vector<int64_t> kv_off(B);
   for (int32_t b = 0; b < B; ++b) {
     kv_off[b] = rows;
-    rows += (int64_t)prior_len[b] + (cu_new[b + 1] - cu_new[b]);
+    const int32_t n = prior_len[b] + (cu_new[b + 1] - cu_new[b]);
+    rows += n;
+    max_n = std::max(max_n, n);
   }
+  // where the expansion and the attention read sequence b's key rows
+  const int64_t* key_off = staged ? kv_off.data() : seq_off;
   const int32_t T = cu_new[B];
-  const PrefillLayout L = prefill_layout(h, T, B, rows, (int)std::min<int64_t>(rows, INT32_MAX));
+  const PrefillLayout L = prefill_layout(h, T, B, rows, (int)std::min<int64_t>(rows, INT32_MAX),
+                                         staged, pg != nullptr);
   int rc = check_ws(h, ws, ws_bytes, L.total);
   if (rc) return rc;
   DeviceGuard g(h->device);
@@ -1768,7 +1827,7 @@ int mla_prefill(mla_handle h, const void* hidden, const int32_t* cu_new, const i
       tok_pos[i] = prior_len[b] + (i - cu_new[b]);
     }
     kvo[b] = kv_off[b];
-    so[b] = seq_off[b];
+    so[b] = key_off[b];
   }
   // query tiles of the MFMA attention, longest key range first
   std::vector<mla::PrefillTile> tiles;
@@ -1778,7 +1837,7 @@ int mla_prefill(mla_handle h, const void* hidden, const int32_t* cu_new, const i
     for (int32_t i = 0; i < n; i += tq) {
       mla::PrefillTile t;
       t.kv_row0 = kv_off[b];
-      t.cache_row0 = seq_off[b];
+      t.cache_row0 = key_off[b];
       t.t0 = cu_new[b] + i;
       t.nq = std::min(tq, n - i);
       t.pos0 = prior_len[b] + i;
@@ -1793,12 +1852,62 @@ int mla_prefill(mla_handle h, const void* hidden, const int32_t* cu_new, const i
   if ((int)tiles.size() > max_prefill_tiles(T, B))
     return fail(h, MLA_ERR_WORKSPACE, "internal: more prefill tiles than planned");
   memcpy(blob.data() + L.tiles_off, tiles.data(), tiles.size() * sizeof(mla::PrefillTile));
+  if (staged) {
+    int32_t* nrows = reinterpret_cast<int32_t*>(blob.data() + L.nrows_off);
+    int64_t* gsrc = reinterpret_cast<int64_t*>(blob.data() + L.gsrc_off);
+    int32_t* pstart = reinterpret_cast<int32_t*>(blob.data() + L.pstart_off);
+    int32_t* pages = reinterpret_cast<int32_t*>(blob.data() + L.pages_off);
+    int64_t np = 0;
+    for (int32_t b = 0; b < B; ++b) {
+      nrows[b] = prior_len[b] + (cu_new[b + 1] - cu_new[b]);
+      gsrc[b] = seq_off ? seq_off[b] : 0;
+      if (pg) {
+        const int64_t n = ((int64_t)nrows[b] + pg->page_rows - 1) / pg->page_rows;
+        if (np + n > max_prefill_pages(B, rows))
+          return fail(h, MLA_ERR_WORKSPACE, "internal: more prefill pages than planned");
+        pstart[b] = (int32_t)np;
+        for (int64_t i = 0; i < n; ++i) pages[np++] = pg->table[(int64_t)b * pg->max_pages + i];
+      }
+    }
+  }
   if ((rc = stage_upload(h, at<char>(ws, L.meta), blob.data(), blob.size()))) return rc;
+  const void* keys = cache;
+  if (staged) {
+    const char* meta = at<char>(ws, L.meta);
+    mla::KeyRowSrc src;
+    src.cache = cache;
+    src.seq_off = reinterpret_cast<const int64_t*>(meta + L.gsrc_off);
+    src.page_start = reinterpret_cast<const int32_t*>(meta + L.pstart_off);
+    src.pages = pg ? reinterpret_cast<const int32_t*>(meta + L.pages_off) : nullptr;
+    src.page_shift = pg ? pg->shift : 0;
+    const int64_t* kvo_d = reinterpret_cast<const int64_t*>(meta + 2 * align_up((size_t)T * 4));
+    if (mla::gather_key_rows(src, h->kv8, kvo_d,
+                             reinterpret_cast<const int32_t*>(meta + L.nrows_off), B, max_n,
+                             h->d.R * (int)h->esz, at<char>(ws, L.keys), h->stream))
+      return fail(h, MLA_ERR_SHAPE, "%s: FP8 rows need kv_lora 512 and qk_rope 64", what);
+    keys = at<char>(ws, L.keys);
+  }
   if (is_f32(h))
-    return run_prefill<float>(h, (const float*)hidden, T, B, cu_new, prior_len, seq_off,
-                              (const float*)cache, (float*)out, ws, L, kv_off.data(),
+    return run_prefill<float>(h, (const float*)hidden, T, B, cu_new, prior_len, key_off,
+                              (const float*)keys, (float*)out, ws, L, kv_off.data(),
                               (int)tiles.size());
-  return run_prefill<bf16>(h, (const bf16*)hidden, T, B, cu_new, prior_len, seq_off,
-                           (const bf16*)cache, (bf16*)out, ws, L, kv_off.data(),
+  return run_prefill<bf16>(h, (const bf16*)hidden, T, B, cu_new, prior_len, key_off,
+                           (const bf16*)keys, (bf16*)out, ws, L, kv_off.data(),
                            (int)tiles.size());
+}
+
+int mla_prefill(mla_handle h, const void* hidden, const int32_t* cu_new, const int32_t* prior_len,
+                const int64_t* seq_off, int32_t B, const void* cache, int64_t cache_rows,
+                void* out, void* ws, size_t ws_bytes) {
+  return prefill_common(h, hidden, cu_new, prior_len, seq_off, nullptr, B, cache, cache_rows,
+                        out, ws, ws_bytes);
+}
+
+int mla_prefill_paged(mla_handle h, const void* hidden, const int32_t* cu_new,
+                      const int32_t* prior_len, const int32_t* block_table, int32_t max_pages,
+                      int32_t page_rows, int32_t B, const void* cache, int64_t cache_rows,
+                      void* out, void* ws, size_t ws_bytes) {
+  const PageArgs pg{block_table, max_pages, page_rows, page_shift_of(page_rows)};
+  return prefill_common(h, hidden, cu_new, prior_len, nullptr, &pg, B, cache, cache_rows, out,
+                        ws, ws_bytes);
 }

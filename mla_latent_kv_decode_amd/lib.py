@@ -76,6 +76,9 @@ _SIGS = {
     "mla_decode_paged_check": (ctypes.c_int, [ctypes.POINTER(MLAConfig), _I32P, _I32P,
                                               ctypes.c_int32, ctypes.c_int32, _I32P,
                                               ctypes.c_int32, ctypes.c_int64, ctypes.c_int32]),
+    "mla_prefill_paged_check": (ctypes.c_int, [ctypes.POINTER(MLAConfig), _I32P, _I32P, _I32P,
+                                               ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                               ctypes.c_int64]),
     "mla_create": (ctypes.c_int, [ctypes.POINTER(MLAConfig), _P, ctypes.POINTER(_P)]),
     "mla_destroy": (ctypes.c_int, [_P]),
     "mla_set_stream": (ctypes.c_int, [_P, _P]),
@@ -122,6 +125,11 @@ _SIGS = {
                                                       ctypes.c_int64]),
     "mla_prefill": (ctypes.c_int, [_P, _P, _I32P, _I32P, _I64P, ctypes.c_int32, _P,
                                    ctypes.c_int64, _P, _P, ctypes.c_size_t]),
+    "mla_prefill_paged_workspace_bytes": (ctypes.c_size_t, [_P, ctypes.c_int32, ctypes.c_int32,
+                                                            ctypes.c_int64]),
+    "mla_prefill_paged": (ctypes.c_int, [_P, _P, _I32P, _I32P, _I32P, ctypes.c_int32,
+                                         ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int64, _P,
+                                         _P, ctypes.c_size_t]),
 }
 
 _lib = None
@@ -453,6 +461,28 @@ class MLALayer:
         rc = self.lib.mla_prefill(self.h, _ptr(hidden), cu_p, pr_p, so_p, B, _ptr(cache),
                                   int(cache.shape[0]), _ptr(out), wsp, wsn)
         self._check(rc, self.h, "mla_prefill")
+        return out
+
+    def prefill_paged(self, hidden, cu_new, prior_len, block_table, page_rows, cache, out=None):
+        """mla_prefill_paged: block_table (B, max_pages) int32 host array; page
+        k of the cache is rows [k * page_rows, (k + 1) * page_rows)."""
+        import torch
+        self._sync_stream()
+        cu_a, cu_p = _i32(cu_new)
+        pr_a, pr_p = _i32(prior_len)
+        bt = np.ascontiguousarray(block_table, dtype=np.int32)
+        bt_a, bt_p = _i32(bt.reshape(-1))
+        B = len(pr_a)
+        T = int(cu_a[-1])
+        rows = int((pr_a.astype(np.int64) + np.diff(cu_a)).sum())
+        if out is None:
+            out = torch.empty((T, self.dims.hidden), dtype=self.torch_dtype, device=self.device)
+        wsp, wsn = self.ws.get(self.lib.mla_prefill_paged_workspace_bytes(self.h, T, B,
+                                                                          max(rows, 1)))
+        rc = self.lib.mla_prefill_paged(self.h, _ptr(hidden), cu_p, pr_p, bt_p, int(bt.shape[1]),
+                                        int(page_rows), B, _ptr(cache), int(cache.shape[0]),
+                                        _ptr(out), wsp, wsn)
+        self._check(rc, self.h, "mla_prefill_paged")
         return out
 
 

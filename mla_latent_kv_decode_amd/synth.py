@@ -101,6 +101,9 @@ WORKLOADS = {
     # V3 ragged decode, B=32, cached rows ~ U{2048..16384}
     "v3_decode_b32": Workload("v3_decode_b32", V3, "bf16", 0.02, "decode", 32,
                               len_lo=2048, len_hi=16384),
+    # the same batch on an FP8 latent cache
+    "v3_decode_b32_fp8": Workload("v3_decode_b32_fp8", V3, "bf16", 0.02, "decode", 32,
+                                  len_lo=2048, len_hi=16384, kv="fp8"),
     # V3 long-context stress: one sequence with 32768 cached rows
     "v3_decode_b1_s32768": Workload("v3_decode_b1_s32768", V3, "bf16", 0.02,
                                     "decode", 1, fixed_lengths=(32768,)),

@@ -361,13 +361,16 @@ def decode_batch(x, lengths, rows_per_seq, w: dict, shape: MLAShape):
 
 
 def prefill_batch(x, cu_new, prior, rows_prior_per_seq, w: dict, shape: MLAShape,
-                  query_subset=None):
+                  query_subset=None, kv_store=None):
     """Chunked causal prefill: sequence b has ``prior[b]`` cached rows and
     new tokens x[cu_new[b]:cu_new[b+1]] at positions prior[b], prior[b]+1, ...
 
     ``query_subset`` (optional, per sequence, indices into that sequence's new
     tokens) limits which outputs are computed; all new rows are still appended
     first, so a kept query sees exactly the keys it would in the full run.
+    ``kv_store`` (optional) is mla_step's: it maps every key row, cached and
+    new, to what the cache hands back when read (the new rows are written
+    before they are read), before the expansion.
     Returns a list of (indices, y_rows) per sequence."""
     x = _f64(x)
     out = []
@@ -378,6 +381,8 @@ def prefill_batch(x, cu_new, prior, rows_prior_per_seq, w: dict, shape: MLAShape
         rows_new = latent_rows(xb, pos, w["w_kva"], w["kv_norm_g"], shape)
         rows = np.concatenate([_f64(rows_prior_per_seq[b]).reshape(-1, shape.row),
                                rows_new], axis=0)
+        if kv_store is not None:
+            rows = kv_store(rows)
         idx = np.arange(n) if query_subset is None else np.asarray(query_subset[b])
         dc = shape.kv_lora
         k_n, v = expand_kv(rows[:, :dc], w["w_kvb"], shape)

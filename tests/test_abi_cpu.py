@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(mla):
     missing = [n for n in names if not hasattr(mla, n)]
     assert not missing, missing
     assert set(names) == set(L._SIGS), set(names) ^ set(L._SIGS)
-    assert mla.mla_abi_version() == 6
+    assert mla.mla_abi_version() == 7
 
 
 def test_status_strings(mla):
@@ -78,9 +78,9 @@ def test_yarn_config_check(mla):
 
 def test_fp8_cache_config_and_row_bytes(mla):
     """FP8 latent rows: accepted for the shapes the FP8 core serves (bf16
-    layer, latent 512, rope 64, a multiple of 16 heads below a multiple of
-    128), refused otherwise; 656 bytes per row (512 codes + 64 bf16 + scale,
-    padded to 16)."""
+    layer, latent 512, rope 64, a multiple of 16 heads, 128-head layers
+    included), refused otherwise; 656 bytes per row (512 codes + 64 bf16 +
+    scale, padded to 16)."""
     ok = lambda c: mla.mla_config_check(ctypes.byref(c))
     rb = lambda c: mla.mla_cache_row_bytes(ctypes.byref(c))
     c8 = cfg(kv_storage=L.MLA_KV_FP8_E4M3)
@@ -88,11 +88,11 @@ def test_fp8_cache_config_and_row_bytes(mla):
     assert rb(cfg()) == 576 * 2 and rb(cfg(synth.TINY, "f32")) == 24 * 4
     assert ok(cfg(kv_storage=2)) == L.MLA_ERR_INVALID_ARG
     assert rb(cfg(kv_storage=2)) == 0
-    for bad in (cfg(synth.V3, kv_storage=1), cfg(synth.TINY, "f32", kv_storage=1),
-                cfg(kv_lora=256, kv_storage=1), cfg(qk_rope=32, kv_storage=1),
-                cfg(n_heads=24, kv_storage=1)):
+    for bad in (cfg(synth.TINY, "f32", kv_storage=1), cfg(kv_lora=256, kv_storage=1),
+                cfg(qk_rope=32, kv_storage=1), cfg(n_heads=24, kv_storage=1)):
         assert ok(bad) == L.MLA_ERR_SHAPE
     assert ok(cfg(n_heads=32, kv_storage=1)) == L.MLA_OK
+    assert ok(cfg(synth.V3, kv_storage=1)) == L.MLA_OK
 
 
 def _i32(a):
@@ -229,6 +229,36 @@ def test_prefill_check(mla):
     assert chk([0, 4, 3], [0, 2], [0, 4], 9) == L.MLA_ERR_INVALID_ARG   # decreasing
     assert chk([0, 4, 7], [0, -2], [0, 4], 9) == L.MLA_ERR_INVALID_ARG
     assert chk([0, 0, 0], [3, 2], [0, 4], 9) == L.MLA_ERR_INVALID_ARG   # no new tokens
+    assert chk([0, 4, 7], [2**31 - 3, 0], [0, 0], 2**40) == L.MLA_ERR_INVALID_ARG  # > int32
+
+
+def test_prefill_paged_check(mla):
+    """mla_prefill_paged's host checks: the rows it reads (prior + new per
+    sequence) must sit on valid pages of the table; the decode checks' page
+    size rules."""
+    c = cfg()
+
+    def chk(cu, prior, table, page_rows, rows):
+        ca, cp = _i32(cu)
+        pa, pp = _i32(prior)
+        t = np.ascontiguousarray(table, dtype=np.int32)
+        ta, tp = _i32(t.reshape(-1))
+        return mla.mla_prefill_paged_check(ctypes.byref(c), cp, pp, tp, t.shape[1], page_rows,
+                                           len(pa), rows)
+
+    # 4 pages of 32 rows: sequence 0 (2 + 38 rows) on pages 3, 1; sequence 1
+    # (0 + 5 rows) on page 0 (its second entry is never read)
+    assert chk([0, 38, 43], [2, 0], [[3, 1], [0, -7]], 32, 128) == L.MLA_OK
+    assert chk([0, 38, 43], [2, 0], [[3, 4], [0, 0]], 32, 128) == L.MLA_ERR_CAPACITY   # page 4
+    assert chk([0, 38, 43], [2, 0], [[3, -1], [0, 0]], 32, 128) == L.MLA_ERR_CAPACITY  # negative
+    assert chk([0, 38, 43], [27, 0], [[3, 1], [0, 0]], 32, 128) == L.MLA_ERR_CAPACITY  # 3 pages
+    for bad_p in (16, 48, 0):
+        assert chk([0, 38, 43], [2, 0], [[3, 1], [0, 0]], bad_p, 128) == L.MLA_ERR_INVALID_ARG
+    assert chk([1, 38, 43], [2, 0], [[3, 1], [0, 0]], 32, 128) == L.MLA_ERR_INVALID_ARG
+    assert chk([0, 38, 37], [2, 0], [[3, 1], [0, 0]], 32, 128) == L.MLA_ERR_INVALID_ARG
+    assert chk([0, 0, 0], [2, 3], [[3, 1], [0, 0]], 32, 128) == L.MLA_ERR_INVALID_ARG
+    # pages may be shared (a common prefix read by both sequences)
+    assert chk([0, 1, 2], [31, 31], [[2], [2]], 32, 128) == L.MLA_OK
 
 
 def test_product_path_has_no_oracle_dependency():

@@ -140,14 +140,35 @@ def test_fp8_decode_step(lens):
         assert err < tol("bf16"), f"seq {b}: y rel err {err:.3e}"
 
 
-def test_fp8_prefill_is_refused():
+def test_fp8_v3_decode_ragged_small():
+    """A 128-head layer (q-LoRA, V3 shapes) on an FP8 cache: the FP8 core runs
+    one workgroup per 16-head group of every part (eight per part here)."""
+    lens = [0, 1, 33, 64, 700, 2000]
+    case = DecodeCase(synth.V3, "bf16", 0.02, lens, kv="fp8")
+    _check(case, range(len(lens)))
+
+
+def test_fp8_v3_decode_step():
+    """The V3 step appends FP8 rows through the q-LoRA projection path."""
     import torch
-    from mla_latent_kv_decode_amd.lib import MLAError, MLA_ERR_SHAPE
-    d = synth.V2_LITE
-    w = synth.make_weights(d, 0.02, "bf16")
-    layer = make_layer(d, "bf16", w, kv="fp8")
-    cache = layer.new_cache(64)
-    x = dev(synth.hidden_states(0, 8, d.hidden, "bf16"), torch.bfloat16)
-    with pytest.raises(MLAError) as e:
-        layer.prefill(x, np.array([0, 8]), np.array([0]), np.array([0]), cache)
-    assert e.value.status == MLA_ERR_SHAPE
+    case = DecodeCase(synth.V3, "bf16", 0.02, [3, 40, 1500], kv="fp8")
+    y = host(case.layer.decode_step(dev(case.x_new, torch.bfloat16), case.seq_off, case.seq_len,
+                                    case.cache))
+    for b in range(case.B):
+        y_ref, _ = case.oracle(b)
+        err = row_rel_err(y[b:b + 1], y_ref[None])[0]
+        assert err < tol("bf16"), f"seq {b}: y rel err {err:.3e}"
+
+
+@pytest.fixture(scope="module")
+def fp8_v3_b32():
+    return full_size_case("v3_decode_b32", kv="fp8")
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("part", range(4))
+def test_fp8_v3_decode_b32_full_size(fp8_v3_b32, part):
+    """The V3 B=32 ragged batch on an FP8 cache: y, q_cat and o_lat of every
+    sequence against the oracle, a quarter of the batch per test."""
+    case, out = fp8_v3_b32
+    _compare(case, out, chunk(case.B, part))

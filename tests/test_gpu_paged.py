@@ -171,3 +171,36 @@ def test_paged_decode_large_pages():
     a second, short ones sharing nothing."""
     case = DecodeCase(synth.V2_LITE, "bf16", 0.02, [4095, 4096, 10, 5000], keep=[0, 1, 3])
     _paged_vs_contiguous(case, 4096, 13, [0, 1, 3])
+
+
+@pytest.mark.parametrize("kv,page_rows", [("dtype", 32), ("dtype", 256), ("fp8", 64)])
+def test_paged_prefill_matches_contiguous(kv, page_rows):
+    """mla_prefill_paged over a pool of pages in random order gives, bit for
+    bit, what mla_prefill gives on the contiguous cache holding the same rows
+    (both expand and attend the same rows in the same order), and matches the
+    oracle; sequences of several pages with ragged last pages, a long prior
+    and a one-token chunk."""
+    import types
+
+    import torch
+    from tests.test_gpu_prefill import check_prefill, prefill_inputs
+    c = prefill_inputs(synth.V2_LITE, "bf16", 0.02, [0, 300, 33], [600, 70, 1], kv=kv)
+    prior = c.prior.astype(np.int32)
+    y_c = c.layer.prefill(c.x_dev, c.cu_new, prior, c.seq_off, c.cache)
+    view = types.SimpleNamespace(seq_len=c.tot, B=len(c.tot), cache=c.cache, seq_off=c.seq_off)
+    pool, table = _page_pool(view, page_rows, seed=7)
+    y_p = c.layer.prefill_paged(c.x_dev, c.cu_new, prior, table, page_rows, pool)
+    assert torch.equal(y_p, y_c)
+    check_prefill(c, host(y_p))
+
+
+def test_paged_prefill_v3():
+    """The 128-head layer (query LoRA) over a paged cache, against the oracle."""
+    import types
+
+    from tests.test_gpu_prefill import check_prefill, prefill_inputs
+    c = prefill_inputs(synth.V3, "bf16", 0.02, [0, 70], [40, 9])
+    view = types.SimpleNamespace(seq_len=c.tot, B=len(c.tot), cache=c.cache, seq_off=c.seq_off)
+    pool, table = _page_pool(view, 32, seed=3)
+    y = c.layer.prefill_paged(c.x_dev, c.cu_new, c.prior.astype(np.int32), table, 32, pool)
+    check_prefill(c, host(y))

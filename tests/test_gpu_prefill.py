@@ -2,45 +2,67 @@
 attends to its own sequence's rows up to its position (cached prefix + the
 new tokens before it)."""
 
+import types
+
 import numpy as np
 import pytest
 
 from mla_latent_kv_decode_amd import synth
+from oracle import fp8 as F8
 from oracle import mla as O
 from tests.helpers import dev, fill_sequence, host, make_layer, oracle_shape, row_rel_err, tol
 
 pytestmark = pytest.mark.gpu
 
 
-def run_prefill_case(dims, dtype, std, prior, new, query_subset=None):
+def prefill_inputs(dims, dtype, std, prior, new, kv="dtype", gap=0):
+    """A chunked-prefill batch: sequence b owns cache rows [seq_off[b],
+    seq_off[b] + prior[b] + new[b]) (gap free rows between sequences), all of
+    them appended through the library first; returns the layer, weights,
+    cache, hidden states and offsets."""
     import torch
     w = synth.make_weights(dims, std, dtype, random_gains=True)
-    layer = make_layer(dims, dtype, w)
+    layer = make_layer(dims, dtype, w, kv=kv)
     prior = np.asarray(prior, np.int64)
     new = np.asarray(new, np.int64)
     tot = prior + new
-    seq_off = np.concatenate([[0], np.cumsum(tot)[:-1]]).astype(np.int64)
+    seq_off = np.concatenate([[0], np.cumsum(tot + gap)[:-1]]).astype(np.int64)
     cu_new = np.concatenate([[0], np.cumsum(new)]).astype(np.int32)
-    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
-    cache = torch.zeros((int(tot.sum()), dims.row), dtype=tdt, device="cuda")
+    cache = layer.new_cache(int((tot + gap).sum()))
     hidden = []
     for b in range(len(prior)):
         x, _ = fill_sequence(layer, dims, dtype, b, int(tot[b]), cache, int(seq_off[b]),
                              keep=True)
         hidden.append(x)
     x_new = np.concatenate([hidden[b][prior[b]:] for b in range(len(prior))])
-    y = host(layer.prefill(dev(x_new, tdt), cu_new, prior.astype(np.int32), seq_off, cache))
-    shp = oracle_shape(dims)
-    rows_prior = [O.latent_rows(hidden[b][:prior[b]], np.arange(prior[b]), w["w_kva"],
-                                w["kv_norm_g"], shp) if prior[b] else np.zeros((0, shp.row))
-                  for b in range(len(prior))]
-    ref = O.prefill_batch(x_new, cu_new, prior, rows_prior, w, shp, query_subset=query_subset)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    return types.SimpleNamespace(dims=dims, dtype=dtype, kv=kv, w=w, layer=layer, prior=prior,
+                                 new=new, tot=tot, seq_off=seq_off, cu_new=cu_new, cache=cache,
+                                 hidden=hidden, x_new=x_new, x_dev=dev(x_new, tdt))
+
+
+def check_prefill(c, y, query_subset=None):
+    """Rows of y (host) against the fp64 oracle (reading FP8 rows back as the
+    cache stores them); returns the worst per-row relative error."""
+    shp = oracle_shape(c.dims)
+    rows_prior = [O.latent_rows(c.hidden[b][:c.prior[b]], np.arange(c.prior[b]), c.w["w_kva"],
+                                c.w["kv_norm_g"], shp) if c.prior[b] else np.zeros((0, shp.row))
+                  for b in range(len(c.prior))]
+    store = (lambda r: F8.fp8_rows(r, shp.kv_lora)) if c.kv == "fp8" else None
+    ref = O.prefill_batch(c.x_new, c.cu_new, c.prior, rows_prior, c.w, shp,
+                          query_subset=query_subset, kv_store=store)
     worst = 0.0
     for b, (idx, yr) in enumerate(ref):
-        err = row_rel_err(y[cu_new[b] + idx], yr)
+        err = row_rel_err(y[c.cu_new[b] + idx], yr)
         worst = max(worst, float(err.max()))
-        assert err.max() < tol(dtype), (b, int(idx[np.argmax(err)]), float(err.max()))
+        assert err.max() < tol(c.dtype), (b, int(idx[np.argmax(err)]), float(err.max()))
     return worst
+
+
+def run_prefill_case(dims, dtype, std, prior, new, query_subset=None, kv="dtype", gap=0):
+    c = prefill_inputs(dims, dtype, std, prior, new, kv=kv, gap=gap)
+    y = host(c.layer.prefill(c.x_dev, c.cu_new, c.prior.astype(np.int32), c.seq_off, c.cache))
+    return check_prefill(c, y, query_subset)
 
 
 def test_tiny_f32_prefill():
@@ -83,3 +105,14 @@ def test_v3_prefill_4x4096_full_size():
     q = np.unique(np.concatenate([np.arange(0, 4096, 64), [1, 31, 32, 255, 256, 2047],
                                   np.arange(4096 - 256, 4096)]))
     run_prefill_case(w.dims, "bf16", w.weight_std, prior, new, query_subset=[q] * 4)
+
+
+def test_v2lite_fp8_prefill():
+    """An FP8 cache: the key rows are decoded to bf16 before the expansion;
+    against the oracle reading its own quantised rows.  Gaps between the
+    sequences' rows exercise the gather's source offsets."""
+    run_prefill_case(synth.V2_LITE, "bf16", 0.02, [0, 300, 33], [600, 70, 1], kv="fp8", gap=5)
+
+
+def test_v3_fp8_prefill_small():
+    run_prefill_case(synth.V3, "bf16", 0.02, [0, 21], [24, 9], kv="fp8")

@@ -435,6 +435,37 @@ def test_fp8_cache_decode_step_stays_near_the_exact_one():
     assert 0 < rel_err(q8, exact) < 2.0 ** -4
 
 
+def test_prefill_batch_is_independent_steps():
+    """oracle.mla.prefill_batch over a ragged batch (a sequence with no prior
+    rows, one with a long prior, a one-token chunk), with and without an FP8
+    read-back and with a query subset, equals oracle.mla.mla_step run on each
+    sequence alone (pinned by brute force and cached == uncached above): a
+    sequence's outputs depend on its own rows only."""
+    d = synth.TINY
+    shp = shape_of(d)
+    w = synth.make_weights(d, 0.05, "f32", random_gains=True)
+    prior, new = np.array([0, 37, 5]), np.array([9, 4, 1])
+    xs = [synth.hidden_states(b, int(prior[b] + new[b]), d.hidden, "f32") for b in range(3)]
+    x_new = np.concatenate([xs[b][prior[b]:] for b in range(3)])
+    cu = np.concatenate([[0], np.cumsum(new)])
+    rows_prior = [O.latent_rows(xs[b][:prior[b]], np.arange(prior[b]), w["w_kva"],
+                                w["kv_norm_g"], shp) for b in range(3)]
+    store = lambda r: F8.fp8_rows(r, shp.kv_lora)  # noqa: E731
+    subset = [np.array([0, 8]), np.array([1, 2, 3]), np.array([0])]
+    for kv_store in (None, store):
+        for qs in (None, subset):
+            got = O.prefill_batch(x_new, cu, prior, rows_prior, w, shp, query_subset=qs,
+                                  kv_store=kv_store)
+            for b, (idx, y) in enumerate(got):
+                want = O.mla_step(xs[b][prior[b]:], prior[b] + np.arange(new[b]), rows_prior[b],
+                                  w, shp, kv_store=kv_store)["y"]
+                assert np.allclose(y, want[idx], rtol=1e-12, atol=1e-14), (b, kv_store, qs)
+    # the read-back reaches the result
+    a = O.prefill_batch(x_new, cu, prior, rows_prior, w, shp)[1][1]
+    q = O.prefill_batch(x_new, cu, prior, rows_prior, w, shp, kv_store=store)[1][1]
+    assert rel_err(q, a) > 1e-6
+
+
 # ---------------------------------------------------------------- paged cache
 from oracle import paged as PG  # noqa: E402
 
