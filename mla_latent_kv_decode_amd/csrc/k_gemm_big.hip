@@ -1,23 +1,29 @@
 // Large-tile bf16 MFMA GEMM for projections with many rows (prefill, bulk
-// appends): C = alpha A W^T with A (M, K) and W (N, K) both row-major and
-// K-contiguous (activations and a linear layer's weight), fp32 accumulation,
-// C stored as bf16 or fp32 with its own row stride.  These are the
+// appends): C = alpha A W^T with A (M, K) and W (N, K), fp32 accumulation, C
+// stored as bf16 or fp32 with its own row stride.  These are the
 // compute-bound, GEMM-shaped steps of prefill ("Transformer and KV Cache
 // Basics", KV Cache -- Conceptually).
+//
+// Operand layout ("fragment-tiled"): both operands are stored as a list of
+// 1 KB fragments, fragment (b, s) = rows 16 b .. 16 b + 15, k = 32 s .. 32 s
+// + 31 at byte (b * K / 32 + s) * 1024, in the lane order of a
+// v_mfma_f32_16x16x32_bf16 operand (lane l holds row l % 16, k = 8 (l / 16)
+// .. + 7, 16 bytes at l * 16).  A row block's fragments follow each other in
+// k, so a tile's operand stream is a sequential read of 1 KB blocks: against
+// the same GEMM reading row-major rows (16 rows x 64 bytes per copy) the copy
+// stream alone runs twice as fast (measured) and the GEMM ~20-35 % faster.
+// Weights are tiled once when they are absorbed; activations by tile_rows
+// just before the product (one extra pass over A).
 //
 // Block = 512 threads (8 waves, two per SIMD, so one wave's fragment reads
 // overlap the other's products) computing a 256 x BN tile of C (BN = 256 or
 // 128); wave (wm, wn) owns rows 128 wm .. +127 and columns (BN / 4) wn .. +
 // BN / 4 - 1.  K advances in steps of 32 through a 4-stage LDS ring filled by
 // global_load_lds_dwordx4 (three steps in flight; one barrier per step both
-// publishes a stage and frees the one the next copy overwrites).
-//
-// LDS layout: a stage is a list of 1 KB fragments, each the 16 rows x 32 k
-// operand of one v_mfma_f32_16x16x32_bf16 stored in lane order (lane l holds
-// row l % 16, k = 8 (l / 16) .. + 7), A's 16-row blocks first, then W's.
-// A copy instruction moves one fragment (lane l fetches exactly the 16 bytes
-// it deposits at l * 16) and an operand read is one contiguous 1 KB ds_read
-// per wave, so neither side has bank conflicts.
+// publishes a stage and frees the one the next copy overwrites).  A copy
+// instruction moves one fragment (lane l fetches the 16 bytes it deposits at
+// l * 16) and an operand read is one contiguous 1 KB ds_read per wave, so
+// neither side has bank conflicts.
 //
 // The product is taken transposed, D = W_frag . A_frag^T (C^T tile), so lane
 // l ends with C[m = l % 16][n = 4 (l / 16) .. + 3]: four adjacent columns of
@@ -27,6 +33,8 @@
 // b runs on XCD b % 8) take a contiguous range of tiles, walked in groups of
 // 8 row tiles, so blocks running together on one XCD share A rows and W rows
 // in that XCD's L2.
+#include <algorithm>
+
 #include "kernels.h"
 
 namespace mla {
@@ -85,8 +93,8 @@ __device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int* tm
 
 template <int BN>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-gemm_big_k(const bf16* __restrict__ A, int64_t lda, const bf16* __restrict__ W, int64_t ldw,
-           int M, int N, int K, int tiles_m, int tiles_n, GemmOut out) {
+gemm_big_k(const bf16* __restrict__ A, const bf16* __restrict__ W, int M, int N, int K,
+           int tiles_m, int tiles_n, GemmOut out) {
   using C = Cfg<BN>;
   __shared__ __attribute__((aligned(1024))) char lds[NST * C::ST];
   int tm, tn;
@@ -98,25 +106,26 @@ gemm_big_k(const bf16* __restrict__ A, int64_t lda, const bf16* __restrict__ W, 
   const uint32_t lds0 = lds_u32(lds);
 
   // the PER_WAVE fragments this wave copies each stage: fragment f = wave *
-  // PER_WAVE + u; rows past M / N re-read the last row (never stored)
+  // PER_WAVE + u of the stage; row blocks past M / N re-read the last one
+  // (never stored)
+  const int nk = K / BK;
+  const int rbA = (M + 15) / 16, rbW = (N + 15) / 16;
   const char* src[C::PER_WAVE];
 #pragma unroll
   for (int u = 0; u < C::PER_WAVE; ++u) {
     const int f = wave * C::PER_WAVE + u;
-    const int kofs = 8 * (lane >> 4);
     if (f < C::A_FR) {
-      const int m = min(m0 + 16 * f + (lane & 15), M - 1);
-      src[u] = reinterpret_cast<const char*>(A + (int64_t)m * lda + kofs);
+      const int rb = min(m0 / 16 + f, rbA - 1);
+      src[u] = reinterpret_cast<const char*>(A) + (int64_t)rb * nk * 1024 + lane * 16;
     } else {
-      const int n = min(n0 + 16 * (f - C::A_FR) + (lane & 15), N - 1);
-      src[u] = reinterpret_cast<const char*>(W + (int64_t)n * ldw + kofs);
+      const int rb = min(n0 / 16 + f - C::A_FR, rbW - 1);
+      src[u] = reinterpret_cast<const char*>(W) + (int64_t)rb * nk * 1024 + lane * 16;
     }
   }
-  const int nk = K / BK;
   auto issue = [&](int kb) {
     const uint32_t st = lds0 + (uint32_t)((kb % NST) * C::ST + wave * C::PER_WAVE * 1024);
 #pragma unroll
-    for (int u = 0; u < C::PER_WAVE; ++u) dma16(src[u] + (int64_t)kb * (BK * 2), st + u * 1024);
+    for (int u = 0; u < C::PER_WAVE; ++u) dma16(src[u] + (int64_t)kb * 1024, st + u * 1024);
   };
   // this wave's copies of step kb are done once at most `later` steps issued
   // after it are still outstanding
@@ -191,7 +200,36 @@ gemm_big_k(const bf16* __restrict__ A, int64_t lda, const bf16* __restrict__ W, 
   }
 }
 
+// Row-major rows (stride ld) -> fragment-tiled layout.  Block = 256 threads
+// for one 16-row block and four 32-k steps: thread t reads 16 bytes of row t /
+// 16 (256 contiguous bytes per row and block) and stores them at their lane
+// position in one of the four fragments (4 KB contiguous per block).  Rows
+// past M are stored as zeros.
+__global__ void __launch_bounds__(256)
+tile_rows_k(const bf16* __restrict__ x, int64_t ld, int M, int nks, bf16* __restrict__ t) {
+  const int r = threadIdx.x >> 4, c = threadIdx.x & 15;
+  const int ks = 4 * blockIdx.x + (c >> 2);
+  if (ks >= nks) return;
+  const int nrb = (M + 15) / 16;
+  for (int rb = blockIdx.y; rb < nrb; rb += gridDim.y) {
+    const int row = 16 * rb + r;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (row < M)
+      v = *reinterpret_cast<const uint4*>(x + (int64_t)row * ld + 32 * ks + 8 * (c & 3));
+    *reinterpret_cast<uint4*>(reinterpret_cast<char*>(t) + ((int64_t)rb * nks + ks) * 1024 +
+                              (r + 16 * (c & 3)) * 16) = v;
+  }
+}
+
 }  // namespace bg
+
+size_t tiled_bytes(int rows, int K) { return (size_t)((rows + 15) / 16) * 16 * K * 2; }
+
+void tile_rows(const bf16* x, int64_t ld, int rows, int K, bf16* t, hipStream_t st) {
+  const int nks = K / 32;
+  const dim3 grid((nks + 3) / 4, std::min((rows + 15) / 16, 65535));
+  bg::tile_rows_k<<<grid, 256, 0, st>>>(x, ld, rows, nks, t);
+}
 
 int gemm_big_bn(int M, int N, int n_cu) {
   // the wider tile unless its grid leaves part of the last wave of tiles idle
@@ -206,15 +244,15 @@ int gemm_big_bn(int M, int N, int n_cu) {
   return eff(256) >= eff(128) ? 256 : 128;
 }
 
-void gemm_big(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int M, int N, int K,
-              const GemmOut& out, int n_cu, hipStream_t st) {
+void gemm_big(const bf16* A, const bf16* W, int M, int N, int K, const GemmOut& out, int n_cu,
+              hipStream_t st) {
   const int bn = gemm_big_bn(M, N, n_cu);
   const int tiles_m = (M + bg::BM - 1) / bg::BM, tiles_n = (N + bn - 1) / bn;
   const dim3 grid(tiles_m * tiles_n);
   if (bn == 256)
-    bg::gemm_big_k<256><<<grid, 512, 0, st>>>(A, lda, W, ldw, M, N, K, tiles_m, tiles_n, out);
+    bg::gemm_big_k<256><<<grid, 512, 0, st>>>(A, W, M, N, K, tiles_m, tiles_n, out);
   else
-    bg::gemm_big_k<128><<<grid, 512, 0, st>>>(A, lda, W, ldw, M, N, K, tiles_m, tiles_n, out);
+    bg::gemm_big_k<128><<<grid, 512, 0, st>>>(A, W, M, N, K, tiles_m, tiles_n, out);
 }
 
 }  // namespace mla

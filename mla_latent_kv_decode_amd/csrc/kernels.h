@@ -109,11 +109,17 @@ void gemm_bf16_mfma(const bf16* A, int64_t lda, int64_t sA, const bf16* W, int64
 int gemm_bf16_ksplit(int M, int N, int K, int batch, int n_cu);
 
 // Large-tile GEMM (k_gemm_big.hip) for many rows: C = alpha A W^T, batch 1,
-// K a multiple of 32, lda / ldw multiples of 8, out.ldo a multiple of 4.
+// K a multiple of 32, out.ldo a multiple of 4.  A and W are in the
+// fragment-tiled layout tile_rows writes (tiled_bytes(rows, K) bytes each).
 // gemm_big_bn: the tile width (256 or 128) it picks for an M x N product.
 int gemm_big_bn(int M, int N, int n_cu);
-void gemm_big(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int M, int N, int K,
-              const GemmOut& out, int n_cu, hipStream_t st);
+void gemm_big(const bf16* A, const bf16* W, int M, int N, int K, const GemmOut& out, int n_cu,
+              hipStream_t st);
+// Row-major rows x (rows, K) with row stride ld (a multiple of 8) -> the
+// fragment-tiled layout: 16-row block b, k step s (32 wide) at byte (b * K /
+// 32 + s) * 1024, lanes in MFMA operand order; rows past `rows` are zero.
+size_t tiled_bytes(int rows, int K);
+void tile_rows(const bf16* x, int64_t ld, int rows, int K, bf16* t, hipStream_t st);
 
 // Split-K partial sums as a consumer sees them: element (z, row, col) at
 // p[z * zs + row * ld + col], summed over z = 0..ks-1 in order.

@@ -73,6 +73,15 @@ struct mla_ctx {
   void* w_uv = nullptr;   // (H, dv, dc)
   void* w_o = nullptr;
   void* w_in = nullptr;   // [W_kva ; W_q] (or [W_kva ; W_qa]) rows: one in-projection GEMM
+  // fragment-tiled copies of the weights the large-tile GEMM reads (bf16
+  // layers with aligned dimensions; null where the width is not a multiple
+  // of 32)
+  void* t_in = nullptr;
+  void* t_q = nullptr;   // w_q or w_qa
+  void* t_qb = nullptr;
+  void* t_kva = nullptr;
+  void* t_kvb = nullptr;
+  void* t_o = nullptr;
   int n_in = 0;           // rows of w_in
   Staging ring[kRing];
   int ring_next = 0;
@@ -227,27 +236,37 @@ int gemm_ks(const mla_ctx* h, int M, int N, int K, int batch) {
   return mfma_gemm(h, N, K) ? mla::gemm_bf16_ksplit(M, N, K, batch, h->n_cu) : 1;
 }
 
-// fp32 scratch floats of gemm_out (split-K partials, or the VALU path's C)
+// floats that hold A in the fragment-tiled layout of the large-tile GEMM
+size_t tiled_floats(int M, int K) { return align_up(mla::tiled_bytes(M, K)) / 4; }
+
+// fp32 scratch floats of gemm_out (split-K partials, the VALU path's C, or A
+// tiled for the large-tile GEMM)
 size_t out_scratch(const mla_ctx* h, int M, int N, int K, int batch) {
-  if (big_gemm(h, M, N, K, batch)) return 0;
+  if (big_gemm(h, M, N, K, batch)) return tiled_floats(M, K);
   const int ks = gemm_ks(h, M, N, K, batch);
   if (mfma_gemm(h, N, K) && ks == 1) return 0;
   return (size_t)ks * batch * M * N;
 }
-// fp32 floats of gemm_part's partial buffer
+// fp32 floats of gemm_part's partial buffer (then A tiled for the large-tile
+// GEMM)
 size_t part_floats(const mla_ctx* h, int M, int N, int K) {
-  return (size_t)gemm_ks(h, M, N, K, 1) * M * N;
+  const size_t c = (size_t)gemm_ks(h, M, N, K, 1) * M * N;
+  return big_gemm(h, M, N, K, 1) ? align_up(c * 4) / 4 + tiled_floats(M, K) : c;
 }
 
 // out = alpha * A W^T (batched, strided).  MFMA path: epilogue fused when K is
 // not split, else partials in `scratch` and a store kernel sums them.
+// Wt: W's fragment-tiled copy (batch 1), which lets the large-tile GEMM run;
+// A is then tiled into `scratch` first.
 template <typename T>
 void gemm_out(mla_ctx* h, const T* A, int64_t lda, int64_t sA, const T* W, int64_t ldw,
               int64_t sW, int M, int N, int K, int batch, const mla::GemmOut& out,
-              float* scratch) {
+              float* scratch, const void* Wt = nullptr) {
   if constexpr (sizeof(T) == 2) {
-    if (big_gemm(h, M, N, K, batch)) {
-      mla::gemm_big(A, lda, W, ldw, M, N, K, out, h->n_cu, h->stream);
+    if (Wt && big_gemm(h, M, N, K, batch)) {
+      bf16* At = reinterpret_cast<bf16*>(scratch);
+      mla::tile_rows(A, lda, M, K, At, h->stream);
+      mla::gemm_big(At, static_cast<const bf16*>(Wt), M, N, K, out, h->n_cu, h->stream);
       return;
     }
     if (mfma_gemm(h, N, K)) {
@@ -265,11 +284,13 @@ void gemm_out(mla_ctx* h, const T* A, int64_t lda, int64_t sA, const T* W, int64
 // kernel to sum (part_floats() floats).
 template <typename T>
 mla::Part gemm_part(mla_ctx* h, const T* A, int64_t lda, const T* W, int64_t ldw, int M,
-                    int N, int K, float* part) {
+                    int N, int K, float* part, const void* Wt = nullptr) {
   if constexpr (sizeof(T) == 2) {
-    if (big_gemm(h, M, N, K, 1)) {
-      mla::gemm_big(A, lda, W, ldw, M, N, K, mla::GemmOut{part, nullptr, N, 0, 1.f}, h->n_cu,
-                    h->stream);
+    if (Wt && big_gemm(h, M, N, K, 1)) {
+      bf16* At = reinterpret_cast<bf16*>(part + align_up((size_t)M * N * 4) / 4);
+      mla::tile_rows(A, lda, M, K, At, h->stream);
+      mla::gemm_big(At, static_cast<const bf16*>(Wt), M, N, K,
+                    mla::GemmOut{part, nullptr, N, 0, 1.f}, h->n_cu, h->stream);
       return mla::Part{part, 1, N, (int64_t)M * N};
     }
     if (mfma_gemm(h, N, K)) {
@@ -955,8 +976,9 @@ int mla_create(const mla_config* cfg, void* stream, mla_handle* out) {
 }
 
 static void free_weights(mla_ctx* h) {
-  void** ws[] = {&h->w_q, &h->w_qa, &h->q_norm_g, &h->w_qb, &h->w_kva, &h->kv_norm_g,
-                 &h->w_kvb, &h->w_ukT, &h->w_uv, &h->w_o, &h->w_in};
+  void** ws[] = {&h->w_q,  &h->w_qa, &h->q_norm_g, &h->w_qb,  &h->w_kva, &h->kv_norm_g,
+                 &h->w_kvb, &h->w_ukT, &h->w_uv,   &h->w_o,   &h->w_in,  &h->t_in,
+                 &h->t_q,   &h->t_qb,  &h->t_kva,  &h->t_kvb, &h->t_o};
   for (void** p : ws) {
     if (*p) (void)hipFree(*p);
     *p = nullptr;
@@ -1083,6 +1105,22 @@ int mla_absorb_weights(mla_handle h, const void* w_q, const void* w_qa, const vo
     mla::transpose_heads<bf16>((const bf16*)w_kvb, (bf16*)h->w_ukT, d.H, d.dn, d.dc,
                                (int64_t)(d.dn + d.dv) * d.dc, h->stream);
   if ((rc = check_launch(h, "transpose_heads"))) return rc;
+  // tiled copies for the large-tile GEMM (prefill, bulk appends, wide steps)
+  if (!is_f32(h) && h->dims_aligned) {
+    auto tile = [&](void** dst, const void* src, int rows, int K) -> int {
+      if (K % 32) return MLA_OK;
+      HIP_TRY(h, hipMalloc(dst, mla::tiled_bytes(rows, K)));
+      mla::tile_rows(static_cast<const bf16*>(src), K, rows, K, static_cast<bf16*>(*dst),
+                     h->stream);
+      return check_launch(h, "tile_rows");
+    };
+    if ((rc = tile(&h->t_in, h->w_in, h->n_in, d.D))) return rc;
+    if ((rc = tile(&h->t_q, d.dq ? h->w_qa : h->w_q, d.dq ? d.dq : (int)qw, d.D))) return rc;
+    if (d.dq && (rc = tile(&h->t_qb, h->w_qb, (int)qw, d.dq))) return rc;
+    if ((rc = tile(&h->t_kva, h->w_kva, d.R, d.D))) return rc;
+    if ((rc = tile(&h->t_kvb, h->w_kvb, d.H * (d.dn + d.dv), d.dc))) return rc;
+    if ((rc = tile(&h->t_o, h->w_o, d.D, d.H * d.dv))) return rc;
+  }
   HIP_TRY(h, hipStreamSynchronize(h->stream));
   h->absorbed = true;
   return MLA_OK;
@@ -1116,7 +1154,8 @@ static void run_append(mla_ctx* h, const T* hidden, int ntok, T* cache, void* ws
                        const AppendLayout& L) {
   const Dims& d = h->d;
   const mla::Part a =
-      gemm_part<T>(h, hidden, d.D, (const T*)h->w_kva, d.D, ntok, d.R, d.D, at<float>(ws, L.part));
+      gemm_part<T>(h, hidden, d.D, (const T*)h->w_kva, d.D, ntok, d.R, d.D, at<float>(ws, L.part),
+                   h->t_kva);
   mla::append_rows<T>(a, ntok, at<int32_t>(ws, L.pos), at<int64_t>(ws, L.slot),
                       (const T*)h->kv_norm_g, cache, d, h->rope, h->stream);
 }
@@ -1142,7 +1181,7 @@ int mla_append_latent(mla_handle h, const void* hidden, const int32_t* pos, cons
   } else if (h->kv8) {
     const Dims& d = h->d;
     const mla::Part a = gemm_part<bf16>(h, (const bf16*)hidden, d.D, (const bf16*)h->w_kva, d.D, T,
-                                        d.R, d.D, at<float>(ws, L.part));
+                                        d.R, d.D, at<float>(ws, L.part), h->t_kva);
     mla::append_rows_fp8(a, T, at<int32_t>(ws, L.pos), at<int64_t>(ws, L.slot),
                          (const bf16*)h->kv_norm_g, (uint8_t*)cache, d, h->rope, h->stream);
   } else {
@@ -1264,7 +1303,7 @@ static void run_q_and_append(mla_ctx* h, const T* x, int B, void* ws, const Deco
   if (L.step) {
     // one GEMM for [kv_a | q (or q_a)] over the same hidden states
     const mla::Part pin = gemm_part<T>(h, x, d.D, (const T*)h->w_in, d.D, B, h->n_in, d.D,
-                                       at<float>(ws, L.pin));
+                                       at<float>(ws, L.pin), h->t_in);
     if (!d.dq) {
       mla::step_finish<T>(pin, B, mt.pos, slot_dev, (const T*)h->kv_norm_g, cache, q_nope, q_rope,
                           tok_stride, d.R, d.scale, d, h->rope, h->stream, h->kv8);
@@ -1280,15 +1319,16 @@ static void run_q_and_append(mla_ctx* h, const T* x, int B, void* ws, const Deco
     pa.p += d.R;
     mla::rmsnorm_rows<T>(pa, B, d.dq, (const T*)h->q_norm_g, d.eps, at<T>(ws, L.cq), h->stream);
     pq = gemm_part<T>(h, at<T>(ws, L.cq), d.dq, (const T*)h->w_qb, d.dq, B, qw, d.dq,
-                      at<float>(ws, L.pq));
+                      at<float>(ws, L.pq), h->t_qb);
   } else if (d.dq) {
     const mla::Part pa = gemm_part<T>(h, x, d.D, (const T*)h->w_qa, d.D, B, d.dq, d.D,
-                                      at<float>(ws, L.pin));
+                                      at<float>(ws, L.pin), h->t_q);
     mla::rmsnorm_rows<T>(pa, B, d.dq, (const T*)h->q_norm_g, d.eps, at<T>(ws, L.cq), h->stream);
     pq = gemm_part<T>(h, at<T>(ws, L.cq), d.dq, (const T*)h->w_qb, d.dq, B, qw, d.dq,
-                      at<float>(ws, L.pq));
+                      at<float>(ws, L.pq), h->t_qb);
   } else {
-    pq = gemm_part<T>(h, x, d.D, (const T*)h->w_q, d.D, B, qw, d.D, at<float>(ws, L.pin));
+    pq = gemm_part<T>(h, x, d.D, (const T*)h->w_q, d.D, B, qw, d.D, at<float>(ws, L.pin),
+                      h->t_q);
   }
   mla::q_finish<T>(pq, B, mt.pos, q_nope, q_rope, tok_stride, d.R, d.scale, d, h->rope,
                    h->stream);
@@ -1428,7 +1468,8 @@ static int run_decode(mla_ctx* h, const T* hidden, int B, int q_len, T* cache, T
     }
   }
   if (!o_done)
-    gemm_out<T>(h, o, ko, 0, (const T*)h->w_o, ko, 0, B, d.D, ko, 1, out_t<T>(out, d.D), scratch);
+    gemm_out<T>(h, o, ko, 0, (const T*)h->w_o, ko, 0, B, d.D, ko, 1, out_t<T>(out, d.D), scratch,
+                h->t_o);
   return check_launch(h, "decode");
 }
 
@@ -1721,22 +1762,24 @@ static int run_prefill(mla_ctx* h, const T* hidden, int ntok, int B, const int32
   const T* qin = hidden;
   int qk = d.D;
   const T* wq = (const T*)h->w_q;
+  const void* wqt = h->t_q;  // its tiled copy
   if (d.dq) {
     const mla::Part pa = gemm_part<T>(h, hidden, d.D, (const T*)h->w_qa, d.D, ntok, d.dq, d.D,
-                                      at<float>(ws, L.pin));
+                                      at<float>(ws, L.pin), h->t_q);
     mla::rmsnorm_rows<T>(pa, ntok, d.dq, (const T*)h->q_norm_g, d.eps, at<T>(ws, L.cq),
                          h->stream);
     qin = at<T>(ws, L.cq);
     qk = d.dq;
     wq = (const T*)h->w_qb;
+    wqt = h->t_qb;
   }
   if (mfma_attn) {
     // the projection writes the bf16 query rows (T, H, dn + dr) directly; the
     // attention kernel rotates the rope parts as it loads them
-    gemm_out<T>(h, qin, qk, 0, wq, qk, 0, ntok, qw, qk, 1, out_t<T>(q_nope, qw), scratch);
+    gemm_out<T>(h, qin, qk, 0, wq, qk, 0, ntok, qw, qk, 1, out_t<T>(q_nope, qw), scratch, wqt);
   } else {
     const mla::Part pq = gemm_part<T>(h, qin, qk, wq, qk, ntok, qw, qk,
-                                      at<float>(ws, d.dq ? L.pq : L.pin));
+                                      at<float>(ws, d.dq ? L.pq : L.pin), wqt);
     mla::q_finish<T>(pq, ntok, tok_pos, q_nope, q_rope, (int64_t)d.H * d.dr, d.dr, 1.f, d,
                      h->rope, h->stream);
   }
@@ -1758,7 +1801,7 @@ static int run_prefill(mla_ctx* h, const T* hidden, int ntok, int B, const int32
       const mla::GemmOut go = mfma_attn ? out_t<T>(at<T>(ws, L.kv) + o0, wkv)
                                         : out_f32(at<float>(ws, L.kv) + o0, wkv);
       gemm_out<T>(h, cache + seq_off[b] * d.R, d.R, 0, (const T*)h->w_kvb, d.dc, 0, (int)rows,
-                  wkv, d.dc, 1, go, scratch);
+                  wkv, d.dc, 1, go, scratch, h->t_kvb);
     }
     b = e;
   }
@@ -1776,7 +1819,7 @@ static int run_prefill(mla_ctx* h, const T* hidden, int ntok, int B, const int32
                                  kv_off, seq_off_d, ntok, o, d, h->stream);
   if (ts >= 0) HIP_TRY(h, hipEventRecord(h->tev[2 * ts + 1], h->stream));
   gemm_out<T>(h, o, (int64_t)d.H * d.dv, 0, (const T*)h->w_o, (int64_t)d.H * d.dv, 0, ntok, d.D,
-              d.H * d.dv, 1, out_t<T>(out, d.D), scratch);
+              d.H * d.dv, 1, out_t<T>(out, d.D), scratch, h->t_o);
   return check_launch(h, "prefill");
 }
 
