@@ -50,6 +50,7 @@ constexpr float kRescale = 8.0f;             // lazy-rescale threshold, log2 uni
 constexpr int kXcds = 8;
 static_assert(NLOAD % LOADERS == 0 && LOADERS == 4 && LOADERS <= NW,
               "tile loads split evenly over 4 waves");
+static_assert(NW * QW * (DV * 2 + 16) <= NST * ST_BYTES, "output tiles fit in the ring");
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x8_t __attribute__((ext_vector_type(8)));
@@ -150,7 +151,7 @@ __global__ void __launch_bounds__(NW * 64, 1)
 prefill_attn_mfma_k(const bf16* __restrict__ q, const bf16* __restrict__ kv,
                     const bf16* __restrict__ cache,
                     const PrefillTile* tiles, int ntiles, int H, float qk_scale,
-                    bf16* __restrict__ o_out, RopeTab rt) {
+                    bf16* __restrict__ o_out, int o_tiled, RopeTab rt) {
   __shared__ __attribute__((aligned(1024))) char lds[NST * ST_BYTES];
   // Block -> (tile, head): every block of head h runs on XCD h % 8, so the
   // tiles of one head share that XCD's L2 for their keys and values.
@@ -351,18 +352,39 @@ prefill_attn_mfma_k(const bf16* __restrict__ q, const bf16* __restrict__ kv,
       o[8][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[nb], ones, o[8][nb], 0, 0, 0);
   }
 
+  // epilogue through LDS: every wave is done with the ring, which now holds
+  // each wave's normalised 32 x 128 output tile (rows padded to 272 bytes so
+  // the four rows a store instruction touches fall on different banks); the
+  // tile then leaves in 16-byte chunks of 8 dims, row-major or in the output
+  // projection's fragment-tiled layout
+  __syncthreads();
   if (!wave_active) return;
+  constexpr int OROW = DV * 2 + 16;
+  char* ot = lds + wave * (QW * OROW);
 #pragma unroll
   for (int nb = 0; nb < NQB; ++nb) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int qi = qw0 + 16 * nb + 4 * lg + i;
-      if (qi >= nq) continue;
       const float inv = 1.f / o[8][nb][i];  // row sum of query 16 nb + 4 lg + i
-      bf16* dst = o_out + ((int64_t)(t0 + qi) * H + h) * DV + lr;
+      bf16* row = reinterpret_cast<bf16*>(ot + (16 * nb + 4 * lg + i) * OROW) + lr;
 #pragma unroll
-      for (int db = 0; db < 8; ++db) dst[16 * db] = f32_to_bf16(o[db][nb][i] * inv);
+      for (int db = 0; db < 8; ++db) row[16 * db] = f32_to_bf16(o[db][nb][i] * inv);
     }
+  }
+#pragma unroll
+  for (int k = 0; k < QW * DV / 8 / 64; ++k) {
+    const int c = lane + 64 * k, r = c >> 4, c8 = c & 15;
+    const int qi = qw0 + r;
+    if (qi >= nq) continue;
+    const uint4 v = *reinterpret_cast<const uint4*>(ot + r * OROW + 16 * c8);
+    const int64_t t = t0 + qi;
+    bf16* dst;
+    if (o_tiled)  // dims 8 c8 .. of head h: fragment (t / 16, 4 h + c8 / 4), lane slot
+      dst = o_out + ((t >> 4) * (H * DV / 32) + h * (DV / 32) + (c8 >> 2)) * 512 +
+            ((t & 15) + 16 * (c8 & 3)) * 8;
+    else
+      dst = o_out + (t * H + h) * DV + 8 * c8;
+    *reinterpret_cast<uint4*>(dst) = v;
   }
 }
 
@@ -372,10 +394,10 @@ int prefill_tile_queries() { return pf::NW * pf::QW; }
 
 void prefill_attn_mfma(const bf16* q, const bf16* kv, const bf16* cache,
                        const PrefillTile* tiles, int ntiles, int H, float scale, bf16* o,
-                       const RopeTab& rt, hipStream_t st) {
+                       bool o_tiled, const RopeTab& rt, hipStream_t st) {
   const int blocks = ntiles * ((H + pf::kXcds - 1) / pf::kXcds) * pf::kXcds;
   pf::prefill_attn_mfma_k<<<blocks, pf::NW * 64, 0, st>>>(q, kv, cache, tiles, ntiles, H,
-                                                  scale * kLog2e, o, rt);
+                                                  scale * kLog2e, o, o_tiled ? 1 : 0, rt);
 }
 
 }  // namespace mla

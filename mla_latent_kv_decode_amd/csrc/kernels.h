@@ -285,10 +285,12 @@ int prefill_tile_queries();
 // MFMA version: bf16, qk_nope = v_head = 128, qk_rope = 64.  q: (T, H, 192)
 // rows [q_nope | q_rope] (the rope part is rotated by the kernel at each
 // query's position); kv: expanded rows (H x [K_nope | V]) in bf16;
-// o: (T, H, 128); scale: softmax scale.
+// o: (T, H, 128) rows, or with o_tiled the fragment-tiled layout of the
+// (T, H * 128) output-projection operand (tiled_bytes(T, H * 128) bytes);
+// scale: softmax scale.
 void prefill_attn_mfma(const bf16* q, const bf16* kv, const bf16* cache,
                        const PrefillTile* tiles, int ntiles, int H, float scale, bf16* o,
-                       const RopeTab& rt, hipStream_t st);
+                       bool o_tiled, const RopeTab& rt, hipStream_t st);
 // kv: per sequence the expanded rows [K_nope_h | V_h] (fp32, row width H*(dn+dv)),
 // sequence b at row kv_off[b]; q_nope (T,H,dn), q_rope (T,H,dr) already rotated.
 template <typename T>

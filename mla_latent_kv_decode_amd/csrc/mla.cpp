@@ -1720,7 +1720,9 @@ PrefillLayout prefill_layout(const mla_ctx* h, int T, int B, int64_t rows, int m
   L.q_nope = c.take((size_t)T * d.H * (d.dn + d.dr) * e);
   L.q_rope = c.take((size_t)T * d.H * std::max(d.dr, 1) * e);
   L.kv = c.take((size_t)rows * d.H * (d.dn + d.dv) * 4);
-  L.o = c.take((size_t)T * d.H * d.dv * e);
+  // attention output: rows, or the output projection's tiled operand
+  L.o = c.take(std::max((size_t)T * d.H * d.dv * e,
+                        is_f32(h) ? (size_t)0 : mla::tiled_bytes(T, d.H * d.dv)));
   L.keys = c.take(staged ? (size_t)rows * d.R * e : 0);
   L.total = c.off;
   return L;
@@ -1806,20 +1808,29 @@ static int run_prefill(mla_ctx* h, const T* hidden, int ntok, int B, const int32
     b = e;
   }
   T* o = at<T>(ws, L.o);
+  // the attention writes its output straight into the output projection's
+  // tiled operand when that product runs on the large-tile GEMM
+  const bool o_tiled = mfma_attn && h->t_o && big_gemm(h, ntok, d.D, d.H * d.dv, 1);
   const int ts = timing_slot(h);
   if (ts >= 0) HIP_TRY(h, hipEventRecord(h->tev[2 * ts], h->stream));
   if constexpr (sizeof(T) == 2) {
     if (mfma_attn)
       mla::prefill_attn_mfma(q_nope, at<bf16>(ws, L.kv), cache,
                              reinterpret_cast<const mla::PrefillTile*>(meta + L.tiles_off),
-                             ntiles, d.H, d.scale, o, h->rope, h->stream);
+                             ntiles, d.H, d.scale, o, o_tiled, h->rope, h->stream);
   }
   if (!mfma_attn)
     mla::prefill_attn_generic<T>(q_nope, q_rope, at<float>(ws, L.kv), cache, tok_seq, tok_pos,
                                  kv_off, seq_off_d, ntok, o, d, h->stream);
   if (ts >= 0) HIP_TRY(h, hipEventRecord(h->tev[2 * ts + 1], h->stream));
-  gemm_out<T>(h, o, (int64_t)d.H * d.dv, 0, (const T*)h->w_o, (int64_t)d.H * d.dv, 0, ntok, d.D,
-              d.H * d.dv, 1, out_t<T>(out, d.D), scratch, h->t_o);
+  if (o_tiled) {
+    if constexpr (sizeof(T) == 2)
+      mla::gemm_big(o, static_cast<const bf16*>(h->t_o), ntok, d.D, d.H * d.dv,
+                    out_t<T>(out, d.D), h->n_cu, h->stream);
+  } else {
+    gemm_out<T>(h, o, (int64_t)d.H * d.dv, 0, (const T*)h->w_o, (int64_t)d.H * d.dv, 0, ntok,
+                d.D, d.H * d.dv, 1, out_t<T>(out, d.D), scratch, h->t_o);
+  }
   return check_launch(h, "prefill");
 }
 
