@@ -68,6 +68,10 @@ def parse():
                     help="budget of the oracle (CPU baseline) sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager calls, no HIP graph")
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="limit the oracle's BLAS threads (0: as configured)")
+    ap.add_argument("--cpu-only", action="store_true",
+                    help="only time the oracle on the workload's sample (no GPU)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for HBM counter calibration)")
     return ap.parse_args()
@@ -130,6 +134,28 @@ def _cpu_model() -> str:
     return "unknown"
 
 
+def _thread_limit(n: int):
+    """A context limiting the oracle's BLAS pools to n threads (n = 0: none)."""
+    import contextlib
+    if n <= 0:
+        return contextlib.nullcontext()
+    from threadpoolctl import threadpool_limits
+    return threadpool_limits(limits=n)
+
+
+def cpu_only(args):
+    """The oracle's cpu_baseline of a workload by itself, on the host only."""
+    from mla_latent_kv_decode_amd import synth
+    wl = synth.WORKLOADS[args.workload]
+    w = synth.make_weights(wl.dims, wl.weight_std, wl.dtype)
+    with _thread_limit(args.cpu_threads):
+        if wl.kind == "prefill":
+            base = cpu_baseline_prefill(wl, w, args.cpu_seconds)
+        else:
+            base = cpu_baseline(wl, w, synth.lengths(wl), args.cpu_seconds)
+    print(json.dumps({"workload": wl.name, "cpu_baseline": base}), flush=True)
+
+
 def cpu_baseline(wl, w, lens, budget_s: float):
     """The fp64 oracle (as it stands) on a bounded sample of the same workload:
     whole sequences from the start of the batch until the time budget is used.
@@ -139,7 +165,7 @@ def cpu_baseline(wl, w, lens, budget_s: float):
     from mla_latent_kv_decode_amd import synth
     d = wl.dims
     store = None
-    row_bytes = ROW_BYTES
+    row_bytes = d.row * (4 if wl.dtype == "f32" else 2)  # the GPU cache's row
     if wl.kv == "fp8":
         from oracle import fp8 as F8
         store = lambda r: F8.fp8_rows(r, d.kv_lora)  # noqa: E731
@@ -303,7 +329,8 @@ def bench_prefill(args, wl):
                      "traffic": None},
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline_prefill(wl, w, args.cpu_seconds)
+        with _thread_limit(args.cpu_threads):
+            res["cpu_baseline"] = cpu_baseline_prefill(wl, w, args.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 
@@ -313,6 +340,10 @@ def main():
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the sharded "
               "design shards sequences across GPUs and is not run here", file=sys.stderr)
         sys.exit(2)
+
+    if args.cpu_only:
+        cpu_only(args)
+        return
 
     import torch
     from mla_latent_kv_decode_amd import synth
@@ -476,7 +507,8 @@ def main():
                      "traffic": traffic},
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(wl, w, lens, args.cpu_seconds)
+        with _thread_limit(args.cpu_threads):
+            res["cpu_baseline"] = cpu_baseline(wl, w, lens, args.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 
