@@ -1,4 +1,4 @@
-// The decode step's weight-streaming GEMMs (M = batch <= 64 rows) with their
+// The decode step's weight-streaming GEMMs (M = query rows <= 128) with their
 // epilogues applied in place, and the kernel that finishes the projections
 // (latent-row append, query RMSNorm, absorbed query).
 //
@@ -41,8 +41,9 @@ constexpr int ROWB = KC * 2;              // 512 bytes per row piece
 constexpr int W_OFF = 0, A_OFF = NT * ROWB;
 constexpr int NST = 3;                    // stages
 constexpr int kXcds = 8;
+constexpr int kMaxStreamRows = 128;  // rows (query rows of a step) the stream GEMMs take
 // MR activation rows per block (16: 24 KB stages, two blocks per compute
-// unit; 32: 32 KB stages, one block).  A block copies (NT + MR) rows over all
+// unit; 32: 32 KB stages, 64: 48 KB stages, one block).  A block copies (NT + MR) rows over all
 // of K, so the copy volume of a launch is (N / NT) (M / MR) (NT + MR) K 2
 // bytes: taller tiles re-read the weights fewer times.
 template <int MR>
@@ -202,7 +203,7 @@ struct EpiQuery {
   int H, dn, dr, dc;
   float scale;
   RopeTab rt;
-  int32_t pos[64];  // positions of the (at most 64) rows, passed by value
+  int32_t pos[kMaxStreamRows];  // positions of the rows, passed by value
   __device__ void operator()(int r, int c, float v0, float v1) const {
     if (c < R) {
       *reinterpret_cast<float2*>(a + (int64_t)r * R + c) = make_float2(v0, v1);
@@ -239,15 +240,21 @@ int device_cu_count() {
 
 namespace skn {
 
-// 32-row blocks (one per compute unit) where they still occupy three quarters
-// of the compute units: fewer weight re-reads; else 16-row blocks (two per
-// compute unit).
+// The tallest row blocks (64 or 32 rows: one block per compute unit; 16 rows:
+// two) whose grid still occupies three quarters of the compute units: taller
+// blocks re-read the weights fewer times.
 template <class Epi>
 void launch_stream(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int M, int N, int K,
                    const Epi& epi, hipStream_t st, HostCopy hc = HostCopy{}) {
   const int ntiles = (N + NT - 1) / NT;
   const int nt8 = (ntiles + kXcds - 1) / kXcds * kXcds;
-  const int m32 = (M + 31) / 32;
+  const int m64 = (M + 63) / 64, m32 = (M + 31) / 32;
+  if (M > 32 && ntiles * m64 * 4 >= device_cu_count() * 3) {
+    hc.first_block = nt8 * m64;
+    gemm_stream_k<64, Epi><<<nt8 * m64 + (hc.n16 > 0 ? hc.blocks : 0), NWV * 64, 0, st>>>(
+        A, lda, W, ldw, M, N, K, m64, epi, hc);
+    return;
+  }
   if (M > 16 && ntiles * m32 * 4 >= device_cu_count() * 3) {
     hc.first_block = nt8 * m32;
     gemm_stream_k<32, Epi><<<nt8 * m32 + (hc.n16 > 0 ? hc.blocks : 0), NWV * 64, 0, st>>>(
@@ -265,7 +272,8 @@ void launch_stream(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int M
 //
 // Absorbed query ("Multi-Head Latent Attention" post, section 3.3): for head h
 // q_cat[t][h][c] = scale * sum_k q_nope[t][h][k] W_ukT[h][c][k] (c < 512,
-// K = dn), one block per (head, 128 columns), wave w on 32 of them.
+// K = dn), one block per (64-row group, head, 128 columns), wave w on 32 of
+// them.
 template <int MT>
 __global__ void __launch_bounds__(256)
 finish_k(const bf16* __restrict__ q_nope, const bf16* __restrict__ w_ukT,
@@ -303,7 +311,9 @@ finish_k(const bf16* __restrict__ q_nope, const bf16* __restrict__ w_ukT,
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int lr = lane & 15, lg = lane >> 4;
-  const int h = blk >> 2, c0 = (blk & 3) * 128 + 32 * wave;
+  // block = (64-row group, head, 128 columns)
+  const int r0 = 64 * (blk / (d.H * 4)), hb = blk % (d.H * 4);
+  const int h = hb >> 2, c0 = (hb & 3) * 128 + 32 * wave;
   const int nks = d.dn / 32;
   f32x4_t acc[MT][2];
 #pragma unroll
@@ -320,7 +330,7 @@ finish_k(const bf16* __restrict__ q_nope, const bf16* __restrict__ w_ukT,
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
         fa[u][mt] = *reinterpret_cast<const bf16x8_t*>(
-            q_nope + ((int64_t)min(16 * mt + lr, B - 1) * d.H + h) * d.dn + 32 * ks + 8 * lg);
+            q_nope + ((int64_t)min(r0 + 16 * mt + lr, B - 1) * d.H + h) * d.dn + 32 * ks + 8 * lg);
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
         fw[u][nb] = *reinterpret_cast<const bf16x8_t*>(wb + (int64_t)16 * nb * d.dn + 32 * ks);
@@ -341,7 +351,7 @@ finish_k(const bf16* __restrict__ q_nope, const bf16* __restrict__ w_ukT,
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int t = 16 * mt + 4 * lg + i;
+        const int t = r0 + 16 * mt + 4 * lg + i;
         if (t < B)
           q_cat[((int64_t)t * d.H + h) * d.R + c0 + 16 * nb + lr] = f32_to_bf16(d.scale * acc[mt][nb][i]);
       }
@@ -349,7 +359,9 @@ finish_k(const bf16* __restrict__ q_nope, const bf16* __restrict__ w_ukT,
 
 }  // namespace skn
 
-bool skinny_ok(int M, int N, int K) { return M >= 1 && M <= 64 && N >= 2 && N % 2 == 0 && K % skn::KC == 0; }
+bool skinny_ok(int M, int N, int K) {
+  return M >= 1 && M <= skn::kMaxStreamRows && N >= 2 && N % 2 == 0 && K % skn::KC == 0;
+}
 
 void skinny_store(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int M, int N, int K,
                   bf16* out, int64_t ldo, float alpha, hipStream_t st) {
@@ -371,7 +383,7 @@ void skinny_query(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int M,
   e.R = R;
   e.q_nope = q_nope;
   e.q_cat = q_cat;
-  for (int i = 0; i < 64; ++i) e.pos[i] = i < M ? pos_host[i] : 0;
+  for (int i = 0; i < skn::kMaxStreamRows; ++i) e.pos[i] = i < M ? pos_host[i] : 0;
   e.H = d.H;
   e.dn = d.dn;
   e.dr = d.dr;
@@ -385,7 +397,9 @@ void decode_finish(const bf16* q_nope, const bf16* w_ukT, bf16* q_cat, int B, bo
                    bool append, bool qnorm, const float* a, int lda, int qa_col, const int32_t* pos,
                    const int64_t* slot, const bf16* kv_gamma, void* cache, const bf16* q_gamma,
                    bf16* cq, const Dims& d, const RopeTab& rt, hipStream_t st, bool kv8) {
-  const int nab = absorb ? d.H * 4 : 0, nap = append ? B : 0, nqn = qnorm ? B : 0;
+  // the absorbed query in groups of up to 64 rows
+  const int nab = absorb ? d.H * 4 * ((B + 63) / 64) : 0, nap = append ? B : 0,
+            nqn = qnorm ? B : 0;
   const int blocks = nab + nap + nqn;
   if (blocks == 0) return;
 #define MLA_FIN(MT)                                                                          \

@@ -164,7 +164,7 @@ template <typename T>
 void cache_write(const T* rows, const int64_t* slot, int ntok, int R, T* cache, hipStream_t st);
 
 // ---- decode-step GEMMs with in-place epilogues (no split over blocks):
-// C = A W^T for M <= 64 rows and K % 512 == 0 (skinny_ok), bf16 operands.
+// C = A W^T for M <= 128 rows and K % 256 == 0 (skinny_ok), bf16 operands.
 bool skinny_ok(int M, int N, int K);
 // compute units of the current device (cached per device)
 int device_cu_count();

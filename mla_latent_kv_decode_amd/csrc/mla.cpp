@@ -1335,7 +1335,7 @@ static void run_q_and_append(mla_ctx* h, const T* x, int B, void* ws, const Deco
 }
 
 // A2-A4 through the decode-step GEMMs with in-place epilogues (bf16 MFMA
-// layers, B <= 64): the first projection leaves the kv_a columns (and q_a) in
+// layers, B <= 128 query rows): the first projection leaves the kv_a columns (and q_a) in
 // fp32 and finishes the query heads itself; one more launch appends the latent
 // rows, normalises q_a and / or forms the absorbed query.
 static bool q_skinny_fits(const mla_ctx* h, int B, const DecodeLayout& L) {
