@@ -437,7 +437,7 @@ int64_t paged_row(const PageArgs& pg, int b, int64_t t) {
 // restart, query load, wave merge and partial write), so spans are balanced
 // on rows + kSegRows * segments: the smallest per-part budget for which a
 // greedy left-to-right fill needs no more than the available parts is found by
-// bisection.  Cuts inside a sequence fall on 16-row sub-tile boundaries.
+// bisection.  Cuts inside a sequence fall on 32-row tile boundaries (kCutAlign).
 constexpr int64_t kSegRows = MLA_SEG_ROWS;
 constexpr int64_t kCutAlign = 32;  // rows per tile of the MFMA cores
 
