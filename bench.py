@@ -366,7 +366,7 @@ def main():
 
     # ---- set-up (untimed): weights, caches filled by append
     w = synth.make_weights(d, wl.weight_std, wl.dtype)
-    layer = MLALayer(d, wl.dtype, kv=wl.kv)
+    layer = MLALayer(d, wl.dtype, kv=wl.kv, absorb=wl.absorb)
     layer.absorb_weights({k: torch.from_numpy(v).cuda().to(tdt) for k, v in w.items()})
     lens = synth.lengths(wl)
     q = wl.q_len  # new tokens per sequence and step
@@ -463,6 +463,13 @@ def main():
     core_ms = float(np.mean(core))
     cache_bytes = float(int(seq_len.sum()) * row_bytes)
     weight_bytes = 2.0 * sum(v.size for v in w.values())
+    if wl.absorb == "materialized":
+        # the decode step reads W_kva, [W_qa,] per head [W^KQ_h ; W_q,rope_h] and W^OV
+        # (and the norms) in place of the factored query, W_kv_b and W_o weights
+        kq = d.q_lora or d.hidden
+        weight_bytes = 2.0 * (d.row * d.hidden + d.q_lora * d.hidden
+                              + d.n_heads * (d.kv_lora + d.qk_rope) * kq
+                              + d.hidden * d.n_heads * d.kv_lora + d.kv_lora + d.q_lora)
     act_bytes = 2.0 * 2 * B * q * d.hidden + B * q * row_bytes  # hidden in, y out, new rows
     gbs = cache_bytes / t_step / 1e9
     core_gbs = cache_bytes / (core_ms * 1e-3) / 1e9

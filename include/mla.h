@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 7
+#define MLA_ABI_VERSION 8
 
 typedef enum mla_status {
   MLA_OK = 0,
@@ -82,6 +82,21 @@ typedef enum mla_dtype { MLA_BF16 = 0, MLA_F32 = 1 } mla_dtype;
  * 512, qk_rope 64 and n_heads a multiple of 16; it serves append, decode and
  * prefill (which decodes the key rows it reads to bf16, c_i rounded once). */
 typedef enum mla_kv_storage { MLA_KV_DTYPE = 0, MLA_KV_FP8_E4M3 = 1 } mla_kv_storage;
+
+/* How decode applies the absorbed weights ("Multi-Head Latent Attention"
+ * post, section 3.5; "Deepseek V2 Lite Inference Engine in C", MLA notes,
+ * variant 2 against variant 3).  MLA_ABSORB_FACTORED: the query path keeps
+ * W_q (or W_qb) and W_UK apart (q_abs_h = W_UK_h^T (W_q x)_h) and the output
+ * keeps W_UV and W_o apart (y = W_o [W_UV_h o_lat_h]_h).
+ * MLA_ABSORB_MATERIALIZED: mla_absorb_weights also forms W^KQ_h = W_UK_h^T
+ * W_q,nope_h (d_c x D, or d_c x q_lora) and W^OV_h = W_o,h W_UV_h (D x d_c)
+ * once, so the decode step reads q_abs_h = W^KQ_h x straight from the
+ * projection and y = sum_h W^OV_h o_lat_h from one product over the latent
+ * sums: fewer launches, more weight bytes (V2-Lite: 71 MB against 21 MB per
+ * step).  Materialised weights are used by the fused decode path (bf16
+ * layers, kv_lora 512, up to 128 query rows); larger batches and prefill use
+ * the factored weights, which the handle keeps as well. */
+typedef enum mla_absorb { MLA_ABSORB_FACTORED = 0, MLA_ABSORB_MATERIALIZED = 1 } mla_absorb;
 
 /* Layer dimensions (MLA post, section 3.2 constructor; section 3.6 widths).
  * qk_rope must be even (RoPE rotates pairs; MLA post section 3.7).  q_lora = 0
@@ -119,6 +134,7 @@ typedef struct mla_config {
   float yarn_beta_fast;   /* e.g. 32 */
   float yarn_beta_slow;   /* e.g. 1; 0 < slow < fast */
   float yarn_mscale;      /* e.g. 0.707 (V2-Lite) or 1 (V3); >= 0 */
+  int32_t absorb;         /* mla_absorb: how the decode path applies the absorbed weights */
 } mla_config;
 
 typedef struct mla_ctx* mla_handle;
@@ -127,9 +143,10 @@ typedef struct mla_ctx* mla_handle;
  * a dimension <= 0 other than qk_rope/q_lora, a negative one, unknown dtype,
  * non-finite or non-positive base/eps, unknown kv_storage, rope_scale > 1 with
  * rope_orig_max < 1, not 0 < yarn_beta_slow < yarn_beta_fast or a negative or
- * non-finite yarn_mscale) or MLA_ERR_SHAPE
- * (odd qk_rope, qk_rope > 128, kv_lora > 1024, v_head > 256, FP8 rows for a
- * layer outside the FP8 shapes).  Makes no HIP call; mla_create runs it
+ * non-finite yarn_mscale, unknown absorb) or MLA_ERR_SHAPE (odd qk_rope,
+ * qk_rope > 128, kv_lora > 1024, v_head > 256, FP8 rows for a layer outside
+ * the FP8 shapes, materialised absorption outside bf16 layers with kv_lora
+ * 512).  Makes no HIP call; mla_create runs it
  * first. */
 int mla_config_check(const mla_config* cfg);
 

@@ -192,9 +192,11 @@ struct EpiF32 {
 };
 
 // Columns [0, R) go to `a` (fp32, row stride R); the rest are query heads of
-// dn + dr columns: the nope part to q_nope (T, H, dn), the rope part rotated at
-// the row's position ("Multi-Head Latent Attention" post, section 3.7: RoPE
-// per head on the decoupled query part) and scaled into q_cat[t][h][dc + i].
+// dn + dr columns: the first dn to q_nope (T, H, dn) or, with q_nope null
+// (materialised absorption: these columns already are W^KQ_h x, dn = dc),
+// scaled into q_cat[t][h][0 .. dc); the rope part rotated at the row's
+// position ("Multi-Head Latent Attention" post, section 3.7: RoPE per head on
+// the decoupled query part) and scaled into q_cat[t][h][dc + i].
 struct EpiQuery {
   float* a;
   int R;
@@ -211,7 +213,11 @@ struct EpiQuery {
     }
     const int cc = c - R, w = dn + dr, h = cc / w, j = cc - h * w;
     if (j < dn) {
-      *reinterpret_cast<uint32_t*>(q_nope + ((int64_t)r * H + h) * dn + j) = pack_bf16x2(v0, v1);
+      if (q_nope)
+        *reinterpret_cast<uint32_t*>(q_nope + ((int64_t)r * H + h) * dn + j) = pack_bf16x2(v0, v1);
+      else
+        *reinterpret_cast<uint32_t*>(q_cat + ((int64_t)r * H + h) * (dc + dr) + j) =
+            pack_bf16x2(scale * v0, scale * v1);
       return;
     }
     const int i = j - dn;
@@ -385,7 +391,7 @@ void skinny_query(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int M,
   e.q_cat = q_cat;
   for (int i = 0; i < skn::kMaxStreamRows; ++i) e.pos[i] = i < M ? pos_host[i] : 0;
   e.H = d.H;
-  e.dn = d.dn;
+  e.dn = q_nope ? d.dn : d.dc;
   e.dr = d.dr;
   e.dc = d.dc;
   e.scale = d.scale;

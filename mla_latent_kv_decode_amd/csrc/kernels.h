@@ -177,7 +177,9 @@ void skinny_f32(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int M, i
 // columns [0, R) of C to a (fp32, row stride R); the remaining columns are
 // query heads [nope (dn) | rope (dr)]: nope to q_nope (M, H, dn), rope rotated
 // at pos_host[row] (a host array, passed to the kernel by value) and scaled by
-// d.scale into q_cat[row][h][dc ..] (row stride H R)
+// d.scale into q_cat[row][h][dc ..] (row stride H R).  With q_nope null the
+// heads are [q_abs (dc) | rope (dr)] (materialised W^KQ rows) and q_abs goes
+// scaled into q_cat[row][h][0 .. dc).
 void skinny_query(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int M, int N, int K,
                   float* a, int R, bf16* q_nope, bf16* q_cat, const int32_t* pos_host,
                   const Dims& d, const RopeTab& rt, hipStream_t st,

@@ -83,6 +83,13 @@ struct mla_ctx {
   void* t_kvb = nullptr;
   void* t_o = nullptr;
   int n_in = 0;           // rows of w_in
+  // materialised absorption (mla_config.absorb): per head [W^KQ_h ; W_q,rope_h]
+  // query rows (behind the W_kva rows without a query LoRA, as w_in), and
+  // W^OV (D, H * dc)
+  bool mat = false;
+  void* m_in = nullptr;   // [W_kva ; per head (W^KQ_h ; W_q,rope_h)] (no query LoRA)
+  void* m_qb = nullptr;   // per head (W^KQ_h ; W_qb,rope_h) (query LoRA)
+  void* m_ov = nullptr;
   Staging ring[kRing];
   int ring_next = 0;
   std::vector<void*> captured;  // pinned staging owned by captured graphs
@@ -690,12 +697,17 @@ int mla_config_check(const mla_config* c) {
   if (c->qk_rope > 2 * mla::kMaxRopePairs) return MLA_ERR_SHAPE;
   if (c->kv_storage != MLA_KV_DTYPE && c->kv_storage != MLA_KV_FP8_E4M3)
     return MLA_ERR_INVALID_ARG;
+  if (c->absorb != MLA_ABSORB_FACTORED && c->absorb != MLA_ABSORB_MATERIALIZED)
+    return MLA_ERR_INVALID_ARG;
   if (!isfinite(c->rope_scale)) return MLA_ERR_INVALID_ARG;
   if (c->rope_scale > 1.f &&
       (c->rope_orig_max < 1 || !isfinite(c->yarn_beta_fast) || !isfinite(c->yarn_beta_slow) ||
        !(c->yarn_beta_slow > 0.f) || !(c->yarn_beta_fast > c->yarn_beta_slow) ||
        !isfinite(c->yarn_mscale) || !(c->yarn_mscale >= 0.f)))
     return MLA_ERR_INVALID_ARG;
+  // materialised weights are read by the fused decode path of bf16 MFMA layers
+  if (c->absorb == MLA_ABSORB_MATERIALIZED && (c->dtype != MLA_BF16 || c->kv_lora != 512))
+    return MLA_ERR_SHAPE;
   if (c->kv_storage == MLA_KV_FP8_E4M3) {
     // the FP8 rows are read by the 16-head-group MFMA core only
     if (c->dtype != MLA_BF16 || c->kv_lora != 512 || c->qk_rope != 64 || c->n_heads % 16)
@@ -956,6 +968,7 @@ int mla_create(const mla_config* cfg, void* stream, mla_handle* out) {
   h->mfma = cfg->dtype == MLA_BF16 && d.dc == 512 && d.dr == 64 && d.H % 16 == 0;
   h->kv8 = cfg->kv_storage == MLA_KV_FP8_E4M3;
   h->n_in = d.R + (d.dq ? d.dq : qw_of(d));
+  h->mat = cfg->absorb == MLA_ABSORB_MATERIALIZED;
   h->dims_aligned = d.D % 8 == 0 && d.dc % 8 == 0 && d.R % 8 == 0 && d.dq % 8 == 0 &&
                     qw_of(d) % 8 == 0 && (d.H * d.dv) % 8 == 0 &&
                     (d.H * (d.dn + d.dv)) % 8 == 0;
@@ -978,7 +991,8 @@ int mla_create(const mla_config* cfg, void* stream, mla_handle* out) {
 static void free_weights(mla_ctx* h) {
   void** ws[] = {&h->w_q,  &h->w_qa, &h->q_norm_g, &h->w_qb,  &h->w_kva, &h->kv_norm_g,
                  &h->w_kvb, &h->w_ukT, &h->w_uv,   &h->w_o,   &h->w_in,  &h->t_in,
-                 &h->t_q,   &h->t_qb,  &h->t_kva,  &h->t_kvb, &h->t_o};
+                 &h->t_q,   &h->t_qb,  &h->t_kva,  &h->t_kvb, &h->t_o,   &h->m_in,
+                 &h->m_qb,  &h->m_ov};
   for (void** p : ws) {
     if (*p) (void)hipFree(*p);
     *p = nullptr;
@@ -1047,6 +1061,67 @@ int mla_set_stream(mla_handle h, void* stream) {
   return MLA_OK;
 }
 
+// Materialised absorption ("Multi-Head Latent Attention" post, section 3.5):
+// per head W^KQ_h = W_UK_h^T W_q,nope_h (dc x K, K = D or q_lora) stacked with
+// the head's rope rows of W_q (or W_qb), and W^OV_h = W_o,h W_UV_h (D x dc),
+// formed once on the device in fp32 and stored in bf16.  Runs after the
+// factored copies exist (w_ukT, w_uv, w_o, w_q / w_qb, w_kva).
+static int materialize(mla_ctx* h) {
+  const Dims& d = h->d;
+  const int K = d.dq ? d.dq : d.D, qrow = d.dc + d.dr;
+  const bf16* wq = static_cast<const bf16*>(d.dq ? h->w_qb : h->w_q);  // (H (dn + dr), K)
+  void* wqT = nullptr;
+  void* wuvT = nullptr;
+  void* scr = nullptr;
+  auto done = [&](int rc) {
+    (void)hipStreamSynchronize(h->stream);
+    for (void* p : {wqT, wuvT, scr})
+      if (p) (void)hipFree(p);
+    return rc;
+  };
+  const size_t sf = std::max(out_scratch(h, d.dc, K, d.dn, d.H), out_scratch(h, d.D, d.dc, d.dv, d.H));
+  if (hipMalloc(&wqT, (size_t)d.H * K * d.dn * 2) != hipSuccess ||
+      hipMalloc(&wuvT, (size_t)d.H * d.dc * d.dv * 2) != hipSuccess ||
+      (sf && hipMalloc(&scr, sf * 4) != hipSuccess))
+    return done(fail(h, MLA_ERR_HIP, "materialised absorption: out of device memory"));
+  bf16* qdst;
+  if (!d.dq) {
+    if (hipMalloc(&h->m_in, ((size_t)d.R + (size_t)d.H * qrow) * d.D * 2) != hipSuccess)
+      return done(fail(h, MLA_ERR_HIP, "materialised absorption: out of device memory"));
+    if (hipMemcpyAsync(h->m_in, h->w_kva, (size_t)d.R * d.D * 2, hipMemcpyDeviceToDevice,
+                       h->stream) != hipSuccess)
+      return done(fail(h, MLA_ERR_HIP, "materialised absorption: copy"));
+    qdst = static_cast<bf16*>(h->m_in) + (size_t)d.R * d.D;
+  } else {
+    if (hipMalloc(&h->m_qb, (size_t)d.H * qrow * d.dq * 2) != hipSuccess)
+      return done(fail(h, MLA_ERR_HIP, "materialised absorption: out of device memory"));
+    qdst = static_cast<bf16*>(h->m_qb);
+  }
+  // W_q,nope_h^T (H, K, dn), then W^KQ_h = W_UK_h^T (dc x dn) . (W_q,nope_h^T)^T
+  mla::transpose_heads<bf16>(wq, static_cast<bf16*>(wqT), d.H, d.dn, K, (int64_t)(d.dn + d.dr) * K,
+                             h->stream);
+  gemm_out<bf16>(h, static_cast<const bf16*>(h->w_ukT), d.dn, (int64_t)d.dc * d.dn,
+                 static_cast<const bf16*>(wqT), d.dn, (int64_t)K * d.dn, d.dc, K, d.dn, d.H,
+                 out_t<bf16>(qdst, K, (int64_t)qrow * K), static_cast<float*>(scr));
+  // the head's rope rows follow its W^KQ rows
+  if (d.dr &&
+      hipMemcpy2DAsync(qdst + (size_t)d.dc * K, (size_t)qrow * K * 2, wq + (size_t)d.dn * K,
+                       (size_t)(d.dn + d.dr) * K * 2, (size_t)d.dr * K * 2, d.H,
+                       hipMemcpyDeviceToDevice, h->stream) != hipSuccess)
+    return done(fail(h, MLA_ERR_HIP, "materialised absorption: copy"));
+  // W_UV_h^T (H, dc, dv), then W^OV_h = W_o,h (D x dv) . (W_UV_h^T)^T into
+  // columns h dc .. of (D, H dc)
+  mla::transpose_heads<bf16>(static_cast<const bf16*>(h->w_uv), static_cast<bf16*>(wuvT), d.H,
+                             d.dv, d.dc, (int64_t)d.dv * d.dc, h->stream);
+  if (hipMalloc(&h->m_ov, (size_t)d.D * d.H * d.dc * 2) != hipSuccess)
+    return done(fail(h, MLA_ERR_HIP, "materialised absorption: out of device memory"));
+  gemm_out<bf16>(h, static_cast<const bf16*>(h->w_o), (int64_t)d.H * d.dv, d.dv,
+                 static_cast<const bf16*>(wuvT), d.dv, (int64_t)d.dc * d.dv, d.D, d.dc, d.dv,
+                 d.H, out_t<bf16>(static_cast<bf16*>(h->m_ov), (int64_t)d.H * d.dc, d.dc),
+                 static_cast<float*>(scr));
+  return done(check_launch(h, "materialised absorption"));
+}
+
 int mla_absorb_weights(mla_handle h, const void* w_q, const void* w_qa, const void* q_norm_g,
                        const void* w_qb, const void* w_kva, const void* kv_norm_g,
                        const void* w_kvb, const void* w_o) {
@@ -1105,6 +1180,7 @@ int mla_absorb_weights(mla_handle h, const void* w_q, const void* w_qa, const vo
     mla::transpose_heads<bf16>((const bf16*)w_kvb, (bf16*)h->w_ukT, d.H, d.dn, d.dc,
                                (int64_t)(d.dn + d.dv) * d.dc, h->stream);
   if ((rc = check_launch(h, "transpose_heads"))) return rc;
+  if (h->mat && !is_f32(h) && (rc = materialize(h))) return rc;
   // tiled copies for the large-tile GEMM (prefill, bulk appends, wide steps)
   if (!is_f32(h) && h->dims_aligned) {
     auto tile = [&](void** dst, const void* src, int rows, int K) -> int {
@@ -1354,11 +1430,18 @@ static void q_skinny_first(mla_ctx* h, const bf16* x, int B, void* ws, const Dec
   const int n1 = L.step ? h->n_in : (d.dq ? d.dq : qw);
   float* a = at<float>(ws, L.pin);  // fp32 rows of the first GEMM's non-query columns
   const bf16* w1 = (const bf16*)(L.step ? h->w_in : (d.dq ? h->w_qa : h->w_q));
-  if (!d.dq)
+  if (!d.dq && h->mat) {
+    // materialised: [W_kva ;] per head [W^KQ_h ; W_q,rope_h] straight into q_cat
+    const int nq = d.H * (d.dc + d.dr);
+    const bf16* wm = static_cast<const bf16*>(h->m_in) + (L.step ? 0 : (size_t)d.R * d.D);
+    mla::skinny_query(x, d.D, wm, d.D, B, (L.step ? d.R : 0) + nq, d.D, a, L.step ? d.R : 0,
+                      nullptr, at<bf16>(ws, L.q_cat), pos_host, d, h->rope, h->stream, hc);
+  } else if (!d.dq) {
     mla::skinny_query(x, d.D, w1, d.D, B, n1, d.D, a, L.step ? d.R : 0, at<bf16>(ws, L.q_nope),
                       at<bf16>(ws, L.q_cat), pos_host, d, h->rope, h->stream, hc);
-  else
+  } else {
     mla::skinny_f32(x, d.D, w1, d.D, B, n1, d.D, a, n1, h->stream, hc);
+  }
 }
 
 static void q_skinny_rest(mla_ctx* h, int B, void* ws, const DecodeLayout& L,
@@ -1374,13 +1457,19 @@ static void q_skinny_rest(mla_ctx* h, int B, void* ws, const DecodeLayout& L,
   const bf16* kv_g = (const bf16*)h->kv_norm_g;
   const int R = L.step ? d.R : 0;  // kv_a columns in front of the query columns
   if (!d.dq) {
-    mla::decode_finish(q_nope, w_ukT, q_cat, B, true, L.step, false, a, R, 0, mt.pos, slot_dev,
-                       kv_g, cache, nullptr, nullptr, d, h->rope, h->stream, h->kv8);
+    // (materialised: the projection already formed q_abs; only the append)
+    mla::decode_finish(q_nope, w_ukT, q_cat, B, !h->mat, L.step, false, a, R, 0, mt.pos,
+                       slot_dev, kv_g, cache, nullptr, nullptr, d, h->rope, h->stream, h->kv8);
     return;
   }
   bf16* cq = at<bf16>(ws, L.cq);
   mla::decode_finish(q_nope, w_ukT, q_cat, B, false, L.step, true, a, n1, R, mt.pos, slot_dev,
                      kv_g, cache, (const bf16*)h->q_norm_g, cq, d, h->rope, h->stream, h->kv8);
+  if (h->mat) {
+    mla::skinny_query(cq, d.dq, (const bf16*)h->m_qb, d.dq, B, d.H * (d.dc + d.dr), d.dq,
+                      nullptr, 0, nullptr, q_cat, pos_host, d, h->rope, h->stream);
+    return;
+  }
   mla::skinny_query(cq, d.dq, (const bf16*)h->w_qb, d.dq, B, qw, d.dq, nullptr, 0, q_nope, q_cat,
                     pos_host, d, h->rope, h->stream);
   mla::decode_finish(q_nope, w_ukT, q_cat, B, true, false, false, nullptr, 0, 0, mt.pos,
@@ -1439,6 +1528,15 @@ static int run_decode(mla_ctx* h, const T* hidden, int B, int q_len, T* cache, T
   T* o = at<T>(ws, L.o);
   bool uv_done = false;
   if constexpr (sizeof(T) == 2) {
+    if (fast && h->mat && mfma_core && mla::skinny_ok(B, d.D, d.H * d.dc)) {
+      // materialised: merged latent sums, then y = W^OV [o_lat_h]_h in one product
+      mla::decode_combine_512(acc, ml, mc, B, d.H, max_chunks, at<float>(ws, L.cacc),
+                              at<float>(ws, L.cml), ring_core(h), (bf16*)o_lat, h->stream);
+      mla::skinny_store((const bf16*)o_lat, (int64_t)d.H * d.dc, (const bf16*)h->m_ov,
+                        (int64_t)d.H * d.dc, B, d.D, d.H * d.dc, (bf16*)out, d.D, 1.f,
+                        h->stream);
+      return check_launch(h, "decode");
+    }
     if (combine_uv(h)) {
       // A6 + A7: combine the partials of each sequence (fixed slot order) and
       // apply W_UV_h to the merged latent sums

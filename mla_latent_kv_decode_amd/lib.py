@@ -27,6 +27,8 @@ MLA_BF16 = 0
 MLA_F32 = 1
 MLA_KV_DTYPE = 0
 MLA_KV_FP8_E4M3 = 1
+MLA_ABSORB_FACTORED = 0
+MLA_ABSORB_MATERIALIZED = 1
 
 _P = ctypes.c_void_p
 _I32P = ctypes.POINTER(ctypes.c_int32)
@@ -42,7 +44,7 @@ class MLAConfig(ctypes.Structure):
                 ("dtype", ctypes.c_int32), ("kv_storage", ctypes.c_int32),
                 ("rope_scale", ctypes.c_float), ("rope_orig_max", ctypes.c_int32),
                 ("yarn_beta_fast", ctypes.c_float), ("yarn_beta_slow", ctypes.c_float),
-                ("yarn_mscale", ctypes.c_float)]
+                ("yarn_mscale", ctypes.c_float), ("absorb", ctypes.c_int32)]
 
 
 class MLADecodeArgs(ctypes.Structure):
@@ -158,8 +160,10 @@ class MLAError(RuntimeError):
         self.status = status
 
 
-def make_config(dims, dtype: str, softmax_scale: float = 0.0, kv: str = "dtype") -> MLAConfig:
-    """kv: "dtype" (cache rows in the layer dtype) or "fp8" (FP8 E4M3 rows)."""
+def make_config(dims, dtype: str, softmax_scale: float = 0.0, kv: str = "dtype",
+                absorb: str = "factored") -> MLAConfig:
+    """kv: "dtype" (cache rows in the layer dtype) or "fp8" (FP8 E4M3 rows);
+    absorb: "factored" or "materialized" (mla_absorb)."""
     return MLAConfig(dims.hidden, dims.n_heads, dims.qk_nope, dims.qk_rope, dims.v_head,
                      dims.kv_lora, dims.q_lora, float(dims.rope_base), float(dims.rms_eps),
                      float(softmax_scale), MLA_BF16 if dtype == "bf16" else MLA_F32,
@@ -168,7 +172,8 @@ def make_config(dims, dtype: str, softmax_scale: float = 0.0, kv: str = "dtype")
                      int(getattr(dims, "rope_orig_max", 4096)),
                      float(getattr(dims, "yarn_beta_fast", 32.0)),
                      float(getattr(dims, "yarn_beta_slow", 1.0)),
-                     float(getattr(dims, "yarn_mscale", 0.0)))
+                     float(getattr(dims, "yarn_mscale", 0.0)),
+                     MLA_ABSORB_MATERIALIZED if absorb == "materialized" else MLA_ABSORB_FACTORED)
 
 
 def _i32(a):
@@ -212,14 +217,15 @@ class MLALayer:
     """One MLA layer bound to a library handle on the current device/stream."""
 
     def __init__(self, dims, dtype: str = "bf16", softmax_scale: float = 0.0, device="cuda",
-                 kv: str = "dtype"):
+                 kv: str = "dtype", absorb: str = "factored"):
         import torch
         self.lib = load()
         self.dims = dims
         self.dtype = dtype
         self.kv = kv
+        self.absorb = absorb
         self.torch_dtype = torch.bfloat16 if dtype == "bf16" else torch.float32
-        self.cfg = make_config(dims, dtype, softmax_scale, kv)
+        self.cfg = make_config(dims, dtype, softmax_scale, kv, absorb)
         self.device = torch.device(device)
         h = ctypes.c_void_p()
         self._check(self.lib.mla_create(ctypes.byref(self.cfg), _stream_ptr(), ctypes.byref(h)),

@@ -77,6 +77,7 @@ class Workload:
     kv: str = "dtype"          # latent cache rows: "dtype" or "fp8" (E4M3 + row scale)
     page_rows: int = 0         # > 0: a paged cache, pages handed out in a seeded random order
     q_len: int = 1             # decode: new tokens per sequence and step
+    absorb: str = "factored"   # decode weights: "factored" or "materialized" (W^KQ, W^OV)
 
 
 WORKLOADS = {
@@ -98,9 +99,17 @@ WORKLOADS = {
     # the same batch decoding two new tokens per sequence and step
     "v2lite_decode_b64_q2": Workload("v2lite_decode_b64_q2", V2_LITE, "bf16", 0.02,
                                      "decode", 64, len_lo=512, len_hi=8192, q_len=2),
+    # the same batch with materialised absorption (W^KQ, W^OV formed once)
+    "v2lite_decode_b64_materialized": Workload("v2lite_decode_b64_materialized", V2_LITE, "bf16",
+                                               0.02, "decode", 64, len_lo=512, len_hi=8192,
+                                               absorb="materialized"),
     # V3 ragged decode, B=32, cached rows ~ U{2048..16384}
     "v3_decode_b32": Workload("v3_decode_b32", V3, "bf16", 0.02, "decode", 32,
                               len_lo=2048, len_hi=16384),
+    # the same batch with materialised absorption
+    "v3_decode_b32_materialized": Workload("v3_decode_b32_materialized", V3, "bf16", 0.02,
+                                           "decode", 32, len_lo=2048, len_hi=16384,
+                                           absorb="materialized"),
     # the same batch on an FP8 latent cache
     "v3_decode_b32_fp8": Workload("v3_decode_b32_fp8", V3, "bf16", 0.02, "decode", 32,
                                   len_lo=2048, len_hi=16384, kv="fp8"),

@@ -43,10 +43,10 @@ def host(t) -> np.ndarray:
     return t.detach().to(torch.float32).cpu().numpy()
 
 
-def make_layer(dims, dtype, weights, kv="dtype"):
+def make_layer(dims, dtype, weights, kv="dtype", absorb="factored"):
     import torch
     from mla_latent_kv_decode_amd.lib import MLALayer
-    layer = MLALayer(dims, dtype, kv=kv)
+    layer = MLALayer(dims, dtype, kv=kv, absorb=absorb)
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     layer.absorb_weights({k: dev(v, tdt) for k, v in weights.items()})
     return layer
@@ -73,14 +73,14 @@ class DecodeCase:
     first: write, then read through the new position)."""
 
     def __init__(self, dims, dtype, std, lens, random_gains=True, keep=None, layer=None,
-                 weights=None, kv="dtype"):
+                 weights=None, kv="dtype", absorb="factored"):
         import torch
         self.dims, self.dtype, self.kv = dims, dtype, kv
         self.lens = np.asarray(lens, dtype=np.int64)
         self.B = len(self.lens)
         self.w = weights if weights is not None else synth.make_weights(
             dims, std, dtype, random_gains=random_gains)
-        self.layer = layer if layer is not None else make_layer(dims, dtype, self.w, kv)
+        self.layer = layer if layer is not None else make_layer(dims, dtype, self.w, kv, absorb)
         self.seq_off, self.seq_len, self.total = synth.decode_layout(self.lens)
         self.cache = self.layer.new_cache(self.total)
         keep = set(range(self.B)) if keep is None else set(keep)

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(mla):
     missing = [n for n in names if not hasattr(mla, n)]
     assert not missing, missing
     assert set(names) == set(L._SIGS), set(names) ^ set(L._SIGS)
-    assert mla.mla_abi_version() == 7
+    assert mla.mla_abi_version() == 8
 
 
 def test_status_strings(mla):
@@ -93,6 +93,19 @@ def test_fp8_cache_config_and_row_bytes(mla):
         assert ok(bad) == L.MLA_ERR_SHAPE
     assert ok(cfg(n_heads=32, kv_storage=1)) == L.MLA_OK
     assert ok(cfg(synth.V3, kv_storage=1)) == L.MLA_OK
+
+
+def test_absorb_config(mla):
+    """Materialised absorption: accepted for bf16 layers with a 512-wide
+    latent (the fused decode path's shapes), refused otherwise; unknown modes
+    are invalid."""
+    ok = lambda c: mla.mla_config_check(ctypes.byref(c))
+    assert ok(cfg(absorb=L.MLA_ABSORB_MATERIALIZED)) == L.MLA_OK
+    assert ok(cfg(synth.V3, absorb=L.MLA_ABSORB_MATERIALIZED)) == L.MLA_OK
+    assert ok(cfg(absorb=2)) == L.MLA_ERR_INVALID_ARG
+    assert ok(cfg(absorb=-1)) == L.MLA_ERR_INVALID_ARG
+    assert ok(cfg(synth.TINY, "f32", absorb=1)) == L.MLA_ERR_SHAPE
+    assert ok(cfg(kv_lora=256, absorb=1)) == L.MLA_ERR_SHAPE
 
 
 def _i32(a):

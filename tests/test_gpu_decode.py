@@ -49,7 +49,8 @@ def full_size_case(workload, kv="dtype"):
     library's append and decoded once (staged) in the launch configuration
     the benchmark times: (case, host outputs)."""
     w = synth.WORKLOADS[workload]
-    case = DecodeCase(w.dims, "bf16", w.weight_std, synth.lengths(w), random_gains=False, kv=kv)
+    case = DecodeCase(w.dims, "bf16", w.weight_std, synth.lengths(w), random_gains=False, kv=kv,
+                      absorb=w.absorb)
     out = _run_host(case, stages=True)
     assert all(np.all(np.isfinite(a)) for a in out)
     return case, out
