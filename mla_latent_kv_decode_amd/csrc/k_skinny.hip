@@ -31,6 +31,7 @@ namespace mla {
 namespace skn {
 
 using ddev::dma16;
+using ddev::dma16_nt;
 using ddev::lds_u32;
 using ddev::wait_vmcnt;
 
@@ -246,6 +247,239 @@ int device_cu_count() {
 
 namespace skn {
 
+// ---- few rows (M <= 32) against large weights: split-K with the activation
+// slice resident in LDS.  The 32-column tiles above re-copy all M x K
+// activations per tile, as many bytes as their weights when M = 32 (V3's W_o:
+// 235 MB of weights, 470 MB of copies).  Here block (slice s, column group g)
+// copies the activations of K slice s once (32 rows x 1024 k = 64 KB, in MFMA
+// fragment order) and each wave streams the fragment-tiled weight blocks of
+// its share (R 16-row blocks; a block's fragments of one slice are 32
+// contiguous KB) through a 3-stage ring of its own in LDS, two batches of
+// 2 R one-KB fragments in flight while one multiplies: each k-step's two
+// activation fragments feed 2 R MFMAs.  All copies are LDS-DMA with explicit
+// waits; the weights are read non-temporally (once), so each weight byte
+// crosses HBM -> CU once.  With one slice the epilogue is applied in place;
+// with more, fp32 partials go to `part` (slice s at s M N) and res_reduce_k
+// sums them in slice order (deterministic).  The product is taken transposed
+// (D = W_frag . A_frag^T), so a lane ends with four adjacent columns of one
+// activation row.
+constexpr int RS_MT = 2;      // 16-row activation blocks (M <= 32)
+constexpr int RS_KS = 1024;   // largest k per slice
+constexpr int RS_KB = 2;      // k-steps per batch
+constexpr int RS_NST = 3;     // ring stages per wave
+constexpr int RS_RMAX = 4;    // weight blocks per wave at most
+constexpr int RS_A_BYTES = RS_MT * (RS_KS / 32) * 1024;              // 64 KB
+constexpr int RS_WST = RS_RMAX * RS_KB * 1024;                       // 8 KB per stage
+constexpr int RS_LDS = RS_A_BYTES + NWV * RS_NST * RS_WST;           // 160 KB
+
+template <int R, class Epi>
+__global__ void __launch_bounds__(256)
+gemm_res_k(const bf16* __restrict__ A, int64_t lda, const bf16* __restrict__ Wt, int M, int N,
+           int K, int KS, int nslice, float* __restrict__ part, Epi epi, HostCopy hc) {
+  static_assert(R <= RS_RMAX, "ring stages hold RS_RMAX weight blocks");
+  constexpr int CPB = R * RS_KB;  // copies per batch and wave
+  __shared__ __attribute__((aligned(1024))) char lds[RS_LDS];
+  const int bid = blockIdx.x;
+  if (hc.n16 > 0 && bid >= hc.first_block) {
+    host_copy(hc, bid - hc.first_block);
+    return;
+  }
+  const int s = bid % nslice, g = bid / nslice;  // slice s on XCD s % 8
+  const int k0 = s * KS, nks = K / 32, sks = min(KS, K - k0) / 32;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const uint32_t lds0 = lds_u32(lds);
+  // the slice's activations: fragment (ks, m) at (ks RS_MT + m) KB, lane l
+  // holding row 16 m + l % 16 (rows past M repeat the last), k = 8 (l / 16)
+  for (int f = wave; f < sks * RS_MT; f += NWV) {
+    const int ks = f / RS_MT, m = f % RS_MT;
+    const int row = min(16 * m + (lane & 15), M - 1);
+    dma16(A + (int64_t)row * lda + k0 + 32 * ks + 8 * (lane >> 4), lds0 + (uint32_t)f * 1024);
+  }
+  // this wave's weight blocks rb0 + 4 r (past the last one the copies repeat
+  // it and nothing is stored), batch b = k-steps 2 b, 2 b + 1 of the slice
+  const int NB = (N + 15) / 16;
+  const int rb0 = g * NWV * R + wave;
+  const char* wsrc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    wsrc[r] = reinterpret_cast<const char*>(Wt) +
+              ((int64_t)min(rb0 + NWV * r, NB - 1) * nks + k0 / 32) * 1024 + lane * 16;
+  const uint32_t ring = lds0 + RS_A_BYTES + (uint32_t)wave * RS_NST * RS_WST;
+  auto issue = [&](int b) {
+    const uint32_t st = ring + (uint32_t)(b % RS_NST) * RS_WST;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int j = 0; j < RS_KB; ++j)
+        dma16_nt(wsrc[r] + (int64_t)(RS_KB * b + j) * 1024, st + (uint32_t)(r * RS_KB + j) * 1024);
+  };
+  const int nb = sks / RS_KB;  // batches per slice (>= 2: K % 256 == 0)
+  issue(0);
+  issue(1);
+  wait_vmcnt<2 * CPB>();  // this wave's activation copies (issued first) are done
+  __syncthreads();        // every wave's activation copies are visible
+  f32x4_t acc[R][RS_MT];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < RS_MT; ++m) acc[r][m] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  const char* al = lds + lane * 16;
+  const char* wl = lds + RS_A_BYTES + wave * RS_NST * RS_WST + lane * 16;
+  for (int b = 0; b < nb; ++b) {
+    // the stage of batch b + 2 held batch b - 1, whose reads ended before
+    // the products of the previous iteration
+    if (b + 2 < nb) issue(b + 2);
+    const int later = min(2, nb - 1 - b);  // batches issued after b
+    if (later == 2) wait_vmcnt<2 * CPB>();
+    else if (later == 1) wait_vmcnt<CPB>();
+    else wait_vmcnt<0>();
+    const char* st = wl + (b % RS_NST) * RS_WST;
+#pragma unroll
+    for (int j = 0; j < RS_KB; ++j) {
+      const int ks = RS_KB * b + j;
+      bf16x8_t a[RS_MT], w[R];
+#pragma unroll
+      for (int m = 0; m < RS_MT; ++m)
+        a[m] = *reinterpret_cast<const bf16x8_t*>(al + (ks * RS_MT + m) * 1024);
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        w[r] = *reinterpret_cast<const bf16x8_t*>(st + (r * RS_KB + j) * 1024);
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < RS_MT; ++m)
+          acc[r][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[r], a[m], acc[r][m], 0, 0, 0);
+    }
+  }
+  // lane: C[row = 16 m + l % 16][col = 16 rb + 4 (l / 16) .. + 3]
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (rb0 + NWV * r >= NB) continue;
+    const int col = 16 * (rb0 + NWV * r) + 4 * (lane >> 4);
+#pragma unroll
+    for (int m = 0; m < RS_MT; ++m) {
+      const int row = 16 * m + (lane & 15);
+      if (row >= M || col >= N) continue;
+      if (nslice == 1) {
+        epi(row, col, acc[r][m][0], acc[r][m][1]);
+        if (col + 2 < N) epi(row, col + 2, acc[r][m][2], acc[r][m][3]);
+      } else {
+        float* dst = part + ((int64_t)s * M + row) * N + col;
+        if (col + 3 < N) {
+          *reinterpret_cast<float4*>(dst) =
+              make_float4(acc[r][m][0], acc[r][m][1], acc[r][m][2], acc[r][m][3]);
+        } else {
+          dst[0] = acc[r][m][0];
+          dst[1] = acc[r][m][1];
+          if (col + 2 < N) {
+            dst[2] = acc[r][m][2];
+            dst[3] = acc[r][m][3];
+          }
+        }
+      }
+    }
+  }
+}
+
+// The partials of gemm_res_k summed, then the epilogue.  A block covers one
+// row and 4 (256 / G) columns: each of G thread groups sums every G-th slice
+// (four adjacent columns per thread, all its loads independent), then the G
+// group sums are added in group order, so the result does not depend on
+// timing.
+template <int G, class Epi>
+__global__ void __launch_bounds__(256)
+res_reduce_k(const float* __restrict__ part, int nslice, int M, int N, Epi epi) {
+  constexpr int QN = 256 / G;  // column quads per block
+  __shared__ float4 red[256];
+  const int g = threadIdx.x / QN, q = threadIdx.x % QN;
+  const int row = blockIdx.y, col = 4 * (blockIdx.x * QN + q);
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (col < N) {
+    const int64_t step = (int64_t)G * M * N;
+    const float* p = part + ((int64_t)g * M + row) * N + col;
+#pragma unroll 4
+    for (int s = g; s < nslice; s += G, p += step) {
+      const float4 x = *reinterpret_cast<const float4*>(p);
+      v.x += x.x;
+      v.y += x.y;
+      v.z += x.z;
+      v.w += x.w;
+    }
+  }
+  red[threadIdx.x] = v;
+  __syncthreads();
+  if (g != 0 || col >= N) return;
+#pragma unroll
+  for (int i = 1; i < G; ++i) {
+    const float4 x = red[i * QN + q];
+    v.x += x.x;
+    v.y += x.y;
+    v.z += x.z;
+    v.w += x.w;
+  }
+  epi(row, col, v.x, v.y);
+  epi(row, col + 2, v.z, v.w);
+}
+
+template <int G, class Epi>
+void launch_reduce(const float* part, int nslice, int M, int N, const Epi& epi, hipStream_t st) {
+  constexpr int QN = 256 / G;
+  res_reduce_k<G, Epi><<<dim3((N / 4 + QN - 1) / QN, M), 256, 0, st>>>(part, nslice, M, N, epi);
+}
+
+// The split: whole K in one slice with the most weight blocks per wave that
+// still give three quarters of the compute units a block; else the largest
+// slice that does, with four, two, then one weight block per wave.
+struct ResPlan {
+  int R = 0, KS = 0, nslice = 0, blocks = 0;
+};
+inline ResPlan res_plan(int M, int N, int K, int ncu) {
+  ResPlan p;
+  const int NB = (N + 15) / 16;
+  auto fits = [&](int R, int KS) {
+    const int ns = (K + KS - 1) / KS, groups = (NB + NWV * R - 1) / (NWV * R);
+    if (ns * groups * 4 < ncu * 3) return false;
+    p.R = R;
+    p.KS = KS;
+    p.nslice = ns;
+    p.blocks = ns * groups;
+    return true;
+  };
+  if (K <= RS_KS)
+    for (int R : {4, 2, 1})
+      if (fits(R, K)) return p;
+  for (int R : {4, 2, 1})
+    for (int KS : {RS_KS, RS_KS / 2, RS_KS / 4})
+      if (KS < K && fits(R, KS)) return p;
+  // nothing fills the chip: one weight block per wave, the smallest slices
+  p.R = 1;
+  p.KS = std::min(K, RS_KS / 4);
+  p.nslice = (K + p.KS - 1) / p.KS;
+  p.blocks = p.nslice * ((NB + NWV - 1) / NWV);
+  return p;
+}
+
+template <class Epi>
+void launch_res(const bf16* A, int64_t lda, const bf16* Wt, int M, int N, int K, float* part,
+                const Epi& epi, hipStream_t st, HostCopy hc) {
+  const ResPlan p = res_plan(M, N, K, device_cu_count());
+  hc.first_block = p.blocks;
+  const int grid = p.blocks + (hc.n16 > 0 ? hc.blocks : 0);
+  if (p.R == 4)
+    gemm_res_k<4, Epi><<<grid, NWV * 64, 0, st>>>(A, lda, Wt, M, N, K, p.KS, p.nslice, part, epi, hc);
+  else if (p.R == 2)
+    gemm_res_k<2, Epi><<<grid, NWV * 64, 0, st>>>(A, lda, Wt, M, N, K, p.KS, p.nslice, part, epi, hc);
+  else
+    gemm_res_k<1, Epi><<<grid, NWV * 64, 0, st>>>(A, lda, Wt, M, N, K, p.KS, p.nslice, part, epi, hc);
+  if (p.nslice > 4)
+    launch_reduce<8>(part, p.nslice, M, N, epi, st);
+  else if (p.nslice > 2)
+    launch_reduce<4>(part, p.nslice, M, N, epi, st);
+  else if (p.nslice == 2)
+    launch_reduce<2>(part, p.nslice, M, N, epi, st);
+}
+
 // The tallest row blocks (64 or 32 rows: one block per compute unit; 16 rows:
 // two) whose grid still occupies three quarters of the compute units: taller
 // blocks re-read the weights fewer times.
@@ -369,21 +603,40 @@ bool skinny_ok(int M, int N, int K) {
   return M >= 1 && M <= skn::kMaxStreamRows && N >= 2 && N % 2 == 0 && K % skn::KC == 0;
 }
 
+int res_slices(int M, int N, int K) {
+  if (M < 1 || M > 16 * skn::RS_MT || K % (64 * skn::RS_KB) != 0 || N % 4 != 0) return 0;
+  if ((size_t)N * K * 2 < (size_t(16) << 20)) return 0;  // small weights: the column tiles
+  return skn::res_plan(M, N, K, device_cu_count()).nslice;
+}
+
+// the resident-activation path applies (and has its partial buffer if it splits K)
+static bool use_res(const StreamRes& r, int M, int N, int K) {
+  const int ns = r.wt ? res_slices(M, N, K) : 0;
+  return ns == 1 || (ns > 1 && r.part);
+}
+
 void skinny_store(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int M, int N, int K,
-                  bf16* out, int64_t ldo, float alpha, hipStream_t st) {
-  skn::launch_stream(A, lda, W, ldw, M, N, K, skn::EpiStore{out, ldo, alpha}, st);
+                  bf16* out, int64_t ldo, float alpha, hipStream_t st, const StreamRes& r) {
+  if (use_res(r, M, N, K))
+    skn::launch_res(A, lda, r.wt, M, N, K, r.part, skn::EpiStore{out, ldo, alpha}, st, HostCopy{});
+  else
+    skn::launch_stream(A, lda, W, ldw, M, N, K, skn::EpiStore{out, ldo, alpha}, st);
 }
 
 void skinny_f32(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int M, int N, int K,
-                float* out, int64_t ldo, hipStream_t st, const HostCopy& hc) {
-  skn::launch_stream(A, lda, W, ldw, M, N, K, skn::EpiF32{out, ldo}, st, hc);
+                float* out, int64_t ldo, hipStream_t st, const HostCopy& hc, const StreamRes& r) {
+  if (use_res(r, M, N, K))
+    skn::launch_res(A, lda, r.wt, M, N, K, r.part, skn::EpiF32{out, ldo}, st, hc);
+  else
+    skn::launch_stream(A, lda, W, ldw, M, N, K, skn::EpiF32{out, ldo}, st, hc);
 }
 
 int host_copy_blocks(int n16) { return std::min(16, std::max(1, (n16 + 1023) / 1024)); }
 
 void skinny_query(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int M, int N, int K,
                   float* a, int R, bf16* q_nope, bf16* q_cat, const int32_t* pos_host,
-                  const Dims& d, const RopeTab& rt, hipStream_t st, const HostCopy& hc) {
+                  const Dims& d, const RopeTab& rt, hipStream_t st, const HostCopy& hc,
+                  const StreamRes& r) {
   skn::EpiQuery e;
   e.a = a;
   e.R = R;
@@ -396,7 +649,10 @@ void skinny_query(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int M,
   e.dc = d.dc;
   e.scale = d.scale;
   e.rt = rt;
-  skn::launch_stream(A, lda, W, ldw, M, N, K, e, st, hc);
+  if (use_res(r, M, N, K))
+    skn::launch_res(A, lda, r.wt, M, N, K, r.part, e, st, hc);
+  else
+    skn::launch_stream(A, lda, W, ldw, M, N, K, e, st, hc);
 }
 
 void decode_finish(const bf16* q_nope, const bf16* w_ukT, bf16* q_cat, int B, bool absorb,

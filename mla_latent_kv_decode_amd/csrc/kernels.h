@@ -168,12 +168,24 @@ void cache_write(const T* rows, const int64_t* slot, int ntok, int R, T* cache, 
 bool skinny_ok(int M, int N, int K);
 // compute units of the current device (cached per device)
 int device_cu_count();
+// For few rows against large weights (M <= 32, N K >= 8 Mi elements,
+// K % 128 == 0, N % 4 == 0) the same products run split-K with the activation
+// slice resident in LDS, over W's fragment-tiled copy (tile_rows layout);
+// res_slices: the K slices that path uses (0: it does not apply).  With more
+// than one slice it needs res_slices * M * N fp32 of partials.
+int res_slices(int M, int N, int K);
+struct StreamRes {
+  const bf16* wt = nullptr;  // W fragment-tiled, or null: the 32-column tiles
+  float* part = nullptr;     // split-K partials
+};
 // out (bf16, row stride ldo) = alpha C
 void skinny_store(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int M, int N, int K,
-                  bf16* out, int64_t ldo, float alpha, hipStream_t st);
+                  bf16* out, int64_t ldo, float alpha, hipStream_t st,
+                  const StreamRes& r = StreamRes{});
 // out (fp32, row stride ldo) = C
 void skinny_f32(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int M, int N, int K,
-                float* out, int64_t ldo, hipStream_t st, const HostCopy& hc = HostCopy{});
+                float* out, int64_t ldo, hipStream_t st, const HostCopy& hc = HostCopy{},
+                const StreamRes& r = StreamRes{});
 // columns [0, R) of C to a (fp32, row stride R); the remaining columns are
 // query heads [nope (dn) | rope (dr)]: nope to q_nope (M, H, dn), rope rotated
 // at pos_host[row] (a host array, passed to the kernel by value) and scaled by
@@ -183,7 +195,7 @@ void skinny_f32(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int M, i
 void skinny_query(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int M, int N, int K,
                   float* a, int R, bf16* q_nope, bf16* q_cat, const int32_t* pos_host,
                   const Dims& d, const RopeTab& rt, hipStream_t st,
-                  const HostCopy& hc = HostCopy{});
+                  const HostCopy& hc = HostCopy{}, const StreamRes& r = StreamRes{});
 // Blocks (of 256 threads) a HostCopy of n16 words takes.
 int host_copy_blocks(int n16);
 // One launch finishing the projections of B tokens, each part optional:

@@ -328,6 +328,7 @@ struct DecodeLayout {
   bool step = false;  // fused append (mla_decode_step)
   int max_cslots = 0;  // chunk slots of the two-pass combine
   size_t meta, scratch, pin, pq, cq, q_nope, q_cat, acc, ml, cacc, cml, o_lat, o;
+  size_t rpart;  // split-K partials of the resident-activation stream GEMMs
   size_t total = 0;
 };
 
@@ -416,6 +417,19 @@ DecodeLayout decode_layout(const mla_ctx* h, int Bs, int64_t total_rows, bool st
   L.cml = c.take((size_t)L.max_cslots * d.H * 2 * 4);
   L.o_lat = c.take((size_t)B * d.H * d.dc * e);
   L.o = c.take((size_t)B * d.H * d.dv * e);
+  // the fused path's few-row products over the tiled weights (W_o, q_b, the
+  // first projection) may split K
+  size_t rp = 0;
+  if (h->mfma) {
+    auto res = [&](int N, int K) {
+      const int ns = mla::res_slices(B, N, K);
+      rp = std::max(rp, ns > 1 ? (size_t)ns * B * N : (size_t)0);
+    };
+    res(d.D, d.H * d.dv);
+    res(step ? h->n_in : (d.dq ? d.dq : qw), d.D);
+    if (d.dq) res(qw, d.dq);
+  }
+  L.rpart = c.take(rp * 4);
   L.total = c.off;
   return L;
 }
@@ -1414,6 +1428,15 @@ static void run_q_and_append(mla_ctx* h, const T* x, int B, void* ws, const Deco
 // layers, B <= 128 query rows): the first projection leaves the kv_a columns (and q_a) in
 // fp32 and finishes the query heads itself; one more launch appends the latent
 // rows, normalises q_a and / or forms the absorbed query.
+// the tiled weight and partial buffer for the resident-activation stream GEMMs
+static mla::StreamRes stream_res(const mla_ctx* h, const void* wt, void* ws,
+                                 const DecodeLayout& L) {
+  mla::StreamRes r;
+  r.wt = static_cast<const bf16*>(wt);
+  r.part = at<float>(ws, L.rpart);
+  return r;
+}
+
 static bool q_skinny_fits(const mla_ctx* h, int B, const DecodeLayout& L) {
   const Dims& d = h->d;
   if (!h->mfma || d.dc != 512 || d.dn % 32 != 0 || d.dr % 2 != 0) return false;
@@ -1438,9 +1461,11 @@ static void q_skinny_first(mla_ctx* h, const bf16* x, int B, void* ws, const Dec
                       nullptr, at<bf16>(ws, L.q_cat), pos_host, d, h->rope, h->stream, hc);
   } else if (!d.dq) {
     mla::skinny_query(x, d.D, w1, d.D, B, n1, d.D, a, L.step ? d.R : 0, at<bf16>(ws, L.q_nope),
-                      at<bf16>(ws, L.q_cat), pos_host, d, h->rope, h->stream, hc);
+                      at<bf16>(ws, L.q_cat), pos_host, d, h->rope, h->stream, hc,
+                      stream_res(h, L.step ? h->t_in : h->t_q, ws, L));
   } else {
-    mla::skinny_f32(x, d.D, w1, d.D, B, n1, d.D, a, n1, h->stream, hc);
+    mla::skinny_f32(x, d.D, w1, d.D, B, n1, d.D, a, n1, h->stream, hc,
+                    stream_res(h, L.step ? h->t_in : h->t_q, ws, L));
   }
 }
 
@@ -1471,7 +1496,8 @@ static void q_skinny_rest(mla_ctx* h, int B, void* ws, const DecodeLayout& L,
     return;
   }
   mla::skinny_query(cq, d.dq, (const bf16*)h->w_qb, d.dq, B, qw, d.dq, nullptr, 0, q_nope, q_cat,
-                    pos_host, d, h->rope, h->stream);
+                    pos_host, d, h->rope, h->stream, mla::HostCopy{},
+                    stream_res(h, h->t_qb, ws, L));
   mla::decode_finish(q_nope, w_ukT, q_cat, B, true, false, false, nullptr, 0, 0, mt.pos,
                      slot_dev, kv_g, cache, nullptr, nullptr, d, h->rope, h->stream);
 }
@@ -1561,7 +1587,7 @@ static int run_decode(mla_ctx* h, const T* hidden, int B, int q_len, T* cache, T
   if constexpr (sizeof(T) == 2) {
     if (h->mfma && mla::skinny_ok(B, d.D, ko)) {
       mla::skinny_store((const bf16*)o, ko, (const bf16*)h->w_o, ko, B, d.D, ko, (bf16*)out, d.D,
-                        1.f, h->stream);
+                        1.f, h->stream, stream_res(h, h->t_o, ws, L));
       o_done = true;
     }
   }
