@@ -99,14 +99,17 @@ def src_hash(path: str) -> str:
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def traffic_from_profile(n_launch_bytes: float):
+def traffic_from_profile(workload: str, kernel: str):
     """HBM bytes per launch of the core kernel from the committed rocprofv3
-    counter summary, or None if absent or taken on a different kernel source."""
+    counter summary, or None if absent, taken on another workload or kernel,
+    or on a different kernel source."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     try:
         t = json.load(open(TRAFFIC_FILE))
     except Exception:
+        return None
+    if str(t.get("workload", "")).split(" ")[0] != workload or t.get("kernel") != kernel:
         return None
     if t.get("kernel_src_sha") != src_hash(CORE_SRC):
         return None
@@ -474,7 +477,10 @@ def main():
     gbs = cache_bytes / t_step / 1e9
     core_gbs = cache_bytes / (core_ms * 1e-3) / 1e9
     fp8 = wl.kv == "fp8"
-    traffic = None if (fp8 or P or q > 1) else traffic_from_profile(cache_bytes)
+    core_kernel = (("decode_core_wide8_k" if fp8 else "decode_core_wide_k")
+                   if d.n_heads % 128 == 0 else
+                   "decode_core_ring8_k" if fp8 else "decode_core_ring_k")
+    traffic = None if (P or q > 1) else traffic_from_profile(wl.name, core_kernel)
 
     res = {
         "metric": "MLA decode latent-KV GB/s + tokens/s (V2-Lite shapes, B=64), % of HBM peak"
@@ -502,8 +508,7 @@ def main():
                    "cache_bytes": int(cache_bytes),
                    "weight_bytes": int(weight_bytes), "hidden": d.hidden, "heads": d.n_heads,
                    "kv_lora": d.kv_lora, "qk_rope": d.qk_rope},
-        "roofline": {"kernel": "decode_core_ring8_k" if fp8 else
-                     "decode_core_wide_k" if d.n_heads % 128 == 0 else "decode_core_ring_k",
+        "roofline": {"kernel": core_kernel,
                      "bound": "hbm",
                      "kernel_timing": "HIP events (no system fence) around every split-S core "
                                       "launch, K eager steps",

@@ -51,9 +51,9 @@ static_assert(NLOAD % LOADERS == 0 && LOADERS <= NW, "tile loads split evenly");
 // exchange area after the ring: every head group's P fragment (1 KB, lane
 // order), the per-head rescale factors and the per-group rescale flags
 constexpr int XP_OFF = NST * ST_BYTES;
-constexpr int XA_OFF = XP_OFF + NW * 1024;
-constexpr int XF_OFF = XA_OFF + HEADS * 4;
-constexpr int LDS_BYTES = XF_OFF + NW * 4;
+// inside the exchange area: P fragments, rescale factors, rescale flags
+constexpr int X_P = 0, X_A = NW * 1024, X_F = X_A + HEADS * 4, X_BYTES = X_F + NW * 4;
+constexpr int LDS_BYTES = XP_OFF + X_BYTES;
 constexpr int CB_W = 32 / NW;                  // 16-column blocks of the latent sum per wave
 constexpr float kRescale = 8.0f;
 constexpr int kXcds = 8;
@@ -108,6 +108,200 @@ __device__ __forceinline__ void issue_tile(const char* base, int last, uint32_t 
   }
 }
 
+// Per-lane LDS offsets of the MFMA operands inside a tile (as in the 16-head
+// core).  Row-wise operand of k-step s < 16: row lr, chunk 4s + lg, i.e. at
+// qk_off[s & 3] + 256 (s >> 2); rope chunk 4(s - 16) + lg at qk_rope[s - 16].
+// Transposing operand of column block cb = 4q + t: lane (g = lg, s = lr)
+// addresses row r = 4g + s/4, columns 16 cb + 4(s % 4): chunk 2cb + h with
+// h = (s % 4) / 2, byte 8(s & 1).  Its position 2(cb ^ a) + (h ^ b) (a = r & 7,
+// b = r >> 3) puts it at pv_e[t] + 128q for even q and pv_e[t] - pv_d + 128q
+// for odd q.
+struct TileOffsets {
+  int qk_off[4], qk_rope0, qk_rope1, pv_e[4], pv_d;
+  __device__ __forceinline__ explicit TileOffsets(int lane) {
+    const int lr = lane & 15, lg = lane >> 4;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) qk_off[k] = lr * 1024 + 16 * ((4 * k + lg) ^ lat_swz(lr));
+    qk_rope0 = ROPE_OFF + lr * 128 + 16 * (lg ^ rope_swz(lr));
+    qk_rope1 = ROPE_OFF + lr * 128 + 16 * ((4 + lg) ^ rope_swz(lr));
+    const int r = 4 * lg + (lr >> 2);
+    const int a = r & 7, b = (r >> 3) & 1, h = (lr & 3) >> 1;
+    pv_d = 256 * (a >> 2);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      pv_e[t] = r * 1024 + 16 * (h ^ b) + 8 * (lr & 1) + 32 * (t ^ (a & 3)) + 128 * (a >> 2);
+  }
+};
+
+// Scores of this wave's 16 heads against the tile at `st` (S^T = K . Q^T for
+// both 16-row blocks), the online softmax (lazy reference maximum; lane holds
+// rows row0 + 16 rb + 4 lg + i of head h0 + lr), and the publication of P (the
+// B operand of the latent sum, in lane order), the rescale factor of each
+// head and whether this group rescaled, in the exchange area at `xch`.
+// F8: the tile holds the rows' codes (exact in bf16) and `scl` their scales
+// s_r; a score is s_r (q_abs . code) + q_rope . k_rope, and the latent sum's
+// operand is p s_r (the softmax sum takes p).
+template <bool F8>
+__device__ __forceinline__ void tile_scores(const char* st, char* xch, const TileOffsets& to,
+                                            const bf16x8_t (&qf)[18], int row0, int nv,
+                                            int wave, int lane, float& m_run, float& l_run,
+                                            const float* scl = nullptr) {
+  const int lr = lane & 15, lg = lane >> 4;
+  f32x4_t sc[2];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const char* sl = st + rb * 16 * 1024;  // latent rows of this block
+    const char* sr = st + rb * 16 * 128;   // rope rows (offsets include ROPE_OFF)
+    f32x4_t sa = (f32x4_t){0.f, 0.f, 0.f, 0.f}, sb = sa;
+#pragma unroll
+    for (int part = 0; part < 6; ++part) {
+      bf16x8_t kf[3];
+#pragma unroll
+      for (int u = 0; u < 3; ++u) {
+        const int s = 3 * part + u;
+        if (s < 16)
+          kf[u] = *reinterpret_cast<const bf16x8_t*>(sl + to.qk_off[s & 3] + 256 * (s >> 2));
+        else
+          kf[u] = *reinterpret_cast<const bf16x8_t*>(sr + (s == 16 ? to.qk_rope0 : to.qk_rope1));
+      }
+#pragma unroll
+      for (int u = 0; u < 3; ++u) {
+        const int s = 3 * part + u;
+        if (F8 && s == 16) {
+          // the latent part complete: scale it by the rows' s_r, then add
+          // the rope products to it
+          const float4 r4 = *reinterpret_cast<const float4*>(scl + 16 * rb + 4 * lg);
+          const f32x4_t lat = sa + sb;
+          sa = (f32x4_t){r4.x * lat[0], r4.y * lat[1], r4.z * lat[2], r4.w * lat[3]};
+          sb = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+        }
+        if (s & 1) sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[u], qf[s], sb, 0, 0, 0);
+        else sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[u], qf[s], sa, 0, 0, 0);
+      }
+    }
+    sc[rb] = sa + sb;
+  }
+  float sv[8];
+  bool grow = false;
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool valid = row0 + 16 * rb + 4 * lg + i < nv;
+      sv[4 * rb + i] = valid ? sc[rb][i] * kLog2e : -INFINITY;
+      grow |= sv[4 * rb + i] > m_run + kRescale;
+    }
+  float alpha = 1.f;
+  const bool resc = __any(grow);
+  if (resc) {
+    float mx = sv[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    l_run *= alpha;
+    m_run = m_new;
+  }
+  float pv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    pv[i] = __builtin_amdgcn_exp2f(sv[i] - m_run);
+    l_run += pv[i];
+  }
+  if constexpr (F8) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const float4 r4 = *reinterpret_cast<const float4*>(scl + 16 * rb + 4 * lg);
+      pv[4 * rb] *= r4.x;
+      pv[4 * rb + 1] *= r4.y;
+      pv[4 * rb + 2] *= r4.z;
+      pv[4 * rb + 3] *= r4.w;
+    }
+  }
+  uint32_t pk[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(pv[2 * i], pv[2 * i + 1]);
+  // (store addresses from the opaque lane index: nothing per lane stays live
+  // across the tile loop for them)
+  const int ln = lane_id_opaque();
+  *reinterpret_cast<bf16x8_t*>(xch + X_P + wave * 1024 + ln * 16) =
+      __builtin_bit_cast(bf16x8_t, pk);
+  if (ln < 16) reinterpret_cast<float*>(xch + X_A)[16 * wave + ln] = alpha;
+  if (ln == 0) reinterpret_cast<int*>(xch + X_F)[wave] = resc ? 1 : 0;
+}
+
+// O^T += C^T . P^T for this wave's columns and every head group: mfma
+// 16x16x32 whose k index runs over rows 4g..4g+3 of row block 0, then of row
+// block 1, for lane group g (the order the softmax lanes hold P in); C^T from
+// two transposing reads per 16-column block, read once.
+__device__ __forceinline__ void tile_latent_sum(const char* st, const char* xch,
+                                                const TileOffsets& to, int wave, int lane,
+                                                f32x4_t (&o)[NW][CB_W]) {
+  const int lr = lane & 15;
+  bf16x8_t cf[CB_W];
+#pragma unroll
+  for (int c = 0; c < CB_W; ++c) {
+    typedef __attribute__((address_space(3))) s16x4_t* lptr;
+    const int q = (CB_W * wave + c) >> 2, tt = (CB_W * wave + c) & 3;
+    const int off = to.pv_e[tt] - (q & 1) * to.pv_d + 128 * q;
+    const s16x4_t c0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lptr)(st + off));
+    const s16x4_t c1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lptr)(st + 16 * 1024 + off));
+    const s16x8_t c8 = __builtin_shufflevector(c0, c1, 0, 1, 2, 3, 4, 5, 6, 7);
+    cf[c] = __builtin_bit_cast(bf16x8_t, c8);
+  }
+  const int* xf = reinterpret_cast<const int*>(xch + X_F);
+  const float* xa = reinterpret_cast<const float*>(xch + X_A);
+#pragma unroll
+  for (int g = 0; g < NW; ++g) {
+    if (xf[g]) {
+      const float a = xa[16 * g + lr];
+#pragma unroll
+      for (int c = 0; c < CB_W; ++c) o[g][c] *= a;
+    }
+    const bf16x8_t pg = *reinterpret_cast<const bf16x8_t*>(xch + X_P + g * 1024 + lane * 16);
+#pragma unroll
+    for (int c = 0; c < CB_W; ++c)
+      o[g][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cf[c], pg, o[g][c], 0, 0, 0);
+  }
+}
+
+// Q^T fragments of head h0 + lr of query row qrow_idx: columns 32 s + 8 lg .. + 7
+__device__ __forceinline__ void load_query(const bf16* q_cat, int64_t qrow_idx, int H, int h0,
+                                           int lane, bf16x8_t (&qf)[18]) {
+  const bf16* qrow = q_cat + (qrow_idx * H + h0 + (lane & 15)) * RW + (lane >> 4) * 8;
+#pragma unroll
+  for (int s = 0; s < 18; ++s) qf[s] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * s);
+#pragma unroll
+  for (int s = 0; s < 18; ++s) asm volatile("" ::"v"(qf[s]));
+}
+
+// The segment's partial: (max, sum) of this wave's heads; the latent sums of
+// this wave's columns for every head.
+__device__ __forceinline__ void store_partial(float* __restrict__ acc_out,
+                                              float* __restrict__ ml_out, int64_t slot, int H,
+                                              int hbase, int wave, int lane, float m_run,
+                                              float l_run, const f32x4_t (&o)[NW][CB_W]) {
+  const int lr = lane & 15, lg = lane >> 4;
+  const int h0 = hbase + wave * 16;
+  float l = l_run;
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  if (lg == 0) {
+    ml_out[(slot * H + h0 + lr) * 2] = m_run;
+    ml_out[(slot * H + h0 + lr) * 2 + 1] = l;
+  }
+#pragma unroll
+  for (int g = 0; g < NW; ++g) {
+    float* pacc = acc_out + (slot * H + hbase + 16 * g + lr) * DC + 16 * CB_W * wave + 4 * lg;
+#pragma unroll
+    for (int c = 0; c < CB_W; ++c)
+      *reinterpret_cast<float4*>(pacc + 16 * c) =
+          make_float4(o[g][c][0], o[g][c][1], o[g][c][2], o[g][c][3]);
+  }
+}
+
 __global__ void __launch_bounds__(512, 1)
 decode_core_wide_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cache, DecodeMeta mt,
                    float* __restrict__ acc_out, float* __restrict__ ml_out, int H, int nparts,
@@ -122,33 +316,10 @@ decode_core_wide_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
   if (part >= nparts) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int lr = lane & 15, lg = lane >> 4;
   const int hbase = hblk * HEADS;
   const int h0 = hbase + wave * 16;  // this wave's softmax heads h0 .. h0 + 15
   const uint32_t lds0 = lds_u32(lds);
-
-  // operand offsets inside a 16-row block (as in the 16-head core)
-  // row-wise operand of k-step s < 16: row lr, chunk 4s + lg, i.e. at
-  // qk_off[s & 3] + 256 (s >> 2); rope chunk 4(s - 16) + lg at qk_rope[s - 16]
-  int qk_off[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) qk_off[k] = lr * 1024 + 16 * ((4 * k + lg) ^ lat_swz(lr));
-  const int qk_rope0 = ROPE_OFF + lr * 128 + 16 * (lg ^ rope_swz(lr));
-  const int qk_rope1 = ROPE_OFF + lr * 128 + 16 * ((4 + lg) ^ rope_swz(lr));
-  // transposing operand of column block cb = 4q + t: lane (g = lg, s = lr)
-  // addresses row r = 4g + s/4, columns 16 cb + 4(s % 4): chunk 2cb + h with
-  // h = (s % 4) / 2, byte 8(s & 1).  Its position 2(cb ^ a) + (h ^ b) (a = r & 7,
-  // b = r >> 3) puts it at pv_e[t] + 128q for even q and pv_e[t] - pv_d + 128q
-  // for odd q.
-  int pv_e[4], pv_d;
-  {
-    const int r = 4 * lg + (lr >> 2);
-    const int a = r & 7, b = (r >> 3) & 1, h = (lr & 3) >> 1;
-    pv_d = 256 * (a >> 2);
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-      pv_e[t] = r * 1024 + 16 * (h ^ b) + 8 * (lr & 1) + 32 * (t ^ (a & 3)) + 128 * (a >> 2);
-  }
+  const TileOffsets to(lane);
 
   const ConstWorkPtr works = reinterpret_cast<ConstWorkPtr>((uintptr_t)mt.work);
   DecodeWork wk = load_work(works + part);
@@ -171,15 +342,8 @@ decode_core_wide_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
     DecodeWork nx = wk;
     if (wk.next >= 0) nx = load_work(works + wk.next);
 
-    // Q^T fragments of head h0 + lr: columns 32 s + 8 lg .. + 7
     bf16x8_t qf[18];
-    {
-      const bf16* qrow = q_cat + ((int64_t)(wk.b * q_len + tok) * H + h0 + lr) * RW + lg * 8;
-#pragma unroll
-      for (int s = 0; s < 18; ++s) qf[s] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * s);
-    }
-#pragma unroll
-    for (int s = 0; s < 18; ++s) asm volatile("" ::"v"(qf[s]));
+    load_query(q_cat, (int64_t)wk.b * q_len + tok, H, h0, lane, qf);
 
     float m_run = -INFINITY, l_run = 0.f;
     // o[g][c][i]: latent sum of head hbase + 16 g + lr, column 16 (CB_W wave + c) + 4 lg + i
@@ -198,128 +362,176 @@ decode_core_wide_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
       __syncthreads();  // tile t is in LDS; every wave is done with tile t-1
       if (t + NST - 1 < ntile) issue(t + NST - 1);
       const char* st = lds + (t % NST) * ST_BYTES;
-      const int row0 = t * TR;
-      // ---- scores of this wave's 16 heads: S^T = K . Q^T for both 16-row blocks
-      f32x4_t sc[2];
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        const char* sl = st + rb * 16 * 1024;  // latent rows of this block
-        const char* sr = st + rb * 16 * 128;   // rope rows (offsets include ROPE_OFF)
-        f32x4_t sa = (f32x4_t){0.f, 0.f, 0.f, 0.f}, sb = sa;
-#pragma unroll
-        for (int part = 0; part < 6; ++part) {
-          bf16x8_t kf[3];
-#pragma unroll
-          for (int u = 0; u < 3; ++u) {
-            const int s = 3 * part + u;
-            if (s < 16)
-              kf[u] = *reinterpret_cast<const bf16x8_t*>(sl + qk_off[s & 3] + 256 * (s >> 2));
-            else
-              kf[u] = *reinterpret_cast<const bf16x8_t*>(sr + (s == 16 ? qk_rope0 : qk_rope1));
-          }
-#pragma unroll
-          for (int u = 0; u < 3; ++u) {
-            const int s = 3 * part + u;
-            if (s & 1) sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[u], qf[s], sb, 0, 0, 0);
-            else sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[u], qf[s], sa, 0, 0, 0);
-          }
-        }
-        sc[rb] = sa + sb;
-      }
-      // ---- online softmax of this wave's heads (lazy reference maximum); lane
-      // holds rows row0 + 16 rb + 4 lg + i of head h0 + lr
-      float sv[8];
-      bool grow = false;
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const bool valid = row0 + 16 * rb + 4 * lg + i < nv;
-          sv[4 * rb + i] = valid ? sc[rb][i] * kLog2e : -INFINITY;
-          grow |= sv[4 * rb + i] > m_run + kRescale;
-        }
-      float alpha = 1.f;
-      const bool resc = __any(grow);
-      if (resc) {
-        float mx = sv[0];
-#pragma unroll
-        for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float m_new = fmaxf(m_run, mx);
-        alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        l_run *= alpha;
-        m_run = m_new;
-      }
-      float pv[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        pv[i] = __builtin_amdgcn_exp2f(sv[i] - m_run);
-        l_run += pv[i];
-      }
-      {
-        uint32_t pk[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(pv[2 * i], pv[2 * i + 1]);
-        // publish P (the B operand of the latent sum, in lane order), the
-        // rescale factor of each head and whether this group rescaled
-        *reinterpret_cast<bf16x8_t*>(lds + XP_OFF + wave * 1024 + lane * 16) =
-            __builtin_bit_cast(bf16x8_t, pk);
-        if (lg == 0) reinterpret_cast<float*>(lds + XA_OFF)[16 * wave + lr] = alpha;
-        if (lane == 0) reinterpret_cast<int*>(lds + XF_OFF)[wave] = resc ? 1 : 0;
-      }
+      tile_scores<false>(st, lds + XP_OFF, to, qf, t * TR, nv, wave, lane, m_run, l_run);
       __syncthreads();  // every group's P of tile t is published
-      // ---- O^T += C^T . P^T for this wave's columns and every head group: mfma
-      // 16x16x32 whose k index runs over rows 4g..4g+3 of row block 0, then of
-      // row block 1, for lane group g (the order the softmax lanes hold P in);
-      // C^T from two transposing reads per 16-column block, read once
-      bf16x8_t cf[CB_W];
-#pragma unroll
-      for (int c = 0; c < CB_W; ++c) {
-        typedef __attribute__((address_space(3))) s16x4_t* lptr;
-        const int q = (CB_W * wave + c) >> 2, tt = (CB_W * wave + c) & 3;
-        const int off = pv_e[tt] - (q & 1) * pv_d + 128 * q;
-        const s16x4_t c0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lptr)(st + off));
-        const s16x4_t c1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lptr)(st + 16 * 1024 + off));
-        const s16x8_t c8 = __builtin_shufflevector(c0, c1, 0, 1, 2, 3, 4, 5, 6, 7);
-        cf[c] = __builtin_bit_cast(bf16x8_t, c8);
-      }
-      const int* xf = reinterpret_cast<const int*>(lds + XF_OFF);
-      const float* xa = reinterpret_cast<const float*>(lds + XA_OFF);
-#pragma unroll
-      for (int g = 0; g < NW; ++g) {
-        if (xf[g]) {
-          const float a = xa[16 * g + lr];
-#pragma unroll
-          for (int c = 0; c < CB_W; ++c) o[g][c] *= a;
-        }
-        const bf16x8_t pg = *reinterpret_cast<const bf16x8_t*>(lds + XP_OFF + g * 1024 + lane * 16);
-#pragma unroll
-        for (int c = 0; c < CB_W; ++c)
-          o[g][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cf[c], pg, o[g][c], 0, 0, 0);
-      }
+      tile_latent_sum(st, lds + XP_OFF, to, wave, lane, o);
     }
 
-    // ---- the segment's partial: (max, sum) of this wave's heads; the latent
-    // sums of this wave's columns for every head
-    {
-      float l = l_run;
-      l += __shfl_xor(l, 16, 64);
-      l += __shfl_xor(l, 32, 64);
-      const int64_t slot = (int64_t)tok * nseg_total + wk.pidx;
-      if (lg == 0) {
-        ml_out[(slot * H + h0 + lr) * 2] = m_run;
-        ml_out[(slot * H + h0 + lr) * 2 + 1] = l;
-      }
+    store_partial(acc_out, ml_out, (int64_t)tok * nseg_total + wk.pidx, H, hbase, wave, lane,
+                  m_run, l_run, o);
+    __syncthreads();  // the stages are refilled by the next segment
+    if (wk.next < 0) break;
+    wk = nx;
+  }
+}
+
+// ---- FP8 rows (656 bytes: 512 E4M3 codes, 64 bf16 rope values, the fp32
+// row scale s).  The raw rows of a 32-row tile stream into a 3-stage ring of
+// 21 KB stages (21 one-KB LDS-DMA copies per tile from waves 0-6, rows laid
+// end to end at r * 656; past the tile's last row the copies re-read it); all
+// eight waves then decode the tile once into a bf16 tile of the layout above
+// (the codes' values, exact in bf16, and the rope values) plus the 32 row
+// scales, which the scores and the latent sum's operand take in fp32 as the
+// 16-head FP8 core does.  Two bf16 tiles alternate, so the decode of tile
+// t + 1 runs beside the scores of tile t:
+//   raw tile t + 1 arrived -> barrier Y(t): tile t decoded, the other bf16
+//   tile, the P area and raw stage of tile t free
+//   -> copy raw tile t + 3; decode raw tile t + 1 into the other bf16 tile;
+//      scores and softmax of tile t
+//   -> barrier X(t): P published -> latent sum of tile t.
+constexpr int F8_RB = 656;                      // bytes per FP8 row
+constexpr int F8_SCALE = 640;                   // byte of the row scale
+constexpr int F8_NR = 3;                        // raw stages
+constexpr int F8_NLOAD = 21;                    // one-KB copies per raw tile (32 x 656 B <= 21 KB)
+constexpr int F8_LOADERS = 7;
+constexpr int F8_LPW = F8_NLOAD / F8_LOADERS;   // 3 per loading wave
+constexpr int F8_RAW_BYTES = F8_NLOAD * 1024;
+constexpr int F8_RAW_OFF = 2 * ST_BYTES;
+constexpr int F8_SC_OFF = F8_RAW_OFF + F8_NR * F8_RAW_BYTES;  // row scales of the two tiles
+constexpr int F8_XP_OFF = F8_SC_OFF + 2 * TR * 4;
+constexpr int F8_LDS_BYTES = F8_XP_OFF + X_BYTES;
+static_assert(F8_NLOAD % F8_LOADERS == 0 && F8_LOADERS <= NW, "raw tile copies split evenly");
+static_assert(TR * F8_RB <= F8_RAW_BYTES, "raw stage holds a tile");
+static_assert(F8_LDS_BYTES <= 160 * 1024, "LDS");
+
+// Copies I = LPW wave .. + LPW - 1 of a raw tile: 16-byte chunk j = 64 I +
+// lane is chunk j % 41 of row j / 41 (rows past `last` re-read it).
+template <bool NT>
+__device__ __forceinline__ void issue_raw_tile(const char* base, int last, uint32_t stage,
+                                               int wave) {
+  const int lane = lane_id_opaque();
 #pragma unroll
-      for (int g = 0; g < NW; ++g) {
-        float* pacc = acc_out + (slot * H + hbase + 16 * g + lr) * DC + 16 * CB_W * wave + 4 * lg;
+  for (int u = 0; u < F8_LPW; ++u) {
+    const int I = F8_LPW * wave + u;
+    const int j = 64 * I + lane;
+    int r = j / (F8_RB / 16);
+    const int c = j - r * (F8_RB / 16);
+    r = r <= last ? r : last;
+    dma16h<NT>(base + (int64_t)r * F8_RB + 16 * c, stage + I * 1024);
+  }
+}
+
+// Rows 4 wave .. 4 wave + 3 of a raw tile decoded into a bf16 tile: lane l
+// turns codes 8 l .. 8 l + 7 of each row into bf16 chunk l (at
+// l ^ lat_swz(r)); lanes 0..31 copy rope chunk l & 7 of row 4 wave + l / 8;
+// lanes 0..3 copy the rows' scales to `scl`.  (The lane index is re-read
+// opaquely so that the per-lane offsets are not kept live across the tile
+// loop.)
+__device__ __forceinline__ void decode_raw_rows(const char* raw, char* dst, float* scl, int wave) {
+  const int lane = lane_id_opaque();
+  constexpr int RPW = TR / NW;  // rows per wave
 #pragma unroll
-        for (int c = 0; c < CB_W; ++c)
-          *reinterpret_cast<float4*>(pacc + 16 * c) =
-              make_float4(o[g][c][0], o[g][c][1], o[g][c][2], o[g][c][3]);
-      }
+  for (int k = 0; k < RPW; ++k) {
+    const int r = RPW * wave + k;
+    const uint2 v = *reinterpret_cast<const uint2*>(raw + r * F8_RB + 8 * lane);
+    const uint32_t w[2] = {v.x, v.y};
+    uint32_t out[4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      out[2 * h] =
+          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[h], 1.0f, false));
+      out[2 * h + 1] =
+          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[h], 1.0f, true));
     }
+    *reinterpret_cast<uint4*>(dst + r * 1024 + 16 * (lane ^ lat_swz(r & 15))) =
+        make_uint4(out[0], out[1], out[2], out[3]);
+  }
+  if (lane < 8 * RPW) {
+    const int r = RPW * wave + (lane >> 3), c = lane & 7;
+    *reinterpret_cast<uint4*>(dst + ROPE_OFF + r * 128 + 16 * (c ^ rope_swz(r & 15))) =
+        *reinterpret_cast<const uint4*>(raw + r * F8_RB + 512 + 16 * c);
+  }
+  if (lane < RPW) {
+    const int r = RPW * wave + lane;
+    scl[r] = *reinterpret_cast<const float*>(raw + r * F8_RB + F8_SCALE);
+  }
+}
+
+__global__ void __launch_bounds__(512, 1)
+decode_core_wide8_k(const bf16* __restrict__ q_cat, const uint8_t* __restrict__ cache,
+                    DecodeMeta mt, float* __restrict__ acc_out, float* __restrict__ ml_out, int H,
+                    int nparts, int q_len, int nseg_total) {
+  __shared__ __attribute__((aligned(1024))) char lds_all[F8_LDS_BYTES];
+  char* xch = lds_all + F8_XP_OFF;  // the exchange area, behind the raw ring
+  const int WG = H / HEADS;
+  const int bid = blockIdx.x;
+  const int part = (bid / (kXcds * WG * q_len)) * kXcds + bid % kXcds;
+  const int hbq = (bid / kXcds) % (WG * q_len);
+  const int tok = hbq / WG, hblk = hbq % WG;
+  if (part >= nparts) return;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int hbase = hblk * HEADS;
+  const int h0 = hbase + wave * 16;
+  const uint32_t raw0 = lds_u32(lds_all) + F8_RAW_OFF;
+  const TileOffsets to(lane);
+
+  const ConstWorkPtr works = reinterpret_cast<ConstWorkPtr>((uintptr_t)mt.work);
+  DecodeWork wk = load_work(works + part);
+  for (;;) {
+    const int n = wk.n;
+    const int nv = token_rows(wk, q_len, tok);
+    const int ntile = (n + TR - 1) / TR;
+    const int64_t wrow = wk.row;
+    const bool once = WG * q_len == 1;
+    auto issue = [&](int t) {
+      if (wave >= F8_LOADERS) return;
+      const char* base =
+          reinterpret_cast<const char*>(cache) + seg_row(mt, wrow, t * TR) * F8_RB;
+      const uint32_t stage = raw0 + (t % F8_NR) * F8_RAW_BYTES;
+      if (once) issue_raw_tile<true>(base, n - t * TR - 1, stage, wave);
+      else issue_raw_tile<false>(base, n - t * TR - 1, stage, wave);
+    };
+#pragma unroll
+    for (int t = 0; t < F8_NR; ++t)
+      if (t < ntile) issue(t);
+    DecodeWork nx = wk;
+    if (wk.next >= 0) nx = load_work(works + wk.next);
+
+    bf16x8_t qf[18];
+    load_query(q_cat, (int64_t)wk.b * q_len + tok, H, h0, lane, qf);
+
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x4_t o[NW][CB_W];
+#pragma unroll
+    for (int g = 0; g < NW; ++g)
+#pragma unroll
+      for (int c = 0; c < CB_W; ++c) o[g][c] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+
+    wait_vmcnt<0>();
+    __syncthreads();  // raw tile 0 arrived
+    float* scl = reinterpret_cast<float*>(lds_all + F8_SC_OFF);  // [tile & 1][row]
+    if (ntile > 0) decode_raw_rows(lds_all + F8_RAW_OFF, lds_all, scl, wave);
+
+    for (int t = 0; t < ntile; ++t) {
+      static_assert(F8_NR == 3, "wait counts below assume 3 raw stages");
+      if (wave < F8_LOADERS && t + 1 < ntile) {
+        if (t + 2 < ntile) wait_vmcnt<F8_LPW>();
+        else wait_vmcnt<0>();
+      }
+      __syncthreads();  // Y(t)
+      if (t + F8_NR < ntile) issue(t + F8_NR);
+      if (t + 1 < ntile)
+        decode_raw_rows(lds_all + F8_RAW_OFF + ((t + 1) % F8_NR) * F8_RAW_BYTES,
+                        lds_all + ((t + 1) & 1) * ST_BYTES, scl + ((t + 1) & 1) * TR, wave);
+      const char* st = lds_all + (t & 1) * ST_BYTES;
+      tile_scores<true>(st, xch, to, qf, t * TR, nv, wave, lane, m_run, l_run, scl + (t & 1) * TR);
+      __syncthreads();  // X(t)
+      tile_latent_sum(st, xch, to, wave, lane, o);
+    }
+
+    store_partial(acc_out, ml_out, (int64_t)tok * nseg_total + wk.pidx, H, hbase, wave, lane,
+                  m_run, l_run, o);
     __syncthreads();  // the stages are refilled by the next segment
     if (wk.next < 0) break;
     wk = nx;
@@ -329,6 +541,15 @@ decode_core_wide_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
 }  // namespace decw
 
 int decode_core_wide_heads() { return decw::HEADS; }
+
+void decode_core_wide8(const bf16* q_cat, const uint8_t* cache, const DecodeMeta& m, int parts,
+                       const TokenSplit& tk, float* acc, float* ml, const Dims& d,
+                       hipStream_t st) {
+  const int wg = d.H / decw::HEADS * tk.q_len;
+  const int blocks = (parts + decw::kXcds - 1) / decw::kXcds * decw::kXcds * wg;
+  decw::decode_core_wide8_k<<<blocks, 64 * decw::NW, 0, st>>>(q_cat, cache, m, acc, ml, d.H,
+                                                              parts, tk.q_len, tk.nseg_total);
+}
 
 void decode_core_wide(const bf16* q_cat, const bf16* cache, const DecodeMeta& m, int parts,
                       const TokenSplit& tk, float* acc, float* ml, const Dims& d,

@@ -227,6 +227,12 @@ int decode_core_wide_heads();
 void decode_core_wide(const bf16* q_cat, const bf16* cache, const DecodeMeta& m, int parts,
                       const TokenSplit& tk, float* acc, float* ml, const Dims& d,
                       hipStream_t st);
+// The same over FP8 rows (fp8_row_bytes(512, 64) bytes): each tile of raw rows
+// is decoded once into the shared bf16 tile (code values, exact) with the row
+// scales applied in fp32 to the scores and the latent sum's operand.
+void decode_core_wide8(const bf16* q_cat, const uint8_t* cache, const DecodeMeta& m, int parts,
+                       const TokenSplit& tk, float* acc, float* ml, const Dims& d,
+                       hipStream_t st);
 // FP8 latent cache (rows of fp8_row_bytes(dc, dr) bytes, dc == 512, dr == 64):
 // the latent row append (as append_rows, into FP8 rows), the store of rows
 // given in bf16 (T x R) into FP8 rows, a raw row-byte scatter, and the ring

@@ -332,10 +332,9 @@ struct DecodeLayout {
   size_t total = 0;
 };
 
-// bf16 layers with many heads use the shared-tile core (FP8 rows are read by
-// the 16-head-group core, one workgroup per group)
+// layers with many heads use the shared-tile core (bf16 or FP8 rows)
 bool wide_core(const mla_ctx* h) {
-  return h->mfma && !h->kv8 && h->d.H % mla::decode_core_wide_heads() == 0;
+  return h->mfma && h->d.H % mla::decode_core_wide_heads() == 0;
 }
 // other MFMA layers use the ring core
 bool ring_core(const mla_ctx* h) { return h->mfma && !wide_core(h); }
@@ -1538,7 +1537,10 @@ static int run_decode(mla_ctx* h, const T* hidden, int B, int q_len, T* cache, T
   if constexpr (sizeof(T) == 2) {
     if (h->mfma) {
       const mla::TokenSplit tk{q_len, nseg_total};
-      if (wide_core(h))
+      if (wide_core(h) && h->kv8)
+        mla::decode_core_wide8(q_cat, (const uint8_t*)(const void*)cache, mt, parts, tk, acc, ml,
+                               d, h->stream);
+      else if (wide_core(h))
         mla::decode_core_wide(q_cat, cache, mt, parts, tk, acc, ml, d, h->stream);
       else if (h->kv8)  // FP8 rows; otherwise as the bf16 ring core
         mla::decode_core_ring8(q_cat, (const uint8_t*)(const void*)cache, mt, parts, tk, acc, ml,

@@ -141,8 +141,9 @@ def test_fp8_decode_step(lens):
 
 
 def test_fp8_v3_decode_ragged_small():
-    """A 128-head layer (q-LoRA, V3 shapes) on an FP8 cache: the FP8 core runs
-    one workgroup per 16-head group of every part (eight per part here)."""
+    """A 128-head layer (q-LoRA, V3 shapes) on an FP8 cache: the many-head
+    core decodes each raw tile once for all 128 heads; an empty sequence, a
+    single row, ragged tails and several tiles."""
     lens = [0, 1, 33, 64, 700, 2000]
     case = DecodeCase(synth.V3, "bf16", 0.02, lens, kv="fp8")
     _check(case, range(len(lens)))

@@ -99,6 +99,11 @@ def test_multitoken_many_head_core():
     case.check(case.run(), [0, 3])
 
 
+def test_multitoken_many_head_fp8_core():
+    case = MTCase(synth.V3, "bf16", 0.02, [0, 33, 300, 2100], 2, keep=[0, 3], kv="fp8")
+    case.check(case.run(), [0, 3])
+
+
 def test_multitoken_paged_and_append():
     """Paged cache (64-row pages in random order) with the append of the new
     rows: the rows it writes and its outputs equal, bit for bit, those of the

@@ -92,6 +92,13 @@ def test_paged_decode_many_head_core():
     _paged_vs_contiguous(case, 64, 9, [0, 3])
 
 
+def test_paged_decode_many_head_fp8_core():
+    """128 heads on FP8 rows: the raw tiles of the many-head FP8 core come
+    through the page list, bit-exact against the contiguous cache."""
+    case = DecodeCase(synth.V3, "bf16", 0.02, [0, 33, 300, 2100], keep=[0, 3], kv="fp8")
+    _paged_vs_contiguous(case, 64, 10, [0, 3])
+
+
 def test_paged_decode_shared_prefix_page():
     """Two sequences whose first page is the same pool page read the same
     first rows: equal, bit for bit, to a contiguous cache in which the second
