@@ -176,7 +176,11 @@ int mla_decode_paged_check(const mla_config* cfg, const int32_t* pos, const int3
                            int64_t cache_rows, int32_t writes);
 
 /* Create a handle on the current HIP device.  stream: a hipStream_t or NULL.
- * *out receives the handle (NULL on failure). */
+ * *out receives the handle (NULL on failure).
+ * With the environment variable MLA_LOG set (to anything but "0") when the
+ * library first logs, mla_create and every decode and prefill call print one
+ * line on stderr: the layer and its attention core, or the call's shape, work
+ * plan (parts, segments, combine chunks, attention tiles) and workspace. */
 int mla_create(const mla_config* cfg, void* stream, mla_handle* out);
 
 /* Synchronise the handle's stream and free everything the library owns. */

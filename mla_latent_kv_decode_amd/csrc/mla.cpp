@@ -10,6 +10,7 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -120,6 +121,26 @@ int fail(mla_ctx* h, int code, const char* fmt, ...) {
     h->err = buf;
   }
   return code;
+}
+
+// MLA_LOG=1 (read once per process): one line per call on stderr with the
+// call's shape, the work plan and the kernels chosen.
+bool log_on() {
+  static const bool on = [] {
+    const char* e = getenv("MLA_LOG");
+    return e && *e && strcmp(e, "0") != 0;
+  }();
+  return on;
+}
+
+void mlog(const char* fmt, ...) {
+  if (!log_on()) return;
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  fprintf(stderr, "[mla] %s\n", buf);
 }
 
 #define HIP_TRY(h, call)                                                              \
@@ -338,6 +359,12 @@ bool wide_core(const mla_ctx* h) {
 }
 // other MFMA layers use the ring core
 bool ring_core(const mla_ctx* h) { return h->mfma && !wide_core(h); }
+// the attention core a decode call of this layer runs
+const char* core_name(const mla_ctx* h) {
+  if (!h->mfma) return "decode_core_generic_k";
+  if (wide_core(h)) return h->kv8 ? "decode_core_wide8_k" : "decode_core_wide_k";
+  return h->kv8 ? "decode_core_ring8_k" : "decode_core_ring_k";
+}
 // the split combine fused with the value un-absorb (MFMA layers with dv = 128)
 bool combine_uv(const mla_ctx* h) { return h->mfma && h->d.dv == 128; }
 
@@ -998,6 +1025,10 @@ int mla_create(const mla_config* cfg, void* stream, mla_handle* out) {
     return MLA_ERR_HIP;
   }
   *out = h;
+  mlog("create: device %d (%d CUs), H=%d D=%d dc=%d dr=%d dn=%d dv=%d q_lora=%d, %s, cache %s, "
+       "absorption %s, decode core %s", h->device, h->n_cu, h->d.H, h->d.D, h->d.dc, h->d.dr,
+       h->d.dn, h->d.dv, h->d.dq, is_f32(h) ? "fp32" : "bf16", h->kv8 ? "FP8 rows" : "dtype rows",
+       h->cfg.absorb ? "materialised" : "factored", core_name(h));
   return MLA_OK;
 }
 
@@ -1664,6 +1695,10 @@ static int decode_exec(mla_ctx* h, const DecodeCall& c, const char* what) {
   mt.pages = c.pg ? at<int32_t>(meta, mo.pages) : nullptr;
   mt.pg_off = c.pg ? at<int32_t>(meta, mo.pg_off) : nullptr;
   mt.page_shift = c.pg ? c.pg->shift : 0;
+  mlog("%s: B=%d q_len=%d rows=%lld, %d parts, %d segments, combine chunks %d, workspace %zu B, "
+       "core %s, projections %s", what, B, q_len, (long long)total, parts, nseg_total, max_chunks,
+       L.total, core_name(h), hc.n16 > 0 ? "stream GEMMs (metadata copied by the first)"
+                                          : "tile GEMMs (metadata copied first)");
   DecodeMeta mc = mt;  // the combine's view: one sequence per query row
   mc.pstart = at<int32_t>(meta, mo.vpstart);
   mc.nseg = at<int32_t>(meta, mo.vnseg);
@@ -2050,6 +2085,10 @@ static int prefill_common(mla_ctx* h, const void* hidden, const int32_t* cu_new,
       }
     }
   }
+  mlog("%s: B=%d new tokens %d, key rows %lld (longest %d), %zu attention tiles of %d queries "
+       "x %d heads, key rows %s, workspace %zu B", what, B, T, (long long)rows, max_n,
+       tiles.size(), tq, h->d.H, staged ? "gathered into the workspace" : "read in place",
+       L.total);
   if ((rc = stage_upload(h, at<char>(ws, L.meta), blob.data(), blob.size()))) return rc;
   const void* keys = cache;
   if (staged) {

@@ -14,7 +14,9 @@ import os
 import numpy as np
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmla.so")
+# MLA_LIB selects another build of the same library (the host-sanitized one
+# in the CPU tests); by default the in-tree libmla.so
+LIB_PATH = os.environ.get("MLA_LIB") or os.path.join(_PKG, "libmla.so")
 
 MLA_OK = 0
 MLA_ERR_INVALID_ARG = -1
