@@ -91,12 +91,27 @@ __device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int* tm
   *tn = in / gm;
 }
 
+// Row stride of the bf16 output tile staged in LDS: 16 bytes past the row, so
+// that the 16 rows x 32 bytes a fragment store covers fall on distinct banks
+// (stride / 4 = 4 mod 64), and the 16-byte reads of 16 consecutive chunks of
+// a row as well.
 template <int BN>
+constexpr int out_row_bytes() { return BN * 2 + 16; }
+template <int BN>
+constexpr int lds_bytes(bool staged) {
+  return staged && BM * out_row_bytes<BN>() > NST * Cfg<BN>::ST ? BM * out_row_bytes<BN>()
+                                                                  : NST * Cfg<BN>::ST;
+}
+
+// STAGED (bf16 output, N and the row stride multiples of 8, 16-byte aligned
+// output): the tile goes through LDS and leaves in 16-byte row chunks, 1 KB
+// of contiguous rows per wave store, instead of 32-byte pieces of 16 rows.
+template <int BN, bool STAGED>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_big_k(const bf16* __restrict__ A, const bf16* __restrict__ W, int M, int N, int K,
            int tiles_m, int tiles_n, GemmOut out) {
   using C = Cfg<BN>;
-  __shared__ __attribute__((aligned(1024))) char lds[NST * C::ST];
+  __shared__ __attribute__((aligned(1024))) char lds[lds_bytes<BN>(STAGED)];
   int tm, tn;
   tile_of(blockIdx.x, tiles_m, tiles_n, &tm, &tn);
   const int m0 = tm * BM, n0 = tn * BN;
@@ -167,6 +182,33 @@ gemm_big_k(const bf16* __restrict__ A, const bf16* __restrict__ W, int M, int N,
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[j], a[i], acc[i][j], 0, 0, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, C::NI + C::NJ, 0);  // the DS reads
     __builtin_amdgcn_sched_group_barrier(0x008, C::NI * C::NJ, 0);  // then the products
+  }
+
+  if constexpr (STAGED) {
+    constexpr int S = out_row_bytes<BN>();
+    __syncthreads();  // every wave is done with the ring
+    // lane holds tile rows wm 128 + 16 i + lane % 16, columns wn WN + 16 j +
+    // 4 (lane / 16) .. + 3
+    const int rw = wm * 128 + (lane & 15), cw = wn * C::WN + 4 * (lane >> 4);
+#pragma unroll
+    for (int i = 0; i < C::NI; ++i)
+#pragma unroll
+      for (int j = 0; j < C::NJ; ++j) {
+        const f32x4_t v = acc[i][j] * out.alpha;
+        *reinterpret_cast<uint2*>(lds + (rw + 16 * i) * S + (cw + 16 * j) * 2) =
+            make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+      }
+    __syncthreads();
+    constexpr int CPR = BN / 8;  // 16-byte chunks per tile row
+#pragma unroll 4
+    for (int c = threadIdx.x; c < BM * CPR; c += 512) {
+      const int r = c / CPR, cc = c % CPR;
+      const int m = m0 + r, n = n0 + 8 * cc;
+      if (m < M && n < N)
+        *reinterpret_cast<uint4*>(out.b16 + (int64_t)m * out.ldo + n) =
+            *reinterpret_cast<const uint4*>(lds + r * S + 16 * cc);
+    }
+    return;
   }
 
   // lane holds C[m][n .. n + 3] of every (i, j) block
@@ -249,10 +291,16 @@ void gemm_big(const bf16* A, const bf16* W, int M, int N, int K, const GemmOut& 
   const int bn = gemm_big_bn(M, N, n_cu);
   const int tiles_m = (M + bg::BM - 1) / bg::BM, tiles_n = (N + bn - 1) / bn;
   const dim3 grid(tiles_m * tiles_n);
-  if (bn == 256)
-    bg::gemm_big_k<256><<<grid, 512, 0, st>>>(A, W, M, N, K, tiles_m, tiles_n, out);
+  const bool staged = !out.f32 && out.b16 && N % 8 == 0 && out.ldo % 8 == 0 &&
+                      (uintptr_t)out.b16 % 16 == 0;
+  if (bn == 256 && staged)
+    bg::gemm_big_k<256, true><<<grid, 512, 0, st>>>(A, W, M, N, K, tiles_m, tiles_n, out);
+  else if (bn == 256)
+    bg::gemm_big_k<256, false><<<grid, 512, 0, st>>>(A, W, M, N, K, tiles_m, tiles_n, out);
+  else if (staged)
+    bg::gemm_big_k<128, true><<<grid, 512, 0, st>>>(A, W, M, N, K, tiles_m, tiles_n, out);
   else
-    bg::gemm_big_k<128><<<grid, 512, 0, st>>>(A, W, M, N, K, tiles_m, tiles_n, out);
+    bg::gemm_big_k<128, false><<<grid, 512, 0, st>>>(A, W, M, N, K, tiles_m, tiles_n, out);
 }
 
 }  // namespace mla
