@@ -256,7 +256,9 @@ __device__ __forceinline__ void tile_latent_sum(const char* st, const char* xch,
 #pragma unroll
   for (int g = 0; g < NW; ++g) {
     if (xf[g]) {
-      const float a = xa[16 * g + lr];
+      // (the rescale factor's address from the opaque lane index: nothing
+      // per lane stays live across the tile loop for it)
+      const float a = xa[16 * g + (lane_id_opaque() & 15)];
 #pragma unroll
       for (int c = 0; c < CB_W; ++c) o[g][c] *= a;
     }
@@ -278,11 +280,17 @@ __device__ __forceinline__ void load_query(const bf16* q_cat, int64_t qrow_idx, 
 }
 
 // The segment's partial: (max, sum) of this wave's heads; the latent sums of
-// this wave's columns for every head.
+// every head (fp32, 2 KB per head), staged through `stage` (the idle tile ring,
+// at least 64 x XR_BYTES) 64 heads at a time so that they leave in 16-byte
+// chunks of whole rows (1 KB of a row per wave store) rather than 64-byte
+// pieces of 16 rows.  Starts with a barrier (the ring's last readers) and
+// leaves the stage in use.
+constexpr int XR_BYTES = DC * 4 + 16;  // staged row: the 16-byte pad spreads 16 rows over the banks
 __device__ __forceinline__ void store_partial(float* __restrict__ acc_out,
                                               float* __restrict__ ml_out, int64_t slot, int H,
                                               int hbase, int wave, int lane, float m_run,
-                                              float l_run, const f32x4_t (&o)[NW][CB_W]) {
+                                              float l_run, const f32x4_t (&o)[NW][CB_W],
+                                              char* stage) {
   const int lr = lane & 15, lg = lane >> 4;
   const int h0 = hbase + wave * 16;
   float l = l_run;
@@ -292,13 +300,24 @@ __device__ __forceinline__ void store_partial(float* __restrict__ acc_out,
     ml_out[(slot * H + h0 + lr) * 2] = m_run;
     ml_out[(slot * H + h0 + lr) * 2 + 1] = l;
   }
+  constexpr int GH = NW / 2;  // head groups per half
 #pragma unroll
-  for (int g = 0; g < NW; ++g) {
-    float* pacc = acc_out + (slot * H + hbase + 16 * g + lr) * DC + 16 * CB_W * wave + 4 * lg;
+  for (int half = 0; half < 2; ++half) {
+    __syncthreads();  // the stage is free
 #pragma unroll
-    for (int c = 0; c < CB_W; ++c)
-      *reinterpret_cast<float4*>(pacc + 16 * c) =
-          make_float4(o[g][c][0], o[g][c][1], o[g][c][2], o[g][c][3]);
+    for (int gg = 0; gg < GH; ++gg)
+#pragma unroll
+      for (int c = 0; c < CB_W; ++c)
+        *reinterpret_cast<f32x4_t*>(stage + (16 * gg + lr) * XR_BYTES +
+                                    (16 * CB_W * wave + 16 * c + 4 * lg) * 4) = o[GH * half + gg][c];
+    __syncthreads();
+    float* dst = acc_out + (slot * H + hbase + 16 * GH * half) * DC;
+#pragma unroll 4
+    for (int k = threadIdx.x; k < 16 * GH * (DC / 4); k += 64 * NW) {
+      const int r = k / (DC / 4), cc = k % (DC / 4);
+      *reinterpret_cast<float4*>(dst + r * DC + 4 * cc) =
+          *reinterpret_cast<const float4*>(stage + r * XR_BYTES + 16 * cc);
+    }
   }
 }
 
@@ -368,7 +387,7 @@ decode_core_wide_k(const bf16* __restrict__ q_cat, const bf16* __restrict__ cach
     }
 
     store_partial(acc_out, ml_out, (int64_t)tok * nseg_total + wk.pidx, H, hbase, wave, lane,
-                  m_run, l_run, o);
+                  m_run, l_run, o, lds);
     __syncthreads();  // the stages are refilled by the next segment
     if (wk.next < 0) break;
     wk = nx;
@@ -403,6 +422,8 @@ constexpr int F8_LDS_BYTES = F8_XP_OFF + X_BYTES;
 static_assert(F8_NLOAD % F8_LOADERS == 0 && F8_LOADERS <= NW, "raw tile copies split evenly");
 static_assert(TR * F8_RB <= F8_RAW_BYTES, "raw stage holds a tile");
 static_assert(F8_LDS_BYTES <= 160 * 1024, "LDS");
+static_assert(16 * (NW / 2) * XR_BYTES <= XP_OFF && 16 * (NW / 2) * XR_BYTES <= F8_SC_OFF,
+              "a staged half of the partial fits in the tile ring");
 
 // Copies I = LPW wave .. + LPW - 1 of a raw tile: 16-byte chunk j = 64 I +
 // lane is chunk j % 41 of row j / 41 (rows past `last` re-read it).
@@ -531,7 +552,7 @@ decode_core_wide8_k(const bf16* __restrict__ q_cat, const uint8_t* __restrict__ 
     }
 
     store_partial(acc_out, ml_out, (int64_t)tok * nseg_total + wk.pidx, H, hbase, wave, lane,
-                  m_run, l_run, o);
+                  m_run, l_run, o, lds_all);
     __syncthreads();  // the stages are refilled by the next segment
     if (wk.next < 0) break;
     wk = nx;
