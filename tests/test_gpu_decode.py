@@ -246,6 +246,24 @@ def test_decode_step_batch_80():
     _step_case(synth.V2_LITE, [3 * b + (b % 7) * 11 for b in range(80)])
 
 
+# A 128-head layer with a 1024-wide query LoRA and hidden 2048: its query
+# up-projection (N = 128 * 192 = 24576, K = 1024, 48 MiB of weights) runs the
+# resident-activation product in one K slice, with the epilogue applied in
+# place; its output projection (N = 2048, K = 16384) in 32 slices and the
+# slice reduction.
+RES_DIMS = synth.LayerDims(hidden=2048, n_heads=128, qk_nope=128, qk_rope=64, v_head=128,
+                           kv_lora=512, q_lora=1024)
+
+
+def test_resident_products_one_and_many_slices():
+    case = DecodeCase(RES_DIMS, "bf16", 0.02, [0, 33, 400])
+    _check(case, range(3))
+
+
+def test_decode_step_resident_one_slice():
+    _step_case(RES_DIMS, [5, 90, 300])
+
+
 def test_core_timing_ring():
     """The library's core-launch timing: a ring of 3 slots after 5 decodes
     holds the last 3 durations, each positive and below a second."""
