@@ -157,7 +157,7 @@ combine_final_512_k(const float* __restrict__ cacc, const float* __restrict__ cm
 // VGPRs at kernel start, while phase 1 runs (rows SB .. 15 of the MFMA row
 // block are zero).  Wave w owns output columns 16 w .. 16 w + 15; o is rounded
 // to bf16.
-constexpr int SB_MAX = 8;              // sequences per block: 8, or 4 to fill the compute units
+constexpr int SB_MAX = 16;             // sequences per block: 16, 8 or 4 to fill the compute units
 constexpr int UV_NW = 8;               // waves
 constexpr int UV_DV = 128;
 constexpr int OROW = DC * 2 + 16;      // LDS row stride in bytes (padding: no bank conflicts)
@@ -287,12 +287,12 @@ void decode_combine_uv(const float* acc, const float* ml, const DecodeMeta& m, i
   if (max_chunks > 1)
     cmb::combine_chunks_512_k<<<dim3(B, H, max_chunks), 256, 0, st>>>(acc, ml, m, H, cacc, cml,
                                                                         o_lat, 1, 0);
-  // 8 sequences per block when that already gives a block per compute unit,
-  // else 4 (each block reads its head's whole W_UV, so fewer, taller blocks
-  // read less; more blocks spread the reads over more compute units)
-  const int sb = (int64_t)H * ((B + cmb::SB_MAX - 1) / cmb::SB_MAX) >= device_cu_count()
-                     ? cmb::SB_MAX
-                     : cmb::SB_MAX / 2;
+  // the most sequences per block (16, 8, else 4) that still give a block per
+  // compute unit: each block reads its head's whole W_UV, so fewer, taller
+  // blocks read less (and fill more of the 16-row product); more blocks
+  // spread the reads over more compute units
+  int sb = cmb::SB_MAX;
+  while (sb > 4 && (int64_t)H * ((B + sb - 1) / sb) < device_cu_count()) sb /= 2;
   cmb::combine_uv_k<<<dim3(H, (B + sb - 1) / sb), cmb::UV_NW * 64, 0, st>>>(
       acc, ml, cacc, cml, m, direct_single ? 1 : 0, w_uv, B, H, o_lat, o, sb);
 }
