@@ -241,9 +241,14 @@ def test_decode_step_v3():
 
 
 def test_decode_step_batch_80():
-    """More than 64 tokens: the projections leave the stream GEMMs for the
-    split-K tile GEMM path."""
+    """80 tokens: the stream GEMMs with 64-row blocks (ragged last block)."""
     _step_case(synth.V2_LITE, [3 * b + (b % 7) * 11 for b in range(80)])
+
+
+def test_decode_step_batch_136():
+    """More than 128 tokens: the projections leave the stream GEMMs for the
+    split-K tile GEMM path."""
+    _step_case(synth.V2_LITE, [2 * b + (b % 5) * 13 for b in range(136)])
 
 
 # A 128-head layer with a 1024-wide query LoRA and hidden 2048: its query
