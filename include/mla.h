@@ -386,8 +386,8 @@ int mla_decode_stage_offsets(mla_handle h, int32_t B, int64_t total_rows,
  * a fixed per-segment cost, and cuts inside a sequence fall on multiples of 32
  * rows (one tile of the MFMA cores).  The library itself uses max_parts = the
  * device's compute units divided by the number of workgroups a part runs (one
- * per 16-head group; one per 128 heads for bf16 layers with a multiple of
- * 128 heads).
+ * per 16-head group; one per 128 heads for layers with a multiple of 128
+ * heads, bf16 or FP8 rows).
  *   seq_len: HOST (B), each >= 1.
  *   part_begin: HOST out (max_parts + 1): segments of part p are
  *     [part_begin[p], part_begin[p+1]).
