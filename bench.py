@@ -270,13 +270,11 @@ def bench_prefill(args, wl):
     x = np.concatenate([synth.hidden_states(b, wl.new_tokens, d.hidden, wl.dtype,
                                             start=int(prior[b])) for b in range(B)])
     xd = torch.from_numpy(x).cuda().to(tdt)
-    pos = np.concatenate([prior[b] + np.arange(cu_new[b + 1] - cu_new[b]) for b in range(B)])
-    slot = np.concatenate([seq_off[b] + pos[cu_new[b]:cu_new[b + 1]] for b in range(B)])
     y = torch.empty((T, d.hidden), dtype=tdt, device="cuda")
 
     def step():
-        layer.append(xd, pos, slot, cache)
-        layer.prefill(xd, cu_new, prior, seq_off, cache, out=y)
+        # append of the new tokens' latent rows + the prefill, in one call
+        layer.prefill_step(xd, cu_new, prior, seq_off, cache, out=y)
 
     for _ in range(max(1, args.warmup)):
         step()
@@ -317,7 +315,7 @@ def bench_prefill(args, wl):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "timing": "eager steps (append + mla_prefill)",
+        "timing": "eager steps (mla_prefill_step: append + prefill)",
         "config": {"workload": wl.name, "batch": B, "new_tokens": wl.new_tokens,
                    "prior": [int(p) for p in prior], "key_rows": key_rows,
                    "causal_pairs": pairs, "step_tflop": round(flops / 1e12, 4),

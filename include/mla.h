@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 8
+#define MLA_ABI_VERSION 9
 
 typedef enum mla_status {
   MLA_OK = 0,
@@ -438,6 +438,28 @@ int mla_prefill(mla_handle h, const void* hidden, const int32_t* cu_new,
                 const int32_t* prior_len, const int64_t* seq_off, int32_t B,
                 const void* cache, int64_t cache_rows, void* out, void* ws,
                 size_t ws_bytes);
+
+/* A2 + P1 -- the prefill step: appends the T new tokens' latent rows (as
+ * mla_append_latent with pos = prior_len[b] + i at cache row seq_off[b] +
+ * prior_len[b] + i) and then runs mla_prefill on them, in one call.  For a
+ * layer with a query LoRA the append's product and the query's first
+ * projection are one product over [W_kva ; W_qa] (in the DeepSeek code the
+ * "Multi-Head Latent Attention" post quotes in section 3.4, wkv_a and wq_a
+ * both take the same hidden state).  Contiguous caches (bf16, fp32 or FP8
+ * rows).
+ *   Arguments as for mla_prefill; cache is written (the new rows) and read.
+ *   Workspace: mla_prefill_step_workspace_bytes (>= mla_prefill's).
+ * Errors: those of mla_prefill, and INVALID_ARG if two new rows share a cache
+ * row or a new row is a row some sequence reads as cached
+ * (mla_prefill_step_check). */
+size_t mla_prefill_step_workspace_bytes(mla_handle h, int32_t T, int32_t B,
+                                        int64_t total_key_rows);
+int mla_prefill_step_check(const mla_config* cfg, const int32_t* cu_new,
+                           const int32_t* prior_len, const int64_t* seq_off, int32_t B,
+                           int64_t cache_rows);
+int mla_prefill_step(mla_handle h, const void* hidden, const int32_t* cu_new,
+                     const int32_t* prior_len, const int64_t* seq_off, int32_t B, void* cache,
+                     int64_t cache_rows, void* out, void* ws, size_t ws_bytes);
 
 /* mla_prefill over a paged cache (the page pool of mla_decode_paged; the
  * KV-cache page grows its cache as a memory pool): position t of sequence b

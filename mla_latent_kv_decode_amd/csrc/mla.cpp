@@ -912,6 +912,24 @@ int mla_prefill_check(const mla_config* cfg, const int32_t* cu_new, const int32_
   return MLA_OK;
 }
 
+// The new rows of a prefill step on a contiguous cache: rows prior_len[b] ..
+// prior_len[b] + n_b - 1 of every sequence, distinct, none of them a row any
+// sequence reads as already cached.
+int mla_prefill_step_check(const mla_config* cfg, const int32_t* cu_new, const int32_t* prior_len,
+                           const int64_t* seq_off, int32_t B, int64_t cache_rows) {
+  const int rc = mla_prefill_check(cfg, cu_new, prior_len, seq_off, B, cache_rows);
+  if (rc) return rc;
+  std::vector<int64_t> w;
+  w.reserve((size_t)cu_new[B]);
+  for (int32_t b = 0; b < B; ++b)
+    for (int32_t i = 0; i < cu_new[b + 1] - cu_new[b]; ++i)
+      w.push_back(seq_off[b] + prior_len[b] + i);
+  return write_read_check(w, [&](auto visit) {
+    for (int32_t b = 0; b < B; ++b)
+      if (prior_len[b] > 0) visit(seq_off[b], seq_off[b] + prior_len[b]);
+  });
+}
+
 int mla_prefill_paged_check(const mla_config* cfg, const int32_t* cu_new,
                             const int32_t* prior_len, const int32_t* block_table,
                             int32_t max_pages, int32_t page_rows, int32_t B, int64_t cache_rows) {
@@ -1833,6 +1851,7 @@ namespace {
 struct PrefillLayout {
   size_t meta, scratch, pin, pq, cq, q_nope, q_rope, kv, o, keys, total;
   size_t meta_bytes, tiles_off;  // blob size and offset of the MFMA query tiles
+  size_t slot_off;               // prefill step: the new rows' cache rows (int64, T)
   // gathered key rows (FP8 or paged caches): offsets in the blob of the per-
   // sequence row counts, source offsets (contiguous) or page list starts
   // (paged), and the page list
@@ -1853,15 +1872,21 @@ int64_t max_prefill_pages(int B, int64_t rows) { return rows / 32 + B; }
 
 // staged: the key rows are gathered into the workspace first (FP8 or paged
 // caches)
+// Columns of the in-projection a prefill step runs: [W_kva ; W_qa] for a
+// query LoRA (one product for the append and the query's first half), else
+// W_kva alone (the query projection then reads the hidden states itself).
+int step_in_cols(const mla_ctx* h) { return h->d.dq ? h->n_in : h->d.R; }
+
 PrefillLayout prefill_layout(const mla_ctx* h, int T, int B, int64_t rows, int max_rows,
-                             bool staged, bool paged) {
+                             bool staged, bool paged, bool step = false) {
   const Dims& d = h->d;
   PrefillLayout L;
   const int qw = qw_of(d);
   const size_t scr = std::max({out_scratch(h, T, d.D, d.H * d.dv, 1),
                                out_scratch(h, max_rows, d.H * (d.dn + d.dv), d.dc, 1),
                                out_scratch(h, T, qw, d.dq ? d.dq : d.D, 1)});
-  const size_t pin = part_floats(h, T, d.dq ? d.dq : qw, d.D);
+  const size_t pin = std::max(part_floats(h, T, d.dq ? d.dq : qw, d.D),
+                              step ? part_floats(h, T, step_in_cols(h), d.D) : (size_t)0);
   const size_t pq = d.dq ? part_floats(h, T, qw, d.dq) : 0;
   const size_t e = h->esz;
   Carve c;
@@ -1872,6 +1897,8 @@ PrefillLayout prefill_layout(const mla_ctx* h, int T, int B, int64_t rows, int m
   L.pages_off = L.pstart_off + align_up((size_t)B * 4);
   L.meta_bytes = !staged ? L.nrows_off
                  : L.pages_off + (paged ? align_up((size_t)max_prefill_pages(B, rows) * 4) : 0);
+  L.slot_off = L.meta_bytes;
+  if (step) L.meta_bytes += align_up((size_t)T * 8);
   L.meta = c.take(L.meta_bytes);
   L.scratch = c.take(scr * 4);
   L.pin = c.take(pin * 4);
@@ -1907,7 +1934,7 @@ template <typename T>
 static int run_prefill(mla_ctx* h, const T* hidden, int ntok, int B, const int32_t* cu_new,
                        const int32_t* prior, const int64_t* seq_off, const T* cache, T* out,
                        void* ws, const PrefillLayout& L, const int64_t* kv_off_h,
-                       int ntiles) {
+                       int ntiles, const mla::Part* qa_done = nullptr) {
   const Dims& d = h->d;
   const int qw = qw_of(d);
   char* meta = at<char>(ws, L.meta);
@@ -1927,8 +1954,10 @@ static int run_prefill(mla_ctx* h, const T* hidden, int ntok, int B, const int32
   const T* wq = (const T*)h->w_q;
   const void* wqt = h->t_q;  // its tiled copy
   if (d.dq) {
-    const mla::Part pa = gemm_part<T>(h, hidden, d.D, (const T*)h->w_qa, d.D, ntok, d.dq, d.D,
-                                      at<float>(ws, L.pin), h->t_q);
+    // (a prefill step has W_qa x already, beside the append's columns)
+    const mla::Part pa = qa_done ? *qa_done
+                                 : gemm_part<T>(h, hidden, d.D, (const T*)h->w_qa, d.D, ntok, d.dq,
+                                                d.D, at<float>(ws, L.pin), h->t_q);
     mla::rmsnorm_rows<T>(pa, ntok, d.dq, (const T*)h->q_norm_g, d.eps, at<T>(ws, L.cq),
                          h->stream);
     qin = at<T>(ws, L.cq);
@@ -2002,13 +2031,14 @@ static int run_prefill(mla_ctx* h, const T* hidden, int ntok, int B, const int32
 static int prefill_common(mla_ctx* h, const void* hidden, const int32_t* cu_new,
                           const int32_t* prior_len, const int64_t* seq_off, const PageArgs* pg,
                           int32_t B, const void* cache, int64_t cache_rows, void* out, void* ws,
-                          size_t ws_bytes) {
-  const char* what = pg ? "prefill_paged" : "prefill";
+                          size_t ws_bytes, bool step = false) {
+  const char* what = pg ? "prefill_paged" : step ? "prefill_step" : "prefill";
   if (!h) return MLA_ERR_INVALID_ARG;
   if (!hidden || !cache || !out) return fail(h, MLA_ERR_INVALID_ARG, "%s: NULL tensor", what);
   const int rc0 = pg ? mla_prefill_paged_check(&h->cfg, cu_new, prior_len, pg->table,
                                                pg->max_pages, pg->page_rows, B, cache_rows)
-                     : mla_prefill_check(&h->cfg, cu_new, prior_len, seq_off, B, cache_rows);
+                  : step ? mla_prefill_step_check(&h->cfg, cu_new, prior_len, seq_off, B, cache_rows)
+                         : mla_prefill_check(&h->cfg, cu_new, prior_len, seq_off, B, cache_rows);
   if (rc0) return fail(h, rc0, "%s: %s (B=%d, cache_rows=%lld)", what, mla_status_string(rc0), B,
                        (long long)cache_rows);
   if (!h->absorbed) return fail(h, MLA_ERR_STATE, "%s before mla_absorb_weights", what);
@@ -2026,7 +2056,7 @@ static int prefill_common(mla_ctx* h, const void* hidden, const int32_t* cu_new,
   const int64_t* key_off = staged ? kv_off.data() : seq_off;
   const int32_t T = cu_new[B];
   const PrefillLayout L = prefill_layout(h, T, B, rows, (int)std::min<int64_t>(rows, INT32_MAX),
-                                         staged, pg != nullptr);
+                                         staged, pg != nullptr, step);
   int rc = check_ws(h, ws, ws_bytes, L.total);
   if (rc) return rc;
   DeviceGuard g(h->device);
@@ -2043,6 +2073,10 @@ static int prefill_common(mla_ctx* h, const void* hidden, const int32_t* cu_new,
     }
     kvo[b] = kv_off[b];
     so[b] = key_off[b];
+  }
+  if (step) {  // the new rows' cache rows
+    int64_t* slot = reinterpret_cast<int64_t*>(blob.data() + L.slot_off);
+    for (int32_t i = 0; i < T; ++i) slot[i] = seq_off[tok_seq[i]] + tok_pos[i];
   }
   // query tiles of the MFMA attention, longest key range first
   std::vector<mla::PrefillTile> tiles;
@@ -2090,6 +2124,40 @@ static int prefill_common(mla_ctx* h, const void* hidden, const int32_t* cu_new,
        tiles.size(), tq, h->d.H, staged ? "gathered into the workspace" : "read in place",
        L.total);
   if ((rc = stage_upload(h, at<char>(ws, L.meta), blob.data(), blob.size()))) return rc;
+  // a prefill step first appends the new tokens' latent rows (c and k_rope
+  // of every new position, "Multi-Head Latent Attention" post, section 3.1),
+  // through one product over [W_kva ; W_qa] for a query LoRA (both take the
+  // same hidden state in the DeepSeek code quoted in section 3.4)
+  mla::Part qa{};
+  bool qa_done = false;
+  if (step) {
+    const Dims& d = h->d;
+    const char* meta = at<char>(ws, L.meta);
+    const int32_t* pos_d = reinterpret_cast<const int32_t*>(meta + align_up((size_t)T * 4));
+    const int64_t* slot_d = reinterpret_cast<const int64_t*>(meta + L.slot_off);
+    const int n = step_in_cols(h);
+    const bool fuse = d.dq > 0;
+    if (is_f32(h)) {
+      const mla::Part a = gemm_part<float>(h, (const float*)hidden, d.D,
+                                           (const float*)(fuse ? h->w_in : h->w_kva), d.D, T, n,
+                                           d.D, at<float>(ws, L.pin), fuse ? h->t_in : h->t_kva);
+      mla::append_rows<float>(a, T, pos_d, slot_d, (const float*)h->kv_norm_g, (float*)cache, d,
+                              h->rope, h->stream);
+      qa = mla::Part{a.p + d.R, a.ks, a.ld, a.zs};
+    } else {
+      const mla::Part a = gemm_part<bf16>(h, (const bf16*)hidden, d.D,
+                                          (const bf16*)(fuse ? h->w_in : h->w_kva), d.D, T, n,
+                                          d.D, at<float>(ws, L.pin), fuse ? h->t_in : h->t_kva);
+      if (h->kv8)
+        mla::append_rows_fp8(a, T, pos_d, slot_d, (const bf16*)h->kv_norm_g, (uint8_t*)cache, d,
+                             h->rope, h->stream);
+      else
+        mla::append_rows<bf16>(a, T, pos_d, slot_d, (const bf16*)h->kv_norm_g, (bf16*)cache, d,
+                               h->rope, h->stream);
+      qa = mla::Part{a.p + d.R, a.ks, a.ld, a.zs};
+    }
+    qa_done = fuse;
+  }
   const void* keys = cache;
   if (staged) {
     const char* meta = at<char>(ws, L.meta);
@@ -2109,10 +2177,10 @@ static int prefill_common(mla_ctx* h, const void* hidden, const int32_t* cu_new,
   if (is_f32(h))
     return run_prefill<float>(h, (const float*)hidden, T, B, cu_new, prior_len, key_off,
                               (const float*)keys, (float*)out, ws, L, kv_off.data(),
-                              (int)tiles.size());
+                              (int)tiles.size(), qa_done ? &qa : nullptr);
   return run_prefill<bf16>(h, (const bf16*)hidden, T, B, cu_new, prior_len, key_off,
                            (const bf16*)keys, (bf16*)out, ws, L, kv_off.data(),
-                           (int)tiles.size());
+                           (int)tiles.size(), qa_done ? &qa : nullptr);
 }
 
 int mla_prefill(mla_handle h, const void* hidden, const int32_t* cu_new, const int32_t* prior_len,
@@ -2120,6 +2188,20 @@ int mla_prefill(mla_handle h, const void* hidden, const int32_t* cu_new, const i
                 void* out, void* ws, size_t ws_bytes) {
   return prefill_common(h, hidden, cu_new, prior_len, seq_off, nullptr, B, cache, cache_rows,
                         out, ws, ws_bytes);
+}
+
+size_t mla_prefill_step_workspace_bytes(mla_handle h, int32_t T, int32_t B,
+                                        int64_t total_key_rows) {
+  if (!h || T <= 0 || B <= 0 || total_key_rows <= 0) return 0;
+  const int max_rows = (int)std::min<int64_t>(total_key_rows, INT32_MAX);
+  return prefill_layout(h, T, B, total_key_rows, max_rows, h->kv8, false, true).total;
+}
+
+int mla_prefill_step(mla_handle h, const void* hidden, const int32_t* cu_new,
+                     const int32_t* prior_len, const int64_t* seq_off, int32_t B, void* cache,
+                     int64_t cache_rows, void* out, void* ws, size_t ws_bytes) {
+  return prefill_common(h, hidden, cu_new, prior_len, seq_off, nullptr, B, cache, cache_rows,
+                        out, ws, ws_bytes, true);
 }
 
 int mla_prefill_paged(mla_handle h, const void* hidden, const int32_t* cu_new,

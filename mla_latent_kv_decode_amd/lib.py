@@ -125,6 +125,12 @@ _SIGS = {
     "mla_core_timing": (ctypes.c_int, [_P, ctypes.c_int32]),
     "mla_core_timing_read": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_float), ctypes.c_int32,
                                             _I32P]),
+    "mla_prefill_step_workspace_bytes": (ctypes.c_size_t, [_P, ctypes.c_int32, ctypes.c_int32,
+                                                           ctypes.c_int64]),
+    "mla_prefill_step_check": (ctypes.c_int, [ctypes.POINTER(MLAConfig), _I32P, _I32P, _I64P,
+                                              ctypes.c_int32, ctypes.c_int64]),
+    "mla_prefill_step": (ctypes.c_int, [_P, _P, _I32P, _I32P, _I64P, ctypes.c_int32, _P,
+                                        ctypes.c_int64, _P, _P, ctypes.c_size_t]),
     "mla_prefill_workspace_bytes": (ctypes.c_size_t, [_P, ctypes.c_int32, ctypes.c_int32,
                                                       ctypes.c_int64]),
     "mla_prefill": (ctypes.c_int, [_P, _P, _I32P, _I32P, _I64P, ctypes.c_int32, _P,
@@ -469,6 +475,27 @@ class MLALayer:
         rc = self.lib.mla_prefill(self.h, _ptr(hidden), cu_p, pr_p, so_p, B, _ptr(cache),
                                   int(cache.shape[0]), _ptr(out), wsp, wsn)
         self._check(rc, self.h, "mla_prefill")
+        return out
+
+    def prefill_step(self, hidden, cu_new, prior_len, seq_off, cache, out=None):
+        """mla_prefill_step: appends the new tokens' latent rows (position
+        prior_len[b] + i at cache row seq_off[b] + prior_len[b] + i), then the
+        prefill, in one call."""
+        import torch
+        self._sync_stream()
+        cu_a, cu_p = _i32(cu_new)
+        pr_a, pr_p = _i32(prior_len)
+        so_a, so_p = _i64(seq_off)
+        B = len(pr_a)
+        T = int(cu_a[-1])
+        rows = int((pr_a.astype(np.int64) + np.diff(cu_a)).sum())
+        if out is None:
+            out = torch.empty((T, self.dims.hidden), dtype=self.torch_dtype, device=self.device)
+        wsp, wsn = self.ws.get(self.lib.mla_prefill_step_workspace_bytes(self.h, T, B,
+                                                                         max(rows, 1)))
+        rc = self.lib.mla_prefill_step(self.h, _ptr(hidden), cu_p, pr_p, so_p, B, _ptr(cache),
+                                       int(cache.shape[0]), _ptr(out), wsp, wsn)
+        self._check(rc, self.h, "mla_prefill_step")
         return out
 
     def prefill_paged(self, hidden, cu_new, prior_len, block_table, page_rows, cache, out=None):

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(mla):
     missing = [n for n in names if not hasattr(mla, n)]
     assert not missing, missing
     assert set(names) == set(L._SIGS), set(names) ^ set(L._SIGS)
-    assert mla.mla_abi_version() == 8
+    assert mla.mla_abi_version() == 9
 
 
 def test_status_strings(mla):
@@ -243,6 +243,33 @@ def test_prefill_check(mla):
     assert chk([0, 4, 7], [0, -2], [0, 4], 9) == L.MLA_ERR_INVALID_ARG
     assert chk([0, 0, 0], [3, 2], [0, 4], 9) == L.MLA_ERR_INVALID_ARG   # no new tokens
     assert chk([0, 4, 7], [2**31 - 3, 0], [0, 0], 2**40) == L.MLA_ERR_INVALID_ARG  # > int32
+
+
+def test_prefill_step_check(mla):
+    """mla_prefill_step writes the new rows itself: they must be distinct cache
+    rows, none of them a row some sequence reads as cached; otherwise as
+    mla_prefill_check."""
+    c = cfg()
+
+    def chk(cu, prior, off, rows):
+        ca, cp = _i32(cu)
+        pa, pp = _i32(prior)
+        oa, op = _i64(off)
+        return mla.mla_prefill_step_check(ctypes.byref(c), cp, pp, op, len(pa), rows)
+
+    assert chk([0, 4, 7], [0, 2], [0, 4], 9) == L.MLA_OK
+    assert chk([0, 4, 7], [0, 2], [0, 4], 8) == L.MLA_ERR_CAPACITY
+    assert chk([0, 4, 7], [0, -2], [0, 4], 9) == L.MLA_ERR_INVALID_ARG
+    # sequence 1's new rows 4..6 would overwrite sequence 0's new rows 2..5
+    assert chk([0, 4, 7], [0, 0], [2, 4], 9) == L.MLA_ERR_INVALID_ARG
+    # sequence 1 (rows 0..4, prior 2) writes rows 2..4, which sequence 0 reads as cached
+    assert chk([0, 1, 4], [4, 2], [0, 0], 9) == L.MLA_ERR_INVALID_ARG
+    # sequence 0 reads rows 0..2 and writes row 3; sequence 1 writes row 4
+    assert chk([0, 1, 2], [3, 0], [0, 4], 9) == L.MLA_OK
+    # ... but not at row 3, sequence 0's new row
+    assert chk([0, 1, 2], [3, 0], [0, 3], 9) == L.MLA_ERR_INVALID_ARG
+    # a shared prefix of 3 rows: both sequences' new rows would start at row 3
+    assert chk([0, 2, 4], [3, 3], [0, 0], 16) == L.MLA_ERR_INVALID_ARG
 
 
 def test_prefill_paged_check(mla):

@@ -98,13 +98,15 @@ def test_v3_prefill_ragged_large_tiles():
 def test_v3_prefill_4x4096_full_size():
     """The V3 chunked prefill at its full size (4 sequences x 4096 new tokens
     after 0 / 2048 / 0 / 2048 cached rows) in the launch configuration the
-    timing uses: every 64th query, the tile and key-tile edges and the whole
-    last 256-query tile of every sequence against the oracle."""
+    timing uses (mla_prefill_step: the fused in-projection and append, then
+    the prefill): the 16,384 appended rows against mla_append_latent's, and
+    every 64th query, the tile and key-tile edges and the whole last 256-query
+    tile of every sequence against the oracle."""
     w = synth.WORKLOADS["v3_prefill_4x4096"]
     prior, new = [0, 2048, 0, 2048], [4096] * 4
     q = np.unique(np.concatenate([np.arange(0, 4096, 64), [1, 31, 32, 255, 256, 2047],
                                   np.arange(4096 - 256, 4096)]))
-    run_prefill_case(w.dims, "bf16", w.weight_std, prior, new, query_subset=[q] * 4)
+    run_step_case(w.dims, "bf16", w.weight_std, prior, new, query_subset=[q] * 4)
 
 
 def test_v2lite_fp8_prefill():
@@ -116,3 +118,57 @@ def test_v2lite_fp8_prefill():
 
 def test_v3_fp8_prefill_small():
     run_prefill_case(synth.V3, "bf16", 0.02, [0, 21], [24, 9], kv="fp8")
+
+
+def run_step_case(dims, dtype, std, prior, new, kv="dtype", gap=0, query_subset=None):
+    """mla_prefill_step against the same batch appended through
+    mla_append_latent: the step must write the new tokens' latent rows (the
+    same rows up to the summation order of the fused in-projection, or the
+    same FP8 codes but for rare rounding ties), leave every other cache row
+    alone, and give the oracle's outputs."""
+    import torch
+    c = prefill_inputs(dims, dtype, std, prior, new, kv=kv, gap=gap)
+    ref_cache = c.cache.clone()
+    idx = np.concatenate([np.arange(c.seq_off[b] + c.prior[b], c.seq_off[b] + c.tot[b])
+                          for b in range(len(c.prior))])
+    idx_d = torch.as_tensor(idx, device="cuda")
+    c.cache[idx_d] = 0
+    y = host(c.layer.prefill_step(c.x_dev, c.cu_new, c.prior.astype(np.int32), c.seq_off,
+                                  c.cache))
+    new_rows, ref_rows = host(c.cache[idx_d]), host(ref_cache[idx_d])
+    if kv == "fp8":
+        assert np.mean(new_rows == ref_rows) > 0.98
+    else:
+        assert row_rel_err(new_rows, ref_rows).max() < tol(dtype)
+    keep = np.setdiff1d(np.arange(c.cache.shape[0]), idx)
+    keep_d = torch.as_tensor(keep, device="cuda")
+    assert torch.equal(c.cache[keep_d], ref_cache[keep_d])
+    return check_prefill(c, y, query_subset)
+
+
+def test_prefill_step_v3_fused_in_projection():
+    """A query LoRA: the append and the query's first projection share one
+    product over [W_kva ; W_qa]."""
+    run_step_case(synth.V3, "bf16", 0.02, [0, 21], [24, 9])
+
+
+@pytest.mark.timeout(300)
+def test_prefill_step_v3_large_tiles():
+    """670 new tokens: the fused in-projection on the large-tile GEMM, with a
+    ragged last row tile; sampled queries."""
+    q0 = np.unique(np.concatenate([np.arange(0, 600, 37), np.arange(590, 600)]))
+    run_step_case(synth.V3, "bf16", 0.02, [0, 300], [600, 70], gap=3,
+                  query_subset=[q0, np.arange(70)])
+
+
+def test_prefill_step_v2lite():
+    """No query LoRA: the append's own product, then the prefill."""
+    run_step_case(synth.V2_LITE, "bf16", 0.02, [0, 37, 100], [40, 13, 1])
+
+
+def test_prefill_step_v3_fp8():
+    run_step_case(synth.V3, "bf16", 0.02, [0, 21], [24, 9], kv="fp8")
+
+
+def test_prefill_step_tiny_f32():
+    run_step_case(synth.TINY, "f32", 0.05, [0, 3, 8], [9, 6, 1])
