@@ -443,10 +443,11 @@ int mla_prefill(mla_handle h, const void* hidden, const int32_t* cu_new,
  * mla_append_latent with pos = prior_len[b] + i at cache row seq_off[b] +
  * prior_len[b] + i) and then runs mla_prefill on them, in one call.  For a
  * layer with a query LoRA the append's product and the query's first
- * projection are one product over [W_kva ; W_qa] (in the DeepSeek code the
+ * projection read the hidden states once (in the DeepSeek code the
  * "Multi-Head Latent Attention" post quotes in section 3.4, wkv_a and wq_a
- * both take the same hidden state).  Contiguous caches (bf16, fp32 or FP8
- * rows).
+ * both take the same hidden state): one product over [W_kva ; W_qa], or for
+ * many tokens two products over one tiled copy of the hidden states.
+ * Contiguous caches (bf16, fp32 or FP8 rows).
  *   Arguments as for mla_prefill; cache is written (the new rows) and read.
  *   Workspace: mla_prefill_step_workspace_bytes (>= mla_prefill's).
  * Errors: those of mla_prefill, and INVALID_ARG if two new rows share a cache

@@ -2126,8 +2126,9 @@ static int prefill_common(mla_ctx* h, const void* hidden, const int32_t* cu_new,
   if ((rc = stage_upload(h, at<char>(ws, L.meta), blob.data(), blob.size()))) return rc;
   // a prefill step first appends the new tokens' latent rows (c and k_rope
   // of every new position, "Multi-Head Latent Attention" post, section 3.1),
-  // through one product over [W_kva ; W_qa] for a query LoRA (both take the
-  // same hidden state in the DeepSeek code quoted in section 3.4)
+  // reading the hidden states once for the append and, with a query LoRA,
+  // the query's first projection (both take the same hidden state in the
+  // DeepSeek code quoted in section 3.4)
   mla::Part qa{};
   bool qa_done = false;
   if (step) {
@@ -2145,9 +2146,25 @@ static int prefill_common(mla_ctx* h, const void* hidden, const int32_t* cu_new,
                               h->rope, h->stream);
       qa = mla::Part{a.p + d.R, a.ks, a.ld, a.zs};
     } else {
-      const mla::Part a = gemm_part<bf16>(h, (const bf16*)hidden, d.D,
-                                          (const bf16*)(fuse ? h->w_in : h->w_kva), d.D, T, n,
-                                          d.D, at<float>(ws, L.pin), fuse ? h->t_in : h->t_kva);
+      mla::Part a;
+      if (fuse && h->t_kva && h->t_q && big_gemm(h, T, n, d.D, 1) &&
+          big_gemm(h, T, d.R, d.D, 1) && big_gemm(h, T, d.dq, d.D, 1)) {
+        // the hidden states tiled once for both products, which write adjacent
+        // columns of one output: as two launches the products fill the compute
+        // units better than one over 576 + dq columns does (its 128-wide
+        // column tiles leave a quarter-full last wave at 16,384 rows)
+        float* pin = at<float>(ws, L.pin);
+        bf16* At = reinterpret_cast<bf16*>(pin + align_up((size_t)T * n * 4) / 4);
+        mla::tile_rows((const bf16*)hidden, d.D, T, d.D, At, h->stream);
+        mla::gemm_big(At, (const bf16*)h->t_kva, T, d.R, d.D,
+                      mla::GemmOut{pin, nullptr, n, 0, 1.f}, h->n_cu, h->stream);
+        mla::gemm_big(At, (const bf16*)h->t_q, T, d.dq, d.D,
+                      mla::GemmOut{pin + d.R, nullptr, n, 0, 1.f}, h->n_cu, h->stream);
+        a = mla::Part{pin, 1, n, (int64_t)T * n};
+      } else {
+        a = gemm_part<bf16>(h, (const bf16*)hidden, d.D, (const bf16*)(fuse ? h->w_in : h->w_kva),
+                            d.D, T, n, d.D, at<float>(ws, L.pin), fuse ? h->t_in : h->t_kva);
+      }
       if (h->kv8)
         mla::append_rows_fp8(a, T, pos_d, slot_d, (const bf16*)h->kv_norm_g, (uint8_t*)cache, d,
                              h->rope, h->stream);
