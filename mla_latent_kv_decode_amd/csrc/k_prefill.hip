@@ -8,13 +8,13 @@
 // rows 0..p of its sequence).  K_nope and V come from the expansion GEMM
 // (rows x H x [K_nope | V], bf16); k_rope is read from the latent cache row.
 //
-// Block = (tile of up to 128 new tokens of one sequence, head).  Wave w owns
-// queries 32w .. 32w+31 of the tile as 2 blocks of 16.  Every value of a wave
-// fits in 256 VGPRs (no accumulation registers), so two blocks share a
-// compute unit and one's softmax overlaps the other's MFMAs.  Keys stream in tiles of
-// 32 through a 4-stage LDS ring filled by global_load_lds_dwordx4 (each wave
-// issues a quarter of every tile; one barrier per tile both publishes the tile
-// and frees the stage the next prefetch overwrites).  Per 32-key tile:
+// Block = (tile of up to 256 new tokens of one sequence, head), 8 waves.  Wave
+// w owns queries 32w .. 32w+31 of the tile as 2 blocks of 16.  Every value of
+// a wave fits in 256 VGPRs (no accumulation registers), so two waves share each
+// SIMD and one's softmax can overlap the other's MFMAs.  Keys stream in tiles
+// of 32 through a 4-stage LDS ring filled by global_load_lds_dwordx4 (waves 0-3
+// each issue a quarter of every tile; one barrier per tile both publishes the
+// tile and frees the stage the next prefetch overwrites).  Per 32-key tile:
 //   S^T (16 keys x 16 queries) = K . Q^T  -- 6 x mfma 16x16x32 per 16-key
 //       block and query block, each K fragment (LDS) reused for the wave's
 //       query blocks;
