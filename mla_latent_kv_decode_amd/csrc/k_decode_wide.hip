@@ -25,8 +25,13 @@
 // Per tile and wave the LDS reads are 18 KB of K fragments, 4 KB of C^T and
 // 8 KB of P (30 KB, against 50 KB when every wave summed all 512 columns for
 // its own heads).  A segment's partial is the softmax waves' (max, sum) per
-// head and the column waves' latent sums.  MFMA operand layouts and the LDS
-// swizzle of a 16-row block are those of the 16-head core.
+// head and the column waves' latent sums, written through the idle tile ring
+// in whole rows.  MFMA operand layouts and the LDS swizzle of a 16-row block
+// are those of the 16-head core.
+//
+// decode_core_wide8_k (below) is the same kernel over FP8 rows: each raw tile
+// is copied once and decoded once into the shared bf16 tile, and the row
+// scales enter the scores and the latent sum's probabilities in fp32.
 #include <utility>
 
 #include "decode_dev.h"
