@@ -1,6 +1,8 @@
 // The decode step's weight-streaming GEMMs (M = query rows <= 128) with their
-// epilogues applied in place, and the kernel that finishes the projections
-// (latent-row append, query RMSNorm, absorbed query).
+// epilogues applied in place, the split-K variant with LDS-resident
+// activations for at most 32 rows against large weights (gemm_res_k, below),
+// and the kernel that finishes the projections (latent-row append, query
+// RMSNorm, absorbed query).
 //
 // C (M x N) = A (M x K) W^T with A row-major activations and W a row-major
 // (N, K) weight (a linear layer), bf16 in, fp32 accumulation, on
@@ -8,12 +10,13 @@
 //   A (16 x 32): lane l holds A[l % 16][8 (l / 16) .. + 7]
 //   B (32 x 16): lane l holds B[8 (l / 16) .. + 7][l % 16]
 //   D (16 x 16): lane l holds D[4 (l / 16) .. + 3][l % 16]
-// A block computes a 16 x 32 tile over all of K, streaming 256-wide K chunks
-// of its 32 weight rows and 16 activation rows into a 3-stage LDS ring with
-// global_load_lds_dwordx4 (each copy is 1 KB: two 512-byte row pieces, so the
-// weights are read in long contiguous runs and the copies hold no registers),
-// two chunks in flight and two blocks per compute unit.  Inside a row piece the 16-byte chunk c of row r is
-// stored at c ^ (r % 16): the operand reads (16 lanes = 16 rows at one K
+// A block computes a 16 (32, 64) x 32 tile over all of K, streaming 256-wide
+// K chunks of its 32 weight rows and 16 (32, 64) activation rows into a
+// 3-stage LDS ring with global_load_lds_dwordx4 (each copy is 1 KB: two
+// 512-byte row pieces, so the weights are read in long contiguous runs and
+// the copies hold no registers), two chunks in flight (16-row tiles: two
+// blocks per compute unit).  Inside a row piece the 16-byte chunk c of row r
+// is stored at c ^ (r % 16): the operand reads (16 lanes = 16 rows at one K
 // offset) then hit distinct banks.  Wave w takes k-steps w and w + 4 of every
 // chunk; the four waves' sums are added through LDS in wave order
 // (deterministic).  Nothing is split over blocks, so the epilogue sees final
@@ -44,8 +47,9 @@ constexpr int NST = 3;                    // stages
 constexpr int kXcds = 8;
 constexpr int kMaxStreamRows = 128;  // rows (query rows of a step) the stream GEMMs take
 // MR activation rows per block (16: 24 KB stages, two blocks per compute
-// unit; 32: 32 KB stages, 64: 48 KB stages, one block).  A block copies (NT + MR) rows over all
-// of K, so the copy volume of a launch is (N / NT) (M / MR) (NT + MR) K 2
+// unit; 32: 32 KB stages, 64: 48 KB stages, one block).  A block copies
+// (NT + MR) rows over all of K, so the copy volume of a launch is
+// (N / NT) (M / MR) (NT + MR) K 2
 // bytes: taller tiles re-read the weights fewer times.
 template <int MR>
 struct Tile {
