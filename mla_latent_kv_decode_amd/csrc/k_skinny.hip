@@ -15,11 +15,13 @@
 // 3-stage LDS ring with global_load_lds_dwordx4 (each copy is 1 KB: two
 // 512-byte row pieces, so the weights are read in long contiguous runs and
 // the copies hold no registers), two chunks in flight (16-row tiles: two
-// blocks per compute unit).  Inside a row piece the 16-byte chunk c of row r
-// is stored at c ^ (r % 16): the operand reads (16 lanes = 16 rows at one K
-// offset) then hit distinct banks.  Wave w takes k-steps w and w + 4 of every
-// chunk; the four waves' sums are added through LDS in wave order
-// (deterministic).  Nothing is split over blocks, so the epilogue sees final
+// blocks per compute unit).  Eight waves issue the copies: L2-to-LDS copy
+// throughput per compute unit grows with the waves issuing them (measured
+// ~46 GB/s with 4 waves, ~62 with 8, on L2-resident data).  Inside a row
+// piece the 16-byte chunk c of row r is stored at c ^ (r % 16): the operand
+// reads (16 lanes = 16 rows at one K offset) then hit distinct banks.  Wave w
+// takes k-step w of every chunk; the eight waves' sums are added through LDS
+// in wave order (deterministic).  Nothing is split over blocks, so the epilogue sees final
 // sums and is applied right there, on adjacent column pairs: a bf16 store, an
 // fp32 store, or the query finish (per head: the nope part stored, the rope
 // part rotated and scaled into q_cat).  The 16-row blocks of a column tile are
@@ -38,7 +40,8 @@ using ddev::dma16_nt;
 using ddev::lds_u32;
 using ddev::wait_vmcnt;
 
-constexpr int NWV = 4;                    // waves
+constexpr int NWV = 4;                    // waves of the split-K products
+constexpr int SWV = 8;                    // waves of the column-tile stream products
 constexpr int NT = 32;                    // output columns per block
 constexpr int KC = 256;                   // K per chunk
 constexpr int ROWB = KC * 2;              // 512 bytes per row piece
@@ -55,8 +58,8 @@ template <int MR>
 struct Tile {
   static constexpr int ST_BYTES = (NT + MR) * ROWB;
   static constexpr int NCOPY = (NT + MR) / 2;  // one-KB copies per chunk
-  static constexpr int CPW = NCOPY / NWV;
-  static_assert(NCOPY % NWV == 0, "copies split evenly over the waves");
+  static constexpr int CPW = NCOPY / SWV;
+  static_assert(NCOPY % SWV == 0, "copies split evenly over the waves");
   static_assert((NST - 2) * CPW <= 63, "copies in flight fit the vmcnt field");
 };
 
@@ -73,13 +76,14 @@ __device__ __forceinline__ void chunk_copy(int i, const bf16* W, int64_t ldw, in
 }
 
 // The extra blocks of a launch that carries a HostCopy: block `blk` of them
-// copies words blk * 256 + threadIdx.x, then every (blocks * 256)-th, four
-// loads in flight per thread.
+// (NTH threads) copies words blk * NTH + threadIdx.x, then every
+// (blocks * NTH)-th, four loads in flight per thread.
+template <int NTH>
 __device__ __forceinline__ void host_copy(const HostCopy& hc, int blk) {
   const uint4* src = static_cast<const uint4*>(hc.src);
   uint4* dst = static_cast<uint4*>(hc.dst);
-  const int stride = hc.blocks * NWV * 64;
-  for (int i0 = blk * NWV * 64 + (int)threadIdx.x; i0 < hc.n16; i0 += 4 * stride) {
+  const int stride = hc.blocks * NTH;
+  for (int i0 = blk * NTH + (int)threadIdx.x; i0 < hc.n16; i0 += 4 * stride) {
     uint4 v[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u)
@@ -91,7 +95,7 @@ __device__ __forceinline__ void host_copy(const HostCopy& hc, int blk) {
 }
 
 template <int MR, class Epi>
-__global__ void __launch_bounds__(NWV * 64)
+__global__ void __launch_bounds__(SWV * 64)
 gemm_stream_k(const bf16* __restrict__ A, int64_t lda, const bf16* __restrict__ W, int64_t ldw,
               int M, int N, int K, int mtiles, Epi epi, HostCopy hc) {
   constexpr int ST_BYTES = Tile<MR>::ST_BYTES, CPW = Tile<MR>::CPW, NMB = MR / 16;
@@ -99,7 +103,7 @@ gemm_stream_k(const bf16* __restrict__ A, int64_t lda, const bf16* __restrict__ 
   // block -> (column tile, row tile); the row tiles of a column tile share an XCD
   const int bid = blockIdx.x;
   if (hc.n16 > 0 && bid >= hc.first_block) {
-    host_copy(hc, bid - hc.first_block);
+    host_copy<SWV * 64>(hc, bid - hc.first_block);
     return;
   }
   const int mt = (bid / kXcds) % mtiles;
@@ -134,8 +138,8 @@ gemm_stream_k(const bf16* __restrict__ A, int64_t lda, const bf16* __restrict__ 
     if (ch + NST - 1 < nchunk) issue(ch + NST - 1);
     const char* st = lds + (ch % NST) * ST_BYTES;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int c = 4 * (wave + 4 * u) + lg;  // 16-byte chunk of this lane's operands
+    for (int u = 0; u < KC / 32 / SWV; ++u) {
+      const int c = 4 * (wave + SWV * u) + lg;  // 16-byte chunk of this lane's operands
       bf16x8_t af[NMB];
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb)
@@ -152,7 +156,8 @@ gemm_stream_k(const bf16* __restrict__ A, int64_t lda, const bf16* __restrict__ 
     }
   }
 
-  // sum the four waves' tiles: red[w][row][col]
+  // sum the waves' tiles: red[w][row][col]
+  static_assert(SWV * MR * NT * 4 <= NST * ST_BYTES, "the wave sums fit in the ring");
   __syncthreads();  // the ring is free
   float* red = reinterpret_cast<float*>(lds);
 #pragma unroll
@@ -164,12 +169,13 @@ gemm_stream_k(const bf16* __restrict__ A, int64_t lda, const bf16* __restrict__ 
         red[(wave * MR + 16 * mb + 4 * lg + i) * NT + 16 * nb + lr] = acc[mb][nb][i];
   __syncthreads();
 #pragma unroll
-  for (int e = 0; e < NMB; ++e) {
-    const int t = threadIdx.x + 256 * e;  // row t / 16, columns 2 (t % 16), + 1
+  for (int e = 0; e < (MR * 16 + SWV * 64 - 1) / (SWV * 64); ++e) {
+    const int t = threadIdx.x + SWV * 64 * e;  // row t / 16, columns 2 (t % 16), + 1
+    if (t >= MR * 16) break;
     const int row = t >> 4, col = 2 * (t & 15);
     float v0 = 0.f, v1 = 0.f;
 #pragma unroll
-    for (int w = 0; w < NWV; ++w) {
+    for (int w = 0; w < SWV; ++w) {
       const float2 p = *reinterpret_cast<const float2*>(red + (w * MR + row) * NT + col);
       v0 += p.x;
       v1 += p.y;
@@ -285,7 +291,7 @@ gemm_res_k(const bf16* __restrict__ A, int64_t lda, const bf16* __restrict__ Wt,
   __shared__ __attribute__((aligned(1024))) char lds[RS_LDS];
   const int bid = blockIdx.x;
   if (hc.n16 > 0 && bid >= hc.first_block) {
-    host_copy(hc, bid - hc.first_block);
+    host_copy<NWV * 64>(hc, bid - hc.first_block);
     return;
   }
   const int s = bid % nslice, g = bid / nslice;  // slice s on XCD s % 8
@@ -495,19 +501,19 @@ void launch_stream(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int M
   const int m64 = (M + 63) / 64, m32 = (M + 31) / 32;
   if (M > 32 && ntiles * m64 * 4 >= device_cu_count() * 3) {
     hc.first_block = nt8 * m64;
-    gemm_stream_k<64, Epi><<<nt8 * m64 + (hc.n16 > 0 ? hc.blocks : 0), NWV * 64, 0, st>>>(
+    gemm_stream_k<64, Epi><<<nt8 * m64 + (hc.n16 > 0 ? hc.blocks : 0), SWV * 64, 0, st>>>(
         A, lda, W, ldw, M, N, K, m64, epi, hc);
     return;
   }
   if (M > 16 && ntiles * m32 * 4 >= device_cu_count() * 3) {
     hc.first_block = nt8 * m32;
-    gemm_stream_k<32, Epi><<<nt8 * m32 + (hc.n16 > 0 ? hc.blocks : 0), NWV * 64, 0, st>>>(
+    gemm_stream_k<32, Epi><<<nt8 * m32 + (hc.n16 > 0 ? hc.blocks : 0), SWV * 64, 0, st>>>(
         A, lda, W, ldw, M, N, K, m32, epi, hc);
     return;
   }
   const int mtiles = (M + 15) / 16;
   hc.first_block = nt8 * mtiles;
-  gemm_stream_k<16, Epi><<<nt8 * mtiles + (hc.n16 > 0 ? hc.blocks : 0), NWV * 64, 0, st>>>(
+  gemm_stream_k<16, Epi><<<nt8 * mtiles + (hc.n16 > 0 ? hc.blocks : 0), SWV * 64, 0, st>>>(
       A, lda, W, ldw, M, N, K, mtiles, epi, hc);
 }
 
@@ -516,8 +522,9 @@ void launch_stream(const bf16* A, int64_t lda, const bf16* W, int64_t ldw, int M
 //
 // Absorbed query ("Multi-Head Latent Attention" post, section 3.3): for head h
 // q_cat[t][h][c] = scale * sum_k q_nope[t][h][k] W_ukT[h][c][k] (c < 512,
-// K = dn), one block per (64-row group, head, 128 columns), wave w on 32 of
-// them.
+// K = dn), one block per (32-row group, head, 128 columns), wave w on 32 of
+// them.  (Groups of 64 rows took ~7 us at 64 query rows, 32 ~5 us: twice the
+// blocks and half the loads per wave before the first product.)
 template <int MT>
 __global__ void __launch_bounds__(256)
 finish_k(const bf16* __restrict__ q_nope, const bf16* __restrict__ w_ukT,
@@ -555,8 +562,9 @@ finish_k(const bf16* __restrict__ q_nope, const bf16* __restrict__ w_ukT,
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int lr = lane & 15, lg = lane >> 4;
-  // block = (64-row group, head, 128 columns)
-  const int r0 = 64 * (blk / (d.H * 4)), hb = blk % (d.H * 4);
+  // block = (32-row group, head, 128 columns)
+  static_assert(MT <= 2, "32-row groups");
+  const int r0 = 32 * (blk / (d.H * 4)), hb = blk % (d.H * 4);
   const int h = hb >> 2, c0 = (hb & 3) * 128 + 32 * wave;
   const int nks = d.dn / 32;
   f32x4_t acc[MT][2];
@@ -663,20 +671,16 @@ void decode_finish(const bf16* q_nope, const bf16* w_ukT, bf16* q_cat, int B, bo
                    bool append, bool qnorm, const float* a, int lda, int qa_col, const int32_t* pos,
                    const int64_t* slot, const bf16* kv_gamma, void* cache, const bf16* q_gamma,
                    bf16* cq, const Dims& d, const RopeTab& rt, hipStream_t st, bool kv8) {
-  // the absorbed query in groups of up to 64 rows
-  const int nab = absorb ? d.H * 4 * ((B + 63) / 64) : 0, nap = append ? B : 0,
+  // the absorbed query in groups of up to 32 rows
+  const int nab = absorb ? d.H * 4 * ((B + 31) / 32) : 0, nap = append ? B : 0,
             nqn = qnorm ? B : 0;
   const int blocks = nab + nap + nqn;
   if (blocks == 0) return;
 #define MLA_FIN(MT)                                                                          \
   skn::finish_k<MT><<<blocks, 256, 0, st>>>(q_nope, w_ukT, q_cat, B, nab, nap, a, lda, qa_col, pos, \
                                             slot, kv_gamma, cache, q_gamma, cq, d, rt, kv8 ? 1 : 0)
-  switch ((B + 15) / 16) {
-    case 1: MLA_FIN(1); break;
-    case 2: MLA_FIN(2); break;
-    case 3: MLA_FIN(3); break;
-    default: MLA_FIN(4); break;
-  }
+  if (B <= 16) MLA_FIN(1);
+  else MLA_FIN(2);
 #undef MLA_FIN
 }
 
