@@ -234,7 +234,7 @@ __device__ __forceinline__ void tile_scores(const char* st, char* xch, const Til
   *reinterpret_cast<bf16x8_t*>(xch + X_P + wave * 1024 + ln * 16) =
       __builtin_bit_cast(bf16x8_t, pk);
   if (ln < 16) reinterpret_cast<float*>(xch + X_A)[16 * wave + ln] = alpha;
-  if (ln == 0) reinterpret_cast<int*>(xch + X_F)[wave] = resc ? 1 : 0;
+  if (ln == 0) reinterpret_cast<unsigned char*>(xch + X_F)[wave] = resc ? 1 : 0;
 }
 
 // O^T += C^T . P^T for this wave's columns and every head group: mfma
@@ -256,21 +256,28 @@ __device__ __forceinline__ void tile_latent_sum(const char* st, const char* xch,
     const s16x8_t c8 = __builtin_shufflevector(c0, c1, 0, 1, 2, 3, 4, 5, 6, 7);
     cf[c] = __builtin_bit_cast(bf16x8_t, c8);
   }
-  const int* xf = reinterpret_cast<const int*>(xch + X_F);
+  // the eight groups' rescale flags (one byte each) in one read, the P
+  // fragments one group ahead of their products
+  static_assert(NW == 8, "eight flag bytes");
+  const uint2 fl = *reinterpret_cast<const uint2*>(xch + X_F);
+  const uint32_t flo = __builtin_amdgcn_readfirstlane(fl.x), fhi = __builtin_amdgcn_readfirstlane(fl.y);
   const float* xa = reinterpret_cast<const float*>(xch + X_A);
+  bf16x8_t pg[NW];
+  pg[0] = *reinterpret_cast<const bf16x8_t*>(xch + X_P + lane * 16);
 #pragma unroll
   for (int g = 0; g < NW; ++g) {
-    if (xf[g]) {
+    if (g + 1 < NW)
+      pg[g + 1] = *reinterpret_cast<const bf16x8_t*>(xch + X_P + (g + 1) * 1024 + lane * 16);
+    if (((g < 4 ? flo : fhi) >> (8 * (g & 3))) & 0xff) {
       // (the rescale factor's address from the opaque lane index: nothing
       // per lane stays live across the tile loop for it)
       const float a = xa[16 * g + (lane_id_opaque() & 15)];
 #pragma unroll
       for (int c = 0; c < CB_W; ++c) o[g][c] *= a;
     }
-    const bf16x8_t pg = *reinterpret_cast<const bf16x8_t*>(xch + X_P + g * 1024 + lane * 16);
 #pragma unroll
     for (int c = 0; c < CB_W; ++c)
-      o[g][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cf[c], pg, o[g][c], 0, 0, 0);
+      o[g][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cf[c], pg[g], o[g][c], 0, 0, 0);
   }
 }
 
