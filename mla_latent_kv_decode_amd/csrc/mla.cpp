@@ -369,7 +369,12 @@ const char* core_name(const mla_ctx* h) {
 bool combine_uv(const mla_ctx* h) { return h->mfma && h->d.dv == 128; }
 
 int max_parts(const mla_ctx* h, int64_t total_rows, int q_len = 1) {
-  int64_t p = (total_rows + 63) / 64;
+  // at least 64 rows per part; 256 for the many-head core, whose partial of a
+  // segment (128 heads x 512 fp32 sums, 262 KB) weighs as much as ~230 rows
+  // of cache: at one sequence of 32,768 rows, 256 parts wrote 67 MB of
+  // partials for 38 MB of rows and needed the combine's first pass
+  const int64_t min_rows = wide_core(h) ? 256 : 64;
+  int64_t p = (total_rows + min_rows - 1) / min_rows;
   // the MFMA cores run one workgroup per compute unit: per 16-head group (or
   // per 128 heads for the many-head core) and new token of a part
   const int64_t wgs = !h->mfma ? h->n_cu
