@@ -373,8 +373,9 @@ int max_parts(const mla_ctx* h, int64_t total_rows, int q_len = 1) {
   // segment (128 heads x 512 fp32 sums, 262 KB) weighs as much as ~230 rows
   // of cache: at one sequence of 32,768 rows, 256 parts wrote 67 MB of
   // partials for 38 MB of rows and needed the combine's first pass
-  const int64_t min_rows = wide_core(h) ? 256 : 64;
-  int64_t p = (total_rows + min_rows - 1) / min_rows;
+  // (rounded down there: 32,768 cached rows plus the new one make 128 parts,
+  // whose partials the combine merges without its first pass, not 129)
+  int64_t p = wide_core(h) ? total_rows / 256 : (total_rows + 63) / 64;
   // the MFMA cores run one workgroup per compute unit: per 16-head group (or
   // per 128 heads for the many-head core) and new token of a part
   const int64_t wgs = !h->mfma ? h->n_cu

@@ -98,11 +98,25 @@ def test_v2lite_decode_b1_s4096():
 
 
 def test_v2lite_long_and_short_mixed():
-    """One long sequence split over many workgroups (its partials need the
-    combine's second pass) next to short ones finished in the first pass."""
+    """One long sequence split over many workgroups (~46 partials, merged by
+    eight waves in the fused combine) next to short ones, one of them
+    finished by the core itself."""
     lens = [3000, 5, 40, 1, 700]
     case = DecodeCase(synth.V2_LITE, "bf16", 0.02, lens)
     _check(case, range(len(lens)))
+
+
+@pytest.mark.parametrize("n_short", [0, 127])
+def test_combine_first_pass(n_short):
+    """A sequence of 20,000 rows split over ~200 parts: more partials than the
+    fused combine merges directly (128 with eight waves on the one sequence of
+    a block, 16 with one wave per sequence at 128 sequences), so the chunked
+    first pass runs before it.  The long sequence against the oracle's
+    absorbed form (pinned equal to the non-absorbed one), a few short ones
+    against the non-absorbed step."""
+    lens = [20000] + [50 + 7 * i for i in range(n_short)]
+    case = DecodeCase(synth.V2_LITE, "bf16", 0.02, lens, keep=[0, 1, n_short] if n_short else [0])
+    _check(case, [0, 1, n_short] if n_short else [0], absorbed_only={0})
 
 
 @pytest.fixture(scope="module")
