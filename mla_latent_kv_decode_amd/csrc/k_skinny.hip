@@ -617,11 +617,12 @@ bool skinny_ok(int M, int N, int K) {
 
 int res_slices(int M, int N, int K) {
   if (M < 1 || M > 16 * skn::RS_MT || K % (64 * skn::RS_KB) != 0 || N % 4 != 0) return 0;
-  // weights under 40 MiB: the column tiles (eight-wave stream products), whose
+  // weights under 80 MiB: the column tiles (eight-wave stream products), whose
   // re-copied activations cost less than the split-K reduction's launch (V3
-  // in-projection, [W_kva; W_qa] 30 MB at 32 rows: step 239-243 -> 234-235 us);
-  // above (V3 q_b 75 MB, W_o 235 MB) the resident-activation split-K wins
-  if ((size_t)N * K * 2 < (size_t(40) << 20)) return 0;
+  // in-projection, [W_kva; W_qa] 30 MB at 32 rows: step 239-243 -> 234-235
+  // us; V3 q_b, 75 MB: B = 1 step 135 -> 127 us, B = 32 unchanged); above
+  // (V3 W_o, 235 MB) the resident-activation split-K wins
+  if ((size_t)N * K * 2 < (size_t(80) << 20)) return 0;
   return skn::res_plan(M, N, K, device_cu_count()).nslice;
 }
 

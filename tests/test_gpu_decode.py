@@ -265,12 +265,14 @@ def test_decode_step_batch_136():
     _step_case(synth.V2_LITE, [2 * b + (b % 5) * 13 for b in range(136)])
 
 
-# A 128-head layer with a 1024-wide query LoRA and hidden 2048: its query
-# up-projection (N = 128 * 192 = 24576, K = 1024, 48 MiB of weights) runs the
+# A 256-head layer with a 1024-wide query LoRA and hidden 2048: its query
+# up-projection (N = 256 * 192 = 49152, K = 1024, 96 MiB of weights) runs the
 # resident-activation product in one K slice, with the epilogue applied in
-# place; its output projection (N = 2048, K = 16384) in 32 slices and the
-# slice reduction.
-RES_DIMS = synth.LayerDims(hidden=2048, n_heads=128, qk_nope=128, qk_rope=64, v_head=128,
+# place; its output projection (N = 2048, K = 32768, 128 MiB) in 32 slices and
+# the slice reduction (both past the 80 MiB from which the split-K products
+# take over from the column tiles); its decode core runs two 128-head
+# workgroups per part.
+RES_DIMS = synth.LayerDims(hidden=2048, n_heads=256, qk_nope=128, qk_rope=64, v_head=128,
                            kv_lora=512, q_lora=1024)
 
 
